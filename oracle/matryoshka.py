@@ -1,0 +1,214 @@
+"""Float64 NumPy definitions of the junction, the exit heads, the
+Matryoshka distillation loss with its logit gradients, greedy argmax and
+accepted-prefix length.  Test infrastructure only (see the package header).
+
+Nothing here is blocked, fused or reordered beyond the definitions; the only
+concession to size is ``forward_tokens``, which evaluates the same
+definitions on a chosen subset of tokens (tokens are independent).
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Junction
+# ---------------------------------------------------------------------------
+def junction(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray) -> np.ndarray:
+    """Parameter-free junction between block m and block m+1.
+
+    "Matryoshka Language Model Suites", junction paragraph, and the key-visual
+    explainer's bottom panel: the m-th output is rescaled to the L2 norm of
+    the fresh embedding of the same token and the two are concatenated along
+    channels; no parameters.  Copyedit of Sec. 2 "Modeling": block m+1 reads
+    the previous block's output together with its own residual table
+    e_{m+1} applied to the original tokens x; with D_0 = 0 block 1 reads
+    e_1[x] alone.
+
+    Readings: per token, L2 over channels; no epsilon; the rescaled output
+    fills the first D_m channels and the embedding the last
+    D_{m+1} - D_m; if either norm is zero the rescaled half is zero.
+
+    h:   [N, D_in] (None or D_in == 0 for block 1); ids: [N] in [0, V);
+    emb: [V, D_out - D_in].  Returns float64 [N, D_out].
+    """
+    g = _f64(emb)[np.asarray(ids, dtype=np.int64)]
+    if h is None or np.asarray(h).shape[1] == 0:
+        return g
+    hf = _f64(h)
+    a = np.sqrt(np.sum(hf * hf, axis=1))
+    b = np.sqrt(np.sum(g * g, axis=1))
+    scale = np.zeros_like(a)
+    ok = (a > 0) & (b > 0)
+    scale[ok] = b[ok] / a[ok]
+    return np.concatenate([hf * scale[:, None], g], axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Heads
+# ---------------------------------------------------------------------------
+def heads(hs: Sequence[np.ndarray], ws: Sequence[np.ndarray]) -> List[np.ndarray]:
+    """Per-exit linear LM heads: l_m = h_m W^m^T.
+
+    Copyedit of Sec. 2 "Modeling": sub-model m is blocks 1..m followed by its
+    own head W^m in R^{V x D_m}; the heads are not nested.  Reading: no bias,
+    no final norm inside the op; logits are token-major [N, V].
+    """
+    return [_f64(h) @ _f64(w).T for h, w in zip(hs, ws)]
+
+
+# ---------------------------------------------------------------------------
+# Softmax pieces
+# ---------------------------------------------------------------------------
+def logsumexp(l: np.ndarray) -> np.ndarray:
+    """log sum_v exp(l_v) over the last axis, two passes with the max shift."""
+    l = _f64(l)
+    mx = np.max(l, axis=-1, keepdims=True)
+    return (mx + np.log(np.sum(np.exp(l - mx), axis=-1, keepdims=True)))[..., 0]
+
+
+def softmax(l: np.ndarray) -> np.ndarray:
+    l = _f64(l)
+    return np.exp(l - logsumexp(l)[..., None])
+
+
+# ---------------------------------------------------------------------------
+# Loss and gradients
+# ---------------------------------------------------------------------------
+def matryoshka_loss(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: float) -> Dict:
+    """Per-exit next-token cross-entropy plus online distillation.
+
+    "Matryoshka Language Model Suites", distillation paragraph: the largest
+    exit's softmax is the teacher and every smaller exit gets a token-level
+    cross-entropy to it, weighted alpha_d = 0.3 and mixed with its own LM
+    loss (follow-up 4 of "Is nesting the cheapest way ...": 0.7 next-token
+    plus 0.3 cross-entropy to the largest model).  Main-visual explainer,
+    panel (b): distillation goes only into the smaller exits.  Limitations
+    paragraph: per-sub-model losses are summed with equal weight.
+
+        CE_m   = LSE(l_m) - l_m[y]
+        Dist_m = -sum_v p_v log softmax(l_m)_v = LSE(l_m) - sum_v p_v l_m,v,
+                 p = softmax(l_M)                              (m < M)
+        L_m    = (1 - alpha) CE_m + alpha Dist_m               (m < M)
+        L_M    = CE_M,          total = sum_m L_m
+
+    Returns per-token arrays ce, dist (0 for the teacher), loss [M, N],
+    total [N], and their means over tokens.
+    """
+    M = len(logits)
+    y = np.asarray(labels, dtype=np.int64)
+    n = y.shape[0]
+    rows = np.arange(n)
+    ls = [_f64(l) for l in logits]
+    lse = np.stack([logsumexp(l) for l in ls])                   # [M, N]
+    ce = np.stack([lse[m] - ls[m][rows, y] for m in range(M)])   # [M, N]
+    p = np.exp(ls[-1] - lse[-1][:, None])
+    dist = np.zeros((M, n))
+    for m in range(M - 1):
+        dist[m] = lse[m] - np.sum(p * ls[m], axis=1)
+    loss = np.empty((M, n))
+    loss[: M - 1] = (1.0 - alpha) * ce[: M - 1] + alpha * dist[: M - 1]
+    loss[M - 1] = ce[M - 1]
+    total = np.sum(loss, axis=0)
+    return {
+        "lse": lse, "ce": ce, "dist": dist, "loss": loss, "total": total,
+        "mean_ce": ce.mean(axis=1), "mean_dist": dist.mean(axis=1),
+        "mean_loss": loss.mean(axis=1), "mean_total": float(total.mean()) if n else 0.0,
+    }
+
+
+def matryoshka_grad(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: float,
+                    grad_scale: float = 1.0) -> List[np.ndarray]:
+    """d(grad_scale * sum_t total_t) / d l_m for every exit.
+
+    The teacher's distribution enters the smaller exits' losses under
+    stop-gradient, so exit M's gradient is that of CE_M alone:
+
+        g_m = grad_scale * (softmax(l_m) - (1 - alpha) onehot(y) - alpha p)   (m < M)
+        g_M = grad_scale * (p - onehot(y))
+    """
+    M = len(logits)
+    y = np.asarray(labels, dtype=np.int64)
+    rows = np.arange(y.shape[0])
+    p = softmax(logits[-1])
+    out = []
+    for m in range(M):
+        if m == M - 1:
+            g = p.copy()
+            g[rows, y] -= 1.0
+        else:
+            g = softmax(logits[m]) - alpha * p
+            g[rows, y] -= 1.0 - alpha
+        out.append(grad_scale * g)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Greedy speculative verification
+# ---------------------------------------------------------------------------
+def argmax_lowest(l: np.ndarray) -> np.ndarray:
+    """Greedy token: index of the largest logit, the lowest index on ties."""
+    l = _f64(l)
+    mx = np.max(l, axis=-1, keepdims=True)
+    idx = np.arange(l.shape[-1])
+    return np.min(np.where(l == mx, idx, l.shape[-1]), axis=-1).astype(np.int64)
+
+
+def accept_prefix(draft: np.ndarray, verify: np.ndarray, draft_len: int) -> np.ndarray:
+    """Accepted draft length per sequence under greedy verification.
+
+    "Matryoshka Language Model Suites", speculative-decoding paragraphs: exit 1
+    drafts and exit M verifies, draft length 6, greedy decoding.  Reading:
+    in one verify pass over P = draft_len + 1 positions, draft token i is
+    accepted while exit 1's greedy token equals exit M's greedy token at every
+    position up to i; the count is the number of leading matches among the
+    first draft_len positions.  draft, verify: int [B, P].
+    """
+    d = np.asarray(draft)
+    v = np.asarray(verify)
+    B = d.shape[0]
+    out = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        k = 0
+        while k < draft_len and d[b, k] == v[b, k]:
+            k += 1
+        out[b] = k
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Chunked evaluation on a subset of tokens
+# ---------------------------------------------------------------------------
+def forward_tokens(hs: Sequence[np.ndarray], ws: Sequence[np.ndarray], labels: np.ndarray,
+                   alpha: float, grad_scale: float = 1.0, rows=None, chunk: int = 1024,
+                   want_grad: bool = True, exits: Optional[Sequence[int]] = None):
+    """Heads, losses and gradients for the tokens ``rows`` (default: all),
+    ``chunk`` tokens at a time.  Returns (loss dict over the rows, list of
+    per-exit gradient arrays [len(rows), V] or None)."""
+    n = hs[0].shape[0]
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    sel = list(range(len(hs))) if exits is None else list(exits)
+    parts = []
+    grads = [[] for _ in sel] if want_grad else None
+    for s in range(0, len(rows), chunk):
+        r = rows[s:s + chunk]
+        lg = heads([hs[m][r] for m in sel], [ws[m] for m in sel])
+        parts.append(matryoshka_loss(lg, labels[r], alpha))
+        if want_grad:
+            for j, g in enumerate(matryoshka_grad(lg, labels[r], alpha, grad_scale)):
+                grads[j].append(g)
+    keys = ("lse", "ce", "dist", "loss")
+    res = {k: np.concatenate([p[k] for p in parts], axis=1) for k in keys}
+    res["total"] = np.concatenate([p["total"] for p in parts])
+    for k in ("ce", "dist", "loss"):
+        res["mean_" + k] = res[k].mean(axis=1)
+    res["mean_total"] = float(res["total"].mean())
+    if want_grad:
+        grads = [np.concatenate(g, axis=0) for g in grads]
+    return res, grads

@@ -1,0 +1,278 @@
+"""Pins for the CPU oracle: brute force, closed forms, library special cases
+and invariants, each chosen so that a plausible slip in the oracle (a dropped
+term, a wrong sign or index, a reversed distillation direction, a transposed
+operand) fails at least one of them."""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------- LSE
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 16])
+def test_lse_brute_force(V):
+    r = rng(V)
+    for scale, shift in [(1.0, 0.0), (10.0, 0.0), (3.0, 700.0), (3.0, -700.0)]:
+        l = r.standard_normal((5, V)) * scale + shift
+        got = oracle.logsumexp(l)
+        for i in range(5):
+            m = max(l[i])
+            want = m + math.log(math.fsum(math.exp(x - m) for x in l[i]))
+            assert got[i] == pytest.approx(want, rel=1e-12, abs=1e-12)
+
+
+def test_lse_shift_invariance():
+    l = rng(1).standard_normal((4, 33))
+    np.testing.assert_allclose(oracle.logsumexp(l + 17.25), oracle.logsumexp(l) + 17.25, rtol=1e-14)
+
+
+# --------------------------------------------------------------------- CE
+def _torch_ce(l, y):
+    return F.cross_entropy(torch.from_numpy(l), torch.from_numpy(y.astype(np.int64)),
+                           reduction="none").numpy()
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_ce_is_library_cross_entropy_at_alpha_zero(M):
+    r = rng(M)
+    V, N = 37, 11
+    ls = [r.standard_normal((N, V)) * 3 for _ in range(M)]
+    y = r.integers(0, V, N)
+    out = oracle.matryoshka_loss(ls, y, 0.0)
+    for m in range(M):
+        np.testing.assert_allclose(out["ce"][m], _torch_ce(ls[m], y), rtol=1e-12)
+        np.testing.assert_allclose(out["loss"][m], _torch_ce(ls[m], y), rtol=1e-12)
+    np.testing.assert_allclose(out["total"], sum(_torch_ce(l, y) for l in ls), rtol=1e-12)
+
+
+def test_single_exit_is_plain_lm_loss_for_any_alpha():
+    r = rng(5)
+    l = r.standard_normal((9, 20)) * 2
+    y = r.integers(0, 20, 9)
+    for a in (0.0, 0.3, 1.0):
+        out = oracle.matryoshka_loss([l], y, a)
+        np.testing.assert_allclose(out["total"], _torch_ce(l, y), rtol=1e-12)
+        assert np.all(out["dist"] == 0)
+
+
+# --------------------------------------------------------------------- distillation
+def test_distillation_equals_teacher_entropy_when_logits_equal():
+    r = rng(7)
+    N, V = 6, 50
+    lt = r.standard_normal((N, V)) * 4
+    y = r.integers(0, V, N)
+    out = oracle.matryoshka_loss([lt.copy(), lt.copy(), lt], y, 0.3)
+    p = scipy.special.softmax(lt, axis=1)
+    H = scipy.stats.entropy(p, axis=1)
+    np.testing.assert_allclose(out["dist"][0], H, rtol=1e-12)
+    np.testing.assert_allclose(out["dist"][1], H, rtol=1e-12)
+
+
+def test_distillation_is_entropy_plus_kl_teacher_to_student():
+    """Dist_m = H(p) + KL(p || q_m): the teacher's distribution is the target."""
+    r = rng(8)
+    N, V = 8, 40
+    ls = [r.standard_normal((N, V)) * s for s in (1.0, 2.0, 3.0)]
+    y = r.integers(0, V, N)
+    out = oracle.matryoshka_loss(ls, y, 0.3)
+    p = scipy.special.softmax(ls[2], axis=1)
+    H = scipy.stats.entropy(p, axis=1)
+    for m in range(2):
+        q = scipy.special.softmax(ls[m], axis=1)
+        kl = scipy.special.rel_entr(p, q).sum(axis=1)
+        np.testing.assert_allclose(out["dist"][m], H + kl, rtol=1e-11)
+        assert np.all(out["dist"][m] >= H - 1e-12)       # Gibbs
+
+
+def test_alpha_one_loss_is_distillation_and_mix_is_linear():
+    r = rng(9)
+    ls = [r.standard_normal((5, 30)) * 2 for _ in range(3)]
+    y = r.integers(0, 30, 5)
+    o1 = oracle.matryoshka_loss(ls, y, 1.0)
+    np.testing.assert_allclose(o1["loss"][:2], o1["dist"][:2], rtol=1e-14)
+    np.testing.assert_allclose(o1["loss"][2], o1["ce"][2], rtol=1e-14)
+    o3 = oracle.matryoshka_loss(ls, y, 0.3)
+    np.testing.assert_allclose(o3["loss"][:2], 0.7 * o3["ce"][:2] + 0.3 * o3["dist"][:2], rtol=1e-13)
+    # the teacher's own loss never depends on alpha
+    np.testing.assert_allclose(o1["loss"][2], o3["loss"][2], rtol=0)
+
+
+# --------------------------------------------------------------------- gradients
+@pytest.mark.parametrize("V", [2, 5, 16])
+@pytest.mark.parametrize("alpha", [0.0, 0.3, 1.0])
+def test_gradients_central_differences(V, alpha):
+    r = rng(V + int(alpha * 10))
+    M, N = 3, 4
+    ls = [r.standard_normal((N, V)) * 2 for _ in range(M)]
+    y = r.integers(0, V, N)
+    gs = 0.5
+    g = oracle.matryoshka_grad(ls, y, alpha, gs)
+    eps = 1e-6
+    for m in range(M):
+        for t in range(N):
+            for v in range(V):
+                lp = [l.copy() for l in ls]
+                lm = [l.copy() for l in ls]
+                lp[m][t, v] += eps
+                lm[m][t, v] -= eps
+                if m < M - 1:
+                    fp = oracle.matryoshka_loss(lp, y, alpha)["total"].sum()
+                    fm = oracle.matryoshka_loss(lm, y, alpha)["total"].sum()
+                else:   # teacher under stop-gradient: only its own CE
+                    fp = oracle.matryoshka_loss(lp, y, alpha)["ce"][M - 1].sum()
+                    fm = oracle.matryoshka_loss(lm, y, alpha)["ce"][M - 1].sum()
+                fd = gs * (fp - fm) / (2 * eps)
+                assert g[m][t, v] == pytest.approx(fd, abs=2e-8)
+
+
+def test_gradient_rows_sum_to_zero_and_teacher_ignores_alpha():
+    r = rng(11)
+    ls = [r.standard_normal((6, 64)) * 3 for _ in range(4)]
+    y = r.integers(0, 64, 6)
+    g03 = oracle.matryoshka_grad(ls, y, 0.3)
+    g1 = oracle.matryoshka_grad(ls, y, 1.0)
+    for g in g03 + g1:
+        np.testing.assert_allclose(g.sum(axis=1), 0, atol=1e-14)
+    np.testing.assert_array_equal(g03[-1], g1[-1])
+    p = scipy.special.softmax(ls[-1], axis=1)
+    for m in range(3):
+        np.testing.assert_allclose(g1[m], scipy.special.softmax(ls[m], axis=1) - p, atol=1e-15)
+
+
+def test_gradient_matches_torch_autograd_with_detached_teacher():
+    r = rng(12)
+    ls = [torch.tensor(r.standard_normal((5, 23)) * 2, requires_grad=True) for _ in range(3)]
+    y = torch.tensor(r.integers(0, 23, 5))
+    p = torch.softmax(ls[-1], dim=1).detach()
+    tot = F.cross_entropy(ls[-1], y, reduction="sum")
+    for m in range(2):
+        ce = F.cross_entropy(ls[m], y, reduction="sum")
+        dist = -(p * torch.log_softmax(ls[m], dim=1)).sum()
+        tot = tot + 0.7 * ce + 0.3 * dist
+    tot.backward()
+    g = oracle.matryoshka_grad([l.detach().numpy() for l in ls], y.numpy(), 0.3)
+    for m in range(3):
+        np.testing.assert_allclose(g[m], ls[m].grad.numpy(), atol=1e-14)
+
+
+# --------------------------------------------------------------------- heads
+def test_heads_against_exactly_rounded_dot_products():
+    r = rng(13)
+    N, V = 5, 7
+    hs = [r.standard_normal((N, d)) * 4 for d in (3, 8, 13)]
+    ws = [r.standard_normal((V, d)) * 0.02 for d in (3, 8, 13)]
+    ls = oracle.heads(hs, ws)
+    for h, w, l in zip(hs, ws, ls):
+        assert l.shape == (N, V)
+        for t in range(N):
+            for v in range(V):
+                want = math.fsum(float(a) * float(b) for a, b in zip(h[t], w[v]))
+                assert l[t, v] == pytest.approx(want, rel=1e-13, abs=1e-16)
+
+
+# --------------------------------------------------------------------- junction
+def test_junction_invariants():
+    r = rng(14)
+    N, Din, Dout, V = 40, 24, 40, 50
+    h = r.standard_normal((N, Din)) * 4
+    h[3] = 0.0
+    emb = r.standard_normal((V, Dout - Din)) * 0.02
+    ids = r.integers(0, V, N)
+    out = oracle.junction(h, ids, emb)
+    assert out.shape == (N, Dout)
+    np.testing.assert_array_equal(out[:, Din:], emb[ids])                    # exact copy
+    b = np.linalg.norm(emb[ids], axis=1)
+    nz = np.arange(N) != 3
+    np.testing.assert_allclose(np.linalg.norm(out[nz, :Din], axis=1), b[nz], rtol=1e-14)
+    cos = np.sum(out[nz, :Din] * h[nz], axis=1) / (
+        np.linalg.norm(out[nz, :Din], axis=1) * np.linalg.norm(h[nz], axis=1))
+    np.testing.assert_allclose(cos, 1.0, rtol=1e-14)                           # positive multiple
+    assert np.all(out[3, :Din] == 0)
+    np.testing.assert_array_equal(oracle.junction(8.0 * h, ids, emb), out)   # scale invariance
+    np.testing.assert_allclose(oracle.junction(0.37 * h, ids, emb), out, rtol=1e-14)
+
+
+def test_junction_block_one_is_embedding_lookup():
+    r = rng(15)
+    emb = r.standard_normal((30, 9))
+    ids = r.integers(0, 30, 17)
+    want = F.embedding(torch.from_numpy(ids), torch.from_numpy(emb)).numpy()
+    np.testing.assert_array_equal(oracle.junction(None, ids, emb), want)
+    np.testing.assert_array_equal(oracle.junction(np.zeros((17, 0)), ids, emb), want)
+
+
+# --------------------------------------------------------------------- argmax / accept
+def test_argmax_ties_lowest_index_brute_force():
+    r = rng(16)
+    l = np.round(r.standard_normal((50, 12)), 1)
+    l[:, 7] = l.max(axis=1)          # plant ties with the max
+    got = oracle.argmax_lowest(l)
+    for t in range(50):
+        best = 0
+        for v in range(12):
+            if l[t, v] > l[t, best]:
+                best = v
+        assert got[t] == best
+    assert np.all(got <= 7)
+
+
+def test_accept_prefix_brute_force():
+    r = rng(17)
+    B, P = 200, 7
+    d = r.integers(0, 3, (B, P))
+    v = np.where(r.random((B, P)) < 0.7, d, r.integers(0, 3, (B, P)))
+    got = oracle.accept_prefix(d, v, 6)
+    for b in range(B):
+        k = 0
+        for i in range(6):
+            if d[b, i] != v[b, i]:
+                break
+            k += 1
+        assert got[b] == k
+    assert set(got.tolist()) >= {0, 6}
+
+
+# --------------------------------------------------------------------- covariance
+def test_vocab_and_token_permutation_covariance():
+    r = rng(18)
+    M, N, V = 3, 12, 31
+    ls = [r.standard_normal((N, V)) * 3 for _ in range(M)]
+    y = r.integers(0, V, N)
+    base = oracle.matryoshka_loss(ls, y, 0.3)
+    gb = oracle.matryoshka_grad(ls, y, 0.3)
+    pv = r.permutation(V)
+    inv = np.argsort(pv)
+    lsp = [l[:, pv] for l in ls]
+    o = oracle.matryoshka_loss(lsp, inv[y], 0.3)
+    np.testing.assert_allclose(o["loss"], base["loss"], rtol=1e-12)
+    for g, g0 in zip(oracle.matryoshka_grad(lsp, inv[y], 0.3), gb):
+        np.testing.assert_allclose(g, g0[:, pv], atol=1e-15)
+    pt = r.permutation(N)
+    o = oracle.matryoshka_loss([l[pt] for l in ls], y[pt], 0.3)
+    np.testing.assert_allclose(o["loss"], base["loss"][:, pt], rtol=1e-14)
+
+
+def test_forward_tokens_chunked_equals_whole():
+    s = synth.make_suite((16, 32, 48), 97, 2, 19, dtype="bf16", seed=3)
+    res, g = oracle.forward_tokens(s.h, s.w, s.labels, 0.3, 0.25, chunk=5)
+    lg = oracle.heads(s.h, s.w)
+    whole = oracle.matryoshka_loss(lg, s.labels, 0.3)
+    gw = oracle.matryoshka_grad(lg, s.labels, 0.3, 0.25)
+    np.testing.assert_allclose(res["loss"], whole["loss"], rtol=1e-13)
+    for a, b in zip(g, gw):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-16)
+    rows = np.array([5, 0, 37])
+    r2, g2 = oracle.forward_tokens(s.h, s.w, s.labels, 0.3, 0.25, rows=rows, exits=(0, 2))
+    np.testing.assert_allclose(r2["ce"][1], oracle.matryoshka_loss([lg[0][rows], lg[2][rows]],
+                                                                   s.labels[rows], 0.3)["ce"][1])

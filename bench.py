@@ -1,0 +1,238 @@
+"""Throughput of the Matryoshka multi-exit hot path on one MI355X.
+
+One step = both junctions (block 1 -> 2, block 2 -> 3), every exit's head,
+the distillation loss and dL/dlogits for all three exits, on one batch of
+seeded synthetic inputs shaped like the 500M / 1.5B / 3B suite (widths 1024,
+2304, 4352; vocabulary 32768; 8 x 2048 tokens; bf16 inputs, fp32
+accumulation; alpha_d = 0.3).  Inputs are resident in HBM before timing.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  Per-kernel durations come from HIP events that the
+library records around every launch on the launch stream during the timed
+steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+WORKLOAD = 2
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nested_exit_lm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the head GEMM from rocprofv3 counter runs, if they
+    were taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("heads_loss_bytes_per_launch")
+
+
+def cpu_baseline(s, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload: the
+    first tokens of the batch, 256 at a time, until `seconds` have passed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    done = 0
+    t0 = time.perf_counter()
+    chunk = 256
+    while done < s.n_tokens:
+        rows = np.arange(done, min(done + chunk, s.n_tokens))
+        oracle.junction(s.h[0][rows], s.ids[rows], s.emb[1])
+        oracle.junction(s.h[1][rows], s.ids[rows], s.emb[2])
+        oracle.forward_tokens(s.h, s.w, s.labels, s.alpha, 1.0, rows=rows, chunk=chunk)
+        done += len(rows)
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} of {s.n_tokens} tokens of the same batch (fp64 NumPy oracle: "
+                      f"both junctions, 3 heads, losses and dlogits), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-verify", action="store_true", help="skip the speculative-verify sub-benchmark")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path is built and timed on a single MI355X "
+              "(token sharding across GPUs is described, not built). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import nested_exit_lm_amd as nel
+
+    nel.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] generating inputs")
+    s = synth.make_workload(WORKLOAD)
+    N, V, D = s.n_tokens, s.vocab, s.widths
+
+    def td(a):
+        return torch.from_numpy(synth.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    hs = [td(x) for x in s.h]
+    ws = [td(x) for x in s.w]
+    embs = [td(x) for x in s.emb]
+    ids = torch.from_numpy(s.ids).to(dev)
+    labels = torch.from_numpy(s.labels).to(dev)
+    j2 = torch.empty(N, D[1], dtype=torch.bfloat16, device=dev)
+    j3 = torch.empty(N, D[2], dtype=torch.bfloat16, device=dev)
+    dl = [torch.empty(N, V, dtype=torch.bfloat16, device=dev) for _ in D]
+    mean = torch.empty(3 * len(D) + 1, dtype=torch.float32, device=dev)
+    tok = torch.empty(len(D), 3, N, dtype=torch.float32, device=dev)
+    wsb = torch.zeros(nel.workspace_size(nel.OP_LOSS, len(D), N, V), dtype=torch.uint8, device=dev)
+
+    def step():
+        nel.junction(hs[0], ids, embs[1], out=j2)
+        nel.junction(hs[1], ids, embs[2], out=j3)
+        nel.matryoshka_loss(hs, ws, labels, alpha_d=s.alpha, grad_scale=1.0, dlogits=dl,
+                            workspace=wsb, mean_loss=mean, token_loss=tok)
+
+    log("[bench] warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nel.timing_reset()
+    nel.timing_enable(True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nel.timing_enable(False)
+    ms = (t1 - t0) * 1e3 / args.steps
+    kern = {}
+    for k in ("junction", "heads_loss", "merge", "means", "finalize"):
+        tot, cnt = nel.timing_read(k)
+        kern[k] = {"avg_ms": tot / max(cnt, 1), "launches": cnt}
+
+    flops = 2.0 * N * V * sum(D)                                   # head GEMM, per launch
+    k2 = kern["heads_loss"]["avg_ms"] / 1e3
+    jbytes = sum(2 * (D[m - 1] + (D[m] - D[m - 1]) + D[m]) * N + 4 * N for m in (1, 2))  # both junctions
+    fbytes = 2 * len(D) * N * V * 2                               # finalize: read s, write g
+    kern["heads_loss"]["tflops"] = flops / k2 / 1e12
+    kern["heads_loss"]["mfma_frac"] = flops / k2 / 1e12 / BF16_PEAK_TFLOPS
+    kern["junction"]["gbs"] = jbytes / 2 / (kern["junction"]["avg_ms"] / 1e3) / 1e9
+    kern["junction"]["hbm_frac"] = kern["junction"]["gbs"] / HBM_PEAK_GBS
+    kern["finalize"]["gbs"] = fbytes / (kern["finalize"]["avg_ms"] / 1e3) / 1e9
+    kern["finalize"]["hbm_frac"] = kern["finalize"]["gbs"] / HBM_PEAK_GBS
+    traffic = measured_traffic()
+    losses = mean.cpu().numpy().tolist()
+    out = {
+        "metric": "tokens/s of junction+3-exit head+distill loss (fwd+dlogits)",
+        "value": N / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": s.name, "widths": list(D), "vocab": V, "batch": s.batch,
+                   "seq_len": s.seq, "tokens": N, "alpha_d": s.alpha, "exits": len(D),
+                   "accumulate": "fp32", "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "kernel": "heads_loss", "achieved": flops / k2 / 1e12,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / k2 / 1e12 / BF16_PEAK_TFLOPS, "traffic": traffic},
+        "kernels": kern,
+        "end_to_end_mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+        "mean_loss": losses,
+    }
+    if not args.no_verify:
+        out["verify_102x7"] = bench_verify(nel, torch, synth, dev, args)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline")
+        out["cpu_baseline"] = cpu_baseline(s, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_verify(nel, torch, synth, dev, args):
+    """Speculative-verify shape: junction 1 -> 2, heads of exits 1 and 3 with greedy
+    argmax, accepted prefix length (102 sequences x 7 positions)."""
+    s = synth.make_workload(4)
+
+    def td(a):
+        return torch.from_numpy(synth.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    hs = [td(s.h[m]) for m in s.exits]
+    ws = [td(s.w[m]) for m in s.exits]
+    emb = td(s.emb[1])
+    ids = torch.from_numpy(s.ids).to(dev)
+    j = torch.empty(s.n_tokens, s.widths[1], dtype=torch.bfloat16, device=dev)
+    wsb = torch.zeros(nel.workspace_size(nel.OP_HEADS, 2, s.n_tokens, s.vocab), dtype=torch.uint8,
+                      device=dev)
+
+    def step():
+        nel.junction(hs[0], ids, emb, out=j)
+        _, am = nel.exit_heads(hs, ws, want_logits=False, want_argmax=True, workspace=wsb)
+        nel.accept_prefix(am[0].view(s.batch, s.seq), am[1].view(s.batch, s.seq), 6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nel.timing_reset()
+    nel.timing_enable(True)
+    steps = max(args.steps, 20)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nel.timing_enable(False)
+    tot, cnt = nel.timing_read("heads_argmax")
+    flops = 2.0 * s.n_tokens * s.vocab * (s.widths[0] + s.widths[2])
+    k = tot / max(cnt, 1) / 1e3
+    return {"ms_per_step": (t1 - t0) * 1e3 / steps, "tokens": s.n_tokens,
+            "heads_argmax_ms": k * 1e3, "heads_argmax_tflops": flops / k / 1e12,
+            "heads_argmax_mfma_frac": flops / k / 1e12 / BF16_PEAK_TFLOPS}
+
+
+if __name__ == "__main__":
+    main()

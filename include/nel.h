@@ -1,0 +1,180 @@
+/*
+ * nel.h -- C ABI of the Matryoshka multi-exit hot path on MI355X (gfx950).
+ *
+ * A Matryoshka suite nests M sub-models in one network: block m has width D_m
+ * (D_1 < ... < D_M), every exit m has its own LM head W^m in R^{V x D_m}, and a
+ * parameter-free junction joins block m to block m+1.  This library computes,
+ * on one GPU, the junction, every exit's logits, and the loss in which the
+ * largest exit's softmax teaches the smaller exits, together with the loss's
+ * gradient with respect to every exit's logits.
+ *
+ * Sources (the paper's equations are referenced, not printed, on the pages):
+ *   "Matryoshka Language Model Suites" (paper summary): paragraphs on the
+ *     junction, on distillation and on speculative decoding;
+ *   "Visualizing Core ideas": panels (b), (c) and (e);
+ *   "Visualizing the core idea of Matryoshka LM Suites": bottom panel;
+ *   copyedit of Sec. 2 "Modeling": notation x, e_m, D_0 = 0, W^m;
+ *   "Is nesting the cheapest way to build a model suite?", follow-up 4:
+ *     the 0.7 / 0.3 mix of next-token loss and cross-entropy to the largest exit.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are device pointers to dense row-major arrays; the caller
+ *     allocates and owns every buffer (inputs, outputs, workspace).  The
+ *     library never allocates, frees or retains a pointer after returning.
+ *   - Element type: NEL_BF16 (bfloat16 storage, fp32 arithmetic) or NEL_F32.
+ *   - Every base pointer must be 16-byte aligned (NEL_EALIGN otherwise).
+ *     Rows whose length is not a multiple of 16 bytes take masked element
+ *     paths, so any V >= 1 and D >= 1 are accepted.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued on it; no call synchronises except nel_read_device_flags and
+ *     nel_timing_read.
+ *   - Host-detectable errors are returned synchronously and nothing is
+ *     launched.  Data errors found on the device (a token id or label outside
+ *     [0, V)) set a bit in a device flag word (NEL_FLAG_*) and turn that
+ *     token's outputs into NaN; the flag word is sticky (OR-ed), the caller
+ *     clears it (nel_clear_device_flags or zero-initialised memory).
+ *   - Token ids and labels are 0-based int32 in [0, V).
+ */
+#ifndef NEL_H
+#define NEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NEL_OK = 0,
+  NEL_EINVAL = -1,      /* bad scalar argument (alpha, n_exits, op, NULL required pointer) */
+  NEL_ESHAPE = -2,      /* a size <= 0 where >= 1 is required, or widths not strictly increasing */
+  NEL_EDTYPE = -3,      /* unknown element type */
+  NEL_EALIGN = -4,      /* a base pointer not 16-byte aligned */
+  NEL_EWORKSPACE = -5,  /* workspace NULL or smaller than nel_workspace_size() */
+  NEL_EHIP = -6         /* the HIP runtime reported an error at launch */
+} nel_status;
+
+typedef enum { NEL_F32 = 0, NEL_BF16 = 1 } nel_dtype;
+
+enum { NEL_FLAG_BAD_ID = 1, NEL_FLAG_BAD_LABEL = 2 };
+
+enum { NEL_OP_LOSS = 0, NEL_OP_HEADS = 1 };
+
+enum { NEL_MAX_EXITS = 8 };
+
+/*
+ * Junction (the paper's Eq. 1, as stated in prose by the summary's junction
+ * paragraph and the key-visual explainer's bottom panel; block inputs from the
+ * copyedit of Sec. 2).  For every token t, with g = emb[ids[t]]:
+ *     out[t, :d_in]     = h[t] * ||g||_2 / ||h[t]||_2       (0 if either norm is 0)
+ *     out[t, d_in:d_out] = g                                 (bit-exact copy)
+ * d_in == 0 is block 1's input: out[t] = emb[ids[t]] (h may be NULL).
+ *   h:   [n_tokens, d_in]             dt     (input)
+ *   ids: [n_tokens] int32 in [0,vocab)       (input)
+ *   emb: [vocab, d_out - d_in]         dt     (input; the residual table e_{m+1})
+ *   out: [n_tokens, d_out]             dt     (output; must not alias the inputs)
+ *   flags: device int32 flag word or NULL; a bad id sets NEL_FLAG_BAD_ID and
+ *          writes a NaN row.
+ * Norms are accumulated in fp32; each output element is rounded once.
+ * Errors: NEL_ESHAPE if n_tokens < 0, d_in < 0, d_out <= d_in or vocab < 1.
+ */
+nel_status nel_junction(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_out,
+                        int32_t vocab, const void* h, const int32_t* ids, const void* emb,
+                        void* out, int32_t* flags, void* stream);
+
+/*
+ * Exit heads with greedy argmax (copyedit of Sec. 2: sub-model m ends in its
+ * own head W^m; the summary's speculative-decoding paragraph: greedy drafting
+ * and verification read the argmax of an exit's logits).  For each of the
+ * n_exits exits e (any subset of a suite, widths d[e] strictly increasing):
+ *     logits_e = h[e] · w[e]^T       fp32 accumulation, [n_tokens, vocab]
+ *     argmax[e * n_tokens + t] = lowest index of the row maximum
+ *   d:      host array [n_exits]
+ *   h:      host array of n_exits device pointers, h[e] is [n_tokens, d[e]] dt
+ *   w:      host array of n_exits device pointers, w[e] is [vocab, d[e]]   dt
+ *   logits: NULL, or host array of n_exits device pointers to fp32 [n_tokens, vocab]
+ *   argmax: NULL, or device int32 [n_exits, n_tokens]
+ *   workspace: device, >= nel_workspace_size(NEL_OP_HEADS, ...) bytes
+ */
+nel_status nel_exit_heads(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                          const int32_t* d, const void* const* h, const void* const* w,
+                          float* const* logits, int32_t* argmax, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * Greedy acceptance (summary's speculative-decoding paragraph: exit 1 drafts,
+ * the largest exit verifies, draft length 6).  For each sequence b, with
+ * P = positions tokens laid out [batch, positions]:
+ *     accepted[b] = number of leading i < draft_len with
+ *                   draft_argmax[b*P + i] == verify_argmax[b*P + i]
+ * Requires 0 <= draft_len <= positions.  All arrays are device int32.
+ */
+nel_status nel_accept_prefix(int32_t batch, int32_t positions, int32_t draft_len,
+                             const int32_t* draft_argmax, const int32_t* verify_argmax,
+                             int32_t* accepted, void* stream);
+
+/*
+ * Matryoshka loss with online distillation and its logit gradients (summary's
+ * distillation and limitations paragraphs; follow-up 4's 0.7/0.3 mix;
+ * main-visual explainer panel (b): distillation only into smaller exits).
+ * Exit n_exits-1 is the teacher M; p = softmax(l_M) is under stop-gradient.
+ * Per token t and exit m, with l_m = h[m] · w[m]^T (fp32 accumulation):
+ *     CE_m   = logsumexp(l_m) - l_m[y_t]
+ *     Dist_m = logsumexp(l_m) - sum_v p_v l_m,v          (m < M; 0 for M)
+ *     L_m    = (1 - alpha_d) CE_m + alpha_d Dist_m       (m < M),  L_M = CE_M
+ *     total  = sum_m L_m
+ *   token_loss: NULL, or device fp32 [n_exits, 3, n_tokens] = (CE, Dist, L)
+ *   mean_loss:  device fp32 [3*n_exits + 1]: mean over tokens of CE_0..CE_{M-1},
+ *               then Dist_0.., then L_0.., then the total (fixed-order sums)
+ *   dlogits:    NULL (loss only), or host array of n_exits device pointers,
+ *               dlogits[e] is [n_tokens, vocab] of type dt, written with
+ *               grad_scale * d(sum_t total_t)/d l_e:
+ *                 m < M: grad_scale (softmax(l_m) - (1-alpha_d) onehot(y) - alpha_d p)
+ *                 M:     grad_scale (p - onehot(y))
+ *   labels: device int32 [n_tokens]; a label outside [0,vocab) sets
+ *           NEL_FLAG_BAD_LABEL in the workspace's first word and NaNs that token.
+ *   workspace: device, >= nel_workspace_size(NEL_OP_LOSS, ...) bytes; its
+ *           first int32 is the device flag word.
+ * No fp32 logit tensor is ever written to memory.
+ * Errors: NEL_EINVAL if alpha_d is outside [0,1] or n_exits outside [1,8].
+ */
+nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                               const int32_t* d, const void* const* h, const void* const* w,
+                               const int32_t* labels, float alpha_d, float grad_scale,
+                               float* token_loss, float* mean_loss, void* const* dlogits,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace an op needs (0 on bad arguments). */
+size_t nel_workspace_size(int32_t op, int32_t n_exits, int64_t n_tokens, int32_t vocab);
+
+/* Copy the device flag word to *host_flags; synchronises `stream`. */
+nel_status nel_read_device_flags(const int32_t* dev_flags, int32_t* host_flags, void* stream);
+
+/* Zero the device flag word (a one-thread kernel on `stream`). */
+nel_status nel_clear_device_flags(int32_t* dev_flags, void* stream);
+
+/* Static text for a status code. */
+const char* nel_status_string(nel_status s);
+
+/*
+ * Measurement hooks.  While enabled, every kernel launch is bracketed by a
+ * pair of hipEvents recorded on the stream it is launched on, and
+ * nel_timing_read sums their elapsed times per kernel.  Kernel ids:
+ * 0 junction, 1 heads+loss statistics GEMM, 2 loss merge, 3 means,
+ * 4 dlogits finalize, 5 heads+argmax GEMM, 6 argmax merge, 7 accept.
+ * Process-global and not thread-safe: for benchmarks only.
+ */
+enum { NEL_K_JUNCTION = 0, NEL_K_HEADS_LOSS = 1, NEL_K_MERGE = 2, NEL_K_MEANS = 3,
+       NEL_K_FINALIZE = 4, NEL_K_HEADS_ARGMAX = 5, NEL_K_ARGMAX_MERGE = 6,
+       NEL_K_ACCEPT = 7, NEL_K_COUNT = 8 };
+nel_status nel_timing_enable(int32_t on);
+/* Synchronises the device, then returns the summed milliseconds and the
+ * number of timed launches of `kernel` since the last reset. */
+nel_status nel_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
+nel_status nel_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NEL_H */

@@ -1,0 +1,300 @@
+"""Python binding of libnel.so, the MI355X (gfx950) Matryoshka multi-exit hot path.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in ``include/nel.h``.  PyTorch supplies device memory and the
+current stream.  There is no fallback: if the library is not built, every
+call raises.
+
+    junction(h, ids, emb)                      -> out
+    exit_heads(hs, ws, want_logits, want_argmax) -> (logits | None, argmax | None)
+    accept_prefix(draft_argmax, verify_argmax, draft_len) -> accepted
+    matryoshka_loss(hs, ws, labels, alpha_d, grad_scale, want_dlogits)
+                                               -> (mean_loss, token_loss, dlogits)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+__all__ = [
+    "NelError", "load", "lib_path", "junction", "exit_heads", "accept_prefix", "matryoshka_loss",
+    "workspace_size", "read_flags", "clear_flags", "status_string", "timing_enable",
+    "timing_read", "timing_reset", "KERNELS", "OP_LOSS", "OP_HEADS", "FLAG_BAD_ID",
+    "FLAG_BAD_LABEL", "Workspace",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+F32, BF16 = 0, 1
+OP_LOSS, OP_HEADS = 0, 1
+FLAG_BAD_ID, FLAG_BAD_LABEL = 1, 2
+MAX_EXITS = 8
+KERNELS = ["junction", "heads_loss", "merge", "means", "finalize", "heads_argmax",
+           "argmax_merge", "accept"]
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libnel.so")
+
+
+class NelError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = status_string(status) if _LIB is not None else str(status)
+        super().__init__(f"{where}: {msg} ({status})")
+
+
+def load():
+    """Load libnel.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    p = lib_path()
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing; build it with `python -m nested_exit_lm_amd.build`")
+    lib = ctypes.CDLL(p)
+    c_int, c_i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    sig = {
+        "nel_junction": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp],
+        "nel_exit_heads": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
+        "nel_accept_prefix": [c_int, c_int, c_int, vp, vp, vp, vp],
+        "nel_matryoshka_loss": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, ctypes.c_float,
+                                ctypes.c_float, vp, vp, vp, vp, sz, vp],
+        "nel_workspace_size": [c_int, c_int, c_i64, c_int],
+        "nel_read_device_flags": [vp, vp, vp],
+        "nel_clear_device_flags": [vp, vp],
+        "nel_status_string": [c_int],
+        "nel_timing_enable": [c_int],
+        "nel_timing_read": [c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
+        "nel_timing_reset": [],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = c_int
+    lib.nel_workspace_size.restype = sz
+    lib.nel_status_string.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().nel_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise NelError(status, where)
+
+
+# ----------------------------------------------------------------- marshalling helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported element type {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, device, name):
+    if t is None:
+        return 0
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be a CUDA tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def _ptrs(ts) -> ctypes.Array:
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = t if isinstance(t, int) else (t.data_ptr() if t is not None else 0)
+    return arr
+
+
+def workspace_size(op: int, n_exits: int, n_tokens: int, vocab: int) -> int:
+    return int(load().nel_workspace_size(op, n_exits, n_tokens, vocab))
+
+
+class Workspace:
+    """A growable device byte buffer; zero-filled when (re)allocated, so the
+    flag word in its first 4 bytes starts clear."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int, device):
+        torch = _torch()
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_WS = {}
+
+
+def _workspace(op, device, nbytes):
+    ws = _WS.setdefault((op, str(device)), Workspace())
+    return ws.get(nbytes, device)
+
+
+# ----------------------------------------------------------------- entry points
+def junction(h, ids, emb, out=None, flags=None):
+    """out[t] = [h[t] * ||emb[ids[t]]|| / ||h[t]||, emb[ids[t]]]; h may be None (block 1)."""
+    torch = _torch()
+    device = emb.device
+    n = ids.shape[0]
+    d_in = 0 if h is None else h.shape[1]
+    de = emb.shape[1]
+    if h is not None and (h.dtype != emb.dtype or h.shape[0] != n):
+        raise ValueError("h must be [n, d_in] with the embedding's dtype")
+    if ids.dtype != torch.int32:
+        raise TypeError("ids must be int32")
+    if out is None:
+        out = torch.empty(n, d_in + de, dtype=emb.dtype, device=device)
+    lib = load()
+    _check(lib.nel_junction(_dt(emb), n, d_in, d_in + de, emb.shape[0], _dev(h, device, "h"),
+                            _dev(ids, device, "ids"), _dev(emb, device, "emb"),
+                            _dev(out, device, "out"), _dev(flags, device, "flags"),
+                            _stream(device)), "nel_junction")
+    return out
+
+
+def exit_heads(hs: Sequence, ws: Sequence, want_logits: bool = False, want_argmax: bool = True,
+               workspace=None):
+    """Logits (fp32, optional) and greedy argmax [n_exits, n] (int32) of each exit's head."""
+    torch = _torch()
+    E = len(hs)
+    if E != len(ws) or not 1 <= E <= MAX_EXITS:
+        raise ValueError("need 1..8 exits with one head each")
+    device = hs[0].device
+    n, V = hs[0].shape[0], ws[0].shape[0]
+    dt = _dt(hs[0])
+    for h, w in zip(hs, ws):
+        if _dt(h) != dt or _dt(w) != dt or h.shape[0] != n or w.shape[0] != V or h.shape[1] != w.shape[1]:
+            raise ValueError("inconsistent exit shapes or dtypes")
+        _dev(h, device, "h")
+        _dev(w, device, "w")
+    d = (ctypes.c_int32 * E)(*[h.shape[1] for h in hs])
+    logits = [torch.empty(n, V, dtype=torch.float32, device=device) for _ in range(E)] if want_logits else None
+    am = torch.empty(E, n, dtype=torch.int32, device=device) if want_argmax else None
+    need = workspace_size(OP_HEADS, E, n, V)
+    wsb = workspace if workspace is not None else _workspace(OP_HEADS, device, need)
+    lib = load()
+    _check(lib.nel_exit_heads(dt, E, n, V, d, _ptrs(hs), _ptrs(ws),
+                              _ptrs(logits) if logits is not None else None,
+                              _dev(am, device, "argmax"), wsb.data_ptr(), wsb.numel(),
+                              _stream(device)), "nel_exit_heads")
+    return logits, am
+
+
+def accept_prefix(draft_argmax, verify_argmax, draft_len: int):
+    """Leading matches among the first draft_len positions, per sequence ([B, P] int32 inputs)."""
+    torch = _torch()
+    device = draft_argmax.device
+    if draft_argmax.shape != verify_argmax.shape or draft_argmax.dim() != 2:
+        raise ValueError("draft and verify argmax must both be [batch, positions]")
+    for t in (draft_argmax, verify_argmax):
+        if t.dtype != torch.int32:
+            raise TypeError("argmax arrays must be int32")
+    B, P = draft_argmax.shape
+    acc = torch.empty(B, dtype=torch.int32, device=device)
+    _check(load().nel_accept_prefix(B, P, draft_len, _dev(draft_argmax, device, "draft"),
+                                    _dev(verify_argmax, device, "verify"),
+                                    _dev(acc, device, "accepted"), _stream(device)),
+           "nel_accept_prefix")
+    return acc
+
+
+def matryoshka_loss(hs: Sequence, ws: Sequence, labels, alpha_d: float = 0.3,
+                    grad_scale: float = 1.0, want_dlogits: bool = True,
+                    want_token_loss: bool = True, dlogits: Optional[List] = None, workspace=None,
+                    mean_loss=None, token_loss=None):
+    """Losses of every exit and, optionally, dL/dlogits (in hs' dtype).
+
+    Returns (mean_loss [3M+1] fp32, token_loss [M, 3, n] fp32 | None, dlogits list | None);
+    mean_loss = (CE_1..CE_M, Dist_1..Dist_M, L_1..L_M, total)."""
+    torch = _torch()
+    E = len(hs)
+    if E != len(ws) or not 1 <= E <= MAX_EXITS:
+        raise ValueError("need 1..8 exits with one head each")
+    device = hs[0].device
+    n, V = hs[0].shape[0], ws[0].shape[0]
+    dt = _dt(hs[0])
+    for h, w in zip(hs, ws):
+        if _dt(h) != dt or _dt(w) != dt or h.shape[0] != n or w.shape[0] != V or h.shape[1] != w.shape[1]:
+            raise ValueError("inconsistent exit shapes or dtypes")
+        _dev(h, device, "h")
+        _dev(w, device, "w")
+    if labels.dtype != torch.int32 or labels.shape != (n,):
+        raise ValueError("labels must be int32 [n]")
+    d = (ctypes.c_int32 * E)(*[h.shape[1] for h in hs])
+    if want_dlogits and dlogits is None:
+        dlogits = [torch.empty(n, V, dtype=hs[0].dtype, device=device) for _ in range(E)]
+    if not want_dlogits:
+        dlogits = None
+    if mean_loss is None:
+        mean_loss = torch.empty(3 * E + 1, dtype=torch.float32, device=device)
+    if want_token_loss and token_loss is None:
+        token_loss = torch.empty(E, 3, n, dtype=torch.float32, device=device)
+    if not want_token_loss:
+        token_loss = None
+    need = workspace_size(OP_LOSS, E, n, V)
+    wsb = workspace if workspace is not None else _workspace(OP_LOSS, device, need)
+    lib = load()
+    _check(lib.nel_matryoshka_loss(dt, E, n, V, d, _ptrs(hs), _ptrs(ws),
+                                   _dev(labels, device, "labels"), float(alpha_d),
+                                   float(grad_scale), _dev(token_loss, device, "token_loss"),
+                                   _dev(mean_loss, device, "mean_loss"),
+                                   _ptrs(dlogits) if dlogits is not None else None,
+                                   wsb.data_ptr(), wsb.numel(), _stream(device)),
+           "nel_matryoshka_loss")
+    return mean_loss, token_loss, dlogits
+
+
+def loss_workspace(device, n_exits: int, n_tokens: int, vocab: int):
+    """The workspace matryoshka_loss uses by default (its first int32 is the flag word)."""
+    return _workspace(OP_LOSS, device, workspace_size(OP_LOSS, n_exits, n_tokens, vocab))
+
+
+def read_flags(flags_tensor) -> int:
+    """Read a device flag word (an int32 tensor or a workspace byte tensor)."""
+    out = ctypes.c_int32(0)
+    dev = flags_tensor.device
+    _check(load().nel_read_device_flags(flags_tensor.data_ptr(), ctypes.addressof(out),
+                                        _stream(dev)), "nel_read_device_flags")
+    return out.value
+
+
+def clear_flags(flags_tensor):
+    _check(load().nel_clear_device_flags(flags_tensor.data_ptr(), _stream(flags_tensor.device)),
+           "nel_clear_device_flags")
+
+
+def timing_enable(on: bool = True):
+    _check(load().nel_timing_enable(1 if on else 0), "nel_timing_enable")
+
+
+def timing_reset():
+    _check(load().nel_timing_reset(), "nel_timing_reset")
+
+
+def timing_read(kernel) -> tuple:
+    """(total milliseconds, launches) of one kernel since the last reset; synchronises."""
+    k = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    ms, cnt = ctypes.c_double(0), ctypes.c_int64(0)
+    _check(load().nel_timing_read(k, ctypes.byref(ms), ctypes.byref(cnt)), "nel_timing_read")
+    return ms.value, cnt.value

@@ -1,0 +1,289 @@
+// C ABI (include/nel.h): argument validation, workspace carving and kernel
+// sequencing.  Every entry point validates everything it can on the host
+// before enqueuing any work, so an error return means nothing was launched.
+#include <limits.h>
+#include <math.h>
+#include <mutex>
+#include <vector>
+
+#include "nel.h"
+#include "common.h"
+#include "internal.h"
+
+using namespace nel;
+
+namespace {
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// ---------------------------------------------------------------- timing hooks
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  struct Pending {
+    int k;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  double total_ms[NEL_K_COUNT] = {};
+  int64_t launches[NEL_K_COUNT] = {};
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+// Brackets one launch with events on its stream when timing is enabled.
+template <typename F>
+hipError_t timed(int k, hipStream_t s, F&& launch) {
+  Timing& T = timing();
+  if (!T.on) return launch();
+  hipEvent_t a, b;
+  if (hipEventCreate(&a) != hipSuccess) return hipErrorUnknown;
+  if (hipEventCreate(&b) != hipSuccess) {
+    hipEventDestroy(a);
+    return hipErrorUnknown;
+  }
+  hipEventRecord(a, s);
+  const hipError_t err = launch();
+  hipEventRecord(b, s);
+  std::lock_guard<std::mutex> g(T.mu);
+  T.pending.push_back({k, a, b});
+  return err;
+}
+
+nel_status from_hip(hipError_t e) { return e == hipSuccess ? NEL_OK : NEL_EHIP; }
+
+nel_status check_exits(int32_t n_exits, int64_t n, const int32_t* d, const void* const* h,
+                       const void* const* w, bool strict) {
+  if (n_exits < 1 || n_exits > NEL_MAX_EXITS) return NEL_EINVAL;
+  if (!d || !h || !w) return NEL_EINVAL;
+  for (int e = 0; e < n_exits; ++e) {
+    if (d[e] < 1) return NEL_ESHAPE;
+    if (strict && e > 0 && d[e] <= d[e - 1]) return NEL_ESHAPE;
+    if (n > 0 && (!h[e] || !w[e])) return NEL_EINVAL;
+    if (misaligned(h[e]) || misaligned(w[e])) return NEL_EALIGN;
+  }
+  return NEL_OK;
+}
+
+bool grid_fits(int64_t n, int32_t vocab) {
+  const int64_t n_tt = (n + kTokTile - 1) / kTokTile;
+  return n_tt * n_vocab_tiles(vocab) <= INT_MAX && n <= (int64_t{1} << 40);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nel_status_string(nel_status s) {
+  switch (s) {
+    case NEL_OK: return "ok";
+    case NEL_EINVAL: return "invalid argument";
+    case NEL_ESHAPE: return "invalid shape";
+    case NEL_EDTYPE: return "invalid element type";
+    case NEL_EALIGN: return "pointer not 16-byte aligned";
+    case NEL_EWORKSPACE: return "workspace missing or too small";
+    case NEL_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t nel_workspace_size(int32_t op, int32_t n_exits, int64_t n_tokens, int32_t vocab) {
+  if (n_exits < 1 || n_exits > NEL_MAX_EXITS || n_tokens < 0 || vocab < 1) return 0;
+  if (op == NEL_OP_LOSS) return loss_ws_layout(n_exits, n_tokens, vocab).total;
+  if (op == NEL_OP_HEADS) return heads_ws_layout(n_exits, n_tokens, vocab).total;
+  return 0;
+}
+
+nel_status nel_junction(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_out,
+                        int32_t vocab, const void* h, const int32_t* ids, const void* emb,
+                        void* out, int32_t* flags, void* stream) {
+  if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
+  if (n_tokens < 0 || d_in < 0 || d_out <= d_in || vocab < 1) return NEL_ESHAPE;
+  if (n_tokens > 0 && (!ids || !emb || !out || (d_in > 0 && !h))) return NEL_EINVAL;
+  if (misaligned(h) || misaligned(ids) || misaligned(emb) || misaligned(out) || misaligned(flags))
+    return NEL_EALIGN;
+  if (n_tokens == 0) return NEL_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(timed(NEL_K_JUNCTION, s, [&] {
+    return dt == NEL_BF16
+               ? launch_junction<bf16_t>(n_tokens, d_in, d_out, vocab, h, ids, emb, out, flags, s)
+               : launch_junction<float>(n_tokens, d_in, d_out, vocab, h, ids, emb, out, flags, s);
+  }));
+}
+
+nel_status nel_exit_heads(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                          const int32_t* d, const void* const* h, const void* const* w,
+                          float* const* logits, int32_t* argmax, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
+  if (n_tokens < 0 || vocab < 1) return NEL_ESHAPE;
+  nel_status st = check_exits(n_exits, n_tokens, d, h, w, /*strict=*/false);
+  if (st != NEL_OK) return st;
+  if (!grid_fits(n_tokens, vocab)) return NEL_ESHAPE;
+  if (logits)
+    for (int e = 0; e < n_exits; ++e) {
+      if (n_tokens > 0 && !logits[e]) return NEL_EINVAL;
+      if (misaligned(logits[e])) return NEL_EALIGN;
+    }
+  if (misaligned(argmax) || misaligned(workspace)) return NEL_EALIGN;
+  const HeadsWs L = heads_ws_layout(n_exits, n_tokens, vocab);
+  if (!workspace || ws_bytes < L.total) return NEL_EWORKSPACE;
+  if (n_tokens == 0 || (!logits && !argmax)) return NEL_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ExitSet ex{};
+  for (int e = 0; e < n_exits; ++e) {
+    ex.h[e] = h[e];
+    ex.w[e] = w[e];
+    ex.out[e] = logits ? logits[e] : nullptr;
+    ex.d[e] = d[e];
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* best = reinterpret_cast<float*>(ws + L.best);
+  hipError_t err = timed(NEL_K_HEADS_ARGMAX, s, [&] {
+    return dt == NEL_BF16 ? launch_heads_argmax<bf16_t>(n_exits, n_tokens, vocab, ex, best, s)
+                          : launch_heads_argmax<float>(n_exits, n_tokens, vocab, ex, best, s);
+  });
+  if (err != hipSuccess) return NEL_EHIP;
+  if (argmax) {
+    err = timed(NEL_K_ARGMAX_MERGE, s, [&] {
+      return launch_argmax_merge(n_exits, n_tokens, vocab, best, argmax, s);
+    });
+  }
+  return from_hip(err);
+}
+
+nel_status nel_accept_prefix(int32_t batch, int32_t positions, int32_t draft_len,
+                             const int32_t* draft_argmax, const int32_t* verify_argmax,
+                             int32_t* accepted, void* stream) {
+  if (batch < 0 || positions < 1 || draft_len < 0 || draft_len > positions) return NEL_ESHAPE;
+  if (batch > 0 && (!draft_argmax || !verify_argmax || !accepted)) return NEL_EINVAL;
+  if (misaligned(draft_argmax) || misaligned(verify_argmax) || misaligned(accepted))
+    return NEL_EALIGN;
+  if (batch == 0) return NEL_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(timed(NEL_K_ACCEPT, s, [&] {
+    return launch_accept(batch, positions, draft_len, draft_argmax, verify_argmax, accepted, s);
+  }));
+}
+
+nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                               const int32_t* d, const void* const* h, const void* const* w,
+                               const int32_t* labels, float alpha_d, float grad_scale,
+                               float* token_loss, float* mean_loss, void* const* dlogits,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
+  if (n_tokens < 0 || vocab < 1) return NEL_ESHAPE;
+  nel_status st = check_exits(n_exits, n_tokens, d, h, w, /*strict=*/true);
+  if (st != NEL_OK) return st;
+  if (!(alpha_d >= 0.f && alpha_d <= 1.f) || !isfinite(grad_scale)) return NEL_EINVAL;
+  if (!grid_fits(n_tokens, vocab)) return NEL_ESHAPE;
+  if (!mean_loss || (n_tokens > 0 && !labels)) return NEL_EINVAL;
+  if (dlogits)
+    for (int e = 0; e < n_exits; ++e) {
+      if (n_tokens > 0 && !dlogits[e]) return NEL_EINVAL;
+      if (misaligned(dlogits[e])) return NEL_EALIGN;
+    }
+  if (misaligned(labels) || misaligned(token_loss) || misaligned(mean_loss) ||
+      misaligned(workspace))
+    return NEL_EALIGN;
+  const LossWs L = loss_ws_layout(n_exits, n_tokens, vocab);
+  if (!workspace || ws_bytes < L.total) return NEL_EWORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* flags = reinterpret_cast<int32_t*>(ws + L.flags);
+  float* stats = reinterpret_cast<float*>(ws + L.stats);
+  float* lab = reinterpret_cast<float*>(ws + L.lab);
+  float* lse = reinterpret_cast<float*>(ws + L.lse);
+  float* tl = token_loss ? token_loss : reinterpret_cast<float*>(ws + L.tokloss);
+  ExitSet ex{};
+  for (int e = 0; e < n_exits; ++e) {
+    ex.h[e] = h[e];
+    ex.w[e] = w[e];
+    ex.out[e] = dlogits ? dlogits[e] : nullptr;
+    ex.d[e] = d[e];
+  }
+  hipError_t err = timed(NEL_K_HEADS_LOSS, s, [&] {
+    return dt == NEL_BF16
+               ? launch_heads_loss<bf16_t>(n_exits, n_tokens, vocab, ex, labels, stats, lab, s)
+               : launch_heads_loss<float>(n_exits, n_tokens, vocab, ex, labels, stats, lab, s);
+  });
+  if (err != hipSuccess) return NEL_EHIP;
+  err = timed(NEL_K_MERGE, s, [&] {
+    return launch_loss_merge(n_exits, n_tokens, vocab, labels, alpha_d, stats, lab, lse, tl, s);
+  });
+  if (err != hipSuccess) return NEL_EHIP;
+  err = timed(NEL_K_MEANS, s, [&] {
+    return launch_loss_means(n_exits, n_tokens, vocab, labels, tl, mean_loss, flags, s);
+  });
+  if (err != hipSuccess) return NEL_EHIP;
+  if (dlogits && n_tokens > 0) {
+    err = timed(NEL_K_FINALIZE, s, [&] {
+      return dt == NEL_BF16 ? launch_finalize<bf16_t>(n_exits, n_tokens, vocab, labels, alpha_d,
+                                                      grad_scale, stats, lse, dlogits, s)
+                            : launch_finalize<float>(n_exits, n_tokens, vocab, labels, alpha_d,
+                                                     grad_scale, stats, lse, dlogits, s);
+    });
+  }
+  return from_hip(err);
+}
+
+nel_status nel_read_device_flags(const int32_t* dev_flags, int32_t* host_flags, void* stream) {
+  if (!dev_flags || !host_flags) return NEL_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(host_flags, dev_flags, sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+      hipSuccess)
+    return NEL_EHIP;
+  return from_hip(hipStreamSynchronize(s));
+}
+
+nel_status nel_clear_device_flags(int32_t* dev_flags, void* stream) {
+  if (!dev_flags) return NEL_EINVAL;
+  if (misaligned(dev_flags)) return NEL_EALIGN;
+  return from_hip(launch_clear_flags(dev_flags, static_cast<hipStream_t>(stream)));
+}
+
+nel_status nel_timing_enable(int32_t on) {
+  timing().on = on != 0;
+  return NEL_OK;
+}
+
+nel_status nel_timing_reset(void) {
+  Timing& T = timing();
+  std::lock_guard<std::mutex> g(T.mu);
+  for (auto& p : T.pending) {
+    hipEventSynchronize(p.b);
+    hipEventDestroy(p.a);
+    hipEventDestroy(p.b);
+  }
+  T.pending.clear();
+  for (int k = 0; k < NEL_K_COUNT; ++k) {
+    T.total_ms[k] = 0.0;
+    T.launches[k] = 0;
+  }
+  return NEL_OK;
+}
+
+nel_status nel_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel >= NEL_K_COUNT || !total_ms || !launches) return NEL_EINVAL;
+  Timing& T = timing();
+  std::lock_guard<std::mutex> g(T.mu);
+  nel_status st = NEL_OK;
+  for (auto& p : T.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess)
+      st = NEL_EHIP;
+    T.total_ms[p.k] += ms;
+    T.launches[p.k] += 1;
+    hipEventDestroy(p.a);
+    hipEventDestroy(p.b);
+  }
+  T.pending.clear();
+  *total_ms = T.total_ms[kernel];
+  *launches = T.launches[kernel];
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Launchers of the gfx950 kernels (host side), shared by the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nel {
+
+constexpr int kMaxExits = 8;
+// Token and vocabulary extent of one head-GEMM workgroup tile.  Loss
+// statistics are kept per (exit, vocabulary tile, token).
+constexpr int kTokTile = 128;
+constexpr int kVocTile = 128;
+
+struct ExitSet {
+  const void* h[kMaxExits];   // [n, d[e]]
+  const void* w[kMaxExits];   // [V, d[e]]
+  void* out[kMaxExits];       // loss: dlogits[e] [n, V] (dt) or null; argmax: fp32 logits or null
+  int d[kMaxExits];
+};
+
+inline int64_t n_vocab_tiles(int vocab) { return (vocab + kVocTile - 1) / kVocTile; }
+
+// Workspace layout of the loss op (byte offsets from the base).
+struct LossWs {
+  size_t flags, stats, lab, lse, tokloss, total;
+};
+inline LossWs loss_ws_layout(int n_exits, int64_t n, int vocab) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  LossWs L;
+  const size_t nvt = static_cast<size_t>(n_vocab_tiles(vocab));
+  L.flags = 0;
+  L.stats = 256;
+  L.lab = L.stats + up(sizeof(float) * n_exits * 3 * nvt * n);
+  L.lse = L.lab + up(sizeof(float) * n_exits * n);
+  L.tokloss = L.lse + up(sizeof(float) * n_exits * n);
+  L.total = L.tokloss + up(sizeof(float) * n_exits * 3 * n);
+  return L;
+}
+struct HeadsWs {
+  size_t flags, best, total;
+};
+inline HeadsWs heads_ws_layout(int n_exits, int64_t n, int vocab) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  HeadsWs L;
+  const size_t nvt = static_cast<size_t>(n_vocab_tiles(vocab));
+  L.flags = 0;
+  L.best = 256;
+  L.total = L.best + up(sizeof(float) * 2 * n_exits * nvt * n);
+  return L;
+}
+
+template <typename T>
+hipError_t launch_junction(int64_t n, int d_in, int d_out, int vocab, const void* h,
+                           const int32_t* ids, const void* emb, void* out, int32_t* flags,
+                           hipStream_t s);
+
+// Head GEMM + per-tile loss statistics (teacher = exit n_exits-1 first).
+template <typename T>
+hipError_t launch_heads_loss(int n_exits, int64_t n, int vocab, const ExitSet& ex,
+                             const int32_t* labels, float* stats, float* lab, hipStream_t s);
+// Head GEMM + per-tile (max, lowest index); optional fp32 logits in ex.out.
+template <typename T>
+hipError_t launch_heads_argmax(int n_exits, int64_t n, int vocab, const ExitSet& ex, float* best,
+                               hipStream_t s);
+
+hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, const int32_t* labels,
+                             float alpha, const float* stats, const float* lab, float* lse,
+                             float* tokloss, hipStream_t s);
+hipError_t launch_loss_means(int n_exits, int64_t n, int vocab, const int32_t* labels,
+                             const float* tokloss, float* means, int32_t* flags, hipStream_t s);
+template <typename T>
+hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const int32_t* labels, float alpha,
+                           float grad_scale, const float* stats, const float* lse,
+                           void* const* dlogits, hipStream_t s);
+hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, const float* best,
+                               int32_t* argmax, hipStream_t s);
+hipError_t launch_accept(int batch, int positions, int draft_len, const int32_t* draft,
+                         const int32_t* verify, int32_t* accepted, hipStream_t s);
+hipError_t launch_clear_flags(int32_t* flags, hipStream_t s);
+
+}  // namespace nel

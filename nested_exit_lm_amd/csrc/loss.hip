@@ -1,0 +1,355 @@
+// Row merge of the head GEMM's per-tile statistics, the token means, the
+// in-place logit-gradient finalisation, the argmax merge and greedy
+// acceptance.
+//
+// Loss ("Matryoshka Language Model Suites", distillation and limitations
+// paragraphs; follow-up 4 of "Is nesting the cheapest way to build a model
+// suite?" for the 0.7 / 0.3 mix), teacher M = last exit, p = softmax(l_M):
+//     CE_m = LSE_m - l_m[y],  Dist_m = LSE_m - sum_v p_v l_m,v   (m < M)
+//     L_m = (1 - a) CE_m + a Dist_m (m < M),  L_M = CE_M,  total = sum_m L_m
+// From the tiles: LSE = online log-sum-exp of (m_tile, sigma_tile) and
+// sum_v p_v l_m,v = sum_tiles exp(m_M,tile - LSE_M) S_m,tile.
+// Gradient (teacher under stop-gradient), written over the tile-shifted
+// logits s = l - m_tile the GEMM left in the caller's buffers:
+//     m < M: gs (exp(s_m + m_m,tile - LSE_m) - a p - (1 - a) [v = y])
+//     M:     gs (p - [v = y]),   p = exp(s_M + m_M,tile - LSE_M)
+#include <limits.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace nel {
+
+namespace {
+
+// ---------------------------------------------------------------- loss merge
+// 256 threads = 64 tokens x 4 tile groups; the groups are merged in LDS in a
+// fixed order, so results do not depend on scheduling.
+__global__ __launch_bounds__(256) void loss_merge_kernel(int M, int64_t n, int vocab,
+                                                         const int32_t* __restrict__ labels,
+                                                         float alpha,
+                                                         const float* __restrict__ stats,
+                                                         const float* __restrict__ lab,
+                                                         float* __restrict__ lse_out,
+                                                         float* __restrict__ tokloss, int n_vt) {
+  __shared__ float sh[4][64][2];
+  const int tl = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 64 + tl;
+  const bool valid = t < n;
+  const int64_t plane = static_cast<int64_t>(n_vt) * n;
+  const int y = valid ? labels[t] : 0;
+  const bool bad = y < 0 || y >= vocab;
+  const float* stT = stats + static_cast<int64_t>(M - 1) * 3 * plane + t;
+  float lseT = 0.f;
+  for (int ei = 0; ei < M; ++ei) {
+    const int e = ei == 0 ? M - 1 : ei - 1;
+    const float* st = stats + static_cast<int64_t>(e) * 3 * plane + t;
+    float m = -INFINITY, s = 0.f;
+    if (valid)
+      for (int vt = g; vt < n_vt; vt += 4) lse_merge(m, s, st[static_cast<int64_t>(vt) * n],
+                                                     st[plane + static_cast<int64_t>(vt) * n]);
+    sh[g][tl][0] = m;
+    sh[g][tl][1] = s;
+    __syncthreads();
+    float Mx = -INFINITY, Sx = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) lse_merge(Mx, Sx, sh[gg][tl][0], sh[gg][tl][1]);
+    __syncthreads();
+    const float L = Mx + flog(Sx);
+    if (ei == 0) lseT = L;
+    float dist = 0.f;
+    if (ei > 0) {
+      float a = 0.f;
+      if (valid)
+        for (int vt = g; vt < n_vt; vt += 4)
+          a = fmaf(fexp(stT[static_cast<int64_t>(vt) * n] - lseT),
+                   st[2 * plane + static_cast<int64_t>(vt) * n], a);
+      sh[g][tl][0] = a;
+      __syncthreads();
+      const float T = (sh[0][tl][0] + sh[1][tl][0]) + (sh[2][tl][0] + sh[3][tl][0]);
+      __syncthreads();
+      dist = L - T;
+    }
+    if (g == 0 && valid) {
+      float ce = L - (bad ? 0.f : lab[static_cast<int64_t>(e) * n + t]);
+      float lm = (ei == 0) ? ce : (1.f - alpha) * ce + alpha * dist;
+      float lse = L;
+      if (bad) ce = dist = lm = lse = __builtin_nanf("");
+      lse_out[static_cast<int64_t>(e) * n + t] = lse;
+      tokloss[(static_cast<int64_t>(e) * 3 + 0) * n + t] = ce;
+      tokloss[(static_cast<int64_t>(e) * 3 + 1) * n + t] = dist;
+      tokloss[(static_cast<int64_t>(e) * 3 + 2) * n + t] = lm;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- means
+// One workgroup; fp64 partial sums in a fixed order.
+__global__ __launch_bounds__(1024) void loss_means_kernel(int M, int64_t n, int vocab,
+                                                          const int32_t* __restrict__ labels,
+                                                          const float* __restrict__ tokloss,
+                                                          float* __restrict__ means,
+                                                          int32_t* __restrict__ flags) {
+  __shared__ double red[1024];
+  const int tid = threadIdx.x;
+  int bad = 0;
+  for (int64_t t = tid; t < n; t += 1024) {
+    const int y = labels[t];
+    bad |= (y < 0 || y >= vocab);
+  }
+  bad = __syncthreads_or(bad);
+  if (tid == 0 && bad && flags) atomicOr(flags, 2 /*NEL_FLAG_BAD_LABEL*/);
+  for (int qi = 0; qi <= 3 * M; ++qi) {
+    double a = 0.0;
+    if (qi < 3 * M) {
+      const int qq = qi / M, e = qi % M;   // output order: CE_*, Dist_*, L_*
+      const float* src = tokloss + (static_cast<int64_t>(e) * 3 + qq) * n;
+      for (int64_t t = tid; t < n; t += 1024) a += static_cast<double>(src[t]);
+    } else {
+      for (int64_t t = tid; t < n; t += 1024) {
+        double tot = 0.0;
+        for (int e = 0; e < M; ++e) tot += static_cast<double>(tokloss[(static_cast<int64_t>(e) * 3 + 2) * n + t]);
+        a += tot;
+      }
+    }
+    red[tid] = a;
+    __syncthreads();
+    for (int w = 512; w >= 1; w >>= 1) {
+      if (tid < w) red[tid] += red[tid + w];
+      __syncthreads();
+    }
+    if (tid == 0) means[qi] = n > 0 ? static_cast<float>(red[0] / static_cast<double>(n)) : 0.f;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- finalize
+struct DlPtrs {
+  void* p[kMaxExits];
+};
+
+// 16-byte chunk path (vocab a multiple of the chunk).  Each workgroup
+// iteration covers 256 consecutive chunks of one token row for all exits.
+template <typename T>
+__global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
+                                                    const int32_t* __restrict__ labels, float alpha,
+                                                    float gs, const float* __restrict__ stats,
+                                                    const float* __restrict__ lse, DlPtrs dl,
+                                                    int n_vt, int segs_per_row) {
+  constexpr int C = Elem<T>::kChunk;
+  const int64_t plane = static_cast<int64_t>(n_vt) * n;
+  const int64_t cpr = vocab / C;
+  const int64_t nseg = n * segs_per_row;
+  for (int64_t seg = blockIdx.x; seg < nseg; seg += gridDim.x) {
+    const int64_t t = seg / segs_per_row;
+    const int64_t c = static_cast<int64_t>(seg - t * segs_per_row) * 256 + threadIdx.x;
+    if (c >= cpr) continue;
+    const int v0 = static_cast<int>(c * C);
+    const int tile = v0 / kVocTile;
+    const int y = labels[t];
+    const bool bad = y < 0 || y >= vocab;
+    u32x4 raw[kMaxExits];
+#pragma unroll
+    for (int e = 0; e < kMaxExits; ++e)
+      if (e < M) raw[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                             static_cast<const T*>(dl.p[e]) + t * vocab) + c);
+    float p[C];
+    {
+      const int e = M - 1;
+      const float off = stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
+                        lse[static_cast<int64_t>(e) * n + t];
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        float s;
+        if constexpr (sizeof(T) == 2)
+          s = __uint_as_float((i & 1) ? (raw[e][i >> 1] & 0xffff0000u) : (raw[e][i >> 1] << 16));
+        else
+          s = __uint_as_float(raw[e][i]);
+        p[i] = fexp(s + off);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kMaxExits; ++e) {
+      if (e >= M) break;
+      const bool teacher = e == M - 1;
+      const float off = stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
+                        lse[static_cast<int64_t>(e) * n + t];
+      const float hot = teacher ? 1.f : 1.f - alpha;
+      float g[C];
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        float val;
+        if (teacher) {
+          val = p[i];
+        } else {
+          float s;
+          if constexpr (sizeof(T) == 2)
+            s = __uint_as_float((i & 1) ? (raw[e][i >> 1] & 0xffff0000u) : (raw[e][i >> 1] << 16));
+          else
+            s = __uint_as_float(raw[e][i]);
+          val = fexp(s + off) - alpha * p[i];
+        }
+        if (v0 + i == y) val -= hot;
+        g[i] = bad ? __builtin_nanf("") : gs * val;
+      }
+      u32x4 o;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(g[2 * j], g[2 * j + 1]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = __float_as_uint(g[j]);
+      }
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<T*>(dl.p[e]) + t * vocab) + c);
+    }
+  }
+}
+
+// Element path for any vocabulary size.
+template <typename T>
+__global__ __launch_bounds__(256) void finalize_elem(int M, int64_t n, int vocab,
+                                                     const int32_t* __restrict__ labels,
+                                                     float alpha, float gs,
+                                                     const float* __restrict__ stats,
+                                                     const float* __restrict__ lse, DlPtrs dl,
+                                                     int n_vt) {
+  const int64_t plane = static_cast<int64_t>(n_vt) * n;
+  const int64_t total = n * vocab;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = i / vocab;
+    const int v = static_cast<int>(i - t * vocab);
+    const int tile = v / kVocTile;
+    const int y = labels[t];
+    const bool bad = y < 0 || y >= vocab;
+    const int eT = M - 1;
+    T* pt = static_cast<T*>(dl.p[eT]) + i;
+    const float p = fexp(Elem<T>::to_f32(*pt) +
+                         stats[static_cast<int64_t>(eT) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
+                         lse[static_cast<int64_t>(eT) * n + t]);
+    for (int e = 0; e < M; ++e) {
+      T* pe = static_cast<T*>(dl.p[e]) + i;
+      float val;
+      if (e == eT) {
+        val = p - (v == y ? 1.f : 0.f);
+      } else {
+        const float q = fexp(Elem<T>::to_f32(*pe) +
+                             stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
+                             lse[static_cast<int64_t>(e) * n + t]);
+        val = q - alpha * p - (v == y ? 1.f - alpha : 0.f);
+      }
+      *pe = Elem<T>::from_f32(bad ? __builtin_nanf("") : gs * val);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- argmax merge
+__global__ __launch_bounds__(256) void argmax_merge_kernel(int E, int64_t n,
+                                                           const float* __restrict__ best,
+                                                           int32_t* __restrict__ argmax, int n_vt) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= E * n) return;
+  const int64_t e = i / n, t = i - e * n;
+  const int64_t plane = static_cast<int64_t>(n_vt) * n;
+  const float* b = best + e * 2 * plane + t;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  for (int vt = 0; vt < n_vt; ++vt) {   // ascending tiles: ties keep the lower index
+    const float v = b[static_cast<int64_t>(vt) * n];
+    if (v > bv) {
+      bv = v;
+      bi = __float_as_int(b[plane + static_cast<int64_t>(vt) * n]);
+    }
+  }
+  argmax[i] = bi;
+}
+
+// ---------------------------------------------------------------- acceptance
+__global__ __launch_bounds__(256) void accept_kernel(int B, int P, int dlen,
+                                                     const int32_t* __restrict__ d,
+                                                     const int32_t* __restrict__ v,
+                                                     int32_t* __restrict__ acc) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  const int64_t base = static_cast<int64_t>(b) * P;
+  int k = 0;
+  while (k < dlen && d[base + k] == v[base + k]) ++k;
+  acc[b] = k;
+}
+
+__global__ void clear_flags_kernel(int32_t* f) { *f = 0; }
+
+}  // namespace
+
+hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, const int32_t* labels, float alpha,
+                             const float* stats, const float* lab, float* lse, float* tokloss,
+                             hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(loss_merge_kernel, dim3(static_cast<unsigned>((n + 63) / 64)), dim3(256), 0, s,
+                     n_exits, n, vocab, labels, alpha, stats, lab, lse, tokloss,
+                     static_cast<int>(n_vocab_tiles(vocab)));
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_means(int n_exits, int64_t n, int vocab, const int32_t* labels,
+                             const float* tokloss, float* means, int32_t* flags, hipStream_t s) {
+  hipLaunchKernelGGL(loss_means_kernel, dim3(1), dim3(1024), 0, s, n_exits, n, vocab, labels,
+                     tokloss, means, flags);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const int32_t* labels, float alpha,
+                           float grad_scale, const float* stats, const float* lse,
+                           void* const* dlogits, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  constexpr int C = Elem<T>::kChunk;
+  DlPtrs dl{};
+  for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
+  const int n_vt = static_cast<int>(n_vocab_tiles(vocab));
+  if (vocab % C == 0) {
+    const int64_t cpr = vocab / C;
+    const int segs = static_cast<int>((cpr + 255) / 256);
+    const int64_t nseg = n * segs;
+    const unsigned grid = static_cast<unsigned>(nseg < 256 * 16 ? nseg : 256 * 16);
+    hipLaunchKernelGGL(finalize_vec<T>, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, labels,
+                       alpha, grad_scale, stats, lse, dl, n_vt, segs);
+  } else {
+    const int64_t total = n * vocab;
+    const int64_t blocks = (total + 255) / 256;
+    const unsigned grid = static_cast<unsigned>(blocks < 256 * 16 ? blocks : 256 * 16);
+    hipLaunchKernelGGL(finalize_elem<T>, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, labels,
+                       alpha, grad_scale, stats, lse, dl, n_vt);
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_finalize<bf16_t>(int, int64_t, int, const int32_t*, float, float,
+                                            const float*, const float*, void* const*, hipStream_t);
+template hipError_t launch_finalize<float>(int, int64_t, int, const int32_t*, float, float,
+                                           const float*, const float*, void* const*, hipStream_t);
+
+hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, const float* best,
+                               int32_t* argmax, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t total = n_exits * n;
+  hipLaunchKernelGGL(argmax_merge_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+                     dim3(256), 0, s, n_exits, n, best, argmax,
+                     static_cast<int>(n_vocab_tiles(vocab)));
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(int batch, int positions, int draft_len, const int32_t* draft,
+                         const int32_t* verify, int32_t* accepted, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(accept_kernel, dim3((batch + 255) / 256), dim3(256), 0, s, batch, positions,
+                     draft_len, draft, verify, accepted);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_flags(int32_t* flags, hipStream_t s) {
+  hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(1), 0, s, flags);
+  return hipGetLastError();
+}
+
+}  // namespace nel

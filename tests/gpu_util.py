@@ -1,0 +1,77 @@
+"""Shared helpers of the GPU tests: moving a synthetic suite to the device,
+reading results back, and the comparison bars."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_tensor(arr: np.ndarray, dtype: str, device="cuda:0"):
+    """A bf16-exact float32 array as a bf16 tensor, or a float32 tensor."""
+    import torch
+    import synth
+    if dtype == "bf16":
+        bits = synth.bf16_bits(arr)
+        return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def to_np(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()
+
+
+class DevSuite:
+    def __init__(self, s, device="cuda:0", exits=None):
+        import torch
+        self.s = s
+        sel = list(range(s.n_exits)) if exits is None else list(exits)
+        self.sel = sel
+        self.h = [dev_tensor(s.h[m], s.dtype, device) for m in sel]
+        self.w = [dev_tensor(s.w[m], s.dtype, device) for m in sel]
+        self.emb = [dev_tensor(e, s.dtype, device) for e in s.emb]
+        self.hall = {m: h for m, h in zip(sel, self.h)}
+        self.ids = torch.from_numpy(s.ids).to(device)
+        self.labels = torch.from_numpy(s.labels).to(device)
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (for normal values)."""
+    ax = np.abs(x).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def assert_loss_close(got: np.ndarray, ref: np.ndarray, rel=1e-3, what=""):
+    """Per element |got - ref| <= rel * max(1, |ref|)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= rel, f"{what}: worst scaled error {worst:.3g} > {rel}"
+    return worst
+
+
+def assert_grad_close(got: np.ndarray, ref: np.ndarray, atol: float, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    worst = float(np.abs(got - ref).max()) if got.size else 0.0
+    assert worst <= atol, f"{what}: max abs error {worst:.3g} > {atol}"
+    return worst
+
+
+def head_error_bound(h: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Upper bound of |fp32 accumulation - exact| per logit: gamma_K sum |h_k w_k| with a
+    generous gamma (any summation order, fp32 products of bf16 values are exact)."""
+    K = h.shape[1]
+    gamma = 2.0 * K * 2.0 ** -24
+    return gamma * (np.abs(h) @ np.abs(w).T)

@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before launching."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nested_exit_lm_amd as nel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "nel.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nel_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = nel.load()
+    syms = declared_symbols()
+    assert len(syms) == 11
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_status_strings_and_workspace_sizes():
+    assert nel.status_string(0) == "ok"
+    assert "workspace" in nel.status_string(-5)
+    assert nel.status_string(-99) == "unknown status"
+    n, V = 16384, 32768
+    nvt = V // 128
+    ws = nel.workspace_size(nel.OP_LOSS, 3, n, V)
+    assert ws >= 4 * (3 * 3 * nvt * n + 3 * n * 5)
+    assert nel.workspace_size(nel.OP_HEADS, 2, 714, V) >= 4 * 2 * 2 * nvt * 714
+    assert nel.workspace_size(nel.OP_LOSS, 0, n, V) == 0
+    assert nel.workspace_size(nel.OP_LOSS, 9, n, V) == 0
+    assert nel.workspace_size(7, 3, n, V) == 0
+
+
+def _arr(t, *v):
+    return (t * len(v))(*v)
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced (validation fails first)
+MIS = 0x10004           # misaligned
+
+
+def test_junction_host_validation():
+    lib = nel.load()
+    assert lib.nel_junction(7, 4, 8, 16, 10, FAKE, FAKE, FAKE, FAKE, None, None) == -3
+    assert lib.nel_junction(1, -1, 8, 16, 10, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert lib.nel_junction(1, 4, 8, 8, 10, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert lib.nel_junction(1, 4, 8, 16, 0, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert lib.nel_junction(1, 4, 8, 16, 10, None, FAKE, FAKE, FAKE, None, None) == -1
+    assert lib.nel_junction(1, 4, 8, 16, 10, MIS, FAKE, FAKE, FAKE, None, None) == -4
+    assert lib.nel_junction(1, 0, 8, 16, 10, None, None, None, None, None, None) == 0
+
+
+def test_loss_host_validation():
+    lib = nel.load()
+    d = _arr(ctypes.c_int32, 8, 16, 24)
+    p3 = _arr(ctypes.c_void_p, FAKE, FAKE, FAKE)
+    ws_need = nel.workspace_size(nel.OP_LOSS, 3, 4, 10)
+
+    def call(dt=1, E=3, n=4, V=10, d=d, h=p3, w=p3, labels=FAKE, alpha=0.3, gs=1.0,
+             mean=FAKE, dl=None, ws=FAKE, wsb=ws_need):
+        return lib.nel_matryoshka_loss(dt, E, n, V, d, h, w, labels, alpha, gs, None, mean, dl, ws,
+                                       wsb, None)
+
+    assert call(dt=5) == -3
+    assert call(E=0) == -1
+    assert call(E=9) == -1
+    assert call(n=-1) == -2
+    assert call(V=0) == -2
+    assert call(d=_arr(ctypes.c_int32, 8, 8, 24)) == -2        # widths must increase strictly
+    assert call(d=_arr(ctypes.c_int32, 0, 8, 24)) == -2
+    assert call(alpha=1.5) == -1
+    assert call(alpha=float("nan")) == -1
+    assert call(gs=float("inf")) == -1
+    assert call(mean=None) == -1
+    assert call(labels=None) == -1
+    assert call(h=_arr(ctypes.c_void_p, FAKE, MIS, FAKE)) == -4
+    assert call(ws=None) == -5
+    assert call(wsb=ws_need - 1) == -5
+    assert call(dl=_arr(ctypes.c_void_p, FAKE, None, FAKE)) == -1
+
+
+def test_heads_and_accept_host_validation():
+    lib = nel.load()
+    d = _arr(ctypes.c_int32, 8, 24)
+    p2 = _arr(ctypes.c_void_p, FAKE, FAKE)
+    need = nel.workspace_size(nel.OP_HEADS, 2, 4, 10)
+    assert lib.nel_exit_heads(3, 2, 4, 10, d, p2, p2, None, FAKE, FAKE, need, None) == -3
+    assert lib.nel_exit_heads(1, 2, 4, 10, d, p2, p2, None, FAKE, FAKE, need - 1, None) == -5
+    assert lib.nel_exit_heads(1, 2, 4, 10, d, p2, p2, None, MIS, FAKE, need, None) == -4
+    assert lib.nel_exit_heads(1, 2, 4, 0, d, p2, p2, None, FAKE, FAKE, need, None) == -2
+    assert lib.nel_accept_prefix(4, 7, 8, FAKE, FAKE, FAKE, None) == -2
+    assert lib.nel_accept_prefix(4, 7, -1, FAKE, FAKE, FAKE, None) == -2
+    assert lib.nel_accept_prefix(4, 7, 6, None, FAKE, FAKE, None) == -1
+    assert lib.nel_accept_prefix(0, 7, 6, None, None, None, None) == 0
+    assert lib.nel_read_device_flags(None, None, None) == -1
+    assert lib.nel_timing_read(99, None, None) == -1
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "nested_exit_lm_amd")
+    for dp, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dp, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", txt, re.M), f
+                assert "oracle/" not in txt, f
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(nel, "_LIB", None)
+    monkeypatch.setattr(nel, "_HERE", str(tmp_path))
+    with pytest.raises(ImportError):
+        nel.load()

@@ -1,0 +1,145 @@
+"""Edge cases of the HIP path: tiny and ragged vocabularies and widths,
+empty batches, many exits, out-of-range labels, the invariants the method
+fixes, and run-to-run determinism."""
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+import oracle
+import synth
+from gpu_util import DevSuite, assert_grad_close, assert_loss_close, log, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def full_compare(nel, s, alpha=0.3, tol_loss=1e-3, tol_grad=2e-2):
+    ds = DevSuite(s)
+    mean, tok, dl = nel.matryoshka_loss(ds.h, ds.w, ds.labels, alpha_d=alpha)
+    tok = to_np(tok)
+    ref, grads = oracle.forward_tokens(s.h, s.w, s.labels, alpha, 1.0)
+    assert_loss_close(tok[:, 0], ref["ce"], tol_loss, "CE")
+    assert_loss_close(tok[:, 1], ref["dist"], tol_loss, "Dist")
+    assert_loss_close(tok[:, 2], ref["loss"], tol_loss, "L")
+    for m in range(s.n_exits):
+        assert_grad_close(to_np(dl[m]), grads[m], tol_grad, f"dlogits {m}")
+    return ds, to_np(mean), tok, dl
+
+
+@pytest.mark.parametrize("V", [1, 2, 7, 16, 129, 257])
+@pytest.mark.parametrize("widths", [(8, 16, 24), (5, 11, 17)])
+def test_tiny_and_ragged_vocab(nel, V, widths):
+    s = synth.make_suite(widths, V, 1, 33, seed=V)
+    log(f"[edge] V={V} widths={widths}")
+    full_compare(nel, s)
+
+
+@pytest.mark.parametrize("N", [1, 2, 127, 128, 129])
+def test_ragged_token_counts(nel, N):
+    s = synth.make_suite((64, 128), 300, 1, N, seed=N)
+    full_compare(nel, s)
+
+
+def test_eight_exits(nel):
+    s = synth.make_suite(tuple(16 * (i + 1) for i in range(8)), 640, 1, 96, seed=51)
+    full_compare(nel, s)
+
+
+def test_empty_batch(nel):
+    import torch
+    s = synth.make_suite((8, 16), 10, 1, 1, seed=52)
+    ds = DevSuite(s)
+    h = [x[:0] for x in ds.h]
+    mean, tok, dl = nel.matryoshka_loss(h, ds.w, ds.labels[:0])
+    torch.cuda.synchronize()
+    assert tok.shape == (2, 3, 0) and dl[0].shape == (0, 10)
+    assert np.all(to_np(mean) == 0)
+    out = nel.junction(h[0], ds.ids[:0], ds.emb[1])
+    assert out.shape == (0, 16)
+
+
+def test_bad_labels_give_nan_and_flag(nel):
+    import torch
+    s = synth.make_suite((32, 64), 200, 1, 40, seed=53)
+    ds = DevSuite(s)
+    labels = ds.labels.clone()
+    labels[3] = 200
+    labels[7] = -5
+    ws = nel.loss_workspace(ds.h[0].device, 2, 40, 200)
+    nel.clear_flags(ws)
+    mean, tok, dl = nel.matryoshka_loss(ds.h, ds.w, labels, workspace=ws)
+    tok = to_np(tok)
+    assert nel.read_flags(ws) == nel.FLAG_BAD_LABEL
+    assert np.all(np.isnan(tok[:, :, [3, 7]]))
+    assert np.all(np.isnan(to_np(dl[0])[[3, 7]]))
+    ok = np.setdiff1d(np.arange(40), [3, 7])
+    ref, grads = oracle.forward_tokens(s.h, s.w, s.labels, 0.3, rows=ok)
+    assert_loss_close(tok[:, 0, ok], ref["ce"], 1e-3, "CE")
+    assert_grad_close(to_np(dl[1])[ok], grads[1], 2e-2, "dlogits")
+    assert np.isnan(to_np(mean)).all()
+    nel.clear_flags(ws)
+    assert nel.read_flags(ws) == 0
+
+
+def test_student_equal_to_teacher_gives_teacher_entropy(nel):
+    """l_1 = l_2 exactly: W^2 = [W^1, 0] and h_2 = [h_1, noise]."""
+    s = synth.make_suite((128, 256), 3000, 2, 96, seed=54)
+    s.w[1][:, :128] = s.w[0]
+    s.w[1][:, 128:] = 0
+    s.h[1][:, :128] = s.h[0]
+    ds = DevSuite(s)
+    _, tok, _ = nel.matryoshka_loss(ds.h, ds.w, ds.labels, alpha_d=0.3)
+    tok = to_np(tok)
+    l = oracle.heads([s.h[1]], [s.w[1]])[0]
+    H = scipy.stats.entropy(scipy.special.softmax(l, axis=1), axis=1)
+    assert_loss_close(tok[0, 1], H, 1e-3, "Dist vs entropy")
+    np.testing.assert_allclose(tok[0, 0], tok[1, 0], rtol=1e-5)   # same CE
+
+
+def test_single_exit_and_alpha_zero_reduce_to_cross_entropy(nel):
+    import torch
+    import torch.nn.functional as F
+    s = synth.make_suite((64, 96, 160), 1100, 1, 130, seed=55)
+    ds = DevSuite(s)
+    for m in range(3):
+        _, tok, dl = nel.matryoshka_loss([ds.h[m]], [ds.w[m]], ds.labels, alpha_d=0.3)
+        l = torch.from_numpy(oracle.heads([s.h[m]], [s.w[m]])[0])
+        ce = F.cross_entropy(l, torch.from_numpy(s.labels).long(), reduction="none").numpy()
+        assert_loss_close(to_np(tok)[0, 0], ce, 1e-3, "M=1 CE")
+        assert_loss_close(to_np(tok)[0, 2], ce, 1e-3, "M=1 L")
+    _, tok, _ = nel.matryoshka_loss(ds.h, ds.w, ds.labels, alpha_d=0.0)
+    tok = to_np(tok)
+    np.testing.assert_array_equal(tok[:, 2], tok[:, 0])
+
+
+def test_determinism(nel):
+    import torch
+    s = synth.make_suite((256, 512, 768), 4096, 2, 300, seed=56)
+    ds = DevSuite(s)
+    a = nel.matryoshka_loss(ds.h, ds.w, ds.labels)
+    a = (a[0].clone(), a[1].clone(), [x.clone() for x in a[2]])
+    b = nel.matryoshka_loss(ds.h, ds.w, ds.labels)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for x, y in zip(a[2], b[2]):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    _, am1 = nel.exit_heads(ds.h, ds.w)
+    _, am2 = nel.exit_heads(ds.h, ds.w)
+    assert torch.equal(am1, am2)
+
+
+def test_vocab_permutation_covariance(nel):
+    s = synth.make_suite((64, 128), 900, 1, 100, seed=57)
+    ds = DevSuite(s)
+    _, tok, dl = nel.matryoshka_loss(ds.h, ds.w, ds.labels)
+    tok = to_np(tok)
+    perm = np.random.default_rng(58).permutation(900)
+    inv = np.argsort(perm)
+    s2 = synth.make_suite((64, 128), 900, 1, 100, seed=57)
+    s2.w = [w[perm] for w in s2.w]
+    s2.labels = inv[s2.labels].astype(np.int32)
+    ds2 = DevSuite(s2)
+    _, tok2, dl2 = nel.matryoshka_loss(ds2.h, ds2.w, ds2.labels)
+    assert_loss_close(to_np(tok2), tok, 1e-4, "permuted losses")
+    for m in range(2):
+        assert_grad_close(to_np(dl2[m]), to_np(dl[m])[:, perm], 1e-2, "permuted dlogits")

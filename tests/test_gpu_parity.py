@@ -1,0 +1,163 @@
+"""HIP path vs the CPU oracle, element by element on the same seeded inputs.
+
+Small suites span several 128x128 tiles with ragged tails and are compared
+in full; the named full-size workloads run in the launch configuration the
+benchmark times and are compared on sampled tokens (every exit, full
+vocabulary rows).  Bars: losses within rel 1e-3 per token (scaled by
+max(1,|ref|)); bf16 logit gradients within 2e-2 max-abs at grad_scale 1;
+fp32 inputs are held to tighter bounds."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import DevSuite, assert_grad_close, assert_loss_close, log, to_np
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = {"bf16": 2e-2, "f32": 1e-4}
+LOSS_TOL = {"bf16": 1e-3, "f32": 1e-4}
+
+
+def run_loss(nel, ds, alpha, grad_scale=1.0, want_dlogits=True):
+    import torch
+    mean, tok, dl = nel.matryoshka_loss(ds.h, ds.w, ds.labels, alpha_d=alpha,
+                                        grad_scale=grad_scale, want_dlogits=want_dlogits)
+    torch.cuda.synchronize()
+    return to_np(mean), to_np(tok), dl
+
+
+def check_full(nel, s, alpha, grad_scale=1.0):
+    ds = DevSuite(s)
+    mean, tok, dl = run_loss(nel, ds, alpha, grad_scale)
+    ref, grads = oracle.forward_tokens(s.h, s.w, s.labels, alpha, grad_scale)
+    M = s.n_exits
+    tol = LOSS_TOL[s.dtype]
+    assert_loss_close(tok[:, 0], ref["ce"], tol, "CE")
+    assert_loss_close(tok[:, 1], ref["dist"], tol, "Dist")
+    assert_loss_close(tok[:, 2], ref["loss"], tol, "L")
+    want_mean = np.concatenate([ref["mean_ce"], ref["mean_dist"], ref["mean_loss"], [ref["mean_total"]]])
+    assert mean.shape == (3 * M + 1,)
+    assert_loss_close(mean, want_mean, tol, "means")
+    for m in range(M):
+        assert_grad_close(to_np(dl[m]), grads[m], GRAD_TOL[s.dtype] * max(1.0, abs(grad_scale)),
+                          f"dlogits exit {m}")
+
+
+SMALL = [
+    ("tiny-3exit-f32", lambda: synth.make_workload(0)),
+    ("bf16-ragged-3exit", lambda: synth.make_suite((64, 128, 200), 1000, 3, 100, seed=11)),
+    ("bf16-4exit-ragged", lambda: synth.make_suite((32, 64, 96, 128), 515, 1, 257, seed=12)),
+    ("bf16-1exit", lambda: synth.make_suite((96,), 300, 2, 65, seed=13)),
+    ("bf16-2exit-wide", lambda: synth.make_suite((256, 512), 2048, 2, 128, seed=14)),
+    ("f32-ragged", lambda: synth.make_suite((40, 72, 136), 777, 1, 200, dtype="f32", seed=15)),
+]
+
+
+@pytest.mark.parametrize("name,make", SMALL, ids=[c[0] for c in SMALL])
+def test_loss_small_full_compare(nel, name, make):
+    s = make()
+    log(f"[parity] {name}: widths={s.widths} V={s.vocab} N={s.n_tokens} dtype={s.dtype}")
+    check_full(nel, s, s.alpha)
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.3, 1.0])
+def test_loss_alpha_sweep_small(nel, alpha):
+    s = synth.make_suite((128, 192, 256), 1536, 2, 160, seed=21)
+    log(f"[parity] alpha={alpha}")
+    check_full(nel, s, alpha)
+
+
+def test_loss_grad_scale(nel):
+    s = synth.make_suite((64, 128, 192), 640, 2, 64, seed=22)
+    check_full(nel, s, 0.3, grad_scale=1.0 / 128)
+
+
+def test_loss_only_matches_loss_with_gradient(nel):
+    import torch
+    s = synth.make_suite((64, 128, 192), 640, 2, 64, seed=23)
+    ds = DevSuite(s)
+    m1, t1, _ = run_loss(nel, ds, 0.3, want_dlogits=True)
+    m2, t2, dl = run_loss(nel, ds, 0.3, want_dlogits=False)
+    assert dl is None
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_array_equal(m1, m2)
+
+
+def sample_rows(n, k, seed):
+    r = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, n - 1, n // 2], r.choice(n, size=k, replace=False)]))
+    return rows
+
+
+@pytest.mark.parametrize("k,alpha", [(1, 0.0), (1, 0.3), (1, 1.0), (2, 0.3), (3, 0.3)])
+def test_loss_full_size_sampled(nel, k, alpha):
+    import torch
+    s = synth.make_workload(k)
+    log(f"[parity] workload {k} ({s.name}) alpha={alpha}: N={s.n_tokens} widths={s.widths}")
+    ds = DevSuite(s)
+    mean, tok, dl = run_loss(nel, ds, alpha)
+    rows = sample_rows(s.n_tokens, 28, 100 + k)
+    ref, grads = oracle.forward_tokens(s.h, s.w, s.labels, alpha, 1.0, rows=rows)
+    assert_loss_close(tok[:, 0, rows], ref["ce"], 1e-3, "CE")
+    assert_loss_close(tok[:, 1, rows], ref["dist"], 1e-3, "Dist")
+    assert_loss_close(tok[:, 2, rows], ref["loss"], 1e-3, "L")
+    idx = torch.from_numpy(rows).cuda()
+    for m in range(s.n_exits):
+        g = to_np(dl[m].index_select(0, idx))
+        err = assert_grad_close(g, grads[m], 2e-2, f"dlogits exit {m}")
+        log(f"  exit {m}: max |dlogits err| {err:.2e}")
+    # the means are the fixed-order means of the per-token values
+    M = s.n_exits
+    want = np.concatenate([tok[:, 0].mean(1), tok[:, 1].mean(1), tok[:, 2].mean(1),
+                           [tok[:, 2].sum(0).mean()]])
+    np.testing.assert_allclose(mean, want, rtol=2e-6, atol=1e-6)
+    # every gradient row sums to zero (grad of a sum of normalised losses)
+    for m in range(M):
+        rs = dl[m].float().sum(dim=1)
+        assert float(rs.abs().max()) < 5e-2
+
+
+def test_junction_parity(nel):
+    import torch
+    for k in (0, 2):
+        s = synth.make_workload(k) if k == 0 else synth.make_workload(k, batch=1)
+        ds = DevSuite(s)
+        log(f"[junction] workload {k}: N={s.n_tokens} widths={s.widths}")
+        for m in range(s.n_exits):
+            h = None if m == 0 else ds.h[m - 1]
+            out = to_np(nel.junction(h, ds.ids, ds.emb[m]))
+            ref = oracle.junction(None if m == 0 else s.h[m - 1], s.ids, s.emb[m])
+            d_in = 0 if m == 0 else s.widths[m - 1]
+            # the embedding half is a bit-exact copy
+            np.testing.assert_array_equal(out[:, d_in:], s.emb[m][s.ids].astype(np.float64))
+            if d_in:
+                if s.dtype == "bf16":
+                    from gpu_util import bf16_ulp
+                    assert np.all(np.abs(out[:, :d_in] - ref[:, :d_in]) <= bf16_ulp(ref[:, :d_in]) + 1e-30)
+                    nrm = np.linalg.norm(out[:, :d_in], axis=1)
+                    b = np.linalg.norm(s.emb[m][s.ids].astype(np.float64), axis=1)
+                    np.testing.assert_allclose(nrm, b, rtol=2 ** -8)
+                else:
+                    np.testing.assert_allclose(out[:, :d_in], ref[:, :d_in], rtol=1e-6, atol=1e-30)
+        torch.cuda.synchronize()
+
+
+def test_junction_generic_widths_and_bad_ids(nel):
+    import torch
+    s = synth.make_suite((13, 40), 50, 1, 37, seed=31)
+    ds = DevSuite(s)
+    ids = ds.ids.clone()
+    ids[5] = 50
+    ids[9] = -1
+    flags = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    out = to_np(nel.junction(ds.h[0], ids, ds.emb[1], flags=flags))
+    ok = np.ones(s.n_tokens, bool)
+    ok[[5, 9]] = False
+    ref = oracle.junction(s.h[0][ok], s.ids[ok], s.emb[1])
+    from gpu_util import bf16_ulp
+    assert np.all(np.abs(out[ok] - ref) <= bf16_ulp(ref) + 1e-30)
+    assert np.all(np.isnan(out[[5, 9]]))
+    assert nel.read_flags(flags) == nel.FLAG_BAD_ID
+    nel.clear_flags(flags)
+    assert nel.read_flags(flags) == 0

@@ -22,9 +22,12 @@
  *     allocates and owns every buffer (inputs, outputs, workspace).  The
  *     library never allocates, frees or retains a pointer after returning.
  *   - Element type: NEL_BF16 (bfloat16 storage, fp32 arithmetic) or NEL_F32.
- *   - Every base pointer must be 16-byte aligned (NEL_EALIGN otherwise).
- *     Rows whose length is not a multiple of 16 bytes take masked element
- *     paths, so any V >= 1 and D >= 1 are accepted.
+ *   - Base pointers of bf16/fp32 tensors (h, w, emb, junction output,
+ *     dlogits, fp32 logits) and of the workspace must be 16-byte aligned;
+ *     int32 arrays (ids, labels, argmax, accepted, flags) and the fp32 loss
+ *     outputs need 4-byte alignment (NEL_EALIGN otherwise).  Rows whose
+ *     length is not a multiple of 16 bytes take masked element paths, so
+ *     any V >= 1 and D >= 1 are accepted.
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *     enqueued on it; no call synchronises except nel_read_device_flags and
  *     nel_timing_read.
@@ -50,7 +53,7 @@ typedef enum {
   NEL_EINVAL = -1,      /* bad scalar argument (alpha, n_exits, op, NULL required pointer) */
   NEL_ESHAPE = -2,      /* a size <= 0 where >= 1 is required, or widths not strictly increasing */
   NEL_EDTYPE = -3,      /* unknown element type */
-  NEL_EALIGN = -4,      /* a base pointer not 16-byte aligned */
+  NEL_EALIGN = -4,      /* a base pointer below its required alignment */
   NEL_EWORKSPACE = -5,  /* workspace NULL or smaller than nel_workspace_size() */
   NEL_EHIP = -6         /* the HIP runtime reported an error at launch */
 } nel_status;

@@ -14,7 +14,11 @@ using namespace nel;
 
 namespace {
 
+// Tensors read or written in 16-byte chunks (h, w, emb, junction output,
+// dlogits, fp32 logits, workspace) need 16-byte alignment; int32 arrays and
+// per-element fp32 outputs need 4.
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
 
 // ---------------------------------------------------------------- timing hooks
 struct Timing {
@@ -82,7 +86,7 @@ const char* nel_status_string(nel_status s) {
     case NEL_EINVAL: return "invalid argument";
     case NEL_ESHAPE: return "invalid shape";
     case NEL_EDTYPE: return "invalid element type";
-    case NEL_EALIGN: return "pointer not 16-byte aligned";
+    case NEL_EALIGN: return "pointer misaligned";
     case NEL_EWORKSPACE: return "workspace missing or too small";
     case NEL_EHIP: return "HIP runtime error";
   }
@@ -102,7 +106,7 @@ nel_status nel_junction(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_
   if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
   if (n_tokens < 0 || d_in < 0 || d_out <= d_in || vocab < 1) return NEL_ESHAPE;
   if (n_tokens > 0 && (!ids || !emb || !out || (d_in > 0 && !h))) return NEL_EINVAL;
-  if (misaligned(h) || misaligned(ids) || misaligned(emb) || misaligned(out) || misaligned(flags))
+  if (misaligned(h) || misaligned4(ids) || misaligned(emb) || misaligned(out) || misaligned4(flags))
     return NEL_EALIGN;
   if (n_tokens == 0) return NEL_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -127,7 +131,7 @@ nel_status nel_exit_heads(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32
       if (n_tokens > 0 && !logits[e]) return NEL_EINVAL;
       if (misaligned(logits[e])) return NEL_EALIGN;
     }
-  if (misaligned(argmax) || misaligned(workspace)) return NEL_EALIGN;
+  if (misaligned4(argmax) || misaligned(workspace)) return NEL_EALIGN;
   const HeadsWs L = heads_ws_layout(n_exits, n_tokens, vocab);
   if (!workspace || ws_bytes < L.total) return NEL_EWORKSPACE;
   if (n_tokens == 0 || (!logits && !argmax)) return NEL_OK;
@@ -141,14 +145,16 @@ nel_status nel_exit_heads(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32
   }
   char* ws = static_cast<char*>(workspace);
   float* best = reinterpret_cast<float*>(ws + L.best);
+  int vtile = kVocTile;
   hipError_t err = timed(NEL_K_HEADS_ARGMAX, s, [&] {
-    return dt == NEL_BF16 ? launch_heads_argmax<bf16_t>(n_exits, n_tokens, vocab, ex, best, s)
-                          : launch_heads_argmax<float>(n_exits, n_tokens, vocab, ex, best, s);
+    return dt == NEL_BF16
+               ? launch_heads_argmax<bf16_t>(n_exits, n_tokens, vocab, ex, best, &vtile, s)
+               : launch_heads_argmax<float>(n_exits, n_tokens, vocab, ex, best, &vtile, s);
   });
   if (err != hipSuccess) return NEL_EHIP;
   if (argmax) {
     err = timed(NEL_K_ARGMAX_MERGE, s, [&] {
-      return launch_argmax_merge(n_exits, n_tokens, vocab, best, argmax, s);
+      return launch_argmax_merge(n_exits, n_tokens, vocab, vtile, best, argmax, s);
     });
   }
   return from_hip(err);
@@ -159,7 +165,7 @@ nel_status nel_accept_prefix(int32_t batch, int32_t positions, int32_t draft_len
                              int32_t* accepted, void* stream) {
   if (batch < 0 || positions < 1 || draft_len < 0 || draft_len > positions) return NEL_ESHAPE;
   if (batch > 0 && (!draft_argmax || !verify_argmax || !accepted)) return NEL_EINVAL;
-  if (misaligned(draft_argmax) || misaligned(verify_argmax) || misaligned(accepted))
+  if (misaligned4(draft_argmax) || misaligned4(verify_argmax) || misaligned4(accepted))
     return NEL_EALIGN;
   if (batch == 0) return NEL_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -185,7 +191,7 @@ nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, 
       if (n_tokens > 0 && !dlogits[e]) return NEL_EINVAL;
       if (misaligned(dlogits[e])) return NEL_EALIGN;
     }
-  if (misaligned(labels) || misaligned(token_loss) || misaligned(mean_loss) ||
+  if (misaligned4(labels) || misaligned4(token_loss) || misaligned4(mean_loss) ||
       misaligned(workspace))
     return NEL_EALIGN;
   const LossWs L = loss_ws_layout(n_exits, n_tokens, vocab);
@@ -205,14 +211,17 @@ nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, 
     ex.out[e] = dlogits ? dlogits[e] : nullptr;
     ex.d[e] = d[e];
   }
+  int vtile = kVocTile;
   hipError_t err = timed(NEL_K_HEADS_LOSS, s, [&] {
-    return dt == NEL_BF16
-               ? launch_heads_loss<bf16_t>(n_exits, n_tokens, vocab, ex, labels, stats, lab, s)
-               : launch_heads_loss<float>(n_exits, n_tokens, vocab, ex, labels, stats, lab, s);
+    return dt == NEL_BF16 ? launch_heads_loss<bf16_t>(n_exits, n_tokens, vocab, ex, labels, stats,
+                                                      lab, &vtile, s)
+                          : launch_heads_loss<float>(n_exits, n_tokens, vocab, ex, labels, stats,
+                                                     lab, &vtile, s);
   });
   if (err != hipSuccess) return NEL_EHIP;
   err = timed(NEL_K_MERGE, s, [&] {
-    return launch_loss_merge(n_exits, n_tokens, vocab, labels, alpha_d, stats, lab, lse, tl, s);
+    return launch_loss_merge(n_exits, n_tokens, vocab, vtile, labels, alpha_d, stats, lab, lse, tl,
+                             s);
   });
   if (err != hipSuccess) return NEL_EHIP;
   err = timed(NEL_K_MEANS, s, [&] {
@@ -221,10 +230,10 @@ nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, 
   if (err != hipSuccess) return NEL_EHIP;
   if (dlogits && n_tokens > 0) {
     err = timed(NEL_K_FINALIZE, s, [&] {
-      return dt == NEL_BF16 ? launch_finalize<bf16_t>(n_exits, n_tokens, vocab, labels, alpha_d,
-                                                      grad_scale, stats, lse, dlogits, s)
-                            : launch_finalize<float>(n_exits, n_tokens, vocab, labels, alpha_d,
-                                                     grad_scale, stats, lse, dlogits, s);
+      return dt == NEL_BF16 ? launch_finalize<bf16_t>(n_exits, n_tokens, vocab, vtile, labels,
+                                                      alpha_d, grad_scale, stats, lse, dlogits, s)
+                            : launch_finalize<float>(n_exits, n_tokens, vocab, vtile, labels,
+                                                     alpha_d, grad_scale, stats, lse, dlogits, s);
     });
   }
   return from_hip(err);
@@ -241,7 +250,7 @@ nel_status nel_read_device_flags(const int32_t* dev_flags, int32_t* host_flags, 
 
 nel_status nel_clear_device_flags(int32_t* dev_flags, void* stream) {
   if (!dev_flags) return NEL_EINVAL;
-  if (misaligned(dev_flags)) return NEL_EALIGN;
+  if (misaligned4(dev_flags)) return NEL_EALIGN;
   return from_hip(launch_clear_flags(dev_flags, static_cast<hipStream_t>(stream)));
 }
 

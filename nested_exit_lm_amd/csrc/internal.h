@@ -7,8 +7,9 @@
 namespace nel {
 
 constexpr int kMaxExits = 8;
-// Token and vocabulary extent of one head-GEMM workgroup tile.  Loss
-// statistics are kept per (exit, vocabulary tile, token).
+// Smallest token and vocabulary extent of a head-GEMM workgroup tile.  Loss
+// statistics are kept per (exit, vocabulary tile, token); the GEMM reports
+// the vocabulary tile it used and the workspace is sized for the smallest.
 constexpr int kTokTile = 128;
 constexpr int kVocTile = 128;
 
@@ -55,25 +56,27 @@ hipError_t launch_junction(int64_t n, int d_in, int d_out, int vocab, const void
                            const int32_t* ids, const void* emb, void* out, int32_t* flags,
                            hipStream_t s);
 
-// Head GEMM + per-tile loss statistics (teacher = exit n_exits-1 first).
+// Head GEMM + per-tile loss statistics (teacher = exit n_exits-1 first);
+// *vtile receives the vocabulary tile size of the statistics.
 template <typename T>
 hipError_t launch_heads_loss(int n_exits, int64_t n, int vocab, const ExitSet& ex,
-                             const int32_t* labels, float* stats, float* lab, hipStream_t s);
+                             const int32_t* labels, float* stats, float* lab, int* vtile,
+                             hipStream_t s);
 // Head GEMM + per-tile (max, lowest index); optional fp32 logits in ex.out.
 template <typename T>
 hipError_t launch_heads_argmax(int n_exits, int64_t n, int vocab, const ExitSet& ex, float* best,
-                               hipStream_t s);
+                               int* vtile, hipStream_t s);
 
-hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, const int32_t* labels,
+hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
                              float alpha, const float* stats, const float* lab, float* lse,
                              float* tokloss, hipStream_t s);
 hipError_t launch_loss_means(int n_exits, int64_t n, int vocab, const int32_t* labels,
                              const float* tokloss, float* means, int32_t* flags, hipStream_t s);
 template <typename T>
-hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const int32_t* labels, float alpha,
-                           float grad_scale, const float* stats, const float* lse,
+hipError_t launch_finalize(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
+                           float alpha, float grad_scale, const float* stats, const float* lse,
                            void* const* dlogits, hipStream_t s);
-hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, const float* best,
+hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, int vtile, const float* best,
                                int32_t* argmax, hipStream_t s);
 hipError_t launch_accept(int batch, int positions, int draft_len, const int32_t* draft,
                          const int32_t* verify, int32_t* accepted, hipStream_t s);

@@ -131,7 +131,7 @@ struct DlPtrs {
 // 16-byte chunk path (vocab a multiple of the chunk).  Each workgroup
 // iteration covers 256 consecutive chunks of one token row for all exits.
 template <typename T>
-__global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
+__global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab, int vtile,
                                                     const int32_t* __restrict__ labels, float alpha,
                                                     float gs, const float* __restrict__ stats,
                                                     const float* __restrict__ lse, DlPtrs dl,
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
     const int64_t c = static_cast<int64_t>(seg - t * segs_per_row) * 256 + threadIdx.x;
     if (c >= cpr) continue;
     const int v0 = static_cast<int>(c * C);
-    const int tile = v0 / kVocTile;
+    const int tile = v0 / vtile;
     const int y = labels[t];
     const bool bad = y < 0 || y >= vocab;
     u32x4 raw[kMaxExits];
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
 
 // Element path for any vocabulary size.
 template <typename T>
-__global__ __launch_bounds__(256) void finalize_elem(int M, int64_t n, int vocab,
+__global__ __launch_bounds__(256) void finalize_elem(int M, int64_t n, int vocab, int vtile,
                                                      const int32_t* __restrict__ labels,
                                                      float alpha, float gs,
                                                      const float* __restrict__ stats,
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void finalize_elem(int M, int64_t n, int vocab
        i += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t t = i / vocab;
     const int v = static_cast<int>(i - t * vocab);
-    const int tile = v / kVocTile;
+    const int tile = v / vtile;
     const int y = labels[t];
     const bool bad = y < 0 || y >= vocab;
     const int eT = M - 1;
@@ -281,13 +281,13 @@ __global__ void clear_flags_kernel(int32_t* f) { *f = 0; }
 
 }  // namespace
 
-hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, const int32_t* labels, float alpha,
-                             const float* stats, const float* lab, float* lse, float* tokloss,
-                             hipStream_t s) {
+hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
+                             float alpha, const float* stats, const float* lab, float* lse,
+                             float* tokloss, hipStream_t s) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(loss_merge_kernel, dim3(static_cast<unsigned>((n + 63) / 64)), dim3(256), 0, s,
                      n_exits, n, vocab, labels, alpha, stats, lab, lse, tokloss,
-                     static_cast<int>(n_vocab_tiles(vocab)));
+                     (vocab + vtile - 1) / vtile);
   return hipGetLastError();
 }
 
@@ -299,43 +299,42 @@ hipError_t launch_loss_means(int n_exits, int64_t n, int vocab, const int32_t* l
 }
 
 template <typename T>
-hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const int32_t* labels, float alpha,
-                           float grad_scale, const float* stats, const float* lse,
+hipError_t launch_finalize(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
+                           float alpha, float grad_scale, const float* stats, const float* lse,
                            void* const* dlogits, hipStream_t s) {
   if (n == 0) return hipSuccess;
   constexpr int C = Elem<T>::kChunk;
   DlPtrs dl{};
   for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
-  const int n_vt = static_cast<int>(n_vocab_tiles(vocab));
+  const int n_vt = (vocab + vtile - 1) / vtile;
   if (vocab % C == 0) {
     const int64_t cpr = vocab / C;
     const int segs = static_cast<int>((cpr + 255) / 256);
     const int64_t nseg = n * segs;
     const unsigned grid = static_cast<unsigned>(nseg < 256 * 16 ? nseg : 256 * 16);
-    hipLaunchKernelGGL(finalize_vec<T>, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, labels,
-                       alpha, grad_scale, stats, lse, dl, n_vt, segs);
+    hipLaunchKernelGGL(finalize_vec<T>, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, vtile,
+                       labels, alpha, grad_scale, stats, lse, dl, n_vt, segs);
   } else {
     const int64_t total = n * vocab;
     const int64_t blocks = (total + 255) / 256;
     const unsigned grid = static_cast<unsigned>(blocks < 256 * 16 ? blocks : 256 * 16);
-    hipLaunchKernelGGL(finalize_elem<T>, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, labels,
-                       alpha, grad_scale, stats, lse, dl, n_vt);
+    hipLaunchKernelGGL(finalize_elem<T>, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, vtile,
+                       labels, alpha, grad_scale, stats, lse, dl, n_vt);
   }
   return hipGetLastError();
 }
 
-template hipError_t launch_finalize<bf16_t>(int, int64_t, int, const int32_t*, float, float,
+template hipError_t launch_finalize<bf16_t>(int, int64_t, int, int, const int32_t*, float, float,
                                             const float*, const float*, void* const*, hipStream_t);
-template hipError_t launch_finalize<float>(int, int64_t, int, const int32_t*, float, float,
+template hipError_t launch_finalize<float>(int, int64_t, int, int, const int32_t*, float, float,
                                            const float*, const float*, void* const*, hipStream_t);
 
-hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, const float* best,
+hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, int vtile, const float* best,
                                int32_t* argmax, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const int64_t total = n_exits * n;
   hipLaunchKernelGGL(argmax_merge_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
-                     dim3(256), 0, s, n_exits, n, best, argmax,
-                     static_cast<int>(n_vocab_tiles(vocab)));
+                     dim3(256), 0, s, n_exits, n, best, argmax, (vocab + vtile - 1) / vtile);
   return hipGetLastError();
 }
 

@@ -44,7 +44,8 @@ def _arr(t, *v):
 
 
 FAKE = 0x10000          # 16-byte aligned, never dereferenced (validation fails first)
-MIS = 0x10004           # misaligned
+MIS = 0x10004           # 4-byte aligned only: misaligned for tensors
+MIS4 = 0x10002          # misaligned for int32 arrays
 
 
 def test_junction_host_validation():
@@ -55,6 +56,7 @@ def test_junction_host_validation():
     assert lib.nel_junction(1, 4, 8, 16, 0, FAKE, FAKE, FAKE, FAKE, None, None) == -2
     assert lib.nel_junction(1, 4, 8, 16, 10, None, FAKE, FAKE, FAKE, None, None) == -1
     assert lib.nel_junction(1, 4, 8, 16, 10, MIS, FAKE, FAKE, FAKE, None, None) == -4
+    assert lib.nel_junction(1, 4, 8, 16, 10, FAKE, MIS4, FAKE, FAKE, None, None) == -4
     assert lib.nel_junction(1, 0, 8, 16, 10, None, None, None, None, None, None) == 0
 
 
@@ -94,7 +96,9 @@ def test_heads_and_accept_host_validation():
     need = nel.workspace_size(nel.OP_HEADS, 2, 4, 10)
     assert lib.nel_exit_heads(3, 2, 4, 10, d, p2, p2, None, FAKE, FAKE, need, None) == -3
     assert lib.nel_exit_heads(1, 2, 4, 10, d, p2, p2, None, FAKE, FAKE, need - 1, None) == -5
-    assert lib.nel_exit_heads(1, 2, 4, 10, d, p2, p2, None, MIS, FAKE, need, None) == -4
+    assert lib.nel_exit_heads(1, 2, 4, 10, d, p2, p2, None, MIS4, FAKE, need, None) == -4
+    assert lib.nel_exit_heads(1, 2, 4, 10, d, p2, p2, None, FAKE, MIS, need, None) == -4
+    assert lib.nel_accept_prefix(4, 7, 6, MIS4, FAKE, FAKE, None) == -4
     assert lib.nel_exit_heads(1, 2, 4, 0, d, p2, p2, None, FAKE, FAKE, need, None) == -2
     assert lib.nel_accept_prefix(4, 7, 8, FAKE, FAKE, FAKE, None) == -2
     assert lib.nel_accept_prefix(4, 7, -1, FAKE, FAKE, FAKE, None) == -2

@@ -148,6 +148,51 @@ nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, 
                                float* token_loss, float* mean_loss, void* const* dlogits,
                                void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * MFMA-tiled head weights.  The contraction of every exit head (copyedit of
+ * Sec. 2: sub-model m ends in its own head W^m) runs fastest when each matrix
+ * core operand is one contiguous 1 KB read, so a bf16 head W [vocab, d] may be
+ * rewritten once into the tiled layout below and then used by the *_packed
+ * entry points, which compute exactly what their row-major counterparts do.
+ * Requires dt == NEL_BF16, vocab % 32 == 0, d % 64 == 0.  The layout, for row
+ * block rb < vocab/32, column pair block kp < d/16, lane l < 64, j < 8:
+ *     packed[((rb * (d/16) + kp) * 64 + l) * 8 + j]
+ *         = w[32 rb + vperm(l % 32)][16 kp + 8 (l / 32) + j],
+ *     vperm(q) = 16 ((q >> 2) & 1) + 4 (q >> 3) + (q & 3).
+ *   w:        device bf16 [vocab, d] (input)
+ *   w_packed: device bf16, vocab * d elements (output; must not overlap w)
+ * Errors: NEL_EDTYPE unless bf16; NEL_ESHAPE if vocab or d breaks the rule
+ * above; NEL_EINVAL for NULL or overlapping buffers; NEL_EALIGN below 16 bytes.
+ */
+nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* w,
+                            void* w_packed, void* stream);
+
+/*
+ * nel_matryoshka_loss with every w[e] in the tiled layout of
+ * nel_pack_weights.  Same arguments, outputs and errors, plus: dt must be
+ * NEL_BF16 (NEL_EDTYPE), vocab % 32 == 0 and every d[e] % 64 == 0
+ * (NEL_ESHAPE), and dlogits must be given (NEL_EINVAL): between the head GEMM
+ * and the final gradient pass the teacher's dlogits buffer holds the
+ * teacher's softmax weights exp(l_M - m) (m its 256-entry tile maximum) in
+ * fp16, which the smaller exits' tiles read back.  Every dlogits buffer is
+ * scratch until the call's work on `stream` has completed.
+ */
+nel_status nel_matryoshka_loss_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens,
+                                      int32_t vocab, const int32_t* d, const void* const* h,
+                                      const void* const* w_packed, const int32_t* labels,
+                                      float alpha_d, float grad_scale, float* token_loss,
+                                      float* mean_loss, void* const* dlogits, void* workspace,
+                                      size_t ws_bytes, void* stream);
+
+/*
+ * nel_exit_heads with every w[e] in the tiled layout of nel_pack_weights
+ * (dt NEL_BF16, vocab % 32 == 0, every d[e] % 64 == 0; same outputs and errors).
+ */
+nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                                 const int32_t* d, const void* const* h,
+                                 const void* const* w_packed, float* const* logits,
+                                 int32_t* argmax, void* workspace, size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace an op needs (0 on bad arguments). */
 size_t nel_workspace_size(int32_t op, int32_t n_exits, int64_t n_tokens, int32_t vocab);
 
@@ -160,17 +205,22 @@ nel_status nel_clear_device_flags(int32_t* dev_flags, void* stream);
 /* Static text for a status code. */
 const char* nel_status_string(nel_status s);
 
+/* Name of the HIP error behind the calling thread's most recent NEL_EHIP
+ * ("none" if there was none); static storage. */
+const char* nel_last_hip_error(void);
+
 /*
  * Measurement hooks.  While enabled, every kernel launch is bracketed by a
  * pair of hipEvents recorded on the stream it is launched on, and
  * nel_timing_read sums their elapsed times per kernel.  Kernel ids:
  * 0 junction, 1 heads+loss statistics GEMM, 2 loss merge, 3 means,
- * 4 dlogits finalize, 5 heads+argmax GEMM, 6 argmax merge, 7 accept.
+ * 4 dlogits finalize, 5 heads+argmax GEMM, 6 argmax merge, 7 accept,
+ * 8 weight packing.
  * Process-global and not thread-safe: for benchmarks only.
  */
 enum { NEL_K_JUNCTION = 0, NEL_K_HEADS_LOSS = 1, NEL_K_MERGE = 2, NEL_K_MEANS = 3,
        NEL_K_FINALIZE = 4, NEL_K_HEADS_ARGMAX = 5, NEL_K_ARGMAX_MERGE = 6,
-       NEL_K_ACCEPT = 7, NEL_K_COUNT = 8 };
+       NEL_K_ACCEPT = 7, NEL_K_PACK = 8, NEL_K_COUNT = 9 };
 nel_status nel_timing_enable(int32_t on);
 /* Synchronises the device, then returns the summed milliseconds and the
  * number of timed launches of `kernel` since the last reset. */

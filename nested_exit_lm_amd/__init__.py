@@ -10,6 +10,8 @@ call raises.
     accept_prefix(draft_argmax, verify_argmax, draft_len) -> accepted
     matryoshka_loss(hs, ws, labels, alpha_d, grad_scale, want_dlogits)
                                                -> (mean_loss, token_loss, dlogits)
+    pack_weights(w)                            -> w in the MFMA-tiled layout (bf16)
+    matryoshka_loss_packed / exit_heads_packed -> as above, on packed weights
 """
 from __future__ import annotations
 
@@ -21,7 +23,7 @@ __all__ = [
     "NelError", "load", "lib_path", "junction", "exit_heads", "accept_prefix", "matryoshka_loss",
     "workspace_size", "read_flags", "clear_flags", "status_string", "timing_enable",
     "timing_read", "timing_reset", "KERNELS", "OP_LOSS", "OP_HEADS", "FLAG_BAD_ID",
-    "FLAG_BAD_LABEL", "Workspace",
+    "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +34,7 @@ OP_LOSS, OP_HEADS = 0, 1
 FLAG_BAD_ID, FLAG_BAD_LABEL = 1, 2
 MAX_EXITS = 8
 KERNELS = ["junction", "heads_loss", "merge", "means", "finalize", "heads_argmax",
-           "argmax_merge", "accept"]
+           "argmax_merge", "accept", "pack"]
 
 
 def lib_path() -> str:
@@ -43,25 +45,50 @@ class NelError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         msg = status_string(status) if _LIB is not None else str(status)
+        if status == -6 and _LIB is not None:
+            msg += " " + _LIB.nel_last_hip_error().decode()
         super().__init__(f"{where}: {msg} ({status})")
 
 
+def _hip_runtimes() -> set:
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {l.split()[-1] for l in f if "libamdhip64" in l}
+    except OSError:
+        return set()
+
+
 def load():
-    """Load libnel.so (raises if it has not been built)."""
+    """Load libnel.so (raises if it has not been built).
+
+    PyTorch is imported first: it carries its own HIP runtime under the same
+    soname, and loading it first makes libnel.so bind to that one.  Two HIP
+    runtimes in one process would own different streams and device state, so
+    that case is refused."""
     global _LIB
     if _LIB is not None:
         return _LIB
     p = lib_path()
     if not os.path.exists(p):
         raise ImportError(f"{p} is missing; build it with `python -m nested_exit_lm_amd.build`")
+    import torch  # noqa: F401  (binds the HIP runtime before libnel.so loads)
     lib = ctypes.CDLL(p)
+    rts = _hip_runtimes()
+    if len(rts) > 1:
+        raise ImportError("two HIP runtimes are loaded (" + ", ".join(sorted(rts)) + "); "
+                          "import torch before any other HIP library")
     c_int, c_i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     sig = {
         "nel_junction": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp],
         "nel_exit_heads": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
+        "nel_exit_heads_packed": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
+        "nel_pack_weights": [c_int, c_int, c_int, vp, vp, vp],
         "nel_accept_prefix": [c_int, c_int, c_int, vp, vp, vp, vp],
         "nel_matryoshka_loss": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, ctypes.c_float,
                                 ctypes.c_float, vp, vp, vp, vp, sz, vp],
+        "nel_matryoshka_loss_packed": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, ctypes.c_float,
+                                       ctypes.c_float, vp, vp, vp, vp, sz, vp],
         "nel_workspace_size": [c_int, c_int, c_i64, c_int],
         "nel_read_device_flags": [vp, vp, vp],
         "nel_clear_device_flags": [vp, vp],
@@ -76,6 +103,8 @@ def load():
         f.restype = c_int
     lib.nel_workspace_size.restype = sz
     lib.nel_status_string.restype = ctypes.c_char_p
+    lib.nel_last_hip_error.argtypes = []
+    lib.nel_last_hip_error.restype = ctypes.c_char_p
     _LIB = lib
     return lib
 
@@ -176,6 +205,16 @@ def junction(h, ids, emb, out=None, flags=None):
 def exit_heads(hs: Sequence, ws: Sequence, want_logits: bool = False, want_argmax: bool = True,
                workspace=None):
     """Logits (fp32, optional) and greedy argmax [n_exits, n] (int32) of each exit's head."""
+    return _exit_heads(False, hs, ws, want_logits, want_argmax, workspace)
+
+
+def exit_heads_packed(hs: Sequence, ws_packed: Sequence, want_logits: bool = False,
+                      want_argmax: bool = True, workspace=None):
+    """exit_heads on head weights from pack_weights (bf16, V % 32 == 0, every d % 64 == 0)."""
+    return _exit_heads(True, hs, ws_packed, want_logits, want_argmax, workspace)
+
+
+def _exit_heads(packed, hs, ws, want_logits, want_argmax, workspace):
     torch = _torch()
     E = len(hs)
     if E != len(ws) or not 1 <= E <= MAX_EXITS:
@@ -194,10 +233,10 @@ def exit_heads(hs: Sequence, ws: Sequence, want_logits: bool = False, want_argma
     need = workspace_size(OP_HEADS, E, n, V)
     wsb = workspace if workspace is not None else _workspace(OP_HEADS, device, need)
     lib = load()
-    _check(lib.nel_exit_heads(dt, E, n, V, d, _ptrs(hs), _ptrs(ws),
-                              _ptrs(logits) if logits is not None else None,
-                              _dev(am, device, "argmax"), wsb.data_ptr(), wsb.numel(),
-                              _stream(device)), "nel_exit_heads")
+    fn, name = ((lib.nel_exit_heads_packed, "nel_exit_heads_packed") if packed
+                else (lib.nel_exit_heads, "nel_exit_heads"))
+    _check(fn(dt, E, n, V, d, _ptrs(hs), _ptrs(ws), _ptrs(logits) if logits is not None else None,
+              _dev(am, device, "argmax"), wsb.data_ptr(), wsb.numel(), _stream(device)), name)
     return logits, am
 
 
@@ -227,6 +266,22 @@ def matryoshka_loss(hs: Sequence, ws: Sequence, labels, alpha_d: float = 0.3,
 
     Returns (mean_loss [3M+1] fp32, token_loss [M, 3, n] fp32 | None, dlogits list | None);
     mean_loss = (CE_1..CE_M, Dist_1..Dist_M, L_1..L_M, total)."""
+    return _loss(False, hs, ws, labels, alpha_d, grad_scale, want_dlogits, want_token_loss,
+                 dlogits, workspace, mean_loss, token_loss)
+
+
+def matryoshka_loss_packed(hs: Sequence, ws_packed: Sequence, labels, alpha_d: float = 0.3,
+                           grad_scale: float = 1.0, want_token_loss: bool = True,
+                           dlogits: Optional[List] = None, workspace=None, mean_loss=None,
+                           token_loss=None):
+    """matryoshka_loss on head weights from pack_weights (bf16, V % 32 == 0, every
+    d % 64 == 0); the logit gradients are always produced."""
+    return _loss(True, hs, ws_packed, labels, alpha_d, grad_scale, True, want_token_loss,
+                 dlogits, workspace, mean_loss, token_loss)
+
+
+def _loss(packed, hs, ws, labels, alpha_d, grad_scale, want_dlogits, want_token_loss, dlogits,
+          workspace, mean_loss, token_loss):
     torch = _torch()
     E = len(hs)
     if E != len(ws) or not 1 <= E <= MAX_EXITS:
@@ -255,14 +310,31 @@ def matryoshka_loss(hs: Sequence, ws: Sequence, labels, alpha_d: float = 0.3,
     need = workspace_size(OP_LOSS, E, n, V)
     wsb = workspace if workspace is not None else _workspace(OP_LOSS, device, need)
     lib = load()
-    _check(lib.nel_matryoshka_loss(dt, E, n, V, d, _ptrs(hs), _ptrs(ws),
-                                   _dev(labels, device, "labels"), float(alpha_d),
-                                   float(grad_scale), _dev(token_loss, device, "token_loss"),
-                                   _dev(mean_loss, device, "mean_loss"),
-                                   _ptrs(dlogits) if dlogits is not None else None,
-                                   wsb.data_ptr(), wsb.numel(), _stream(device)),
-           "nel_matryoshka_loss")
+    fn, name = ((lib.nel_matryoshka_loss_packed, "nel_matryoshka_loss_packed") if packed
+                else (lib.nel_matryoshka_loss, "nel_matryoshka_loss"))
+    _check(fn(dt, E, n, V, d, _ptrs(hs), _ptrs(ws), _dev(labels, device, "labels"),
+              float(alpha_d), float(grad_scale), _dev(token_loss, device, "token_loss"),
+              _dev(mean_loss, device, "mean_loss"),
+              _ptrs(dlogits) if dlogits is not None else None, wsb.data_ptr(), wsb.numel(),
+              _stream(device)), name)
     return mean_loss, token_loss, dlogits
+
+
+def pack_weights(w, out=None):
+    """Rewrite a bf16 head weight [V, d] (V % 32 == 0, d % 64 == 0) into the MFMA-tiled layout
+    the *_packed entry points read.  The result has w's shape and dtype; its element order is
+    the tiled one, so it is only meaningful to those entry points."""
+    torch = _torch()
+    if w.dim() != 2 or w.dtype != torch.bfloat16:
+        raise ValueError("w must be a 2-D bfloat16 tensor")
+    device = w.device
+    if out is None:
+        out = torch.empty_like(w)
+    elif out.shape != w.shape or out.dtype != w.dtype:
+        raise ValueError("out must match w's shape and dtype")
+    _check(load().nel_pack_weights(BF16, w.shape[0], w.shape[1], _dev(w, device, "w"),
+                                   _dev(out, device, "out"), _stream(device)), "nel_pack_weights")
+    return out
 
 
 def loss_workspace(device, n_exits: int, n_tokens: int, vocab: int):

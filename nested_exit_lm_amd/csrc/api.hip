@@ -38,25 +38,40 @@ Timing& timing() {
 }
 
 // Brackets one launch with events on its stream when timing is enabled.
+// Every launch goes through here.  hipGetLastError reports the last error of
+// any runtime call on this thread, including calls other libraries made and
+// ignored; it is cleared first so that a launch reports only its own error.
 template <typename F>
 hipError_t timed(int k, hipStream_t s, F&& launch) {
+  (void)hipGetLastError();
   Timing& T = timing();
   if (!T.on) return launch();
   hipEvent_t a, b;
   if (hipEventCreate(&a) != hipSuccess) return hipErrorUnknown;
   if (hipEventCreate(&b) != hipSuccess) {
-    hipEventDestroy(a);
+    (void)hipEventDestroy(a);
     return hipErrorUnknown;
   }
-  hipEventRecord(a, s);
-  const hipError_t err = launch();
-  hipEventRecord(b, s);
+  if (hipEventRecord(a, s) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    return hipErrorUnknown;
+  }
+  hipError_t err = launch();
+  if (hipEventRecord(b, s) != hipSuccess && err == hipSuccess) err = hipErrorUnknown;
   std::lock_guard<std::mutex> g(T.mu);
   T.pending.push_back({k, a, b});
   return err;
 }
 
-nel_status from_hip(hipError_t e) { return e == hipSuccess ? NEL_OK : NEL_EHIP; }
+// The HIP error behind this thread's most recent NEL_EHIP.
+thread_local hipError_t g_last_hip = hipSuccess;
+
+nel_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return NEL_OK;
+  g_last_hip = e;
+  return NEL_EHIP;
+}
 
 nel_status check_exits(int32_t n_exits, int64_t n, const int32_t* d, const void* const* h,
                        const void* const* w, bool strict) {
@@ -79,6 +94,10 @@ bool grid_fits(int64_t n, int32_t vocab) {
 }  // namespace
 
 extern "C" {
+
+const char* nel_last_hip_error(void) {
+  return g_last_hip == hipSuccess ? "none" : hipGetErrorName(g_last_hip);
+}
 
 const char* nel_status_string(nel_status s) {
   switch (s) {
@@ -117,14 +136,36 @@ nel_status nel_junction(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_
   }));
 }
 
-nel_status nel_exit_heads(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
-                          const int32_t* d, const void* const* h, const void* const* w,
-                          float* const* logits, int32_t* argmax, void* workspace,
-                          size_t ws_bytes, void* stream) {
+nel_status nel_accept_prefix(int32_t batch, int32_t positions, int32_t draft_len,
+                             const int32_t* draft_argmax, const int32_t* verify_argmax,
+                             int32_t* accepted, void* stream) {
+  if (batch < 0 || positions < 1 || draft_len < 0 || draft_len > positions) return NEL_ESHAPE;
+  if (batch > 0 && (!draft_argmax || !verify_argmax || !accepted)) return NEL_EINVAL;
+  if (misaligned4(draft_argmax) || misaligned4(verify_argmax) || misaligned4(accepted))
+    return NEL_EALIGN;
+  if (batch == 0) return NEL_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(timed(NEL_K_ACCEPT, s, [&] {
+    return launch_accept(batch, positions, draft_len, draft_argmax, verify_argmax, accepted, s);
+  }));
+}
+
+}  // extern "C"
+
+namespace {
+
+nel_status exit_heads_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_tokens,
+                           int32_t vocab, const int32_t* d, const void* const* h,
+                           const void* const* w, float* const* logits, int32_t* argmax,
+                           void* workspace, size_t ws_bytes, void* stream) {
   if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
+  if (packed && dt != NEL_BF16) return NEL_EDTYPE;
   if (n_tokens < 0 || vocab < 1) return NEL_ESHAPE;
   nel_status st = check_exits(n_exits, n_tokens, d, h, w, /*strict=*/false);
   if (st != NEL_OK) return st;
+  if (packed)
+    for (int e = 0; e < n_exits; ++e)
+      if (!packed_shape_ok(vocab, d[e])) return NEL_ESHAPE;
   if (!grid_fits(n_tokens, vocab)) return NEL_ESHAPE;
   if (logits)
     for (int e = 0; e < n_exits; ++e) {
@@ -145,44 +186,37 @@ nel_status nel_exit_heads(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32
   }
   char* ws = static_cast<char*>(workspace);
   float* best = reinterpret_cast<float*>(ws + L.best);
-  int vtile = kVocTile;
+  TileInfo info;
   hipError_t err = timed(NEL_K_HEADS_ARGMAX, s, [&] {
+    if (packed) return launch_heads_argmax_packed(n_exits, n_tokens, vocab, ex, best, &info, s);
     return dt == NEL_BF16
-               ? launch_heads_argmax<bf16_t>(n_exits, n_tokens, vocab, ex, best, &vtile, s)
-               : launch_heads_argmax<float>(n_exits, n_tokens, vocab, ex, best, &vtile, s);
+               ? launch_heads_argmax<bf16_t>(n_exits, n_tokens, vocab, ex, best, &info, s)
+               : launch_heads_argmax<float>(n_exits, n_tokens, vocab, ex, best, &info, s);
   });
-  if (err != hipSuccess) return NEL_EHIP;
+  if (err != hipSuccess) return from_hip(err);
   if (argmax) {
     err = timed(NEL_K_ARGMAX_MERGE, s, [&] {
-      return launch_argmax_merge(n_exits, n_tokens, vocab, vtile, best, argmax, s);
+      return launch_argmax_merge(n_exits, n_tokens, vocab, info.vtile, best, argmax, s);
     });
   }
   return from_hip(err);
 }
 
-nel_status nel_accept_prefix(int32_t batch, int32_t positions, int32_t draft_len,
-                             const int32_t* draft_argmax, const int32_t* verify_argmax,
-                             int32_t* accepted, void* stream) {
-  if (batch < 0 || positions < 1 || draft_len < 0 || draft_len > positions) return NEL_ESHAPE;
-  if (batch > 0 && (!draft_argmax || !verify_argmax || !accepted)) return NEL_EINVAL;
-  if (misaligned4(draft_argmax) || misaligned4(verify_argmax) || misaligned4(accepted))
-    return NEL_EALIGN;
-  if (batch == 0) return NEL_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip(timed(NEL_K_ACCEPT, s, [&] {
-    return launch_accept(batch, positions, draft_len, draft_argmax, verify_argmax, accepted, s);
-  }));
-}
-
-nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
-                               const int32_t* d, const void* const* h, const void* const* w,
-                               const int32_t* labels, float alpha_d, float grad_scale,
-                               float* token_loss, float* mean_loss, void* const* dlogits,
-                               void* workspace, size_t ws_bytes, void* stream) {
+nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                     const int32_t* d, const void* const* h, const void* const* w,
+                     const int32_t* labels, float alpha_d, float grad_scale, float* token_loss,
+                     float* mean_loss, void* const* dlogits, void* workspace, size_t ws_bytes,
+                     void* stream) {
   if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
+  if (packed && dt != NEL_BF16) return NEL_EDTYPE;
   if (n_tokens < 0 || vocab < 1) return NEL_ESHAPE;
   nel_status st = check_exits(n_exits, n_tokens, d, h, w, /*strict=*/true);
   if (st != NEL_OK) return st;
+  if (packed) {
+    for (int e = 0; e < n_exits; ++e)
+      if (!packed_shape_ok(vocab, d[e])) return NEL_ESHAPE;
+    if (!dlogits) return NEL_EINVAL;   // the teacher's buffer carries its weights
+  }
   if (!(alpha_d >= 0.f && alpha_d <= 1.f) || !isfinite(grad_scale)) return NEL_EINVAL;
   if (!grid_fits(n_tokens, vocab)) return NEL_ESHAPE;
   if (!mean_loss || (n_tokens > 0 && !labels)) return NEL_EINVAL;
@@ -211,46 +245,102 @@ nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, 
     ex.out[e] = dlogits ? dlogits[e] : nullptr;
     ex.d[e] = d[e];
   }
-  int vtile = kVocTile;
+  TileInfo info;
   hipError_t err = timed(NEL_K_HEADS_LOSS, s, [&] {
+    if (packed)
+      return launch_heads_loss_packed(n_exits, n_tokens, vocab, ex, labels, stats, lab, &info, s);
     return dt == NEL_BF16 ? launch_heads_loss<bf16_t>(n_exits, n_tokens, vocab, ex, labels, stats,
-                                                      lab, &vtile, s)
+                                                      lab, &info, s)
                           : launch_heads_loss<float>(n_exits, n_tokens, vocab, ex, labels, stats,
-                                                     lab, &vtile, s);
+                                                     lab, &info, s);
   });
-  if (err != hipSuccess) return NEL_EHIP;
+  if (err != hipSuccess) return from_hip(err);
   err = timed(NEL_K_MERGE, s, [&] {
-    return launch_loss_merge(n_exits, n_tokens, vocab, vtile, labels, alpha_d, stats, lab, lse, tl,
+    return launch_loss_merge(n_exits, n_tokens, vocab, info.vtile, labels, alpha_d, stats, lab, lse, tl,
                              s);
   });
-  if (err != hipSuccess) return NEL_EHIP;
+  if (err != hipSuccess) return from_hip(err);
   err = timed(NEL_K_MEANS, s, [&] {
     return launch_loss_means(n_exits, n_tokens, vocab, labels, tl, mean_loss, flags, s);
   });
-  if (err != hipSuccess) return NEL_EHIP;
+  if (err != hipSuccess) return from_hip(err);
   if (dlogits && n_tokens > 0) {
     err = timed(NEL_K_FINALIZE, s, [&] {
-      return dt == NEL_BF16 ? launch_finalize<bf16_t>(n_exits, n_tokens, vocab, vtile, labels,
+      return dt == NEL_BF16 ? launch_finalize<bf16_t>(n_exits, n_tokens, vocab, info, labels,
                                                       alpha_d, grad_scale, stats, lse, dlogits, s)
-                            : launch_finalize<float>(n_exits, n_tokens, vocab, vtile, labels,
+                            : launch_finalize<float>(n_exits, n_tokens, vocab, info, labels,
                                                      alpha_d, grad_scale, stats, lse, dlogits, s);
     });
   }
   return from_hip(err);
 }
 
+}  // namespace
+
+extern "C" {
+
+nel_status nel_exit_heads(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                          const int32_t* d, const void* const* h, const void* const* w,
+                          float* const* logits, int32_t* argmax, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  return exit_heads_impl(false, dt, n_exits, n_tokens, vocab, d, h, w, logits, argmax, workspace,
+                         ws_bytes, stream);
+}
+
+nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                                 const int32_t* d, const void* const* h,
+                                 const void* const* w_packed, float* const* logits,
+                                 int32_t* argmax, void* workspace, size_t ws_bytes, void* stream) {
+  return exit_heads_impl(true, dt, n_exits, n_tokens, vocab, d, h, w_packed, logits, argmax,
+                         workspace, ws_bytes, stream);
+}
+
+nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                               const int32_t* d, const void* const* h, const void* const* w,
+                               const int32_t* labels, float alpha_d, float grad_scale,
+                               float* token_loss, float* mean_loss, void* const* dlogits,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  return loss_impl(false, dt, n_exits, n_tokens, vocab, d, h, w, labels, alpha_d, grad_scale,
+                   token_loss, mean_loss, dlogits, workspace, ws_bytes, stream);
+}
+
+nel_status nel_matryoshka_loss_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens,
+                                      int32_t vocab, const int32_t* d, const void* const* h,
+                                      const void* const* w_packed, const int32_t* labels,
+                                      float alpha_d, float grad_scale, float* token_loss,
+                                      float* mean_loss, void* const* dlogits, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+  return loss_impl(true, dt, n_exits, n_tokens, vocab, d, h, w_packed, labels, alpha_d,
+                   grad_scale, token_loss, mean_loss, dlogits, workspace, ws_bytes, stream);
+}
+
+nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* w, void* w_packed,
+                            void* stream) {
+  if (dt != NEL_BF16) return NEL_EDTYPE;
+  if (!packed_shape_ok(vocab, d)) return NEL_ESHAPE;
+  if (!w || !w_packed) return NEL_EINVAL;
+  if (misaligned(w) || misaligned(w_packed)) return NEL_EALIGN;
+  const char* a = static_cast<const char*>(w);
+  const char* b = static_cast<const char*>(w_packed);
+  const size_t bytes = static_cast<size_t>(vocab) * d * 2;
+  if (a < b + bytes && b < a + bytes) return NEL_EINVAL;   // overlapping buffers
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(timed(NEL_K_PACK, s, [&] { return launch_pack_weights(vocab, d, w, w_packed, s); }));
+}
+
 nel_status nel_read_device_flags(const int32_t* dev_flags, int32_t* host_flags, void* stream) {
   if (!dev_flags || !host_flags) return NEL_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(host_flags, dev_flags, sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
-      hipSuccess)
-    return NEL_EHIP;
+  const hipError_t e = hipMemcpyAsync(host_flags, dev_flags, sizeof(int32_t),
+                                      hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return from_hip(e);
   return from_hip(hipStreamSynchronize(s));
 }
 
 nel_status nel_clear_device_flags(int32_t* dev_flags, void* stream) {
   if (!dev_flags) return NEL_EINVAL;
   if (misaligned4(dev_flags)) return NEL_EALIGN;
+  (void)hipGetLastError();
   return from_hip(launch_clear_flags(dev_flags, static_cast<hipStream_t>(stream)));
 }
 
@@ -263,9 +353,9 @@ nel_status nel_timing_reset(void) {
   Timing& T = timing();
   std::lock_guard<std::mutex> g(T.mu);
   for (auto& p : T.pending) {
-    hipEventSynchronize(p.b);
-    hipEventDestroy(p.a);
-    hipEventDestroy(p.b);
+    (void)hipEventSynchronize(p.b);
+    (void)hipEventDestroy(p.a);
+    (void)hipEventDestroy(p.b);
   }
   T.pending.clear();
   for (int k = 0; k < NEL_K_COUNT; ++k) {
@@ -282,12 +372,13 @@ nel_status nel_timing_read(int32_t kernel, double* total_ms, int64_t* launches) 
   nel_status st = NEL_OK;
   for (auto& p : T.pending) {
     float ms = 0.f;
-    if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess)
-      st = NEL_EHIP;
+    hipError_t e = hipEventSynchronize(p.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.a, p.b);
+    if (e != hipSuccess) st = from_hip(e);
     T.total_ms[p.k] += ms;
     T.launches[p.k] += 1;
-    hipEventDestroy(p.a);
-    hipEventDestroy(p.b);
+    (void)hipEventDestroy(p.a);
+    (void)hipEventDestroy(p.b);
   }
   T.pending.clear();
   *total_ms = T.total_ms[kernel];

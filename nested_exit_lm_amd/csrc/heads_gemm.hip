@@ -32,80 +32,38 @@
 // chunk swizzle chosen so that every 16-lane pass of a 16-byte LDS access
 // touches all 64 banks once.
 //
-// Two kernels share the epilogues:
-//  * big (bf16, every width a multiple of 64): one wavefront per SIMD with
-//    the full register file, wavefront tile 64 tokens x 128 vocabulary,
-//    workgroup tile 128 x 256.  Global loads run three K steps ahead of the
-//    MFMAs through three register staging sets (the load latency of the
-//    memory system is several times one K step), into two LDS stages;
-//  * generic (any shape, bf16 or fp32): wavefront tile 64 x 64, workgroup
-//    128 x 128, two workgroups per CU, one K step of prefetch, zero fill at
-//    every edge.
+// Wavefront tile 64 x 64, workgroup 128 x 128, two workgroups per CU, one K
+// step of register prefetch into two LDS stages, zero fill at every edge, so
+// any width and vocabulary size is accepted.  (bf16 weights in the MFMA-tiled
+// layout take the faster kernel in heads_packed.hip.)
 #include <limits.h>
 
 #include "common.h"
 #include "internal.h"
+#include "tiles.h"
 
 namespace nel {
 
 namespace {
 
 constexpr int kRowBytes = 128;           // LDS row: 8 chunks of 16 bytes
-constexpr float kMasked = -1.0e30f;      // logit of a vocabulary entry beyond V
-
-enum { kModeLoss = 0, kModeArgmax = 1 };
 
 template <typename T> struct KStep;
 template <> struct KStep<bf16_t> { static constexpr int v = 64; };   // 64 bf16 = 128 bytes
 template <> struct KStep<float> { static constexpr int v = 32; };    // 32 fp32 = 128 bytes
 
-// generic kernel: wavefront 64 x 64 (2 x 2 blocks), workgroup 128 x 128
+// wavefront 64 x 64 (2 x 2 blocks), workgroup 128 x 128
 constexpr int kGenThreads = 256;
 constexpr int kGenTok = 128;
 constexpr int kGenVoc = 128;
 constexpr int kGenStage = (kGenVoc + kGenTok) * kRowBytes;           // 32 KB
-// big kernel: wavefront 64 x 128 (2 x 4 blocks), workgroup 128 x 256
-constexpr int kBigThreads = 256;
-constexpr int kBigTok = 128;
-constexpr int kBigVoc = 256;
-constexpr int kBigStage = (kBigVoc + kBigTok) * kRowBytes;           // 48 KB
-constexpr int kBigChunks = kBigStage / 16 / kBigThreads;             // 16-byte loads per thread per stage
-constexpr int kBigDepth = 3;                                         // register staging sets
-
-// Tile order: workgroups resident on one XCD take `group` token tiles x
-// (resident / group) vocabulary tiles.
-#ifndef NEL_BIG_GROUP
-#define NEL_BIG_GROUP 8
-#endif
-constexpr int kGroupBig = NEL_BIG_GROUP;
 constexpr int kGroupGen = 8;
 
-// A-row q of a 32-row MFMA block holds vocabulary entry vperm(q), chosen so
-// that accumulator register r of lane half h is vocabulary entry 16h + r.
-__device__ __forceinline__ int vperm(int q) { return ((q >> 2) & 1) * 16 + (q >> 3) * 4 + (q & 3); }
 // Chunk swizzles (row r's logical chunk c sits at physical chunk c ^ swz(r)).
 // The bank group of a 16-byte access is (row parity, physical chunk); the
 // swizzles give distinct groups to the rows any 16 consecutive lanes read.
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) & 3) | ((r >> 2) & 4); }
 __device__ __forceinline__ int swz_b(int r) { return (r >> 1) & 7; }
-
-// Workgroup id -> (token tile, vocabulary tile).  Consecutive ids are spread
-// over the 8 XCDs, so ids are first regrouped per XCD; each XCD then walks
-// groups of `group` token tiles across the vocabulary, so the workgroups
-// resident on one XCD share a few token and vocabulary operand panels in its L2.
-__device__ __forceinline__ void tile_coords(int bid, int n_tt, int n_vt, int group, int& tt,
-                                            int& vt) {
-  const int G = n_tt * n_vt;
-  int L = bid;
-  if ((G & 7) == 0) L = (bid & 7) * (G >> 3) + (bid >> 3);
-  const int per_group = group * n_vt;
-  const int g = L / per_group;
-  const int first = g * group;
-  const int gs = min(n_tt - first, group);
-  const int r = L - g * per_group;
-  tt = first + r % gs;
-  vt = r / gs;
-}
 
 // Per-lane coordinates inside the accumulator tile of one wavefront.
 template <int NTB, int NVB>
@@ -234,10 +192,8 @@ __device__ __forceinline__ void mask_tail(f32x16 (&acc)[NTB][NVB], const LaneMap
         if (L.vbase[vb] + r >= vocab) acc[tb][vb][r] = kMasked;
 }
 
-// Teacher weights w = exp(l_M - m_M) in (0, 1], kept between the teacher's
-// epilogue and the smaller exits' ones: fp32, or packed fp16 pairs (relative
-// rounding 2^-11, which moves the teacher-weighted logit mean by at most
-// 2^-11 times the spread of the logits) where registers are short.
+// Teacher weights w = exp(l_M - m_M) in (0, 1], kept in registers between the
+// teacher's epilogue and the smaller exits' ones.
 template <int NTB, int NVB>
 struct TeacherW32 {
   float v[NTB][NVB][16];
@@ -250,21 +206,6 @@ struct TeacherW32 {
     x1 = v[tb][vb][r + 1];
   }
 };
-template <int NTB, int NVB>
-struct TeacherW16 {
-  typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
-  uint32_t v[NTB][NVB][8];
-  __device__ __forceinline__ void set2(int tb, int vb, int r, float x0, float x1) {
-    const half2_t h = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
-    v[tb][vb][r >> 1] = __builtin_bit_cast(uint32_t, h);
-  }
-  __device__ __forceinline__ void get2(int tb, int vb, int r, float& x0, float& x1) const {
-    const half2_t h = __builtin_bit_cast(half2_t, v[tb][vb][r >> 1]);
-    x0 = static_cast<float>(h[0]);
-    x1 = static_cast<float>(h[1]);
-  }
-};
-
 // ---------------------------------------------------------------------------
 // Loss epilogue for exit e.  Two wavefront rows (wt) of NTB x 32 tokens; the
 // two vocabulary wavefronts (wv) of a row are combined through LDS.  `vt` is
@@ -574,159 +515,12 @@ __global__ __launch_bounds__(kGenThreads, 2) void heads_kernel_generic(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Big kernel (bf16; every width a multiple of 64; V a multiple of 8).
-//
-// K steps of all exits form one sequence.  Every exit's steps are padded to
-// a multiple of kBigDepth with "phantom" steps (they load and stage a real
-// slice, the exit's last, and compute nothing) so that the register staging
-// set of a step is fixed by its position in the unrolled loop body and an
-// exit always ends at the end of a loop iteration.  At step g a wavefront
-// loads stage g + 3 into register set g % 3, writes set (g + 1) % 3 (stage
-// g + 1, loaded two steps earlier) into LDS stage (g + 1) % 2, and computes
-// LDS stage g % 2; rows beyond the matrix are clamped to its last row
-// (finite values whose results are masked or never stored).
-template <int MODE>
-__global__ __launch_bounds__(kBigThreads, 1) void heads_kernel_big(
-    ExitSet /*read through the kernarg pointer*/, int n_exits, int64_t n, int vocab,
-    const int32_t* __restrict__ labels, float* __restrict__ stats, float* __restrict__ lab,
-    int n_tt, int n_vt) {
-  const ExitSet& ex = *(const ExitSet*)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int BK = 64;
-  constexpr int NTB = 2, NVB = 4;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBigStage];
-  __shared__ float xmax[2][2][NTB * 32];
-  __shared__ float xsum[2][2][NTB * 32][2];
-
-  const int tid = threadIdx.x;
-  int tt, vt;
-  tile_coords(blockIdx.x, n_tt, n_vt, kGroupBig, tt, vt);
-  const int64_t t0 = static_cast<int64_t>(tt) * kBigTok;
-  const int v0 = vt * kBigVoc;
-  const auto L = lane_map<NTB, NVB>(tid, t0, v0, n, labels, MODE == kModeLoss);
-  int a_row[NVB], a_x[NVB], b_row[NTB], b_x[NTB];
-  operand_offsets(L, kBigVoc * kRowBytes, a_row, a_x, b_row, b_x);
-
-  auto exit_at = [&](int ei) {
-    return (MODE == kModeLoss) ? (ei == 0 ? n_exits - 1 : ei - 1) : ei;
-  };
-  auto steps_of = [&](int ei) { return ex.d[exit_at(ei)] / BK; };
-  auto padded = [&](int ei) { return (steps_of(ei) + kBigDepth - 1) / kBigDepth * kBigDepth; };
-
-  // Stage cursor for loads: exit position and step within its padded steps.
-  // Chunk j of a thread is chunk id qd = tid + 256 j of the stage: ids below
-  // 8 * kBigVoc are W rows qd / 8, the rest H rows; qd % 8 is the chunk.
-  int ld_ei = 0, ld_j = 0;
-  auto gload = [&](u32x4 (&R)[kBigChunks]) {
-    const int ei = ld_ei < n_exits ? ld_ei : n_exits - 1;
-    const int e = exit_at(ei);
-    const int D = ex.d[e];
-    const int s = D / BK;
-    const int k0 = (ld_ei < n_exits ? min(ld_j, s - 1) : s - 1) * BK;
-    const bf16_t* __restrict__ W = static_cast<const bf16_t*>(ex.w[e]);
-    const bf16_t* __restrict__ H = static_cast<const bf16_t*>(ex.h[e]);
-#pragma unroll
-    for (int j = 0; j < kBigChunks; ++j) {
-      const int qd = tid + kBigThreads * j;   // compile-time split: j < 8 -> W, else H
-      const int c = qd & 7;
-      const bf16_t* src;
-      if (j < kBigVoc * 8 / kBigThreads) {
-        const int64_t g = min(v0 + (qd >> 3), vocab - 1);
-        src = W + g * D + k0 + c * 8;
-      } else {
-        const int r = (qd - kBigVoc * 8) >> 3;
-        const int64_t g = t0 + r < n ? t0 + r : n - 1;
-        src = H + g * D + k0 + c * 8;
-      }
-      R[j] = *reinterpret_cast<const u32x4*>(src);
-    }
-    if (ld_ei < n_exits && ++ld_j == padded(ld_ei)) {
-      ld_j = 0;
-      ++ld_ei;
-    }
-  };
-  auto sstore = [&](const u32x4 (&R)[kBigChunks], int buf) {
-    uint8_t* S = lds + buf * kBigStage;
-#pragma unroll
-    for (int j = 0; j < kBigChunks; ++j) {
-      const int qd = tid + kBigThreads * j;
-      const int c = qd & 7;
-      int off;
-      if (j < kBigVoc * 8 / kBigThreads) {
-        const int row = qd >> 3;
-        off = row * kRowBytes + ((c ^ swz_a(row)) << 4);
-      } else {
-        const int row = (qd - kBigVoc * 8) >> 3;
-        off = kBigVoc * kRowBytes + row * kRowBytes + ((c ^ swz_b(row)) << 4);
-      }
-      *reinterpret_cast<u32x4*>(S + off) = R[j];
-    }
-  };
-
-  f32x16 acc[NTB][NVB];
-  TeacherW16<NTB, NVB> wt_;   // teacher weights exp(l_M - m_M) (loss mode)
-  u32x4 R0[kBigChunks], R1[kBigChunks], R2[kBigChunks];
-
-  gload(R0);
-  gload(R1);
-  gload(R2);
-  sstore(R0, 0);
-  __syncthreads();
-
-  int g = 0;                 // global step
-  int cp_ei = 0, cp_j = 0;   // the step being computed: exit position, step within it
-  auto step = [&](u32x4 (&Rload)[kBigChunks], const u32x4 (&Rnext)[kBigChunks]) {
-    gload(Rload);                                // stage g + 3 (this set held stage g, in LDS already)
-    if (cp_j == 0) zero_acc(acc);
-    if (cp_j < steps_of(cp_ei))
-      mfma_step<bf16_t, BK>(acc, lds + (g & 1) * kBigStage, a_row, a_x, b_row, b_x, L.hl);
-    sstore(Rnext, (g + 1) & 1);                  // stage g + 1
-    __syncthreads();
-    ++cp_j;
-    ++g;
-  };
-  for (int ei = 0; ei < n_exits;) {
-    step(R0, R1);
-    step(R1, R2);
-    step(R2, R0);
-    if (cp_j == padded(ei)) {
-      const int e = exit_at(ei);
-      const bool teacher = (MODE == kModeLoss) && ei == 0;
-      if (v0 + kBigVoc > vocab) mask_tail(acc, L, vocab);
-      if constexpr (MODE == kModeLoss)
-        loss_epilogue<bf16_t, NTB, NVB, true>(acc, wt_, L, teacher, e, n, vocab, t0, vt, n_vt,
-                                              ex.out[e], stats, lab, xmax, xsum);
-      else
-        argmax_epilogue<NTB, NVB, true>(acc, L, e, n, vocab, t0, vt, n_vt, ex.out[e], stats, xsum);
-      cp_j = 0;
-      ++cp_ei;
-      ++ei;
-    }
-  }
-}
-
-bool big_shapes(int n_exits, int vocab, const ExitSet& ex) {
-  if (vocab % 8 != 0) return false;
-  for (int e = 0; e < n_exits; ++e)
-    if (ex.d[e] % 64 != 0) return false;
-  return true;
-}
-
 template <typename T, int MODE>
 hipError_t launch_heads(int n_exits, int64_t n, int vocab, const ExitSet& ex,
-                        const int32_t* labels, float* stats, float* lab, int* vtile, hipStream_t s) {
-  if constexpr (sizeof(T) == 2) {
-    if (big_shapes(n_exits, vocab, ex)) {
-      *vtile = kBigVoc;
-      if (n == 0) return hipSuccess;
-      const int n_tt = static_cast<int>((n + kBigTok - 1) / kBigTok);
-      const int n_vt = (vocab + kBigVoc - 1) / kBigVoc;
-      hipLaunchKernelGGL((heads_kernel_big<MODE>), dim3(n_tt * n_vt), dim3(kBigThreads), 0, s, ex,
-                         n_exits, n, vocab, labels, stats, lab, n_tt, n_vt);
-      return hipGetLastError();
-    }
-  }
-  *vtile = kGenVoc;
+                        const int32_t* labels, float* stats, float* lab, TileInfo* info,
+                        hipStream_t s) {
+  info->vtile = kGenVoc;
+  info->teacher_w16 = false;
   if (n == 0) return hipSuccess;
   constexpr int C = Elem<T>::kChunk;
   const int n_tt = static_cast<int>((n + kGenTok - 1) / kGenTok);
@@ -745,24 +539,24 @@ hipError_t launch_heads(int n_exits, int64_t n, int vocab, const ExitSet& ex,
 
 template <typename T>
 hipError_t launch_heads_loss(int n_exits, int64_t n, int vocab, const ExitSet& ex,
-                             const int32_t* labels, float* stats, float* lab, int* vtile,
+                             const int32_t* labels, float* stats, float* lab, TileInfo* info,
                              hipStream_t s) {
-  return launch_heads<T, kModeLoss>(n_exits, n, vocab, ex, labels, stats, lab, vtile, s);
+  return launch_heads<T, kModeLoss>(n_exits, n, vocab, ex, labels, stats, lab, info, s);
 }
 
 template <typename T>
 hipError_t launch_heads_argmax(int n_exits, int64_t n, int vocab, const ExitSet& ex, float* best,
-                               int* vtile, hipStream_t s) {
-  return launch_heads<T, kModeArgmax>(n_exits, n, vocab, ex, nullptr, best, nullptr, vtile, s);
+                               TileInfo* info, hipStream_t s) {
+  return launch_heads<T, kModeArgmax>(n_exits, n, vocab, ex, nullptr, best, nullptr, info, s);
 }
 
 template hipError_t launch_heads_loss<bf16_t>(int, int64_t, int, const ExitSet&, const int32_t*,
-                                              float*, float*, int*, hipStream_t);
+                                              float*, float*, TileInfo*, hipStream_t);
 template hipError_t launch_heads_loss<float>(int, int64_t, int, const ExitSet&, const int32_t*,
-                                             float*, float*, int*, hipStream_t);
-template hipError_t launch_heads_argmax<bf16_t>(int, int64_t, int, const ExitSet&, float*, int*,
+                                             float*, float*, TileInfo*, hipStream_t);
+template hipError_t launch_heads_argmax<bf16_t>(int, int64_t, int, const ExitSet&, float*, TileInfo*,
                                                 hipStream_t);
-template hipError_t launch_heads_argmax<float>(int, int64_t, int, const ExitSet&, float*, int*,
+template hipError_t launch_heads_argmax<float>(int, int64_t, int, const ExitSet&, float*, TileInfo*,
                                                hipStream_t);
 
 }  // namespace nel

@@ -20,6 +20,15 @@ struct ExitSet {
   int d[kMaxExits];
 };
 
+// What the head GEMM that ran tells the passes after it: the vocabulary
+// width of its statistics tiles, and whether the teacher's gradient buffer
+// holds fp16 teacher weights exp(l_M - m) (packed-weight GEMM) rather than the
+// tile-shifted logits l_M - m in the element type.
+struct TileInfo {
+  int vtile = kVocTile;
+  bool teacher_w16 = false;
+};
+
 inline int64_t n_vocab_tiles(int vocab) { return (vocab + kVocTile - 1) / kVocTile; }
 
 // Workspace layout of the loss op (byte offsets from the base).
@@ -56,16 +65,26 @@ hipError_t launch_junction(int64_t n, int d_in, int d_out, int vocab, const void
                            const int32_t* ids, const void* emb, void* out, int32_t* flags,
                            hipStream_t s);
 
-// Head GEMM + per-tile loss statistics (teacher = exit n_exits-1 first);
-// *vtile receives the vocabulary tile size of the statistics.
+// Head GEMM + per-tile loss statistics (teacher = exit n_exits-1 first),
+// row-major weights.
 template <typename T>
 hipError_t launch_heads_loss(int n_exits, int64_t n, int vocab, const ExitSet& ex,
-                             const int32_t* labels, float* stats, float* lab, int* vtile,
+                             const int32_t* labels, float* stats, float* lab, TileInfo* info,
                              hipStream_t s);
 // Head GEMM + per-tile (max, lowest index); optional fp32 logits in ex.out.
 template <typename T>
 hipError_t launch_heads_argmax(int n_exits, int64_t n, int vocab, const ExitSet& ex, float* best,
-                               int* vtile, hipStream_t s);
+                               TileInfo* info, hipStream_t s);
+
+// MFMA-tiled (packed) bf16 weights: shape rule, packing, and the two GEMMs.
+// The loss GEMM needs every ex.out[e] (the teacher's holds its weights).
+bool packed_shape_ok(int vocab, int d);
+hipError_t launch_pack_weights(int vocab, int d, const void* w, void* packed, hipStream_t s);
+hipError_t launch_heads_loss_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
+                                    const int32_t* labels, float* stats, float* lab,
+                                    TileInfo* info, hipStream_t s);
+hipError_t launch_heads_argmax_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
+                                      float* best, TileInfo* info, hipStream_t s);
 
 hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
                              float alpha, const float* stats, const float* lab, float* lse,
@@ -73,7 +92,8 @@ hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const
 hipError_t launch_loss_means(int n_exits, int64_t n, int vocab, const int32_t* labels,
                              const float* tokloss, float* means, int32_t* flags, hipStream_t s);
 template <typename T>
-hipError_t launch_finalize(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
+hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const TileInfo& info,
+                           const int32_t* labels,
                            float alpha, float grad_scale, const float* stats, const float* lse,
                            void* const* dlogits, hipStream_t s);
 hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, int vtile, const float* best,

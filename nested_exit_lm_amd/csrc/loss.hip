@@ -130,7 +130,9 @@ struct DlPtrs {
 
 // 16-byte chunk path (vocab a multiple of the chunk).  Each workgroup
 // iteration covers 256 consecutive chunks of one token row for all exits.
-template <typename T>
+// TW16: the teacher's buffer holds fp16 weights w = exp(l_M - m) of its tile
+// (so p = w exp(m - lse)) instead of the shifted logits l_M - m.
+template <typename T, bool TW16>
 __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab, int vtile,
                                                     const int32_t* __restrict__ labels, float alpha,
                                                     float gs, const float* __restrict__ stats,
@@ -153,19 +155,37 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
     for (int e = 0; e < kMaxExits; ++e)
       if (e < M) raw[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
                              static_cast<const T*>(dl.p[e]) + t * vocab) + c);
+    // The teacher's chunk in a vector of its own: every element index below is
+    // a compile-time constant (no indexing of raw[] by the run-time M - 1).
+    const u32x4 traw = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(static_cast<const T*>(dl.p[M - 1]) + t * vocab) + c);
     float p[C];
     {
       const int e = M - 1;
       const float off = stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
                         lse[static_cast<int64_t>(e) * n + t];
+      if constexpr (TW16 && sizeof(T) == 2) {
+        typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+        const float scale = fexp(off);
 #pragma unroll
-      for (int i = 0; i < C; ++i) {
-        float s;
-        if constexpr (sizeof(T) == 2)
-          s = __uint_as_float((i & 1) ? (raw[e][i >> 1] & 0xffff0000u) : (raw[e][i >> 1] << 16));
-        else
-          s = __uint_as_float(raw[e][i]);
-        p[i] = fexp(s + off);
+        for (int j = 0; j < 4; ++j) {
+          // (bit_cast of a vector-element expression reads element 0 on this
+          // compiler; the element goes through a scalar first)
+          const uint32_t word = traw[j];
+          const half2_t hw = __builtin_bit_cast(half2_t, word);
+          p[2 * j] = static_cast<float>(hw[0]) * scale;
+          p[2 * j + 1] = static_cast<float>(hw[1]) * scale;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          float s;
+          if constexpr (sizeof(T) == 2)
+            s = __uint_as_float((i & 1) ? (traw[i >> 1] & 0xffff0000u) : (traw[i >> 1] << 16));
+          else
+            s = __uint_as_float(traw[i]);
+          p[i] = fexp(s + off);
+        }
       }
     }
 #pragma unroll
@@ -299,11 +319,13 @@ hipError_t launch_loss_means(int n_exits, int64_t n, int vocab, const int32_t* l
 }
 
 template <typename T>
-hipError_t launch_finalize(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
-                           float alpha, float grad_scale, const float* stats, const float* lse,
-                           void* const* dlogits, hipStream_t s) {
+hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const TileInfo& info,
+                           const int32_t* labels, float alpha, float grad_scale,
+                           const float* stats, const float* lse, void* const* dlogits,
+                           hipStream_t s) {
   if (n == 0) return hipSuccess;
   constexpr int C = Elem<T>::kChunk;
+  const int vtile = info.vtile;
   DlPtrs dl{};
   for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
   const int n_vt = (vocab + vtile - 1) / vtile;
@@ -312,9 +334,14 @@ hipError_t launch_finalize(int n_exits, int64_t n, int vocab, int vtile, const i
     const int segs = static_cast<int>((cpr + 255) / 256);
     const int64_t nseg = n * segs;
     const unsigned grid = static_cast<unsigned>(nseg < 256 * 16 ? nseg : 256 * 16);
-    hipLaunchKernelGGL(finalize_vec<T>, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, vtile,
-                       labels, alpha, grad_scale, stats, lse, dl, n_vt, segs);
+    if (info.teacher_w16)
+      hipLaunchKernelGGL((finalize_vec<T, true>), dim3(grid), dim3(256), 0, s, n_exits, n, vocab,
+                         vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, segs);
+    else
+      hipLaunchKernelGGL((finalize_vec<T, false>), dim3(grid), dim3(256), 0, s, n_exits, n, vocab,
+                         vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, segs);
   } else {
+    if (info.teacher_w16) return hipErrorInvalidValue;   // the packed GEMM needs V % 32 == 0
     const int64_t total = n * vocab;
     const int64_t blocks = (total + 255) / 256;
     const unsigned grid = static_cast<unsigned>(blocks < 256 * 16 ? blocks : 256 * 16);
@@ -324,10 +351,12 @@ hipError_t launch_finalize(int n_exits, int64_t n, int vocab, int vtile, const i
   return hipGetLastError();
 }
 
-template hipError_t launch_finalize<bf16_t>(int, int64_t, int, int, const int32_t*, float, float,
-                                            const float*, const float*, void* const*, hipStream_t);
-template hipError_t launch_finalize<float>(int, int64_t, int, int, const int32_t*, float, float,
-                                           const float*, const float*, void* const*, hipStream_t);
+template hipError_t launch_finalize<bf16_t>(int, int64_t, int, const TileInfo&, const int32_t*,
+                                            float, float, const float*, const float*,
+                                            void* const*, hipStream_t);
+template hipError_t launch_finalize<float>(int, int64_t, int, const TileInfo&, const int32_t*,
+                                           float, float, const float*, const float*, void* const*,
+                                           hipStream_t);
 
 hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, int vtile, const float* best,
                                int32_t* argmax, hipStream_t s) {

@@ -75,3 +75,46 @@ def head_error_bound(h: np.ndarray, w: np.ndarray) -> np.ndarray:
     K = h.shape[1]
     gamma = 2.0 * K * 2.0 ** -24
     return gamma * (np.abs(h) @ np.abs(w).T)
+
+
+GRAD_TOL = {"bf16": 2e-2, "f32": 1e-4}
+LOSS_TOL = {"bf16": 1e-3, "f32": 1e-4}
+
+
+def run_loss(nel, ds, alpha, grad_scale=1.0, want_dlogits=True, packed=None):
+    """The loss through the C ABI; `packed` is None (row-major heads) or the list of
+    packed head weights."""
+    import torch
+    if packed is None:
+        mean, tok, dl = nel.matryoshka_loss(ds.h, ds.w, ds.labels, alpha_d=alpha,
+                                            grad_scale=grad_scale, want_dlogits=want_dlogits)
+    else:
+        mean, tok, dl = nel.matryoshka_loss_packed(ds.h, packed, ds.labels, alpha_d=alpha,
+                                                   grad_scale=grad_scale)
+    torch.cuda.synchronize()
+    return to_np(mean), to_np(tok), dl
+
+
+def check_full(nel, s, alpha, grad_scale=1.0, packed=False):
+    """Every token, every exit, every vocabulary entry against the oracle."""
+    import oracle
+    ds = DevSuite(s)
+    pw = [nel.pack_weights(w) for w in ds.w] if packed else None
+    mean, tok, dl = run_loss(nel, ds, alpha, grad_scale, packed=pw)
+    ref, grads = oracle.forward_tokens(s.h, s.w, s.labels, alpha, grad_scale)
+    M = s.n_exits
+    tol = LOSS_TOL[s.dtype]
+    assert_loss_close(tok[:, 0], ref["ce"], tol, "CE")
+    assert_loss_close(tok[:, 1], ref["dist"], tol, "Dist")
+    assert_loss_close(tok[:, 2], ref["loss"], tol, "L")
+    want_mean = np.concatenate([ref["mean_ce"], ref["mean_dist"], ref["mean_loss"], [ref["mean_total"]]])
+    assert mean.shape == (3 * M + 1,)
+    assert_loss_close(mean, want_mean, tol, "means")
+    for m in range(M):
+        assert_grad_close(to_np(dl[m]), grads[m], GRAD_TOL[s.dtype] * max(1.0, abs(grad_scale)),
+                          f"dlogits exit {m}")
+
+
+def sample_rows(n, k, seed):
+    r = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, n - 1, n // 2], r.choice(n, size=k, replace=False)]))

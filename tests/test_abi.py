@@ -20,7 +20,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = nel.load()
     syms = declared_symbols()
-    assert len(syms) == 11
+    assert len(syms) == 15
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -29,6 +29,7 @@ def test_status_strings_and_workspace_sizes():
     assert nel.status_string(0) == "ok"
     assert "workspace" in nel.status_string(-5)
     assert nel.status_string(-99) == "unknown status"
+    assert nel.load().nel_last_hip_error() == b"none"
     n, V = 16384, 32768
     nvt = V // 128
     ws = nel.workspace_size(nel.OP_LOSS, 3, n, V)
@@ -106,6 +107,46 @@ def test_heads_and_accept_host_validation():
     assert lib.nel_accept_prefix(0, 7, 6, None, None, None, None) == 0
     assert lib.nel_read_device_flags(None, None, None) == -1
     assert lib.nel_timing_read(99, None, None) == -1
+
+
+def test_packed_host_validation():
+    lib = nel.load()
+    # nel_pack_weights: bf16 only, V % 32 == 0, d % 64 == 0, distinct aligned buffers
+    assert lib.nel_pack_weights(0, 64, 128, FAKE, FAKE + 65536, None) == -3
+    assert lib.nel_pack_weights(1, 48, 128, FAKE, FAKE + 65536, None) == -2
+    assert lib.nel_pack_weights(1, 64, 96, FAKE, FAKE + 65536, None) == -2
+    assert lib.nel_pack_weights(1, 0, 128, FAKE, FAKE + 65536, None) == -2
+    assert lib.nel_pack_weights(1, 64, 128, None, FAKE, None) == -1
+    assert lib.nel_pack_weights(1, 64, 128, MIS, FAKE + 65536, None) == -4
+    assert lib.nel_pack_weights(1, 64, 128, FAKE, FAKE + 1024, None) == -1   # overlapping
+    d = _arr(ctypes.c_int32, 64, 128, 192)
+    p3 = _arr(ctypes.c_void_p, FAKE, FAKE, FAKE)
+    ws_need = nel.workspace_size(nel.OP_LOSS, 3, 4, 256)
+
+    def loss(dt=1, V=256, d=d, dl=p3, alpha=0.3):
+        return lib.nel_matryoshka_loss_packed(dt, 3, 4, V, d, p3, p3, FAKE, alpha, 1.0, None, FAKE,
+                                              dl, FAKE, ws_need, None)
+
+    assert loss(dt=0) == -3                                    # fp32 has no packed form
+    assert loss(V=100) == -2
+    assert loss(d=_arr(ctypes.c_int32, 64, 128, 200)) == -2    # a width not a multiple of 64
+    assert loss(d=_arr(ctypes.c_int32, 64, 64, 192)) == -2
+    assert loss(dl=None) == -1                                 # gradients are required
+    assert loss(alpha=-0.1) == -1
+    d2 = _arr(ctypes.c_int32, 64, 192)
+    p2 = _arr(ctypes.c_void_p, FAKE, FAKE)
+    need = nel.workspace_size(nel.OP_HEADS, 2, 4, 256)
+    assert lib.nel_exit_heads_packed(0, 2, 4, 256, d2, p2, p2, None, FAKE, FAKE, need, None) == -3
+    assert lib.nel_exit_heads_packed(1, 2, 4, 250, d2, p2, p2, None, FAKE, FAKE, need, None) == -2
+    assert lib.nel_exit_heads_packed(1, 2, 4, 256, _arr(ctypes.c_int32, 64, 100), p2, p2, None,
+                                     FAKE, FAKE, need, None) == -2
+
+
+def test_one_hip_runtime_after_load():
+    """libnel.so binds to the HIP runtime PyTorch carries (same soname), never a second one."""
+    nel.load()
+    rts = nel._hip_runtimes()
+    assert len(rts) == 1, rts
 
 
 def test_product_path_never_touches_the_oracle():

@@ -11,38 +11,10 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import DevSuite, assert_grad_close, assert_loss_close, log, to_np
+from gpu_util import (DevSuite, assert_grad_close, assert_loss_close, check_full, log, run_loss,
+                      sample_rows, to_np)
 
 pytestmark = pytest.mark.gpu
-
-GRAD_TOL = {"bf16": 2e-2, "f32": 1e-4}
-LOSS_TOL = {"bf16": 1e-3, "f32": 1e-4}
-
-
-def run_loss(nel, ds, alpha, grad_scale=1.0, want_dlogits=True):
-    import torch
-    mean, tok, dl = nel.matryoshka_loss(ds.h, ds.w, ds.labels, alpha_d=alpha,
-                                        grad_scale=grad_scale, want_dlogits=want_dlogits)
-    torch.cuda.synchronize()
-    return to_np(mean), to_np(tok), dl
-
-
-def check_full(nel, s, alpha, grad_scale=1.0):
-    ds = DevSuite(s)
-    mean, tok, dl = run_loss(nel, ds, alpha, grad_scale)
-    ref, grads = oracle.forward_tokens(s.h, s.w, s.labels, alpha, grad_scale)
-    M = s.n_exits
-    tol = LOSS_TOL[s.dtype]
-    assert_loss_close(tok[:, 0], ref["ce"], tol, "CE")
-    assert_loss_close(tok[:, 1], ref["dist"], tol, "Dist")
-    assert_loss_close(tok[:, 2], ref["loss"], tol, "L")
-    want_mean = np.concatenate([ref["mean_ce"], ref["mean_dist"], ref["mean_loss"], [ref["mean_total"]]])
-    assert mean.shape == (3 * M + 1,)
-    assert_loss_close(mean, want_mean, tol, "means")
-    for m in range(M):
-        assert_grad_close(to_np(dl[m]), grads[m], GRAD_TOL[s.dtype] * max(1.0, abs(grad_scale)),
-                          f"dlogits exit {m}")
-
 
 SMALL = [
     ("tiny-3exit-f32", lambda: synth.make_workload(0)),
@@ -82,12 +54,6 @@ def test_loss_only_matches_loss_with_gradient(nel):
     assert dl is None
     np.testing.assert_array_equal(t1, t2)
     np.testing.assert_array_equal(m1, m2)
-
-
-def sample_rows(n, k, seed):
-    r = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, 1, n - 1, n // 2], r.choice(n, size=k, replace=False)]))
-    return rows
 
 
 @pytest.mark.parametrize("k,alpha", [(1, 0.0), (1, 0.3), (1, 1.0), (2, 0.3), (3, 0.3)])

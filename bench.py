@@ -1,10 +1,11 @@
 """Throughput of the Matryoshka multi-exit hot path on one MI355X.
 
-One step = both junctions (block 1 -> 2, block 2 -> 3), every exit's head,
-the distillation loss and dL/dlogits for all three exits, on one batch of
-seeded synthetic inputs shaped like the 500M / 1.5B / 3B suite (widths 1024,
-2304, 4352; vocabulary 32768; 8 x 2048 tokens; bf16 inputs, fp32
-accumulation; alpha_d = 0.3).  Inputs are resident in HBM before timing.
+One step = both junctions (block 1 -> 2, block 2 -> 3), the rewrite of the
+three row-major heads into the MFMA-tiled layout, every exit's head, the
+distillation loss and dL/dlogits for all three exits, on one batch of seeded
+synthetic inputs shaped like the 500M / 1.5B / 3B suite (widths 1024, 2304,
+4352; vocabulary 32768; 8 x 2048 tokens; bf16 inputs, fp32 accumulation;
+alpha_d = 0.3).  Inputs are resident in HBM before timing.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
@@ -91,7 +92,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-verify", action="store_true", help="skip the speculative-verify sub-benchmark")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB read + 1 GiB write kernel three times (the "
+                         "reference that scales the HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="read the rocprofv3 FETCH_SIZE / WRITE_SIZE runs, write "
+                         "profiles/traffic.json, and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path is built and timed on a single MI355X "
               "(token sharding across GPUs is described, not built). Run with --gpus 1.",
@@ -119,6 +129,7 @@ def main():
     labels = torch.from_numpy(s.labels).to(dev)
     j2 = torch.empty(N, D[1], dtype=torch.bfloat16, device=dev)
     j3 = torch.empty(N, D[2], dtype=torch.bfloat16, device=dev)
+    pw = [torch.empty_like(w) for w in ws]
     dl = [torch.empty(N, V, dtype=torch.bfloat16, device=dev) for _ in D]
     mean = torch.empty(3 * len(D) + 1, dtype=torch.float32, device=dev)
     tok = torch.empty(len(D), 3, N, dtype=torch.float32, device=dev)
@@ -127,9 +138,19 @@ def main():
     def step():
         nel.junction(hs[0], ids, embs[1], out=j2)
         nel.junction(hs[1], ids, embs[2], out=j3)
-        nel.matryoshka_loss(hs, ws, labels, alpha_d=s.alpha, grad_scale=1.0, dlogits=dl,
-                            workspace=wsb, mean_loss=mean, token_loss=tok)
+        for w, p in zip(ws, pw):
+            nel.pack_weights(w, out=p)
+        nel.matryoshka_loss_packed(hs, pw, labels, alpha_d=s.alpha, grad_scale=1.0, dlogits=dl,
+                                   workspace=wsb, mean_loss=mean, token_loss=tok)
 
+    if args.calibrate_copy:
+        log("[bench] copy calibration: 3 x (read 1 GiB, write 1 GiB)")
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
     log("[bench] warmup")
     for _ in range(args.warmup):
         step()
@@ -146,7 +167,7 @@ def main():
     nel.timing_enable(False)
     ms = (t1 - t0) * 1e3 / args.steps
     kern = {}
-    for k in ("junction", "heads_loss", "merge", "means", "finalize"):
+    for k in ("junction", "pack", "heads_loss", "merge", "means", "finalize"):
         tot, cnt = nel.timing_read(k)
         kern[k] = {"avg_ms": tot / max(cnt, 1), "launches": cnt}
 
@@ -154,12 +175,15 @@ def main():
     k2 = kern["heads_loss"]["avg_ms"] / 1e3
     jbytes = sum(2 * (D[m - 1] + (D[m] - D[m - 1]) + D[m]) * N + 4 * N for m in (1, 2))  # both junctions
     fbytes = 2 * len(D) * N * V * 2                               # finalize: read s, write g
+    pbytes = 2 * V * sum(D) * 2 / len(D)                          # pack: read + write, per launch
     kern["heads_loss"]["tflops"] = flops / k2 / 1e12
     kern["heads_loss"]["mfma_frac"] = flops / k2 / 1e12 / BF16_PEAK_TFLOPS
     kern["junction"]["gbs"] = jbytes / 2 / (kern["junction"]["avg_ms"] / 1e3) / 1e9
     kern["junction"]["hbm_frac"] = kern["junction"]["gbs"] / HBM_PEAK_GBS
     kern["finalize"]["gbs"] = fbytes / (kern["finalize"]["avg_ms"] / 1e3) / 1e9
     kern["finalize"]["hbm_frac"] = kern["finalize"]["gbs"] / HBM_PEAK_GBS
+    kern["pack"]["gbs"] = pbytes / (kern["pack"]["avg_ms"] / 1e3) / 1e9
+    kern["pack"]["hbm_frac"] = kern["pack"]["gbs"] / HBM_PEAK_GBS
     traffic = measured_traffic()
     losses = mean.cpu().numpy().tolist()
     out = {
@@ -193,6 +217,53 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _read_counter_csv(d):
+    """{kernel name: [counter value per dispatch]} from a rocprofv3 --pmc run directory."""
+    import csv
+    import glob
+    out = {}
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """HBM traffic per launch of the head GEMM: rocprofv3 FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled so that the calibration kernel (1 GiB read,
+    1 GiB written) reads exactly its size."""
+    fetch, write = _read_counter_csv(fetch_dir), _read_counter_csv(write_dir)
+
+    def pick(dct, key):
+        names = [k for k in dct if key in k]
+        if not names:
+            raise KeyError(f"no kernel matching {key}")
+        vals = [v for k in names for v in dct[k]]
+        return names[0], vals
+
+    gib_kib = float(1 << 20)
+    _, cf = pick(fetch, "AUnaryFunctor")     # the calibration kernel: b = a * 1.0 over 1 GiB
+    _, cw = pick(write, "AUnaryFunctor")
+    f_scale = gib_kib / (sorted(cf)[len(cf) // 2])
+    w_scale = gib_kib / (sorted(cw)[len(cw) // 2])
+    name, hf = pick(fetch, "heads_kernel_packed")
+    _, hw = pick(write, "heads_kernel_packed")
+    fb = sum(hf) / len(hf) * 1024 * f_scale
+    wb = sum(hw) / len(hw) * 1024 * w_scale
+    res = {"source_hash": kernel_source_hash(), "kernel": name,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "heads_loss_fetch_bytes": fb, "heads_loss_write_bytes": wb,
+           "heads_loss_bytes_per_launch": fb + wb}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
+
+
 def bench_verify(nel, torch, synth, dev, args):
     """Speculative-verify shape: junction 1 -> 2, heads of exits 1 and 3 with greedy
     argmax, accepted prefix length (102 sequences x 7 positions)."""
@@ -202,7 +273,8 @@ def bench_verify(nel, torch, synth, dev, args):
         return torch.from_numpy(synth.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     hs = [td(s.h[m]) for m in s.exits]
-    ws = [td(s.w[m]) for m in s.exits]
+    # decoding reuses the same heads every step: they are packed once, up front
+    ws = [nel.pack_weights(td(s.w[m])) for m in s.exits]
     emb = td(s.emb[1])
     ids = torch.from_numpy(s.ids).to(dev)
     j = torch.empty(s.n_tokens, s.widths[1], dtype=torch.bfloat16, device=dev)
@@ -211,7 +283,7 @@ def bench_verify(nel, torch, synth, dev, args):
 
     def step():
         nel.junction(hs[0], ids, emb, out=j)
-        _, am = nel.exit_heads(hs, ws, want_logits=False, want_argmax=True, workspace=wsb)
+        _, am = nel.exit_heads_packed(hs, ws, want_logits=False, want_argmax=True, workspace=wsb)
         nel.accept_prefix(am[0].view(s.batch, s.seq), am[1].view(s.batch, s.seq), 6)
 
     for _ in range(args.warmup):
@@ -230,6 +302,7 @@ def bench_verify(nel, torch, synth, dev, args):
     flops = 2.0 * s.n_tokens * s.vocab * (s.widths[0] + s.widths[2])
     k = tot / max(cnt, 1) / 1e3
     return {"ms_per_step": (t1 - t0) * 1e3 / steps, "tokens": s.n_tokens,
+            "weights": "packed once before timing (static heads in decoding)",
             "heads_argmax_ms": k * 1e3, "heads_argmax_tflops": flops / k / 1e12,
             "heads_argmax_mfma_frac": flops / k / 1e12 / BF16_PEAK_TFLOPS}
 

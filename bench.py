@@ -36,10 +36,14 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# Sources that make up the head GEMM whose HBM traffic the counter runs measured.
+GEMM_SOURCES = ("heads_packed.hip", "common.h", "tiles.h", "internal.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nested_exit_lm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in GEMM_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

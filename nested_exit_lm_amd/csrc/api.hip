@@ -238,6 +238,7 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
   float* lab = reinterpret_cast<float*>(ws + L.lab);
   float* lse = reinterpret_cast<float*>(ws + L.lse);
   float* tl = token_loss ? token_loss : reinterpret_cast<float*>(ws + L.tokloss);
+  double* partials = reinterpret_cast<double*>(ws + L.partials);
   ExitSet ex{};
   for (int e = 0; e < n_exits; ++e) {
     ex.h[e] = h[e];
@@ -257,11 +258,11 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
   if (err != hipSuccess) return from_hip(err);
   err = timed(NEL_K_MERGE, s, [&] {
     return launch_loss_merge(n_exits, n_tokens, vocab, info.vtile, labels, alpha_d, stats, lab, lse, tl,
-                             s);
+                             partials, flags, s);
   });
   if (err != hipSuccess) return from_hip(err);
   err = timed(NEL_K_MEANS, s, [&] {
-    return launch_loss_means(n_exits, n_tokens, vocab, labels, tl, mean_loss, flags, s);
+    return launch_loss_means(n_exits, n_tokens, partials, mean_loss, s);
   });
   if (err != hipSuccess) return from_hip(err);
   if (dlogits && n_tokens > 0) {

@@ -31,9 +31,14 @@ struct TileInfo {
 
 inline int64_t n_vocab_tiles(int vocab) { return (vocab + kVocTile - 1) / kVocTile; }
 
+// Tokens per workgroup of the loss merge; each workgroup leaves fp64 partial
+// sums of the 3M + 1 reported means.
+constexpr int kMergeTok = 64;
+inline int64_t n_merge_blocks(int64_t n) { return (n + kMergeTok - 1) / kMergeTok; }
+
 // Workspace layout of the loss op (byte offsets from the base).
 struct LossWs {
-  size_t flags, stats, lab, lse, tokloss, total;
+  size_t flags, stats, lab, lse, tokloss, partials, total;
 };
 inline LossWs loss_ws_layout(int n_exits, int64_t n, int vocab) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -44,7 +49,8 @@ inline LossWs loss_ws_layout(int n_exits, int64_t n, int vocab) {
   L.lab = L.stats + up(sizeof(float) * n_exits * 3 * nvt * n);
   L.lse = L.lab + up(sizeof(float) * n_exits * n);
   L.tokloss = L.lse + up(sizeof(float) * n_exits * n);
-  L.total = L.tokloss + up(sizeof(float) * n_exits * 3 * n);
+  L.partials = L.tokloss + up(sizeof(float) * n_exits * 3 * n);
+  L.total = L.partials + up(sizeof(double) * (3 * n_exits + 1) * n_merge_blocks(n));
   return L;
 }
 struct HeadsWs {
@@ -88,9 +94,9 @@ hipError_t launch_heads_argmax_packed(int n_exits, int64_t n, int vocab, const E
 
 hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
                              float alpha, const float* stats, const float* lab, float* lse,
-                             float* tokloss, hipStream_t s);
-hipError_t launch_loss_means(int n_exits, int64_t n, int vocab, const int32_t* labels,
-                             const float* tokloss, float* means, int32_t* flags, hipStream_t s);
+                             float* tokloss, double* partials, int32_t* flags, hipStream_t s);
+hipError_t launch_loss_means(int n_exits, int64_t n, const double* partials, float* means,
+                             hipStream_t s);
 template <typename T>
 hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const TileInfo& info,
                            const int32_t* labels,

@@ -24,23 +24,37 @@ namespace {
 
 // ---------------------------------------------------------------- loss merge
 // 256 threads = 64 tokens x 4 tile groups; the groups are merged in LDS in a
-// fixed order, so results do not depend on scheduling.
+// fixed order, so results do not depend on scheduling.  The first wavefront
+// (one lane per token) also reduces the workgroup's per-token values into
+// fp64 partial sums of the reported means, in a fixed butterfly order:
+// partials[block][q], q = CE_0.., Dist_0.., L_0.., total.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
 __global__ __launch_bounds__(256) void loss_merge_kernel(int M, int64_t n, int vocab,
                                                          const int32_t* __restrict__ labels,
                                                          float alpha,
                                                          const float* __restrict__ stats,
                                                          const float* __restrict__ lab,
                                                          float* __restrict__ lse_out,
-                                                         float* __restrict__ tokloss, int n_vt) {
+                                                         float* __restrict__ tokloss,
+                                                         double* __restrict__ partials,
+                                                         int32_t* __restrict__ flags, int n_vt) {
   __shared__ float sh[4][64][2];
   const int tl = threadIdx.x & 63, g = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 64 + tl;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeTok + tl;
   const bool valid = t < n;
   const int64_t plane = static_cast<int64_t>(n_vt) * n;
   const int y = valid ? labels[t] : 0;
   const bool bad = y < 0 || y >= vocab;
+  if (g == 0 && valid && bad && flags) atomicOr(flags, 2 /*NEL_FLAG_BAD_LABEL*/);
+  double* part = partials + static_cast<int64_t>(blockIdx.x) * (3 * M + 1);
   const float* stT = stats + static_cast<int64_t>(M - 1) * 3 * plane + t;
   float lseT = 0.f;
+  double total = 0.0;
   for (int ei = 0; ei < M; ++ei) {
     const int e = ei == 0 ? M - 1 : ei - 1;
     const float* st = stats + static_cast<int64_t>(e) * 3 * plane + t;
@@ -70,55 +84,53 @@ __global__ __launch_bounds__(256) void loss_merge_kernel(int M, int64_t n, int v
       __syncthreads();
       dist = L - T;
     }
-    if (g == 0 && valid) {
-      float ce = L - (bad ? 0.f : lab[static_cast<int64_t>(e) * n + t]);
+    if (g == 0) {   // wavefront-uniform branch: the 64 token lanes
+      float ce = L - ((bad || !valid) ? 0.f : lab[static_cast<int64_t>(e) * n + t]);
       float lm = (ei == 0) ? ce : (1.f - alpha) * ce + alpha * dist;
       float lse = L;
       if (bad) ce = dist = lm = lse = __builtin_nanf("");
-      lse_out[static_cast<int64_t>(e) * n + t] = lse;
-      tokloss[(static_cast<int64_t>(e) * 3 + 0) * n + t] = ce;
-      tokloss[(static_cast<int64_t>(e) * 3 + 1) * n + t] = dist;
-      tokloss[(static_cast<int64_t>(e) * 3 + 2) * n + t] = lm;
+      if (valid) {
+        lse_out[static_cast<int64_t>(e) * n + t] = lse;
+        tokloss[(static_cast<int64_t>(e) * 3 + 0) * n + t] = ce;
+        tokloss[(static_cast<int64_t>(e) * 3 + 1) * n + t] = dist;
+        tokloss[(static_cast<int64_t>(e) * 3 + 2) * n + t] = lm;
+      }
+      const double sce = wave_sum_f64(valid ? static_cast<double>(ce) : 0.0);
+      const double sdi = wave_sum_f64(valid ? static_cast<double>(dist) : 0.0);
+      const double slm = wave_sum_f64(valid ? static_cast<double>(lm) : 0.0);
+      total += valid ? static_cast<double>(lm) : 0.0;
+      if (tl == 0) {
+        part[e] = sce;
+        part[M + e] = sdi;
+        part[2 * M + e] = slm;
+      }
     }
+  }
+  if (g == 0) {
+    const double st = wave_sum_f64(total);
+    if (tl == 0) part[3 * M] = st;
   }
 }
 
 // ---------------------------------------------------------------- means
-// One workgroup; fp64 partial sums in a fixed order.
-__global__ __launch_bounds__(1024) void loss_means_kernel(int M, int64_t n, int vocab,
-                                                          const int32_t* __restrict__ labels,
-                                                          const float* __restrict__ tokloss,
-                                                          float* __restrict__ means,
-                                                          int32_t* __restrict__ flags) {
-  __shared__ double red[1024];
-  const int tid = threadIdx.x;
-  int bad = 0;
-  for (int64_t t = tid; t < n; t += 1024) {
-    const int y = labels[t];
-    bad |= (y < 0 || y >= vocab);
-  }
-  bad = __syncthreads_or(bad);
-  if (tid == 0 && bad && flags) atomicOr(flags, 2 /*NEL_FLAG_BAD_LABEL*/);
+// Means from the merge's partial sums: thread i of the workgroup adds the
+// partials of blocks i, i + 256, ... and the 256 results are combined in a
+// fixed tree, so the means do not depend on scheduling.
+__global__ __launch_bounds__(256) void loss_means_kernel(int M, int64_t n, int64_t nblk,
+                                                         const double* __restrict__ partials,
+                                                         float* __restrict__ means) {
+  __shared__ double red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int qi = 0; qi <= 3 * M; ++qi) {
     double a = 0.0;
-    if (qi < 3 * M) {
-      const int qq = qi / M, e = qi % M;   // output order: CE_*, Dist_*, L_*
-      const float* src = tokloss + (static_cast<int64_t>(e) * 3 + qq) * n;
-      for (int64_t t = tid; t < n; t += 1024) a += static_cast<double>(src[t]);
-    } else {
-      for (int64_t t = tid; t < n; t += 1024) {
-        double tot = 0.0;
-        for (int e = 0; e < M; ++e) tot += static_cast<double>(tokloss[(static_cast<int64_t>(e) * 3 + 2) * n + t]);
-        a += tot;
-      }
-    }
-    red[tid] = a;
+    for (int64_t b = tid; b < nblk; b += 256) a += partials[b * (3 * M + 1) + qi];
+    a = wave_sum_f64(a);
+    if (lane == 0) red[wave] = a;
     __syncthreads();
-    for (int w = 512; w >= 1; w >>= 1) {
-      if (tid < w) red[tid] += red[tid + w];
-      __syncthreads();
-    }
-    if (tid == 0) means[qi] = n > 0 ? static_cast<float>(red[0] / static_cast<double>(n)) : 0.f;
+    if (tid == 0)
+      means[qi] = n > 0 ? static_cast<float>(((red[0] + red[1]) + (red[2] + red[3])) /
+                                             static_cast<double>(n))
+                        : 0.f;
     __syncthreads();
   }
 }
@@ -303,18 +315,18 @@ __global__ void clear_flags_kernel(int32_t* f) { *f = 0; }
 
 hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
                              float alpha, const float* stats, const float* lab, float* lse,
-                             float* tokloss, hipStream_t s) {
+                             float* tokloss, double* partials, int32_t* flags, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(loss_merge_kernel, dim3(static_cast<unsigned>((n + 63) / 64)), dim3(256), 0, s,
-                     n_exits, n, vocab, labels, alpha, stats, lab, lse, tokloss,
+  hipLaunchKernelGGL(loss_merge_kernel, dim3(static_cast<unsigned>(n_merge_blocks(n))), dim3(256), 0,
+                     s, n_exits, n, vocab, labels, alpha, stats, lab, lse, tokloss, partials, flags,
                      (vocab + vtile - 1) / vtile);
   return hipGetLastError();
 }
 
-hipError_t launch_loss_means(int n_exits, int64_t n, int vocab, const int32_t* labels,
-                             const float* tokloss, float* means, int32_t* flags, hipStream_t s) {
-  hipLaunchKernelGGL(loss_means_kernel, dim3(1), dim3(1024), 0, s, n_exits, n, vocab, labels,
-                     tokloss, means, flags);
+hipError_t launch_loss_means(int n_exits, int64_t n, const double* partials, float* means,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(loss_means_kernel, dim3(1), dim3(256), 0, s, n_exits, n, n_merge_blocks(n),
+                     partials, means);
   return hipGetLastError();
 }
 

@@ -96,6 +96,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-verify", action="store_true", help="skip the speculative-verify sub-benchmark")
+    ap.add_argument("--no-backward", action="store_true", help="skip the head-backward sub-benchmark")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB read + 1 GiB write kernel three times (the "
                          "reference that scales the HBM byte counters)")
@@ -162,14 +163,19 @@ def main():
     nel.timing_reset()
     nel.timing_enable(True)
     log(f"[bench] timing {args.steps} steps")
+    # events on the stream every kernel is launched on, around each step
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     nel.timing_enable(False)
     ms = (t1 - t0) * 1e3 / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     kern = {}
     for k in ("junction", "pack", "heads_loss", "merge", "means", "finalize"):
         tot, cnt = nel.timing_read(k)
@@ -198,6 +204,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": per_step[len(per_step) // 2],
+        "ms_per_step_min": per_step[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -215,6 +223,8 @@ def main():
     }
     if not args.no_verify:
         out["verify_102x7"] = bench_verify(nel, torch, synth, dev, args)
+    if not args.no_backward:
+        out["head_backward"] = bench_backward(nel, torch, hs, ws, dl, args)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
         out["cpu_baseline"] = cpu_baseline(s, args.cpu_seconds)
@@ -266,6 +276,45 @@ def summarize_counters(fetch_dir, write_dir):
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res))
+
+
+def bench_backward(nel, torch, hs, ws, dl, args):
+    """Backward of the three exit heads on the step's own logit gradients:
+    dh_m = G_m W^m (bf16) and dW^m = G_m^T h_m (fp32), with the operand transposes."""
+    N, V = dl[0].shape
+    D = [h.shape[1] for h in hs]
+    need = max(nel.head_backward_workspace_size(N, V, d) for d in D)
+    wsb = torch.empty(need, dtype=torch.uint8, device=hs[0].device)
+    dhs = [torch.empty_like(h) for h in hs]
+    dws = [torch.empty(V, d, dtype=torch.float32, device=h.device) for h, d in zip(hs, D)]
+
+    def step():
+        for m in range(len(D)):
+            nel.head_backward(dl[m], hs[m], ws[m], dh=dhs[m], dw=dws[m], workspace=wsb)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    nel.timing_reset()
+    nel.timing_enable(True)
+    steps = max(args.steps // 2, 3)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nel.timing_enable(False)
+    res = {"ms_per_step": (t1 - t0) * 1e3 / steps,
+           "work": "dh (bf16) and dW (fp32) of all three heads from the step's dlogits"}
+    flops = 2.0 * N * V * sum(D)          # per GEMM kind, all exits
+    for k in ("bwd_pack", "bwd_dh", "bwd_dw"):
+        tot, cnt = nel.timing_read(k)
+        res[k + "_ms"] = tot / steps
+    res["dh_tflops"] = flops / (res["bwd_dh_ms"] / 1e3) / 1e12
+    res["dw_tflops"] = flops / (res["bwd_dw_ms"] / 1e3) / 1e12
+    res["dh_mfma_frac"] = res["dh_tflops"] / BF16_PEAK_TFLOPS
+    res["dw_mfma_frac"] = res["dw_tflops"] / BF16_PEAK_TFLOPS
+    return res
 
 
 def bench_verify(nel, torch, synth, dev, args):

@@ -193,6 +193,29 @@ nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens
                                  const void* const* w_packed, float* const* logits,
                                  int32_t* argmax, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Backward of one exit head (the step after the loss: l = h W^T with W the
+ * exit's head, copyedit of Sec. 2 "Modeling"; G = dL/dl from
+ * nel_matryoshka_loss*).  By the chain rule, with fp32 accumulation:
+ *     dh = G W       [n_tokens, d]  in dt (bf16)
+ *     dw = G^T h     [vocab, d]     fp32
+ *   dlogits: device bf16 [n_tokens, vocab] (G, input)
+ *   h:       device bf16 [n_tokens, d]     (the exit's block output, input)
+ *   w:       device bf16 [vocab, d]        (the head, row-major, input)
+ *   dh, dw:  device outputs, each may be NULL (not both); they must not alias
+ *            the inputs or the workspace
+ *   workspace: device, >= nel_head_backward_workspace() bytes (transposed and
+ *            tiled copies of W, h and G)
+ * Requires dt == NEL_BF16 (NEL_EDTYPE), vocab and d multiples of 64 and the
+ * padded token count below 2^24 (NEL_ESHAPE).  n_tokens == 0 sets dw to 0.
+ */
+nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int32_t d,
+                             const void* dlogits, const void* h, const void* w, void* dh,
+                             float* dw, void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace nel_head_backward needs (0 on bad arguments). */
+size_t nel_head_backward_workspace(int64_t n_tokens, int32_t vocab, int32_t d);
+
 /* Bytes of device workspace an op needs (0 on bad arguments). */
 size_t nel_workspace_size(int32_t op, int32_t n_exits, int64_t n_tokens, int32_t vocab);
 
@@ -215,12 +238,13 @@ const char* nel_last_hip_error(void);
  * nel_timing_read sums their elapsed times per kernel.  Kernel ids:
  * 0 junction, 1 heads+loss statistics GEMM, 2 loss merge, 3 means,
  * 4 dlogits finalize, 5 heads+argmax GEMM, 6 argmax merge, 7 accept,
- * 8 weight packing.
+ * 8 weight packing, 9 head-backward operand transposes, 10 dH GEMM, 11 dW GEMM.
  * Process-global and not thread-safe: for benchmarks only.
  */
 enum { NEL_K_JUNCTION = 0, NEL_K_HEADS_LOSS = 1, NEL_K_MERGE = 2, NEL_K_MEANS = 3,
        NEL_K_FINALIZE = 4, NEL_K_HEADS_ARGMAX = 5, NEL_K_ARGMAX_MERGE = 6,
-       NEL_K_ACCEPT = 7, NEL_K_PACK = 8, NEL_K_COUNT = 9 };
+       NEL_K_ACCEPT = 7, NEL_K_PACK = 8, NEL_K_BWD_PACK = 9, NEL_K_BWD_DH = 10,
+       NEL_K_BWD_DW = 11, NEL_K_COUNT = 12 };
 nel_status nel_timing_enable(int32_t on);
 /* Synchronises the device, then returns the summed milliseconds and the
  * number of timed launches of `kernel` since the last reset. */

@@ -12,6 +12,7 @@ call raises.
                                                -> (mean_loss, token_loss, dlogits)
     pack_weights(w)                            -> w in the MFMA-tiled layout (bf16)
     matryoshka_loss_packed / exit_heads_packed -> as above, on packed weights
+    head_backward(dlogits, h, w)               -> (dL/dh bf16, dL/dW fp32) of one exit head
 """
 from __future__ import annotations
 
@@ -23,7 +24,8 @@ __all__ = [
     "NelError", "load", "lib_path", "junction", "exit_heads", "accept_prefix", "matryoshka_loss",
     "workspace_size", "read_flags", "clear_flags", "status_string", "timing_enable",
     "timing_read", "timing_reset", "KERNELS", "OP_LOSS", "OP_HEADS", "FLAG_BAD_ID",
-    "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed",
+    "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed", "head_backward",
+    "head_backward_workspace_size",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +36,7 @@ OP_LOSS, OP_HEADS = 0, 1
 FLAG_BAD_ID, FLAG_BAD_LABEL = 1, 2
 MAX_EXITS = 8
 KERNELS = ["junction", "heads_loss", "merge", "means", "finalize", "heads_argmax",
-           "argmax_merge", "accept", "pack"]
+           "argmax_merge", "accept", "pack", "bwd_pack", "bwd_dh", "bwd_dw"]
 
 
 def lib_path() -> str:
@@ -90,6 +92,8 @@ def load():
         "nel_matryoshka_loss_packed": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, ctypes.c_float,
                                        ctypes.c_float, vp, vp, vp, vp, sz, vp],
         "nel_workspace_size": [c_int, c_int, c_i64, c_int],
+        "nel_head_backward": [c_int, c_i64, c_int, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
+        "nel_head_backward_workspace": [c_i64, c_int, c_int],
         "nel_read_device_flags": [vp, vp, vp],
         "nel_clear_device_flags": [vp, vp],
         "nel_status_string": [c_int],
@@ -102,6 +106,7 @@ def load():
         f.argtypes = args
         f.restype = c_int
     lib.nel_workspace_size.restype = sz
+    lib.nel_head_backward_workspace.restype = sz
     lib.nel_status_string.restype = ctypes.c_char_p
     lib.nel_last_hip_error.argtypes = []
     lib.nel_last_hip_error.restype = ctypes.c_char_p
@@ -370,3 +375,41 @@ def timing_read(kernel) -> tuple:
     ms, cnt = ctypes.c_double(0), ctypes.c_int64(0)
     _check(load().nel_timing_read(k, ctypes.byref(ms), ctypes.byref(cnt)), "nel_timing_read")
     return ms.value, cnt.value
+
+
+def head_backward_workspace_size(n_tokens: int, vocab: int, d: int) -> int:
+    return int(load().nel_head_backward_workspace(n_tokens, vocab, d))
+
+
+_BWD_WS = Workspace()
+
+
+def head_backward(dlogits, h, w, want_dh: bool = True, want_dw: bool = True, dh=None, dw=None,
+                  workspace=None):
+    """Backward of one exit head l = h W^T: (dL/dh = G W in bf16, dL/dW = G^T h in fp32),
+    with G = dlogits (bf16 [n, V]); either output may be skipped (None returned)."""
+    torch = _torch()
+    device = dlogits.device
+    n, V = dlogits.shape
+    d = h.shape[1]
+    for t, name in ((dlogits, "dlogits"), (h, "h"), (w, "w")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    if h.shape[0] != n or w.shape != (V, d):
+        raise ValueError("need dlogits [n, V], h [n, d], w [V, d]")
+    if want_dh and dh is None:
+        dh = torch.empty(n, d, dtype=torch.bfloat16, device=device)
+    if want_dw and dw is None:
+        dw = torch.empty(V, d, dtype=torch.float32, device=device)
+    if not want_dh:
+        dh = None
+    if not want_dw:
+        dw = None
+    need = head_backward_workspace_size(n, V, d)
+    wsb = workspace if workspace is not None else _BWD_WS.get(need, device)
+    _check(load().nel_head_backward(BF16, n, V, d, _dev(dlogits, device, "dlogits"),
+                                    _dev(h, device, "h"), _dev(w, device, "w"),
+                                    _dev(dh, device, "dh"), _dev(dw, device, "dw"),
+                                    wsb.data_ptr(), wsb.numel(), _stream(device)),
+           "nel_head_backward")
+    return dh, dw

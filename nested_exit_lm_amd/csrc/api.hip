@@ -9,6 +9,7 @@
 #include "nel.h"
 #include "common.h"
 #include "internal.h"
+#include "packed_core.h"
 
 using namespace nel;
 
@@ -327,6 +328,69 @@ nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* 
   if (a < b + bytes && b < a + bytes) return NEL_EINVAL;   // overlapping buffers
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(timed(NEL_K_PACK, s, [&] { return launch_pack_weights(vocab, d, w, w_packed, s); }));
+}
+
+// Shape rule of the head backward: bf16, V and d multiples of 64, and every
+// grid and 32-bit in-tile byte offset within range.
+static bool head_bwd_shape_ok(int64_t n, int32_t vocab, int32_t d) {
+  if (n < 0 || vocab < 64 || vocab % 64 != 0 || d < 64 || d % 64 != 0) return false;
+  const int64_t n_pad = (n + 63) / 64 * 64;
+  if (n_pad >= (int64_t{1} << 24) || vocab >= (1 << 24)) return false;
+  return (n_pad / 64) * (vocab / 64) < (int64_t{1} << 31) &&
+         (int64_t{vocab} / 64) * (d / 64) < (int64_t{1} << 31);
+}
+
+size_t nel_head_backward_workspace(int64_t n_tokens, int32_t vocab, int32_t d) {
+  if (!head_bwd_shape_ok(n_tokens, vocab, d)) return 0;
+  return head_bwd_ws_layout(n_tokens, vocab, d).total;
+}
+
+nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int32_t d,
+                             const void* dlogits, const void* h, const void* w, void* dh,
+                             float* dw, void* workspace, size_t ws_bytes, void* stream) {
+  if (dt != NEL_BF16) return NEL_EDTYPE;
+  if (!head_bwd_shape_ok(n_tokens, vocab, d)) return NEL_ESHAPE;
+  if (!dh && !dw) return NEL_EINVAL;
+  if (n_tokens > 0 && (!dlogits || !h || !w)) return NEL_EINVAL;
+  if (misaligned(dlogits) || misaligned(h) || misaligned(w) || misaligned(dh) || misaligned(dw) ||
+      misaligned(workspace))
+    return NEL_EALIGN;
+  const HeadBwdWs L = head_bwd_ws_layout(n_tokens, vocab, d);
+  if (!workspace || ws_bytes < L.total) return NEL_EWORKSPACE;
+  if (n_tokens == 0) {   // no tokens: dH is empty, dW = 0
+    if (!dw) return NEL_OK;
+    hipStream_t s0 = static_cast<hipStream_t>(stream);
+    return from_hip(timed(NEL_K_BWD_DW, s0, [&] {
+      return launch_zero_f32(dw, static_cast<int64_t>(vocab) * d, s0);
+    }));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  void* wt = ws + L.wt;
+  void* ht = ws + L.ht;
+  void* gt = ws + L.gt;
+  hipError_t err;
+  if (dh) {
+    err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack_t(w, vocab, d, vocab, wt, s); });
+    if (err != hipSuccess) return from_hip(err);
+    err = timed(NEL_K_BWD_DH, s, [&] {
+      return launch_bwd_gemm<bf16_t>(wt, d, dlogits, n_tokens, vocab, vocab,
+                                     static_cast<bf16_t*>(dh), d, s);
+    });
+    if (err != hipSuccess) return from_hip(err);
+  }
+  if (dw) {
+    err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack_t(h, n_tokens, d, L.n_pad, ht, s); });
+    if (err != hipSuccess) return from_hip(err);
+    err = timed(NEL_K_BWD_PACK, s,
+                [&] { return launch_transpose(dlogits, n_tokens, vocab, L.n_pad, gt, s); });
+    if (err != hipSuccess) return from_hip(err);
+    err = timed(NEL_K_BWD_DW, s, [&] {
+      return launch_bwd_gemm<float>(ht, d, gt, vocab, L.n_pad, L.n_pad, dw, d, s);
+    });
+    if (err != hipSuccess) return from_hip(err);
+  }
+  return NEL_OK;
 }
 
 nel_status nel_read_device_flags(const int32_t* dev_flags, int32_t* host_flags, void* stream) {

@@ -1,0 +1,232 @@
+// Backward of one exit head (bf16, gfx950): with G = dL/dl (the logit
+// gradients) and l = h W^T (copyedit of Sec. 2 "Modeling": sub-model m ends
+// in its own head W^m in R^{V x D}), the chain rule gives
+//     dH = G W      [N x D] = sum over the vocabulary
+//     dW = G^T h    [V x D] = sum over the tokens.
+// Both run on the MFMA main loop of packed_core.h, whose A operand is
+// MFMA-tiled and whose B operand is row-major with K contiguous:
+//     dH:  A = W^T tiled (rows d, K = vocabulary),  B = G (rows tokens, K = vocabulary)
+//     dW:  A = h^T tiled (rows d, K = tokens),      B = G^T (rows vocabulary, K = tokens)
+// so each lane's accumulators are 16 consecutive d of one output row and the
+// stores are row-major.  W^T and h^T are written tiled by one transposing
+// pass each; G^T by one transpose (all three HBM-bound, into the workspace;
+// K is zero-padded to a multiple of 64).
+#include "common.h"
+#include "internal.h"
+#include "packed_core.h"
+#include "tiles.h"
+
+namespace nel {
+
+namespace {
+
+constexpr int kBwdGroup = 8;   // B tiles per tile group (see tile_coords)
+
+// ---------------------------------------------------------------- packing
+// Tiled A operand of S^T for S [k_rows, R] row-major (R % 64 == 0): element
+// (r, k) = S[k][r] for k < k_rows, 0 up to k_pad.  One workgroup per 64 x 64
+// tile: rows k0..k0+63 of S are read whole (128-byte pieces) into LDS, then
+// every thread writes two 16-byte lane slots of the tile's eight 1 KB blocks,
+// reading its 8 elements down an LDS column.
+__global__ __launch_bounds__(256) void pack_t_kernel(const bf16_t* __restrict__ S,
+                                                     bf16_t* __restrict__ P, int64_t k_rows,
+                                                     int R, int64_t k_pad, int r_tiles) {
+  __shared__ bf16_t tile[64][64 + 2];   // +2: row pitch 132 bytes spreads the column reads
+  const int tid = threadIdx.x;
+  const int rt = static_cast<int>(blockIdx.x % r_tiles);
+  const int64_t kt = blockIdx.x / r_tiles;
+  const int r0 = rt * 64;
+  const int64_t k0 = kt * 64;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + 256 * j, row = i >> 3, ch = i & 7;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k0 + row < k_rows)
+      v = *reinterpret_cast<const u32x4*>(S + (k0 + row) * R + r0 + ch * 8);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[row][ch * 8]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dst[w] = v[w];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + 256 * j;          // 512 lane slots: block (rbl, kpl), lane l
+    const int l = i & 63, blk = i >> 6;   // blk 0..7
+    const int rbl = blk & 1, kpl = blk >> 1;
+    const int r = 32 * rbl + vperm(l & 31);
+    const int kk = 16 * kpl + 8 * (l >> 5);
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      v[w] = static_cast<uint32_t>(tile[kk + 2 * w][r]) |
+             (static_cast<uint32_t>(tile[kk + 2 * w + 1][r]) << 16);
+    const int64_t rb = r0 / 32 + rbl, kp = k0 / 16 + kpl;
+    *reinterpret_cast<u32x4*>(P + ((rb * (k_pad / 16) + kp) * 64 + l) * 8) = v;
+  }
+}
+
+// G [n, V] -> G^T [V, n_pad] row-major, columns n..n_pad-1 zero (V % 64 == 0).
+// 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* __restrict__ G,
+                                                        bf16_t* __restrict__ GT, int64_t n,
+                                                        int vocab, int64_t n_pad, int v_tiles) {
+  __shared__ bf16_t tile[64][64 + 2];
+  const int tid = threadIdx.x;
+  const int vt = static_cast<int>(blockIdx.x % v_tiles);
+  const int64_t tt = blockIdx.x / v_tiles;
+  const int v0 = vt * 64;
+  const int64_t t0 = tt * 64;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + 256 * j, row = i >> 3, ch = i & 7;   // row = token
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (t0 + row < n) v = *reinterpret_cast<const u32x4*>(G + (t0 + row) * vocab + v0 + ch * 8);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[row][ch * 8]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dst[w] = v[w];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + 256 * j, row = i >> 3, ch = i & 7;   // row = vocabulary entry
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      v[w] = static_cast<uint32_t>(tile[ch * 8 + 2 * w][row]) |
+             (static_cast<uint32_t>(tile[ch * 8 + 2 * w + 1][row]) << 16);
+    *reinterpret_cast<u32x4*>(GT + (v0 + row) * n_pad + t0 + ch * 8) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t count) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < count;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------- GEMM
+// out[b][a] = sum_k A[a][k] B[b][k] for a < a_rows, b < b_rows; A tiled
+// (a_rows % 32 == 0, K % 64 == 0), B row-major with row stride ldb.
+template <typename OutT>
+__global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
+    const bf16_t* __restrict__ A, int a_rows, const bf16_t* __restrict__ B, int64_t b_rows,
+    int64_t ldb, int64_t K, OutT* __restrict__ out, int64_t ldo, int n_bt, int n_at) {
+  constexpr int NTB = kPkNTB, NAB = kPkNAB;
+  __shared__ u32x4 hs[2][8 * kPkBRows];
+  const int tid = threadIdx.x, lane = tid & 63, q = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int bt, at;
+  tile_coords(blockIdx.x, n_bt, n_at, kBwdGroup, bt, at);
+  const int64_t b0 = static_cast<int64_t>(bt) * kPkBRows;
+  const int aw = at * kPkARows + wave * (NAB * 32);   // this wavefront's first A row
+  const int rb0 = min(aw >> 5, a_rows / 32 - 1), rb1 = min((aw >> 5) + 1, a_rows / 32 - 1);
+  const PackedLanes pl = packed_lanes(tid);
+  uint32_t boff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t row = min(b0 + pl.brow + 32 * j, b_rows - 1) - b0;
+    boff[j] = static_cast<uint32_t>((row * ldb + pl.bchunk * 8) * 2);
+  }
+  const char* Ab = reinterpret_cast<const char*>(A);
+  const char* Bb = reinterpret_cast<const char*>(B) + b0 * ldb * 2;
+  f32x16 acc[NTB][NAB];
+  packed_tile_gemm<NTB, NAB>(acc, hs, Ab + static_cast<int64_t>(rb0) * 64 * K,
+                             Ab + static_cast<int64_t>(rb1) * 64 * K, Bb, boff, pl,
+                             static_cast<int>(K / kPkBK));
+  // Stores: a wave-uniform tile base and 32-bit lane offsets (the tile is
+  // 128 rows of ldo elements, ldo < 2^24), so no 64-bit address per block
+  // stays live across the main loop.
+  char* obase = reinterpret_cast<char*>(out) + b0 * ldo * static_cast<int64_t>(sizeof(OutT));
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    const int rloc = tb * 32 + q;
+    if (b0 + rloc >= b_rows) continue;
+#pragma unroll
+    for (int ab = 0; ab < NAB; ++ab) {
+      const int a = aw + ab * 32 + 16 * hl;   // a_rows % 32 == 0: all 16 inside or all beyond
+      if (a >= a_rows) continue;
+      const uint32_t off = (static_cast<uint32_t>(rloc) * static_cast<uint32_t>(ldo) +
+                            static_cast<uint32_t>(a)) * static_cast<uint32_t>(sizeof(OutT));
+      u32x4* dst = reinterpret_cast<u32x4*>(obase + off);
+      if constexpr (sizeof(OutT) == 2) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          u32x4 pk;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            pk[j] = pack_bf16x2(acc[tb][ab][8 * h2 + 2 * j], acc[tb][ab][8 * h2 + 2 * j + 1]);
+          dst[h2] = pk;
+        }
+      } else {
+        // (+ 0.0f: storing the accumulators unchanged made the register
+        // allocator spill accumulator blocks inside the main loop)
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) {
+          u32x4 pk;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pk[j] = __float_as_uint(acc[tb][ab][4 * h4 + j] + 0.0f);
+          dst[h4] = pk;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+HeadBwdWs head_bwd_ws_layout(int64_t n, int vocab, int d) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  HeadBwdWs L;
+  L.n_pad = (n + kPkBK - 1) / kPkBK * kPkBK;
+  L.wt = 0;
+  L.ht = L.wt + up(sizeof(bf16_t) * static_cast<size_t>(vocab) * d);
+  L.gt = L.ht + up(sizeof(bf16_t) * static_cast<size_t>(L.n_pad) * d);
+  L.total = L.gt + up(sizeof(bf16_t) * static_cast<size_t>(L.n_pad) * vocab);
+  return L;
+}
+
+hipError_t launch_pack_t(const void* S, int64_t k_rows, int R, int64_t k_pad, void* P,
+                         hipStream_t s) {
+  const int r_tiles = R / 64;
+  const int64_t tiles = static_cast<int64_t>(r_tiles) * (k_pad / 64);
+  hipLaunchKernelGGL(pack_t_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(S), static_cast<bf16_t*>(P), k_rows, R, k_pad,
+                     r_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void* G, int64_t n, int vocab, int64_t n_pad, void* GT,
+                            hipStream_t s) {
+  const int v_tiles = vocab / 64;
+  const int64_t tiles = static_cast<int64_t>(v_tiles) * (n_pad / 64);
+  hipLaunchKernelGGL(transpose_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(G), static_cast<bf16_t*>(GT), n, vocab, n_pad,
+                     v_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t s) {
+  const int64_t blocks = (count + 255) / 256;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
+                     dim3(256), 0, s, p, count);
+  return hipGetLastError();
+}
+
+template <typename OutT>
+hipError_t launch_bwd_gemm(const void* A, int a_rows, const void* B, int64_t b_rows, int64_t ldb,
+                           int64_t K, OutT* out, int64_t ldo, hipStream_t s) {
+  if (b_rows == 0) return hipSuccess;
+  const int n_bt = static_cast<int>((b_rows + kPkBRows - 1) / kPkBRows);
+  const int n_at = (a_rows + kPkARows - 1) / kPkARows;
+  hipLaunchKernelGGL((bwd_gemm_kernel<OutT>), dim3(static_cast<unsigned>(n_bt) * n_at),
+                     dim3(kPkThreads), 0, s, static_cast<const bf16_t*>(A), a_rows,
+                     static_cast<const bf16_t*>(B), b_rows, ldb, K, out, ldo, n_bt, n_at);
+  return hipGetLastError();
+}
+
+template hipError_t launch_bwd_gemm<bf16_t>(const void*, int, const void*, int64_t, int64_t,
+                                            int64_t, bf16_t*, int64_t, hipStream_t);
+template hipError_t launch_bwd_gemm<float>(const void*, int, const void*, int64_t, int64_t,
+                                           int64_t, float*, int64_t, hipStream_t);
+
+}  // namespace nel

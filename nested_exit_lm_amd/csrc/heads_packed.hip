@@ -18,14 +18,10 @@
 // so every operand load is one contiguous 1 KB read.
 //
 // Workgroup: 4 wavefronts, tile 128 tokens x 256 vocabulary entries, two
-// workgroups per CU.  Wavefront w owns vocabulary entries [64w, 64w + 64) of
-// the tile for all 128 tokens (4 x 2 accumulator blocks of 32 x 32).  Per K
-// step of 64: the W operands of the next step are loaded straight into a
-// second register set while the MFMAs consume the current one; the 128 x 64
-// token slice of h is loaded once per workgroup, written to LDS, and read by
-// all four wavefronts.  LDS holds h chunk-major, token (t, chunk c) in 16-byte
-// slot 128 c + (t ^ 2c): the reads of 16 consecutive tokens and the writes of
-// 2 tokens x 8 chunks both cover all 64 banks once per 16-lane pass.
+// workgroups per CU; the main loop (packed_core.h) streams W (the packed A
+// operand) straight into registers and stages the token slice of h (the B
+// operand) through LDS.  Wavefront w owns vocabulary entries [64w, 64w + 64)
+// of the tile for all 128 tokens (4 x 2 accumulator blocks of 32 x 32).
 //
 // Loss epilogue.  The teacher (last exit) runs first; its weights
 // w = exp(l_M - m) (m the tile's row maximum) go to the teacher's own gradient
@@ -37,19 +33,16 @@
 
 #include "common.h"
 #include "internal.h"
+#include "packed_core.h"
 #include "tiles.h"
 
 namespace nel {
 
 namespace {
 
-constexpr int kPkThreads = 256;
-constexpr int kPkTok = 128;
-constexpr int kPkVoc = 256;
-constexpr int kPkBK = 64;      // K per step
-constexpr int kPkNTB = 4;      // token blocks of 32 per wavefront
-constexpr int kPkNVB = 2;      // vocabulary blocks of 32 per wavefront
-constexpr int kPkGroup = 8;    // token tiles per tile group (see tile_coords)
+constexpr int kPkTok = kPkBRows;   // tokens per workgroup (the B rows)
+constexpr int kPkVoc = kPkARows;   // vocabulary entries per workgroup (the A rows)
+constexpr int kPkGroup = 8;        // token tiles per tile group (see tile_coords)
 
 typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 
@@ -95,7 +88,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
   // The exit table is the first kernel argument; indexing it through the
   // kernarg segment pointer keeps per-exit lookups scalar.
   const ExitSet& ex = *(const ExitSet*)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int NTB = kPkNTB, NVB = kPkNVB;
+  constexpr int NTB = kPkNTB, NVB = kPkNAB;
   __shared__ u32x4 hs[2][8 * kPkTok];
   __shared__ float xmax[4][kPkTok];
   __shared__ float xsum[4][kPkTok][2];
@@ -115,100 +108,24 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
   const int vlane = vw + 16 * hl;   // first of this lane's 16 consecutive entries in block 0
   // W row block of the loads for block 0 and block 1, clamped: rows beyond V are never stored
   const int rb0 = min(vw >> 5, vocab / 32 - 1), rb1 = min((vw >> 5) + 1, vocab / 32 - 1);
-  // h staging: chunk i = tid + 256 j of the 128 x 64 slice is token i / 8 = tid / 8 + 32 j,
-  // chunk c = tid % 8.  LDS slot 128 c + (t ^ 2c) = hslot + 32 j (2c < 32 leaves bit 5 alone).
-  const int hc = tid & 7, ht = tid >> 3;
-  const int hslot = hc * kPkTok + (ht ^ (2 * hc));
-  uint32_t hoff[4];   // byte offsets from row t0 (rows beyond n clamped to n - 1)
-  // B fragment of K slice s, token block tb: chunk c = 2s + hl, token 32 tb + q,
-  // slot 128 c + ((32 tb + q) ^ 2c) = bslot[s] + 32 tb.
-  int bslot[4];
-#pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) {
-    const int c = 2 * s4 + hl;
-    bslot[s4] = c * kPkTok + (q ^ (2 * c));
-  }
+  const PackedLanes pl = packed_lanes(tid);
+  uint32_t hoff[4];   // byte offsets of this thread's h chunks from row t0 (rows beyond n clamped)
 
   f32x16 acc[NTB][NVB];
   for (int ei = 0; ei < n_exits; ++ei) {
     const int e = (MODE == kModeLoss) ? (ei == 0 ? n_exits - 1 : ei - 1) : ei;
     const bool teacher = (MODE == kModeLoss) && ei == 0;
     const int D = ex.d[e];
-    const int nsteps = D / kPkBK;
     // wave-uniform bases; per-lane 32-bit byte offsets
     const char* __restrict__ Hb = static_cast<const char*>(ex.h[e]) + t0 * D * 2;
     const char* __restrict__ P = static_cast<const char*>(ex.w[e]);
-    const char* __restrict__ W0 = P + static_cast<int64_t>(rb0) * 64 * D;
-    const char* __restrict__ W1 = P + static_cast<int64_t>(rb1) * 64 * D;
-    const uint32_t woff = static_cast<uint32_t>(lane) * 16u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t row = min(t0 + ht + 32 * j, n - 1) - t0;
-      hoff[j] = static_cast<uint32_t>((row * D + hc * 8) * 2);
+      const int64_t row = min(t0 + pl.brow + 32 * j, n - 1) - t0;
+      hoff[j] = static_cast<uint32_t>((row * D + pl.bchunk * 8) * 2);
     }
-
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[tb][vb][r] = 0.f;
-
-    u32x4 R0[NVB][4], R1[NVB][4], hr[4];
-    // W operands of step g: 1 KB blocks kp = 4g + s of the lane's two row blocks
-    auto load_w = [&](u32x4 (&dst)[NVB][4], int g) {
-      const char* a0 = W0 + static_cast<int64_t>(g) * 4096;
-      const char* a1 = W1 + static_cast<int64_t>(g) * 4096;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        dst[0][s4] = *reinterpret_cast<const u32x4*>(a0 + woff + s4 * 1024);
-        dst[1][s4] = *reinterpret_cast<const u32x4*>(a1 + woff + s4 * 1024);
-      }
-    };
-    auto load_h = [&](int g) {
-      const char* a = Hb + static_cast<int64_t>(g) * (kPkBK * 2);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hr[j] = *reinterpret_cast<const u32x4*>(a + hoff[j]);
-    };
-    auto store_h = [&](int st) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hs[st][hslot + 32 * j] = hr[j];
-    };
-    auto mfma = [&](const u32x4 (&cur)[NVB][4], int st) {
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        bf16x8 b[NTB];
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) b[tb] = __builtin_bit_cast(bf16x8, hs[st][bslot[s4] + 32 * tb]);
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, cur[vb][s4]);
-#pragma unroll
-          for (int tb = 0; tb < NTB; ++tb)
-            acc[tb][vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[tb], acc[tb][vb], 0, 0, 0);
-        }
-      }
-    };
-    // Step g: prefetch step g + 1 (the last step re-reads itself), compute
-    // step g from LDS stage st, publish the prefetched h slice in stage st ^ 1.
-    auto step = [&](const u32x4 (&cur)[NVB][4], u32x4 (&nxt)[NVB][4], int g, int st) {
-      const int gn = g + 1 < nsteps ? g + 1 : g;
-      load_h(gn);
-      load_w(nxt, gn);
-      mfma(cur, st);
-      store_h(st ^ 1);
-      __syncthreads();
-    };
-    load_h(0);
-    store_h(0);
-    load_w(R0, 0);
-    __syncthreads();
-    int g = 0;
-    for (; g + 2 <= nsteps; g += 2) {
-      step(R0, R1, g, 0);
-      step(R1, R0, g + 1, 1);
-    }
-    if (g < nsteps) step(R0, R1, g, 0);
+    packed_tile_gemm<NTB, NVB>(acc, hs, P + static_cast<int64_t>(rb0) * 64 * D,
+                               P + static_cast<int64_t>(rb1) * 64 * D, Hb, hoff, pl, D / kPkBK);
 
     // vocabulary entries beyond V (last tile only) vanish under exp and never win a max
     if (vt * kPkVoc + kPkVoc > vocab) {

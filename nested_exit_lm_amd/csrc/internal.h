@@ -66,6 +66,25 @@ inline HeadsWs heads_ws_layout(int n_exits, int64_t n, int vocab) {
   return L;
 }
 
+// Workspace of the head backward (byte offsets): W^T and h^T in the tiled
+// layout, G^T row-major; K of the token dimension padded to n_pad.
+struct HeadBwdWs {
+  int64_t n_pad;
+  size_t wt, ht, gt, total;
+};
+HeadBwdWs head_bwd_ws_layout(int64_t n, int vocab, int d);
+// Tiled A operand of S^T for S [k_rows, R] row-major, K zero-padded to k_pad.
+hipError_t launch_pack_t(const void* S, int64_t k_rows, int R, int64_t k_pad, void* P,
+                         hipStream_t s);
+// G [n, V] -> G^T [V, n_pad], zero-padded.
+hipError_t launch_transpose(const void* G, int64_t n, int vocab, int64_t n_pad, void* GT,
+                            hipStream_t s);
+hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t s);
+// out[b][a] = sum_k A[a][k] B[b][k]; A tiled (a_rows x K), B row-major (b_rows x ldb).
+template <typename OutT>
+hipError_t launch_bwd_gemm(const void* A, int a_rows, const void* B, int64_t b_rows, int64_t ldb,
+                           int64_t K, OutT* out, int64_t ldo, hipStream_t s);
+
 template <typename T>
 hipError_t launch_junction(int64_t n, int d_in, int d_out, int vocab, const void* h,
                            const int32_t* ids, const void* emb, void* out, int32_t* flags,

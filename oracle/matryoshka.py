@@ -63,6 +63,18 @@ def heads(hs: Sequence[np.ndarray], ws: Sequence[np.ndarray]) -> List[np.ndarray
     return [_f64(h) @ _f64(w).T for h, w in zip(hs, ws)]
 
 
+def head_backward(g: np.ndarray, h: np.ndarray, w: np.ndarray):
+    """Backward of one linear head l = h W^T (the head of `heads`): with
+    G = dL/dl, the chain rule gives dL/dh = G W and dL/dW = G^T h.
+
+    Copyedit of Sec. 2 "Modeling" for the head; G is what `matryoshka_grad`
+    returns for that exit (the teacher's under stop-gradient).  Returns
+    (dh [N, D], dw [V, D]).
+    """
+    g64 = _f64(g)
+    return g64 @ _f64(w), g64.T @ _f64(h)
+
+
 # ---------------------------------------------------------------------------
 # Softmax pieces
 # ---------------------------------------------------------------------------

@@ -20,7 +20,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = nel.load()
     syms = declared_symbols()
-    assert len(syms) == 15
+    assert len(syms) == 17
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -140,6 +140,29 @@ def test_packed_host_validation():
     assert lib.nel_exit_heads_packed(1, 2, 4, 250, d2, p2, p2, None, FAKE, FAKE, need, None) == -2
     assert lib.nel_exit_heads_packed(1, 2, 4, 256, _arr(ctypes.c_int32, 64, 100), p2, p2, None,
                                      FAKE, FAKE, need, None) == -2
+
+
+def test_head_backward_host_validation():
+    lib = nel.load()
+    need = nel.head_backward_workspace_size(100, 256, 128)
+    assert need > 0
+    assert nel.head_backward_workspace_size(100, 250, 128) == 0
+    assert nel.head_backward_workspace_size(100, 256, 96) == 0
+
+    def call(dt=1, n=100, V=256, d=128, g=FAKE, h=FAKE, w=FAKE, dh=FAKE, dw=FAKE, ws=FAKE,
+             wsb=need):
+        return lib.nel_head_backward(dt, n, V, d, g, h, w, dh, dw, ws, wsb, None)
+
+    assert call(dt=0) == -3                 # bf16 only
+    assert call(V=250) == -2
+    assert call(d=100) == -2
+    assert call(n=-1) == -2
+    assert call(dh=None, dw=None) == -1     # nothing to compute
+    assert call(g=None) == -1
+    assert call(h=MIS) == -4
+    assert call(dw=MIS) == -4
+    assert call(ws=None) == -5
+    assert call(wsb=need - 1) == -5
 
 
 def test_one_hip_runtime_after_load():

@@ -1,0 +1,109 @@
+"""Backward of one exit head (nel_head_backward) against the oracle:
+dH = G W (bf16 output) and dW = G^T h (fp32 output), G = the logit gradients.
+
+Bars: fp32 accumulation in any order is within gamma_K * (|A| |B|) of the
+exact product (products of bf16 values are exact in fp32), with
+gamma_K = 2 K 2^-24; the bf16 output adds half an ulp (2^-8 relative)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import dev_tensor, log, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def bound(a, b, K):
+    return 2.0 * K * 2.0 ** -24 * (np.abs(a) @ np.abs(b))
+
+
+def check(nel, g, h, w, want_dh=True, want_dw=True):
+    import torch
+    G, H, W = dev_tensor(g, "bf16"), dev_tensor(h, "bf16"), dev_tensor(w, "bf16")
+    dh, dw = nel.head_backward(G, H, W, want_dh=want_dh, want_dw=want_dw)
+    torch.cuda.synchronize()
+    ref_dh, ref_dw = oracle.head_backward(g, h, w)
+    n, V = g.shape
+    if want_dh:
+        got = to_np(dh)
+        b = bound(g, w, V)
+        tol = 2.0 ** -8 * (np.abs(ref_dh) + b) + b + 1e-30
+        assert np.all(np.abs(got - ref_dh) <= tol), f"dh: worst {np.max(np.abs(got - ref_dh) / tol):.3g} x bound"
+    else:
+        assert dh is None
+    if want_dw:
+        got = to_np(dw)
+        tol = bound(g.T, h, n) + 1e-30
+        assert np.all(np.abs(got - ref_dw) <= tol), f"dw: worst {np.max(np.abs(got - ref_dw) / tol):.3g} x bound"
+    else:
+        assert dw is None
+
+
+def oracle_gradients(widths, V, B, S, seed):
+    """A suite and the oracle's bf16-rounded logit gradients of every exit."""
+    s = synth.make_suite(widths, V, B, S, seed=seed)
+    g = oracle.matryoshka_grad(oracle.heads(s.h, s.w), s.labels, 0.3)
+    return s, [synth.round_to_bf16(gm.astype(np.float32)) for gm in g]
+
+
+CASES = [
+    # widths (all multiples of 64), V, batch, seq: ragged token counts, d below and
+    # above one 256-row tile, a vocabulary of one K step
+    ("3exit-ragged", (64, 128, 192), 1024, 3, 100, 61),
+    ("partial-A-tile", (320,), 512, 1, 129, 62),
+    ("tiny-vocab", (64, 128), 64, 1, 65, 63),
+    ("one-token", (128,), 256, 1, 1, 64),
+]
+
+
+@pytest.mark.parametrize("name,widths,V,B,S,seed", CASES, ids=[c[0] for c in CASES])
+def test_head_backward_small(nel, name, widths, V, B, S, seed):
+    s, g = oracle_gradients(widths, V, B, S, seed)
+    log(f"[bwd] {name}: n={s.n_tokens} V={V} widths={widths}")
+    for m in range(s.n_exits):
+        check(nel, g[m], s.h[m], s.w[m])
+
+
+def test_head_backward_single_outputs(nel):
+    s, g = oracle_gradients((128, 256), 512, 2, 70, 65)
+    check(nel, g[1], s.h[1], s.w[1], want_dh=True, want_dw=False)
+    check(nel, g[0], s.h[0], s.w[0], want_dh=False, want_dw=True)
+
+
+def test_head_backward_no_tokens_zeroes_dw(nel):
+    import torch
+    V, d = 128, 64
+    G = torch.empty(0, V, dtype=torch.bfloat16, device="cuda:0")
+    H = torch.empty(0, d, dtype=torch.bfloat16, device="cuda:0")
+    W = torch.ones(V, d, dtype=torch.bfloat16, device="cuda:0")
+    dw = torch.full((V, d), 7.0, dtype=torch.float32, device="cuda:0")
+    _, out = nel.head_backward(G, H, W, want_dh=False, dw=dw)
+    assert float(out.abs().max()) == 0.0
+
+
+def test_head_backward_full_size_sampled(nel):
+    """The benchmark's largest exit (n = 16384, V = 32768, d = 4352) on seeded
+    synthetic inputs; sampled rows of dH and of dW against the oracle."""
+    import torch
+    n, V, d = 16384, 32768, 4352
+    r = np.random.default_rng(66)
+    h = synth.round_to_bf16((r.standard_normal((n, d), dtype=np.float32) * 4.0))
+    w = synth.round_to_bf16((r.standard_normal((V, d), dtype=np.float32) * 0.02))
+    g = np.empty((n, V), dtype=np.float32)
+    for i in range(0, n, 2048):
+        g[i:i + 2048] = synth.round_to_bf16(r.standard_normal((min(2048, n - i), V), dtype=np.float32) * 1e-3)
+    log(f"[bwd] full size n={n} V={V} d={d}")
+    G, H, W = dev_tensor(g, "bf16"), dev_tensor(h, "bf16"), dev_tensor(w, "bf16")
+    dh, dw = nel.head_backward(G, H, W)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, n - 1], r.choice(n, 13, replace=False)]))
+    cols = np.unique(np.concatenate([[0, V - 1], r.choice(V, 14, replace=False)]))
+    got_dh = to_np(dh[torch.from_numpy(rows).cuda()])
+    ref_dh = g[rows].astype(np.float64) @ w.astype(np.float64)
+    b = bound(g[rows], w, V)
+    tol = 2.0 ** -8 * (np.abs(ref_dh) + b) + b
+    assert np.all(np.abs(got_dh - ref_dh) <= tol)
+    got_dw = to_np(dw[torch.from_numpy(cols).cuda()])
+    ref_dw = g[:, cols].T.astype(np.float64) @ h.astype(np.float64)
+    assert np.all(np.abs(got_dw - ref_dw) <= bound(g[:, cols].T, h, n))

@@ -166,6 +166,66 @@ def test_gradient_matches_torch_autograd_with_detached_teacher():
         np.testing.assert_allclose(g[m], ls[m].grad.numpy(), atol=1e-14)
 
 
+# ------------------------------------------------------------- head backward
+def test_head_backward_matches_torch_autograd_through_the_heads():
+    """dL/dh_m and dL/dW^m of the whole forward (heads + loss, teacher detached)
+    by torch autograd equal head_backward(matryoshka_grad, h_m, W^m)."""
+    r = rng(14)
+    D, V, N = (3, 5, 7), 11, 6
+    hs = [torch.tensor(r.standard_normal((N, d)), requires_grad=True) for d in D]
+    ws = [torch.tensor(r.standard_normal((V, d)) * 0.5, requires_grad=True) for d in D]
+    y = torch.tensor(r.integers(0, V, N))
+    ls = [h @ w.T for h, w in zip(hs, ws)]
+    p = torch.softmax(ls[-1], dim=1).detach()
+    tot = F.cross_entropy(ls[-1], y, reduction="sum")
+    for m in range(2):
+        tot = tot + 0.7 * F.cross_entropy(ls[m], y, reduction="sum") \
+            - 0.3 * (p * torch.log_softmax(ls[m], dim=1)).sum()
+    tot.backward()
+    g = oracle.matryoshka_grad([l.detach().numpy() for l in ls], y.numpy(), 0.3)
+    for m in range(3):
+        dh, dw = oracle.head_backward(g[m], hs[m].detach().numpy(), ws[m].detach().numpy())
+        np.testing.assert_allclose(dh, hs[m].grad.numpy(), atol=1e-13)
+        np.testing.assert_allclose(dw, ws[m].grad.numpy(), atol=1e-13)
+
+
+def test_head_backward_finite_differences_student_exit():
+    """Central differences of the total loss in a student's h and W."""
+    r = rng(15)
+    D, V, N = (2, 4), 5, 3
+    hs = [r.standard_normal((N, d)) for d in D]
+    ws = [r.standard_normal((V, d)) * 0.7 for d in D]
+    y = r.integers(0, V, N)
+
+    def total(hs_, ws_):
+        return oracle.matryoshka_loss(oracle.heads(hs_, ws_), y, 0.3)["total"].sum()
+
+    g = oracle.matryoshka_grad(oracle.heads(hs, ws), y, 0.3)
+    dh, dw = oracle.head_backward(g[0], hs[0], ws[0])
+    eps = 1e-6
+    for (arr, grad) in ((hs[0], dh), (ws[0], dw)):
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            fp = total(hs, ws)
+            arr[idx] = old - eps
+            fm = total(hs, ws)
+            arr[idx] = old
+            assert grad[idx] == pytest.approx((fp - fm) / (2 * eps), abs=1e-8)
+
+
+def test_head_backward_weight_gradient_columns_sum_to_zero():
+    """Rows of G sum to zero, so sum_v dW[v] = sum_t (sum_v G[t, v]) h[t] = 0."""
+    r = rng(16)
+    ls = [r.standard_normal((9, 40)) for _ in range(2)]
+    g = oracle.matryoshka_grad(ls, r.integers(0, 40, 9), 0.3)
+    h = r.standard_normal((9, 8))
+    w = r.standard_normal((40, 8))
+    for gm in g:
+        _, dw = oracle.head_backward(gm, h, w)
+        np.testing.assert_allclose(dw.sum(axis=0), 0, atol=1e-12)
+
+
 # --------------------------------------------------------------------- heads
 def test_heads_against_exactly_rounded_dot_products():
     r = rng(13)

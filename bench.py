@@ -224,7 +224,7 @@ def main():
     if not args.no_verify:
         out["verify_102x7"] = bench_verify(nel, torch, synth, dev, args)
     if not args.no_backward:
-        out["head_backward"] = bench_backward(nel, torch, hs, ws, dl, args)
+        out["backward"] = bench_backward(nel, torch, hs, ws, dl, args, ids=ids, embs=embs)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
         out["cpu_baseline"] = cpu_baseline(s, args.cpu_seconds)
@@ -278,9 +278,10 @@ def summarize_counters(fetch_dir, write_dir):
     print(json.dumps(res))
 
 
-def bench_backward(nel, torch, hs, ws, dl, args):
+def bench_backward(nel, torch, hs, ws, dl, args, ids=None, embs=None):
     """Backward of the three exit heads on the step's own logit gradients:
-    dh_m = G_m W^m (bf16) and dW^m = G_m^T h_m (fp32), with the operand transposes."""
+    dh_m = G_m W^m (bf16) and dW^m = G_m^T h_m (fp32), with the operand transposes;
+    and the backward of both junctions on seeded synthetic upstream gradients."""
     N, V = dl[0].shape
     D = [h.shape[1] for h in hs]
     need = max(nel.head_backward_workspace_size(N, V, d) for d in D)
@@ -314,6 +315,33 @@ def bench_backward(nel, torch, hs, ws, dl, args):
     res["dw_tflops"] = flops / (res["bwd_dw_ms"] / 1e3) / 1e12
     res["dh_mfma_frac"] = res["dh_tflops"] / BF16_PEAK_TFLOPS
     res["dw_mfma_frac"] = res["dw_tflops"] / BF16_PEAK_TFLOPS
+    if ids is not None:
+        g = torch.Generator(device=hs[0].device)
+        g.manual_seed(7)
+        douts = [(torch.randn(N, D[m], generator=g, device=hs[0].device) * 1e-2).bfloat16()
+                 for m in (1, 2)]
+        jdh = [torch.empty_like(hs[m]) for m in (0, 1)]
+        jde = [torch.empty(V, D[m] - D[m - 1], dtype=torch.float32, device=hs[0].device)
+               for m in (1, 2)]
+
+        def jstep():
+            for i, m in enumerate((1, 2)):
+                nel.junction_backward(hs[m - 1], ids, embs[m], douts[i], dh=jdh[i], demb=jde[i])
+
+        jstep()
+        torch.cuda.synchronize()
+        nel.timing_reset()
+        nel.timing_enable(True)
+        for _ in range(steps):
+            jstep()
+        torch.cuda.synchronize()
+        nel.timing_enable(False)
+        tot, cnt = nel.timing_read("junction_bwd")
+        # per token: read h, dout, the embedding row; write dh; per vocabulary row: write demb
+        jbytes = sum(N * (2 * D[m - 1] + 2 * D[m] + 2 * (D[m] - D[m - 1]) + 2 * D[m - 1] + 4)
+                     + V * 4 * (D[m] - D[m - 1]) for m in (1, 2))
+        res["junction_bwd_ms"] = tot / steps
+        res["junction_bwd_gbs"] = jbytes / (tot / steps / 1e3) / 1e9
     return res
 
 

@@ -194,6 +194,32 @@ nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens
                                  int32_t* argmax, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Backward of the junction (nel_junction).  With g = emb[ids[t]], a = ||h[t]||,
+ * b = ||g||, the forward out[t] = [h[t] b / a, g] and the upstream gradient
+ * dout[t] = [dh_up, dg_up] (split at d_in), the chain rule gives
+ *     dh[t]   = (b / a) (dh_up - h[t] (h[t] . dh_up) / a^2)        (0 if a or b is 0)
+ *     demb[v] = sum_{t: ids[t] = v} (dg_up[t] + c_t g / b),  c_t = (h[t] . dh_up) / a
+ * ("Matryoshka Language Model Suites", junction paragraph, for the forward).
+ * stop_grad != 0 is arm (B) of follow-up 2 on "Is nesting the cheapest way to
+ * build a model suite?": no gradient reaches h through the junction (dh = 0)
+ * while the embedding still receives both terms.
+ *   h:     [n_tokens, d_in] dt, or NULL when d_in == 0 (block 1)
+ *   ids:   [n_tokens] int32;  emb: [vocab, d_out - d_in] dt;  dout: [n_tokens, d_out] dt
+ *   dh:    NULL or [n_tokens, d_in] dt (must be NULL when d_in == 0)
+ *   demb:  NULL or fp32 [vocab, d_out - d_in], every row written (0 for ids
+ *          no token uses); each row is summed in token order (deterministic)
+ *   flags: device flag word or NULL; a bad id sets NEL_FLAG_BAD_ID, NaNs its dh
+ *          row and contributes nothing to demb
+ *   workspace: >= nel_junction_backward_workspace(n_tokens, vocab) bytes
+ */
+nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_out,
+                                 int32_t vocab, const void* h, const int32_t* ids,
+                                 const void* emb, const void* dout, int32_t stop_grad, void* dh,
+                                 float* demb, int32_t* flags, void* workspace, size_t ws_bytes,
+                                 void* stream);
+size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t vocab);
+
+/*
  * Backward of one exit head (the step after the loss: l = h W^T with W the
  * exit's head, copyedit of Sec. 2 "Modeling"; G = dL/dl from
  * nel_matryoshka_loss*).  By the chain rule, with fp32 accumulation:
@@ -238,13 +264,14 @@ const char* nel_last_hip_error(void);
  * nel_timing_read sums their elapsed times per kernel.  Kernel ids:
  * 0 junction, 1 heads+loss statistics GEMM, 2 loss merge, 3 means,
  * 4 dlogits finalize, 5 heads+argmax GEMM, 6 argmax merge, 7 accept,
- * 8 weight packing, 9 head-backward operand transposes, 10 dH GEMM, 11 dW GEMM.
+ * 8 weight packing, 9 head-backward operand transposes, 10 dH GEMM, 11 dW GEMM,
+ * 12 junction backward.
  * Process-global and not thread-safe: for benchmarks only.
  */
 enum { NEL_K_JUNCTION = 0, NEL_K_HEADS_LOSS = 1, NEL_K_MERGE = 2, NEL_K_MEANS = 3,
        NEL_K_FINALIZE = 4, NEL_K_HEADS_ARGMAX = 5, NEL_K_ARGMAX_MERGE = 6,
        NEL_K_ACCEPT = 7, NEL_K_PACK = 8, NEL_K_BWD_PACK = 9, NEL_K_BWD_DH = 10,
-       NEL_K_BWD_DW = 11, NEL_K_COUNT = 12 };
+       NEL_K_BWD_DW = 11, NEL_K_JUNCTION_BWD = 12, NEL_K_COUNT = 13 };
 nel_status nel_timing_enable(int32_t on);
 /* Synchronises the device, then returns the summed milliseconds and the
  * number of timed launches of `kernel` since the last reset. */

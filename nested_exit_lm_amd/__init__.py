@@ -13,6 +13,7 @@ call raises.
     pack_weights(w)                            -> w in the MFMA-tiled layout (bf16)
     matryoshka_loss_packed / exit_heads_packed -> as above, on packed weights
     head_backward(dlogits, h, w)               -> (dL/dh bf16, dL/dW fp32) of one exit head
+    junction_backward(h, ids, emb, dout)       -> (dL/dh, dL/demb fp32) of one junction
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ __all__ = [
     "workspace_size", "read_flags", "clear_flags", "status_string", "timing_enable",
     "timing_read", "timing_reset", "KERNELS", "OP_LOSS", "OP_HEADS", "FLAG_BAD_ID",
     "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed", "head_backward",
-    "head_backward_workspace_size",
+    "head_backward_workspace_size", "junction_backward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +37,7 @@ OP_LOSS, OP_HEADS = 0, 1
 FLAG_BAD_ID, FLAG_BAD_LABEL = 1, 2
 MAX_EXITS = 8
 KERNELS = ["junction", "heads_loss", "merge", "means", "finalize", "heads_argmax",
-           "argmax_merge", "accept", "pack", "bwd_pack", "bwd_dh", "bwd_dw"]
+           "argmax_merge", "accept", "pack", "bwd_pack", "bwd_dh", "bwd_dw", "junction_bwd"]
 
 
 def lib_path() -> str:
@@ -94,6 +95,9 @@ def load():
         "nel_workspace_size": [c_int, c_int, c_i64, c_int],
         "nel_head_backward": [c_int, c_i64, c_int, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
         "nel_head_backward_workspace": [c_i64, c_int, c_int],
+        "nel_junction_backward": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, c_int, vp, vp,
+                                  vp, vp, sz, vp],
+        "nel_junction_backward_workspace": [c_i64, c_int],
         "nel_read_device_flags": [vp, vp, vp],
         "nel_clear_device_flags": [vp, vp],
         "nel_status_string": [c_int],
@@ -107,6 +111,7 @@ def load():
         f.restype = c_int
     lib.nel_workspace_size.restype = sz
     lib.nel_head_backward_workspace.restype = sz
+    lib.nel_junction_backward_workspace.restype = sz
     lib.nel_status_string.restype = ctypes.c_char_p
     lib.nel_last_hip_error.argtypes = []
     lib.nel_last_hip_error.restype = ctypes.c_char_p
@@ -413,3 +418,42 @@ def head_backward(dlogits, h, w, want_dh: bool = True, want_dw: bool = True, dh=
                                     wsb.data_ptr(), wsb.numel(), _stream(device)),
            "nel_head_backward")
     return dh, dw
+
+
+_JBWD_WS = Workspace()
+
+
+def junction_backward(h, ids, emb, dout, stop_grad: bool = False, want_dh: bool = True,
+                      want_demb: bool = True, dh=None, demb=None, flags=None, workspace=None):
+    """Gradients of junction(h, ids, emb) given dout = dL/dout: (dL/dh in h's dtype or None,
+    dL/demb fp32 [V, d_out - d_in] or None).  h may be None (block 1)."""
+    torch = _torch()
+    device = emb.device
+    n = ids.shape[0]
+    d_in = 0 if h is None else h.shape[1]
+    de = emb.shape[1]
+    if dout.shape != (n, d_in + de) or dout.dtype != emb.dtype:
+        raise ValueError("dout must be [n, d_in + d_emb] in the embedding's dtype")
+    if h is not None and (h.dtype != emb.dtype or h.shape[0] != n):
+        raise ValueError("h must be [n, d_in] in the embedding's dtype")
+    if ids.dtype != torch.int32:
+        raise TypeError("ids must be int32")
+    if want_dh and d_in > 0 and dh is None:
+        dh = torch.empty(n, d_in, dtype=emb.dtype, device=device)
+    if not want_dh or d_in == 0:
+        dh = None
+    if want_demb and demb is None:
+        demb = torch.empty(emb.shape[0], de, dtype=torch.float32, device=device)
+    if not want_demb:
+        demb = None
+    lib = load()
+    need = int(lib.nel_junction_backward_workspace(n, emb.shape[0]))
+    wsb = workspace if workspace is not None else _JBWD_WS.get(need, device)
+    _check(lib.nel_junction_backward(_dt(emb), n, d_in, d_in + de, emb.shape[0],
+                                     _dev(h, device, "h"), _dev(ids, device, "ids"),
+                                     _dev(emb, device, "emb"), _dev(dout, device, "dout"),
+                                     1 if stop_grad else 0, _dev(dh, device, "dh"),
+                                     _dev(demb, device, "demb"), _dev(flags, device, "flags"),
+                                     wsb.data_ptr(), wsb.numel(), _stream(device)),
+           "nel_junction_backward")
+    return dh, demb

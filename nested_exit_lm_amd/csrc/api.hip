@@ -330,6 +330,41 @@ nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* 
   return from_hip(timed(NEL_K_PACK, s, [&] { return launch_pack_weights(vocab, d, w, w_packed, s); }));
 }
 
+size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t vocab) {
+  if (n_tokens < 0 || vocab < 1) return 0;
+  return junction_bwd_ws_layout(n_tokens, vocab).total;
+}
+
+nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_out,
+                                 int32_t vocab, const void* h, const int32_t* ids,
+                                 const void* emb, const void* dout, int32_t stop_grad, void* dh,
+                                 float* demb, int32_t* flags, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
+  if (n_tokens < 0 || d_in < 0 || d_out <= d_in || vocab < 1) return NEL_ESHAPE;
+  if (n_tokens > (int64_t{1} << 40)) return NEL_ESHAPE;
+  if (!dh && !demb) return NEL_EINVAL;
+  if (d_in == 0 && dh) return NEL_EINVAL;   // block 1 has no h to differentiate
+  if (n_tokens > 0 && (!ids || !emb || !dout || (d_in > 0 && !h))) return NEL_EINVAL;
+  if (demb && !emb) return NEL_EINVAL;
+  if (misaligned(h) || misaligned4(ids) || misaligned(emb) || misaligned(dout) ||
+      misaligned(dh) || misaligned(demb) || misaligned4(flags) || misaligned(workspace))
+    return NEL_EALIGN;
+  const JunctionBwdWs L = junction_bwd_ws_layout(n_tokens, vocab);
+  if (!workspace || ws_bytes < L.total) return NEL_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* ct = reinterpret_cast<float*>(ws + L.ct);
+  int32_t* used = reinterpret_cast<int32_t*>(ws + L.used);
+  return from_hip(timed(NEL_K_JUNCTION_BWD, s, [&] {
+    return dt == NEL_BF16
+               ? launch_junction_backward<bf16_t>(n_tokens, d_in, d_out, vocab, h, ids, emb, dout,
+                                                  stop_grad != 0, dh, demb, ct, used, flags, s)
+               : launch_junction_backward<float>(n_tokens, d_in, d_out, vocab, h, ids, emb, dout,
+                                                 stop_grad != 0, dh, demb, ct, used, flags, s);
+  }));
+}
+
 // Shape rule of the head backward: bf16, V and d multiples of 64, and every
 // grid and 32-bit in-tile byte offset within range.
 static bool head_bwd_shape_ok(int64_t n, int32_t vocab, int32_t d) {

@@ -66,6 +66,17 @@ inline HeadsWs heads_ws_layout(int n_exits, int64_t n, int vocab) {
   return L;
 }
 
+// Workspace of the junction backward: c_t per token, row-used marks per id.
+struct JunctionBwdWs {
+  size_t ct, used, total;
+};
+JunctionBwdWs junction_bwd_ws_layout(int64_t n, int vocab);
+template <typename T>
+hipError_t launch_junction_backward(int64_t n, int d_in, int d_out, int vocab, const void* h,
+                                    const int32_t* ids, const void* emb, const void* dout,
+                                    int stop_grad, void* dh, float* demb, float* ct,
+                                    int32_t* used, int32_t* flags, hipStream_t s);
+
 // Workspace of the head backward (byte offsets): W^T and h^T in the tiled
 // layout, G^T row-major; K of the token dimension padded to n_pad.
 struct HeadBwdWs {

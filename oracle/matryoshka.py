@@ -53,6 +53,43 @@ def junction(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray) -> np.nd
 # ---------------------------------------------------------------------------
 # Heads
 # ---------------------------------------------------------------------------
+def junction_backward(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray,
+                      dout: np.ndarray, stop_grad: bool = False):
+    """Gradients of `junction` by the chain rule, given dL/dout.
+
+    Forward per token: g = e[x], a = ||h||, b = ||g||, out = [h b / a, g]
+    (junction paragraph of the paper summary; 0 rescaled half if a or b is 0).
+    With dout = [du, dg] split at d_in:
+        dL/dh   = (b / a) (du - h (h . du) / a^2)
+        dL/dg   = dg + ((h . du) / a) g / b      (d||g||/dg = g / ||g||)
+    and dL/de[v] sums dL/dg over the tokens with id v.  stop_grad (arm (B) of
+    follow-up 2 on the follow-ups page: every block learns only from its own
+    exit) treats h as a constant: dL/dh = 0, dL/dg unchanged.
+    Returns (dh or None when h is None, demb [V, d_out - d_in]).
+    """
+    g = _f64(emb)[ids]
+    dout = _f64(dout)
+    d_in = 0 if h is None else h.shape[1]
+    du, dg = dout[:, :d_in], dout[:, d_in:]
+    demb = np.zeros_like(_f64(emb))
+    np.add.at(demb, ids, dg)
+    if h is None:
+        return None, demb
+    h = _f64(h)
+    a = np.linalg.norm(h, axis=1)
+    b = np.linalg.norm(g, axis=1)
+    live = (a > 0) & (b > 0)
+    hd = np.sum(h * du, axis=1)
+    sa = np.where(live, a, 1.0)
+    sb = np.where(live, b, 1.0)
+    dh = np.where(live, b / sa, 0.0)[:, None] * (du - h * (hd / sa ** 2)[:, None])
+    if stop_grad:
+        dh = np.zeros_like(h)
+    c = np.where(live, hd / sa, 0.0)
+    np.add.at(demb, ids, (c / sb)[:, None] * g)
+    return dh, demb
+
+
 def heads(hs: Sequence[np.ndarray], ws: Sequence[np.ndarray]) -> List[np.ndarray]:
     """Per-exit linear LM heads: l_m = h_m W^m^T.
 

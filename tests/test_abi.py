@@ -20,7 +20,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = nel.load()
     syms = declared_symbols()
-    assert len(syms) == 17
+    assert len(syms) == 19
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -161,6 +161,28 @@ def test_head_backward_host_validation():
     assert call(g=None) == -1
     assert call(h=MIS) == -4
     assert call(dw=MIS) == -4
+    assert call(ws=None) == -5
+    assert call(wsb=need - 1) == -5
+
+
+def test_junction_backward_host_validation():
+    lib = nel.load()
+    need = int(lib.nel_junction_backward_workspace(10, 50))
+    assert need > 0
+
+    def call(dt=1, n=10, d_in=8, d_out=16, V=50, h=FAKE, ids=FAKE, emb=FAKE, dout=FAKE, sg=0,
+             dh=FAKE, demb=FAKE, ws=FAKE, wsb=need):
+        return lib.nel_junction_backward(dt, n, d_in, d_out, V, h, ids, emb, dout, sg, dh, demb,
+                                         None, ws, wsb, None)
+
+    assert call(dt=4) == -3
+    assert call(d_out=8) == -2
+    assert call(V=0) == -2
+    assert call(dh=None, demb=None) == -1
+    assert call(d_in=0, h=None) == -1          # block 1 has no dh
+    assert call(h=None) == -1
+    assert call(ids=MIS4) == -4
+    assert call(demb=MIS) == -4
     assert call(ws=None) == -5
     assert call(wsb=need - 1) == -5
 

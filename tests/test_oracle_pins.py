@@ -166,6 +166,60 @@ def test_gradient_matches_torch_autograd_with_detached_teacher():
         np.testing.assert_allclose(g[m], ls[m].grad.numpy(), atol=1e-14)
 
 
+# --------------------------------------------------------- junction backward
+def _torch_junction(h, g):
+    a = torch.linalg.norm(h, dim=1, keepdim=True)
+    b = torch.linalg.norm(g, dim=1, keepdim=True)
+    return torch.cat([h * (b / a), g], dim=1)
+
+
+@pytest.mark.parametrize("stop_grad", [False, True])
+def test_junction_backward_matches_torch_autograd(stop_grad):
+    """Autograd through the junction (norms, rescale, concat, embedding lookup
+    with repeated ids) equals the oracle's chain-rule gradients."""
+    r = rng(17)
+    n, d_in, de, V = 9, 5, 4, 6
+    ids = np.array([0, 3, 3, 1, 0, 3, 5, 2, 3])
+    h = torch.tensor(r.standard_normal((n, d_in)) * 4, requires_grad=True)
+    emb = torch.tensor(r.standard_normal((V, de)) * 0.02, requires_grad=True)
+    dout = r.standard_normal((n, d_in + de))
+    hin = h.detach() if stop_grad else h
+    out = _torch_junction(hin, emb[torch.from_numpy(ids)])
+    (out * torch.from_numpy(dout)).sum().backward()
+    dh, demb = oracle.junction_backward(h.detach().numpy(), ids, emb.detach().numpy(), dout,
+                                        stop_grad=stop_grad)
+    np.testing.assert_allclose(demb, emb.grad.numpy(), atol=1e-12)
+    if stop_grad:
+        assert h.grad is None and np.all(dh == 0)
+    else:
+        np.testing.assert_allclose(dh, h.grad.numpy(), atol=1e-12)
+
+
+def test_junction_backward_block_one_is_scatter_add():
+    """d_in = 0: out = e[x], so demb is the scatter-add of dout by id."""
+    r = rng(18)
+    ids = np.array([2, 2, 0, 4, 2])
+    emb = r.standard_normal((6, 3))
+    dout = r.standard_normal((5, 3))
+    dh, demb = oracle.junction_backward(None, ids, emb, dout)
+    want = np.zeros((6, 3))
+    for t, v in enumerate(ids):
+        want[v] += dout[t]
+    assert dh is None
+    np.testing.assert_array_equal(demb, want)
+
+
+def test_junction_backward_gradient_is_orthogonal_to_h():
+    """The rescaled half keeps its norm fixed at ||g||, so dL/dh has no
+    component along h: h . dL/dh = 0."""
+    r = rng(19)
+    h = r.standard_normal((7, 6))
+    emb = r.standard_normal((3, 2))
+    ids = r.integers(0, 3, 7)
+    dh, _ = oracle.junction_backward(h, ids, emb, r.standard_normal((7, 8)))
+    np.testing.assert_allclose(np.sum(h * dh, axis=1), 0, atol=1e-12)
+
+
 # ------------------------------------------------------------- head backward
 def test_head_backward_matches_torch_autograd_through_the_heads():
     """dL/dh_m and dL/dW^m of the whole forward (heads + loss, teacher detached)

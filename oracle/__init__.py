@@ -27,5 +27,6 @@ factor, a temperature): against the paper itself the oracle is
 """
 from .matryoshka import (  # noqa: F401
     junction, junction_backward, heads, head_backward, logsumexp, softmax, matryoshka_loss, matryoshka_grad,
-    argmax_lowest, accept_prefix, forward_tokens,
+    argmax_lowest, accept_prefix, forward_tokens, nucleus, sample_inverse_cdf,
+    speculative_verify,
 )

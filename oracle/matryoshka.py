@@ -231,6 +231,85 @@ def accept_prefix(draft: np.ndarray, verify: np.ndarray, draft_len: int) -> np.n
     return out
 
 
+def nucleus(l: np.ndarray, temperature: float = 1.0, top_p: float = 1.0) -> np.ndarray:
+    """Sampling distribution of one exit at one position (last axis = vocabulary).
+
+    softmax(l / temperature), restricted to the nucleus and renormalised: the
+    most probable entries whose probabilities reach top_p (the pages report
+    nucleus sampling for speculative decoding without its settings, so both
+    are parameters).  Reading for ties: every entry whose probability equals
+    that of the last entry needed is kept too, so the set does not depend on
+    an ordering of equal values.  top_p >= 1 keeps everything.
+    """
+    p = softmax(_f64(l) / temperature)
+    if top_p >= 1.0:
+        return p
+    flat = p.reshape(-1, p.shape[-1])
+    out = np.empty_like(flat)
+    for i, row in enumerate(flat):
+        srt = np.sort(row)[::-1]
+        k = min(int(np.searchsorted(np.cumsum(srt), top_p)), row.size - 1)
+        keep = np.where(row >= srt[k], row, 0.0)
+        out[i] = keep / keep.sum()
+    return out.reshape(p.shape)
+
+
+def sample_inverse_cdf(w: np.ndarray, u: float) -> int:
+    """The entry v of weights w >= 0 (vocabulary order) where the running sum
+    first exceeds u * sum(w); u in [0, 1).  Entries of weight 0 are never drawn."""
+    w = _f64(w)
+    c = np.cumsum(w)
+    v = int(np.searchsorted(c, u * c[-1], side="right"))
+    nz = np.nonzero(w > 0)[0]
+    return int(min(v, nz[-1]))
+
+
+def speculative_verify(draft_logits: np.ndarray, verify_logits: np.ndarray,
+                       draft_tokens: np.ndarray, u_accept: np.ndarray, u_next: np.ndarray,
+                       draft_len: int, temperature: float = 1.0, top_p: float = 1.0):
+    """Speculative sampling with the draft exit's distribution p and the
+    verifying exit's q at every position (follow-up 4 of the follow-ups page:
+    a drafted token is accepted with probability beta = sum_v min(p_v, q_v),
+    after Leviathan et al.; the paper summary's speculative-decoding paragraph
+    for the nested draft / verifier pair under nucleus sampling).
+
+    Per sequence b, positions i < draft_len hold drafted tokens x_i:
+      beta[b, i] = sum_v min(p_v, q_v)                      (p, q = nucleus(...))
+      x_i is accepted iff u_accept[b, i] * p(x_i) < q(x_i)  (probability min(1, q/p))
+      accepted[b] = number of leading accepted tokens
+      next[b]: after the first rejection at k, a draw from max(0, q_k - p_k)
+               (from q_k if that is all zero); if all are accepted, a draw from
+               q at position draft_len; draws by sample_inverse_cdf(., u_next[b]).
+    draft_logits, verify_logits: [B, P, V] with P >= draft_len + 1.
+    Returns (beta [B, draft_len], accepted [B], next [B]).
+    """
+    dl = _f64(draft_logits)
+    vl = _f64(verify_logits)
+    B = dl.shape[0]
+    beta = np.zeros((B, draft_len))
+    acc = np.zeros(B, dtype=np.int64)
+    nxt = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        p = nucleus(dl[b, :draft_len + 1], temperature, top_p)
+        q = nucleus(vl[b, :draft_len + 1], temperature, top_p)
+        beta[b] = np.minimum(p[:draft_len], q[:draft_len]).sum(axis=1)
+        k = 0
+        while k < draft_len:
+            x = int(draft_tokens[b, k])
+            if u_accept[b, k] * p[k, x] < q[k, x]:
+                k += 1
+            else:
+                break
+        acc[b] = k
+        if k < draft_len:
+            r = np.maximum(q[k] - p[k], 0.0)
+            w = r if r.sum() > 0 else q[k]
+        else:
+            w = q[draft_len]
+        nxt[b] = sample_inverse_cdf(w, float(u_next[b]))
+    return beta, acc, nxt
+
+
 # ---------------------------------------------------------------------------
 # Chunked evaluation on a subset of tokens
 # ---------------------------------------------------------------------------

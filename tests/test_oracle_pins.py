@@ -390,3 +390,76 @@ def test_forward_tokens_chunked_equals_whole():
     r2, g2 = oracle.forward_tokens(s.h, s.w, s.labels, 0.3, 0.25, rows=rows, exits=(0, 2))
     np.testing.assert_allclose(r2["ce"][1], oracle.matryoshka_loss([lg[0][rows], lg[2][rows]],
                                                                    s.labels[rows], 0.3)["ce"][1])
+
+
+# ------------------------------------------------------ sampled verification
+def test_beta_is_one_minus_total_variation():
+    """beta = sum_v min(p_v, q_v) = 1 - TV(p, q) for any two distributions."""
+    r = rng(20)
+    B, V = 5, 50
+    dl = r.standard_normal((B, 2, V)) * 2
+    vl = r.standard_normal((B, 2, V)) * 2
+    beta, _, _ = oracle.speculative_verify(dl, vl, np.zeros((B, 2), int), np.zeros((B, 2)),
+                                           np.zeros(B), 1, temperature=0.8, top_p=0.9)
+    p = oracle.nucleus(dl[:, 0], 0.8, 0.9)
+    q = oracle.nucleus(vl[:, 0], 0.8, 0.9)
+    np.testing.assert_allclose(beta[:, 0], 1.0 - 0.5 * np.abs(p - q).sum(axis=1), atol=1e-12)
+
+
+def test_nucleus_limits():
+    r = rng(21)
+    l = r.standard_normal((4, 30)) * 3
+    np.testing.assert_allclose(oracle.nucleus(l, 1.0, 1.0), scipy.special.softmax(l, axis=1), atol=1e-15)
+    tiny = oracle.nucleus(l, 1.0, 1e-9)
+    np.testing.assert_array_equal(np.argmax(tiny, axis=1), np.argmax(l, axis=1))
+    assert np.all(np.isclose(tiny.max(axis=1), 1.0))
+    # the kept set is a set of top entries reaching the mass, ties at the edge kept
+    lt = np.array([3.0, 1.0, 1.0, 0.0, -1.0])
+    p = scipy.special.softmax(lt)
+    keep = oracle.nucleus(lt, 1.0, p[0] + 1e-9) > 0
+    np.testing.assert_array_equal(keep, [True, True, True, False, False])
+    for tp in (0.3, 0.6, 0.95):
+        n = oracle.nucleus(l, 1.0, tp)
+        full = scipy.special.softmax(l, axis=1)
+        for i in range(4):
+            kept = n[i] > 0
+            assert full[i][kept].sum() >= tp - 1e-12
+            assert full[i][kept].min() >= full[i][~kept].max(initial=0.0)
+
+
+def test_speculative_sampling_emits_the_verifier_distribution():
+    """Integrated over the drafted token (drawn from p) and over both uniforms,
+    the first emitted token is distributed exactly as q: the accept / residual
+    rule of speculative sampling.  Midpoint grids of 200 points per uniform."""
+    r = rng(22)
+    V = 3
+    dl = r.standard_normal((1, 2, V)) * 1.5
+    vl = r.standard_normal((1, 2, V)) * 1.5
+    p = oracle.nucleus(dl[0, 0])
+    q = oracle.nucleus(vl[0, 0])
+    grid = (np.arange(200) + 0.5) / 200
+    dist = np.zeros(V)
+    for x in range(V):
+        for ua in grid:
+            for un in grid:
+                _, acc, nxt = oracle.speculative_verify(dl, vl, np.array([[x, 0]]),
+                                                        np.array([[ua, 0.0]]), np.array([un]), 1)
+                emitted = x if acc[0] == 1 else nxt[0]
+                dist[emitted] += p[x] / len(grid) ** 2
+    np.testing.assert_allclose(dist, q, atol=1e-2)
+
+
+def test_greedy_limit_is_greedy_acceptance():
+    """As the temperature goes to 0 with drafted tokens the draft exit's argmax,
+    acceptance is the greedy prefix match and the next token the verifier's argmax
+    at the first mismatch."""
+    r = rng(23)
+    B, P, V = 20, 7, 40
+    dl = r.standard_normal((B, P, V)) * 2
+    vl = dl + r.standard_normal((B, P, V)) * 0.8
+    dtok = oracle.argmax_lowest(dl)
+    _, acc, nxt = oracle.speculative_verify(dl, vl, dtok, r.random((B, P)), r.random(B), 6,
+                                            temperature=1e-4)
+    vtok = oracle.argmax_lowest(vl)
+    np.testing.assert_array_equal(acc, oracle.accept_prefix(dtok, vtok, 6))
+    np.testing.assert_array_equal(nxt, vtok[np.arange(B), acc])

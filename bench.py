@@ -382,7 +382,35 @@ def bench_verify(nel, torch, synth, dev, args):
     tot, cnt = nel.timing_read("heads_argmax")
     flops = 2.0 * s.n_tokens * s.vocab * (s.widths[0] + s.widths[2])
     k = tot / max(cnt, 1) / 1e3
+    # sampled verification (nucleus 0.9, T = 1): heads with fp32 logits, then
+    # acceptance and the next-token draw from uniforms drawn up front
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    B, P = s.batch, s.seq
+    toks = torch.randint(0, s.vocab, (B, P), generator=g, device=dev, dtype=torch.int32)
+    ua = torch.rand(B, P, generator=g, device=dev)
+    un = torch.rand(B, generator=g, device=dev)
+
+    def sstep():
+        nel.junction(hs[0], ids, emb, out=j)
+        lg, _ = nel.exit_heads_packed(hs, ws, want_logits=True, want_argmax=False, workspace=wsb)
+        nel.speculative_verify(lg[0], lg[1], toks, ua, un, 6, temperature=1.0, top_p=0.9)
+
+    for _ in range(args.warmup):
+        sstep()
+    torch.cuda.synchronize()
+    nel.timing_reset()
+    nel.timing_enable(True)
+    t2 = time.perf_counter()
+    for _ in range(steps):
+        sstep()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    nel.timing_enable(False)
+    stot, _ = nel.timing_read("speculative")
     return {"ms_per_step": (t1 - t0) * 1e3 / steps, "tokens": s.n_tokens,
+            "sampled_ms_per_step": (t3 - t2) * 1e3 / steps,
+            "speculative_kernels_ms": stot / steps,
             "weights": "packed once before timing (static heads in decoding)",
             "heads_argmax_ms": k * 1e3, "heads_argmax_tflops": flops / k / 1e12,
             "heads_argmax_mfma_frac": flops / k / 1e12 / BF16_PEAK_TFLOPS}

@@ -118,6 +118,44 @@ nel_status nel_accept_prefix(int32_t batch, int32_t positions, int32_t draft_len
                              int32_t* accepted, void* stream);
 
 /*
+ * Sampled speculative verification ("Is nesting the cheapest way to build a
+ * model suite?", follow-up 4: a drafted token is accepted with probability
+ * beta = sum_v min(p_v, q_v); "Matryoshka Language Model Suites",
+ * speculative-decoding paragraph: exit 1 drafts, the largest exit verifies,
+ * also under nucleus sampling).  For sequence b and position i of P, p and q
+ * are the draft and verifying exits' distributions: softmax(logits / T)
+ * restricted to the nucleus (the most probable entries whose probability
+ * reaches top_p, entries tied with the last one needed kept too) and
+ * renormalised.  Then
+ *     beta[b, i]    = sum_v min(p_v, q_v)                         (i < draft_len)
+ *     accepted[b]   = number of leading i < draft_len with u_accept[b, i] p(x_i) < q(x_i),
+ *                     x_i = draft_tokens[b, i]
+ *     next_token[b] = after a rejection at k: a draw from max(0, q_k - p_k)
+ *                     (from q_k if that is all zero); otherwise a draw from q
+ *                     at position draft_len.  The draw is the first entry (in
+ *                     vocabulary order) where the running sum of the weights
+ *                     exceeds u_next[b] times their total.
+ *   draft_logits, verify_logits: device fp32 [batch, positions, vocab] (e.g.
+ *       the logits output of nel_exit_heads*), positions >= draft_len + 1
+ *   draft_tokens, u_accept: device [batch, positions] (int32, fp32 in [0, 1))
+ *   u_next: device fp32 [batch] in [0, 1);  beta: NULL or fp32 [batch, draft_len]
+ *   accepted, next_token: device int32 [batch]
+ *   flags: NULL or device flag word: a drafted token outside [0, vocab) sets
+ *       NEL_FLAG_BAD_ID and counts as rejected
+ *   workspace: >= nel_speculative_workspace(batch, draft_len) bytes
+ * Every decision is taken in fp32 from the given logits.  Requires
+ * vocab <= 32768 (NEL_ESHAPE), temperature > 0 and 0 < top_p <= 1 (NEL_EINVAL).
+ */
+nel_status nel_speculative_verify(int32_t batch, int32_t positions, int32_t draft_len,
+                                  int32_t vocab, const float* draft_logits,
+                                  const float* verify_logits, const int32_t* draft_tokens,
+                                  const float* u_accept, const float* u_next, float temperature,
+                                  float top_p, float* beta, int32_t* accepted,
+                                  int32_t* next_token, int32_t* flags, void* workspace,
+                                  size_t ws_bytes, void* stream);
+size_t nel_speculative_workspace(int32_t batch, int32_t draft_len);
+
+/*
  * Matryoshka loss with online distillation and its logit gradients (summary's
  * distillation and limitations paragraphs; follow-up 4's 0.7/0.3 mix;
  * main-visual explainer panel (b): distillation only into smaller exits).
@@ -265,13 +303,14 @@ const char* nel_last_hip_error(void);
  * 0 junction, 1 heads+loss statistics GEMM, 2 loss merge, 3 means,
  * 4 dlogits finalize, 5 heads+argmax GEMM, 6 argmax merge, 7 accept,
  * 8 weight packing, 9 head-backward operand transposes, 10 dH GEMM, 11 dW GEMM,
- * 12 junction backward.
+ * 12 junction backward, 13 sampled speculative verification.
  * Process-global and not thread-safe: for benchmarks only.
  */
 enum { NEL_K_JUNCTION = 0, NEL_K_HEADS_LOSS = 1, NEL_K_MERGE = 2, NEL_K_MEANS = 3,
        NEL_K_FINALIZE = 4, NEL_K_HEADS_ARGMAX = 5, NEL_K_ARGMAX_MERGE = 6,
        NEL_K_ACCEPT = 7, NEL_K_PACK = 8, NEL_K_BWD_PACK = 9, NEL_K_BWD_DH = 10,
-       NEL_K_BWD_DW = 11, NEL_K_JUNCTION_BWD = 12, NEL_K_COUNT = 13 };
+       NEL_K_BWD_DW = 11, NEL_K_JUNCTION_BWD = 12, NEL_K_SPECULATIVE = 13,
+       NEL_K_COUNT = 14 };
 nel_status nel_timing_enable(int32_t on);
 /* Synchronises the device, then returns the summed milliseconds and the
  * number of timed launches of `kernel` since the last reset. */

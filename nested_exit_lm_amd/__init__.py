@@ -14,6 +14,8 @@ call raises.
     matryoshka_loss_packed / exit_heads_packed -> as above, on packed weights
     head_backward(dlogits, h, w)               -> (dL/dh bf16, dL/dW fp32) of one exit head
     junction_backward(h, ids, emb, dout)       -> (dL/dh, dL/demb fp32) of one junction
+    speculative_verify(draft_logits, verify_logits, tokens, u_accept, u_next, draft_len)
+                                               -> (beta, accepted, next_token)
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ __all__ = [
     "workspace_size", "read_flags", "clear_flags", "status_string", "timing_enable",
     "timing_read", "timing_reset", "KERNELS", "OP_LOSS", "OP_HEADS", "FLAG_BAD_ID",
     "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed", "head_backward",
-    "head_backward_workspace_size", "junction_backward",
+    "head_backward_workspace_size", "junction_backward", "speculative_verify",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +39,7 @@ OP_LOSS, OP_HEADS = 0, 1
 FLAG_BAD_ID, FLAG_BAD_LABEL = 1, 2
 MAX_EXITS = 8
 KERNELS = ["junction", "heads_loss", "merge", "means", "finalize", "heads_argmax",
-           "argmax_merge", "accept", "pack", "bwd_pack", "bwd_dh", "bwd_dw", "junction_bwd"]
+           "argmax_merge", "accept", "pack", "bwd_pack", "bwd_dh", "bwd_dw", "junction_bwd", "speculative"]
 
 
 def lib_path() -> str:
@@ -98,6 +100,9 @@ def load():
         "nel_junction_backward": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, c_int, vp, vp,
                                   vp, vp, sz, vp],
         "nel_junction_backward_workspace": [c_i64, c_int],
+        "nel_speculative_verify": [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, ctypes.c_float,
+                                   ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
+        "nel_speculative_workspace": [c_int, c_int],
         "nel_read_device_flags": [vp, vp, vp],
         "nel_clear_device_flags": [vp, vp],
         "nel_status_string": [c_int],
@@ -112,6 +117,7 @@ def load():
     lib.nel_workspace_size.restype = sz
     lib.nel_head_backward_workspace.restype = sz
     lib.nel_junction_backward_workspace.restype = sz
+    lib.nel_speculative_workspace.restype = sz
     lib.nel_status_string.restype = ctypes.c_char_p
     lib.nel_last_hip_error.argtypes = []
     lib.nel_last_hip_error.restype = ctypes.c_char_p
@@ -457,3 +463,41 @@ def junction_backward(h, ids, emb, dout, stop_grad: bool = False, want_dh: bool 
                                      wsb.data_ptr(), wsb.numel(), _stream(device)),
            "nel_junction_backward")
     return dh, demb
+
+
+_SPEC_WS = Workspace()
+
+
+def speculative_verify(draft_logits, verify_logits, draft_tokens, u_accept, u_next,
+                       draft_len: int, temperature: float = 1.0, top_p: float = 1.0,
+                       want_beta: bool = True, flags=None, workspace=None):
+    """Sampled speculative verification from two exits' fp32 logits [B, P, V]
+    (or [B*P, V] with draft_tokens / u_accept [B, P]).  Returns
+    (beta [B, draft_len] | None, accepted [B], next_token [B])."""
+    torch = _torch()
+    device = draft_logits.device
+    B, P = draft_tokens.shape
+    V = draft_logits.shape[-1]
+    for t, name in ((draft_logits, "draft_logits"), (verify_logits, "verify_logits"),
+                    (u_accept, "u_accept"), (u_next, "u_next")):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if draft_tokens.dtype != torch.int32:
+        raise TypeError("draft_tokens must be int32")
+    if draft_logits.numel() != B * P * V or verify_logits.numel() != B * P * V:
+        raise ValueError("logits must hold [B, P, V]")
+    beta = torch.empty(B, max(draft_len, 0), dtype=torch.float32, device=device) if want_beta else None
+    acc = torch.empty(B, dtype=torch.int32, device=device)
+    nxt = torch.empty(B, dtype=torch.int32, device=device)
+    lib = load()
+    need = int(lib.nel_speculative_workspace(B, draft_len))
+    wsb = workspace if workspace is not None else _SPEC_WS.get(need, device)
+    _check(lib.nel_speculative_verify(B, P, draft_len, V, _dev(draft_logits, device, "draft_logits"),
+                                      _dev(verify_logits, device, "verify_logits"),
+                                      _dev(draft_tokens, device, "draft_tokens"),
+                                      _dev(u_accept, device, "u_accept"), _dev(u_next, device, "u_next"),
+                                      float(temperature), float(top_p), _dev(beta, device, "beta"),
+                                      _dev(acc, device, "accepted"), _dev(nxt, device, "next_token"),
+                                      _dev(flags, device, "flags"), wsb.data_ptr(), wsb.numel(),
+                                      _stream(device)), "nel_speculative_verify")
+    return beta, acc, nxt

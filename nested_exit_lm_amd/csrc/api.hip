@@ -330,6 +330,41 @@ nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* 
   return from_hip(timed(NEL_K_PACK, s, [&] { return launch_pack_weights(vocab, d, w, w_packed, s); }));
 }
 
+size_t nel_speculative_workspace(int32_t batch, int32_t draft_len) {
+  if (batch < 0 || draft_len < 0) return 0;
+  return speculative_ws_bytes(batch, draft_len) + 256;
+}
+
+nel_status nel_speculative_verify(int32_t batch, int32_t positions, int32_t draft_len,
+                                  int32_t vocab, const float* draft_logits,
+                                  const float* verify_logits, const int32_t* draft_tokens,
+                                  const float* u_accept, const float* u_next, float temperature,
+                                  float top_p, float* beta, int32_t* accepted,
+                                  int32_t* next_token, int32_t* flags, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  if (batch < 0 || draft_len < 0 || positions < draft_len + 1 || vocab < 1 || vocab > 32768)
+    return NEL_ESHAPE;
+  if (static_cast<int64_t>(batch) * (draft_len + 1) * 2 > INT_MAX) return NEL_ESHAPE;
+  if (!(temperature > 0.f) || !isfinite(temperature) || !(top_p > 0.f && top_p <= 1.f))
+    return NEL_EINVAL;
+  if (batch > 0 && (!draft_logits || !verify_logits || !u_next || !accepted || !next_token ||
+                    (draft_len > 0 && (!draft_tokens || !u_accept))))
+    return NEL_EINVAL;
+  if (misaligned4(draft_logits) || misaligned4(verify_logits) || misaligned4(draft_tokens) ||
+      misaligned4(u_accept) || misaligned4(u_next) || misaligned4(beta) ||
+      misaligned4(accepted) || misaligned4(next_token) || misaligned4(flags) ||
+      misaligned(workspace))
+    return NEL_EALIGN;
+  if (!workspace || ws_bytes < speculative_ws_bytes(batch, draft_len)) return NEL_EWORKSPACE;
+  if (batch == 0) return NEL_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(timed(NEL_K_SPECULATIVE, s, [&] {
+    return launch_speculative_verify(batch, positions, draft_len, vocab, draft_logits,
+                                     verify_logits, draft_tokens, u_accept, u_next, temperature,
+                                     top_p, beta, accepted, next_token, flags, workspace, s);
+  }));
+}
+
 size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t vocab) {
   if (n_tokens < 0 || vocab < 1) return 0;
   return junction_bwd_ws_layout(n_tokens, vocab).total;

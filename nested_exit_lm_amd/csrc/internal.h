@@ -66,6 +66,15 @@ inline HeadsWs heads_ws_layout(int n_exits, int64_t n, int vocab) {
   return L;
 }
 
+// Sampled speculative verification (fp32 logits of the two exits).
+size_t speculative_ws_bytes(int batch, int draft_len);
+hipError_t launch_speculative_verify(int batch, int positions, int draft_len, int vocab,
+                                     const float* draft, const float* verify,
+                                     const int32_t* tokens, const float* u_accept,
+                                     const float* u_next, float temperature, float top_p,
+                                     float* beta, int32_t* accepted, int32_t* next_token,
+                                     int32_t* flags, void* workspace, hipStream_t s);
+
 // Workspace of the junction backward: c_t per token, row-used marks per id.
 struct JunctionBwdWs {
   size_t ct, used, total;

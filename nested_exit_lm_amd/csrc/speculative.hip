@@ -1,0 +1,266 @@
+// Sampled speculative verification from the draft and verifying exits' fp32
+// logits (follow-up 4 on "Is nesting the cheapest way to build a model
+// suite?": a drafted token is accepted with probability
+// beta = sum_v min(p_v, q_v); "Matryoshka Language Model Suites",
+// speculative-decoding paragraph: the nested draft / verifier pair under
+// nucleus sampling).
+//
+// Per position the sampling distribution of an exit is softmax(l / T)
+// restricted to its nucleus (the most probable entries reaching top_p, every
+// entry tied with the last one needed included) and renormalised.  Per
+// sequence: drafted token x_i (i < L) is accepted iff u_i p(x_i) < q(x_i);
+// after the first rejection at k the next token is drawn from max(0, q_k - p_k)
+// (q_k if that is all zero), after L acceptances from q at position L; draws
+// are inverse-CDF in vocabulary order with the caller's uniform.
+//
+// Kernels: (1) per exit and position, the row maximum, the softmax sum and the
+// nucleus threshold, found exactly by a 32-step bisection on order-preserving
+// integer keys of the unnormalised probabilities (every step a fixed-order
+// workgroup reduction in fp64, so every thread takes the same decision);
+// (2) beta per drafted position; (3) per sequence, the acceptance chain and
+// the draw, whose running sums are fp64.  Probabilities themselves are fp32.
+// A row lives in registers (V <= 256 x kPer).
+#include "common.h"
+#include "internal.h"
+
+namespace nel {
+
+namespace {
+
+constexpr int kPer = 128;   // row entries per thread: V <= 32768
+
+// float -> uint32 with the same order (no NaNs)
+__device__ __forceinline__ uint32_t fkey(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Unnormalised probability exp(l / T - max) of a raw logit.  Multiply and
+// subtract are kept separate (no contraction) so that every kernel derives
+// bit-identical values, and with them identical nucleus membership.
+__device__ __forceinline__ float scaled(float l, float inv_t) { return __fmul_rn(l, inv_t); }
+__device__ __forceinline__ float unnorm(float l, float inv_t, float mx) {
+  return fexp(__fsub_rn(scaled(l, inv_t), mx));
+}
+
+// Sum over the 256-thread workgroup in a fixed order; every thread gets it.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Row statistics of one (exit, position): stats = {max of l/T, nucleus sum
+// sum_{kept} exp(l/T - max), threshold key (bits), unused}.
+// Thread t holds entries t + 256 j.
+__global__ __launch_bounds__(256) void nucleus_stats_kernel(
+    const float* __restrict__ draft, const float* __restrict__ verify, int positions, int rows_per_seq,
+    int vocab, float inv_t, float top_p, float4* __restrict__ stats) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int nrows = gridDim.x / 2;
+  const int exit = blockIdx.x / nrows, r = blockIdx.x % nrows;   // r = b * rows_per_seq + i
+  const int b = r / rows_per_seq, i = r % rows_per_seq;
+  const float* row = (exit == 0 ? draft : verify) + (static_cast<int64_t>(b) * positions + i) * vocab;
+  float x[kPer];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int v = tid + 256 * j;
+    x[j] = v < vocab ? row[v] : -INFINITY;
+    if (v < vocab) mx = fmaxf(mx, scaled(x[j], inv_t));
+  }
+  mx = block_max(mx, red);
+  // From here the row is held as order keys of the unnormalised probabilities
+  // (all >= 0, so the value is the key's low 31 bits).
+  uint32_t key[kPer];
+  float s = 0.f;   // this thread's share of the softmax sum
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int v = tid + 256 * j;
+    const float e = v < vocab ? unnorm(x[j], inv_t, mx) : 0.f;   // the unnormalised probability
+    key[j] = fkey(e);
+    s += e;
+  }
+  auto val = [](uint32_t k) { return __uint_as_float(k & 0x7fffffffu); };
+  // largest key K with mass(key >= K) >= top_p.  Each thread's 128 terms are
+  // summed in fp32, the workgroup's 256 partial sums in fp64.
+  __shared__ double red64[4];
+  const double s64 = block_sum_f64(s, red64);
+  uint32_t K = 0;
+  if (top_p < 1.f) {
+    const double need = static_cast<double>(top_p) * s64;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = K | (1u << bit);
+      float m = 0.f;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) m += key[j] >= cand ? val(key[j]) : 0.f;
+      if (block_sum_f64(m, red64) >= need) K = cand;
+    }
+  }
+  float snp = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) snp += key[j] >= K ? val(key[j]) : 0.f;
+  const float sn = static_cast<float>(block_sum_f64(snp, red64));
+  if (tid == 0) stats[blockIdx.x] = make_float4(mx, sn, __uint_as_float(K), static_cast<float>(s64));
+}
+
+// Nucleus probability of entry value l (raw logit) under row stats st.
+__device__ __forceinline__ float nprob(float l, float inv_t, float4 st) {
+  const float e = unnorm(l, inv_t, st.x);
+  return fkey(e) >= __float_as_uint(st.z) ? e / st.y : 0.f;
+}
+
+__global__ __launch_bounds__(256) void beta_kernel(const float* __restrict__ draft,
+                                                   const float* __restrict__ verify, int positions,
+                                                   int rows_per_seq, int draft_len, int vocab,
+                                                   float inv_t, const float4* __restrict__ stats,
+                                                   float* __restrict__ beta) {
+  __shared__ float red[4];
+  const int b = blockIdx.x / draft_len, i = blockIdx.x % draft_len;
+  const int nrows = gridDim.x / draft_len * rows_per_seq;
+  const int r = b * rows_per_seq + i;
+  const float4 sp = stats[r], sq = stats[nrows + r];
+  const int64_t off = (static_cast<int64_t>(b) * positions + i) * vocab;
+  float acc = 0.f;
+  for (int v = threadIdx.x; v < vocab; v += 256)
+    acc += fminf(nprob(draft[off + v], inv_t, sp), nprob(verify[off + v], inv_t, sq));
+  acc = block_sum(acc, red);
+  if (threadIdx.x == 0) beta[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void accept_draw_kernel(
+    const float* __restrict__ draft, const float* __restrict__ verify, int positions,
+    int rows_per_seq, int draft_len, int vocab, float inv_t, const float4* __restrict__ stats,
+    const int32_t* __restrict__ tokens, const float* __restrict__ u_accept,
+    const float* __restrict__ u_next, int32_t* __restrict__ accepted,
+    int32_t* __restrict__ next_token, int32_t* __restrict__ flags) {
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int nrows = gridDim.x * rows_per_seq;
+  // acceptance chain (every thread computes it identically)
+  int k = 0;
+  bool bad = false;
+  for (; k < draft_len; ++k) {
+    const int64_t pos = static_cast<int64_t>(b) * positions + k;
+    const int x = tokens[pos];
+    if (x < 0 || x >= vocab) {
+      bad = true;
+      break;
+    }
+    const int r = b * rows_per_seq + k;
+    const float p = nprob(draft[pos * vocab + x], inv_t, stats[r]);
+    const float q = nprob(verify[pos * vocab + x], inv_t, stats[nrows + r]);
+    if (!(u_accept[pos] * p < q)) break;
+  }
+  if (bad && tid == 0 && flags) atomicOr(flags, 1 /*NEL_FLAG_BAD_ID*/);
+  // the distribution of the next token: residual at k, or q at position L
+  const int r = b * rows_per_seq + k;
+  const float4 sp = stats[r], sq = stats[nrows + r];
+  const int64_t off = (static_cast<int64_t>(b) * positions + k) * vocab;
+  const bool residual = k < draft_len;
+  // this thread's contiguous chunk of the vocabulary
+  const int per = (vocab + 255) / 256;
+  const int v0 = tid * per, v1 = min(v0 + per, vocab);
+  auto weight = [&](int v, bool res) {
+    const float q = nprob(verify[off + v], inv_t, sq);
+    return res ? fmaxf(q - nprob(draft[off + v], inv_t, sp), 0.f) : q;
+  };
+  // running sums of the draw in fp64: chunk sums, their exclusive prefix in
+  // thread order, then the crossing inside the one chunk that holds it
+  __shared__ double red64[4];
+  __shared__ double excl[256];
+  __shared__ double seq_total;
+  __shared__ int firstpick, lastpos;
+  double part = 0.0;
+  for (int v = v0; v < v1; ++v) part += weight(v, residual);
+  bool res = residual;
+  if (residual && !(block_sum_f64(part, red64) > 0.0)) {   // q == p on the nucleus: draw from q
+    res = false;
+    part = 0.0;
+    for (int v = v0; v < v1; ++v) part += weight(v, false);
+  }
+  __syncthreads();
+  excl[tid] = part;
+  if (tid == 0) {
+    firstpick = 0x7fffffff;
+    lastpos = -1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double run = 0.0;
+    for (int t = 0; t < 256; ++t) {
+      const double c = excl[t];
+      excl[t] = run;
+      run += c;
+    }
+    seq_total = run;
+  }
+  __syncthreads();
+  const double target = static_cast<double>(u_next[b]) * seq_total;
+  // the last entry of positive weight is the fallback when rounding leaves
+  // the target uncrossed
+  double run = excl[tid];
+  int pick = -1, last_pos = -1;
+  for (int v = v0; v < v1; ++v) {
+    const float w = weight(v, res);
+    if (w > 0.f) last_pos = v;
+    if (pick < 0 && w > 0.f && run + w > target) pick = v;
+    run += w;
+  }
+  if (pick >= 0) atomicMin(&firstpick, pick);
+  if (last_pos >= 0) atomicMax(&lastpos, last_pos);
+  __syncthreads();
+  if (tid == 0) {
+    accepted[b] = k;
+    next_token[b] = firstpick != 0x7fffffff ? firstpick : lastpos;
+  }
+}
+
+}  // namespace
+
+size_t speculative_ws_bytes(int batch, int draft_len) {
+  return sizeof(float4) * 2 * static_cast<size_t>(batch) * (draft_len + 1);
+}
+
+hipError_t launch_speculative_verify(int batch, int positions, int draft_len, int vocab,
+                                     const float* draft, const float* verify,
+                                     const int32_t* tokens, const float* u_accept,
+                                     const float* u_next, float temperature, float top_p,
+                                     float* beta, int32_t* accepted, int32_t* next_token,
+                                     int32_t* flags, void* workspace, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  const int rows_per_seq = draft_len + 1;
+  const float inv_t = 1.f / temperature;
+  float4* stats = static_cast<float4*>(workspace);
+  hipLaunchKernelGGL(nucleus_stats_kernel, dim3(2 * batch * rows_per_seq), dim3(256), 0, s, draft,
+                     verify, positions, rows_per_seq, vocab, inv_t, top_p, stats);
+  if (beta && draft_len > 0)
+    hipLaunchKernelGGL(beta_kernel, dim3(batch * draft_len), dim3(256), 0, s, draft, verify,
+                       positions, rows_per_seq, draft_len, vocab, inv_t, stats, beta);
+  hipLaunchKernelGGL(accept_draw_kernel, dim3(batch), dim3(256), 0, s, draft, verify, positions,
+                     rows_per_seq, draft_len, vocab, inv_t, stats, tokens, u_accept, u_next,
+                     accepted, next_token, flags);
+  return hipGetLastError();
+}
+
+}  // namespace nel

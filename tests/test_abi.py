@@ -20,7 +20,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = nel.load()
     syms = declared_symbols()
-    assert len(syms) == 19
+    assert len(syms) == 21
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -185,6 +185,28 @@ def test_junction_backward_host_validation():
     assert call(demb=MIS) == -4
     assert call(ws=None) == -5
     assert call(wsb=need - 1) == -5
+
+
+def test_speculative_host_validation():
+    lib = nel.load()
+    need = int(lib.nel_speculative_workspace(4, 6))
+    assert need >= 16 * 2 * 4 * 7
+
+    def call(B=4, P=7, L=6, V=100, T=1.0, tp=0.9, dl=FAKE, vl=FAKE, tok=FAKE, ua=FAKE, un=FAKE,
+             acc=FAKE, nxt=FAKE, ws=FAKE, wsb=need):
+        return lib.nel_speculative_verify(B, P, L, V, dl, vl, tok, ua, un, T, tp, None, acc, nxt,
+                                          None, ws, wsb, None)
+
+    assert call(P=6) == -2                  # needs draft_len + 1 positions
+    assert call(V=40000) == -2
+    assert call(T=0.0) == -1
+    assert call(T=float("nan")) == -1
+    assert call(tp=0.0) == -1
+    assert call(tp=1.5) == -1
+    assert call(dl=None) == -1
+    assert call(tok=MIS4) == -4
+    assert call(wsb=need // 2) == -5
+    assert call(B=0, dl=None, vl=None, tok=None, ua=None, un=None, acc=None, nxt=None) == 0
 
 
 def test_one_hip_runtime_after_load():

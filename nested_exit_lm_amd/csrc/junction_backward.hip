@@ -81,10 +81,33 @@ __global__ __launch_bounds__(256) void junction_bwd_token(
 // One 256-thread workgroup per embedding row v.  Each scan step reads 1024
 // ids (4 per thread), lists the matching tokens in token order in LDS, and
 // adds their delta_g rows into per-thread fp32 column accumulators; columns
-// go in slabs of 256 x kCols.
+// go in slabs of 256 x kCols.  VEC (rows in whole 16-byte chunks): thread t
+// owns columns kCols t .. kCols t + 7 of the slab and reads them as 16-byte
+// chunks; otherwise it owns columns t + 256 j with element reads.  Eight
+// tokens' rows are requested before any is added, in token order.
 constexpr int kCols = 8;
 
 template <typename T>
+__device__ __forceinline__ void load_cols(const T* p, float (&x)[kCols]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 r = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(r[j] << 16);
+      x[2 * j + 1] = __uint_as_float(r[j] & 0xffff0000u);
+    }
+  } else {
+    const u32x4 r0 = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 r1 = *reinterpret_cast<const u32x4*>(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = __uint_as_float(r0[j]);
+      x[4 + j] = __uint_as_float(r1[j]);
+    }
+  }
+}
+
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void junction_bwd_emb(
     int64_t n, int d_in, int d_out, int vocab, const int32_t* __restrict__ ids,
     const T* __restrict__ emb, const T* __restrict__ dout, const float* __restrict__ ct,
@@ -145,23 +168,29 @@ __global__ __launch_bounds__(256) void junction_bwd_emb(
       for (int i = 0; i < 4; ++i)
         if (m[i]) list[before++] = static_cast<int32_t>(base + 4 * tid + i - base);
       __syncthreads();
-      // 8 tokens' rows are requested together, then added in token order
+      // 8 tokens' rows are requested together (beyond the list: the last
+      // listed token, not added), then added in token order
       for (int k0 = 0; k0 < total; k0 += 8) {
         float x[8][kCols], cx[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const bool ok = k0 + u < total;
-          const int64_t t = base + (ok ? list[k0 + u] : list[k0]);
+          const int64_t t = base + list[min(k0 + u, total - 1)];
           const T* drow = dout + t * d_out + d_in;   // delta_g
+          if constexpr (VEC) {
+            const int cb = c0 + tid * kCols;
+            if (cb < de) load_cols(drow + cb, x[u]);
+          } else {
 #pragma unroll
-          for (int j = 0; j < kCols; ++j) {
-            const int c = c0 + tid + 256 * j;
-            x[u][j] = (ok && c < de) ? ld(drow, c) : 0.f;
+            for (int j = 0; j < kCols; ++j) {
+              const int c = c0 + tid + 256 * j;
+              x[u][j] = c < de ? ld(drow, c) : 0.f;
+            }
           }
-          cx[u] = ok ? ct[t] : 0.f;
+          cx[u] = ct[t];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
+          if (k0 + u >= total) break;
 #pragma unroll
           for (int j = 0; j < kCols; ++j) acc[j] += x[u][j];
           csum += cx[u];
@@ -170,7 +199,7 @@ __global__ __launch_bounds__(256) void junction_bwd_emb(
     }
 #pragma unroll
     for (int j = 0; j < kCols; ++j) {
-      const int c = c0 + tid + 256 * j;
+      const int c = VEC ? c0 + tid * kCols + j : c0 + tid + 256 * j;
       if (c < de) orow[c] = acc[j] + csum * ld(erow, c) * ginv;
     }
   }
@@ -208,10 +237,20 @@ hipError_t launch_junction_backward(int64_t n, int d_in, int d_out, int vocab, c
                        static_cast<const T*>(emb), static_cast<const T*>(dout), stop_grad,
                        static_cast<T*>(dh), ct, used, flags);
   }
-  if (demb)
-    hipLaunchKernelGGL((junction_bwd_emb<T>), dim3(static_cast<unsigned>(vocab)), dim3(256), 0, s,
-                       n, d_in, d_out, vocab, ids, static_cast<const T*>(emb),
-                       static_cast<const T*>(dout), ct, used, demb);
+  if (demb) {
+    // 16-byte chunks of delta_g: the buffer, every row start (t d_out + d_in) and the width aligned
+    constexpr int C = Elem<T>::kChunk;
+    const int de = d_out - d_in;
+    if (d_out % C == 0 && d_in % C == 0 && de % kCols == 0 &&
+        reinterpret_cast<uintptr_t>(dout) % 16 == 0)
+      hipLaunchKernelGGL((junction_bwd_emb<T, true>), dim3(static_cast<unsigned>(vocab)), dim3(256),
+                         0, s, n, d_in, d_out, vocab, ids, static_cast<const T*>(emb),
+                         static_cast<const T*>(dout), ct, used, demb);
+    else
+      hipLaunchKernelGGL((junction_bwd_emb<T, false>), dim3(static_cast<unsigned>(vocab)),
+                         dim3(256), 0, s, n, d_in, d_out, vocab, ids, static_cast<const T*>(emb),
+                         static_cast<const T*>(dout), ct, used, demb);
+  }
   return hipGetLastError();
 }
 

@@ -245,17 +245,23 @@ nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens
  *   ids:   [n_tokens] int32;  emb: [vocab, d_out - d_in] dt;  dout: [n_tokens, d_out] dt
  *   dh:    NULL or [n_tokens, d_in] dt (must be NULL when d_in == 0)
  *   demb:  NULL or fp32 [vocab, d_out - d_in], every row written (0 for ids
- *          no token uses); each row is summed in token order (deterministic)
+ *          no token uses).  Each row's tokens are taken in token order, in
+ *          consecutive groups of 64 summed in order, and the group sums are
+ *          added in order: reruns are bit-identical
  *   flags: device flag word or NULL; a bad id sets NEL_FLAG_BAD_ID, NaNs its dh
  *          row and contributes nothing to demb
- *   workspace: >= nel_junction_backward_workspace(n_tokens, vocab) bytes
+ *   workspace: >= nel_junction_backward_workspace(n_tokens, d_in, d_out, vocab)
+ *          bytes (grows with n_tokens * vocab / 256 and with the embedding width)
+ * n_tokens above 2^30 is NEL_ESHAPE.
  */
 nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_out,
                                  int32_t vocab, const void* h, const int32_t* ids,
                                  const void* emb, const void* dout, int32_t stop_grad, void* dh,
                                  float* demb, int32_t* flags, void* workspace, size_t ws_bytes,
                                  void* stream);
-size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t vocab);
+/* Bytes of workspace nel_junction_backward needs (0 on bad arguments). */
+size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t d_in, int32_t d_out,
+                                       int32_t vocab);
 
 /*
  * Backward of one exit head (the step after the loss: l = h W^T with W the

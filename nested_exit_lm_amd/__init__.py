@@ -99,7 +99,7 @@ def load():
         "nel_head_backward_workspace": [c_i64, c_int, c_int],
         "nel_junction_backward": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, c_int, vp, vp,
                                   vp, vp, sz, vp],
-        "nel_junction_backward_workspace": [c_i64, c_int],
+        "nel_junction_backward_workspace": [c_i64, c_int, c_int, c_int],
         "nel_speculative_verify": [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, ctypes.c_float,
                                    ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
         "nel_speculative_workspace": [c_int, c_int],
@@ -453,7 +453,7 @@ def junction_backward(h, ids, emb, dout, stop_grad: bool = False, want_dh: bool 
     if not want_demb:
         demb = None
     lib = load()
-    need = int(lib.nel_junction_backward_workspace(n, emb.shape[0]))
+    need = int(lib.nel_junction_backward_workspace(n, d_in, d_in + de, emb.shape[0]))
     wsb = workspace if workspace is not None else _JBWD_WS.get(need, device)
     _check(lib.nel_junction_backward(_dt(emb), n, d_in, d_in + de, emb.shape[0],
                                      _dev(h, device, "h"), _dev(ids, device, "ids"),

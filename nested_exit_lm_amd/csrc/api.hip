@@ -365,9 +365,11 @@ nel_status nel_speculative_verify(int32_t batch, int32_t positions, int32_t draf
   }));
 }
 
-size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t vocab) {
-  if (n_tokens < 0 || vocab < 1) return 0;
-  return junction_bwd_ws_layout(n_tokens, vocab).total;
+size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t d_in, int32_t d_out,
+                                       int32_t vocab) {
+  if (n_tokens < 0 || n_tokens > kJunctionBwdMaxTokens || d_in < 0 || d_out <= d_in || vocab < 1)
+    return 0;
+  return junction_bwd_ws_layout(n_tokens, d_in, d_out, vocab).total;
 }
 
 nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_out,
@@ -377,7 +379,7 @@ nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, i
                                  void* stream) {
   if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
   if (n_tokens < 0 || d_in < 0 || d_out <= d_in || vocab < 1) return NEL_ESHAPE;
-  if (n_tokens > (int64_t{1} << 40)) return NEL_ESHAPE;
+  if (n_tokens > kJunctionBwdMaxTokens) return NEL_ESHAPE;
   if (!dh && !demb) return NEL_EINVAL;
   if (d_in == 0 && dh) return NEL_EINVAL;   // block 1 has no h to differentiate
   if (n_tokens > 0 && (!ids || !emb || !dout || (d_in > 0 && !h))) return NEL_EINVAL;
@@ -385,18 +387,15 @@ nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, i
   if (misaligned(h) || misaligned4(ids) || misaligned(emb) || misaligned(dout) ||
       misaligned(dh) || misaligned(demb) || misaligned4(flags) || misaligned(workspace))
     return NEL_EALIGN;
-  const JunctionBwdWs L = junction_bwd_ws_layout(n_tokens, vocab);
+  const JunctionBwdWs L = junction_bwd_ws_layout(n_tokens, d_in, d_out, vocab);
   if (!workspace || ws_bytes < L.total) return NEL_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  float* ct = reinterpret_cast<float*>(ws + L.ct);
-  int32_t* used = reinterpret_cast<int32_t*>(ws + L.used);
   return from_hip(timed(NEL_K_JUNCTION_BWD, s, [&] {
     return dt == NEL_BF16
                ? launch_junction_backward<bf16_t>(n_tokens, d_in, d_out, vocab, h, ids, emb, dout,
-                                                  stop_grad != 0, dh, demb, ct, used, flags, s)
+                                                  stop_grad != 0, dh, demb, workspace, flags, s)
                : launch_junction_backward<float>(n_tokens, d_in, d_out, vocab, h, ids, emb, dout,
-                                                 stop_grad != 0, dh, demb, ct, used, flags, s);
+                                                 stop_grad != 0, dh, demb, workspace, flags, s);
   }));
 }
 

@@ -75,16 +75,22 @@ hipError_t launch_speculative_verify(int batch, int positions, int draft_len, in
                                      float* beta, int32_t* accepted, int32_t* next_token,
                                      int32_t* flags, void* workspace, hipStream_t s);
 
-// Workspace of the junction backward: c_t per token, row-used marks per id.
+// Workspace of the junction backward (byte offsets): c_t, rank in block and
+// the id-sorted token list per token; per-block counts per id; per id: count,
+// list start, first partial slot; the totals of segments and partial slots;
+// per-workgroup totals of the id scan; per segment {id, list begin, list end,
+// partial slot}; the partial slot -> id table; partial sums.
 struct JunctionBwdWs {
-  size_t ct, used, total;
+  size_t ct, rank, list, hist, cnt, rowoff, poff, counts, wgtot, seginfo, prow, pcs, partial, total;
 };
-JunctionBwdWs junction_bwd_ws_layout(int64_t n, int vocab);
+JunctionBwdWs junction_bwd_ws_layout(int64_t n, int d_in, int d_out, int vocab);
+// Token indices, list offsets and segment numbers are int32.
+constexpr int64_t kJunctionBwdMaxTokens = int64_t{1} << 30;
 template <typename T>
 hipError_t launch_junction_backward(int64_t n, int d_in, int d_out, int vocab, const void* h,
                                     const int32_t* ids, const void* emb, const void* dout,
-                                    int stop_grad, void* dh, float* demb, float* ct,
-                                    int32_t* used, int32_t* flags, hipStream_t s);
+                                    int stop_grad, void* dh, float* demb, void* workspace,
+                                    int32_t* flags, hipStream_t s);
 
 // Workspace of the head backward (byte offsets): W^T and h^T in the tiled
 // layout, G^T row-major; K of the token dimension padded to n_pad.

@@ -167,8 +167,10 @@ def test_head_backward_host_validation():
 
 def test_junction_backward_host_validation():
     lib = nel.load()
-    need = int(lib.nel_junction_backward_workspace(10, 50))
+    need = int(lib.nel_junction_backward_workspace(10, 8, 16, 50))
     assert need > 0
+    assert lib.nel_junction_backward_workspace(10, 8, 8, 50) == 0
+    assert lib.nel_junction_backward_workspace((1 << 30) + 1, 8, 16, 50) == 0
 
     def call(dt=1, n=10, d_in=8, d_out=16, V=50, h=FAKE, ids=FAKE, emb=FAKE, dout=FAKE, sg=0,
              dh=FAKE, demb=FAKE, ws=FAKE, wsb=need):
@@ -178,6 +180,7 @@ def test_junction_backward_host_validation():
     assert call(dt=4) == -3
     assert call(d_out=8) == -2
     assert call(V=0) == -2
+    assert call(n=(1 << 30) + 1) == -2
     assert call(dh=None, demb=None) == -1
     assert call(d_in=0, h=None) == -1          # block 1 has no dh
     assert call(h=None) == -1

@@ -26,7 +26,7 @@ factor, a temperature): against the paper itself the oracle is
 "parity unpinned"; it is pinned to the reading stated in each docstring.
 """
 from .matryoshka import (  # noqa: F401
-    junction, junction_backward, heads, head_backward, logsumexp, softmax, matryoshka_loss, matryoshka_grad,
+    junction, junction_backward, JUNCTION_RESCALE, JUNCTION_NO_RESCALE, JUNCTION_ZERO_FILL, heads, head_backward, logsumexp, softmax, matryoshka_loss, matryoshka_grad,
     argmax_lowest, accept_prefix, forward_tokens, nucleus, sample_inverse_cdf,
     speculative_verify,
 )

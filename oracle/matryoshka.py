@@ -20,7 +20,14 @@ def _f64(x) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Junction
 # ---------------------------------------------------------------------------
-def junction(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray) -> np.ndarray:
+# Junction modes: the method's junction and the two ablations the paper
+# summary and the key-visual explainer report at 200M scale (dropping the
+# norm match; filling the new channels with zeros).
+JUNCTION_RESCALE, JUNCTION_NO_RESCALE, JUNCTION_ZERO_FILL = 0, 1, 2
+
+
+def junction(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray,
+             mode: int = JUNCTION_RESCALE) -> np.ndarray:
     """Parameter-free junction between block m and block m+1.
 
     "Matryoshka Language Model Suites", junction paragraph, and the key-visual
@@ -35,26 +42,33 @@ def junction(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray) -> np.nd
     fills the first D_m channels and the embedding the last
     D_{m+1} - D_m; if either norm is zero the rescaled half is zero.
 
+    Ablation modes (same passages, the 200M ablation sentences):
+      JUNCTION_NO_RESCALE: out = [h, g]   (the norm match dropped)
+      JUNCTION_ZERO_FILL:  out = [h b / a, 0]   (the new channels are zeros;
+        reading: the rescale target stays the fresh embedding's norm b, since
+        rescaling to the norm of the zeros would erase h altogether)
+
     h:   [N, D_in] (None or D_in == 0 for block 1); ids: [N] in [0, V);
     emb: [V, D_out - D_in].  Returns float64 [N, D_out].
     """
     g = _f64(emb)[np.asarray(ids, dtype=np.int64)]
+    fill = np.zeros_like(g) if mode == JUNCTION_ZERO_FILL else g
     if h is None or np.asarray(h).shape[1] == 0:
-        return g
+        return fill
     hf = _f64(h)
+    if mode == JUNCTION_NO_RESCALE:
+        return np.concatenate([hf, g], axis=1)
     a = np.sqrt(np.sum(hf * hf, axis=1))
     b = np.sqrt(np.sum(g * g, axis=1))
     scale = np.zeros_like(a)
     ok = (a > 0) & (b > 0)
     scale[ok] = b[ok] / a[ok]
-    return np.concatenate([hf * scale[:, None], g], axis=1)
+    return np.concatenate([hf * scale[:, None], fill], axis=1)
 
 
-# ---------------------------------------------------------------------------
-# Heads
-# ---------------------------------------------------------------------------
 def junction_backward(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray,
-                      dout: np.ndarray, stop_grad: bool = False):
+                      dout: np.ndarray, stop_grad: bool = False,
+                      mode: int = JUNCTION_RESCALE):
     """Gradients of `junction` by the chain rule, given dL/dout.
 
     Forward per token: g = e[x], a = ||h||, b = ||g||, out = [h b / a, g]
@@ -62,20 +76,25 @@ def junction_backward(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray,
     With dout = [du, dg] split at d_in:
         dL/dh   = (b / a) (du - h (h . du) / a^2)
         dL/dg   = dg + ((h . du) / a) g / b      (d||g||/dg = g / ||g||)
-    and dL/de[v] sums dL/dg over the tokens with id v.  stop_grad (arm (B) of
-    follow-up 2 on the follow-ups page: every block learns only from its own
-    exit) treats h as a constant: dL/dh = 0, dL/dg unchanged.
-    Returns (dh or None when h is None, demb [V, d_out - d_in]).
+    and dL/de[v] sums dL/dg over the tokens with id v.  The ablation modes
+    drop terms: JUNCTION_NO_RESCALE has dL/dh = du and dL/dg = dg;
+    JUNCTION_ZERO_FILL has no dg term (the zeros do not depend on e).
+    stop_grad (arm (B) of follow-up 2 on the follow-ups page: every block
+    learns only from its own exit) treats h as a constant: dL/dh = 0, dL/dg
+    unchanged.  Returns (dh or None when h is None, demb [V, d_out - d_in]).
     """
     g = _f64(emb)[ids]
     dout = _f64(dout)
     d_in = 0 if h is None else h.shape[1]
     du, dg = dout[:, :d_in], dout[:, d_in:]
     demb = np.zeros_like(_f64(emb))
-    np.add.at(demb, ids, dg)
+    if mode != JUNCTION_ZERO_FILL:
+        np.add.at(demb, ids, dg)
     if h is None:
         return None, demb
     h = _f64(h)
+    if mode == JUNCTION_NO_RESCALE:
+        return (np.zeros_like(h) if stop_grad else du.copy()), demb
     a = np.linalg.norm(h, axis=1)
     b = np.linalg.norm(g, axis=1)
     live = (a > 0) & (b > 0)
@@ -90,6 +109,9 @@ def junction_backward(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray,
     return dh, demb
 
 
+# ---------------------------------------------------------------------------
+# Heads
+# ---------------------------------------------------------------------------
 def heads(hs: Sequence[np.ndarray], ws: Sequence[np.ndarray]) -> List[np.ndarray]:
     """Per-exit linear LM heads: l_m = h_m W^m^T.
 

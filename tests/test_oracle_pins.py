@@ -195,6 +195,60 @@ def test_junction_backward_matches_torch_autograd(stop_grad):
         np.testing.assert_allclose(dh, h.grad.numpy(), atol=1e-12)
 
 
+def _torch_junction_mode(h, g, mode):
+    """The three junction modes written directly in torch."""
+    if mode == oracle.JUNCTION_NO_RESCALE:
+        return torch.cat([h, g], dim=1)
+    a = torch.linalg.norm(h, dim=1, keepdim=True)
+    b = torch.linalg.norm(g, dim=1, keepdim=True)
+    tail = torch.zeros_like(g) if mode == oracle.JUNCTION_ZERO_FILL else g
+    return torch.cat([h * (b / a), tail], dim=1)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("stop_grad", [False, True])
+def test_junction_mode_backward_matches_torch_autograd(mode, stop_grad):
+    """The ablation modes: autograd through the torch forward of each mode."""
+    r = rng(24)
+    n, d_in, de, V = 8, 5, 3, 4
+    ids = np.array([0, 2, 2, 1, 0, 2, 3, 2])
+    h = torch.tensor(r.standard_normal((n, d_in)) * 4, requires_grad=True)
+    emb = torch.tensor(r.standard_normal((V, de)) * 0.02, requires_grad=True)
+    dout = r.standard_normal((n, d_in + de))
+    hin = h.detach() if stop_grad else h
+    out = _torch_junction_mode(hin, emb[torch.from_numpy(ids)], mode)
+    (out * torch.from_numpy(dout)).sum().backward()
+    dh, demb = oracle.junction_backward(h.detach().numpy(), ids, emb.detach().numpy(), dout,
+                                        stop_grad=stop_grad, mode=mode)
+    np.testing.assert_allclose(demb, emb.grad.numpy(), atol=1e-12)
+    if stop_grad:
+        assert np.all(dh == 0)
+    else:
+        np.testing.assert_allclose(dh, h.grad.numpy(), atol=1e-12)
+
+
+def test_junction_modes_forward():
+    """No rescale is a plain concatenation (torch.cat of h and the embedding
+    lookup); zero fill keeps the rescaled half (norm = ||e[x]||) and zeros the
+    rest; at block 1 they are the lookup and all zeros."""
+    r = rng(25)
+    n, d_in, de, V = 6, 4, 3, 5
+    h = r.standard_normal((n, d_in)) * 4
+    emb = r.standard_normal((V, de)) * 0.02
+    ids = r.integers(0, V, n)
+    g = torch.nn.functional.embedding(torch.from_numpy(ids), torch.from_numpy(emb)).numpy()
+    np.testing.assert_array_equal(oracle.junction(h, ids, emb, oracle.JUNCTION_NO_RESCALE),
+                                  torch.cat([torch.from_numpy(h), torch.from_numpy(g)], 1).numpy())
+    z = oracle.junction(h, ids, emb, oracle.JUNCTION_ZERO_FILL)
+    assert np.all(z[:, d_in:] == 0)
+    np.testing.assert_allclose(np.linalg.norm(z[:, :d_in], axis=1), np.linalg.norm(g, axis=1),
+                               rtol=1e-14)
+    cos = np.sum(z[:, :d_in] * h, 1) / np.linalg.norm(z[:, :d_in], axis=1) / np.linalg.norm(h, axis=1)
+    np.testing.assert_allclose(cos, 1.0, rtol=1e-14)
+    np.testing.assert_array_equal(oracle.junction(None, ids, emb, oracle.JUNCTION_NO_RESCALE), g)
+    assert np.all(oracle.junction(None, ids, emb, oracle.JUNCTION_ZERO_FILL) == 0)
+
+
 def test_junction_backward_block_one_is_scatter_add():
     """d_in = 0: out = e[x], so demb is the scatter-add of dout by id."""
     r = rng(18)

@@ -66,6 +66,16 @@ enum { NEL_OP_LOSS = 0, NEL_OP_HEADS = 1 };
 
 enum { NEL_MAX_EXITS = 8 };
 
+/* Junction modes: the method's junction and the two ablations of the paper
+ * summary's junction paragraph and the key-visual explainer (200M scale):
+ * dropping the norm match, and filling the new channels with zeros. */
+typedef enum {
+  NEL_JUNCTION_RESCALE = 0,     /* out = [h ||g|| / ||h||, g]  (the method) */
+  NEL_JUNCTION_NO_RESCALE = 1,  /* out = [h, g] */
+  NEL_JUNCTION_ZERO_FILL = 2    /* out = [h ||g|| / ||h||, 0]: the target norm is
+                                   still the fresh embedding's */
+} nel_junction_mode;
+
 /*
  * Junction (the paper's Eq. 1, as stated in prose by the summary's junction
  * paragraph and the key-visual explainer's bottom panel; block inputs from the
@@ -77,14 +87,16 @@ enum { NEL_MAX_EXITS = 8 };
  *   ids: [n_tokens] int32 in [0,vocab)       (input)
  *   emb: [vocab, d_out - d_in]         dt     (input; the residual table e_{m+1})
  *   out: [n_tokens, d_out]             dt     (output; must not alias the inputs)
+ *   mode: a nel_junction_mode (NEL_JUNCTION_RESCALE is the method)
  *   flags: device int32 flag word or NULL; a bad id sets NEL_FLAG_BAD_ID and
  *          writes a NaN row.
  * Norms are accumulated in fp32; each output element is rounded once.
- * Errors: NEL_ESHAPE if n_tokens < 0, d_in < 0, d_out <= d_in or vocab < 1.
+ * Errors: NEL_ESHAPE if n_tokens < 0, d_in < 0, d_out <= d_in or vocab < 1;
+ * NEL_EINVAL for an unknown mode.
  */
 nel_status nel_junction(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_out,
                         int32_t vocab, const void* h, const int32_t* ids, const void* emb,
-                        void* out, int32_t* flags, void* stream);
+                        void* out, int32_t mode, int32_t* flags, void* stream);
 
 /*
  * Exit heads with greedy argmax (copyedit of Sec. 2: sub-model m ends in its
@@ -240,7 +252,10 @@ nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens
  * ("Matryoshka Language Model Suites", junction paragraph, for the forward).
  * stop_grad != 0 is arm (B) of follow-up 2 on "Is nesting the cheapest way to
  * build a model suite?": no gradient reaches h through the junction (dh = 0)
- * while the embedding still receives both terms.
+ * while the embedding still receives both terms.  mode (nel_junction_mode)
+ * selects the forward it differentiates: NEL_JUNCTION_NO_RESCALE gives
+ * dh = dh_up and demb[v] = sum dg_up; NEL_JUNCTION_ZERO_FILL drops the dg_up
+ * term (the zeros do not depend on emb).
  *   h:     [n_tokens, d_in] dt, or NULL when d_in == 0 (block 1)
  *   ids:   [n_tokens] int32;  emb: [vocab, d_out - d_in] dt;  dout: [n_tokens, d_out] dt
  *   dh:    NULL or [n_tokens, d_in] dt (must be NULL when d_in == 0)
@@ -256,9 +271,9 @@ nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens
  */
 nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_out,
                                  int32_t vocab, const void* h, const int32_t* ids,
-                                 const void* emb, const void* dout, int32_t stop_grad, void* dh,
-                                 float* demb, int32_t* flags, void* workspace, size_t ws_bytes,
-                                 void* stream);
+                                 const void* emb, const void* dout, int32_t stop_grad,
+                                 int32_t mode, void* dh, float* demb, int32_t* flags,
+                                 void* workspace, size_t ws_bytes, void* stream);
 /* Bytes of workspace nel_junction_backward needs (0 on bad arguments). */
 size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t d_in, int32_t d_out,
                                        int32_t vocab);

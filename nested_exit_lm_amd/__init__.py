@@ -29,12 +29,14 @@ __all__ = [
     "timing_read", "timing_reset", "KERNELS", "OP_LOSS", "OP_HEADS", "FLAG_BAD_ID",
     "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed", "head_backward",
     "head_backward_workspace_size", "junction_backward", "speculative_verify",
+    "JUNCTION_RESCALE", "JUNCTION_NO_RESCALE", "JUNCTION_ZERO_FILL",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 F32, BF16 = 0, 1
+JUNCTION_RESCALE, JUNCTION_NO_RESCALE, JUNCTION_ZERO_FILL = 0, 1, 2
 OP_LOSS, OP_HEADS = 0, 1
 FLAG_BAD_ID, FLAG_BAD_LABEL = 1, 2
 MAX_EXITS = 8
@@ -85,7 +87,7 @@ def load():
                           "import torch before any other HIP library")
     c_int, c_i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     sig = {
-        "nel_junction": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp],
+        "nel_junction": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, c_int, vp, vp],
         "nel_exit_heads": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
         "nel_exit_heads_packed": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
         "nel_pack_weights": [c_int, c_int, c_int, vp, vp, vp],
@@ -97,8 +99,8 @@ def load():
         "nel_workspace_size": [c_int, c_int, c_i64, c_int],
         "nel_head_backward": [c_int, c_i64, c_int, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
         "nel_head_backward_workspace": [c_i64, c_int, c_int],
-        "nel_junction_backward": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, c_int, vp, vp,
-                                  vp, vp, sz, vp],
+        "nel_junction_backward": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, c_int, c_int,
+                                  vp, vp, vp, vp, sz, vp],
         "nel_junction_backward_workspace": [c_i64, c_int, c_int, c_int],
         "nel_speculative_verify": [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, ctypes.c_float,
                                    ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
@@ -197,8 +199,9 @@ def _workspace(op, device, nbytes):
 
 
 # ----------------------------------------------------------------- entry points
-def junction(h, ids, emb, out=None, flags=None):
-    """out[t] = [h[t] * ||emb[ids[t]]|| / ||h[t]||, emb[ids[t]]]; h may be None (block 1)."""
+def junction(h, ids, emb, out=None, flags=None, mode: int = 0):
+    """out[t] = [h[t] * ||emb[ids[t]]|| / ||h[t]||, emb[ids[t]]]; h may be None (block 1).
+    mode: JUNCTION_RESCALE (the method), JUNCTION_NO_RESCALE, JUNCTION_ZERO_FILL."""
     torch = _torch()
     device = emb.device
     n = ids.shape[0]
@@ -213,7 +216,7 @@ def junction(h, ids, emb, out=None, flags=None):
     lib = load()
     _check(lib.nel_junction(_dt(emb), n, d_in, d_in + de, emb.shape[0], _dev(h, device, "h"),
                             _dev(ids, device, "ids"), _dev(emb, device, "emb"),
-                            _dev(out, device, "out"), _dev(flags, device, "flags"),
+                            _dev(out, device, "out"), int(mode), _dev(flags, device, "flags"),
                             _stream(device)), "nel_junction")
     return out
 
@@ -430,7 +433,8 @@ _JBWD_WS = Workspace()
 
 
 def junction_backward(h, ids, emb, dout, stop_grad: bool = False, want_dh: bool = True,
-                      want_demb: bool = True, dh=None, demb=None, flags=None, workspace=None):
+                      want_demb: bool = True, dh=None, demb=None, flags=None, workspace=None,
+                      mode: int = 0):
     """Gradients of junction(h, ids, emb) given dout = dL/dout: (dL/dh in h's dtype or None,
     dL/demb fp32 [V, d_out - d_in] or None).  h may be None (block 1)."""
     torch = _torch()
@@ -458,7 +462,7 @@ def junction_backward(h, ids, emb, dout, stop_grad: bool = False, want_dh: bool 
     _check(lib.nel_junction_backward(_dt(emb), n, d_in, d_in + de, emb.shape[0],
                                      _dev(h, device, "h"), _dev(ids, device, "ids"),
                                      _dev(emb, device, "emb"), _dev(dout, device, "dout"),
-                                     1 if stop_grad else 0, _dev(dh, device, "dh"),
+                                     1 if stop_grad else 0, int(mode), _dev(dh, device, "dh"),
                                      _dev(demb, device, "demb"), _dev(flags, device, "flags"),
                                      wsb.data_ptr(), wsb.numel(), _stream(device)),
            "nel_junction_backward")

@@ -122,9 +122,10 @@ size_t nel_workspace_size(int32_t op, int32_t n_exits, int64_t n_tokens, int32_t
 
 nel_status nel_junction(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_out,
                         int32_t vocab, const void* h, const int32_t* ids, const void* emb,
-                        void* out, int32_t* flags, void* stream) {
+                        void* out, int32_t mode, int32_t* flags, void* stream) {
   if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
   if (n_tokens < 0 || d_in < 0 || d_out <= d_in || vocab < 1) return NEL_ESHAPE;
+  if (mode < NEL_JUNCTION_RESCALE || mode > NEL_JUNCTION_ZERO_FILL) return NEL_EINVAL;
   if (n_tokens > 0 && (!ids || !emb || !out || (d_in > 0 && !h))) return NEL_EINVAL;
   if (misaligned(h) || misaligned4(ids) || misaligned(emb) || misaligned(out) || misaligned4(flags))
     return NEL_EALIGN;
@@ -132,8 +133,10 @@ nel_status nel_junction(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(timed(NEL_K_JUNCTION, s, [&] {
     return dt == NEL_BF16
-               ? launch_junction<bf16_t>(n_tokens, d_in, d_out, vocab, h, ids, emb, out, flags, s)
-               : launch_junction<float>(n_tokens, d_in, d_out, vocab, h, ids, emb, out, flags, s);
+               ? launch_junction<bf16_t>(n_tokens, d_in, d_out, vocab, h, ids, emb, out, flags,
+                                         mode, s)
+               : launch_junction<float>(n_tokens, d_in, d_out, vocab, h, ids, emb, out, flags,
+                                        mode, s);
   }));
 }
 
@@ -374,11 +377,12 @@ size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t d_in, int32_t d
 
 nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, int32_t d_out,
                                  int32_t vocab, const void* h, const int32_t* ids,
-                                 const void* emb, const void* dout, int32_t stop_grad, void* dh,
-                                 float* demb, int32_t* flags, void* workspace, size_t ws_bytes,
-                                 void* stream) {
+                                 const void* emb, const void* dout, int32_t stop_grad,
+                                 int32_t mode, void* dh, float* demb, int32_t* flags,
+                                 void* workspace, size_t ws_bytes, void* stream) {
   if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
   if (n_tokens < 0 || d_in < 0 || d_out <= d_in || vocab < 1) return NEL_ESHAPE;
+  if (mode < NEL_JUNCTION_RESCALE || mode > NEL_JUNCTION_ZERO_FILL) return NEL_EINVAL;
   if (n_tokens > kJunctionBwdMaxTokens) return NEL_ESHAPE;
   if (!dh && !demb) return NEL_EINVAL;
   if (d_in == 0 && dh) return NEL_EINVAL;   // block 1 has no h to differentiate
@@ -393,9 +397,9 @@ nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, i
   return from_hip(timed(NEL_K_JUNCTION_BWD, s, [&] {
     return dt == NEL_BF16
                ? launch_junction_backward<bf16_t>(n_tokens, d_in, d_out, vocab, h, ids, emb, dout,
-                                                  stop_grad != 0, dh, demb, workspace, flags, s)
+                                                  stop_grad != 0, mode, dh, demb, workspace, flags, s)
                : launch_junction_backward<float>(n_tokens, d_in, d_out, vocab, h, ids, emb, dout,
-                                                 stop_grad != 0, dh, demb, workspace, flags, s);
+                                                 stop_grad != 0, mode, dh, demb, workspace, flags, s);
   }));
 }
 

@@ -6,6 +6,9 @@
 
 namespace nel {
 
+// Junction modes (values of nel_junction_mode).
+constexpr int kJunctionRescale = 0, kJunctionNoRescale = 1, kJunctionZeroFill = 2;
+
 constexpr int kMaxExits = 8;
 // Smallest token and vocabulary extent of a head-GEMM workgroup tile.  Loss
 // statistics are kept per (exit, vocabulary tile, token); the GEMM reports
@@ -89,8 +92,8 @@ constexpr int64_t kJunctionBwdMaxTokens = int64_t{1} << 30;
 template <typename T>
 hipError_t launch_junction_backward(int64_t n, int d_in, int d_out, int vocab, const void* h,
                                     const int32_t* ids, const void* emb, const void* dout,
-                                    int stop_grad, void* dh, float* demb, void* workspace,
-                                    int32_t* flags, hipStream_t s);
+                                    int stop_grad, int mode, void* dh, float* demb,
+                                    void* workspace, int32_t* flags, hipStream_t s);
 
 // Workspace of the head backward (byte offsets): W^T and h^T in the tiled
 // layout, G^T row-major; K of the token dimension padded to n_pad.
@@ -114,7 +117,7 @@ hipError_t launch_bwd_gemm(const void* A, int a_rows, const void* B, int64_t b_r
 template <typename T>
 hipError_t launch_junction(int64_t n, int d_in, int d_out, int vocab, const void* h,
                            const int32_t* ids, const void* emb, void* out, int32_t* flags,
-                           hipStream_t s);
+                           int mode, hipStream_t s);
 
 // Head GEMM + per-tile loss statistics (teacher = exit n_exits-1 first),
 // row-major weights.

@@ -6,6 +6,10 @@
 // residual embedding e_{m+1}[x_t] and concatenated with it along channels.
 // Block 1 reads e_1[x_t] alone (copyedit of Sec. 2, D_0 = 0).
 //
+// Modes (the 200M ablations of the same passages): kJunctionNoRescale passes
+// h through unscaled; kJunctionZeroFill writes zeros in place of the
+// embedding while the rescale target stays ||e_{m+1}[x_t]||.
+//
 // HBM-bound: each token reads d_in + (d_out - d_in) elements and writes d_out.
 // Every lane moves 16-byte chunks; the token's chunks stay in registers
 // between the norm pass and the write pass, so h and the embedding row are
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(256) void junction_vec(int64_t n, int d_in, int d_o
                                                     const T* __restrict__ h,
                                                     const int32_t* __restrict__ ids,
                                                     const T* __restrict__ emb, T* __restrict__ out,
-                                                    int32_t* __restrict__ flags) {
+                                                    int32_t* __restrict__ flags, int mode) {
   constexpr int C = Elem<T>::kChunk;
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + (threadIdx.x >> 6);
@@ -102,12 +106,13 @@ __global__ __launch_bounds__(256) void junction_vec(int64_t n, int d_in, int d_o
   }
   sh = wave_sum(sh);
   se = wave_sum(se);
-  const float k = norm_ratio(sh, se);
+  const float k = mode == kJunctionNoRescale ? 1.f : norm_ratio(sh, se);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) {
     const int c = lane + 64 * j;
     if (c < nh) __builtin_nontemporal_store(chunk_scale<T>(hc[j], k), orow + c);
-    if (c < ne) __builtin_nontemporal_store(ec[j], orow + nh + c);
+    if (c < ne) __builtin_nontemporal_store(mode == kJunctionZeroFill ? zero : ec[j], orow + nh + c);
   }
 }
 
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(256) void junction_elem(int64_t n, int d_in, int d_
                                                      const T* __restrict__ h,
                                                      const int32_t* __restrict__ ids,
                                                      const T* __restrict__ emb, T* __restrict__ out,
-                                                     int32_t* __restrict__ flags) {
+                                                     int32_t* __restrict__ flags, int mode) {
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + (threadIdx.x >> 6);
   if (t >= n) return;
@@ -143,9 +148,10 @@ __global__ __launch_bounds__(256) void junction_elem(int64_t n, int d_in, int d_
   }
   sh = wave_sum(sh);
   se = wave_sum(se);
-  const float k = norm_ratio(sh, se);
+  const float k = mode == kJunctionNoRescale ? 1.f : norm_ratio(sh, se);
   for (int c = lane; c < d_in; c += 64) orow[c] = Elem<T>::from_f32(Elem<T>::to_f32(hrow[c]) * k);
-  for (int c = lane; c < de; c += 64) orow[d_in + c] = erow[c];
+  for (int c = lane; c < de; c += 64)
+    orow[d_in + c] = mode == kJunctionZeroFill ? Elem<T>::from_f32(0.f) : erow[c];
 }
 
 }  // namespace
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(256) void junction_elem(int64_t n, int d_in, int d_
 template <typename T>
 hipError_t launch_junction(int64_t n, int d_in, int d_out, int vocab, const void* h,
                            const int32_t* ids, const void* emb, void* out, int32_t* flags,
-                           hipStream_t s) {
+                           int mode, hipStream_t s) {
   if (n == 0) return hipSuccess;
   constexpr int C = Elem<T>::kChunk;
   const int de = d_out - d_in;
@@ -165,16 +171,16 @@ hipError_t launch_junction(int64_t n, int d_in, int d_out, int vocab, const void
   T* op = static_cast<T*>(out);
   if (vec)
     hipLaunchKernelGGL(junction_vec<T>, grid, dim3(256), 0, s, n, d_in, d_out, vocab, hp, ids, ep,
-                       op, flags);
+                       op, flags, mode);
   else
     hipLaunchKernelGGL(junction_elem<T>, grid, dim3(256), 0, s, n, d_in, d_out, vocab, hp, ids,
-                       ep, op, flags);
+                       ep, op, flags, mode);
   return hipGetLastError();
 }
 
 template hipError_t launch_junction<bf16_t>(int64_t, int, int, int, const void*, const int32_t*,
-                                            const void*, void*, int32_t*, hipStream_t);
+                                            const void*, void*, int32_t*, int, hipStream_t);
 template hipError_t launch_junction<float>(int64_t, int, int, int, const void*, const int32_t*,
-                                           const void*, void*, int32_t*, hipStream_t);
+                                           const void*, void*, int32_t*, int, hipStream_t);
 
 }  // namespace nel

@@ -11,7 +11,9 @@
 // Both are 0 where the forward's rescaled half is identically 0.  With the
 // stop-gradient option ("Is nesting the cheapest way to build a model
 // suite?", follow-up 2, arm (B): each block learns only from its own exit)
-// dL/dh_t = 0 while the embedding still receives both terms.
+// dL/dh_t = 0 while the embedding still receives both terms.  The ablation
+// modes drop terms: no rescale has dL/dh = delta_h, c_t = 0; zero fill has no
+// delta_g term.
 //
 // dL/dh and c_t: one wavefront per token (16-byte chunks where rows allow).  dL/de is a sum over the tokens of
 // each id, and ids follow a Zipf law (one id can hold 15 % of the tokens), so
@@ -61,7 +63,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void junction_bwd_token(
     int64_t n, int d_in, int d_out, int vocab, const T* __restrict__ h,
     const int32_t* __restrict__ ids, const T* __restrict__ emb, const T* __restrict__ dout,
-    int stop_grad, T* __restrict__ dh, float* __restrict__ ct, int32_t* __restrict__ flags) {
+    int stop_grad, T* __restrict__ dh, float* __restrict__ ct, int32_t* __restrict__ flags, int mode) {
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + (threadIdx.x >> 6);
   if (t >= n) return;
@@ -92,11 +94,12 @@ __global__ __launch_bounds__(256) void junction_bwd_token(
   sh = wave_sum(sh);
   se = wave_sum(se);
   hd = wave_sum(hd);
-  const bool live = sh > 0.f && se > 0.f;   // the rescaled half is not identically 0
+  const bool norm = mode != kJunctionNoRescale;
+  const bool live = norm && sh > 0.f && se > 0.f;   // the rescaled half depends on a and b
   const float a = sqrtf(sh);
   if (lane == 0) ct[t] = live ? hd / a : 0.f;
   if (!dh) return;
-  const float k = (live && !stop_grad) ? sqrtf(se) / a : 0.f;
+  const float k = stop_grad ? 0.f : norm ? (live ? sqrtf(se) / a : 0.f) : 1.f;
   const float proj = live ? hd / sh : 0.f;
   for (int c = lane; c < d_in; c += 64)
     dh[t * d_in + c] = Elem<T>::from_f32(k * (ld(drow, c) - ld(hrow, c) * proj));
@@ -143,7 +146,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void junction_bwd_token_vec(
     int64_t n, int d_in, int d_out, int vocab, const T* __restrict__ h,
     const int32_t* __restrict__ ids, const T* __restrict__ emb, const T* __restrict__ dout,
-    int stop_grad, T* __restrict__ dh, float* __restrict__ ct, int32_t* __restrict__ flags) {
+    int stop_grad, T* __restrict__ dh, float* __restrict__ ct, int32_t* __restrict__ flags, int mode) {
   constexpr int C = Chunk<T>::C;
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + (threadIdx.x >> 6);
@@ -195,11 +198,12 @@ __global__ __launch_bounds__(256) void junction_bwd_token_vec(
   sh = wave_sum(sh);
   se = wave_sum(se);
   hd = wave_sum(hd);
-  const bool live = sh > 0.f && se > 0.f;
+  const bool norm = mode != kJunctionNoRescale;
+  const bool live = norm && sh > 0.f && se > 0.f;
   const float a = sqrtf(sh);
   if (lane == 0) ct[t] = live ? hd / a : 0.f;
   if (!dh) return;
-  const float k = (live && !stop_grad) ? sqrtf(se) / a : 0.f;
+  const float k = stop_grad ? 0.f : norm ? (live ? sqrtf(se) / a : 0.f) : 1.f;
   const float proj = live ? hd / sh : 0.f;
   u32x4* orow = reinterpret_cast<u32x4*>(dh + t * d_in);
 #pragma unroll
@@ -422,7 +426,7 @@ __global__ __launch_bounds__(256) void segsum_kernel(
     int d_in, int d_out, const T* __restrict__ emb, const T* __restrict__ dout,
     const float* __restrict__ ct, const int32_t* __restrict__ list,
     const int4* __restrict__ seginfo, const int32_t* __restrict__ counts,
-    float* __restrict__ partial, float* __restrict__ pcs, float* __restrict__ demb) {
+    float* __restrict__ partial, float* __restrict__ pcs, float* __restrict__ demb, int use_dg) {
   static_assert(!ONE || VEC, "one-slab path reads 16-byte chunks");
   __shared__ float red[4];
   const int de = d_out - d_in;
@@ -455,7 +459,10 @@ __global__ __launch_bounds__(256) void segsum_kernel(
         for (int u = 0; u < 8; ++u) {
           const int64_t t = list[min(k + u, k1 - 1)];
           const T* drow = dout + t * d_out + d_in;   // delta_g
-          if constexpr (VEC) {
+          if (!use_dg) {
+#pragma unroll
+            for (int q = 0; q < kCols; ++q) x[u][q] = 0.f;
+          } else if constexpr (VEC) {
             const int cb = col_of<true>(c0, 0);
             if (cb < de) load_cols(drow + cb, x[u]);
           } else {
@@ -630,8 +637,8 @@ JunctionBwdWs junction_bwd_ws_layout(int64_t n, int d_in, int d_out, int vocab) 
 template <typename T>
 hipError_t launch_junction_backward(int64_t n, int d_in, int d_out, int vocab, const void* h,
                                     const int32_t* ids, const void* emb, const void* dout,
-                                    int stop_grad, void* dh, float* demb, void* workspace,
-                                    int32_t* flags, hipStream_t s) {
+                                    int stop_grad, int mode, void* dh, float* demb,
+                                    void* workspace, int32_t* flags, hipStream_t s) {
   const JunctionBwdWs L = junction_bwd_ws_layout(n, d_in, d_out, vocab);
   char* ws = static_cast<char*>(workspace);
   auto i32 = [&](size_t off) { return reinterpret_cast<int32_t*>(ws + off); };
@@ -648,11 +655,13 @@ hipError_t launch_junction_backward(int64_t n, int d_in, int d_out, int vocab, c
     if (chunked && d_in <= 64 * kTokNch * C)
       hipLaunchKernelGGL((junction_bwd_token_vec<T>), grid, dim3(256), 0, s, n, d_in, d_out,
                          vocab, static_cast<const T*>(h), ids, static_cast<const T*>(emb),
-                         static_cast<const T*>(dout), stop_grad, static_cast<T*>(dh), ct, flags);
+                         static_cast<const T*>(dout), stop_grad, static_cast<T*>(dh), ct, flags,
+                         mode);
     else
       hipLaunchKernelGGL((junction_bwd_token<T>), grid, dim3(256), 0, s, n, d_in, d_out, vocab,
                          static_cast<const T*>(h), ids, static_cast<const T*>(emb),
-                         static_cast<const T*>(dout), stop_grad, static_cast<T*>(dh), ct, flags);
+                         static_cast<const T*>(dout), stop_grad, static_cast<T*>(dh), ct, flags,
+                         mode);
   }
   if (!demb) return hipGetLastError();
   const int de = d_out - d_in;
@@ -682,15 +691,16 @@ hipError_t launch_junction_backward(int64_t n, int d_in, int d_out, int vocab, c
     const T* d = static_cast<const T*>(dout);
     const int32_t* lst = i32(L.list);
     const int32_t* cn = i32(L.counts);
+    const int use_dg = mode != kJunctionZeroFill;   // zero fill: the zeros do not depend on e
     if (vec && de <= 256 * kCols)
       hipLaunchKernelGGL((segsum_kernel<T, true, true>), sgrid, dim3(256), 0, s, d_in, d_out, e,
-                         d, ct, lst, seginfo, cn, partial, pcs, demb);
+                         d, ct, lst, seginfo, cn, partial, pcs, demb, use_dg);
     else if (vec)
       hipLaunchKernelGGL((segsum_kernel<T, true, false>), sgrid, dim3(256), 0, s, d_in, d_out, e,
-                         d, ct, lst, seginfo, cn, partial, pcs, demb);
+                         d, ct, lst, seginfo, cn, partial, pcs, demb, use_dg);
     else
       hipLaunchKernelGGL((segsum_kernel<T, false, false>), sgrid, dim3(256), 0, s, d_in, d_out, e,
-                         d, ct, lst, seginfo, cn, partial, pcs, demb);
+                         d, ct, lst, seginfo, cn, partial, pcs, demb, use_dg);
     if (vec)
       hipLaunchKernelGGL((combine_kernel<T, true>), cgrid, dim3(256), 0, s, d_in, d_out, e,
                          i32(L.cnt), i32(L.poff), i32(L.prow), cn, partial, pcs, demb);
@@ -705,9 +715,11 @@ hipError_t launch_junction_backward(int64_t n, int d_in, int d_out, int vocab, c
 
 template hipError_t launch_junction_backward<bf16_t>(int64_t, int, int, int, const void*,
                                                      const int32_t*, const void*, const void*, int,
-                                                     void*, float*, void*, int32_t*, hipStream_t);
+                                                     int, void*, float*, void*, int32_t*,
+                                                     hipStream_t);
 template hipError_t launch_junction_backward<float>(int64_t, int, int, int, const void*,
                                                     const int32_t*, const void*, const void*, int,
-                                                    void*, float*, void*, int32_t*, hipStream_t);
+                                                    int, void*, float*, void*, int32_t*,
+                                                    hipStream_t);
 
 }  // namespace nel

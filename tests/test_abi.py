@@ -51,14 +51,16 @@ MIS4 = 0x10002          # misaligned for int32 arrays
 
 def test_junction_host_validation():
     lib = nel.load()
-    assert lib.nel_junction(7, 4, 8, 16, 10, FAKE, FAKE, FAKE, FAKE, None, None) == -3
-    assert lib.nel_junction(1, -1, 8, 16, 10, FAKE, FAKE, FAKE, FAKE, None, None) == -2
-    assert lib.nel_junction(1, 4, 8, 8, 10, FAKE, FAKE, FAKE, FAKE, None, None) == -2
-    assert lib.nel_junction(1, 4, 8, 16, 0, FAKE, FAKE, FAKE, FAKE, None, None) == -2
-    assert lib.nel_junction(1, 4, 8, 16, 10, None, FAKE, FAKE, FAKE, None, None) == -1
-    assert lib.nel_junction(1, 4, 8, 16, 10, MIS, FAKE, FAKE, FAKE, None, None) == -4
-    assert lib.nel_junction(1, 4, 8, 16, 10, FAKE, MIS4, FAKE, FAKE, None, None) == -4
-    assert lib.nel_junction(1, 0, 8, 16, 10, None, None, None, None, None, None) == 0
+    assert lib.nel_junction(7, 4, 8, 16, 10, FAKE, FAKE, FAKE, FAKE, 0, None, None) == -3
+    assert lib.nel_junction(1, -1, 8, 16, 10, FAKE, FAKE, FAKE, FAKE, 0, None, None) == -2
+    assert lib.nel_junction(1, 4, 8, 8, 10, FAKE, FAKE, FAKE, FAKE, 0, None, None) == -2
+    assert lib.nel_junction(1, 4, 8, 16, 0, FAKE, FAKE, FAKE, FAKE, 0, None, None) == -2
+    assert lib.nel_junction(1, 4, 8, 16, 10, None, FAKE, FAKE, FAKE, 0, None, None) == -1
+    assert lib.nel_junction(1, 4, 8, 16, 10, MIS, FAKE, FAKE, FAKE, 0, None, None) == -4
+    assert lib.nel_junction(1, 4, 8, 16, 10, FAKE, MIS4, FAKE, FAKE, 0, None, None) == -4
+    assert lib.nel_junction(1, 0, 8, 16, 10, None, None, None, None, 0, None, None) == 0
+    assert lib.nel_junction(1, 4, 8, 16, 10, FAKE, FAKE, FAKE, FAKE, 3, None, None) == -1
+    assert lib.nel_junction(1, 4, 8, 16, 10, FAKE, FAKE, FAKE, FAKE, -1, None, None) == -1
 
 
 def test_loss_host_validation():
@@ -173,14 +175,15 @@ def test_junction_backward_host_validation():
     assert lib.nel_junction_backward_workspace((1 << 30) + 1, 8, 16, 50) == 0
 
     def call(dt=1, n=10, d_in=8, d_out=16, V=50, h=FAKE, ids=FAKE, emb=FAKE, dout=FAKE, sg=0,
-             dh=FAKE, demb=FAKE, ws=FAKE, wsb=need):
-        return lib.nel_junction_backward(dt, n, d_in, d_out, V, h, ids, emb, dout, sg, dh, demb,
+             dh=FAKE, demb=FAKE, ws=FAKE, wsb=need, mode=0):
+        return lib.nel_junction_backward(dt, n, d_in, d_out, V, h, ids, emb, dout, sg, mode, dh, demb,
                                          None, ws, wsb, None)
 
     assert call(dt=4) == -3
     assert call(d_out=8) == -2
     assert call(V=0) == -2
     assert call(n=(1 << 30) + 1) == -2
+    assert call(mode=3) == -1
     assert call(dh=None, demb=None) == -1
     assert call(d_in=0, h=None) == -1          # block 1 has no dh
     assert call(h=None) == -1

@@ -16,7 +16,9 @@ each function states the reading it implements):
 * "Editing the methods of ...": copyedit of Sec. 2 "Modeling" -- the
   notation x, e_m in R^{V x (D_m - D_{m-1})}, D_0 = 0, W^m in R^{V x D_m}.
 * "Is nesting the cheapest way to build a model suite?" -- follow-up 4:
-  the 0.7 next-token / 0.3 teacher cross-entropy mix.
+  the 0.7 next-token / 0.3 teacher cross-entropy mix, beta = sum min(p, q),
+  and the reverse-KL / Jensen-Shannon / acceptance-loss swaps; follow-up 2,
+  arm (B): the stop-gradient at the junction.
 
 Pins: every function is checked by ``tests/test_oracle_pins.py`` and
 ``tests/test_golden.py`` against closed forms, brute force and library
@@ -26,7 +28,8 @@ factor, a temperature): against the paper itself the oracle is
 "parity unpinned"; it is pinned to the reading stated in each docstring.
 """
 from .matryoshka import (  # noqa: F401
-    junction, junction_backward, JUNCTION_RESCALE, JUNCTION_NO_RESCALE, JUNCTION_ZERO_FILL, heads, head_backward, logsumexp, softmax, matryoshka_loss, matryoshka_grad,
+    junction, junction_backward, JUNCTION_RESCALE, JUNCTION_NO_RESCALE, JUNCTION_ZERO_FILL,
+    divergence, divergence_grad, DIV_FORWARD, DIV_REVERSE_KL, DIV_JS, DIV_TV, heads, head_backward, logsumexp, softmax, matryoshka_loss, matryoshka_grad,
     argmax_lowest, accept_prefix, forward_tokens, nucleus, sample_inverse_cdf,
     speculative_verify,
 )

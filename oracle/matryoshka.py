@@ -152,7 +152,66 @@ def softmax(l: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Loss and gradients
 # ---------------------------------------------------------------------------
-def matryoshka_loss(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: float) -> Dict:
+# Distillation divergences D(p, q) between the teacher p = softmax(l_M) and a
+# student q = softmax(l_m).  DIV_FORWARD is the method's cross-entropy to the
+# teacher (summary's distillation paragraph; follow-up 4's 0.3 term); the
+# others are the swaps follow-up 4 of "Is nesting the cheapest way to build a
+# model suite?" proposes: reverse KL, Jensen-Shannon, and an acceptance loss,
+# read as the total-variation distance 1 - beta = 1 - sum_v min(p_v, q_v)
+# (beta is the acceptance probability the same follow-up defines).
+DIV_FORWARD, DIV_REVERSE_KL, DIV_JS, DIV_TV = 0, 1, 2, 3
+
+
+def _xlogy(x, y):
+    """x log y with 0 log 0 = 0."""
+    return np.where(x > 0, x * np.log(np.where(x > 0, y, 1.0)), 0.0)
+
+
+def divergence(p: np.ndarray, q: np.ndarray, kind: int) -> np.ndarray:
+    """D(p, q) per row (last axis = vocabulary), p the teacher, q the student.
+        DIV_FORWARD:    -sum p log q
+        DIV_REVERSE_KL: sum q (log q - log p)
+        DIV_JS:         (KL(p || m) + KL(q || m)) / 2,  m = (p + q) / 2
+        DIV_TV:         sum |p - q| / 2  =  1 - sum min(p, q)
+    """
+    p, q = _f64(p), _f64(q)
+    if kind == DIV_FORWARD:
+        return -np.sum(_xlogy(p, q), axis=-1)
+    if kind == DIV_REVERSE_KL:
+        return np.sum(_xlogy(q, q) - _xlogy(q, p), axis=-1)
+    if kind == DIV_JS:
+        m = 0.5 * (p + q)
+        return 0.5 * np.sum(_xlogy(p, p) - _xlogy(p, m) + _xlogy(q, q) - _xlogy(q, m), axis=-1)
+    if kind == DIV_TV:
+        return 0.5 * np.sum(np.abs(p - q), axis=-1)
+    raise ValueError(kind)
+
+
+def divergence_grad(p: np.ndarray, q: np.ndarray, kind: int) -> np.ndarray:
+    """dD/dl for q = softmax(l), p held fixed (the teacher under stop-gradient).
+    With r_v = dD/dq_v, the softmax's chain rule gives q_v (r_v - sum_u q_u r_u):
+        DIV_FORWARD:    r = -p / q               ->  q - p
+        DIV_REVERSE_KL: r = log q - log p + 1    ->  q (log q - log p - D)
+        DIV_JS:         r = log(q / m) / 2
+        DIV_TV:         r = sign(q - p) / 2      (0 where q = p)
+    """
+    p, q = _f64(p), _f64(q)
+    if kind == DIV_FORWARD:
+        return q - p
+    if kind == DIV_REVERSE_KL:
+        r = np.log(q) - np.log(p)
+    elif kind == DIV_JS:
+        r = 0.5 * (np.log(q) - np.log(0.5 * (p + q)))
+    elif kind == DIV_TV:
+        r = 0.5 * np.sign(q - p)
+    else:
+        raise ValueError(kind)
+    return q * (r - np.sum(q * r, axis=-1, keepdims=True))
+
+
+def matryoshka_loss(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: float,
+                    exit_weights: Optional[Sequence[float]] = None,
+                    div: int = DIV_FORWARD) -> Dict:
     """Per-exit next-token cross-entropy plus online distillation.
 
     "Matryoshka Language Model Suites", distillation paragraph: the largest
@@ -161,13 +220,15 @@ def matryoshka_loss(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: flo
     loss (follow-up 4 of "Is nesting the cheapest way ...": 0.7 next-token
     plus 0.3 cross-entropy to the largest model).  Main-visual explainer,
     panel (b): distillation goes only into the smaller exits.  Limitations
-    paragraph: per-sub-model losses are summed with equal weight.
+    paragraph: per-sub-model losses are summed with equal weight, and
+    reweighting them is the fix a 200M sweep points to (exit_weights lambda,
+    default all 1).
 
         CE_m   = LSE(l_m) - l_m[y]
-        Dist_m = -sum_v p_v log softmax(l_m)_v = LSE(l_m) - sum_v p_v l_m,v,
-                 p = softmax(l_M)                              (m < M)
+        Dist_m = D(p, softmax(l_m)),  p = softmax(l_M)          (m < M)
+                 (DIV_FORWARD: -sum_v p_v log softmax(l_m)_v = LSE(l_m) - sum_v p_v l_m,v)
         L_m    = (1 - alpha) CE_m + alpha Dist_m               (m < M)
-        L_M    = CE_M,          total = sum_m L_m
+        L_M    = CE_M,          total = sum_m lambda_m L_m
 
     Returns per-token arrays ce, dist (0 for the teacher), loss [M, N],
     total [N], and their means over tokens.
@@ -175,6 +236,7 @@ def matryoshka_loss(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: flo
     M = len(logits)
     y = np.asarray(labels, dtype=np.int64)
     n = y.shape[0]
+    lam = np.ones(M) if exit_weights is None else _f64(exit_weights)
     rows = np.arange(n)
     ls = [_f64(l) for l in logits]
     lse = np.stack([logsumexp(l) for l in ls])                   # [M, N]
@@ -182,11 +244,14 @@ def matryoshka_loss(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: flo
     p = np.exp(ls[-1] - lse[-1][:, None])
     dist = np.zeros((M, n))
     for m in range(M - 1):
-        dist[m] = lse[m] - np.sum(p * ls[m], axis=1)
+        if div == DIV_FORWARD:
+            dist[m] = lse[m] - np.sum(p * ls[m], axis=1)
+        else:
+            dist[m] = divergence(p, np.exp(ls[m] - lse[m][:, None]), div)
     loss = np.empty((M, n))
     loss[: M - 1] = (1.0 - alpha) * ce[: M - 1] + alpha * dist[: M - 1]
     loss[M - 1] = ce[M - 1]
-    total = np.sum(loss, axis=0)
+    total = np.sum(lam[:, None] * loss, axis=0)
     return {
         "lse": lse, "ce": ce, "dist": dist, "loss": loss, "total": total,
         "mean_ce": ce.mean(axis=1), "mean_dist": dist.mean(axis=1),
@@ -195,17 +260,20 @@ def matryoshka_loss(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: flo
 
 
 def matryoshka_grad(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: float,
-                    grad_scale: float = 1.0) -> List[np.ndarray]:
+                    grad_scale: float = 1.0, exit_weights: Optional[Sequence[float]] = None,
+                    div: int = DIV_FORWARD) -> List[np.ndarray]:
     """d(grad_scale * sum_t total_t) / d l_m for every exit.
 
     The teacher's distribution enters the smaller exits' losses under
     stop-gradient, so exit M's gradient is that of CE_M alone:
 
-        g_m = grad_scale * (softmax(l_m) - (1 - alpha) onehot(y) - alpha p)   (m < M)
-        g_M = grad_scale * (p - onehot(y))
+        g_m = grad_scale lambda_m ((1 - alpha)(q_m - onehot(y)) + alpha dD/dl_m)   (m < M)
+        g_M = grad_scale lambda_M (p - onehot(y))
+    (DIV_FORWARD: dD/dl_m = q_m - p, so g_m = q_m - (1 - alpha) onehot(y) - alpha p.)
     """
     M = len(logits)
     y = np.asarray(labels, dtype=np.int64)
+    lam = np.ones(M) if exit_weights is None else _f64(exit_weights)
     rows = np.arange(y.shape[0])
     p = softmax(logits[-1])
     out = []
@@ -213,10 +281,14 @@ def matryoshka_grad(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: flo
         if m == M - 1:
             g = p.copy()
             g[rows, y] -= 1.0
-        else:
+        elif div == DIV_FORWARD:
             g = softmax(logits[m]) - alpha * p
             g[rows, y] -= 1.0 - alpha
-        out.append(grad_scale * g)
+        else:
+            q = softmax(logits[m])
+            g = (1.0 - alpha) * q + alpha * divergence_grad(p, q, div)
+            g[rows, y] -= 1.0 - alpha
+        out.append(grad_scale * lam[m] * g)
     return out
 
 
@@ -337,7 +409,8 @@ def speculative_verify(draft_logits: np.ndarray, verify_logits: np.ndarray,
 # ---------------------------------------------------------------------------
 def forward_tokens(hs: Sequence[np.ndarray], ws: Sequence[np.ndarray], labels: np.ndarray,
                    alpha: float, grad_scale: float = 1.0, rows=None, chunk: int = 1024,
-                   want_grad: bool = True, exits: Optional[Sequence[int]] = None):
+                   want_grad: bool = True, exits: Optional[Sequence[int]] = None,
+                   exit_weights: Optional[Sequence[float]] = None, div: int = DIV_FORWARD):
     """Heads, losses and gradients for the tokens ``rows`` (default: all),
     ``chunk`` tokens at a time.  Returns (loss dict over the rows, list of
     per-exit gradient arrays [len(rows), V] or None)."""
@@ -349,9 +422,10 @@ def forward_tokens(hs: Sequence[np.ndarray], ws: Sequence[np.ndarray], labels: n
     for s in range(0, len(rows), chunk):
         r = rows[s:s + chunk]
         lg = heads([hs[m][r] for m in sel], [ws[m] for m in sel])
-        parts.append(matryoshka_loss(lg, labels[r], alpha))
+        parts.append(matryoshka_loss(lg, labels[r], alpha, exit_weights, div))
         if want_grad:
-            for j, g in enumerate(matryoshka_grad(lg, labels[r], alpha, grad_scale)):
+            for j, g in enumerate(matryoshka_grad(lg, labels[r], alpha, grad_scale, exit_weights,
+                                                  div)):
                 grads[j].append(g)
     keys = ("lse", "ce", "dist", "loss")
     res = {k: np.concatenate([p[k] for p in parts], axis=1) for k in keys}

@@ -517,3 +517,93 @@ def test_greedy_limit_is_greedy_acceptance():
     vtok = oracle.argmax_lowest(vl)
     np.testing.assert_array_equal(acc, oracle.accept_prefix(dtok, vtok, 6))
     np.testing.assert_array_equal(nxt, vtok[np.arange(B), acc])
+
+
+# ------------------------------------------------ divergences and exit weights
+def test_divergence_values_against_scipy():
+    """Reverse KL is scipy's relative entropy of q to p; Jensen-Shannon is the
+    square of scipy's Jensen-Shannon distance (natural log); total variation is
+    half the L1 distance and 1 - beta of the speculative rule."""
+    import scipy.spatial.distance
+    import scipy.stats
+    r = rng(30)
+    lp = r.standard_normal((6, 40)) * 2
+    lq = r.standard_normal((6, 40)) * 2
+    p, q = scipy.special.softmax(lp, axis=1), scipy.special.softmax(lq, axis=1)
+    np.testing.assert_allclose(oracle.divergence(p, q, oracle.DIV_REVERSE_KL),
+                               scipy.stats.entropy(q, p, axis=1), rtol=1e-12)
+    np.testing.assert_allclose(oracle.divergence(p, q, oracle.DIV_FORWARD),
+                               scipy.stats.entropy(p, axis=1) + scipy.stats.entropy(p, q, axis=1),
+                               rtol=1e-12)
+    js = np.array([scipy.spatial.distance.jensenshannon(p[i], q[i]) ** 2 for i in range(6)])
+    np.testing.assert_allclose(oracle.divergence(p, q, oracle.DIV_JS), js, rtol=1e-10)
+    beta, _, _ = oracle.speculative_verify(lq[:, None, :].repeat(2, 1), lp[:, None, :].repeat(2, 1),
+                                           np.zeros((6, 2), int), np.zeros((6, 2)), np.zeros(6), 1)
+    np.testing.assert_allclose(oracle.divergence(p, q, oracle.DIV_TV), 1.0 - beta[:, 0], rtol=1e-12)
+    np.testing.assert_allclose(oracle.divergence(p, q, oracle.DIV_TV),
+                               0.5 * np.abs(p - q).sum(axis=1), rtol=1e-12)
+    for k in (oracle.DIV_REVERSE_KL, oracle.DIV_JS, oracle.DIV_TV):
+        np.testing.assert_allclose(oracle.divergence(p, p, k), 0.0, atol=1e-15)
+
+
+@pytest.mark.parametrize("div", [1, 2, 3])
+def test_divergence_loss_gradient_central_differences(div):
+    """The whole loss (three exits, alpha, exit weights) with each divergence:
+    the oracle gradient of every student exit against central differences of
+    the oracle total, the teacher held fixed inside D (stop-gradient)."""
+    r = rng(31 + div)
+    V, n, M, alpha = 7, 3, 3, 0.4
+    lam = np.array([0.5, 2.0, 1.5])
+    ls = [r.standard_normal((n, V)) * 1.5 for _ in range(M)]
+    y = r.integers(0, V, n)
+    g = oracle.matryoshka_grad(ls, y, alpha, exit_weights=lam, div=div)
+    p = scipy.special.softmax(ls[-1], axis=1)
+    eps = 1e-6
+    for m in range(M - 1):
+        num = np.zeros((n, V))
+        for t in range(n):
+            for v in range(V):
+                def total(delta):
+                    lm = ls[m].copy()
+                    lm[t, v] += delta
+                    q = scipy.special.softmax(lm, axis=1)
+                    ce = -np.log(q[np.arange(n), y])
+                    return np.sum(lam[m] * ((1 - alpha) * ce + alpha * oracle.divergence(p, q, div)))
+                num[t, v] = (total(eps) - total(-eps)) / (2 * eps)
+        np.testing.assert_allclose(g[m], num, atol=1e-7)
+    # the teacher's gradient ignores the divergence, scaled by its weight
+    q = p.copy()
+    q[np.arange(n), y] -= 1.0
+    np.testing.assert_allclose(g[-1], lam[-1] * q, atol=1e-15)
+
+
+def test_reverse_kl_gradient_matches_torch_kl_div():
+    """torch.nn.functional.kl_div with log targets computes KL(target || input):
+    target = log_softmax of the student, input = the detached teacher's."""
+    r = rng(35)
+    n, V = 5, 11
+    ls = torch.tensor(r.standard_normal((n, V)) * 2, requires_grad=True)
+    lt = torch.tensor(r.standard_normal((n, V)) * 2)
+    kl = torch.nn.functional.kl_div(torch.log_softmax(lt, 1), torch.log_softmax(ls, 1),
+                                    reduction="none", log_target=True).sum(1)
+    kl.sum().backward()
+    p = scipy.special.softmax(lt.numpy(), axis=1)
+    q = scipy.special.softmax(ls.detach().numpy(), axis=1)
+    np.testing.assert_allclose(oracle.divergence(p, q, oracle.DIV_REVERSE_KL), kl.detach().numpy(),
+                               rtol=1e-12)
+    np.testing.assert_allclose(oracle.divergence_grad(p, q, oracle.DIV_REVERSE_KL), ls.grad.numpy(),
+                               atol=1e-13)
+
+
+def test_exit_weights_scale_total_and_gradients():
+    """total = sum_m lambda_m L_m; equal weights of 1 are the default."""
+    r = rng(36)
+    ls = [r.standard_normal((4, 9)) for _ in range(3)]
+    y = r.integers(0, 9, 4)
+    lam = np.array([0.25, 3.0, 0.5])
+    a = oracle.matryoshka_loss(ls, y, 0.3)
+    b = oracle.matryoshka_loss(ls, y, 0.3, exit_weights=lam)
+    np.testing.assert_array_equal(a["loss"], b["loss"])
+    np.testing.assert_allclose(b["total"], (lam[:, None] * a["loss"]).sum(0), rtol=1e-15)
+    ones = oracle.matryoshka_loss(ls, y, 0.3, exit_weights=np.ones(3))
+    np.testing.assert_array_equal(ones["total"], a["total"])

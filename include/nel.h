@@ -66,6 +66,19 @@ enum { NEL_OP_LOSS = 0, NEL_OP_HEADS = 1 };
 
 enum { NEL_MAX_EXITS = 8 };
 
+/* Distillation divergences D(p, q), p = the teacher's softmax, q a smaller
+ * exit's.  NEL_DIV_FORWARD is the method (summary's distillation paragraph;
+ * follow-up 4 of "Is nesting the cheapest way to build a model suite?": 0.3
+ * cross-entropy to the largest model).  The others are the swaps the same
+ * follow-up proposes; its acceptance loss is read as the total variation,
+ * 1 - beta with beta = sum_v min(p_v, q_v) the acceptance probability. */
+typedef enum {
+  NEL_DIV_FORWARD = 0,      /* -sum p log q */
+  NEL_DIV_REVERSE_KL = 1,   /* sum q (log q - log p) */
+  NEL_DIV_JS = 2,           /* (KL(p || m) + KL(q || m)) / 2, m = (p + q) / 2 */
+  NEL_DIV_TV = 3            /* sum |p - q| / 2 */
+} nel_divergence;
+
 /* Junction modes: the method's junction and the two ablations of the paper
  * summary's junction paragraph and the key-visual explainer (200M scale):
  * dropping the norm match, and filling the new channels with zeros. */
@@ -172,29 +185,42 @@ size_t nel_speculative_workspace(int32_t batch, int32_t draft_len);
  * distillation and limitations paragraphs; follow-up 4's 0.7/0.3 mix;
  * main-visual explainer panel (b): distillation only into smaller exits).
  * Exit n_exits-1 is the teacher M; p = softmax(l_M) is under stop-gradient.
- * Per token t and exit m, with l_m = h[m] · w[m]^T (fp32 accumulation):
+ * Per token t and exit m, with l_m = h[m] · w[m]^T (fp32 accumulation) and
+ * q_m = softmax(l_m):
  *     CE_m   = logsumexp(l_m) - l_m[y_t]
- *     Dist_m = logsumexp(l_m) - sum_v p_v l_m,v          (m < M; 0 for M)
+ *     Dist_m = D(p, q_m)                                  (m < M; 0 for M)
+ *              NEL_DIV_FORWARD: logsumexp(l_m) - sum_v p_v l_m,v
  *     L_m    = (1 - alpha_d) CE_m + alpha_d Dist_m       (m < M),  L_M = CE_M
- *     total  = sum_m L_m
+ *     total  = sum_m lambda_m L_m
+ *   exit_weights: NULL (every lambda_m = 1, the summary's equal weights) or a
+ *               host array of n_exits finite values >= 0 (the reweighting
+ *               of the limitations paragraph)
+ *   divergence: a nel_divergence; other than NEL_DIV_FORWARD it needs dlogits
+ *               (its pass reads every exit's stored shifted logits)
  *   token_loss: NULL, or device fp32 [n_exits, 3, n_tokens] = (CE, Dist, L)
  *   mean_loss:  device fp32 [3*n_exits + 1]: mean over tokens of CE_0..CE_{M-1},
  *               then Dist_0.., then L_0.., then the total (fixed-order sums)
  *   dlogits:    NULL (loss only), or host array of n_exits device pointers,
  *               dlogits[e] is [n_tokens, vocab] of type dt, written with
  *               grad_scale * d(sum_t total_t)/d l_e:
- *                 m < M: grad_scale (softmax(l_m) - (1-alpha_d) onehot(y) - alpha_d p)
- *                 M:     grad_scale (p - onehot(y))
+ *                 m < M: grad_scale lambda_m ((1-alpha_d)(q_m - onehot(y)) + alpha_d dD/dl_m)
+ *                        (NEL_DIV_FORWARD: dD/dl_m = q_m - p)
+ *                 M:     grad_scale lambda_M (p - onehot(y))
  *   labels: device int32 [n_tokens]; a label outside [0,vocab) sets
  *           NEL_FLAG_BAD_LABEL in the workspace's first word and NaNs that token.
  *   workspace: device, >= nel_workspace_size(NEL_OP_LOSS, ...) bytes; its
  *           first int32 is the device flag word.
- * No fp32 logit tensor is ever written to memory.
- * Errors: NEL_EINVAL if alpha_d is outside [0,1] or n_exits outside [1,8].
+ * No fp32 logit tensor is ever written to memory.  With NEL_DIV_FORWARD the
+ * distillation term comes from fp32 logits; the other divergences are summed
+ * from the stored shifted logits (bf16 for dt = NEL_BF16).
+ * Errors: NEL_EINVAL if alpha_d is outside [0,1], n_exits outside [1,8], a
+ * weight is negative or not finite, the divergence is unknown, or it needs
+ * dlogits and they are NULL.
  */
 nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
                                const int32_t* d, const void* const* h, const void* const* w,
                                const int32_t* labels, float alpha_d, float grad_scale,
+                               const float* exit_weights, int32_t divergence,
                                float* token_loss, float* mean_loss, void* const* dlogits,
                                void* workspace, size_t ws_bytes, void* stream);
 
@@ -224,15 +250,17 @@ nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* 
  * (NEL_ESHAPE), and dlogits must be given (NEL_EINVAL): between the head GEMM
  * and the final gradient pass the teacher's dlogits buffer holds the
  * teacher's softmax weights exp(l_M - m) (m its 256-entry tile maximum) in
- * fp16, which the smaller exits' tiles read back.  Every dlogits buffer is
+ * fp16, which the smaller exits' tiles read back (with NEL_DIV_FORWARD; the
+ * other divergences store l_M - m in bf16 instead).  Every dlogits buffer is
  * scratch until the call's work on `stream` has completed.
  */
 nel_status nel_matryoshka_loss_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens,
                                       int32_t vocab, const int32_t* d, const void* const* h,
                                       const void* const* w_packed, const int32_t* labels,
-                                      float alpha_d, float grad_scale, float* token_loss,
-                                      float* mean_loss, void* const* dlogits, void* workspace,
-                                      size_t ws_bytes, void* stream);
+                                      float alpha_d, float grad_scale, const float* exit_weights,
+                                      int32_t divergence, float* token_loss, float* mean_loss,
+                                      void* const* dlogits, void* workspace, size_t ws_bytes,
+                                      void* stream);
 
 /*
  * nel_exit_heads with every w[e] in the tiled layout of nel_pack_weights
@@ -331,7 +359,7 @@ enum { NEL_K_JUNCTION = 0, NEL_K_HEADS_LOSS = 1, NEL_K_MERGE = 2, NEL_K_MEANS = 
        NEL_K_FINALIZE = 4, NEL_K_HEADS_ARGMAX = 5, NEL_K_ARGMAX_MERGE = 6,
        NEL_K_ACCEPT = 7, NEL_K_PACK = 8, NEL_K_BWD_PACK = 9, NEL_K_BWD_DH = 10,
        NEL_K_BWD_DW = 11, NEL_K_JUNCTION_BWD = 12, NEL_K_SPECULATIVE = 13,
-       NEL_K_COUNT = 14 };
+       NEL_K_DIVERGENCE = 14, NEL_K_COUNT = 15 };
 nel_status nel_timing_enable(int32_t on);
 /* Synchronises the device, then returns the summed milliseconds and the
  * number of timed launches of `kernel` since the last reset. */

@@ -29,7 +29,8 @@ __all__ = [
     "timing_read", "timing_reset", "KERNELS", "OP_LOSS", "OP_HEADS", "FLAG_BAD_ID",
     "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed", "head_backward",
     "head_backward_workspace_size", "junction_backward", "speculative_verify",
-    "JUNCTION_RESCALE", "JUNCTION_NO_RESCALE", "JUNCTION_ZERO_FILL",
+    "JUNCTION_RESCALE", "JUNCTION_NO_RESCALE", "JUNCTION_ZERO_FILL", "DIV_FORWARD",
+    "DIV_REVERSE_KL", "DIV_JS", "DIV_TV",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,11 +38,13 @@ _LIB = None
 
 F32, BF16 = 0, 1
 JUNCTION_RESCALE, JUNCTION_NO_RESCALE, JUNCTION_ZERO_FILL = 0, 1, 2
+DIV_FORWARD, DIV_REVERSE_KL, DIV_JS, DIV_TV = 0, 1, 2, 3
 OP_LOSS, OP_HEADS = 0, 1
 FLAG_BAD_ID, FLAG_BAD_LABEL = 1, 2
 MAX_EXITS = 8
 KERNELS = ["junction", "heads_loss", "merge", "means", "finalize", "heads_argmax",
-           "argmax_merge", "accept", "pack", "bwd_pack", "bwd_dh", "bwd_dw", "junction_bwd", "speculative"]
+           "argmax_merge", "accept", "pack", "bwd_pack", "bwd_dh", "bwd_dw", "junction_bwd", "speculative",
+           "divergence"]
 
 
 def lib_path() -> str:
@@ -93,9 +96,9 @@ def load():
         "nel_pack_weights": [c_int, c_int, c_int, vp, vp, vp],
         "nel_accept_prefix": [c_int, c_int, c_int, vp, vp, vp, vp],
         "nel_matryoshka_loss": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, ctypes.c_float,
-                                ctypes.c_float, vp, vp, vp, vp, sz, vp],
+                                ctypes.c_float, vp, c_int, vp, vp, vp, vp, sz, vp],
         "nel_matryoshka_loss_packed": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, ctypes.c_float,
-                                       ctypes.c_float, vp, vp, vp, vp, sz, vp],
+                                       ctypes.c_float, vp, c_int, vp, vp, vp, vp, sz, vp],
         "nel_workspace_size": [c_int, c_int, c_i64, c_int],
         "nel_head_backward": [c_int, c_i64, c_int, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
         "nel_head_backward_workspace": [c_i64, c_int, c_int],
@@ -280,27 +283,32 @@ def accept_prefix(draft_argmax, verify_argmax, draft_len: int):
 def matryoshka_loss(hs: Sequence, ws: Sequence, labels, alpha_d: float = 0.3,
                     grad_scale: float = 1.0, want_dlogits: bool = True,
                     want_token_loss: bool = True, dlogits: Optional[List] = None, workspace=None,
-                    mean_loss=None, token_loss=None):
+                    mean_loss=None, token_loss=None, exit_weights: Optional[Sequence[float]] = None,
+                    divergence: int = 0):
     """Losses of every exit and, optionally, dL/dlogits (in hs' dtype).
 
+    exit_weights: per-exit weights of the total (None: all 1); divergence: DIV_FORWARD
+    (the cross-entropy to the teacher), DIV_REVERSE_KL, DIV_JS or DIV_TV (these need
+    the logit gradients).
     Returns (mean_loss [3M+1] fp32, token_loss [M, 3, n] fp32 | None, dlogits list | None);
     mean_loss = (CE_1..CE_M, Dist_1..Dist_M, L_1..L_M, total)."""
     return _loss(False, hs, ws, labels, alpha_d, grad_scale, want_dlogits, want_token_loss,
-                 dlogits, workspace, mean_loss, token_loss)
+                 dlogits, workspace, mean_loss, token_loss, exit_weights, divergence)
 
 
 def matryoshka_loss_packed(hs: Sequence, ws_packed: Sequence, labels, alpha_d: float = 0.3,
                            grad_scale: float = 1.0, want_token_loss: bool = True,
                            dlogits: Optional[List] = None, workspace=None, mean_loss=None,
-                           token_loss=None):
+                           token_loss=None, exit_weights: Optional[Sequence[float]] = None,
+                           divergence: int = 0):
     """matryoshka_loss on head weights from pack_weights (bf16, V % 32 == 0, every
     d % 64 == 0); the logit gradients are always produced."""
     return _loss(True, hs, ws_packed, labels, alpha_d, grad_scale, True, want_token_loss,
-                 dlogits, workspace, mean_loss, token_loss)
+                 dlogits, workspace, mean_loss, token_loss, exit_weights, divergence)
 
 
 def _loss(packed, hs, ws, labels, alpha_d, grad_scale, want_dlogits, want_token_loss, dlogits,
-          workspace, mean_loss, token_loss):
+          workspace, mean_loss, token_loss, exit_weights=None, divergence=0):
     torch = _torch()
     E = len(hs)
     if E != len(ws) or not 1 <= E <= MAX_EXITS:
@@ -331,8 +339,14 @@ def _loss(packed, hs, ws, labels, alpha_d, grad_scale, want_dlogits, want_token_
     lib = load()
     fn, name = ((lib.nel_matryoshka_loss_packed, "nel_matryoshka_loss_packed") if packed
                 else (lib.nel_matryoshka_loss, "nel_matryoshka_loss"))
+    lam = None
+    if exit_weights is not None:
+        if len(exit_weights) != E:
+            raise ValueError("exit_weights needs one weight per exit")
+        lam = (ctypes.c_float * E)(*[float(x) for x in exit_weights])
     _check(fn(dt, E, n, V, d, _ptrs(hs), _ptrs(ws), _dev(labels, device, "labels"),
-              float(alpha_d), float(grad_scale), _dev(token_loss, device, "token_loss"),
+              float(alpha_d), float(grad_scale), lam, int(divergence),
+              _dev(token_loss, device, "token_loss"),
               _dev(mean_loss, device, "mean_loss"),
               _ptrs(dlogits) if dlogits is not None else None, wsb.data_ptr(), wsb.numel(),
               _stream(device)), name)

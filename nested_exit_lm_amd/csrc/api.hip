@@ -208,7 +208,8 @@ nel_status exit_heads_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n
 
 nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
                      const int32_t* d, const void* const* h, const void* const* w,
-                     const int32_t* labels, float alpha_d, float grad_scale, float* token_loss,
+                     const int32_t* labels, float alpha_d, float grad_scale,
+                     const float* exit_weights, int32_t div, float* token_loss,
                      float* mean_loss, void* const* dlogits, void* workspace, size_t ws_bytes,
                      void* stream) {
   if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
@@ -222,6 +223,15 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
     if (!dlogits) return NEL_EINVAL;   // the teacher's buffer carries its weights
   }
   if (!(alpha_d >= 0.f && alpha_d <= 1.f) || !isfinite(grad_scale)) return NEL_EINVAL;
+  if (div < NEL_DIV_FORWARD || div > NEL_DIV_TV) return NEL_EINVAL;
+  if (div != NEL_DIV_FORWARD && !dlogits) return NEL_EINVAL;   // its pass reads the stored logits
+  ExitW lam;
+  for (int e = 0; e < kMaxExits; ++e) lam.w[e] = 1.f;
+  if (exit_weights)
+    for (int e = 0; e < n_exits; ++e) {
+      if (!(exit_weights[e] >= 0.f) || !isfinite(exit_weights[e])) return NEL_EINVAL;
+      lam.w[e] = exit_weights[e];
+    }
   if (!grid_fits(n_tokens, vocab)) return NEL_ESHAPE;
   if (!mean_loss || (n_tokens > 0 && !labels)) return NEL_EINVAL;
   if (dlogits)
@@ -251,9 +261,11 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
     ex.d[e] = d[e];
   }
   TileInfo info;
+  const bool fwd = div == NEL_DIV_FORWARD;
   hipError_t err = timed(NEL_K_HEADS_LOSS, s, [&] {
     if (packed)
-      return launch_heads_loss_packed(n_exits, n_tokens, vocab, ex, labels, stats, lab, &info, s);
+      return launch_heads_loss_packed(n_exits, n_tokens, vocab, ex, labels, stats, lab, fwd, &info,
+                                      s);
     return dt == NEL_BF16 ? launch_heads_loss<bf16_t>(n_exits, n_tokens, vocab, ex, labels, stats,
                                                       lab, &info, s)
                           : launch_heads_loss<float>(n_exits, n_tokens, vocab, ex, labels, stats,
@@ -262,9 +274,21 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
   if (err != hipSuccess) return from_hip(err);
   err = timed(NEL_K_MERGE, s, [&] {
     return launch_loss_merge(n_exits, n_tokens, vocab, info.vtile, labels, alpha_d, stats, lab, lse, tl,
-                             partials, flags, s);
+                             partials, flags, lam, !fwd, s);
   });
   if (err != hipSuccess) return from_hip(err);
+  float* dv = reinterpret_cast<float*>(ws + L.dv);
+  float* kv = reinterpret_cast<float*>(ws + L.kv);
+  if (!fwd) {
+    err = timed(NEL_K_DIVERGENCE, s, [&] {
+      return dt == NEL_BF16
+                 ? launch_divergence<bf16_t>(n_exits, n_tokens, vocab, info, div, alpha_d, stats,
+                                             lse, dlogits, dv, kv, tl, partials, lam, s)
+                 : launch_divergence<float>(n_exits, n_tokens, vocab, info, div, alpha_d, stats,
+                                            lse, dlogits, dv, kv, tl, partials, lam, s);
+    });
+    if (err != hipSuccess) return from_hip(err);
+  }
   err = timed(NEL_K_MEANS, s, [&] {
     return launch_loss_means(n_exits, n_tokens, partials, mean_loss, s);
   });
@@ -272,9 +296,11 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
   if (dlogits && n_tokens > 0) {
     err = timed(NEL_K_FINALIZE, s, [&] {
       return dt == NEL_BF16 ? launch_finalize<bf16_t>(n_exits, n_tokens, vocab, info, labels,
-                                                      alpha_d, grad_scale, stats, lse, dlogits, s)
+                                                      alpha_d, grad_scale, stats, lse, dlogits,
+                                                      div, kv, lam, s)
                             : launch_finalize<float>(n_exits, n_tokens, vocab, info, labels,
-                                                     alpha_d, grad_scale, stats, lse, dlogits, s);
+                                                     alpha_d, grad_scale, stats, lse, dlogits,
+                                                     div, kv, lam, s);
     });
   }
   return from_hip(err);
@@ -303,20 +329,24 @@ nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens
 nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
                                const int32_t* d, const void* const* h, const void* const* w,
                                const int32_t* labels, float alpha_d, float grad_scale,
+                               const float* exit_weights, int32_t divergence,
                                float* token_loss, float* mean_loss, void* const* dlogits,
                                void* workspace, size_t ws_bytes, void* stream) {
   return loss_impl(false, dt, n_exits, n_tokens, vocab, d, h, w, labels, alpha_d, grad_scale,
-                   token_loss, mean_loss, dlogits, workspace, ws_bytes, stream);
+                   exit_weights, divergence, token_loss, mean_loss, dlogits, workspace, ws_bytes,
+                   stream);
 }
 
 nel_status nel_matryoshka_loss_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens,
                                       int32_t vocab, const int32_t* d, const void* const* h,
                                       const void* const* w_packed, const int32_t* labels,
-                                      float alpha_d, float grad_scale, float* token_loss,
-                                      float* mean_loss, void* const* dlogits, void* workspace,
-                                      size_t ws_bytes, void* stream) {
+                                      float alpha_d, float grad_scale, const float* exit_weights,
+                                      int32_t divergence, float* token_loss, float* mean_loss,
+                                      void* const* dlogits, void* workspace, size_t ws_bytes,
+                                      void* stream) {
   return loss_impl(true, dt, n_exits, n_tokens, vocab, d, h, w_packed, labels, alpha_d,
-                   grad_scale, token_loss, mean_loss, dlogits, workspace, ws_bytes, stream);
+                   grad_scale, exit_weights, divergence, token_loss, mean_loss, dlogits,
+                   workspace, ws_bytes, stream);
 }
 
 nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* w, void* w_packed,

@@ -28,7 +28,9 @@
 // buffer as fp16 (relative rounding 2^-11), where the smaller exits' epilogues
 // of the same workgroup read them back, lane for lane, to form
 // S = sum_v w_v l_m,v; the smaller exits store l - m in bf16.  The finalize
-// pass turns both into gradients in place.
+// pass turns both into gradients in place.  kModeLossPlain (divergences other
+// than the cross-entropy to the teacher, whose passes read every exit's l - m)
+// stores l - m in bf16 for every exit and forms no S.
 #include <limits.h>
 
 #include "common.h"
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
   int ylab[NTB];
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb)
-    ylab[tb] = (MODE == kModeLoss && tq + tb * 32 < n) ? labels[tq + tb * 32] : -1;
+    ylab[tb] = (MODE != kModeArgmax && tq + tb * 32 < n) ? labels[tq + tb * 32] : -1;
   const int vlane = vw + 16 * hl;   // first of this lane's 16 consecutive entries in block 0
   // W row block of the loads for block 0 and block 1, clamped: rows beyond V are never stored
   const int rb0 = min(vw >> 5, vocab / 32 - 1), rb1 = min((vw >> 5) + 1, vocab / 32 - 1);
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
     }
 
     const int64_t plane = static_cast<int64_t>(n_vt) * n;
-    if constexpr (MODE == kModeLoss) {
+    if constexpr (MODE != kModeArgmax) {
       // (1) row maximum over the tile's 256 entries: registers, lane 32 apart, 4 wavefronts
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
             }
           } else {
             u32x4 wv[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-            if (ok) {
+            if (MODE == kModeLoss && ok) {
               const u32x4* src = reinterpret_cast<const u32x4*>(TW + off);
               wv[0] = src[0];
               wv[1] = src[1];
@@ -205,9 +207,11 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
               const float a0 = acc[tb][vb][r], a1 = acc[tb][vb][r + 1];
               s0 += __builtin_amdgcn_exp2f(fmaf(a0, kLog2e, -ml));
               s1 += __builtin_amdgcn_exp2f(fmaf(a1, kLog2e, -ml));
-              const uint32_t wp2 = wv[r >> 3][(r >> 1) & 3];
-              S0 = fmaf(f16_lo(wp2), a0, S0);
-              S1 = fmaf(f16_hi(wp2), a1, S1);
+              if constexpr (MODE == kModeLoss) {
+                const uint32_t wp2 = wv[r >> 3][(r >> 1) & 3];
+                S0 = fmaf(f16_lo(wp2), a0, S0);
+                S1 = fmaf(f16_hi(wp2), a1, S1);
+              }
               pk[r >> 3][(r >> 1) & 3] = pack_bf16x2(a0 - M[tb], a1 - M[tb]);
             }
             if (ok) {
@@ -243,7 +247,8 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
         float* st = stats + (static_cast<int64_t>(e) * 3 * n_vt + vt) * n + tk;
         st[0] = Mw;
         st[plane] = (xsum[0][j][0] + xsum[1][j][0]) + (xsum[2][j][0] + xsum[3][j][0]);
-        if (!teacher) st[2 * plane] = (xsum[0][j][1] + xsum[1][j][1]) + (xsum[2][j][1] + xsum[3][j][1]);
+        if (MODE == kModeLoss && !teacher)
+          st[2 * plane] = (xsum[0][j][1] + xsum[1][j][1]) + (xsum[2][j][1] + xsum[3][j][1]);
       }
     } else {
       // per token the tile's (max, lowest index); optional fp32 logits
@@ -337,7 +342,9 @@ hipError_t launch_pack_weights(int vocab, int d, const void* w, void* packed, hi
 
 hipError_t launch_heads_loss_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
                                     const int32_t* labels, float* stats, float* lab,
-                                    TileInfo* info, hipStream_t s) {
+                                    bool dist_stats, TileInfo* info, hipStream_t s) {
+  if (!dist_stats)
+    return launch_packed<kModeLossPlain>(n_exits, n, vocab, ex, labels, stats, lab, info, s);
   return launch_packed<kModeLoss>(n_exits, n, vocab, ex, labels, stats, lab, info, s);
 }
 

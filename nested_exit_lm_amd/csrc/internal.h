@@ -10,6 +10,14 @@ namespace nel {
 constexpr int kJunctionRescale = 0, kJunctionNoRescale = 1, kJunctionZeroFill = 2;
 
 constexpr int kMaxExits = 8;
+
+// Distillation divergences (values of nel_divergence).
+constexpr int kDivForward = 0, kDivReverseKL = 1, kDivJS = 2, kDivTV = 3;
+
+// Per-exit loss weights, passed to kernels by value.
+struct ExitW {
+  float w[kMaxExits];
+};
 // Smallest token and vocabulary extent of a head-GEMM workgroup tile.  Loss
 // statistics are kept per (exit, vocabulary tile, token); the GEMM reports
 // the vocabulary tile it used and the workspace is sized for the smallest.
@@ -39,9 +47,10 @@ inline int64_t n_vocab_tiles(int vocab) { return (vocab + kVocTile - 1) / kVocTi
 constexpr int kMergeTok = 64;
 inline int64_t n_merge_blocks(int64_t n) { return (n + kMergeTok - 1) / kMergeTok; }
 
-// Workspace layout of the loss op (byte offsets from the base).
+// Workspace layout of the loss op (byte offsets from the base); dv and kv
+// hold a divergence's value and gradient row constant per (exit, token).
 struct LossWs {
-  size_t flags, stats, lab, lse, tokloss, partials, total;
+  size_t flags, stats, lab, lse, tokloss, partials, dv, kv, total;
 };
 inline LossWs loss_ws_layout(int n_exits, int64_t n, int vocab) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -53,7 +62,9 @@ inline LossWs loss_ws_layout(int n_exits, int64_t n, int vocab) {
   L.lse = L.lab + up(sizeof(float) * n_exits * n);
   L.tokloss = L.lse + up(sizeof(float) * n_exits * n);
   L.partials = L.tokloss + up(sizeof(float) * n_exits * 3 * n);
-  L.total = L.partials + up(sizeof(double) * (3 * n_exits + 1) * n_merge_blocks(n));
+  L.dv = L.partials + up(sizeof(double) * (3 * n_exits + 1) * n_merge_blocks(n));
+  L.kv = L.dv + up(sizeof(float) * n_exits * n);
+  L.total = L.kv + up(sizeof(float) * n_exits * n);
   return L;
 }
 struct HeadsWs {
@@ -134,22 +145,32 @@ hipError_t launch_heads_argmax(int n_exits, int64_t n, int vocab, const ExitSet&
 // The loss GEMM needs every ex.out[e] (the teacher's holds its weights).
 bool packed_shape_ok(int vocab, int d);
 hipError_t launch_pack_weights(int vocab, int d, const void* w, void* packed, hipStream_t s);
+// dist_stats: the teacher's weights and the teacher-weighted sums for the
+// cross-entropy to the teacher; without them every exit stores l - m in bf16.
 hipError_t launch_heads_loss_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
                                     const int32_t* labels, float* stats, float* lab,
-                                    TileInfo* info, hipStream_t s);
+                                    bool dist_stats, TileInfo* info, hipStream_t s);
 hipError_t launch_heads_argmax_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
                                       float* best, TileInfo* info, hipStream_t s);
 
 hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
                              float alpha, const float* stats, const float* lab, float* lse,
-                             float* tokloss, double* partials, int32_t* flags, hipStream_t s);
+                             float* tokloss, double* partials, int32_t* flags, const ExitW& lam,
+                             bool skip_dist, hipStream_t s);
+// Divergence D (not the forward cross-entropy) per student and token, then
+// the losses and mean partials with it (after launch_loss_merge with skip_dist).
+template <typename T>
+hipError_t launch_divergence(int n_exits, int64_t n, int vocab, const TileInfo& info, int div,
+                             float alpha, const float* stats, const float* lse,
+                             void* const* dlogits, float* dv, float* kv, float* tokloss,
+                             double* partials, const ExitW& lam, hipStream_t s);
 hipError_t launch_loss_means(int n_exits, int64_t n, const double* partials, float* means,
                              hipStream_t s);
 template <typename T>
 hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const TileInfo& info,
-                           const int32_t* labels,
-                           float alpha, float grad_scale, const float* stats, const float* lse,
-                           void* const* dlogits, hipStream_t s);
+                           const int32_t* labels, float alpha, float grad_scale,
+                           const float* stats, const float* lse, void* const* dlogits, int div,
+                           const float* kv, const ExitW& lam, hipStream_t s);
 hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, int vtile, const float* best,
                                int32_t* argmax, hipStream_t s);
 hipError_t launch_accept(int batch, int positions, int draft_len, const int32_t* draft,

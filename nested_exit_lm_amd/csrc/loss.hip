@@ -13,6 +13,15 @@
 // logits s = l - m_tile the GEMM left in the caller's buffers:
 //     m < M: gs (exp(s_m + m_m,tile - LSE_m) - a p - (1 - a) [v = y])
 //     M:     gs (p - [v = y]),   p = exp(s_M + m_M,tile - LSE_M)
+// Exit weights lambda (limitations paragraph: reweighting the per-exit
+// losses) scale exit m's gradient and its share of the total.
+// Other divergences D(p, q) in place of the cross-entropy to the teacher
+// (follow-up 4: reverse KL, Jensen-Shannon, an acceptance loss read as the
+// total variation 1 - sum min(p, q)) need p and q per entry after the row's
+// LSE is known: div_stats_kernel reads the stored s of the teacher and each
+// student and reduces D and the gradient's row constant K = sum_v q_v r_v,
+// r = dD/dq; the student gradient is then
+//     gs lambda_m ((1 - a)(q - [v = y]) + a q (r - K)).
 #include <limits.h>
 
 #include "common.h"
@@ -42,7 +51,8 @@ __global__ __launch_bounds__(256) void loss_merge_kernel(int M, int64_t n, int v
                                                          float* __restrict__ lse_out,
                                                          float* __restrict__ tokloss,
                                                          double* __restrict__ partials,
-                                                         int32_t* __restrict__ flags, int n_vt) {
+                                                         int32_t* __restrict__ flags, int n_vt,
+                                                         ExitW lam, int skip_dist) {
   __shared__ float sh[4][64][2];
   const int tl = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeTok + tl;
@@ -72,7 +82,7 @@ __global__ __launch_bounds__(256) void loss_merge_kernel(int M, int64_t n, int v
     const float L = Mx + flog(Sx);
     if (ei == 0) lseT = L;
     float dist = 0.f;
-    if (ei > 0) {
+    if (ei > 0 && !skip_dist) {   // (otherwise div_finish_kernel supplies Dist)
       float a = 0.f;
       if (valid)
         for (int vt = g; vt < n_vt; vt += 4)
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(256) void loss_merge_kernel(int M, int64_t n, int v
       const double sce = wave_sum_f64(valid ? static_cast<double>(ce) : 0.0);
       const double sdi = wave_sum_f64(valid ? static_cast<double>(dist) : 0.0);
       const double slm = wave_sum_f64(valid ? static_cast<double>(lm) : 0.0);
-      total += valid ? static_cast<double>(lm) : 0.0;
+      total += valid ? static_cast<double>(lam.w[e]) * lm : 0.0;
       if (tl == 0) {
         part[e] = sce;
         part[M + e] = sdi;
@@ -135,21 +145,183 @@ __global__ __launch_bounds__(256) void loss_means_kernel(int M, int64_t n, int64
   }
 }
 
-// ---------------------------------------------------------------- finalize
+// ---------------------------------------------------------------- divergences
+// The exits' gradient buffers (dlogits), by value.
 struct DlPtrs {
   void* p[kMaxExits];
 };
+
+// Per entry of one token row, given the teacher's and a student's log-probs
+// (lp, lq) and probabilities (p, q): the divergence term d and q_v r_v.
+template <int DIV>
+__device__ __forceinline__ void div_terms(float lp, float lq, float p, float q, float& d,
+                                          float& qr) {
+  if constexpr (DIV == kDivReverseKL) {
+    d = q * (lq - lp);   // r = log q - log p (+ 1, which K cancels)
+    qr = d;
+  } else if constexpr (DIV == kDivJS) {
+    // log m = log((p + q) / 2) from the log-probs, stable where p or q underflows
+    const float hi = fmaxf(lp, lq), lo = fminf(lp, lq);
+    const float lm = hi + flog(1.f + fexp(lo - hi)) - kLn2;
+    d = 0.5f * (p * (lp - lm) + q * (lq - lm));
+    qr = 0.5f * q * (lq - lm);
+  } else {   // kDivTV
+    d = 0.5f * fabsf(p - q);
+    qr = q > p ? 0.5f * q : (q < p ? -0.5f * q : 0.f);
+  }
+}
+
+template <int DIV>
+__device__ __forceinline__ float div_r(float lp, float lq, float p, float q) {
+  if constexpr (DIV == kDivReverseKL) {
+    return lq - lp;
+  } else if constexpr (DIV == kDivJS) {
+    const float hi = fmaxf(lp, lq), lo = fminf(lp, lq);
+    return 0.5f * (lq - (hi + flog(1.f + fexp(lo - hi)) - kLn2));
+  } else {
+    return q > p ? 0.5f : (q < p ? -0.5f : 0.f);
+  }
+}
+
+__device__ __forceinline__ float elem_f32(const u32x4& r, int i, bf16_t) {
+  return __uint_as_float((i & 1) ? (r[i >> 1] & 0xffff0000u) : (r[i >> 1] << 16));
+}
+__device__ __forceinline__ float elem_f32(const u32x4& r, int i, float) {
+  return __uint_as_float(r[i]);
+}
+
+// One workgroup per token row (grid-stride): for every student e < M - 1,
+// dv[e][t] = D(p, q_e) and kv[e][t] = K, each a per-thread fp32 sum in
+// vocabulary order combined in a fixed tree.  The stored s are read, not
+// modified (the teacher's as shifted logits: never the fp16 weight form).
+template <typename T, int DIV>
+__global__ __launch_bounds__(256) void div_stats_kernel(int M, int64_t n, int vocab, int vtile,
+                                                        const float* __restrict__ stats,
+                                                        const float* __restrict__ lse, DlPtrs dl,
+                                                        int n_vt, float* __restrict__ dv,
+                                                        float* __restrict__ kv) {
+  constexpr int C = Elem<T>::kChunk;
+  __shared__ float red[4][2 * (kMaxExits - 1)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t plane = static_cast<int64_t>(n_vt) * n;
+  const int S = M - 1;
+  for (int64_t t = blockIdx.x; t < n; t += gridDim.x) {
+    float D[kMaxExits - 1], K[kMaxExits - 1];
+#pragma unroll
+    for (int e = 0; e < kMaxExits - 1; ++e) D[e] = K[e] = 0.f;
+    auto off = [&](int e, int tile) {
+      return stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
+             lse[static_cast<int64_t>(e) * n + t];
+    };
+    if (vocab % C == 0) {
+      const int64_t cpr = vocab / C;
+      for (int64_t c = tid; c < cpr; c += 256) {
+        const int tile = static_cast<int>(c * C) / vtile;
+        const u32x4 tr = reinterpret_cast<const u32x4*>(static_cast<const T*>(dl.p[M - 1]) + t * vocab)[c];
+        const float oT = off(M - 1, tile);
+        float lp[C], p[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          lp[i] = elem_f32(tr, i, T{}) + oT;
+          p[i] = fexp(lp[i]);
+        }
+#pragma unroll
+        for (int e = 0; e < kMaxExits - 1; ++e) {
+          if (e >= S) break;
+          const u32x4 sr = reinterpret_cast<const u32x4*>(static_cast<const T*>(dl.p[e]) + t * vocab)[c];
+          const float oe = off(e, tile);
+#pragma unroll
+          for (int i = 0; i < C; ++i) {
+            const float lq = elem_f32(sr, i, T{}) + oe;
+            float d, qr;
+            div_terms<DIV>(lp[i], lq, p[i], fexp(lq), d, qr);
+            D[e] += d;
+            K[e] += qr;
+          }
+        }
+      }
+    } else {
+      for (int v = tid; v < vocab; v += 256) {
+        const int tile = v / vtile;
+        const float lp = Elem<T>::to_f32(static_cast<const T*>(dl.p[M - 1])[t * vocab + v]) + off(M - 1, tile);
+        const float p = fexp(lp);
+        for (int e = 0; e < S; ++e) {
+          const float lq = Elem<T>::to_f32(static_cast<const T*>(dl.p[e])[t * vocab + v]) + off(e, tile);
+          float d, qr;
+          div_terms<DIV>(lp, lq, p, fexp(lq), d, qr);
+          D[e] += d;
+          K[e] += qr;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kMaxExits - 1; ++e) {
+      if (e >= S) break;
+      const float a = wave_sum(D[e]), b = wave_sum(K[e]);
+      if (lane == 0) {
+        red[wave][2 * e] = a;
+        red[wave][2 * e + 1] = b;
+      }
+    }
+    __syncthreads();
+    if (tid < 2 * S) {
+      const float x = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+      ((tid & 1) ? kv : dv)[static_cast<int64_t>(tid >> 1) * n + t] = x;
+    }
+    __syncthreads();   // red is reused by the next row
+  }
+}
+
+// Losses and mean partials once D is known (the merge's tail with Dist from
+// dv): one wavefront per kMergeTok tokens, the same partial layout and order.
+__global__ __launch_bounds__(64) void div_finish_kernel(int M, int64_t n, float alpha,
+                                                        const float* __restrict__ dv,
+                                                        float* __restrict__ tokloss,
+                                                        double* __restrict__ partials, ExitW lam) {
+  const int tl = threadIdx.x;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeTok + tl;
+  const bool valid = t < n;
+  double* part = partials + static_cast<int64_t>(blockIdx.x) * (3 * M + 1);
+  double total = 0.0;
+  for (int ei = 0; ei < M; ++ei) {
+    const int e = ei == 0 ? M - 1 : ei - 1;
+    float ce = 0.f, dist = 0.f, lm = 0.f;
+    if (valid) {
+      ce = tokloss[(static_cast<int64_t>(e) * 3 + 0) * n + t];
+      dist = ei == 0 ? 0.f : dv[static_cast<int64_t>(e) * n + t];
+      if (ce != ce) dist = ce;   // a bad label (NaN) stays NaN
+      lm = ei == 0 ? ce : (1.f - alpha) * ce + alpha * dist;
+      tokloss[(static_cast<int64_t>(e) * 3 + 1) * n + t] = dist;
+      tokloss[(static_cast<int64_t>(e) * 3 + 2) * n + t] = lm;
+    }
+    const double sce = wave_sum_f64(valid ? static_cast<double>(ce) : 0.0);
+    const double sdi = wave_sum_f64(valid ? static_cast<double>(dist) : 0.0);
+    const double slm = wave_sum_f64(valid ? static_cast<double>(lm) : 0.0);
+    total += valid ? static_cast<double>(lam.w[e]) * lm : 0.0;
+    if (tl == 0) {
+      part[e] = sce;
+      part[M + e] = sdi;
+      part[2 * M + e] = slm;
+    }
+  }
+  const double st = wave_sum_f64(total);
+  if (tl == 0) part[3 * M] = st;
+}
+
+// ---------------------------------------------------------------- finalize
 
 // 16-byte chunk path (vocab a multiple of the chunk).  Each workgroup
 // iteration covers 256 consecutive chunks of one token row for all exits.
 // TW16: the teacher's buffer holds fp16 weights w = exp(l_M - m) of its tile
 // (so p = w exp(m - lse)) instead of the shifted logits l_M - m.
-template <typename T, bool TW16>
+template <typename T, bool TW16, int DIV>
 __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab, int vtile,
                                                     const int32_t* __restrict__ labels, float alpha,
                                                     float gs, const float* __restrict__ stats,
                                                     const float* __restrict__ lse, DlPtrs dl,
-                                                    int n_vt, int segs_per_row) {
+                                                    int n_vt, int segs_per_row,
+                                                    const float* __restrict__ kv, ExitW lam) {
+  static_assert(!TW16 || DIV == kDivForward, "divergences read the teacher's shifted logits");
   constexpr int C = Elem<T>::kChunk;
   const int64_t plane = static_cast<int64_t>(n_vt) * n;
   const int64_t cpr = vocab / C;
@@ -171,7 +343,7 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
     // a compile-time constant (no indexing of raw[] by the run-time M - 1).
     const u32x4 traw = __builtin_nontemporal_load(
         reinterpret_cast<const u32x4*>(static_cast<const T*>(dl.p[M - 1]) + t * vocab) + c);
-    float p[C];
+    float p[C], lp[C];
     {
       const int e = M - 1;
       const float off = stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
@@ -196,7 +368,8 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
             s = __uint_as_float((i & 1) ? (traw[i >> 1] & 0xffff0000u) : (traw[i >> 1] << 16));
           else
             s = __uint_as_float(traw[i]);
-          p[i] = fexp(s + off);
+          lp[i] = s + off;
+          p[i] = fexp(lp[i]);
         }
       }
     }
@@ -207,6 +380,10 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
       const float off = stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
                         lse[static_cast<int64_t>(e) * n + t];
       const float hot = teacher ? 1.f : 1.f - alpha;
+      const float ge = gs * lam.w[e];
+      float kc = 0.f;
+      if constexpr (DIV != kDivForward)
+        if (!teacher) kc = kv[static_cast<int64_t>(e) * n + t];
       float g[C];
 #pragma unroll
       for (int i = 0; i < C; ++i) {
@@ -219,10 +396,15 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
             s = __uint_as_float((i & 1) ? (raw[e][i >> 1] & 0xffff0000u) : (raw[e][i >> 1] << 16));
           else
             s = __uint_as_float(raw[e][i]);
-          val = fexp(s + off) - alpha * p[i];
+          const float lq = s + off;
+          const float q = fexp(lq);
+          if constexpr (DIV == kDivForward)
+            val = q - alpha * p[i];
+          else
+            val = (1.f - alpha) * q + alpha * q * (div_r<DIV>(lp[i], lq, p[i], q) - kc);
         }
         if (v0 + i == y) val -= hot;
-        g[i] = bad ? __builtin_nanf("") : gs * val;
+        g[i] = bad ? __builtin_nanf("") : ge * val;
       }
       u32x4 o;
       if constexpr (sizeof(T) == 2) {
@@ -238,13 +420,14 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
 }
 
 // Element path for any vocabulary size.
-template <typename T>
+template <typename T, int DIV>
 __global__ __launch_bounds__(256) void finalize_elem(int M, int64_t n, int vocab, int vtile,
                                                      const int32_t* __restrict__ labels,
                                                      float alpha, float gs,
                                                      const float* __restrict__ stats,
                                                      const float* __restrict__ lse, DlPtrs dl,
-                                                     int n_vt) {
+                                                     int n_vt, const float* __restrict__ kv,
+                                                     ExitW lam) {
   const int64_t plane = static_cast<int64_t>(n_vt) * n;
   const int64_t total = n * vocab;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
@@ -256,21 +439,28 @@ __global__ __launch_bounds__(256) void finalize_elem(int M, int64_t n, int vocab
     const bool bad = y < 0 || y >= vocab;
     const int eT = M - 1;
     T* pt = static_cast<T*>(dl.p[eT]) + i;
-    const float p = fexp(Elem<T>::to_f32(*pt) +
-                         stats[static_cast<int64_t>(eT) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
-                         lse[static_cast<int64_t>(eT) * n + t]);
+    const float lp = Elem<T>::to_f32(*pt) +
+                     stats[static_cast<int64_t>(eT) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
+                     lse[static_cast<int64_t>(eT) * n + t];
+    const float p = fexp(lp);
     for (int e = 0; e < M; ++e) {
       T* pe = static_cast<T*>(dl.p[e]) + i;
       float val;
       if (e == eT) {
         val = p - (v == y ? 1.f : 0.f);
       } else {
-        const float q = fexp(Elem<T>::to_f32(*pe) +
-                             stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
-                             lse[static_cast<int64_t>(e) * n + t]);
-        val = q - alpha * p - (v == y ? 1.f - alpha : 0.f);
+        const float lq = Elem<T>::to_f32(*pe) +
+                         stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
+                         lse[static_cast<int64_t>(e) * n + t];
+        const float q = fexp(lq);
+        if constexpr (DIV == kDivForward)
+          val = q - alpha * p;
+        else
+          val = (1.f - alpha) * q +
+                alpha * q * (div_r<DIV>(lp, lq, p, q) - kv[static_cast<int64_t>(e) * n + t]);
+        if (v == y) val -= 1.f - alpha;
       }
-      *pe = Elem<T>::from_f32(bad ? __builtin_nanf("") : gs * val);
+      *pe = Elem<T>::from_f32(bad ? __builtin_nanf("") : gs * lam.w[e] * val);
     }
   }
 }
@@ -315,13 +505,55 @@ __global__ void clear_flags_kernel(int32_t* f) { *f = 0; }
 
 hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const int32_t* labels,
                              float alpha, const float* stats, const float* lab, float* lse,
-                             float* tokloss, double* partials, int32_t* flags, hipStream_t s) {
+                             float* tokloss, double* partials, int32_t* flags, const ExitW& lam,
+                             bool skip_dist, hipStream_t s) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(loss_merge_kernel, dim3(static_cast<unsigned>(n_merge_blocks(n))), dim3(256), 0,
                      s, n_exits, n, vocab, labels, alpha, stats, lab, lse, tokloss, partials, flags,
-                     (vocab + vtile - 1) / vtile);
+                     (vocab + vtile - 1) / vtile, lam, skip_dist ? 1 : 0);
   return hipGetLastError();
 }
+
+template <typename T>
+hipError_t launch_divergence(int n_exits, int64_t n, int vocab, const TileInfo& info, int div,
+                             float alpha, const float* stats, const float* lse,
+                             void* const* dlogits, float* dv, float* kv, float* tokloss,
+                             double* partials, const ExitW& lam, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (info.teacher_w16) return hipErrorInvalidValue;   // needs the teacher's shifted logits
+  DlPtrs dl{};
+  for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
+  const int n_vt = (vocab + info.vtile - 1) / info.vtile;
+  if (n_exits > 1) {
+    const unsigned grid = static_cast<unsigned>(n < 256 * 16 ? n : 256 * 16);
+    switch (div) {
+      case kDivReverseKL:
+        hipLaunchKernelGGL((div_stats_kernel<T, kDivReverseKL>), dim3(grid), dim3(256), 0, s,
+                           n_exits, n, vocab, info.vtile, stats, lse, dl, n_vt, dv, kv);
+        break;
+      case kDivJS:
+        hipLaunchKernelGGL((div_stats_kernel<T, kDivJS>), dim3(grid), dim3(256), 0, s, n_exits, n,
+                           vocab, info.vtile, stats, lse, dl, n_vt, dv, kv);
+        break;
+      case kDivTV:
+        hipLaunchKernelGGL((div_stats_kernel<T, kDivTV>), dim3(grid), dim3(256), 0, s, n_exits, n,
+                           vocab, info.vtile, stats, lse, dl, n_vt, dv, kv);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
+  hipLaunchKernelGGL(div_finish_kernel, dim3(static_cast<unsigned>(n_merge_blocks(n))), dim3(64), 0,
+                     s, n_exits, n, alpha, dv, tokloss, partials, lam);
+  return hipGetLastError();
+}
+
+template hipError_t launch_divergence<bf16_t>(int, int64_t, int, const TileInfo&, int, float,
+                                              const float*, const float*, void* const*, float*,
+                                              float*, float*, double*, const ExitW&, hipStream_t);
+template hipError_t launch_divergence<float>(int, int64_t, int, const TileInfo&, int, float,
+                                             const float*, const float*, void* const*, float*,
+                                             float*, float*, double*, const ExitW&, hipStream_t);
 
 hipError_t launch_loss_means(int n_exits, int64_t n, const double* partials, float* means,
                              hipStream_t s) {
@@ -330,45 +562,80 @@ hipError_t launch_loss_means(int n_exits, int64_t n, const double* partials, flo
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const TileInfo& info,
-                           const int32_t* labels, float alpha, float grad_scale,
-                           const float* stats, const float* lse, void* const* dlogits,
-                           hipStream_t s) {
-  if (n == 0) return hipSuccess;
+template <typename T, int DIV>
+static void finalize_div(int n_exits, int64_t n, int vocab, const TileInfo& info,
+                         const int32_t* labels, float alpha, float grad_scale, const float* stats,
+                         const float* lse, const DlPtrs& dl, const float* kv, const ExitW& lam,
+                         hipStream_t s) {
   constexpr int C = Elem<T>::kChunk;
   const int vtile = info.vtile;
-  DlPtrs dl{};
-  for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
   const int n_vt = (vocab + vtile - 1) / vtile;
   if (vocab % C == 0) {
     const int64_t cpr = vocab / C;
     const int segs = static_cast<int>((cpr + 255) / 256);
     const int64_t nseg = n * segs;
     const unsigned grid = static_cast<unsigned>(nseg < 256 * 16 ? nseg : 256 * 16);
-    if (info.teacher_w16)
-      hipLaunchKernelGGL((finalize_vec<T, true>), dim3(grid), dim3(256), 0, s, n_exits, n, vocab,
-                         vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, segs);
-    else
-      hipLaunchKernelGGL((finalize_vec<T, false>), dim3(grid), dim3(256), 0, s, n_exits, n, vocab,
-                         vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, segs);
+    if constexpr (DIV == kDivForward) {
+      if (info.teacher_w16) {
+        hipLaunchKernelGGL((finalize_vec<T, true, DIV>), dim3(grid), dim3(256), 0, s, n_exits, n,
+                           vocab, vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, segs, kv,
+                           lam);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((finalize_vec<T, false, DIV>), dim3(grid), dim3(256), 0, s, n_exits, n,
+                       vocab, vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, segs, kv,
+                       lam);
   } else {
-    if (info.teacher_w16) return hipErrorInvalidValue;   // the packed GEMM needs V % 32 == 0
     const int64_t total = n * vocab;
     const int64_t blocks = (total + 255) / 256;
     const unsigned grid = static_cast<unsigned>(blocks < 256 * 16 ? blocks : 256 * 16);
-    hipLaunchKernelGGL(finalize_elem<T>, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, vtile,
-                       labels, alpha, grad_scale, stats, lse, dl, n_vt);
+    hipLaunchKernelGGL((finalize_elem<T, DIV>), dim3(grid), dim3(256), 0, s, n_exits, n, vocab,
+                       vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, kv, lam);
+  }
+}
+
+template <typename T>
+hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const TileInfo& info,
+                           const int32_t* labels, float alpha, float grad_scale,
+                           const float* stats, const float* lse, void* const* dlogits, int div,
+                           const float* kv, const ExitW& lam, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  constexpr int C = Elem<T>::kChunk;
+  if (info.teacher_w16 && (vocab % C != 0 || div != kDivForward))
+    return hipErrorInvalidValue;   // the packed GEMM needs V % 32 == 0; fp16 weights: forward only
+  DlPtrs dl{};
+  for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
+  switch (div) {
+    case kDivForward:
+      finalize_div<T, kDivForward>(n_exits, n, vocab, info, labels, alpha, grad_scale, stats, lse,
+                                   dl, kv, lam, s);
+      break;
+    case kDivReverseKL:
+      finalize_div<T, kDivReverseKL>(n_exits, n, vocab, info, labels, alpha, grad_scale, stats,
+                                     lse, dl, kv, lam, s);
+      break;
+    case kDivJS:
+      finalize_div<T, kDivJS>(n_exits, n, vocab, info, labels, alpha, grad_scale, stats, lse, dl,
+                              kv, lam, s);
+      break;
+    case kDivTV:
+      finalize_div<T, kDivTV>(n_exits, n, vocab, info, labels, alpha, grad_scale, stats, lse, dl,
+                              kv, lam, s);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template hipError_t launch_finalize<bf16_t>(int, int64_t, int, const TileInfo&, const int32_t*,
                                             float, float, const float*, const float*,
-                                            void* const*, hipStream_t);
+                                            void* const*, int, const float*, const ExitW&,
+                                            hipStream_t);
 template hipError_t launch_finalize<float>(int, int64_t, int, const TileInfo&, const int32_t*,
                                            float, float, const float*, const float*, void* const*,
-                                           hipStream_t);
+                                           int, const float*, const ExitW&, hipStream_t);
 
 hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, int vtile, const float* best,
                                int32_t* argmax, hipStream_t s) {

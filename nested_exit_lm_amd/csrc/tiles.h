@@ -5,7 +5,7 @@
 namespace nel {
 
 constexpr float kMasked = -1.0e30f;   // logit of a vocabulary entry beyond V
-enum { kModeLoss = 0, kModeArgmax = 1 };
+enum { kModeLoss = 0, kModeArgmax = 1, kModeLossPlain = 2 };   // plain: no distillation sums
 
 // A-row q of a 32-row MFMA block holds vocabulary entry vperm(q), chosen so
 // that accumulator register r of lane half h is vocabulary entry 16h + r

@@ -70,9 +70,9 @@ def test_loss_host_validation():
     ws_need = nel.workspace_size(nel.OP_LOSS, 3, 4, 10)
 
     def call(dt=1, E=3, n=4, V=10, d=d, h=p3, w=p3, labels=FAKE, alpha=0.3, gs=1.0,
-             mean=FAKE, dl=None, ws=FAKE, wsb=ws_need):
-        return lib.nel_matryoshka_loss(dt, E, n, V, d, h, w, labels, alpha, gs, None, mean, dl, ws,
-                                       wsb, None)
+             mean=FAKE, dl=None, ws=FAKE, wsb=ws_need, lam=None, div=0):
+        return lib.nel_matryoshka_loss(dt, E, n, V, d, h, w, labels, alpha, gs, lam, div, None,
+                                       mean, dl, ws, wsb, None)
 
     assert call(dt=5) == -3
     assert call(E=0) == -1
@@ -90,6 +90,12 @@ def test_loss_host_validation():
     assert call(ws=None) == -5
     assert call(wsb=ws_need - 1) == -5
     assert call(dl=_arr(ctypes.c_void_p, FAKE, None, FAKE)) == -1
+    assert call(div=4) == -1
+    assert call(div=-1) == -1
+    assert call(div=1) == -1                                 # needs the logit gradient buffers
+    assert call(lam=_arr(ctypes.c_float, 1.0, -0.5, 1.0)) == -1
+    assert call(lam=_arr(ctypes.c_float, 1.0, float("nan"), 1.0)) == -1
+    assert call(lam=_arr(ctypes.c_float, 1.0, float("inf"), 1.0)) == -1
 
 
 def test_heads_and_accept_host_validation():
@@ -125,9 +131,9 @@ def test_packed_host_validation():
     p3 = _arr(ctypes.c_void_p, FAKE, FAKE, FAKE)
     ws_need = nel.workspace_size(nel.OP_LOSS, 3, 4, 256)
 
-    def loss(dt=1, V=256, d=d, dl=p3, alpha=0.3):
-        return lib.nel_matryoshka_loss_packed(dt, 3, 4, V, d, p3, p3, FAKE, alpha, 1.0, None, FAKE,
-                                              dl, FAKE, ws_need, None)
+    def loss(dt=1, V=256, d=d, dl=p3, alpha=0.3, div=0):
+        return lib.nel_matryoshka_loss_packed(dt, 3, 4, V, d, p3, p3, FAKE, alpha, 1.0, None, div,
+                                              None, FAKE, dl, FAKE, ws_need, None)
 
     assert loss(dt=0) == -3                                    # fp32 has no packed form
     assert loss(V=100) == -2

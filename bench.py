@@ -97,6 +97,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-verify", action="store_true", help="skip the speculative-verify sub-benchmark")
     ap.add_argument("--no-backward", action="store_true", help="skip the head-backward sub-benchmark")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the sub-benchmark of the divergences and junction modes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB read + 1 GiB write kernel three times (the "
                          "reference that scales the HBM byte counters)")
@@ -225,6 +227,9 @@ def main():
         out["verify_102x7"] = bench_verify(nel, torch, synth, dev, args)
     if not args.no_backward:
         out["backward"] = bench_backward(nel, torch, hs, ws, dl, args, ids=ids, embs=embs)
+    if not args.no_variants:
+        out["variants"] = bench_variants(nel, torch, hs, pw, labels, dl, wsb, mean, tok, s.alpha,
+                                         args, ids=ids, embs=embs)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
         out["cpu_baseline"] = cpu_baseline(s, args.cpu_seconds)
@@ -342,6 +347,47 @@ def bench_backward(nel, torch, hs, ws, dl, args, ids=None, embs=None):
                      + V * 4 * (D[m] - D[m - 1]) for m in (1, 2))
         res["junction_bwd_ms"] = tot / steps
         res["junction_bwd_gbs"] = jbytes / (tot / steps / 1e3) / 1e9
+    return res
+
+
+def bench_variants(nel, torch, hs, pw, labels, dl, wsb, mean, tok, alpha, args, ids, embs):
+    """The same loss step (packed heads, already packed) with each other
+    divergence and with per-exit weights, and junction 2 -> 3 in each mode.
+    The divergence pass reads the stored shifted logits of every exit once."""
+    N, V = dl[0].shape
+    D = [h.shape[1] for h in hs]
+    M = len(D)
+    steps = max(args.steps // 4, 3)
+
+    def timed(fn, kernel):
+        fn()
+        torch.cuda.synchronize()
+        nel.timing_reset()
+        nel.timing_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        nel.timing_enable(False)
+        tot, _ = nel.timing_read(kernel)
+        return (t1 - t0) * 1e3 / steps, tot / steps
+
+    res = {"steps": steps, "work": "packed heads + loss + dlogits (no junction, no weight packing)"}
+    for name, div, lam in (("forward", 0, None), ("forward_weighted", 0, [0.5, 1.0, 2.0]),
+                           ("reverse_kl", 1, None), ("js", 2, None), ("tv", 3, None)):
+        ms, dms = timed(lambda: nel.matryoshka_loss_packed(
+            hs, pw, labels, alpha_d=alpha, dlogits=dl, workspace=wsb, mean_loss=mean,
+            token_loss=tok, exit_weights=lam, divergence=div), "divergence")
+        r = {"ms_per_step": ms}
+        if div:
+            r["divergence_pass_ms"] = dms
+            r["divergence_pass_gbs"] = M * N * V * 2 / (dms / 1e3) / 1e9   # reads every exit's s
+        res[name] = r
+    out = torch.empty(N, D[2], dtype=hs[0].dtype, device=hs[0].device)
+    for name, mode in (("rescale", 0), ("no_rescale", 1), ("zero_fill", 2)):
+        ms, jms = timed(lambda: nel.junction(hs[1], ids, embs[2], out=out, mode=mode), "junction")
+        res["junction_2to3_" + name + "_ms"] = jms
     return res
 
 

@@ -13,13 +13,14 @@
 // (q_k if that is all zero), after L acceptances from q at position L; draws
 // are inverse-CDF in vocabulary order with the caller's uniform.
 //
-// Kernels: (1) per exit and position, the row maximum, the softmax sum and the
-// nucleus threshold, found exactly by a 32-step bisection on order-preserving
-// integer keys of the unnormalised probabilities (every step a fixed-order
-// workgroup reduction in fp64, so every thread takes the same decision);
+// Kernels: (1) per exit and position (a 1024-thread workgroup), the row
+// maximum, the softmax sum and the nucleus threshold, found exactly by a
+// 32-step bisection on order-preserving integer keys of the unnormalised
+// probabilities (every step a fixed-order workgroup reduction in fp64, so
+// every thread takes the same decision);
 // (2) beta per drafted position; (3) per sequence, the acceptance chain and
 // the draw, whose running sums are fp64.  Probabilities themselves are fp32.
-// A row lives in registers (V <= 256 x kPer).
+// A row lives in registers (V <= kStatThreads x kPer).
 #include "common.h"
 #include "internal.h"
 
@@ -27,7 +28,8 @@ namespace nel {
 
 namespace {
 
-constexpr int kPer = 128;   // row entries per thread: V <= 32768
+constexpr int kStatThreads = 1024;   // threads per row of the statistics kernel
+constexpr int kPer = 32;             // row entries per thread: V <= 32768
 
 // float -> uint32 with the same order (no NaNs)
 __device__ __forceinline__ uint32_t fkey(float x) {
@@ -43,15 +45,32 @@ __device__ __forceinline__ float unnorm(float l, float inv_t, float mx) {
   return fexp(__fsub_rn(scaled(l, inv_t), mx));
 }
 
-// Sum over the 256-thread workgroup in a fixed order; every thread gets it.
+// Reductions over a workgroup of NW wavefronts in a fixed order (wavefront
+// results combined as a balanced tree); every thread gets the result.
+template <int NW, typename T>
+__device__ __forceinline__ T tree_sum(const T* r) {
+  if constexpr (NW == 1)
+    return r[0];
+  else
+    return tree_sum<NW / 2>(r) + tree_sum<NW / 2>(r + NW / 2);
+}
+template <int NW>
+__device__ __forceinline__ float tree_max(const float* r) {
+  if constexpr (NW == 1)
+    return r[0];
+  else
+    return fmaxf(tree_max<NW / 2>(r), tree_max<NW / 2>(r + NW / 2));
+}
+template <int NW = 4>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
+  return tree_sum<NW>(red);
 }
+template <int NW = 4>
 __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -59,24 +78,28 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   __syncthreads();
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
+  return tree_sum<NW>(red);
 }
+template <int NW = 4>
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  return tree_max<NW>(red);
 }
 
 // Row statistics of one (exit, position): stats = {max of l/T, nucleus sum
-// sum_{kept} exp(l/T - max), threshold key (bits), unused}.
-// Thread t holds entries t + 256 j.
-__global__ __launch_bounds__(256) void nucleus_stats_kernel(
+// sum_{kept} exp(l/T - max), threshold key (bits), softmax sum}.
+// Thread t holds entries t + kStatThreads j; each thread's sums run over four
+// interleaved partial sums (independent add chains) combined in a fixed order.
+__global__ __launch_bounds__(kStatThreads) void nucleus_stats_kernel(
     const float* __restrict__ draft, const float* __restrict__ verify, int positions, int rows_per_seq,
     int vocab, float inv_t, float top_p, float4* __restrict__ stats) {
-  __shared__ float red[4];
+  constexpr int NW = kStatThreads / 64;
+  __shared__ float red[NW];
+  __shared__ double red64[NW];
   const int tid = threadIdx.x;
   const int nrows = gridDim.x / 2;
   const int exit = blockIdx.x / nrows, r = blockIdx.x % nrows;   // r = b * rows_per_seq + i
@@ -86,42 +109,41 @@ __global__ __launch_bounds__(256) void nucleus_stats_kernel(
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int v = tid + 256 * j;
+    const int v = tid + kStatThreads * j;
     x[j] = v < vocab ? row[v] : -INFINITY;
     if (v < vocab) mx = fmaxf(mx, scaled(x[j], inv_t));
   }
-  mx = block_max(mx, red);
+  mx = block_max<NW>(mx, red);
   // From here the row is held as order keys of the unnormalised probabilities
   // (all >= 0, so the value is the key's low 31 bits).
   uint32_t key[kPer];
-  float s = 0.f;   // this thread's share of the softmax sum
+  float sp[4] = {0.f, 0.f, 0.f, 0.f};   // this thread's share of the softmax sum
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int v = tid + 256 * j;
+    const int v = tid + kStatThreads * j;
     const float e = v < vocab ? unnorm(x[j], inv_t, mx) : 0.f;   // the unnormalised probability
     key[j] = fkey(e);
-    s += e;
+    sp[j & 3] += e;
   }
   auto val = [](uint32_t k) { return __uint_as_float(k & 0x7fffffffu); };
-  // largest key K with mass(key >= K) >= top_p.  Each thread's 128 terms are
-  // summed in fp32, the workgroup's 256 partial sums in fp64.
-  __shared__ double red64[4];
-  const double s64 = block_sum_f64(s, red64);
+  auto mass = [&](uint32_t K) {   // this thread's mass of keys >= K
+    float m[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) m[j & 3] += key[j] >= K ? val(key[j]) : 0.f;
+    return (m[0] + m[1]) + (m[2] + m[3]);
+  };
+  // largest key K with mass(key >= K) >= top_p.  Each thread's 32 terms are
+  // summed in fp32, the workgroup's 1024 partial sums in fp64.
+  const double s64 = block_sum_f64<NW>((sp[0] + sp[1]) + (sp[2] + sp[3]), red64);
   uint32_t K = 0;
   if (top_p < 1.f) {
     const double need = static_cast<double>(top_p) * s64;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = K | (1u << bit);
-      float m = 0.f;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) m += key[j] >= cand ? val(key[j]) : 0.f;
-      if (block_sum_f64(m, red64) >= need) K = cand;
+      if (block_sum_f64<NW>(mass(cand), red64) >= need) K = cand;
     }
   }
-  float snp = 0.f;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) snp += key[j] >= K ? val(key[j]) : 0.f;
-  const float sn = static_cast<float>(block_sum_f64(snp, red64));
+  const float sn = static_cast<float>(block_sum_f64<NW>(mass(K), red64));
   if (tid == 0) stats[blockIdx.x] = make_float4(mx, sn, __uint_as_float(K), static_cast<float>(s64));
 }
 
@@ -252,7 +274,7 @@ hipError_t launch_speculative_verify(int batch, int positions, int draft_len, in
   const int rows_per_seq = draft_len + 1;
   const float inv_t = 1.f / temperature;
   float4* stats = static_cast<float4*>(workspace);
-  hipLaunchKernelGGL(nucleus_stats_kernel, dim3(2 * batch * rows_per_seq), dim3(256), 0, s, draft,
+  hipLaunchKernelGGL(nucleus_stats_kernel, dim3(2 * batch * rows_per_seq), dim3(kStatThreads), 0, s, draft,
                      verify, positions, rows_per_seq, vocab, inv_t, top_p, stats);
   if (beta && draft_len > 0)
     hipLaunchKernelGGL(beta_kernel, dim3(batch * draft_len), dim3(256), 0, s, draft, verify,

@@ -5,7 +5,8 @@ its decisions in fp32, the oracle in fp64.  A decision on a sequence's path
 whose fp64 margin is below what the kernel's rounding can move (2e-6 of the
 mass for where the nucleus ends, 1e-5 relative for a tie at its edge or an
 accept comparison, 1e-6 of the total for a draw boundary; the kernel sums the
-masses from fp32 partials of 128 terms in fp64, and the draw in fp64)
+masses from per-thread fp32 partials of 32 terms combined in fp64, and the
+draw in fp64)
 is "borderline": either outcome is accepted there, and the sequence is checked
 for validity instead of equality.  beta is compared to 2e-5."""
 import numpy as np

@@ -99,6 +99,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the head-backward sub-benchmark")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the sub-benchmark of the divergences and junction modes")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the matrix-core rate probe (random and constant operands)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB read + 1 GiB write kernel three times (the "
                          "reference that scales the HBM byte counters)")
@@ -223,6 +225,8 @@ def main():
         "end_to_end_mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
         "mean_loss": losses,
     }
+    if not args.no_probe:
+        out["mfma_probe"] = bench_mfma_probe(nel, torch, dev)
     if not args.no_verify:
         out["verify_102x7"] = bench_verify(nel, torch, synth, dev, args)
     if not args.no_backward:
@@ -347,6 +351,34 @@ def bench_backward(nel, torch, hs, ws, dl, args, ids=None, embs=None):
                      + V * 4 * (D[m] - D[m - 1]) for m in (1, 2))
         res["junction_bwd_ms"] = tot / steps
         res["junction_bwd_gbs"] = jbytes / (tot / steps / 1e3) / 1e9
+    return res
+
+
+def bench_mfma_probe(nel, torch, dev):
+    """The dense bf16 matrix-core rate this device sustains with no memory
+    traffic (nel_probe_mfma): on random bf16 operands, as the head GEMM
+    multiplies, and on constant ones.  Two workgroups of 4 wavefronts per CU,
+    as in the head GEMM; the median of 3 launches of about 20 ms."""
+    blocks, iters = 2 * 256, 40000
+    flops = blocks * 4 * iters * 8 * 32768.0
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    res = {"blocks": blocks, "iters": iters, "peak_tflops": BF16_PEAK_TFLOPS}
+    for name, ops in (("random", torch.randn(16, 64, 8, generator=g, device=dev).bfloat16()),
+                      ("constant", torch.ones(16, 64, 8, dtype=torch.bfloat16, device=dev))):
+        nel.probe_mfma(ops, iters // 10, blocks)
+        times = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            nel.probe_mfma(ops, iters, blocks)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[1]
+        res[name + "_tflops"] = flops / (ms / 1e3) / 1e12
+        res[name + "_frac_of_peak"] = res[name + "_tflops"] / BF16_PEAK_TFLOPS
     return res
 
 

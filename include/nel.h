@@ -302,6 +302,25 @@ nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, i
                                  const void* emb, const void* dout, int32_t stop_grad,
                                  int32_t mode, void* dh, float* demb, int32_t* flags,
                                  void* workspace, size_t ws_bytes, void* stream);
+/*
+ * Measurement aid (not a step of the method): the dense bf16 matrix-core rate
+ * the device sustains on the given operand data.  The head GEMM's rate is
+ * quoted against the published peak; on this chip the rate also depends on
+ * the data multiplied (the clock drops under the power of toggling operands),
+ * and this probe measures that ceiling with no memory traffic.  Each of the
+ * `blocks` workgroups (4 wavefronts) loads 8 operand pairs into registers
+ * once, then issues iters x 8 MFMAs 32x32x16 (each 32768 flop per wavefront),
+ * cycling through the pairs into four accumulator chains.
+ *   operands: device, 16 x 64 x 8 bf16 (pair s: A at block 2s, B at 2s + 1;
+ *             64 lanes x 8 elements each), 16-byte aligned
+ *   sink:     device fp32 [blocks * 4]: per wavefront, the sum of its
+ *             accumulators (all-ones operands give 131072 x iters)
+ * Time it with events on `stream`.  Errors: NEL_ESHAPE if iters or blocks < 1,
+ * NEL_EINVAL for NULL pointers, NEL_EALIGN.
+ */
+nel_status nel_probe_mfma(const void* operands, int32_t iters, int32_t blocks, float* sink,
+                          void* stream);
+
 /* Bytes of workspace nel_junction_backward needs (0 on bad arguments). */
 size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t d_in, int32_t d_out,
                                        int32_t vocab);

@@ -29,7 +29,7 @@ __all__ = [
     "timing_read", "timing_reset", "KERNELS", "OP_LOSS", "OP_HEADS", "FLAG_BAD_ID",
     "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed", "head_backward",
     "head_backward_workspace_size", "junction_backward", "speculative_verify",
-    "JUNCTION_RESCALE", "JUNCTION_NO_RESCALE", "JUNCTION_ZERO_FILL", "DIV_FORWARD",
+    "probe_mfma", "JUNCTION_RESCALE", "JUNCTION_NO_RESCALE", "JUNCTION_ZERO_FILL", "DIV_FORWARD",
     "DIV_REVERSE_KL", "DIV_JS", "DIV_TV",
 ]
 
@@ -108,6 +108,7 @@ def load():
         "nel_speculative_verify": [c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, ctypes.c_float,
                                    ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
         "nel_speculative_workspace": [c_int, c_int],
+        "nel_probe_mfma": [vp, c_int, c_int, vp, vp],
         "nel_read_device_flags": [vp, vp, vp],
         "nel_clear_device_flags": [vp, vp],
         "nel_status_string": [c_int],
@@ -519,3 +520,19 @@ def speculative_verify(draft_logits, verify_logits, draft_tokens, u_accept, u_ne
                                       _dev(flags, device, "flags"), wsb.data_ptr(), wsb.numel(),
                                       _stream(device)), "nel_speculative_verify")
     return beta, acc, nxt
+
+
+def probe_mfma(operands, iters: int, blocks: int, sink=None):
+    """Launch the matrix-core rate probe on the current stream (a measurement aid):
+    operands bf16 [16, 64, 8] (8 A/B pairs of 64 lanes x 8); returns sink fp32 [blocks * 4].
+    Time it with events on the current stream."""
+    torch = _torch()
+    device = operands.device
+    if operands.dtype != torch.bfloat16 or operands.numel() != 16 * 64 * 8:
+        raise ValueError("operands must be bf16 with 16 x 64 x 8 elements")
+    if sink is None:
+        sink = torch.empty(blocks * 4, dtype=torch.float32, device=device)
+    lib = load()
+    _check(lib.nel_probe_mfma(_dev(operands, device, "operands"), int(iters), int(blocks),
+                              _dev(sink, device, "sink"), _stream(device)), "nel_probe_mfma")
+    return sink

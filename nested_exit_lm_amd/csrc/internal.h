@@ -177,4 +177,9 @@ hipError_t launch_accept(int batch, int positions, int draft_len, const int32_t*
                          const int32_t* verify, int32_t* accepted, hipStream_t s);
 hipError_t launch_clear_flags(int32_t* flags, hipStream_t s);
 
+// Matrix-core rate probe: `blocks` workgroups of 4 wavefronts, each running
+// iters x 8 MFMAs (32x32x16 bf16) on the operand sets in `operands`.
+hipError_t launch_mfma_rate(const void* operands, int iters, int blocks, float* sink,
+                            hipStream_t s);
+
 }  // namespace nel

@@ -20,9 +20,17 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = nel.load()
     syms = declared_symbols()
-    assert len(syms) == 21
+    assert len(syms) == 22
     for s in syms:
         assert hasattr(lib, s), s
+
+
+def test_probe_host_validation():
+    lib = nel.load()
+    assert lib.nel_probe_mfma(FAKE, 0, 1, FAKE, None) == -2
+    assert lib.nel_probe_mfma(FAKE, 1, 0, FAKE, None) == -2
+    assert lib.nel_probe_mfma(None, 1, 1, FAKE, None) == -1
+    assert lib.nel_probe_mfma(MIS, 1, 1, FAKE, None) == -4
 
 
 def test_status_strings_and_workspace_sizes():

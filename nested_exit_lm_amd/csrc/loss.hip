@@ -32,8 +32,9 @@ namespace nel {
 namespace {
 
 // ---------------------------------------------------------------- loss merge
-// 256 threads = 64 tokens x 4 tile groups; the groups are merged in LDS in a
-// fixed order, so results do not depend on scheduling.  The first wavefront
+// 1024 threads = 64 tokens x kMergeGroups tile groups (group g takes tiles
+// g, g + kMergeGroups, ...); the groups are merged in LDS in a fixed order,
+// so results do not depend on scheduling.  The first wavefront
 // (one lane per token) also reduces the workgroup's per-token values into
 // fp64 partial sums of the reported means, in a fixed butterfly order:
 // partials[block][q], q = CE_0.., Dist_0.., L_0.., total.
@@ -43,7 +44,17 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-__global__ __launch_bounds__(256) void loss_merge_kernel(int M, int64_t n, int vocab,
+constexpr int kMergeGroups = 16;
+
+template <int N>
+__device__ __forceinline__ float group_tree(const float (*sh)[64][2], int tl) {
+  if constexpr (N == 1)
+    return sh[0][tl][0];
+  else
+    return group_tree<N / 2>(sh, tl) + group_tree<N / 2>(sh + N / 2, tl);
+}
+
+__global__ __launch_bounds__(1024) void loss_merge_kernel(int M, int64_t n, int vocab,
                                                          const int32_t* __restrict__ labels,
                                                          float alpha,
                                                          const float* __restrict__ stats,
@@ -53,7 +64,7 @@ __global__ __launch_bounds__(256) void loss_merge_kernel(int M, int64_t n, int v
                                                          double* __restrict__ partials,
                                                          int32_t* __restrict__ flags, int n_vt,
                                                          ExitW lam, int skip_dist) {
-  __shared__ float sh[4][64][2];
+  __shared__ float sh[kMergeGroups][64][2];
   const int tl = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeTok + tl;
   const bool valid = t < n;
@@ -70,14 +81,14 @@ __global__ __launch_bounds__(256) void loss_merge_kernel(int M, int64_t n, int v
     const float* st = stats + static_cast<int64_t>(e) * 3 * plane + t;
     float m = -INFINITY, s = 0.f;
     if (valid)
-      for (int vt = g; vt < n_vt; vt += 4) lse_merge(m, s, st[static_cast<int64_t>(vt) * n],
-                                                     st[plane + static_cast<int64_t>(vt) * n]);
+      for (int vt = g; vt < n_vt; vt += kMergeGroups)
+        lse_merge(m, s, st[static_cast<int64_t>(vt) * n], st[plane + static_cast<int64_t>(vt) * n]);
     sh[g][tl][0] = m;
     sh[g][tl][1] = s;
     __syncthreads();
     float Mx = -INFINITY, Sx = 0.f;
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) lse_merge(Mx, Sx, sh[gg][tl][0], sh[gg][tl][1]);
+    for (int gg = 0; gg < kMergeGroups; ++gg) lse_merge(Mx, Sx, sh[gg][tl][0], sh[gg][tl][1]);
     __syncthreads();
     const float L = Mx + flog(Sx);
     if (ei == 0) lseT = L;
@@ -85,12 +96,12 @@ __global__ __launch_bounds__(256) void loss_merge_kernel(int M, int64_t n, int v
     if (ei > 0 && !skip_dist) {   // (otherwise div_finish_kernel supplies Dist)
       float a = 0.f;
       if (valid)
-        for (int vt = g; vt < n_vt; vt += 4)
+        for (int vt = g; vt < n_vt; vt += kMergeGroups)
           a = fmaf(fexp(stT[static_cast<int64_t>(vt) * n] - lseT),
                    st[2 * plane + static_cast<int64_t>(vt) * n], a);
       sh[g][tl][0] = a;
       __syncthreads();
-      const float T = (sh[0][tl][0] + sh[1][tl][0]) + (sh[2][tl][0] + sh[3][tl][0]);
+      const float T = group_tree<kMergeGroups>(sh, tl);
       __syncthreads();
       dist = L - T;
     }
@@ -466,24 +477,37 @@ __global__ __launch_bounds__(256) void finalize_elem(int M, int64_t n, int vocab
 }
 
 // ---------------------------------------------------------------- argmax merge
+// One wavefront per (exit, token): lane l takes tiles l, l + 64, ... in
+// ascending order (strict > keeps a tile's lower index on ties), then the
+// lanes' winners are combined by value, the lower index on ties.
 __global__ __launch_bounds__(256) void argmax_merge_kernel(int E, int64_t n,
                                                            const float* __restrict__ best,
                                                            int32_t* __restrict__ argmax, int n_vt) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= E * n) return;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= E * n) return;   // wavefront-uniform
   const int64_t e = i / n, t = i - e * n;
   const int64_t plane = static_cast<int64_t>(n_vt) * n;
   const float* b = best + e * 2 * plane + t;
   float bv = -INFINITY;
   int bi = INT_MAX;
-  for (int vt = 0; vt < n_vt; ++vt) {   // ascending tiles: ties keep the lower index
+  for (int vt = lane; vt < n_vt; vt += 64) {
     const float v = b[static_cast<int64_t>(vt) * n];
     if (v > bv) {
       bv = v;
       bi = __float_as_int(b[plane + static_cast<int64_t>(vt) * n]);
     }
   }
-  argmax[i] = bi;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, kWave);
+    const int oi = __shfl_xor(bi, o, kWave);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if (lane == 0) argmax[i] = bi;
 }
 
 // ---------------------------------------------------------------- acceptance
@@ -508,7 +532,7 @@ hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const
                              float* tokloss, double* partials, int32_t* flags, const ExitW& lam,
                              bool skip_dist, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(loss_merge_kernel, dim3(static_cast<unsigned>(n_merge_blocks(n))), dim3(256), 0,
+  hipLaunchKernelGGL(loss_merge_kernel, dim3(static_cast<unsigned>(n_merge_blocks(n))), dim3(1024), 0,
                      s, n_exits, n, vocab, labels, alpha, stats, lab, lse, tokloss, partials, flags,
                      (vocab + vtile - 1) / vtile, lam, skip_dist ? 1 : 0);
   return hipGetLastError();
@@ -641,7 +665,7 @@ hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, int vtile, con
                                int32_t* argmax, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const int64_t total = n_exits * n;
-  hipLaunchKernelGGL(argmax_merge_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+  hipLaunchKernelGGL(argmax_merge_kernel, dim3(static_cast<unsigned>((total + 3) / 4)),
                      dim3(256), 0, s, n_exits, n, best, argmax, (vocab + vtile - 1) / vtile);
   return hipGetLastError();
 }

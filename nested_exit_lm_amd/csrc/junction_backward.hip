@@ -665,10 +665,11 @@ hipError_t launch_junction_backward(int64_t n, int d_in, int d_out, int vocab, c
   }
   if (!demb) return hipGetLastError();
   const int de = d_out - d_in;
-  const int64_t zc = nblk * vocab;
+  const int64_t zc = nblk * vocab;   // 0 without tokens
   const int64_t zb = (zc + 255) / 256;
-  hipLaunchKernelGGL(zero_i32_kernel, dim3(static_cast<unsigned>(zb < 4096 ? zb : 4096)),
-                     dim3(256), 0, s, hist, zc);
+  if (zc > 0)
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(static_cast<unsigned>(zb < 4096 ? zb : 4096)),
+                       dim3(256), 0, s, hist, zc);
   if (n > 0)
     hipLaunchKernelGGL(rank_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, n, vocab,
                        ids, i32(L.rank), hist);

@@ -143,3 +143,57 @@ def test_vocab_permutation_covariance(nel):
     assert_loss_close(to_np(tok2), tok, 1e-4, "permuted losses")
     for m in range(2):
         assert_grad_close(to_np(dl2[m]), to_np(dl[m])[:, perm], 1e-2, "permuted dlogits")
+
+
+def test_junction_backward_without_tokens(nel):
+    """No tokens: dL/dh is empty and every embedding row's gradient is 0, in
+    every junction mode and at block 1."""
+    import torch
+    s = synth.make_suite((8, 16), 10, 1, 3, seed=53)
+    ds = DevSuite(s)
+    dout = torch.zeros(0, 16, dtype=torch.bfloat16, device="cuda:0")
+    for mode in (0, 1, 2):
+        dh, demb = nel.junction_backward(ds.h[0][:0], ds.ids[:0], ds.emb[1], dout, mode=mode)
+        torch.cuda.synchronize()
+        assert dh.shape == (0, 8) and demb.shape == (10, 8)
+        assert float(demb.abs().max()) == 0.0
+        assert nel.junction(ds.h[0][:0], ds.ids[:0], ds.emb[1], mode=mode).shape == (0, 16)
+    _, demb = nel.junction_backward(None, ds.ids[:0], ds.emb[0],
+                                    torch.zeros(0, 8, dtype=torch.bfloat16, device="cuda:0"))
+    torch.cuda.synchronize()
+    assert float(demb.abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("div", [1, 2, 3])
+def test_divergence_degenerate(nel, div):
+    """V = 1: every softmax is [1], so CE, every divergence and every gradient
+    are 0.  One token at V = 7 (fp32): the oracle, entry by entry."""
+    import torch
+    s = synth.make_suite((8, 16, 24), 1, 1, 5, dtype="f32", seed=54)
+    ds = DevSuite(s)
+    mean, tok, dl = nel.matryoshka_loss(ds.h, ds.w, ds.labels, divergence=div)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(to_np(tok)) <= 1e-6) and np.all(np.abs(to_np(mean)) <= 1e-6)
+    for g in dl:
+        assert float(g.abs().max()) <= 1e-6
+    s = synth.make_suite((8, 16, 24), 7, 1, 1, dtype="f32", seed=55)
+    ds = DevSuite(s)
+    mean, tok, dl = nel.matryoshka_loss(ds.h, ds.w, ds.labels, divergence=div,
+                                        exit_weights=[0.5, 1.5, 1.0])
+    torch.cuda.synchronize()
+    ref, grads = oracle.forward_tokens(s.h, s.w, s.labels, s.alpha, exit_weights=[0.5, 1.5, 1.0],
+                                       div=div)
+    np.testing.assert_allclose(to_np(tok)[:, 1], ref["dist"], atol=1e-5, rtol=1e-4)
+    np.testing.assert_allclose(to_np(tok)[:, 2], ref["loss"], atol=1e-5, rtol=1e-4)
+    for m in range(3):
+        np.testing.assert_allclose(to_np(dl[m]), grads[m], atol=1e-4)
+
+
+def test_speculative_empty_batch(nel):
+    import torch
+    z = torch.zeros(0, 7, 50, dtype=torch.float32, device="cuda:0")
+    beta, acc, nxt = nel.speculative_verify(z, z, torch.zeros(0, 7, dtype=torch.int32, device="cuda:0"),
+                                            torch.zeros(0, 7, device="cuda:0"),
+                                            torch.zeros(0, device="cuda:0"), 6)
+    torch.cuda.synchronize()
+    assert beta.shape == (0, 6) and acc.shape == (0,) and nxt.shape == (0,)

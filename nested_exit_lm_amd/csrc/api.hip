@@ -262,10 +262,14 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
   }
   TileInfo info;
   const bool fwd = div == NEL_DIV_FORWARD;
+  // packed heads with the method's divergence: fp16 scratch, and the
+  // teacher-weighted sums formed by the row-wise gradient pass
+  const bool rows = packed && fwd;
+  const int scratch = !fwd ? kScratchPlain : rows ? kScratchF16 : kScratchDistStats;
   hipError_t err = timed(NEL_K_HEADS_LOSS, s, [&] {
     if (packed)
-      return launch_heads_loss_packed(n_exits, n_tokens, vocab, ex, labels, stats, lab, fwd, &info,
-                                      s);
+      return launch_heads_loss_packed(n_exits, n_tokens, vocab, ex, labels, stats, lab, scratch,
+                                      &info, s);
     return dt == NEL_BF16 ? launch_heads_loss<bf16_t>(n_exits, n_tokens, vocab, ex, labels, stats,
                                                       lab, &info, s)
                           : launch_heads_loss<float>(n_exits, n_tokens, vocab, ex, labels, stats,
@@ -274,7 +278,7 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
   if (err != hipSuccess) return from_hip(err);
   err = timed(NEL_K_MERGE, s, [&] {
     return launch_loss_merge(n_exits, n_tokens, vocab, info.vtile, labels, alpha_d, stats, lab, lse, tl,
-                             partials, flags, lam, !fwd, s);
+                             partials, flags, lam, !fwd || rows, s);
   });
   if (err != hipSuccess) return from_hip(err);
   float* dv = reinterpret_cast<float*>(ws + L.dv);
@@ -289,11 +293,22 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
     });
     if (err != hipSuccess) return from_hip(err);
   }
+  if (rows && n_tokens > 0) {
+    err = timed(NEL_K_FINALIZE, s, [&] {
+      return launch_finalize_rows(n_exits, n_tokens, vocab, info, labels, alpha_d, grad_scale,
+                                  stats, lse, dlogits, dv, lam, s);
+    });
+    if (err != hipSuccess) return from_hip(err);
+  }
   err = timed(NEL_K_MEANS, s, [&] {
+    if (rows) {
+      const hipError_t e = launch_loss_finish(n_exits, n_tokens, alpha_d, dv, tl, partials, lam, s);
+      if (e != hipSuccess) return e;
+    }
     return launch_loss_means(n_exits, n_tokens, partials, mean_loss, s);
   });
   if (err != hipSuccess) return from_hip(err);
-  if (dlogits && n_tokens > 0) {
+  if (dlogits && n_tokens > 0 && !rows) {
     err = timed(NEL_K_FINALIZE, s, [&] {
       return dt == NEL_BF16 ? launch_finalize<bf16_t>(n_exits, n_tokens, vocab, info, labels,
                                                       alpha_d, grad_scale, stats, lse, dlogits,

@@ -30,7 +30,10 @@
 // S = sum_v w_v l_m,v; the smaller exits store l - m in bf16.  The finalize
 // pass turns both into gradients in place.  kModeLossPlain (divergences other
 // than the cross-entropy to the teacher, whose passes read every exit's l - m)
-// stores l - m in bf16 for every exit and forms no S.
+// stores l - m in bf16 for every exit and forms no S.  kModeLossF16 keeps the
+// teacher's fp16 weights but stores the smaller exits' l - m in fp16 and
+// forms no S: the row-wise gradient pass forms sum_v p_v l_m,v instead, so no
+// epilogue reads the teacher's weights back.
 #include <limits.h>
 
 #include "common.h"
@@ -115,8 +118,8 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
 
   f32x16 acc[NTB][NVB];
   for (int ei = 0; ei < n_exits; ++ei) {
-    const int e = (MODE == kModeLoss) ? (ei == 0 ? n_exits - 1 : ei - 1) : ei;
-    const bool teacher = (MODE == kModeLoss) && ei == 0;
+    const int e = (MODE != kModeArgmax) ? (ei == 0 ? n_exits - 1 : ei - 1) : ei;
+    const bool teacher = (MODE == kModeLoss || MODE == kModeLossF16) && ei == 0;
     const int D = ex.d[e];
     // wave-uniform bases; per-lane 32-bit byte offsets
     const char* __restrict__ Hb = static_cast<const char*>(ex.h[e]) + t0 * D * 2;
@@ -212,7 +215,8 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
                 S0 = fmaf(f16_lo(wp2), a0, S0);
                 S1 = fmaf(f16_hi(wp2), a1, S1);
               }
-              pk[r >> 3][(r >> 1) & 3] = pack_bf16x2(a0 - M[tb], a1 - M[tb]);
+              pk[r >> 3][(r >> 1) & 3] = MODE == kModeLossF16 ? pack_f16x2(a0 - M[tb], a1 - M[tb])
+                                                              : pack_bf16x2(a0 - M[tb], a1 - M[tb]);
             }
             if (ok) {
               u32x4* dst = reinterpret_cast<u32x4*>(O + off);
@@ -318,7 +322,8 @@ hipError_t launch_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
                          const int32_t* labels, float* stats, float* lab, TileInfo* info,
                          hipStream_t s) {
   info->vtile = kPkVoc;
-  info->teacher_w16 = MODE == kModeLoss;
+  info->teacher_w16 = MODE == kModeLoss || MODE == kModeLossF16;
+  info->student_f16 = MODE == kModeLossF16;
   if (n == 0) return hipSuccess;
   const int n_tt = static_cast<int>((n + kPkTok - 1) / kPkTok);
   const int n_vt = (vocab + kPkVoc - 1) / kPkVoc;
@@ -341,10 +346,12 @@ hipError_t launch_pack_weights(int vocab, int d, const void* w, void* packed, hi
 }
 
 hipError_t launch_heads_loss_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
-                                    const int32_t* labels, float* stats, float* lab,
-                                    bool dist_stats, TileInfo* info, hipStream_t s) {
-  if (!dist_stats)
+                                    const int32_t* labels, float* stats, float* lab, int scratch,
+                                    TileInfo* info, hipStream_t s) {
+  if (scratch == kScratchPlain)
     return launch_packed<kModeLossPlain>(n_exits, n, vocab, ex, labels, stats, lab, info, s);
+  if (scratch == kScratchF16)
+    return launch_packed<kModeLossF16>(n_exits, n, vocab, ex, labels, stats, lab, info, s);
   return launch_packed<kModeLoss>(n_exits, n, vocab, ex, labels, stats, lab, info, s);
 }
 

@@ -38,6 +38,7 @@ struct ExitSet {
 struct TileInfo {
   int vtile = kVocTile;
   bool teacher_w16 = false;
+  bool student_f16 = false;   // the smaller exits' l - m in fp16 (not the element type)
 };
 
 inline int64_t n_vocab_tiles(int vocab) { return (vocab + kVocTile - 1) / kVocTile; }
@@ -145,11 +146,14 @@ hipError_t launch_heads_argmax(int n_exits, int64_t n, int vocab, const ExitSet&
 // The loss GEMM needs every ex.out[e] (the teacher's holds its weights).
 bool packed_shape_ok(int vocab, int d);
 hipError_t launch_pack_weights(int vocab, int d, const void* w, void* packed, hipStream_t s);
-// dist_stats: the teacher's weights and the teacher-weighted sums for the
-// cross-entropy to the teacher; without them every exit stores l - m in bf16.
+// What the packed loss GEMM leaves for the passes after it: the teacher's
+// weights and the teacher-weighted sums (kScratchDistStats); l - m in bf16 for
+// every exit (kScratchPlain); the teacher's weights and the smaller exits'
+// l - m in fp16 (kScratchF16, for finalize_rows).
+constexpr int kScratchDistStats = 0, kScratchPlain = 1, kScratchF16 = 2;
 hipError_t launch_heads_loss_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
-                                    const int32_t* labels, float* stats, float* lab,
-                                    bool dist_stats, TileInfo* info, hipStream_t s);
+                                    const int32_t* labels, float* stats, float* lab, int scratch,
+                                    TileInfo* info, hipStream_t s);
 hipError_t launch_heads_argmax_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
                                       float* best, TileInfo* info, hipStream_t s);
 
@@ -157,6 +161,15 @@ hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const
                              float alpha, const float* stats, const float* lab, float* lse,
                              float* tokloss, double* partials, int32_t* flags, const ExitW& lam,
                              bool skip_dist, hipStream_t s);
+// After kScratchF16: every exit's gradient in place, one token row per
+// workgroup, and dv[e][t] = Dist_e from the teacher-weighted logit sums.
+hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInfo& info,
+                                const int32_t* labels, float alpha, float grad_scale,
+                                const float* stats, const float* lse, void* const* dlogits,
+                                float* dv, const ExitW& lam, hipStream_t s);
+// The losses and mean partials with Dist from dv (after launch_loss_merge with skip_dist).
+hipError_t launch_loss_finish(int n_exits, int64_t n, float alpha, const float* dv,
+                              float* tokloss, double* partials, const ExitW& lam, hipStream_t s);
 // Divergence D (not the forward cross-entropy) per student and token, then
 // the losses and mean partials with it (after launch_loss_merge with skip_dist).
 template <typename T>

@@ -430,6 +430,104 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
   }
 }
 
+// Packed path with fp16 scratch: the teacher's buffer holds its fp16 weights
+// w = exp(l_M - m), each smaller exit's its fp16 l - m (m the 256-entry tile
+// maximum).  One workgroup per token row (grid-stride) writes every exit's
+// gradient in place, as finalize_vec, and reduces per smaller exit
+// sum_v p_v l_m,v (l_m,v = (l - m) + m) in a fixed order (per-thread fp32 in
+// vocabulary order, then a fixed tree): dv[e][t] = LSE_e - that sum, the
+// cross-entropy to the teacher.
+__global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int vocab, int vtile,
+                                                         const int32_t* __restrict__ labels,
+                                                         float alpha, float gs,
+                                                         const float* __restrict__ stats,
+                                                         const float* __restrict__ lse, DlPtrs dl,
+                                                         int n_vt, float* __restrict__ dv,
+                                                         ExitW lam) {
+  typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+  __shared__ float red[4][kMaxExits];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t plane = static_cast<int64_t>(n_vt) * n;
+  const int64_t cpr = vocab / 8;
+  const int S = M - 1;
+  for (int64_t t = blockIdx.x; t < n; t += gridDim.x) {
+    const int y = labels[t];
+    const bool bad = y < 0 || y >= vocab;
+    const float lseT = lse[static_cast<int64_t>(M - 1) * n + t];
+    float acc[kMaxExits - 1];
+#pragma unroll
+    for (int e = 0; e < kMaxExits - 1; ++e) acc[e] = 0.f;
+    for (int64_t c = tid; c < cpr; c += 256) {
+      const int v0 = static_cast<int>(c * 8);
+      const int64_t tile = v0 / vtile;
+      const u32x4 tw = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
+      const float scT =
+          fexp(stats[static_cast<int64_t>(M - 1) * 3 * plane + tile * n + t] - lseT);
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t word = tw[j];   // (a scalar first: see finalize_vec)
+        const half2_t hw = __builtin_bit_cast(half2_t, word);
+        p[2 * j] = static_cast<float>(hw[0]) * scT;
+        p[2 * j + 1] = static_cast<float>(hw[1]) * scT;
+      }
+#pragma unroll
+      for (int e = 0; e < kMaxExits - 1; ++e) {
+        if (e >= S) break;
+        const u32x4 sr = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(dl.p[e]) + t * vocab) + c);
+        const float mt = stats[static_cast<int64_t>(e) * 3 * plane + tile * n + t];
+        const float off = mt - lse[static_cast<int64_t>(e) * n + t];
+        const float ge = gs * lam.w[e];
+        float g[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t word = sr[j];
+          const half2_t hs = __builtin_bit_cast(half2_t, word);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int i = 2 * j + h;
+            const float sv = static_cast<float>(hs[h]);
+            acc[e] = fmaf(p[i], sv + mt, acc[e]);
+            float val = fexp(sv + off) - alpha * p[i];
+            if (v0 + i == y) val -= 1.f - alpha;
+            g[i] = bad ? __builtin_nanf("") : ge * val;
+          }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(g[2 * j], g[2 * j + 1]);
+        __builtin_nontemporal_store(
+            o, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[e]) + t * vocab) + c);
+      }
+      const float gT = gs * lam.w[M - 1];
+      float g[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float val = p[i] - (v0 + i == y ? 1.f : 0.f);
+        g[i] = bad ? __builtin_nanf("") : gT * val;
+      }
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(g[2 * j], g[2 * j + 1]);
+      __builtin_nontemporal_store(
+          o, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
+    }
+#pragma unroll
+    for (int e = 0; e < kMaxExits - 1; ++e) {
+      if (e >= S) break;
+      const float a = wave_sum(acc[e]);
+      if (lane == 0) red[wave][e] = a;
+    }
+    __syncthreads();
+    if (tid < S)
+      dv[static_cast<int64_t>(tid) * n + t] = lse[static_cast<int64_t>(tid) * n + t] -
+                                              ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]));
+    __syncthreads();   // red is reused by the next row
+  }
+}
+
 // Element path for any vocabulary size.
 template <typename T, int DIV>
 __global__ __launch_bounds__(256) void finalize_elem(int M, int64_t n, int vocab, int vtile,
@@ -538,13 +636,37 @@ hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const
   return hipGetLastError();
 }
 
+hipError_t launch_loss_finish(int n_exits, int64_t n, float alpha, const float* dv,
+                              float* tokloss, double* partials, const ExitW& lam, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(div_finish_kernel, dim3(static_cast<unsigned>(n_merge_blocks(n))), dim3(64), 0,
+                     s, n_exits, n, alpha, dv, tokloss, partials, lam);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInfo& info,
+                                const int32_t* labels, float alpha, float grad_scale,
+                                const float* stats, const float* lse, void* const* dlogits,
+                                float* dv, const ExitW& lam, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (!info.teacher_w16 || !info.student_f16 || vocab % 8 != 0) return hipErrorInvalidValue;
+  DlPtrs dl{};
+  for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
+  const unsigned grid = static_cast<unsigned>(n < 256 * 16 ? n : 256 * 16);
+  hipLaunchKernelGGL(finalize_rows_f16, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, info.vtile,
+                     labels, alpha, grad_scale, stats, lse, dl, (vocab + info.vtile - 1) / info.vtile,
+                     dv, lam);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_divergence(int n_exits, int64_t n, int vocab, const TileInfo& info, int div,
                              float alpha, const float* stats, const float* lse,
                              void* const* dlogits, float* dv, float* kv, float* tokloss,
                              double* partials, const ExitW& lam, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (info.teacher_w16) return hipErrorInvalidValue;   // needs the teacher's shifted logits
+  if (info.teacher_w16 || info.student_f16)
+    return hipErrorInvalidValue;   // needs every exit's shifted logits in the element type
   DlPtrs dl{};
   for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
   const int n_vt = (vocab + info.vtile - 1) / info.vtile;
@@ -567,9 +689,7 @@ hipError_t launch_divergence(int n_exits, int64_t n, int vocab, const TileInfo& 
         return hipErrorInvalidValue;
     }
   }
-  hipLaunchKernelGGL(div_finish_kernel, dim3(static_cast<unsigned>(n_merge_blocks(n))), dim3(64), 0,
-                     s, n_exits, n, alpha, dv, tokloss, partials, lam);
-  return hipGetLastError();
+  return launch_loss_finish(n_exits, n, alpha, dv, tokloss, partials, lam, s);
 }
 
 template hipError_t launch_divergence<bf16_t>(int, int64_t, int, const TileInfo&, int, float,
@@ -626,6 +746,7 @@ hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const TileInfo& in
                            const float* kv, const ExitW& lam, hipStream_t s) {
   if (n == 0) return hipSuccess;
   constexpr int C = Elem<T>::kChunk;
+  if (info.student_f16) return hipErrorInvalidValue;   // finalize_rows reads that scratch
   if (info.teacher_w16 && (vocab % C != 0 || div != kDivForward))
     return hipErrorInvalidValue;   // the packed GEMM needs V % 32 == 0; fp16 weights: forward only
   DlPtrs dl{};

@@ -437,6 +437,7 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
 // sum_v p_v l_m,v (l_m,v = (l - m) + m) in a fixed order (per-thread fp32 in
 // vocabulary order, then a fixed tree): dv[e][t] = LSE_e - that sum, the
 // cross-entropy to the teacher.
+template <int MS>   // the most smaller exits the loops are unrolled for
 __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int vocab, int vtile,
                                                          const int32_t* __restrict__ labels,
                                                          float alpha, float gs,
@@ -454,9 +455,10 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
     const int y = labels[t];
     const bool bad = y < 0 || y >= vocab;
     const float lseT = lse[static_cast<int64_t>(M - 1) * n + t];
-    float acc[kMaxExits - 1];
+    float acc[MS];
 #pragma unroll
-    for (int e = 0; e < kMaxExits - 1; ++e) acc[e] = 0.f;
+    for (int e = 0; e < MS; ++e) acc[e] = 0.f;
+#pragma unroll 2
     for (int64_t c = tid; c < cpr; c += 256) {
       const int v0 = static_cast<int>(c * 8);
       const int64_t tile = v0 / vtile;
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
         p[2 * j + 1] = static_cast<float>(hw[1]) * scT;
       }
 #pragma unroll
-      for (int e = 0; e < kMaxExits - 1; ++e) {
+      for (int e = 0; e < MS; ++e) {
         if (e >= S) break;
         const u32x4 sr = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(dl.p[e]) + t * vocab) + c);
@@ -515,7 +517,7 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
           o, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
     }
 #pragma unroll
-    for (int e = 0; e < kMaxExits - 1; ++e) {
+    for (int e = 0; e < MS; ++e) {
       if (e >= S) break;
       const float a = wave_sum(acc[e]);
       if (lane == 0) red[wave][e] = a;
@@ -653,9 +655,13 @@ hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInf
   DlPtrs dl{};
   for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
   const unsigned grid = static_cast<unsigned>(n < 256 * 16 ? n : 256 * 16);
-  hipLaunchKernelGGL(finalize_rows_f16, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, info.vtile,
-                     labels, alpha, grad_scale, stats, lse, dl, (vocab + info.vtile - 1) / info.vtile,
-                     dv, lam);
+  const int n_vt = (vocab + info.vtile - 1) / info.vtile;
+  if (n_exits <= 3)
+    hipLaunchKernelGGL((finalize_rows_f16<2>), dim3(grid), dim3(256), 0, s, n_exits, n, vocab,
+                       info.vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, dv, lam);
+  else
+    hipLaunchKernelGGL((finalize_rows_f16<kMaxExits - 1>), dim3(grid), dim3(256), 0, s, n_exits, n,
+                       vocab, info.vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, dv, lam);
   return hipGetLastError();
 }
 

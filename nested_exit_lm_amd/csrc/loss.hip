@@ -654,7 +654,8 @@ hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInf
   if (!info.teacher_w16 || !info.student_f16 || vocab % 8 != 0) return hipErrorInvalidValue;
   DlPtrs dl{};
   for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
-  const unsigned grid = static_cast<unsigned>(n < 256 * 16 ? n : 256 * 16);
+  // one workgroup per row up to 65536 rows (grid-stride beyond)
+  const unsigned grid = static_cast<unsigned>(n < 65536 ? n : 65536);
   const int n_vt = (vocab + info.vtile - 1) / info.vtile;
   if (n_exits <= 3)
     hipLaunchKernelGGL((finalize_rows_f16<2>), dim3(grid), dim3(256), 0, s, n_exits, n, vocab,

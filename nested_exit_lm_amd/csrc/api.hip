@@ -265,10 +265,9 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
   // packed heads with the method's divergence: fp16 scratch, and the
   // teacher-weighted sums formed by the row-wise gradient pass
   const bool rows = packed && fwd;
-  const int scratch = !fwd ? kScratchPlain : rows ? kScratchF16 : kScratchDistStats;
   hipError_t err = timed(NEL_K_HEADS_LOSS, s, [&] {
     if (packed)
-      return launch_heads_loss_packed(n_exits, n_tokens, vocab, ex, labels, stats, lab, scratch,
+      return launch_heads_loss_packed(n_exits, n_tokens, vocab, ex, labels, stats, lab, !fwd,
                                       &info, s);
     return dt == NEL_BF16 ? launch_heads_loss<bf16_t>(n_exits, n_tokens, vocab, ex, labels, stats,
                                                       lab, &info, s)

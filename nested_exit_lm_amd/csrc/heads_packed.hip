@@ -23,17 +23,14 @@
 // operand) through LDS.  Wavefront w owns vocabulary entries [64w, 64w + 64)
 // of the tile for all 128 tokens (4 x 2 accumulator blocks of 32 x 32).
 //
-// Loss epilogue.  The teacher (last exit) runs first; its weights
-// w = exp(l_M - m) (m the tile's row maximum) go to the teacher's own gradient
-// buffer as fp16 (relative rounding 2^-11), where the smaller exits' epilogues
-// of the same workgroup read them back, lane for lane, to form
-// S = sum_v w_v l_m,v; the smaller exits store l - m in bf16.  The finalize
-// pass turns both into gradients in place.  kModeLossPlain (divergences other
-// than the cross-entropy to the teacher, whose passes read every exit's l - m)
-// stores l - m in bf16 for every exit and forms no S.  kModeLossF16 keeps the
-// teacher's fp16 weights but stores the smaller exits' l - m in fp16 and
-// forms no S: the row-wise gradient pass forms sum_v p_v l_m,v instead, so no
-// epilogue reads the teacher's weights back.
+// Loss epilogue: per (token, tile) the row maximum m, sum exp(l - m) and the
+// label's logit, and one 16-bit copy of the tile in the exit's gradient
+// buffer.  kModeLossF16 (the cross-entropy to the teacher): the teacher (last
+// exit, run first) stores its weights w = exp(l_M - m), the smaller exits
+// l - m, both fp16 (relative rounding 2^-11); the row-wise gradient pass
+// forms the teacher-weighted sums sum_v p_v l_m,v from them.  kModeLossPlain
+// (the other divergences, whose pass reads every exit's l - m) stores l - m
+// in bf16 for every exit.  No epilogue reads another exit's tile back.
 #include <limits.h>
 
 #include "common.h"
@@ -54,12 +51,6 @@ typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   const half2_t h = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
   return __builtin_bit_cast(uint32_t, h);
-}
-__device__ __forceinline__ float f16_lo(uint32_t u) {
-  return static_cast<float>(__builtin_bit_cast(half2_t, u)[0]);
-}
-__device__ __forceinline__ float f16_hi(uint32_t u) {
-  return static_cast<float>(__builtin_bit_cast(half2_t, u)[1]);
 }
 
 // ---------------------------------------------------------------- packing
@@ -119,7 +110,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
   f32x16 acc[NTB][NVB];
   for (int ei = 0; ei < n_exits; ++ei) {
     const int e = (MODE != kModeArgmax) ? (ei == 0 ? n_exits - 1 : ei - 1) : ei;
-    const bool teacher = (MODE == kModeLoss || MODE == kModeLossF16) && ei == 0;
+    const bool teacher = MODE == kModeLossF16 && ei == 0;
     const int D = ex.d[e];
     // wave-uniform bases; per-lane 32-bit byte offsets
     const char* __restrict__ Hb = static_cast<const char*>(ex.h[e]) + t0 * D * 2;
@@ -169,13 +160,12 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
       }
       // (2) sums, teacher weights / shifted logits, label logit
       bf16_t* __restrict__ O = static_cast<bf16_t*>(ex.out[e]);
-      const bf16_t* __restrict__ TW = static_cast<const bf16_t*>(ex.out[n_exits - 1]);
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
         const float ml = M[tb] * kLog2e;
         const int64_t tok = tq + 32 * tb;
         const bool row_ok = tok < n;
-        float s0 = 0.f, s1 = 0.f, S0 = 0.f, S1 = 0.f;
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb) {
           // V is a multiple of 32, so a lane's 16 entries are all inside or all beyond V
@@ -198,23 +188,12 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
               dst[1] = pk[1];
             }
           } else {
-            u32x4 wv[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-            if (MODE == kModeLoss && ok) {
-              const u32x4* src = reinterpret_cast<const u32x4*>(TW + off);
-              wv[0] = src[0];
-              wv[1] = src[1];
-            }
             u32x4 pk[2];
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
               const float a0 = acc[tb][vb][r], a1 = acc[tb][vb][r + 1];
               s0 += __builtin_amdgcn_exp2f(fmaf(a0, kLog2e, -ml));
               s1 += __builtin_amdgcn_exp2f(fmaf(a1, kLog2e, -ml));
-              if constexpr (MODE == kModeLoss) {
-                const uint32_t wp2 = wv[r >> 3][(r >> 1) & 3];
-                S0 = fmaf(f16_lo(wp2), a0, S0);
-                S1 = fmaf(f16_hi(wp2), a1, S1);
-              }
               pk[r >> 3][(r >> 1) & 3] = MODE == kModeLossF16 ? pack_f16x2(a0 - M[tb], a1 - M[tb])
                                                               : pack_bf16x2(a0 - M[tb], a1 - M[tb]);
             }
@@ -232,13 +211,9 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
             lab[static_cast<int64_t>(e) * n + tok] = val;
           }
         }
-        float s = s0 + s1, S = S0 + S1;
+        float s = s0 + s1;
         s += __shfl_xor(s, 32, 64);
-        S += __shfl_xor(S, 32, 64);
-        if (hl == 0) {
-          xsum[wave][tb * 32 + q][0] = s;
-          xsum[wave][tb * 32 + q][1] = S;
-        }
+        if (hl == 0) xsum[wave][tb * 32 + q][0] = s;
       }
       __syncthreads();
       // (3) wavefront w writes the statistics of token block w
@@ -251,8 +226,6 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
         float* st = stats + (static_cast<int64_t>(e) * 3 * n_vt + vt) * n + tk;
         st[0] = Mw;
         st[plane] = (xsum[0][j][0] + xsum[1][j][0]) + (xsum[2][j][0] + xsum[3][j][0]);
-        if (MODE == kModeLoss && !teacher)
-          st[2 * plane] = (xsum[0][j][1] + xsum[1][j][1]) + (xsum[2][j][1] + xsum[3][j][1]);
       }
     } else {
       // per token the tile's (max, lowest index); optional fp32 logits
@@ -322,7 +295,7 @@ hipError_t launch_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
                          const int32_t* labels, float* stats, float* lab, TileInfo* info,
                          hipStream_t s) {
   info->vtile = kPkVoc;
-  info->teacher_w16 = MODE == kModeLoss || MODE == kModeLossF16;
+  info->teacher_w16 = MODE == kModeLossF16;
   info->student_f16 = MODE == kModeLossF16;
   if (n == 0) return hipSuccess;
   const int n_tt = static_cast<int>((n + kPkTok - 1) / kPkTok);
@@ -346,13 +319,11 @@ hipError_t launch_pack_weights(int vocab, int d, const void* w, void* packed, hi
 }
 
 hipError_t launch_heads_loss_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
-                                    const int32_t* labels, float* stats, float* lab, int scratch,
+                                    const int32_t* labels, float* stats, float* lab, bool plain,
                                     TileInfo* info, hipStream_t s) {
-  if (scratch == kScratchPlain)
+  if (plain)
     return launch_packed<kModeLossPlain>(n_exits, n, vocab, ex, labels, stats, lab, info, s);
-  if (scratch == kScratchF16)
-    return launch_packed<kModeLossF16>(n_exits, n, vocab, ex, labels, stats, lab, info, s);
-  return launch_packed<kModeLoss>(n_exits, n, vocab, ex, labels, stats, lab, info, s);
+  return launch_packed<kModeLossF16>(n_exits, n, vocab, ex, labels, stats, lab, info, s);
 }
 
 hipError_t launch_heads_argmax_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,

@@ -33,8 +33,9 @@ struct ExitSet {
 
 // What the head GEMM that ran tells the passes after it: the vocabulary
 // width of its statistics tiles, and whether the teacher's gradient buffer
-// holds fp16 teacher weights exp(l_M - m) (packed-weight GEMM) rather than the
-// tile-shifted logits l_M - m in the element type.
+// holds fp16 teacher weights exp(l_M - m) and the smaller exits' fp16 l - m
+// (packed GEMM, cross-entropy to the teacher) rather than the tile-shifted
+// logits l - m in the element type.
 struct TileInfo {
   int vtile = kVocTile;
   bool teacher_w16 = false;
@@ -147,12 +148,10 @@ hipError_t launch_heads_argmax(int n_exits, int64_t n, int vocab, const ExitSet&
 bool packed_shape_ok(int vocab, int d);
 hipError_t launch_pack_weights(int vocab, int d, const void* w, void* packed, hipStream_t s);
 // What the packed loss GEMM leaves for the passes after it: the teacher's
-// weights and the teacher-weighted sums (kScratchDistStats); l - m in bf16 for
-// every exit (kScratchPlain); the teacher's weights and the smaller exits'
-// l - m in fp16 (kScratchF16, for finalize_rows).
-constexpr int kScratchDistStats = 0, kScratchPlain = 1, kScratchF16 = 2;
+// weights and the smaller exits' l - m in fp16 (for finalize_rows), or with
+// `plain` l - m in bf16 for every exit (for the other divergences).
 hipError_t launch_heads_loss_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
-                                    const int32_t* labels, float* stats, float* lab, int scratch,
+                                    const int32_t* labels, float* stats, float* lab, bool plain,
                                     TileInfo* info, hipStream_t s);
 hipError_t launch_heads_argmax_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
                                       float* best, TileInfo* info, hipStream_t s);
@@ -161,7 +160,7 @@ hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const
                              float alpha, const float* stats, const float* lab, float* lse,
                              float* tokloss, double* partials, int32_t* flags, const ExitW& lam,
                              bool skip_dist, hipStream_t s);
-// After kScratchF16: every exit's gradient in place, one token row per
+// After the fp16 scratch: every exit's gradient in place, one token row per
 // workgroup, and dv[e][t] = Dist_e from the teacher-weighted logit sums.
 hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInfo& info,
                                 const int32_t* labels, float alpha, float grad_scale,

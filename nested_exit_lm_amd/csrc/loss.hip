@@ -323,16 +323,13 @@ __global__ __launch_bounds__(64) void div_finish_kernel(int M, int64_t n, float 
 
 // 16-byte chunk path (vocab a multiple of the chunk).  Each workgroup
 // iteration covers 256 consecutive chunks of one token row for all exits.
-// TW16: the teacher's buffer holds fp16 weights w = exp(l_M - m) of its tile
-// (so p = w exp(m - lse)) instead of the shifted logits l_M - m.
-template <typename T, bool TW16, int DIV>
+template <typename T, int DIV>
 __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab, int vtile,
                                                     const int32_t* __restrict__ labels, float alpha,
                                                     float gs, const float* __restrict__ stats,
                                                     const float* __restrict__ lse, DlPtrs dl,
                                                     int n_vt, int segs_per_row,
                                                     const float* __restrict__ kv, ExitW lam) {
-  static_assert(!TW16 || DIV == kDivForward, "divergences read the teacher's shifted logits");
   constexpr int C = Elem<T>::kChunk;
   const int64_t plane = static_cast<int64_t>(n_vt) * n;
   const int64_t cpr = vocab / C;
@@ -359,29 +356,15 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
       const int e = M - 1;
       const float off = stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
                         lse[static_cast<int64_t>(e) * n + t];
-      if constexpr (TW16 && sizeof(T) == 2) {
-        typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
-        const float scale = fexp(off);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // (bit_cast of a vector-element expression reads element 0 on this
-          // compiler; the element goes through a scalar first)
-          const uint32_t word = traw[j];
-          const half2_t hw = __builtin_bit_cast(half2_t, word);
-          p[2 * j] = static_cast<float>(hw[0]) * scale;
-          p[2 * j + 1] = static_cast<float>(hw[1]) * scale;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-          float s;
-          if constexpr (sizeof(T) == 2)
-            s = __uint_as_float((i & 1) ? (traw[i >> 1] & 0xffff0000u) : (traw[i >> 1] << 16));
-          else
-            s = __uint_as_float(traw[i]);
-          lp[i] = s + off;
-          p[i] = fexp(lp[i]);
-        }
+      for (int i = 0; i < C; ++i) {
+        float s;
+        if constexpr (sizeof(T) == 2)
+          s = __uint_as_float((i & 1) ? (traw[i >> 1] & 0xffff0000u) : (traw[i >> 1] << 16));
+        else
+          s = __uint_as_float(traw[i]);
+        lp[i] = s + off;
+        p[i] = fexp(lp[i]);
       }
     }
 #pragma unroll
@@ -469,7 +452,9 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
       float p[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t word = tw[j];   // (a scalar first: see finalize_vec)
+        // (bit_cast of a vector-element expression read element 0 on this
+        // compiler: the element goes through a scalar first)
+        const uint32_t word = tw[j];
         const half2_t hw = __builtin_bit_cast(half2_t, word);
         p[2 * j] = static_cast<float>(hw[0]) * scT;
         p[2 * j + 1] = static_cast<float>(hw[1]) * scT;
@@ -726,15 +711,7 @@ static void finalize_div(int n_exits, int64_t n, int vocab, const TileInfo& info
     const int segs = static_cast<int>((cpr + 255) / 256);
     const int64_t nseg = n * segs;
     const unsigned grid = static_cast<unsigned>(nseg < 256 * 16 ? nseg : 256 * 16);
-    if constexpr (DIV == kDivForward) {
-      if (info.teacher_w16) {
-        hipLaunchKernelGGL((finalize_vec<T, true, DIV>), dim3(grid), dim3(256), 0, s, n_exits, n,
-                           vocab, vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, segs, kv,
-                           lam);
-        return;
-      }
-    }
-    hipLaunchKernelGGL((finalize_vec<T, false, DIV>), dim3(grid), dim3(256), 0, s, n_exits, n,
+    hipLaunchKernelGGL((finalize_vec<T, DIV>), dim3(grid), dim3(256), 0, s, n_exits, n,
                        vocab, vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, segs, kv,
                        lam);
   } else {
@@ -752,10 +729,8 @@ hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const TileInfo& in
                            const float* stats, const float* lse, void* const* dlogits, int div,
                            const float* kv, const ExitW& lam, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  constexpr int C = Elem<T>::kChunk;
-  if (info.student_f16) return hipErrorInvalidValue;   // finalize_rows reads that scratch
-  if (info.teacher_w16 && (vocab % C != 0 || div != kDivForward))
-    return hipErrorInvalidValue;   // the packed GEMM needs V % 32 == 0; fp16 weights: forward only
+  if (info.teacher_w16 || info.student_f16)
+    return hipErrorInvalidValue;   // fp16 scratch: finalize_rows reads it
   DlPtrs dl{};
   for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
   switch (div) {

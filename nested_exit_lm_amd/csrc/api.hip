@@ -171,6 +171,9 @@ nel_status exit_heads_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n
     for (int e = 0; e < n_exits; ++e)
       if (!packed_shape_ok(vocab, d[e])) return NEL_ESHAPE;
   if (!grid_fits(n_tokens, vocab)) return NEL_ESHAPE;
+  // the packed argmax grid has a workgroup per (token tile, 256-entry tile, exit)
+  if (packed && (n_tokens + 127) / 128 * ((vocab + 255) / 256) * n_exits > INT_MAX)
+    return NEL_ESHAPE;
   if (logits)
     for (int e = 0; e < n_exits; ++e) {
       if (n_tokens > 0 && !logits[e]) return NEL_EINVAL;

@@ -91,8 +91,18 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
 
   const int tid = threadIdx.x, lane = tid & 63, q = lane & 31, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Loss modes: every exit in one workgroup (the teacher first).  Argmax: one
+  // exit per workgroup, the widest exit's tiles first, so that at small token
+  // counts the narrow exits' short workgroups fill the last round.
+  int ei0 = 0, ei1 = n_exits, bid = blockIdx.x;
+  if constexpr (MODE == kModeArgmax) {
+    const int k = blockIdx.x / (n_tt * n_vt);
+    ei0 = n_exits - 1 - k;
+    ei1 = ei0 + 1;
+    bid = blockIdx.x - k * (n_tt * n_vt);
+  }
   int tt, vt;
-  tile_coords(blockIdx.x, n_tt, n_vt, kPkGroup, tt, vt);
+  tile_coords(bid, n_tt, n_vt, kPkGroup, tt, vt);
   const int64_t t0 = static_cast<int64_t>(tt) * kPkTok;
   const int vw = vt * kPkVoc + wave * (NVB * 32);   // this wavefront's first vocabulary entry
   const int64_t tq = t0 + q;                        // token of this lane in token block 0
@@ -108,7 +118,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
   uint32_t hoff[4];   // byte offsets of this thread's h chunks from row t0 (rows beyond n clamped)
 
   f32x16 acc[NTB][NVB];
-  for (int ei = 0; ei < n_exits; ++ei) {
+  for (int ei = ei0; ei < ei1; ++ei) {
     const int e = (MODE != kModeArgmax) ? (ei == 0 ? n_exits - 1 : ei - 1) : ei;
     const bool teacher = MODE == kModeLossF16 && ei == 0;
     const int D = ex.d[e];
@@ -300,8 +310,9 @@ hipError_t launch_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
   if (n == 0) return hipSuccess;
   const int n_tt = static_cast<int>((n + kPkTok - 1) / kPkTok);
   const int n_vt = (vocab + kPkVoc - 1) / kPkVoc;
-  hipLaunchKernelGGL((heads_kernel_packed<MODE>), dim3(n_tt * n_vt), dim3(kPkThreads), 0, s, ex,
-                     n_exits, n, vocab, labels, stats, lab, n_tt, n_vt);
+  const int splits = MODE == kModeArgmax ? n_exits : 1;   // argmax: a workgroup per exit
+  hipLaunchKernelGGL((heads_kernel_packed<MODE>), dim3(n_tt * n_vt * splits), dim3(kPkThreads), 0,
+                     s, ex, n_exits, n, vocab, labels, stats, lab, n_tt, n_vt);
   return hipGetLastError();
 }
 

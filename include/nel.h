@@ -248,11 +248,12 @@ nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* 
  * nel_pack_weights.  Same arguments, outputs and errors, plus: dt must be
  * NEL_BF16 (NEL_EDTYPE), vocab % 32 == 0 and every d[e] % 64 == 0
  * (NEL_ESHAPE), and dlogits must be given (NEL_EINVAL): between the head GEMM
- * and the final gradient pass the teacher's dlogits buffer holds the
- * teacher's softmax weights exp(l_M - m) (m its 256-entry tile maximum) in
- * fp16, which the smaller exits' tiles read back (with NEL_DIV_FORWARD; the
- * other divergences store l_M - m in bf16 instead).  Every dlogits buffer is
- * scratch until the call's work on `stream` has completed.
+ * and the final gradient pass the dlogits buffers hold 16-bit scratch.  With
+ * NEL_DIV_FORWARD the teacher's holds its softmax weights exp(l_M - m) (m the
+ * 256-entry tile maximum) and the smaller exits' hold l - m, all fp16; the
+ * gradient pass forms the teacher-weighted logit sums of Dist from them.  The
+ * other divergences store l - m in bf16 for every exit.  Every dlogits buffer
+ * is scratch until the call's work on `stream` has completed.
  */
 nel_status nel_matryoshka_loss_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens,
                                       int32_t vocab, const int32_t* d, const void* const* h,

@@ -293,21 +293,31 @@ def bench_backward(nel, torch, hs, ws, dl, args, ids=None, embs=None):
     and the backward of both junctions on seeded synthetic upstream gradients."""
     N, V = dl[0].shape
     D = [h.shape[1] for h in hs]
-    need = max(nel.head_backward_workspace_size(N, V, d) for d in D)
+    need = nel.heads_backward_workspace_size(N, V, D)
     wsb = torch.empty(need, dtype=torch.uint8, device=hs[0].device)
     dhs = [torch.empty_like(h) for h in hs]
     dws = [torch.empty(V, d, dtype=torch.float32, device=h.device) for h, d in zip(hs, D)]
+    steps = max(args.steps // 2, 3)
 
-    def step():
+    def per_exit():
         for m in range(len(D)):
             nel.head_backward(dl[m], hs[m], ws[m], dh=dhs[m], dw=dws[m], workspace=wsb)
 
+    def step():   # one grouped dh launch and one grouped dW launch for all exits
+        nel.heads_backward(dl, hs, ws, dhs=dhs, dws=dws, workspace=wsb)
+
+    per_exit()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        per_exit()
+    torch.cuda.synchronize()
+    per_exit_ms = (time.perf_counter() - t0) * 1e3 / steps
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
     nel.timing_reset()
     nel.timing_enable(True)
-    steps = max(args.steps // 2, 3)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
@@ -315,6 +325,7 @@ def bench_backward(nel, torch, hs, ws, dl, args, ids=None, embs=None):
     t1 = time.perf_counter()
     nel.timing_enable(False)
     res = {"ms_per_step": (t1 - t0) * 1e3 / steps,
+           "per_exit_calls_ms_per_step": per_exit_ms,
            "work": "dh (bf16) and dW (fp32) of all three heads from the step's dlogits"}
     flops = 2.0 * N * V * sum(D)          # per GEMM kind, all exits
     for k in ("bwd_pack", "bwd_dh", "bwd_dw"):

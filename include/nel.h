@@ -349,6 +349,27 @@ nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int3
 /* Bytes of workspace nel_head_backward needs (0 on bad arguments). */
 size_t nel_head_backward_workspace(int64_t n_tokens, int32_t vocab, int32_t d);
 
+/*
+ * nel_head_backward for every exit of a suite at once: the same outputs,
+ * bit-identical, but each of the two GEMMs (dh for all exits, then dw for
+ * all exits) is one launch, so one exit's workgroups fill another's last
+ * partial round on the device.
+ *   d:       host array [n_exits] of widths (each a multiple of 64)
+ *   dlogits, h, w: host arrays of n_exits device pointers, as in nel_head_backward
+ *   dh, dw:  NULL (skip that output for every exit) or host arrays of n_exits
+ *            device pointers, none NULL; not both NULL
+ *   workspace: >= nel_heads_backward_workspace() bytes
+ * Errors as nel_head_backward; NEL_EINVAL for n_exits outside [1, 8] or a
+ * NULL entry.
+ */
+nel_status nel_heads_backward(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                              const int32_t* d, const void* const* dlogits,
+                              const void* const* h, const void* const* w, void* const* dh,
+                              float* const* dw, void* workspace, size_t ws_bytes, void* stream);
+/* Bytes of workspace nel_heads_backward needs (0 on bad arguments). */
+size_t nel_heads_backward_workspace(int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                                    const int32_t* d);
+
 /* Bytes of device workspace an op needs (0 on bad arguments). */
 size_t nel_workspace_size(int32_t op, int32_t n_exits, int64_t n_tokens, int32_t vocab);
 

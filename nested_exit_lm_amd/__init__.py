@@ -102,6 +102,8 @@ def load():
         "nel_workspace_size": [c_int, c_int, c_i64, c_int],
         "nel_head_backward": [c_int, c_i64, c_int, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
         "nel_head_backward_workspace": [c_i64, c_int, c_int],
+        "nel_heads_backward": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "nel_heads_backward_workspace": [c_int, c_i64, c_int, vp],
         "nel_junction_backward": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, c_int, c_int,
                                   vp, vp, vp, vp, sz, vp],
         "nel_junction_backward_workspace": [c_i64, c_int, c_int, c_int],
@@ -122,6 +124,7 @@ def load():
         f.restype = c_int
     lib.nel_workspace_size.restype = sz
     lib.nel_head_backward_workspace.restype = sz
+    lib.nel_heads_backward_workspace.restype = sz
     lib.nel_junction_backward_workspace.restype = sz
     lib.nel_speculative_workspace.restype = sz
     lib.nel_status_string.restype = ctypes.c_char_p
@@ -442,6 +445,55 @@ def head_backward(dlogits, h, w, want_dh: bool = True, want_dw: bool = True, dh=
                                     wsb.data_ptr(), wsb.numel(), _stream(device)),
            "nel_head_backward")
     return dh, dw
+
+
+def heads_backward_workspace_size(n_tokens: int, vocab: int, widths) -> int:
+    ds = (ctypes.c_int32 * len(widths))(*widths)
+    return int(load().nel_heads_backward_workspace(len(widths), n_tokens, vocab, ds))
+
+
+def heads_backward(dlogits, hs, ws, want_dh: bool = True, want_dw: bool = True, dhs=None,
+                   dws=None, workspace=None):
+    """head_backward for every exit in two launches (one grouped dh GEMM, one grouped
+    dW GEMM): lists (dh_m bf16 [n, d_m] or None, dW_m fp32 [V, d_m] or None), with the
+    same bits as the per-exit call."""
+    torch = _torch()
+    M = len(hs)
+    if not (len(dlogits) == M == len(ws)) or M == 0:
+        raise ValueError("need one dlogits, h and w per exit")
+    device = dlogits[0].device
+    n, V = dlogits[0].shape
+    widths = [h.shape[1] for h in hs]
+    for m in range(M):
+        for t, name in ((dlogits[m], "dlogits"), (hs[m], "h"), (ws[m], "w")):
+            if t.dtype != torch.bfloat16:
+                raise TypeError(f"{name}[{m}] must be bfloat16")
+        if dlogits[m].shape != (n, V) or hs[m].shape[0] != n or ws[m].shape != (V, widths[m]):
+            raise ValueError("need dlogits[m] [n, V], h[m] [n, d_m], w[m] [V, d_m]")
+    if want_dh:
+        dhs = dhs if dhs is not None else [
+            torch.empty(n, d, dtype=torch.bfloat16, device=device) for d in widths]
+    if want_dw:
+        dws = dws if dws is not None else [
+            torch.empty(V, d, dtype=torch.float32, device=device) for d in widths]
+    if not want_dh:
+        dhs = None
+    if not want_dw:
+        dws = None
+    for lst, name in ((dhs, "dhs"), (dws, "dws")):
+        if lst is not None and len(lst) != M:
+            raise ValueError(f"{name} needs one tensor per exit")
+    need = heads_backward_workspace_size(n, V, widths)
+    wsb = workspace if workspace is not None else _BWD_WS.get(need, device)
+    ds = (ctypes.c_int32 * M)(*widths)
+    g = _ptrs([_dev(t, device, "dlogits") for t in dlogits])
+    hp = _ptrs([_dev(t, device, "h") for t in hs])
+    wp = _ptrs([_dev(t, device, "w") for t in ws])
+    dhp = _ptrs([_dev(t, device, "dh") for t in dhs]) if dhs is not None else None
+    dwp = _ptrs([_dev(t, device, "dw") for t in dws]) if dws is not None else None
+    _check(load().nel_heads_backward(BF16, M, n, V, ds, g, hp, wp, dhp, dwp, wsb.data_ptr(),
+                                     wsb.numel(), _stream(device)), "nel_heads_backward")
+    return dhs, dws
 
 
 _JBWD_WS = Workspace()

@@ -522,6 +522,83 @@ nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int3
   return NEL_OK;
 }
 
+// Workspace of nel_heads_backward: the per-exit layouts one after another.
+static size_t heads_bwd_offset(int32_t e, int64_t n, int32_t vocab, const int32_t* d) {
+  size_t o = 0;
+  for (int32_t k = 0; k < e; ++k) o += head_bwd_ws_layout(n, vocab, d[k]).total;
+  return o;
+}
+
+size_t nel_heads_backward_workspace(int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                                    const int32_t* d) {
+  if (n_exits < 1 || n_exits > NEL_MAX_EXITS || !d) return 0;
+  for (int32_t e = 0; e < n_exits; ++e)
+    if (!head_bwd_shape_ok(n_tokens, vocab, d[e])) return 0;
+  return heads_bwd_offset(n_exits, n_tokens, vocab, d);
+}
+
+nel_status nel_heads_backward(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                              const int32_t* d, const void* const* dlogits,
+                              const void* const* h, const void* const* w, void* const* dh,
+                              float* const* dw, void* workspace, size_t ws_bytes, void* stream) {
+  if (dt != NEL_BF16) return NEL_EDTYPE;
+  if (n_exits < 1 || n_exits > NEL_MAX_EXITS || !d) return NEL_EINVAL;
+  for (int32_t e = 0; e < n_exits; ++e)
+    if (!head_bwd_shape_ok(n_tokens, vocab, d[e])) return NEL_ESHAPE;
+  if (!dh && !dw) return NEL_EINVAL;
+  if (n_tokens > 0 && (!dlogits || !h || !w)) return NEL_EINVAL;
+  for (int32_t e = 0; e < n_exits; ++e) {
+    if (n_tokens > 0 && (!dlogits[e] || !h[e] || !w[e])) return NEL_EINVAL;
+    if ((dh && !dh[e]) || (dw && !dw[e])) return NEL_EINVAL;
+    if ((n_tokens > 0 && (misaligned(dlogits[e]) || misaligned(h[e]) || misaligned(w[e]))) ||
+        (dh && misaligned(dh[e])) || (dw && misaligned(dw[e])))
+      return NEL_EALIGN;
+  }
+  if (misaligned(workspace)) return NEL_EALIGN;
+  if (!workspace || ws_bytes < heads_bwd_offset(n_exits, n_tokens, vocab, d))
+    return NEL_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (n_tokens == 0) {   // no tokens: dH is empty, dW = 0
+    if (!dw) return NEL_OK;
+    for (int32_t e = 0; e < n_exits && err == hipSuccess; ++e)
+      err = timed(NEL_K_BWD_DW, s, [&] {
+        return launch_zero_f32(dw[e], static_cast<int64_t>(vocab) * d[e], s);
+      });
+    return from_hip(err);
+  }
+  char* ws = static_cast<char*>(workspace);
+  BwdGroup gh{}, gw{};
+  for (int32_t e = 0; e < n_exits; ++e) {
+    const HeadBwdWs L = head_bwd_ws_layout(n_tokens, vocab, d[e]);
+    char* base = ws + heads_bwd_offset(e, n_tokens, vocab, d);
+    if (dh) {
+      err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack_t(w[e], vocab, d[e], vocab, base + L.wt, s); });
+      if (err != hipSuccess) return from_hip(err);
+      if (!bwd_group_add(gh, base + L.wt, d[e], dlogits[e], n_tokens, vocab, vocab, dh[e], d[e]))
+        return NEL_ESHAPE;
+    }
+    if (dw) {
+      err = timed(NEL_K_BWD_PACK, s, [&] {
+        return launch_pack_t(h[e], n_tokens, d[e], L.n_pad, base + L.ht, s);
+      });
+      if (err != hipSuccess) return from_hip(err);
+      err = timed(NEL_K_BWD_PACK, s, [&] {
+        return launch_transpose(dlogits[e], n_tokens, vocab, L.n_pad, base + L.gt, s);
+      });
+      if (err != hipSuccess) return from_hip(err);
+      if (!bwd_group_add(gw, base + L.ht, d[e], base + L.gt, vocab, L.n_pad, L.n_pad, dw[e], d[e]))
+        return NEL_ESHAPE;
+    }
+  }
+  if (dh) {
+    err = timed(NEL_K_BWD_DH, s, [&] { return launch_bwd_group<bf16_t>(gh, s); });
+    if (err != hipSuccess) return from_hip(err);
+  }
+  if (dw) err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float>(gw, s); });
+  return from_hip(err);
+}
+
 nel_status nel_read_device_flags(const int32_t* dev_flags, int32_t* host_flags, void* stream) {
   if (!dev_flags || !host_flags) return NEL_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -11,6 +11,8 @@
 // stores are row-major.  W^T and h^T are written tiled by one transposing
 // pass each; G^T by one transpose (all three HBM-bound, into the workspace;
 // K is zero-padded to a multiple of 64).
+#include <cstdint>
+
 #include "common.h"
 #include "internal.h"
 #include "packed_core.h"
@@ -106,17 +108,29 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
 
 // ---------------------------------------------------------------- GEMM
 // out[b][a] = sum_k A[a][k] B[b][k] for a < a_rows, b < b_rows; A tiled
-// (a_rows % 32 == 0, K % 64 == 0), B row-major with row stride ldb.
+// (a_rows % 32 == 0, K % 64 == 0), B row-major with row stride ldb.  One
+// launch covers a group of such products (the exits of a suite): workgroup
+// ids are split by the prefix sums `first` of the products' tile counts, so
+// one product's workgroups fill another's last partial round.
 template <typename OutT>
 __global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
-    const bf16_t* __restrict__ A, int a_rows, const bf16_t* __restrict__ B, int64_t b_rows,
-    int64_t ldb, int64_t K, OutT* __restrict__ out, int64_t ldo, int n_bt, int n_at) {
+    BwdGroup /*read through the kernarg pointer*/) {
+  // Per-product fields are read through the kernarg segment pointer, which
+  // keeps the lookups by a run-time product index scalar.
+  const BwdGroup& g = *(const BwdGroup*)__builtin_amdgcn_kernarg_segment_ptr();
   constexpr int NTB = kPkNTB, NAB = kPkNAB;
   __shared__ u32x4 hs[2][8 * kPkBRows];
+  int e = 0;
+  while (e + 1 < g.count && static_cast<int>(blockIdx.x) >= g.first[e + 1]) ++e;
+  const bf16_t* __restrict__ A = g.A[e];
+  const bf16_t* __restrict__ B = g.B[e];
+  OutT* __restrict__ out = static_cast<OutT*>(g.out[e]);
+  const int a_rows = g.a_rows[e];
+  const int64_t b_rows = g.b_rows[e], ldb = g.ldb[e], K = g.K[e], ldo = g.ldo[e];
   const int tid = threadIdx.x, lane = tid & 63, q = lane & 31, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bt, at;
-  tile_coords(blockIdx.x, n_bt, n_at, kBwdGroup, bt, at);
+  tile_coords(static_cast<int>(blockIdx.x) - g.first[e], g.n_bt[e], g.n_at[e], kBwdGroup, bt, at);
   const int64_t b0 = static_cast<int64_t>(bt) * kPkBRows;
   const int aw = at * kPkARows + wave * (NAB * 32);   // this wavefront's first A row
   const int rb0 = min(aw >> 5, a_rows / 32 - 1), rb1 = min((aw >> 5) + 1, a_rows / 32 - 1);
@@ -212,21 +226,50 @@ hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Adds product (A, B) -> out to a group; false if the group is full.
+bool bwd_group_add(BwdGroup& g, const void* A, int a_rows, const void* B, int64_t b_rows,
+                   int64_t ldb, int64_t K, void* out, int64_t ldo) {
+  if (b_rows == 0) return true;   // nothing to compute
+  if (g.count >= kMaxExits) return false;
+  const int64_t n_bt = (b_rows + kPkBRows - 1) / kPkBRows;
+  const int64_t n_at = (int64_t{a_rows} + kPkARows - 1) / kPkARows;
+  if (g.first[g.count] + n_bt * n_at > INT32_MAX) return false;   // grid size is an int
+  const int e = g.count++;
+  g.A[e] = static_cast<const bf16_t*>(A);
+  g.B[e] = static_cast<const bf16_t*>(B);
+  g.out[e] = out;
+  g.a_rows[e] = a_rows;
+  g.b_rows[e] = b_rows;
+  g.ldb[e] = ldb;
+  g.K[e] = K;
+  g.ldo[e] = ldo;
+  g.n_bt[e] = static_cast<int>(n_bt);
+  g.n_at[e] = static_cast<int>(n_at);
+  g.first[e + 1] = g.first[e] + g.n_bt[e] * g.n_at[e];
+  return true;
+}
+
+template <typename OutT>
+hipError_t launch_bwd_group(const BwdGroup& g, hipStream_t s) {
+  if (g.count == 0 || g.first[g.count] == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_gemm_kernel<OutT>), dim3(static_cast<unsigned>(g.first[g.count])),
+                     dim3(kPkThreads), 0, s, g);
+  return hipGetLastError();
+}
+
 template <typename OutT>
 hipError_t launch_bwd_gemm(const void* A, int a_rows, const void* B, int64_t b_rows, int64_t ldb,
                            int64_t K, OutT* out, int64_t ldo, hipStream_t s) {
-  if (b_rows == 0) return hipSuccess;
-  const int n_bt = static_cast<int>((b_rows + kPkBRows - 1) / kPkBRows);
-  const int n_at = (a_rows + kPkARows - 1) / kPkARows;
-  hipLaunchKernelGGL((bwd_gemm_kernel<OutT>), dim3(static_cast<unsigned>(n_bt) * n_at),
-                     dim3(kPkThreads), 0, s, static_cast<const bf16_t*>(A), a_rows,
-                     static_cast<const bf16_t*>(B), b_rows, ldb, K, out, ldo, n_bt, n_at);
-  return hipGetLastError();
+  BwdGroup g{};
+  if (!bwd_group_add(g, A, a_rows, B, b_rows, ldb, K, out, ldo)) return hipErrorInvalidValue;
+  return launch_bwd_group<OutT>(g, s);
 }
 
 template hipError_t launch_bwd_gemm<bf16_t>(const void*, int, const void*, int64_t, int64_t,
                                             int64_t, bf16_t*, int64_t, hipStream_t);
 template hipError_t launch_bwd_gemm<float>(const void*, int, const void*, int64_t, int64_t,
                                            int64_t, float*, int64_t, hipStream_t);
+template hipError_t launch_bwd_group<bf16_t>(const BwdGroup&, hipStream_t);
+template hipError_t launch_bwd_group<float>(const BwdGroup&, hipStream_t);
 
 }  // namespace nel

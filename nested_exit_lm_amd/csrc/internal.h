@@ -115,6 +115,21 @@ struct HeadBwdWs {
   size_t wt, ht, gt, total;
 };
 HeadBwdWs head_bwd_ws_layout(int64_t n, int vocab, int d);
+// A group of backward products out[b][a] = sum_k A[a][k] B[b][k] (one per
+// exit) for one launch; first[e] is the first workgroup id of product e.
+struct BwdGroup {
+  const uint16_t* A[kMaxExits];
+  const uint16_t* B[kMaxExits];
+  void* out[kMaxExits];
+  int64_t b_rows[kMaxExits], ldb[kMaxExits], K[kMaxExits], ldo[kMaxExits];
+  int a_rows[kMaxExits], n_bt[kMaxExits], n_at[kMaxExits];
+  int first[kMaxExits + 1];
+  int count;
+};
+bool bwd_group_add(BwdGroup& g, const void* A, int a_rows, const void* B, int64_t b_rows,
+                   int64_t ldb, int64_t K, void* out, int64_t ldo);
+template <typename OutT>
+hipError_t launch_bwd_group(const BwdGroup& g, hipStream_t s);
 // Tiled A operand of S^T for S [k_rows, R] row-major, K zero-padded to k_pad.
 hipError_t launch_pack_t(const void* S, int64_t k_rows, int R, int64_t k_pad, void* P,
                          hipStream_t s);

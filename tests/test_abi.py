@@ -20,7 +20,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = nel.load()
     syms = declared_symbols()
-    assert len(syms) == 22
+    assert len(syms) == 24
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -177,6 +177,39 @@ def test_head_backward_host_validation():
     assert call(g=None) == -1
     assert call(h=MIS) == -4
     assert call(dw=MIS) == -4
+    assert call(ws=None) == -5
+    assert call(wsb=need - 1) == -5
+
+
+def test_heads_backward_host_validation():
+    lib = nel.load()
+    d2 = _arr(ctypes.c_int32, 64, 128)
+    need = nel.heads_backward_workspace_size(100, 256, [64, 128])
+    assert need == (nel.head_backward_workspace_size(100, 256, 64)
+                    + nel.head_backward_workspace_size(100, 256, 128))
+    assert nel.heads_backward_workspace_size(100, 256, [64, 96]) == 0
+    assert lib.nel_heads_backward_workspace(0, 100, 256, d2) == 0
+    assert lib.nel_heads_backward_workspace(9, 100, 256, d2) == 0
+    assert lib.nel_heads_backward_workspace(2, 100, 256, None) == 0
+    p2 = _arr(ctypes.c_void_p, FAKE, FAKE)
+
+    def call(dt=1, E=2, n=100, V=256, d=d2, g=p2, h=p2, w=p2, dh=p2, dw=p2, ws=FAKE, wsb=need):
+        return lib.nel_heads_backward(dt, E, n, V, d, g, h, w, dh, dw, ws, wsb, None)
+
+    assert call(dt=0) == -3                 # bf16 only
+    assert call(E=0) == -1
+    assert call(E=9) == -1
+    assert call(d=None) == -1
+    assert call(V=250) == -2
+    assert call(d=_arr(ctypes.c_int32, 64, 100)) == -2
+    assert call(n=-1) == -2
+    assert call(dh=None, dw=None) == -1     # nothing to compute
+    assert call(g=None) == -1
+    assert call(h=_arr(ctypes.c_void_p, FAKE, None)) == -1
+    assert call(dw=_arr(ctypes.c_void_p, None, FAKE)) == -1
+    assert call(h=_arr(ctypes.c_void_p, FAKE, MIS)) == -4
+    assert call(dh=_arr(ctypes.c_void_p, MIS, FAKE)) == -4
+    assert call(ws=MIS) == -4
     assert call(ws=None) == -5
     assert call(wsb=need - 1) == -5
 

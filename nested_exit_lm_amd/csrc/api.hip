@@ -497,7 +497,6 @@ nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int3
   char* ws = static_cast<char*>(workspace);
   void* wt = ws + L.wt;
   void* ht = ws + L.ht;
-  void* gt = ws + L.gt;
   hipError_t err;
   if (dh) {
     err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack_t(w, vocab, d, vocab, wt, s); });
@@ -511,12 +510,11 @@ nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int3
   if (dw) {
     err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack_t(h, n_tokens, d, L.n_pad, ht, s); });
     if (err != hipSuccess) return from_hip(err);
-    err = timed(NEL_K_BWD_PACK, s,
-                [&] { return launch_transpose(dlogits, n_tokens, vocab, L.n_pad, gt, s); });
-    if (err != hipSuccess) return from_hip(err);
-    err = timed(NEL_K_BWD_DW, s, [&] {
-      return launch_bwd_gemm<float>(ht, d, gt, vocab, L.n_pad, L.n_pad, dw, d, s);
-    });
+    // G itself is the K-major B operand: no transposed copy
+    BwdGroup gw{};
+    if (!bwd_group_add(gw, ht, d, dlogits, vocab, vocab, L.n_pad, dw, d, n_tokens))
+      return NEL_ESHAPE;
+    err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float, true>(gw, s); });
     if (err != hipSuccess) return from_hip(err);
   }
   return NEL_OK;
@@ -583,19 +581,16 @@ nel_status nel_heads_backward(nel_dtype dt, int32_t n_exits, int64_t n_tokens, i
         return launch_pack_t(h[e], n_tokens, d[e], L.n_pad, base + L.ht, s);
       });
       if (err != hipSuccess) return from_hip(err);
-      err = timed(NEL_K_BWD_PACK, s, [&] {
-        return launch_transpose(dlogits[e], n_tokens, vocab, L.n_pad, base + L.gt, s);
-      });
-      if (err != hipSuccess) return from_hip(err);
-      if (!bwd_group_add(gw, base + L.ht, d[e], base + L.gt, vocab, L.n_pad, L.n_pad, dw[e], d[e]))
+      if (!bwd_group_add(gw, base + L.ht, d[e], dlogits[e], vocab, vocab, L.n_pad, dw[e], d[e],
+                         n_tokens))
         return NEL_ESHAPE;
     }
   }
   if (dh) {
-    err = timed(NEL_K_BWD_DH, s, [&] { return launch_bwd_group<bf16_t>(gh, s); });
+    err = timed(NEL_K_BWD_DH, s, [&] { return launch_bwd_group<bf16_t, false>(gh, s); });
     if (err != hipSuccess) return from_hip(err);
   }
-  if (dw) err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float>(gw, s); });
+  if (dw) err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float, true>(gw, s); });
   return from_hip(err);
 }
 

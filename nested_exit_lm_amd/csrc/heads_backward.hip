@@ -3,14 +3,16 @@
 // in its own head W^m in R^{V x D}), the chain rule gives
 //     dH = G W      [N x D] = sum over the vocabulary
 //     dW = G^T h    [V x D] = sum over the tokens.
-// Both run on the MFMA main loop of packed_core.h, whose A operand is
-// MFMA-tiled and whose B operand is row-major with K contiguous:
-//     dH:  A = W^T tiled (rows d, K = vocabulary),  B = G (rows tokens, K = vocabulary)
-//     dW:  A = h^T tiled (rows d, K = tokens),      B = G^T (rows vocabulary, K = tokens)
+// Both run on the MFMA main loops of packed_core.h, whose A operand is
+// MFMA-tiled:
+//     dH:  A = W^T tiled (rows d, K = vocabulary),  B = G row-major (rows tokens,
+//          K = vocabulary contiguous)
+//     dW:  A = h^T tiled (rows d, K = tokens),      B = G read K-major (rows
+//          vocabulary, K = tokens): staged in LDS as stored and transposed by
+//          the LDS fragment loads, so G is never copied
 // so each lane's accumulators are 16 consecutive d of one output row and the
 // stores are row-major.  W^T and h^T are written tiled by one transposing
-// pass each; G^T by one transpose (all three HBM-bound, into the workspace;
-// K is zero-padded to a multiple of 64).
+// pass each (HBM-bound, into the workspace; K zero-padded to a multiple of 64).
 #include <cstdint>
 
 #include "common.h"
@@ -67,39 +69,6 @@ __global__ __launch_bounds__(256) void pack_t_kernel(const bf16_t* __restrict__ 
   }
 }
 
-// G [n, V] -> G^T [V, n_pad] row-major, columns n..n_pad-1 zero (V % 64 == 0).
-// 64 x 64 tiles through LDS.
-__global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* __restrict__ G,
-                                                        bf16_t* __restrict__ GT, int64_t n,
-                                                        int vocab, int64_t n_pad, int v_tiles) {
-  __shared__ bf16_t tile[64][64 + 2];
-  const int tid = threadIdx.x;
-  const int vt = static_cast<int>(blockIdx.x % v_tiles);
-  const int64_t tt = blockIdx.x / v_tiles;
-  const int v0 = vt * 64;
-  const int64_t t0 = tt * 64;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = tid + 256 * j, row = i >> 3, ch = i & 7;   // row = token
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (t0 + row < n) v = *reinterpret_cast<const u32x4*>(G + (t0 + row) * vocab + v0 + ch * 8);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[row][ch * 8]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) dst[w] = v[w];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = tid + 256 * j, row = i >> 3, ch = i & 7;   // row = vocabulary entry
-    u32x4 v;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      v[w] = static_cast<uint32_t>(tile[ch * 8 + 2 * w][row]) |
-             (static_cast<uint32_t>(tile[ch * 8 + 2 * w + 1][row]) << 16);
-    *reinterpret_cast<u32x4*>(GT + (v0 + row) * n_pad + t0 + ch * 8) = v;
-  }
-}
-
 __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t count) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < count;
        i += static_cast<int64_t>(gridDim.x) * 256)
@@ -112,7 +81,7 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
 // launch covers a group of such products (the exits of a suite): workgroup
 // ids are split by the prefix sums `first` of the products' tile counts, so
 // one product's workgroups fill another's last partial round.
-template <typename OutT>
+template <typename OutT, bool KMAJOR>
 __global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
     BwdGroup /*read through the kernarg pointer*/) {
   // Per-product fields are read through the kernarg segment pointer, which
@@ -134,19 +103,27 @@ __global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
   const int64_t b0 = static_cast<int64_t>(bt) * kPkBRows;
   const int aw = at * kPkARows + wave * (NAB * 32);   // this wavefront's first A row
   const int rb0 = min(aw >> 5, a_rows / 32 - 1), rb1 = min((aw >> 5) + 1, a_rows / 32 - 1);
-  const PackedLanes pl = packed_lanes(tid);
-  uint32_t boff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t row = min(b0 + pl.brow + 32 * j, b_rows - 1) - b0;
-    boff[j] = static_cast<uint32_t>((row * ldb + pl.bchunk * 8) * 2);
-  }
   const char* Ab = reinterpret_cast<const char*>(A);
-  const char* Bb = reinterpret_cast<const char*>(B) + b0 * ldb * 2;
   f32x16 acc[NTB][NAB];
-  packed_tile_gemm<NTB, NAB>(acc, hs, Ab + static_cast<int64_t>(rb0) * 64 * K,
-                             Ab + static_cast<int64_t>(rb1) * 64 * K, Bb, boff, pl,
-                             static_cast<int>(K / kPkBK));
+  if constexpr (KMAJOR) {
+    const int cols = static_cast<int>(min(b_rows - b0, static_cast<int64_t>(kPkBRows)));
+    packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, Ab + static_cast<int64_t>(rb0) * 64 * K,
+                                      Ab + static_cast<int64_t>(rb1) * 64 * K,
+                                      reinterpret_cast<const char*>(B + b0), ldb, g.k_valid[e],
+                                      cols, static_cast<int>(K / kPkBK));
+  } else {
+    const PackedLanes pl = packed_lanes(tid);
+    uint32_t boff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t row = min(b0 + pl.brow + 32 * j, b_rows - 1) - b0;
+      boff[j] = static_cast<uint32_t>((row * ldb + pl.bchunk * 8) * 2);
+    }
+    const char* Bb = reinterpret_cast<const char*>(B) + b0 * ldb * 2;
+    packed_tile_gemm<NTB, NAB>(acc, hs, Ab + static_cast<int64_t>(rb0) * 64 * K,
+                               Ab + static_cast<int64_t>(rb1) * 64 * K, Bb, boff, pl,
+                               static_cast<int>(K / kPkBK));
+  }
   // Stores: a wave-uniform tile base and 32-bit lane offsets (the tile is
   // 128 rows of ldo elements, ldo < 2^24), so no 64-bit address per block
   // stays live across the main loop.
@@ -194,8 +171,7 @@ HeadBwdWs head_bwd_ws_layout(int64_t n, int vocab, int d) {
   L.n_pad = (n + kPkBK - 1) / kPkBK * kPkBK;
   L.wt = 0;
   L.ht = L.wt + up(sizeof(bf16_t) * static_cast<size_t>(vocab) * d);
-  L.gt = L.ht + up(sizeof(bf16_t) * static_cast<size_t>(L.n_pad) * d);
-  L.total = L.gt + up(sizeof(bf16_t) * static_cast<size_t>(L.n_pad) * vocab);
+  L.total = L.ht + up(sizeof(bf16_t) * static_cast<size_t>(L.n_pad) * d);
   return L;
 }
 
@@ -209,16 +185,6 @@ hipError_t launch_pack_t(const void* S, int64_t k_rows, int R, int64_t k_pad, vo
   return hipGetLastError();
 }
 
-hipError_t launch_transpose(const void* G, int64_t n, int vocab, int64_t n_pad, void* GT,
-                            hipStream_t s) {
-  const int v_tiles = vocab / 64;
-  const int64_t tiles = static_cast<int64_t>(v_tiles) * (n_pad / 64);
-  hipLaunchKernelGGL(transpose_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s,
-                     static_cast<const bf16_t*>(G), static_cast<bf16_t*>(GT), n, vocab, n_pad,
-                     v_tiles);
-  return hipGetLastError();
-}
-
 hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t s) {
   const int64_t blocks = (count + 255) / 256;
   hipLaunchKernelGGL(zero_f32_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
@@ -228,7 +194,7 @@ hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t s) {
 
 // Adds product (A, B) -> out to a group; false if the group is full.
 bool bwd_group_add(BwdGroup& g, const void* A, int a_rows, const void* B, int64_t b_rows,
-                   int64_t ldb, int64_t K, void* out, int64_t ldo) {
+                   int64_t ldb, int64_t K, void* out, int64_t ldo, int64_t k_valid) {
   if (b_rows == 0) return true;   // nothing to compute
   if (g.count >= kMaxExits) return false;
   const int64_t n_bt = (b_rows + kPkBRows - 1) / kPkBRows;
@@ -243,16 +209,17 @@ bool bwd_group_add(BwdGroup& g, const void* A, int a_rows, const void* B, int64_
   g.ldb[e] = ldb;
   g.K[e] = K;
   g.ldo[e] = ldo;
+  g.k_valid[e] = k_valid < 0 ? K : k_valid;
   g.n_bt[e] = static_cast<int>(n_bt);
   g.n_at[e] = static_cast<int>(n_at);
   g.first[e + 1] = g.first[e] + g.n_bt[e] * g.n_at[e];
   return true;
 }
 
-template <typename OutT>
+template <typename OutT, bool KMAJOR>
 hipError_t launch_bwd_group(const BwdGroup& g, hipStream_t s) {
   if (g.count == 0 || g.first[g.count] == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_gemm_kernel<OutT>), dim3(static_cast<unsigned>(g.first[g.count])),
+  hipLaunchKernelGGL((bwd_gemm_kernel<OutT, KMAJOR>), dim3(static_cast<unsigned>(g.first[g.count])),
                      dim3(kPkThreads), 0, s, g);
   return hipGetLastError();
 }
@@ -262,14 +229,15 @@ hipError_t launch_bwd_gemm(const void* A, int a_rows, const void* B, int64_t b_r
                            int64_t K, OutT* out, int64_t ldo, hipStream_t s) {
   BwdGroup g{};
   if (!bwd_group_add(g, A, a_rows, B, b_rows, ldb, K, out, ldo)) return hipErrorInvalidValue;
-  return launch_bwd_group<OutT>(g, s);
+  return launch_bwd_group<OutT, false>(g, s);
 }
 
 template hipError_t launch_bwd_gemm<bf16_t>(const void*, int, const void*, int64_t, int64_t,
                                             int64_t, bf16_t*, int64_t, hipStream_t);
 template hipError_t launch_bwd_gemm<float>(const void*, int, const void*, int64_t, int64_t,
                                            int64_t, float*, int64_t, hipStream_t);
-template hipError_t launch_bwd_group<bf16_t>(const BwdGroup&, hipStream_t);
-template hipError_t launch_bwd_group<float>(const BwdGroup&, hipStream_t);
+template hipError_t launch_bwd_group<bf16_t, false>(const BwdGroup&, hipStream_t);
+template hipError_t launch_bwd_group<float, false>(const BwdGroup&, hipStream_t);
+template hipError_t launch_bwd_group<float, true>(const BwdGroup&, hipStream_t);
 
 }  // namespace nel

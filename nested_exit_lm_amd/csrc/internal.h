@@ -109,10 +109,10 @@ hipError_t launch_junction_backward(int64_t n, int d_in, int d_out, int vocab, c
                                     void* workspace, int32_t* flags, hipStream_t s);
 
 // Workspace of the head backward (byte offsets): W^T and h^T in the tiled
-// layout, G^T row-major; K of the token dimension padded to n_pad.
+// layout; K of the token dimension padded to n_pad.
 struct HeadBwdWs {
   int64_t n_pad;
-  size_t wt, ht, gt, total;
+  size_t wt, ht, total;
 };
 HeadBwdWs head_bwd_ws_layout(int64_t n, int vocab, int d);
 // A group of backward products out[b][a] = sum_k A[a][k] B[b][k] (one per
@@ -122,20 +122,21 @@ struct BwdGroup {
   const uint16_t* B[kMaxExits];
   void* out[kMaxExits];
   int64_t b_rows[kMaxExits], ldb[kMaxExits], K[kMaxExits], ldo[kMaxExits];
+  int64_t k_valid[kMaxExits];   // K-major B: K rows that exist (the rest read as 0)
   int a_rows[kMaxExits], n_bt[kMaxExits], n_at[kMaxExits];
   int first[kMaxExits + 1];
   int count;
 };
 bool bwd_group_add(BwdGroup& g, const void* A, int a_rows, const void* B, int64_t b_rows,
-                   int64_t ldb, int64_t K, void* out, int64_t ldo);
-template <typename OutT>
+                   int64_t ldb, int64_t K, void* out, int64_t ldo, int64_t k_valid = -1);
+// KMAJOR: B(b, k) is element k * ldb + b of a row-major [K x ldb] matrix
+// (b_rows columns of it; K rows k_valid.. read as 0); else B is row-major
+// [b_rows x ldb] with K contiguous.
+template <typename OutT, bool KMAJOR>
 hipError_t launch_bwd_group(const BwdGroup& g, hipStream_t s);
 // Tiled A operand of S^T for S [k_rows, R] row-major, K zero-padded to k_pad.
 hipError_t launch_pack_t(const void* S, int64_t k_rows, int R, int64_t k_pad, void* P,
                          hipStream_t s);
-// G [n, V] -> G^T [V, n_pad], zero-padded.
-hipError_t launch_transpose(const void* G, int64_t n, int vocab, int64_t n_pad, void* GT,
-                            hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t s);
 // out[b][a] = sum_k A[a][k] B[b][k]; A tiled (a_rows x K), B row-major (b_rows x ldb).
 template <typename OutT>

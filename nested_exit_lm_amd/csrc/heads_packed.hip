@@ -170,18 +170,24 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
       }
       // (2) sums, teacher weights / shifted logits, label logit
       bf16_t* __restrict__ O = static_cast<bf16_t*>(ex.out[e]);
+      // The 16-bit copies leave through LDS, one 32-token block at a time: a
+      // lane holds 32 bytes of one token row, but the wavefront's 64 entries
+      // of a row are one aligned 128-byte line, so after a wave-local
+      // transpose eight lanes store a whole line (the MFMA lanes would write
+      // 32 rows x 2 pieces per store instead).  The wavefront uses its own
+      // 4 KB of the B stage, which no wavefront reads again before the barrier
+      // that ends this block.  Row r, 16-byte chunk c sits at slot
+      // 8 r + (c ^ ((r / 2) mod 8)): writes and reads cover all 64 banks.
+      char* const stage = reinterpret_cast<char*>(&hs[0][0]) + wave * 4096;
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
         const float ml = M[tb] * kLog2e;
         const int64_t tok = tq + 32 * tb;
-        const bool row_ok = tok < n;
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb) {
           // V is a multiple of 32, so a lane's 16 entries are all inside or all beyond V
           const int vbase = vlane + 32 * vb;
-          const bool ok = row_ok && vbase < vocab;
-          const int64_t off = tok * vocab + vbase;
           if (teacher) {
             u32x4 pk[2];
 #pragma unroll
@@ -192,11 +198,11 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
               s1 += x1;
               pk[r >> 3][(r >> 1) & 3] = pack_f16x2(x0, x1);
             }
-            if (ok) {
-              u32x4* dst = reinterpret_cast<u32x4*>(O + off);
-              dst[0] = pk[0];
-              dst[1] = pk[1];
-            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+              *reinterpret_cast<u32x4*>(stage +
+                                        (8 * q + ((4 * vb + 2 * hl + h2) ^ ((q >> 1) & 7))) * 16) =
+                  pk[h2];
           } else {
             u32x4 pk[2];
 #pragma unroll
@@ -207,11 +213,11 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
               pk[r >> 3][(r >> 1) & 3] = MODE == kModeLossF16 ? pack_f16x2(a0 - M[tb], a1 - M[tb])
                                                               : pack_bf16x2(a0 - M[tb], a1 - M[tb]);
             }
-            if (ok) {
-              u32x4* dst = reinterpret_cast<u32x4*>(O + off);
-              dst[0] = pk[0];
-              dst[1] = pk[1];
-            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+              *reinterpret_cast<u32x4*>(stage +
+                                        (8 * q + ((4 * vb + 2 * hl + h2) ^ ((q >> 1) & 7))) * 16) =
+                  pk[h2];
           }
           const int dd = ylab[tb] - vbase;
           if (static_cast<unsigned>(dd) < 16u && ylab[tb] < vocab) {
@@ -221,6 +227,23 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
             lab[static_cast<int64_t>(e) * n + tok] = val;
           }
         }
+        __builtin_amdgcn_wave_barrier();
+        {
+          // wave-uniform row base, 32-bit lane offsets (a block is 32 rows of 2 V bytes)
+          const int ch = lane & 7;
+          const uint32_t loff = (static_cast<uint32_t>(lane >> 3) * static_cast<uint32_t>(vocab) +
+                                 8u * static_cast<uint32_t>(ch)) * 2u;
+          const bool col_ok = vw + 8 * ch < vocab;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = 8 * j + (lane >> 3);
+            const u32x4 v =
+                *reinterpret_cast<const u32x4*>(stage + (8 * row + (ch ^ ((row >> 1) & 7))) * 16);
+            char* rb = reinterpret_cast<char*>(O) + ((t0 + 32 * tb + 8 * j) * vocab + vw) * 2;
+            if (col_ok && t0 + 32 * tb + row < n) *reinterpret_cast<u32x4*>(rb + loff) = v;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
         float s = s0 + s1;
         s += __shfl_xor(s, 32, 64);
         if (hl == 0) xsum[wave][tb * 32 + q][0] = s;

@@ -337,8 +337,8 @@ size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t d_in, int32_t d
  *   w:       device bf16 [vocab, d]        (the head, row-major, input)
  *   dh, dw:  device outputs, each may be NULL (not both); they must not alias
  *            the inputs or the workspace
- *   workspace: device, >= nel_head_backward_workspace() bytes (transposed and
- *            tiled copies of W, h and G)
+ *   workspace: device, >= nel_head_backward_workspace() bytes (the
+ *            transposed, MFMA-tiled copies of W and h; G is read in place)
  * Requires dt == NEL_BF16 (NEL_EDTYPE), vocab and d multiples of 64 and the
  * padded token count below 2^24 (NEL_ESHAPE).  n_tokens == 0 sets dw to 0.
  */
@@ -392,7 +392,7 @@ const char* nel_last_hip_error(void);
  * nel_timing_read sums their elapsed times per kernel.  Kernel ids:
  * 0 junction, 1 heads+loss statistics GEMM, 2 loss merge, 3 means,
  * 4 dlogits finalize, 5 heads+argmax GEMM, 6 argmax merge, 7 accept,
- * 8 weight packing, 9 head-backward operand transposes, 10 dH GEMM, 11 dW GEMM,
+ * 8 weight packing, 9 head-backward operand packs, 10 dH GEMM, 11 dW GEMM,
  * 12 junction backward, 13 sampled speculative verification.
  * Process-global and not thread-safe: for benchmarks only.
  */

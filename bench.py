@@ -295,7 +295,7 @@ def summarize_counters(fetch_dir, write_dir):
 
 def bench_backward(nel, torch, hs, ws, dl, args, ids=None, embs=None):
     """Backward of the three exit heads on the step's own logit gradients:
-    dh_m = G_m W^m (bf16) and dW^m = G_m^T h_m (fp32), with the operand transposes;
+    dh_m = G_m W^m (bf16) and dW^m = G_m^T h_m (fp32), with the W and h operand packs;
     and the backward of both junctions on seeded synthetic upstream gradients."""
     N, V = dl[0].shape
     D = [h.shape[1] for h in hs]

@@ -76,8 +76,8 @@ def cpu_baseline(s, seconds: float):
     chunk = 256
     while done < s.n_tokens:
         rows = np.arange(done, min(done + chunk, s.n_tokens))
-        oracle.junction(s.h[0][rows], s.ids[rows], s.emb[1])
-        oracle.junction(s.h[1][rows], s.ids[rows], s.emb[2])
+        for m in range(1, s.n_exits):
+            oracle.junction(s.h[m - 1][rows], s.ids[rows], s.emb[m])
         oracle.forward_tokens(s.h, s.w, s.labels, s.alpha, 1.0, rows=rows, chunk=chunk)
         done += len(rows)
         if time.perf_counter() - t0 > seconds:
@@ -85,7 +85,8 @@ def cpu_baseline(s, seconds: float):
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {done} of {s.n_tokens} tokens of the same batch (fp64 NumPy oracle: "
-                      f"both junctions, 3 heads, losses and dlogits), {el:.1f} s"}
+                      f"{s.n_exits - 1} junctions, {s.n_exits} heads, losses and dlogits), "
+                      f"{el:.1f} s"}
 
 
 def main():
@@ -104,6 +105,10 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB read + 1 GiB write kernel three times (the "
                          "reference that scales the HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line: one JSON line with the loss step of "
+                         "every training-shaped workload (tiny f32, 200M proxy, 500M/1.5B/3B, "
+                         "4 exits), the verify shape, and a bounded oracle sample for each")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="read the rocprofv3 FETCH_SIZE / WRITE_SIZE runs, write "
                          "profiles/traffic.json, and exit")
@@ -124,6 +129,9 @@ def main():
     nel.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        print(json.dumps({"sweep": bench_sweep(nel, torch, synth, dev, args)}), flush=True)
+        return
     log("[bench] generating inputs")
     s = synth.make_workload(WORKLOAD)
     N, V, D = s.n_tokens, s.vocab, s.widths
@@ -437,6 +445,90 @@ def bench_variants(nel, torch, hs, pw, labels, dl, wsb, mean, tok, alpha, args, 
     for name, mode in (("rescale", 0), ("no_rescale", 1), ("zero_fill", 2)):
         ms, jms = timed(lambda: nel.junction(hs[1], ids, embs[2], out=out, mode=mode), "junction")
         res["junction_2to3_" + name + "_ms"] = jms
+    return res
+
+
+def bench_sweep(nel, torch, synth, dev, args):
+    """The loss step (every junction, the weight packs, heads + loss + dlogits) of
+    workloads 0-3, timed like the benchmark line, with the per-kernel rates and a
+    bounded oracle sample; then the verify shape."""
+    res = []
+    for k in range(4):
+        s = synth.make_workload(k)
+        log(f"[sweep] workload {k} ({s.name})")
+        N, V, D, M = s.n_tokens, s.vocab, s.widths, s.n_exits
+        f32 = s.dtype == "f32"
+        es = 4 if f32 else 2
+
+        def td(a):
+            if f32:
+                return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+            return torch.from_numpy(synth.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        hs = [td(x) for x in s.h]
+        ws = [td(x) for x in s.w]
+        embs = [td(x) for x in s.emb]
+        ids = torch.from_numpy(s.ids).to(dev)
+        labels = torch.from_numpy(s.labels).to(dev)
+        js = [torch.empty(N, D[m], dtype=hs[0].dtype, device=dev) for m in range(1, M)]
+        pw = None if f32 else [torch.empty_like(w) for w in ws]
+        dl = [torch.empty(N, V, dtype=hs[0].dtype, device=dev) for _ in D]
+        mean = torch.empty(3 * M + 1, dtype=torch.float32, device=dev)
+        tok = torch.empty(M, 3, N, dtype=torch.float32, device=dev)
+        wsb = torch.zeros(nel.workspace_size(nel.OP_LOSS, M, N, V), dtype=torch.uint8, device=dev)
+
+        def step():
+            for m in range(1, M):
+                nel.junction(hs[m - 1], ids, embs[m], out=js[m - 1])
+            if f32:
+                nel.matryoshka_loss(hs, ws, labels, alpha_d=s.alpha, dlogits=dl, workspace=wsb,
+                                    mean_loss=mean, token_loss=tok)
+            else:
+                for w, p in zip(ws, pw):
+                    nel.pack_weights(w, out=p)
+                nel.matryoshka_loss_packed(hs, pw, labels, alpha_d=s.alpha, dlogits=dl,
+                                           workspace=wsb, mean_loss=mean, token_loss=tok)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        nel.timing_reset()
+        nel.timing_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        nel.timing_enable(False)
+
+        def avg(kname):
+            tot, cnt = nel.timing_read(kname)
+            return tot / max(cnt, 1)
+
+        jms, kms, fms = avg("junction"), avg("heads_loss"), avg("finalize")
+        jbytes = sum(es * (D[m - 1] + (D[m] - D[m - 1]) + D[m]) * N + 4 * N
+                     for m in range(1, M)) / (M - 1)                     # per junction launch
+        fbytes = 2 * M * N * V * es
+        flops = 2.0 * N * V * sum(D)
+        row = {"workload": s.name, "tokens": N, "widths": list(D), "vocab": V, "dtype": s.dtype,
+               "ms_per_step": ms, "tokens_per_s": N / (ms / 1e3),
+               "junction_ms": jms, "junction_gbs": jbytes / (jms / 1e3) / 1e9,
+               "heads_loss_ms": kms, "heads_loss_tflops": flops / (kms / 1e3) / 1e12,
+               "finalize_ms": fms, "finalize_gbs": fbytes / (fms / 1e3) / 1e9,
+               "merge_ms": avg("merge")}
+        row["junction_hbm_frac"] = row["junction_gbs"] / HBM_PEAK_GBS
+        row["heads_loss_mfma_frac"] = row["heads_loss_tflops"] / BF16_PEAK_TFLOPS
+        row["finalize_hbm_frac"] = row["finalize_gbs"] / HBM_PEAK_GBS
+        if not args.no_cpu_baseline:
+            row["cpu_baseline"] = cpu_baseline(s, args.cpu_seconds / 3)
+        res.append(row)
+        del hs, ws, embs, js, pw, dl, wsb
+        torch.cuda.empty_cache()
+    if not args.no_verify:
+        log("[sweep] verify shape")
+        v = bench_verify(nel, torch, synth, dev, args)
+        v["workload"] = "spec-verify-102x7"
+        res.append(v)
     return res
 
 

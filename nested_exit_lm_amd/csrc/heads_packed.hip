@@ -240,7 +240,9 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
             const u32x4 v =
                 *reinterpret_cast<const u32x4*>(stage + (8 * row + (ch ^ ((row >> 1) & 7))) * 16);
             char* rb = reinterpret_cast<char*>(O) + ((t0 + 32 * tb + 8 * j) * vocab + vw) * 2;
-            if (col_ok && t0 + 32 * tb + row < n) *reinterpret_cast<u32x4*>(rb + loff) = v;
+            // whole lines, not read again before the gradient pass: nontemporal
+            if (col_ok && t0 + 32 * tb + row < n)
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
           }
         }
         __builtin_amdgcn_wave_barrier();

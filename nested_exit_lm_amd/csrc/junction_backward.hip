@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void rowscan_kernel(int vocab, const int32_t* 
       seginfo[s0 + j] = make_int4(v, r0 + j * kSeg, r0 + min(c, (j + 1) * kSeg), ns > 1 ? p0 + j : -1);
     for (int j = 0; j < part_count(c); ++j) prow_id[p0 + j] = v;
   }
-  if (w == gridDim.x - 1 && tid == 0) {
+  if (w == static_cast<int>(gridDim.x) - 1 && tid == 0) {
     counts[0] = tot[1] + wt[1];
     counts[1] = tot[2] + wt[2];
   }

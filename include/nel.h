@@ -339,8 +339,9 @@ size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t d_in, int32_t d
  *            the inputs or the workspace
  *   workspace: device, >= nel_head_backward_workspace() bytes (the
  *            transposed, MFMA-tiled copies of W and h; G is read in place)
- * Requires dt == NEL_BF16 (NEL_EDTYPE), vocab and d multiples of 64 and the
- * padded token count below 2^24 (NEL_ESHAPE).  n_tokens == 0 sets dw to 0.
+ * Requires dt == NEL_BF16 (NEL_EDTYPE), vocab and d multiples of 64, d below
+ * 2^22 and the padded token count below 2^24 (NEL_ESHAPE).  n_tokens == 0
+ * sets dw to 0.
  */
 nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int32_t d,
                              const void* dlogits, const void* h, const void* w, void* dh,

@@ -462,7 +462,8 @@ nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, i
 // Shape rule of the head backward: bf16, V and d multiples of 64, and every
 // grid and 32-bit in-tile byte offset within range.
 static bool head_bwd_shape_ok(int64_t n, int32_t vocab, int32_t d) {
-  if (n < 0 || vocab < 64 || vocab % 64 != 0 || d < 64 || d % 64 != 0) return false;
+  if (n < 0 || vocab < 64 || vocab % 64 != 0 || d < 64 || d % 64 != 0 || d >= (1 << 22))
+    return false;
   const int64_t n_pad = (n + 63) / 64 * 64;
   if (n_pad >= (int64_t{1} << 24) || vocab >= (1 << 24)) return false;
   return (n_pad / 64) * (vocab / 64) < (int64_t{1} << 31) &&

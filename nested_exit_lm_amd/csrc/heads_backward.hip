@@ -124,29 +124,38 @@ __global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
                                Ab + static_cast<int64_t>(rb1) * 64 * K, Bb, boff, pl,
                                static_cast<int>(K / kPkBK));
   }
-  // Stores: a wave-uniform tile base and 32-bit lane offsets (the tile is
-  // 128 rows of ldo elements, ldo < 2^24), so no 64-bit address per block
-  // stays live across the main loop.
-  char* obase = reinterpret_cast<char*>(out) + b0 * ldo * static_cast<int64_t>(sizeof(OutT));
+  // Stores leave through a wave-local LDS transpose, one 32-row block at a
+  // time: a lane holds 16 consecutive outputs of one row, but the
+  // wavefront's 64 outputs of a row are whole 128-byte lines (bf16: one,
+  // fp32: two), so after the transpose each store instruction writes whole
+  // lines, nontemporal (nothing reads them back here).  The wavefront uses
+  // its own 8 KB of the B stage, free since the main loop's last barrier.
+  // Row r, 16-byte chunk c sits at slot CPR r + (c ^ swizzle(r)), CPR chunks
+  // per row; writes and reads then cover all 64 banks.  Addresses: a
+  // wave-uniform 64-bit row base and 32-bit lane offsets (the outputs' row
+  // length ldo is below 2^22).
+  constexpr int ES = sizeof(OutT);
+  constexpr int CPR = 64 * ES / 16;              // 16-byte chunks per row: 8 or 16
+  constexpr int RPS = 64 / CPR;                  // rows per wavefront store: 8 or 4
+  auto swz = [](int r) { return CPR == 8 ? (r >> 1) & 7 : r & 15; };
+  char* const stage = reinterpret_cast<char*>(&hs[0][0]) + wave * 8192;
+  const bool col_ok = aw < a_rows;               // a_rows % 64 == 0: all 64 columns or none
+  const int ch = lane % CPR;
+  const uint32_t loff = (static_cast<uint32_t>(lane / CPR) * static_cast<uint32_t>(ldo) +
+                         static_cast<uint32_t>(aw + ch * (16 / ES))) * ES;
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb) {
-    const int rloc = tb * 32 + q;
-    if (b0 + rloc >= b_rows) continue;
 #pragma unroll
     for (int ab = 0; ab < NAB; ++ab) {
-      const int a = aw + ab * 32 + 16 * hl;   // a_rows % 32 == 0: all 16 inside or all beyond
-      if (a >= a_rows) continue;
-      const uint32_t off = (static_cast<uint32_t>(rloc) * static_cast<uint32_t>(ldo) +
-                            static_cast<uint32_t>(a)) * static_cast<uint32_t>(sizeof(OutT));
-      u32x4* dst = reinterpret_cast<u32x4*>(obase + off);
-      if constexpr (sizeof(OutT) == 2) {
+      if constexpr (ES == 2) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           u32x4 pk;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             pk[j] = pack_bf16x2(acc[tb][ab][8 * h2 + 2 * j], acc[tb][ab][8 * h2 + 2 * j + 1]);
-          dst[h2] = pk;
+          const int c = 4 * ab + 2 * hl + h2;
+          *reinterpret_cast<u32x4*>(stage + (CPR * q + (c ^ swz(q))) * 16) = pk;
         }
       } else {
         // (+ 0.0f: storing the accumulators unchanged made the register
@@ -156,10 +165,22 @@ __global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
           u32x4 pk;
 #pragma unroll
           for (int j = 0; j < 4; ++j) pk[j] = __float_as_uint(acc[tb][ab][4 * h4 + j] + 0.0f);
-          dst[h4] = pk;
+          const int c = 8 * ab + 4 * hl + h4;
+          *reinterpret_cast<u32x4*>(stage + (CPR * q + (c ^ swz(q))) * 16) = pk;
         }
       }
     }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < 32 / RPS; ++j) {
+      const int row = RPS * j + lane / CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (CPR * row + (ch ^ swz(row))) * 16);
+      const int64_t r0 = b0 + 32 * tb + RPS * j;   // this store's first row
+      char* rb = static_cast<char*>(static_cast<void*>(out)) + r0 * ldo * ES;
+      if (col_ok && r0 + lane / CPR < b_rows)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 

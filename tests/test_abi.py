@@ -172,6 +172,7 @@ def test_head_backward_host_validation():
     assert call(dt=0) == -3                 # bf16 only
     assert call(V=250) == -2
     assert call(d=100) == -2
+    assert call(d=1 << 22) == -2            # output row offsets stay 32-bit within a tile
     assert call(n=-1) == -2
     assert call(dh=None, dw=None) == -1     # nothing to compute
     assert call(g=None) == -1

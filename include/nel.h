@@ -246,8 +246,8 @@ nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* 
 /*
  * nel_matryoshka_loss with every w[e] in the tiled layout of
  * nel_pack_weights.  Same arguments, outputs and errors, plus: dt must be
- * NEL_BF16 (NEL_EDTYPE), vocab % 32 == 0 and every d[e] % 64 == 0
- * (NEL_ESHAPE), and dlogits must be given (NEL_EINVAL): between the head GEMM
+ * NEL_BF16 (NEL_EDTYPE), vocab % 32 == 0 and every d[e] % 64 == 0 and
+ * below 2^24 (NEL_ESHAPE), and dlogits must be given (NEL_EINVAL): between the head GEMM
  * and the final gradient pass the dlogits buffers hold 16-bit scratch.  With
  * NEL_DIV_FORWARD the teacher's holds its softmax weights exp(l_M - m) (m the
  * 256-entry tile maximum) and the smaller exits' hold l - m, all fp16; the
@@ -265,7 +265,8 @@ nel_status nel_matryoshka_loss_packed(nel_dtype dt, int32_t n_exits, int64_t n_t
 
 /*
  * nel_exit_heads with every w[e] in the tiled layout of nel_pack_weights
- * (dt NEL_BF16, vocab % 32 == 0, every d[e] % 64 == 0; same outputs and errors).
+ * (dt NEL_BF16, vocab % 32 == 0, every d[e] % 64 == 0 and below 2^24; same
+ * outputs and errors).
  */
 nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
                                  const int32_t* d, const void* const* h,

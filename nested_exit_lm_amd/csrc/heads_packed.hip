@@ -343,7 +343,10 @@ hipError_t launch_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
 
 }  // namespace
 
-bool packed_shape_ok(int vocab, int d) { return vocab >= 32 && vocab % 32 == 0 && d >= 64 && d % 64 == 0; }
+// d below 2^24 keeps the 32-bit byte offsets of a 128-token slice of h in range.
+bool packed_shape_ok(int vocab, int d) {
+  return vocab >= 32 && vocab % 32 == 0 && d >= 64 && d % 64 == 0 && d < (1 << 24);
+}
 
 hipError_t launch_pack_weights(int vocab, int d, const void* w, void* packed, hipStream_t s) {
   const int64_t chunks = static_cast<int64_t>(vocab) * d / 8;

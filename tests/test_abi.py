@@ -156,6 +156,8 @@ def test_packed_host_validation():
     assert lib.nel_exit_heads_packed(1, 2, 4, 250, d2, p2, p2, None, FAKE, FAKE, need, None) == -2
     assert lib.nel_exit_heads_packed(1, 2, 4, 256, _arr(ctypes.c_int32, 64, 100), p2, p2, None,
                                      FAKE, FAKE, need, None) == -2
+    assert lib.nel_exit_heads_packed(1, 2, 4, 256, _arr(ctypes.c_int32, 64, 1 << 24), p2, p2,
+                                     None, FAKE, FAKE, need, None) == -2   # 32-bit slice offsets
 
 
 def test_head_backward_host_validation():

@@ -37,7 +37,7 @@ def log(msg):
 
 
 # Sources that make up the head GEMM whose HBM traffic the counter runs measured.
-GEMM_SOURCES = ("heads_packed.hip", "common.h", "tiles.h", "internal.h")
+GEMM_SOURCES = ("heads_packed.hip", "packed_core.h", "common.h", "tiles.h", "internal.h")
 
 
 def kernel_source_hash() -> str:

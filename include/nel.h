@@ -305,14 +305,13 @@ nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, i
                                  int32_t mode, void* dh, float* demb, int32_t* flags,
                                  void* workspace, size_t ws_bytes, void* stream);
 /*
- * Measurement aid (not a step of the method): the dense bf16 matrix-core rate
- * the device sustains on the given operand data.  The head GEMM's rate is
- * quoted against the published peak; on this chip the rate also depends on
- * the data multiplied (the clock drops under the power of toggling operands),
- * and this probe measures that ceiling with no memory traffic.  Each of the
+ * Measurement aid (not a step of the method): a register-only loop of bf16
+ * MFMAs on the given operand data, with no memory traffic.  Each of the
  * `blocks` workgroups (4 wavefronts) loads 8 operand pairs into registers
  * once, then issues iters x 8 MFMAs 32x32x16 (each 32768 flop per wavefront),
- * cycling through the pairs into four accumulator chains.
+ * cycling through the pairs into four accumulator chains.  Its rate is not a
+ * ceiling for the head GEMM: built into this library it reads lower than the
+ * same loop built as a standalone program.
  *   operands: device, 16 x 64 x 8 bf16 (pair s: A at block 2s, B at 2s + 1;
  *             64 lanes x 8 elements each), 16-byte aligned
  *   sink:     device fp32 [blocks * 4]: per wavefront, the sum of its

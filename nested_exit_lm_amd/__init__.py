@@ -3,7 +3,8 @@
 Argument marshalling only: every step runs in the HIP kernels behind the C
 ABI declared in ``include/nel.h``.  PyTorch supplies device memory and the
 current stream.  There is no fallback: if the library is not built, every
-call raises.
+call raises.  A call without a ``workspace`` argument uses a cached buffer of
+its own per operation, device and stream.
 
     junction(h, ids, emb)                      -> out
     exit_heads(hs, ws, want_logits, want_argmax) -> (logits | None, argmax | None)
@@ -13,6 +14,7 @@ call raises.
     pack_weights(w)                            -> w in the MFMA-tiled layout (bf16)
     matryoshka_loss_packed / exit_heads_packed -> as above, on packed weights
     head_backward(dlogits, h, w)               -> (dL/dh bf16, dL/dW fp32) of one exit head
+    heads_backward(dlogits, hs, ws)            -> ([dL/dh_m], [dL/dW_m]) of every exit, grouped
     junction_backward(h, ids, emb, dout)       -> (dL/dh, dL/demb fp32) of one junction
     speculative_verify(draft_logits, verify_logits, tokens, u_accept, u_next, draft_len)
                                                -> (beta, accepted, next_token)
@@ -28,7 +30,8 @@ __all__ = [
     "workspace_size", "read_flags", "clear_flags", "status_string", "timing_enable",
     "timing_read", "timing_reset", "KERNELS", "OP_LOSS", "OP_HEADS", "FLAG_BAD_ID",
     "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed", "head_backward",
-    "head_backward_workspace_size", "junction_backward", "speculative_verify",
+    "head_backward_workspace_size", "heads_backward", "heads_backward_workspace_size", "loss_workspace",
+    "junction_backward", "speculative_verify",
     "probe_mfma", "JUNCTION_RESCALE", "JUNCTION_NO_RESCALE", "JUNCTION_ZERO_FILL", "DIV_FORWARD",
     "DIV_REVERSE_KL", "DIV_JS", "DIV_TV",
 ]
@@ -201,7 +204,10 @@ _WS = {}
 
 
 def _workspace(op, device, nbytes):
-    ws = _WS.setdefault((op, str(device)), Workspace())
+    """The default workspace of an operation: one per (operation, device,
+    stream).  Calls on one stream run in issue order, so they can share it;
+    a call on another stream gets its own and cannot overwrite it mid-use."""
+    ws = _WS.setdefault((op, str(device), _stream(device)), Workspace())
     return ws.get(nbytes, device)
 
 
@@ -413,8 +419,6 @@ def head_backward_workspace_size(n_tokens: int, vocab: int, d: int) -> int:
     return int(load().nel_head_backward_workspace(n_tokens, vocab, d))
 
 
-_BWD_WS = Workspace()
-
 
 def head_backward(dlogits, h, w, want_dh: bool = True, want_dw: bool = True, dh=None, dw=None,
                   workspace=None):
@@ -438,7 +442,7 @@ def head_backward(dlogits, h, w, want_dh: bool = True, want_dw: bool = True, dh=
     if not want_dw:
         dw = None
     need = head_backward_workspace_size(n, V, d)
-    wsb = workspace if workspace is not None else _BWD_WS.get(need, device)
+    wsb = workspace if workspace is not None else _workspace("head_backward", device, need)
     _check(load().nel_head_backward(BF16, n, V, d, _dev(dlogits, device, "dlogits"),
                                     _dev(h, device, "h"), _dev(w, device, "w"),
                                     _dev(dh, device, "dh"), _dev(dw, device, "dw"),
@@ -484,7 +488,7 @@ def heads_backward(dlogits, hs, ws, want_dh: bool = True, want_dw: bool = True, 
         if lst is not None and len(lst) != M:
             raise ValueError(f"{name} needs one tensor per exit")
     need = heads_backward_workspace_size(n, V, widths)
-    wsb = workspace if workspace is not None else _BWD_WS.get(need, device)
+    wsb = workspace if workspace is not None else _workspace("head_backward", device, need)
     ds = (ctypes.c_int32 * M)(*widths)
     g = _ptrs([_dev(t, device, "dlogits") for t in dlogits])
     hp = _ptrs([_dev(t, device, "h") for t in hs])
@@ -495,8 +499,6 @@ def heads_backward(dlogits, hs, ws, want_dh: bool = True, want_dw: bool = True, 
                                      wsb.numel(), _stream(device)), "nel_heads_backward")
     return dhs, dws
 
-
-_JBWD_WS = Workspace()
 
 
 def junction_backward(h, ids, emb, dout, stop_grad: bool = False, want_dh: bool = True,
@@ -525,7 +527,7 @@ def junction_backward(h, ids, emb, dout, stop_grad: bool = False, want_dh: bool 
         demb = None
     lib = load()
     need = int(lib.nel_junction_backward_workspace(n, d_in, d_in + de, emb.shape[0]))
-    wsb = workspace if workspace is not None else _JBWD_WS.get(need, device)
+    wsb = workspace if workspace is not None else _workspace("junction_backward", device, need)
     _check(lib.nel_junction_backward(_dt(emb), n, d_in, d_in + de, emb.shape[0],
                                      _dev(h, device, "h"), _dev(ids, device, "ids"),
                                      _dev(emb, device, "emb"), _dev(dout, device, "dout"),
@@ -535,8 +537,6 @@ def junction_backward(h, ids, emb, dout, stop_grad: bool = False, want_dh: bool 
            "nel_junction_backward")
     return dh, demb
 
-
-_SPEC_WS = Workspace()
 
 
 def speculative_verify(draft_logits, verify_logits, draft_tokens, u_accept, u_next,
@@ -562,7 +562,7 @@ def speculative_verify(draft_logits, verify_logits, draft_tokens, u_accept, u_ne
     nxt = torch.empty(B, dtype=torch.int32, device=device)
     lib = load()
     need = int(lib.nel_speculative_workspace(B, draft_len))
-    wsb = workspace if workspace is not None else _SPEC_WS.get(need, device)
+    wsb = workspace if workspace is not None else _workspace("speculative", device, need)
     _check(lib.nel_speculative_verify(B, P, draft_len, V, _dev(draft_logits, device, "draft_logits"),
                                       _dev(verify_logits, device, "verify_logits"),
                                       _dev(draft_tokens, device, "draft_tokens"),

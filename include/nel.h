@@ -31,6 +31,12 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *     enqueued on it; no call synchronises except nel_read_device_flags and
  *     nel_timing_read.
+ *   - A workspace is in use until the call's work on `stream` has finished.
+ *     Calls that may run at the same time (on different streams) need
+ *     separate workspaces; calls on one stream may share one.  The library
+ *     keeps no device state between calls; its only host state is the
+ *     timing record (nel_timing_*), which is safe to use from several
+ *     threads, and the per-thread last HIP error.
  *   - Host-detectable errors are returned synchronously and nothing is
  *     launched.  Data errors found on the device (a token id or label outside
  *     [0, V)) set a bit in a device flag word (NEL_FLAG_*) and turn that

@@ -3,6 +3,7 @@
 // before enqueuing any work, so an error return means nothing was launched.
 #include <limits.h>
 #include <math.h>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -24,7 +25,7 @@ bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) !
 // ---------------------------------------------------------------- timing hooks
 struct Timing {
   std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};   // read without the lock on every launch
   struct Pending {
     int k;
     hipEvent_t a, b;
@@ -46,7 +47,7 @@ template <typename F>
 hipError_t timed(int k, hipStream_t s, F&& launch) {
   (void)hipGetLastError();
   Timing& T = timing();
-  if (!T.on) return launch();
+  if (!T.on.load(std::memory_order_relaxed)) return launch();
   hipEvent_t a, b;
   if (hipEventCreate(&a) != hipSuccess) return hipErrorUnknown;
   if (hipEventCreate(&b) != hipSuccess) {
@@ -612,7 +613,7 @@ nel_status nel_clear_device_flags(int32_t* dev_flags, void* stream) {
 }
 
 nel_status nel_timing_enable(int32_t on) {
-  timing().on = on != 0;
+  timing().on.store(on != 0, std::memory_order_relaxed);
   return NEL_OK;
 }
 

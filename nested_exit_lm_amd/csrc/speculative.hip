@@ -15,9 +15,10 @@
 //
 // Kernels: (1) per exit and position (a 1024-thread workgroup), the row
 // maximum, the softmax sum and the nucleus threshold, found exactly by a
-// 32-step bisection on order-preserving integer keys of the unnormalised
-// probabilities (every step a fixed-order workgroup reduction in fp64, so
-// every thread takes the same decision);
+// bisection on order-preserving integer keys of the unnormalised
+// probabilities (30 steps: the two top bits are fixed; every step a
+// fixed-order workgroup reduction in fp64, so every thread takes the same
+// decision);
 // (2) beta per drafted position; (3) per sequence, the acceptance chain and
 // the draw, whose running sums are fp64.  Probabilities themselves are fp32.
 // A row lives in registers (V <= kStatThreads x kPer).
@@ -80,6 +81,21 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   __syncthreads();
   return tree_sum<NW>(red);
 }
+// The same sum with one barrier instead of two, for a sequence of reductions
+// that alternate between two slot arrays: the barrier of one reduction also
+// orders every read of the other array (by the reduction before it) ahead of
+// the next write to it.
+template <int NW>
+__device__ __forceinline__ double block_sum_f64_alt(double v, double (&red)[2][NW], int& parity) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double* r = red[parity];
+  parity ^= 1;
+  if (lane == 0) r[wave] = v;
+  __syncthreads();
+  return tree_sum<NW>(r);
+}
 template <int NW = 4>
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
@@ -99,7 +115,8 @@ __global__ __launch_bounds__(kStatThreads) void nucleus_stats_kernel(
     int vocab, float inv_t, float top_p, float4* __restrict__ stats) {
   constexpr int NW = kStatThreads / 64;
   __shared__ float red[NW];
-  __shared__ double red64[NW];
+  __shared__ double red64[2][NW];
+  int parity = 0;
   const int tid = threadIdx.x;
   const int nrows = gridDim.x / 2;
   const int exit = blockIdx.x / nrows, r = blockIdx.x % nrows;   // r = b * rows_per_seq + i
@@ -134,16 +151,22 @@ __global__ __launch_bounds__(kStatThreads) void nucleus_stats_kernel(
   };
   // largest key K with mass(key >= K) >= top_p.  Each thread's 32 terms are
   // summed in fp32, the workgroup's 1024 partial sums in fp64.
-  const double s64 = block_sum_f64<NW>((sp[0] + sp[1]) + (sp[2] + sp[3]), red64);
+  const double s64 = block_sum_f64_alt<NW>((sp[0] + sp[1]) + (sp[2] + sp[3]), red64, parity);
   uint32_t K = 0;
   if (top_p < 1.f) {
     const double need = static_cast<double>(top_p) * s64;
-    for (int bit = 31; bit >= 0; --bit) {
+    // The two top bits are decided without a reduction.  Bit 31: every key
+    // has it (all values are >= 0), and the mass of all keys is s64 itself
+    // (the same fp32 terms added in the same order), which is >= need.
+    // Bit 30: keys with it hold values >= 2, and no value exceeds exp(0) = 1,
+    // so that mass is 0 < need.
+    K = 0x80000000u;
+    for (int bit = 29; bit >= 0; --bit) {
       const uint32_t cand = K | (1u << bit);
-      if (block_sum_f64<NW>(mass(cand), red64) >= need) K = cand;
+      if (block_sum_f64_alt<NW>(mass(cand), red64, parity) >= need) K = cand;
     }
   }
-  const float sn = static_cast<float>(block_sum_f64<NW>(mass(K), red64));
+  const float sn = static_cast<float>(block_sum_f64_alt<NW>(mass(K), red64, parity));
   if (tid == 0) stats[blockIdx.x] = make_float4(mx, sn, __uint_as_float(K), static_cast<float>(s64));
 }
 

@@ -110,7 +110,10 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 // sum_{kept} exp(l/T - max), threshold key (bits), softmax sum}.
 // Thread t holds entries t + kStatThreads j; each thread's sums run over four
 // interleaved partial sums (independent add chains) combined in a fixed order.
-__global__ __launch_bounds__(kStatThreads) void nucleus_stats_kernel(
+// Eight wavefronts per SIMD (64 registers per lane, a few values spilled) let
+// two workgroups share a CU, so one's reductions overlap the other's
+// arithmetic; measured faster than one workgroup per CU at 68 registers.
+__global__ __launch_bounds__(kStatThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void nucleus_stats_kernel(
     const float* __restrict__ draft, const float* __restrict__ verify, int positions, int rows_per_seq,
     int vocab, float inv_t, float top_p, float4* __restrict__ stats) {
   constexpr int NW = kStatThreads / 64;
@@ -131,22 +134,22 @@ __global__ __launch_bounds__(kStatThreads) void nucleus_stats_kernel(
     if (v < vocab) mx = fmaxf(mx, scaled(x[j], inv_t));
   }
   mx = block_max<NW>(mx, red);
-  // From here the row is held as order keys of the unnormalised probabilities
-  // (all >= 0, so the value is the key's low 31 bits).
-  uint32_t key[kPer];
+  // From here the row is held as its unnormalised probabilities, in place of
+  // the logits.  They are all >= 0, so their bit patterns order like their
+  // values, and the order key of a value is its bits with bit 31 set: a key
+  // K >= 2^31 selects the values whose bits are >= K - 2^31, and K = 0 all.
   float sp[4] = {0.f, 0.f, 0.f, 0.f};   // this thread's share of the softmax sum
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int v = tid + kStatThreads * j;
-    const float e = v < vocab ? unnorm(x[j], inv_t, mx) : 0.f;   // the unnormalised probability
-    key[j] = fkey(e);
-    sp[j & 3] += e;
+    x[j] = v < vocab ? unnorm(x[j], inv_t, mx) : 0.f;
+    sp[j & 3] += x[j];
   }
-  auto val = [](uint32_t k) { return __uint_as_float(k & 0x7fffffffu); };
   auto mass = [&](uint32_t K) {   // this thread's mass of keys >= K
+    const uint32_t lo = K & 0x7fffffffu;
     float m[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) m[j & 3] += key[j] >= K ? val(key[j]) : 0.f;
+    for (int j = 0; j < kPer; ++j) m[j & 3] += __float_as_uint(x[j]) >= lo ? x[j] : 0.f;
     return (m[0] + m[1]) + (m[2] + m[3]);
   };
   // largest key K with mass(key >= K) >= top_p.  Each thread's 32 terms are

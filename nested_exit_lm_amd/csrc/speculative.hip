@@ -20,7 +20,8 @@
 // fixed-order workgroup reduction in fp64, so every thread takes the same
 // decision);
 // (2) beta per drafted position; (3) per sequence, the acceptance chain and
-// the draw, whose running sums are fp64.  Probabilities themselves are fp32.
+// the draw from weights staged in LDS, whose running sums are fp64.
+// Probabilities themselves are fp32.
 // A row lives in registers (V <= kStatThreads x kPer).
 #include "common.h"
 #include "internal.h"
@@ -31,6 +32,7 @@ namespace {
 
 constexpr int kStatThreads = 1024;   // threads per row of the statistics kernel
 constexpr int kPer = 32;             // row entries per thread: V <= 32768
+constexpr int kMaxVocab = kStatThreads * kPer;
 
 // float -> uint32 with the same order (no NaNs)
 __device__ __forceinline__ uint32_t fkey(float x) {
@@ -190,9 +192,23 @@ __global__ __launch_bounds__(256) void beta_kernel(const float* __restrict__ dra
   const int r = b * rows_per_seq + i;
   const float4 sp = stats[r], sq = stats[nrows + r];
   const int64_t off = (static_cast<int64_t>(b) * positions + i) * vocab;
+  // eight entries per thread per round, their loads issued together; the
+  // sum runs over them in vocabulary order
   float acc = 0.f;
-  for (int v = threadIdx.x; v < vocab; v += 256)
-    acc += fminf(nprob(draft[off + v], inv_t, sp), nprob(verify[off + v], inv_t, sq));
+  for (int base = 0; base < vocab; base += 256 * 8) {
+    float dv[8], qv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int v = base + static_cast<int>(threadIdx.x) + 256 * u;
+      dv[u] = v < vocab ? draft[off + v] : 0.f;
+      qv[u] = v < vocab ? verify[off + v] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int v = base + static_cast<int>(threadIdx.x) + 256 * u;
+      if (v < vocab) acc += fminf(nprob(dv[u], inv_t, sp), nprob(qv[u], inv_t, sq));
+    }
+  }
   acc = block_sum(acc, red);
   if (threadIdx.x == 0) beta[blockIdx.x] = acc;
 }
@@ -229,23 +245,47 @@ __global__ __launch_bounds__(256) void accept_draw_kernel(
   // this thread's contiguous chunk of the vocabulary
   const int per = (vocab + 255) / 256;
   const int v0 = tid * per, v1 = min(v0 + per, vocab);
-  auto weight = [&](int v, bool res) {
-    const float q = nprob(verify[off + v], inv_t, sq);
-    return res ? fmaxf(q - nprob(draft[off + v], inv_t, sp), 0.f) : q;
+  // The row's weights are computed once, with coalesced reads, into LDS; one
+  // pad word per 128 entries keeps the chunk-wise reads below free of bank
+  // conflicts when chunks are 128 entries long (V = 32768).
+  __shared__ float wl[kMaxVocab + kMaxVocab / 128];
+  // eight entries per thread per round, their loads issued together
+  auto stage = [&](bool res) {
+    for (int base = 0; base < vocab; base += 256 * 8) {
+      float qv[8], dv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = base + tid + 256 * u;
+        qv[u] = v < vocab ? verify[off + v] : 0.f;
+        dv[u] = v < vocab && res ? draft[off + v] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = base + tid + 256 * u;
+        if (v < vocab) {
+          const float q = nprob(qv[u], inv_t, sq);
+          wl[v + (v >> 7)] = res ? fmaxf(q - nprob(dv[u], inv_t, sp), 0.f) : q;
+        }
+      }
+    }
+    __syncthreads();
   };
+  auto w_at = [&](int v) { return wl[v + (v >> 7)]; };
   // running sums of the draw in fp64: chunk sums, their exclusive prefix in
   // thread order, then the crossing inside the one chunk that holds it
   __shared__ double red64[4];
   __shared__ double excl[256];
+  __shared__ double red_lane[64];
   __shared__ double seq_total;
   __shared__ int firstpick, lastpos;
+  stage(residual);
   double part = 0.0;
-  for (int v = v0; v < v1; ++v) part += weight(v, residual);
-  bool res = residual;
+  for (int v = v0; v < v1; ++v) part += w_at(v);
   if (residual && !(block_sum_f64(part, red64) > 0.0)) {   // q == p on the nucleus: draw from q
-    res = false;
+    __syncthreads();
+    stage(false);
     part = 0.0;
-    for (int v = v0; v < v1; ++v) part += weight(v, false);
+    for (int v = v0; v < v1; ++v) part += w_at(v);
   }
   __syncthreads();
   excl[tid] = part;
@@ -254,14 +294,31 @@ __global__ __launch_bounds__(256) void accept_draw_kernel(
     lastpos = -1;
   }
   __syncthreads();
-  if (tid == 0) {
-    double run = 0.0;
-    for (int t = 0; t < 256; ++t) {
-      const double c = excl[t];
-      excl[t] = run;
-      run += c;
+  // exclusive prefix of the 256 chunk sums by wavefront 0: each lane adds
+  // four consecutive chunks in order, lane 0 runs over the 64 lane totals,
+  // each lane then offsets its four (a fixed order, so the result is
+  // reproducible)
+  if (tid < 64) {
+    const double c0 = excl[4 * tid], c1 = excl[4 * tid + 1], c2 = excl[4 * tid + 2],
+                 c3 = excl[4 * tid + 3];
+    const double s1 = c0 + c1, s2 = s1 + c2, s3 = s2 + c3;
+    red_lane[tid] = s3;
+    __builtin_amdgcn_wave_barrier();
+    if (tid == 0) {
+      double run = 0.0;
+      for (int t = 0; t < 64; ++t) {
+        const double c = red_lane[t];
+        red_lane[t] = run;
+        run += c;
+      }
+      seq_total = run;
     }
-    seq_total = run;
+    __builtin_amdgcn_wave_barrier();
+    const double base = red_lane[tid];
+    excl[4 * tid] = base;
+    excl[4 * tid + 1] = base + c0;
+    excl[4 * tid + 2] = base + s1;
+    excl[4 * tid + 3] = base + s2;
   }
   __syncthreads();
   const double target = static_cast<double>(u_next[b]) * seq_total;
@@ -270,7 +327,7 @@ __global__ __launch_bounds__(256) void accept_draw_kernel(
   double run = excl[tid];
   int pick = -1, last_pos = -1;
   for (int v = v0; v < v1; ++v) {
-    const float w = weight(v, res);
+    const float w = w_at(v);
     if (w > 0.f) last_pos = v;
     if (pick < 0 && w > 0.f && run + w > target) pick = v;
     run += w;

@@ -100,9 +100,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the head-backward sub-benchmark")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the sub-benchmark of the divergences and junction modes")
-    ap.add_argument("--no-probe", action="store_true",
+    ap.add_argument("--no-reference", "--no-probe", dest="no_reference", action="store_true",
                     help="skip the reference measurement: the vendor library's plain GEMM on "
-                         "the widest exit's shape")
+                         "the widest exit's shape (--no-probe is the older name)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB read + 1 GiB write kernel three times (the "
                          "reference that scales the HBM byte counters)")
@@ -240,7 +240,7 @@ def main():
         "end_to_end_mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
         "mean_loss": losses,
     }
-    if not args.no_probe:
+    if not args.no_reference:
         out["reference"] = bench_reference(torch, dev)
     if not args.no_verify:
         out["verify_102x7"] = bench_verify(nel, torch, synth, dev, args)

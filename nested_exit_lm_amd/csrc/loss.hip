@@ -164,6 +164,16 @@ struct DlPtrs {
 
 // Per entry of one token row, given the teacher's and a student's log-probs
 // (lp, lq) and probabilities (p, q): the divergence term d and q_v r_v.
+// log m, m = (p + q) / 2, for the Jensen-Shannon terms: from the
+// probabilities while their sum is a normal float (one logarithm), else from
+// the log-probabilities, which stays finite where both underflow.
+__device__ __forceinline__ float js_log_mix(float lp, float lq, float p, float q) {
+  const float s = p + q;
+  if (s >= 0x1p-100f) return flog(s) - kLn2;
+  const float hi = fmaxf(lp, lq), lo = fminf(lp, lq);
+  return hi + flog(1.f + fexp(lo - hi)) - kLn2;
+}
+
 template <int DIV>
 __device__ __forceinline__ void div_terms(float lp, float lq, float p, float q, float& d,
                                           float& qr) {
@@ -171,9 +181,7 @@ __device__ __forceinline__ void div_terms(float lp, float lq, float p, float q, 
     d = q * (lq - lp);   // r = log q - log p (+ 1, which K cancels)
     qr = d;
   } else if constexpr (DIV == kDivJS) {
-    // log m = log((p + q) / 2) from the log-probs, stable where p or q underflows
-    const float hi = fmaxf(lp, lq), lo = fminf(lp, lq);
-    const float lm = hi + flog(1.f + fexp(lo - hi)) - kLn2;
+    const float lm = js_log_mix(lp, lq, p, q);
     d = 0.5f * (p * (lp - lm) + q * (lq - lm));
     qr = 0.5f * q * (lq - lm);
   } else {   // kDivTV
@@ -187,8 +195,7 @@ __device__ __forceinline__ float div_r(float lp, float lq, float p, float q) {
   if constexpr (DIV == kDivReverseKL) {
     return lq - lp;
   } else if constexpr (DIV == kDivJS) {
-    const float hi = fmaxf(lp, lq), lo = fminf(lp, lq);
-    return 0.5f * (lq - (hi + flog(1.f + fexp(lo - hi)) - kLn2));
+    return 0.5f * (lq - js_log_mix(lp, lq, p, q));
   } else {
     return q > p ? 0.5f : (q < p ? -0.5f : 0.f);
   }

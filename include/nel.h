@@ -35,8 +35,8 @@
  *     Calls that may run at the same time (on different streams) need
  *     separate workspaces; calls on one stream may share one.  The library
  *     keeps no device state between calls; its only host state is the
- *     timing record (nel_timing_*), which is safe to use from several
- *     threads, and the per-thread last HIP error.
+ *     timing record (nel_timing_*, see there) and the per-thread last HIP
+ *     error.
  *   - Host-detectable errors are returned synchronously and nothing is
  *     launched.  Data errors found on the device (a token id or label outside
  *     [0, V)) set a bit in a device flag word (NEL_FLAG_*) and turn that
@@ -173,7 +173,14 @@ nel_status nel_accept_prefix(int32_t batch, int32_t positions, int32_t draft_len
  *   accepted, next_token: device int32 [batch]
  *   flags: NULL or device flag word: a drafted token outside [0, vocab) sets
  *       NEL_FLAG_BAD_ID and counts as rejected
- *   workspace: >= nel_speculative_workspace(batch, draft_len) bytes
+ *   workspace: >= nel_speculative_workspace(batch, draft_len) bytes.  When the
+ *       call's work has completed, its first 2 * batch * (draft_len + 1) fp32
+ *       quadruples hold the statistics of every row, the draft exit's first:
+ *       quadruple (x * batch + b) * (draft_len + 1) + i, x = 0 draft / 1 verify,
+ *       is {max_v fl(l_v / T), nucleus mass sum_{kept} e_v, the threshold (the
+ *       smallest e_v kept; 0 when top_p = 1), the softmax mass sum_v e_v},
+ *       with e_v = exp(fl(l_v / T) - max) in fp32 and entry v kept iff
+ *       e_v >= the threshold.  Nothing else is returned there.
  * Every decision is taken in fp32 from the given logits.  Requires
  * vocab <= 32768 (NEL_ESHAPE), temperature > 0 and 0 < top_p <= 1 (NEL_EINVAL).
  */
@@ -310,24 +317,6 @@ nel_status nel_junction_backward(nel_dtype dt, int64_t n_tokens, int32_t d_in, i
                                  const void* emb, const void* dout, int32_t stop_grad,
                                  int32_t mode, void* dh, float* demb, int32_t* flags,
                                  void* workspace, size_t ws_bytes, void* stream);
-/*
- * Measurement aid (not a step of the method): a register-only loop of bf16
- * MFMAs on the given operand data, with no memory traffic.  Each of the
- * `blocks` workgroups (4 wavefronts) loads 8 operand pairs into registers
- * once, then issues iters x 8 MFMAs 32x32x16 (each 32768 flop per wavefront),
- * cycling through the pairs into four accumulator chains.  Its rate is not a
- * ceiling for the head GEMM: built into this library it reads lower than the
- * same loop built as a standalone program.
- *   operands: device, 16 x 64 x 8 bf16 (pair s: A at block 2s, B at 2s + 1;
- *             64 lanes x 8 elements each), 16-byte aligned
- *   sink:     device fp32 [blocks * 4]: per wavefront, the sum of its
- *             accumulators (all-ones operands give 131072 x iters)
- * Time it with events on `stream`.  Errors: NEL_ESHAPE if iters or blocks < 1,
- * NEL_EINVAL for NULL pointers, NEL_EALIGN.
- */
-nel_status nel_probe_mfma(const void* operands, int32_t iters, int32_t blocks, float* sink,
-                          void* stream);
-
 /* Bytes of workspace nel_junction_backward needs (0 on bad arguments). */
 size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t d_in, int32_t d_out,
                                        int32_t vocab);
@@ -400,8 +389,10 @@ const char* nel_last_hip_error(void);
  * 0 junction, 1 heads+loss statistics GEMM, 2 loss merge, 3 means,
  * 4 dlogits finalize, 5 heads+argmax GEMM, 6 argmax merge, 7 accept,
  * 8 weight packing, 9 head-backward operand packs, 10 dH GEMM, 11 dW GEMM,
- * 12 junction backward, 13 sampled speculative verification.
- * Process-global and not thread-safe: for benchmarks only.
+ * 12 junction backward, 13 sampled speculative verification, 14 divergence pass.
+ * The record is process-global.  A lock guards it, so launching and reading
+ * from several threads is free of data races, but launches from every thread
+ * and stream are summed together: for benchmarks, with one thread launching.
  */
 enum { NEL_K_JUNCTION = 0, NEL_K_HEADS_LOSS = 1, NEL_K_MERGE = 2, NEL_K_MEANS = 3,
        NEL_K_FINALIZE = 4, NEL_K_HEADS_ARGMAX = 5, NEL_K_ARGMAX_MERGE = 6,

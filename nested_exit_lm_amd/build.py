@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnel.so")
 SOURCES = ["junction.hip", "junction_backward.hip", "heads_gemm.hip", "heads_packed.hip", "heads_backward.hip", "loss.hip",
-           "speculative.hip", "probe.hip", "api.hip"]
+           "speculative.hip", "api.hip"]
 ARCH = "gfx950"
 
 

@@ -416,15 +416,6 @@ nel_status nel_speculative_verify(int32_t batch, int32_t positions, int32_t draf
   }));
 }
 
-nel_status nel_probe_mfma(const void* operands, int32_t iters, int32_t blocks, float* sink,
-                          void* stream) {
-  if (iters < 1 || blocks < 1) return NEL_ESHAPE;
-  if (!operands || !sink) return NEL_EINVAL;
-  if (misaligned(operands) || misaligned4(sink)) return NEL_EALIGN;
-  return from_hip(launch_mfma_rate(operands, iters, blocks, sink,
-                                   static_cast<hipStream_t>(stream)));
-}
-
 size_t nel_junction_backward_workspace(int64_t n_tokens, int32_t d_in, int32_t d_out,
                                        int32_t vocab) {
   if (n_tokens < 0 || n_tokens > kJunctionBwdMaxTokens || d_in < 0 || d_out <= d_in || vocab < 1)

@@ -27,9 +27,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// fp16 <-> fp32 (round to nearest even).  The loss path keeps its 16-bit
+// scratch (tile-shifted logits l - m <= 0, teacher weights in [0, 1]) in fp16:
+// relative rounding 2^-11, three bits more than bf16, and the range of
+// l - m (down to -65504) is far beyond where exp(l - m) vanishes.
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const half2_t h = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // e^x and ln(x) through the base-2 hardware transcendentals.
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float flog(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
+
+// Makes this wavefront's LDS stores visible to its own later LDS loads of
+// other lanes' slots.  The wave barrier alone is treated by the compiler as
+// touching no memory, so it could forward a lane's own stored value to a load
+// of another lane's slot; wavefront-scope release/acquire fences around it
+// forbid that reordering.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -53,6 +80,25 @@ template <> struct Elem<float> {
   static constexpr int kChunk = 4;
   __device__ static float to_f32(float v) { return v; }
   __device__ static float from_f32(float v) { return v; }
+};
+
+// Codec of the loss path's per-entry scratch for element type T: fp16 bits
+// for bf16 inputs (see above), the fp32 value itself for fp32 inputs.  A
+// 16-byte chunk holds Elem<T>::kChunk entries either way.
+template <typename T> struct Scratch;
+template <> struct Scratch<bf16_t> {
+  __device__ static float get(const u32x4& r, int i) {
+    const uint32_t w = r[i >> 1];   // (a vector element through a scalar first)
+    return f16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xffffu));
+  }
+  __device__ static float load(const bf16_t* p) { return f16_bits_to_f32(*p); }
+  __device__ static bf16_t encode(float v) { return f32_to_f16_bits(v); }
+  __device__ static uint32_t pack2(float lo, float hi) { return pack_f16x2(lo, hi); }
+};
+template <> struct Scratch<float> {
+  __device__ static float get(const u32x4& r, int i) { return __uint_as_float(r[i]); }
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static float encode(float v) { return v; }
 };
 
 // Online (max, sum of exp) merge: (m, s) <- (m, s) (+) (m2, s2).

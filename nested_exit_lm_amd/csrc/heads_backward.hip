@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
         }
       }
     }
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < 32 / RPS; ++j) {
       const int row = RPS * j + lane / CPR;
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
       if (col_ok && r0 + lane / CPR < b_rows)
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
     }
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
   }
 }
 

@@ -14,8 +14,8 @@
 //     m    = max_v l          sigma = sum_v exp(l - m)
 //     S    = sum_v w_v l_m,v  (smaller exits: the teacher-weighted logit sum)
 //     l[y] (the label's logit, captured by the one lane that holds it)
-// and, when a gradient is wanted, the tile-shifted copy l - m (rounded once to
-// the caller's element type) into the caller's dlogits buffer.  A later pass
+// and, when a gradient is wanted, the tile-shifted copy l - m (rounded once:
+// fp16 for bf16 inputs, fp32 for fp32) into the caller's dlogits buffer.  A later pass
 // merges the tiles (online log-sum-exp) and finalises the gradient in place.
 //
 // Argmax epilogue: per token the tile's (max, lowest index), optionally the
@@ -286,7 +286,7 @@ __device__ __forceinline__ void loss_epilogue(f32x16 (&acc)[NTB][NVB], TW& wt_,
         lab[static_cast<int64_t>(e) * n + L.tok[tb]] = val;
       }
     }
-    // tile-shifted logits l - M into the gradient buffer
+    // tile-shifted logits l - M into the gradient buffer (codec Scratch<T>)
     if (out != nullptr && L.tok[tb] < n) {
       T* orow = static_cast<T*>(out) + L.tok[tb] * vocab;
 #pragma unroll
@@ -299,7 +299,7 @@ __device__ __forceinline__ void loss_epilogue(f32x16 (&acc)[NTB][NVB], TW& wt_,
               u32x4 pk;
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                pk[j] = pack_bf16x2(acc[tb][vb][8 * h2 + 2 * j] - m, acc[tb][vb][8 * h2 + 2 * j + 1] - m);
+                pk[j] = Scratch<T>::pack2(acc[tb][vb][8 * h2 + 2 * j] - m, acc[tb][vb][8 * h2 + 2 * j + 1] - m);
               dst[h2] = pk;
             }
           } else {
@@ -314,7 +314,7 @@ __device__ __forceinline__ void loss_epilogue(f32x16 (&acc)[NTB][NVB], TW& wt_,
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (L.vbase[vb] + r < vocab) orow[L.vbase[vb] + r] = Elem<T>::from_f32(acc[tb][vb][r] - m);
+            if (L.vbase[vb] + r < vocab) orow[L.vbase[vb] + r] = Scratch<T>::encode(acc[tb][vb][r] - m);
         }
       }
     }

@@ -25,12 +25,13 @@
 //
 // Loss epilogue: per (token, tile) the row maximum m, sum exp(l - m) and the
 // label's logit, and one 16-bit copy of the tile in the exit's gradient
-// buffer.  kModeLossF16 (the cross-entropy to the teacher): the teacher (last
-// exit, run first) stores its weights w = exp(l_M - m), the smaller exits
-// l - m, both fp16 (relative rounding 2^-11); the row-wise gradient pass
-// forms the teacher-weighted sums sum_v p_v l_m,v from them.  kModeLossPlain
-// (the other divergences, whose pass reads every exit's l - m) stores l - m
-// in bf16 for every exit.  No epilogue reads another exit's tile back.
+// buffer, in fp16 (relative rounding 2^-11).  kModeLossF16 (the
+// cross-entropy to the teacher): the teacher (last exit, run first) stores its
+// weights w = exp(l_M - m), the smaller exits l - m; the row-wise gradient
+// pass forms the teacher-weighted sums sum_v p_v l_m,v from them.
+// kModeLossPlain (the other divergences, whose pass reads every exit's
+// l - m) stores l - m for every exit.  No epilogue reads another exit's tile
+// back.
 #include <limits.h>
 
 #include "common.h"
@@ -45,13 +46,6 @@ namespace {
 constexpr int kPkTok = kPkBRows;   // tokens per workgroup (the B rows)
 constexpr int kPkVoc = kPkARows;   // vocabulary entries per workgroup (the A rows)
 constexpr int kPkGroup = 8;        // token tiles per tile group (see tile_coords)
-
-typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
-
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  const half2_t h = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
-  return __builtin_bit_cast(uint32_t, h);
-}
 
 // ---------------------------------------------------------------- packing
 // One thread per 16-byte chunk of W, visited as (row block rb, 64-column
@@ -210,8 +204,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
               const float a0 = acc[tb][vb][r], a1 = acc[tb][vb][r + 1];
               s0 += __builtin_amdgcn_exp2f(fmaf(a0, kLog2e, -ml));
               s1 += __builtin_amdgcn_exp2f(fmaf(a1, kLog2e, -ml));
-              pk[r >> 3][(r >> 1) & 3] = MODE == kModeLossF16 ? pack_f16x2(a0 - M[tb], a1 - M[tb])
-                                                              : pack_bf16x2(a0 - M[tb], a1 - M[tb]);
+              pk[r >> 3][(r >> 1) & 3] = pack_f16x2(a0 - M[tb], a1 - M[tb]);
             }
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
@@ -227,7 +220,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
             lab[static_cast<int64_t>(e) * n + tok] = val;
           }
         }
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
         {
           // wave-uniform row base, 32-bit lane offsets (a block is 32 rows of 2 V bytes)
           const int ch = lane & 7;
@@ -245,7 +238,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
               __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
           }
         }
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
         float s = s0 + s1;
         s += __shfl_xor(s, 32, 64);
         if (hl == 0) xsum[wave][tb * 32 + q][0] = s;
@@ -331,7 +324,6 @@ hipError_t launch_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
                          hipStream_t s) {
   info->vtile = kPkVoc;
   info->teacher_w16 = MODE == kModeLossF16;
-  info->student_f16 = MODE == kModeLossF16;
   if (n == 0) return hipSuccess;
   const int n_tt = static_cast<int>((n + kPkTok - 1) / kPkTok);
   const int n_vt = (vocab + kPkVoc - 1) / kPkVoc;

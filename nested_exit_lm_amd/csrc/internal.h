@@ -33,13 +33,12 @@ struct ExitSet {
 
 // What the head GEMM that ran tells the passes after it: the vocabulary
 // width of its statistics tiles, and whether the teacher's gradient buffer
-// holds fp16 teacher weights exp(l_M - m) and the smaller exits' fp16 l - m
-// (packed GEMM, cross-entropy to the teacher) rather than the tile-shifted
-// logits l - m in the element type.
+// holds its weights exp(l_M - m) (packed GEMM, cross-entropy to the teacher)
+// rather than its tile-shifted logits l - m.  Either way the scratch is in
+// the codec Scratch<T> of the element type (fp16 for bf16 inputs).
 struct TileInfo {
   int vtile = kVocTile;
   bool teacher_w16 = false;
-  bool student_f16 = false;   // the smaller exits' l - m in fp16 (not the element type)
 };
 
 inline int64_t n_vocab_tiles(int vocab) { return (vocab + kVocTile - 1) / kVocTile; }
@@ -204,10 +203,5 @@ hipError_t launch_argmax_merge(int n_exits, int64_t n, int vocab, int vtile, con
 hipError_t launch_accept(int batch, int positions, int draft_len, const int32_t* draft,
                          const int32_t* verify, int32_t* accepted, hipStream_t s);
 hipError_t launch_clear_flags(int32_t* flags, hipStream_t s);
-
-// Matrix-core rate probe: `blocks` workgroups of 4 wavefronts, each running
-// iters x 8 MFMAs (32x32x16 bf16) on the operand sets in `operands`.
-hipError_t launch_mfma_rate(const void* operands, int iters, int blocks, float* sink,
-                            hipStream_t s);
 
 }  // namespace nel

@@ -201,13 +201,6 @@ __device__ __forceinline__ float div_r(float lp, float lq, float p, float q) {
   }
 }
 
-__device__ __forceinline__ float elem_f32(const u32x4& r, int i, bf16_t) {
-  return __uint_as_float((i & 1) ? (r[i >> 1] & 0xffff0000u) : (r[i >> 1] << 16));
-}
-__device__ __forceinline__ float elem_f32(const u32x4& r, int i, float) {
-  return __uint_as_float(r[i]);
-}
-
 // One workgroup per token row (grid-stride): for every student e < M - 1,
 // dv[e][t] = D(p, q_e) and kv[e][t] = K, each a per-thread fp32 sum in
 // vocabulary order combined in a fixed tree.  The stored s are read, not
@@ -240,7 +233,7 @@ __global__ __launch_bounds__(256) void div_stats_kernel(int M, int64_t n, int vo
         float lp[C], p[C];
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-          lp[i] = elem_f32(tr, i, T{}) + oT;
+          lp[i] = Scratch<T>::get(tr, i) + oT;
           p[i] = fexp(lp[i]);
         }
 #pragma unroll
@@ -250,7 +243,7 @@ __global__ __launch_bounds__(256) void div_stats_kernel(int M, int64_t n, int vo
           const float oe = off(e, tile);
 #pragma unroll
           for (int i = 0; i < C; ++i) {
-            const float lq = elem_f32(sr, i, T{}) + oe;
+            const float lq = Scratch<T>::get(sr, i) + oe;
             float d, qr;
             div_terms<DIV>(lp[i], lq, p[i], fexp(lq), d, qr);
             D[e] += d;
@@ -261,10 +254,10 @@ __global__ __launch_bounds__(256) void div_stats_kernel(int M, int64_t n, int vo
     } else {
       for (int v = tid; v < vocab; v += 256) {
         const int tile = v / vtile;
-        const float lp = Elem<T>::to_f32(static_cast<const T*>(dl.p[M - 1])[t * vocab + v]) + off(M - 1, tile);
+        const float lp = Scratch<T>::load(static_cast<const T*>(dl.p[M - 1]) + t * vocab + v) + off(M - 1, tile);
         const float p = fexp(lp);
         for (int e = 0; e < S; ++e) {
-          const float lq = Elem<T>::to_f32(static_cast<const T*>(dl.p[e])[t * vocab + v]) + off(e, tile);
+          const float lq = Scratch<T>::load(static_cast<const T*>(dl.p[e]) + t * vocab + v) + off(e, tile);
           float d, qr;
           div_terms<DIV>(lp, lq, p, fexp(lq), d, qr);
           D[e] += d;
@@ -365,12 +358,7 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
                         lse[static_cast<int64_t>(e) * n + t];
 #pragma unroll
       for (int i = 0; i < C; ++i) {
-        float s;
-        if constexpr (sizeof(T) == 2)
-          s = __uint_as_float((i & 1) ? (traw[i >> 1] & 0xffff0000u) : (traw[i >> 1] << 16));
-        else
-          s = __uint_as_float(traw[i]);
-        lp[i] = s + off;
+        lp[i] = Scratch<T>::get(traw, i) + off;
         p[i] = fexp(lp[i]);
       }
     }
@@ -392,12 +380,7 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
         if (teacher) {
           val = p[i];
         } else {
-          float s;
-          if constexpr (sizeof(T) == 2)
-            s = __uint_as_float((i & 1) ? (raw[e][i >> 1] & 0xffff0000u) : (raw[e][i >> 1] << 16));
-          else
-            s = __uint_as_float(raw[e][i]);
-          const float lq = s + off;
+          const float lq = Scratch<T>::get(raw[e], i) + off;
           const float q = fexp(lq);
           if constexpr (DIV == kDivForward)
             val = q - alpha * p[i];
@@ -435,7 +418,6 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
                                                          const float* __restrict__ lse, DlPtrs dl,
                                                          int n_vt, float* __restrict__ dv,
                                                          ExitW lam) {
-  typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
   __shared__ float red[4][kMaxExits];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t plane = static_cast<int64_t>(n_vt) * n;
@@ -542,7 +524,7 @@ __global__ __launch_bounds__(256) void finalize_elem(int M, int64_t n, int vocab
     const bool bad = y < 0 || y >= vocab;
     const int eT = M - 1;
     T* pt = static_cast<T*>(dl.p[eT]) + i;
-    const float lp = Elem<T>::to_f32(*pt) +
+    const float lp = Scratch<T>::load(pt) +
                      stats[static_cast<int64_t>(eT) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
                      lse[static_cast<int64_t>(eT) * n + t];
     const float p = fexp(lp);
@@ -552,7 +534,7 @@ __global__ __launch_bounds__(256) void finalize_elem(int M, int64_t n, int vocab
       if (e == eT) {
         val = p - (v == y ? 1.f : 0.f);
       } else {
-        const float lq = Elem<T>::to_f32(*pe) +
+        const float lq = Scratch<T>::load(pe) +
                          stats[static_cast<int64_t>(e) * 3 * plane + static_cast<int64_t>(tile) * n + t] -
                          lse[static_cast<int64_t>(e) * n + t];
         const float q = fexp(lq);
@@ -643,7 +625,7 @@ hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInf
                                 const float* stats, const float* lse, void* const* dlogits,
                                 float* dv, const ExitW& lam, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (!info.teacher_w16 || !info.student_f16 || vocab % 8 != 0) return hipErrorInvalidValue;
+  if (!info.teacher_w16 || vocab % 8 != 0) return hipErrorInvalidValue;
   DlPtrs dl{};
   for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
   // one workgroup per row up to 65536 rows (grid-stride beyond)
@@ -664,8 +646,8 @@ hipError_t launch_divergence(int n_exits, int64_t n, int vocab, const TileInfo& 
                              void* const* dlogits, float* dv, float* kv, float* tokloss,
                              double* partials, const ExitW& lam, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (info.teacher_w16 || info.student_f16)
-    return hipErrorInvalidValue;   // needs every exit's shifted logits in the element type
+  if (info.teacher_w16)
+    return hipErrorInvalidValue;   // needs every exit's shifted logits
   DlPtrs dl{};
   for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
   const int n_vt = (vocab + info.vtile - 1) / info.vtile;
@@ -736,8 +718,8 @@ hipError_t launch_finalize(int n_exits, int64_t n, int vocab, const TileInfo& in
                            const float* stats, const float* lse, void* const* dlogits, int div,
                            const float* kv, const ExitW& lam, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (info.teacher_w16 || info.student_f16)
-    return hipErrorInvalidValue;   // fp16 scratch: finalize_rows reads it
+  if (info.teacher_w16)
+    return hipErrorInvalidValue;   // teacher weights: finalize_rows reads them
   DlPtrs dl{};
   for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
   switch (div) {

@@ -34,12 +34,6 @@ constexpr int kStatThreads = 1024;   // threads per row of the statistics kernel
 constexpr int kPer = 32;             // row entries per thread: V <= 32768
 constexpr int kMaxVocab = kStatThreads * kPer;
 
-// float -> uint32 with the same order (no NaNs)
-__device__ __forceinline__ uint32_t fkey(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // Unnormalised probability exp(l / T - max) of a raw logit.  Multiply and
 // subtract are kept separate (no contraction) so that every kernel derives
 // bit-identical values, and with them identical nucleus membership.
@@ -109,7 +103,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 }
 
 // Row statistics of one (exit, position): stats = {max of l/T, nucleus sum
-// sum_{kept} exp(l/T - max), threshold key (bits), softmax sum}.
+// sum_{kept} exp(l/T - max), threshold (the smallest kept value), softmax sum}.
 // Thread t holds entries t + kStatThreads j; each thread's sums run over four
 // interleaved partial sums (independent add chains) combined in a fixed order.
 // Eight wavefronts per SIMD (64 registers per lane, a few values spilled) let
@@ -172,13 +166,17 @@ __global__ __launch_bounds__(kStatThreads) __attribute__((amdgpu_waves_per_eu(8,
     }
   }
   const float sn = static_cast<float>(block_sum_f64_alt<NW>(mass(K), red64, parity));
-  if (tid == 0) stats[blockIdx.x] = make_float4(mx, sn, __uint_as_float(K), static_cast<float>(s64));
+  // the threshold as a value: the smallest kept e (K without its order bit;
+  // 0 keeps every entry when top_p = 1)
+  if (tid == 0)
+    stats[blockIdx.x] = make_float4(mx, sn, __uint_as_float(K & 0x7fffffffu), static_cast<float>(s64));
 }
 
 // Nucleus probability of entry value l (raw logit) under row stats st.
 __device__ __forceinline__ float nprob(float l, float inv_t, float4 st) {
   const float e = unnorm(l, inv_t, st.x);
-  return fkey(e) >= __float_as_uint(st.z) ? e / st.y : 0.f;
+  // e >= 0, so comparing bit patterns compares values
+  return __float_as_uint(e) >= __float_as_uint(st.z) ? e / st.y : 0.f;
 }
 
 __global__ __launch_bounds__(256) void beta_kernel(const float* __restrict__ draft,
@@ -303,7 +301,7 @@ __global__ __launch_bounds__(256) void accept_draw_kernel(
                  c3 = excl[4 * tid + 3];
     const double s1 = c0 + c1, s2 = s1 + c2, s3 = s2 + c3;
     red_lane[tid] = s3;
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     if (tid == 0) {
       double run = 0.0;
       for (int t = 0; t < 64; ++t) {
@@ -313,7 +311,7 @@ __global__ __launch_bounds__(256) void accept_draw_kernel(
       }
       seq_total = run;
     }
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     const double base = red_lane[tid];
     excl[4 * tid] = base;
     excl[4 * tid + 1] = base + c0;

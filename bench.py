@@ -62,18 +62,24 @@ def measured_traffic():
     return d.get("heads_loss_bytes_per_launch")
 
 
-def cpu_baseline(s, seconds: float):
-    """The oracle, as it stands, on a bounded sample of the same workload: the
-    first tokens of the batch, 256 at a time, until `seconds` have passed."""
-    import oracle
+def _blas_info():
+    """BLAS library NumPy calls (vendor, version, threads), via threadpoolctl."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": int(i.get("num_threads", 1))}
     except Exception:
-        threads = os.cpu_count()
+        pass
+    return {"vendor": None, "version": None, "threads": os.cpu_count()}
+
+
+def _oracle_rate(oracle, s, seconds, chunk=256):
+    """Tokens/s of the oracle's forward (junctions, heads, losses, dlogits) on
+    the first tokens of the batch, `chunk` at a time, until `seconds` pass."""
     done = 0
     t0 = time.perf_counter()
-    chunk = 256
     while done < s.n_tokens:
         rows = np.arange(done, min(done + chunk, s.n_tokens))
         for m in range(1, s.n_exits):
@@ -82,11 +88,55 @@ def cpu_baseline(s, seconds: float):
         done += len(rows)
         if time.perf_counter() - t0 > seconds:
             break
-    el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {done} of {s.n_tokens} tokens of the same batch (fp64 NumPy oracle: "
-                      f"{s.n_exits - 1} junctions, {s.n_exits} heads, losses and dlogits), "
-                      f"{el:.1f} s"}
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(s, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload: the
+    first tokens of the batch, 256 at a time, until `seconds` have passed; in
+    float64 (the parity oracle: `value`) and again in float32 (the same
+    definitions in single precision: `value_fp32`)."""
+    import oracle
+    blas = _blas_info()
+    done, el = _oracle_rate(oracle, s, seconds)
+    with oracle.working_precision(np.float32):
+        done32, el32 = _oracle_rate(oracle, s, seconds / 2)
+    return {"value": done / el, "unit": "tokens/s", "cores": blas["threads"], "kind": "oracle",
+            "value_fp32": done32 / el32, "host_cpus": os.cpu_count(), "blas": blas,
+            "sample": f"first {done} of {s.n_tokens} tokens of the same batch (NumPy oracle: "
+                      f"{s.n_exits - 1} junctions, {s.n_exits} heads, losses and dlogits) in float64, "
+                      f"{el:.1f} s; first {done32} tokens in float32, {el32:.1f} s; "
+                      f"{blas['threads']} BLAS threads ({blas['vendor']} {blas['version']}) "
+                      f"on {os.cpu_count()} host CPUs"}
+
+
+def junction_cold(nel, torch, dev, hs, ids, embs, j2, j3, jbytes, s, reps=10):
+    """Both junctions timed with a cold last-level cache: before each pair a
+    512 MiB buffer is overwritten, which evicts the 256 MB MALL, so the first
+    read of every embedding row comes from HBM.  Repeated rows of the Zipf ids
+    within one launch may still hit in the caches; `distinct_row_bytes` is the
+    traffic if every distinct embedding row were read exactly once."""
+    evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ms = []
+    for _ in range(reps):
+        evict.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        nel.junction(hs[0], ids, embs[1], out=j2)
+        nel.junction(hs[1], ids, embs[2], out=j3)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b) / 2)
+    ms.sort()
+    med = ms[len(ms) // 2]
+    D, N = s.widths, s.n_tokens
+    nd = len(np.unique(s.ids))
+    distinct = sum(2 * (D[m - 1] * N + (D[m] - D[m - 1]) * nd + D[m] * N) + 4 * N for m in (1, 2)) / 2
+    del evict
+    return {"cold_avg_ms": med, "cold_gbs": jbytes / 2 / (med / 1e3) / 1e9,
+            "cold_hbm_frac": jbytes / 2 / (med / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "distinct_ids": nd, "distinct_row_bytes": distinct,
+            "cold_gbs_distinct_rows": distinct / (med / 1e3) / 1e9}
 
 
 def main():
@@ -213,6 +263,7 @@ def main():
     mbytes = 4 * N * (2 * len(D) * n_vt + len(D) + 1 + len(D) + 3 * len(D))
     kern["merge"]["gbs"] = mbytes / (kern["merge"]["avg_ms"] / 1e3) / 1e9
     kern["merge"]["hbm_frac"] = kern["merge"]["gbs"] / HBM_PEAK_GBS
+    kern["junction"].update(junction_cold(nel, torch, dev, hs, ids, embs, j2, j3, jbytes, s))
     traffic = measured_traffic()
     losses = mean.cpu().numpy().tolist()
     out = {

@@ -8,13 +8,33 @@ definitions on a chosen subset of tokens (tokens are independent).
 """
 from __future__ import annotations
 
+import contextlib
 from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
+# Working precision of every definition below: float64 for all parity use.
+# The benchmark's CPU baseline also times the same definitions in float32
+# (``working_precision``); that changes the type the steps run in, not the
+# steps.
+_DTYPE = np.float64
 
-def _f64(x) -> np.ndarray:
-    return np.asarray(x, dtype=np.float64)
+
+def _real(x) -> np.ndarray:
+    return np.asarray(x, dtype=_DTYPE)
+
+
+@contextlib.contextmanager
+def working_precision(dtype):
+    """Run the definitions in ``dtype`` (np.float32 for the CPU speed
+    baseline) inside the block; float64 again afterwards."""
+    global _DTYPE
+    old = _DTYPE
+    _DTYPE = np.dtype(dtype).type
+    try:
+        yield
+    finally:
+        _DTYPE = old
 
 
 # ---------------------------------------------------------------------------
@@ -51,11 +71,11 @@ def junction(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray,
     h:   [N, D_in] (None or D_in == 0 for block 1); ids: [N] in [0, V);
     emb: [V, D_out - D_in].  Returns float64 [N, D_out].
     """
-    g = _f64(emb)[np.asarray(ids, dtype=np.int64)]
+    g = _real(emb)[np.asarray(ids, dtype=np.int64)]
     fill = np.zeros_like(g) if mode == JUNCTION_ZERO_FILL else g
     if h is None or np.asarray(h).shape[1] == 0:
         return fill
-    hf = _f64(h)
+    hf = _real(h)
     if mode == JUNCTION_NO_RESCALE:
         return np.concatenate([hf, g], axis=1)
     a = np.sqrt(np.sum(hf * hf, axis=1))
@@ -83,16 +103,16 @@ def junction_backward(h: Optional[np.ndarray], ids: np.ndarray, emb: np.ndarray,
     learns only from its own exit) treats h as a constant: dL/dh = 0, dL/dg
     unchanged.  Returns (dh or None when h is None, demb [V, d_out - d_in]).
     """
-    g = _f64(emb)[ids]
-    dout = _f64(dout)
+    g = _real(emb)[ids]
+    dout = _real(dout)
     d_in = 0 if h is None else h.shape[1]
     du, dg = dout[:, :d_in], dout[:, d_in:]
-    demb = np.zeros_like(_f64(emb))
+    demb = np.zeros_like(_real(emb))
     if mode != JUNCTION_ZERO_FILL:
         np.add.at(demb, ids, dg)
     if h is None:
         return None, demb
-    h = _f64(h)
+    h = _real(h)
     if mode == JUNCTION_NO_RESCALE:
         return (np.zeros_like(h) if stop_grad else du.copy()), demb
     a = np.linalg.norm(h, axis=1)
@@ -119,7 +139,7 @@ def heads(hs: Sequence[np.ndarray], ws: Sequence[np.ndarray]) -> List[np.ndarray
     own head W^m in R^{V x D_m}; the heads are not nested.  Reading: no bias,
     no final norm inside the op; logits are token-major [N, V].
     """
-    return [_f64(h) @ _f64(w).T for h, w in zip(hs, ws)]
+    return [_real(h) @ _real(w).T for h, w in zip(hs, ws)]
 
 
 def head_backward(g: np.ndarray, h: np.ndarray, w: np.ndarray):
@@ -130,8 +150,8 @@ def head_backward(g: np.ndarray, h: np.ndarray, w: np.ndarray):
     returns for that exit (the teacher's under stop-gradient).  Returns
     (dh [N, D], dw [V, D]).
     """
-    g64 = _f64(g)
-    return g64 @ _f64(w), g64.T @ _f64(h)
+    gr = _real(g)
+    return gr @ _real(w), gr.T @ _real(h)
 
 
 # ---------------------------------------------------------------------------
@@ -139,13 +159,13 @@ def head_backward(g: np.ndarray, h: np.ndarray, w: np.ndarray):
 # ---------------------------------------------------------------------------
 def logsumexp(l: np.ndarray) -> np.ndarray:
     """log sum_v exp(l_v) over the last axis, two passes with the max shift."""
-    l = _f64(l)
+    l = _real(l)
     mx = np.max(l, axis=-1, keepdims=True)
     return (mx + np.log(np.sum(np.exp(l - mx), axis=-1, keepdims=True)))[..., 0]
 
 
 def softmax(l: np.ndarray) -> np.ndarray:
-    l = _f64(l)
+    l = _real(l)
     return np.exp(l - logsumexp(l)[..., None])
 
 
@@ -174,7 +194,7 @@ def divergence(p: np.ndarray, q: np.ndarray, kind: int) -> np.ndarray:
         DIV_JS:         (KL(p || m) + KL(q || m)) / 2,  m = (p + q) / 2
         DIV_TV:         sum |p - q| / 2  =  1 - sum min(p, q)
     """
-    p, q = _f64(p), _f64(q)
+    p, q = _real(p), _real(q)
     if kind == DIV_FORWARD:
         return -np.sum(_xlogy(p, q), axis=-1)
     if kind == DIV_REVERSE_KL:
@@ -195,7 +215,7 @@ def divergence_grad(p: np.ndarray, q: np.ndarray, kind: int) -> np.ndarray:
         DIV_JS:         r = log(q / m) / 2
         DIV_TV:         r = sign(q - p) / 2      (0 where q = p)
     """
-    p, q = _f64(p), _f64(q)
+    p, q = _real(p), _real(q)
     if kind == DIV_FORWARD:
         return q - p
     if kind == DIV_REVERSE_KL:
@@ -236,9 +256,9 @@ def matryoshka_loss(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: flo
     M = len(logits)
     y = np.asarray(labels, dtype=np.int64)
     n = y.shape[0]
-    lam = np.ones(M) if exit_weights is None else _f64(exit_weights)
+    lam = np.ones(M) if exit_weights is None else _real(exit_weights)
     rows = np.arange(n)
-    ls = [_f64(l) for l in logits]
+    ls = [_real(l) for l in logits]
     lse = np.stack([logsumexp(l) for l in ls])                   # [M, N]
     ce = np.stack([lse[m] - ls[m][rows, y] for m in range(M)])   # [M, N]
     p = np.exp(ls[-1] - lse[-1][:, None])
@@ -273,7 +293,7 @@ def matryoshka_grad(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: flo
     """
     M = len(logits)
     y = np.asarray(labels, dtype=np.int64)
-    lam = np.ones(M) if exit_weights is None else _f64(exit_weights)
+    lam = np.ones(M) if exit_weights is None else _real(exit_weights)
     rows = np.arange(y.shape[0])
     p = softmax(logits[-1])
     out = []
@@ -297,7 +317,7 @@ def matryoshka_grad(logits: Sequence[np.ndarray], labels: np.ndarray, alpha: flo
 # ---------------------------------------------------------------------------
 def argmax_lowest(l: np.ndarray) -> np.ndarray:
     """Greedy token: index of the largest logit, the lowest index on ties."""
-    l = _f64(l)
+    l = _real(l)
     mx = np.max(l, axis=-1, keepdims=True)
     idx = np.arange(l.shape[-1])
     return np.min(np.where(l == mx, idx, l.shape[-1]), axis=-1).astype(np.int64)
@@ -335,7 +355,7 @@ def nucleus(l: np.ndarray, temperature: float = 1.0, top_p: float = 1.0) -> np.n
     that of the last entry needed is kept too, so the set does not depend on
     an ordering of equal values.  top_p >= 1 keeps everything.
     """
-    p = softmax(_f64(l) / temperature)
+    p = softmax(_real(l) / temperature)
     if top_p >= 1.0:
         return p
     flat = p.reshape(-1, p.shape[-1])
@@ -351,7 +371,7 @@ def nucleus(l: np.ndarray, temperature: float = 1.0, top_p: float = 1.0) -> np.n
 def sample_inverse_cdf(w: np.ndarray, u: float) -> int:
     """The entry v of weights w >= 0 (vocabulary order) where the running sum
     first exceeds u * sum(w); u in [0, 1).  Entries of weight 0 are never drawn."""
-    w = _f64(w)
+    w = _real(w)
     c = np.cumsum(w)
     v = int(np.searchsorted(c, u * c[-1], side="right"))
     nz = np.nonzero(w > 0)[0]
@@ -377,8 +397,8 @@ def speculative_verify(draft_logits: np.ndarray, verify_logits: np.ndarray,
     draft_logits, verify_logits: [B, P, V] with P >= draft_len + 1.
     Returns (beta [B, draft_len], accepted [B], next [B]).
     """
-    dl = _f64(draft_logits)
-    vl = _f64(verify_logits)
+    dl = _real(draft_logits)
+    vl = _real(verify_logits)
     B = dl.shape[0]
     beta = np.zeros((B, draft_len))
     acc = np.zeros(B, dtype=np.int64)

@@ -81,34 +81,53 @@ def test_bad_labels_give_nan_and_flag(nel):
     assert nel.read_flags(ws) == 0
 
 
-def test_student_equal_to_teacher_gives_teacher_entropy(nel):
-    """l_1 = l_2 exactly: W^2 = [W^1, 0] and h_2 = [h_1, noise]."""
-    s = synth.make_suite((128, 256), 3000, 2, 96, seed=54)
+def _loss_either(nel, ds, packed, hs=None, ws=None, alpha=0.3):
+    """(tok, dlogits) of the row-major or the packed (benchmarked) path."""
+    hs = ds.h if hs is None else hs
+    ws = ds.w if ws is None else ws
+    if packed:
+        _, tok, dl = nel.matryoshka_loss_packed(hs, [nel.pack_weights(w) for w in ws], ds.labels,
+                                                alpha_d=alpha)
+    else:
+        _, tok, dl = nel.matryoshka_loss(hs, ws, ds.labels, alpha_d=alpha)
+    return to_np(tok), dl
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["row-major", "packed"])
+def test_student_equal_to_teacher_gives_teacher_entropy(nel, packed):
+    """l_1 = l_2 exactly: W^2 = [W^1, 0] and h_2 = [h_1, noise].  On the packed
+    path Dist is formed from the fp16 teacher weights and fp16 l - m."""
+    V = 3008 if packed else 3000
+    s = synth.make_suite((128, 256), V, 2, 96, seed=54)
     s.w[1][:, :128] = s.w[0]
     s.w[1][:, 128:] = 0
     s.h[1][:, :128] = s.h[0]
     ds = DevSuite(s)
-    _, tok, _ = nel.matryoshka_loss(ds.h, ds.w, ds.labels, alpha_d=0.3)
-    tok = to_np(tok)
+    tok, _ = _loss_either(nel, ds, packed)
     l = oracle.heads([s.h[1]], [s.w[1]])[0]
     H = scipy.stats.entropy(scipy.special.softmax(l, axis=1), axis=1)
     assert_loss_close(tok[0, 1], H, 1e-3, "Dist vs entropy")
     np.testing.assert_allclose(tok[0, 0], tok[1, 0], rtol=1e-5)   # same CE
 
 
-def test_single_exit_and_alpha_zero_reduce_to_cross_entropy(nel):
-    import torch
+@pytest.mark.parametrize("packed", [False, True], ids=["row-major", "packed"])
+def test_single_exit_and_alpha_zero_reduce_to_cross_entropy(nel, packed):
     import torch.nn.functional as F
-    s = synth.make_suite((64, 96, 160), 1100, 1, 130, seed=55)
+    import torch
+    widths, V = ((64, 128, 192), 1120) if packed else ((64, 96, 160), 1100)
+    s = synth.make_suite(widths, V, 1, 130, seed=55)
     ds = DevSuite(s)
     for m in range(3):
-        _, tok, dl = nel.matryoshka_loss([ds.h[m]], [ds.w[m]], ds.labels, alpha_d=0.3)
+        tok, dl = _loss_either(nel, ds, packed, hs=[ds.h[m]], ws=[ds.w[m]])
         l = torch.from_numpy(oracle.heads([s.h[m]], [s.w[m]])[0])
         ce = F.cross_entropy(l, torch.from_numpy(s.labels).long(), reduction="none").numpy()
-        assert_loss_close(to_np(tok)[0, 0], ce, 1e-3, "M=1 CE")
-        assert_loss_close(to_np(tok)[0, 2], ce, 1e-3, "M=1 L")
-    _, tok, _ = nel.matryoshka_loss(ds.h, ds.w, ds.labels, alpha_d=0.0)
-    tok = to_np(tok)
+        assert_loss_close(tok[0, 0], ce, 1e-3, "M=1 CE")
+        assert_loss_close(tok[0, 2], ce, 1e-3, "M=1 L")
+        # the single exit's gradient is softmax - onehot (the teacher's, unmixed)
+        g = scipy.special.softmax(l.numpy(), axis=1)
+        g[np.arange(len(s.labels)), s.labels] -= 1.0
+        assert_grad_close(to_np(dl[0]), g, 2e-2, "M=1 dlogits")
+    tok, _ = _loss_either(nel, ds, packed, alpha=0.0)
     np.testing.assert_array_equal(tok[:, 2], tok[:, 0])
 
 

@@ -61,7 +61,8 @@ typedef enum {
   NEL_EDTYPE = -3,      /* unknown element type */
   NEL_EALIGN = -4,      /* a base pointer below its required alignment */
   NEL_EWORKSPACE = -5,  /* workspace NULL or smaller than nel_workspace_size() */
-  NEL_EHIP = -6         /* the HIP runtime reported an error at launch */
+  NEL_EHIP = -6,        /* the HIP runtime reported an error at launch */
+  NEL_ETOOLARGE = -7    /* beyond the fixed scratch of nel_exit_heads_packed_noalloc */
 } nel_status;
 
 typedef enum { NEL_F32 = 0, NEL_BF16 = 1 } nel_dtype;
@@ -285,6 +286,30 @@ nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens
                                  const int32_t* d, const void* const* h,
                                  const void* const* w_packed, float* const* logits,
                                  int32_t* argmax, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nel_exit_heads_packed for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, outputs and errors, without the workspace: the
+ * per-tile partial results live in a fixed device array of
+ * NEL_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  It calls no allocating routine (nor the timing
+ * hooks, which create events).  The caller still passes inputs and outputs.
+ *   - A request whose partial results exceed the array is NEL_ETOOLARGE (with
+ *     nothing launched): it needs 256 + 8 * n_exits * n_tokens * ceil(vocab / 128)
+ *     bytes, e.g. up to 4095 tokens for two exits at vocab 32768.
+ *   - Every call on one GPU shares that GPU's array, and nothing in it has to
+ *     start at zero (each call writes every value it reads).  Calls that
+ *     overlap on one GPU (other streams, other threads) race: serialise them.
+ *   - `stream` must belong to the current device (NEL_EINVAL otherwise).
+ *   - The array's device address is looked up on the first call on a device
+ *     (hipGetSymbolAddress, no allocation).
+ */
+enum { NEL_NOALLOC_SCRATCH_BYTES = 16 << 20 };
+nel_status nel_exit_heads_packed_noalloc(nel_dtype dt, int32_t n_exits, int64_t n_tokens,
+                                         int32_t vocab, const int32_t* d, const void* const* h,
+                                         const void* const* w_packed, float* const* logits,
+                                         int32_t* argmax, void* stream);
 
 /*
  * Backward of the junction (nel_junction).  With g = emb[ids[t]], a = ||h[t]||,

@@ -31,7 +31,7 @@ __all__ = [
     "timing_read", "timing_reset", "KERNELS", "OP_LOSS", "OP_HEADS", "FLAG_BAD_ID",
     "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed", "head_backward",
     "head_backward_workspace_size", "heads_backward", "heads_backward_workspace_size", "loss_workspace",
-    "junction_backward", "speculative_verify", "speculative_row_stats",
+    "junction_backward", "speculative_verify", "speculative_row_stats", "exit_heads_packed_noalloc",
     "JUNCTION_RESCALE", "JUNCTION_NO_RESCALE", "JUNCTION_ZERO_FILL", "DIV_FORWARD",
     "DIV_REVERSE_KL", "DIV_JS", "DIV_TV",
 ]
@@ -96,6 +96,7 @@ def load():
         "nel_junction": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, c_int, vp, vp],
         "nel_exit_heads": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
         "nel_exit_heads_packed": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp, vp, sz, vp],
+        "nel_exit_heads_packed_noalloc": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp, vp],
         "nel_pack_weights": [c_int, c_int, c_int, vp, vp, vp],
         "nel_accept_prefix": [c_int, c_int, c_int, vp, vp, vp, vp],
         "nel_matryoshka_loss": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, ctypes.c_float,
@@ -269,6 +270,43 @@ def _exit_heads(packed, hs, ws, want_logits, want_argmax, workspace):
     _check(fn(dt, E, n, V, d, _ptrs(hs), _ptrs(ws), _ptrs(logits) if logits is not None else None,
               _dev(am, device, "argmax"), wsb.data_ptr(), wsb.numel(), _stream(device)), name)
     return logits, am
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+ETOOLARGE = -7
+
+
+def exit_heads_packed_noalloc(hs: Sequence, ws_packed: Sequence, logits: Optional[List] = None,
+                              argmax=None):
+    """exit_heads_packed through the allocation-free entry point: the library
+    uses its fixed per-GPU scratch instead of a workspace, and every output is
+    the caller's (`logits`: None or a list of fp32 [n, V] tensors; `argmax`:
+    None or int32 [n_exits, n]).  Calls that overlap on one GPU race.
+    Returns (logits, argmax) as given."""
+    E = len(hs)
+    if E != len(ws_packed) or not 1 <= E <= MAX_EXITS:
+        raise ValueError("need 1..8 exits with one head each")
+    device = hs[0].device
+    n, V = hs[0].shape[0], ws_packed[0].shape[0]
+    for h, w in zip(hs, ws_packed):
+        if _dt(h) != BF16 or _dt(w) != BF16 or h.shape[0] != n or w.shape[0] != V or h.shape[1] != w.shape[1]:
+            raise ValueError("inconsistent exit shapes or dtypes (bf16 packed heads)")
+        _dev(h, device, "h")
+        _dev(w, device, "w")
+    if logits is not None:
+        if len(logits) != E:
+            raise ValueError("one logits tensor per exit")
+        for t in logits:
+            if tuple(t.shape) != (n, V) or t.dtype != _torch().float32:
+                raise ValueError("logits must be fp32 [n, V]")
+            _dev(t, device, "logits")
+    if argmax is not None and (tuple(argmax.shape) != (E, n) or argmax.dtype != _torch().int32):
+        raise ValueError("argmax must be int32 [n_exits, n]")
+    d = (ctypes.c_int32 * E)(*[h.shape[1] for h in hs])
+    _check(load().nel_exit_heads_packed_noalloc(
+        BF16, E, n, V, d, _ptrs(hs), _ptrs(ws_packed), _ptrs(logits) if logits is not None else None,
+        _dev(argmax, device, "argmax"), _stream(device)), "nel_exit_heads_packed_noalloc")
+    return logits, argmax
 
 
 def accept_prefix(draft_argmax, verify_argmax, draft_len: int):

@@ -110,6 +110,7 @@ const char* nel_status_string(nel_status s) {
     case NEL_EALIGN: return "pointer misaligned";
     case NEL_EWORKSPACE: return "workspace missing or too small";
     case NEL_EHIP: return "HIP runtime error";
+    case NEL_ETOOLARGE: return "request exceeds the fixed scratch of the allocation-free entry point";
   }
   return "unknown status";
 }
@@ -159,10 +160,12 @@ nel_status nel_accept_prefix(int32_t batch, int32_t positions, int32_t draft_len
 
 namespace {
 
-nel_status exit_heads_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_tokens,
-                           int32_t vocab, const int32_t* d, const void* const* h,
-                           const void* const* w, float* const* logits, int32_t* argmax,
-                           void* workspace, size_t ws_bytes, void* stream) {
+// Host validation of an exit-heads call (everything but the workspace); on
+// success *L is the workspace layout the call needs.
+nel_status exit_heads_check(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_tokens,
+                            int32_t vocab, const int32_t* d, const void* const* h,
+                            const void* const* w, float* const* logits, const int32_t* argmax,
+                            HeadsWs* L) {
   if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
   if (packed && dt != NEL_BF16) return NEL_EDTYPE;
   if (n_tokens < 0 || vocab < 1) return NEL_ESHAPE;
@@ -180,11 +183,19 @@ nel_status exit_heads_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n
       if (n_tokens > 0 && !logits[e]) return NEL_EINVAL;
       if (misaligned(logits[e])) return NEL_EALIGN;
     }
-  if (misaligned4(argmax) || misaligned(workspace)) return NEL_EALIGN;
-  const HeadsWs L = heads_ws_layout(n_exits, n_tokens, vocab);
-  if (!workspace || ws_bytes < L.total) return NEL_EWORKSPACE;
+  if (misaligned4(argmax)) return NEL_EALIGN;
+  *L = heads_ws_layout(n_exits, n_tokens, vocab);
+  return NEL_OK;
+}
+
+// The exit-heads kernels on a validated call, with `ws` (>= L.total bytes) as
+// the per-tile partial results.  hooks = false bypasses the timing hooks
+// (which create events).
+nel_status exit_heads_run(bool packed, bool hooks, nel_dtype dt, int32_t n_exits,
+                          int64_t n_tokens, int32_t vocab, const int32_t* d, const void* const* h,
+                          const void* const* w, float* const* logits, int32_t* argmax, char* ws,
+                          const HeadsWs& L, hipStream_t s) {
   if (n_tokens == 0 || (!logits && !argmax)) return NEL_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   ExitSet ex{};
   for (int e = 0; e < n_exits; ++e) {
     ex.h[e] = h[e];
@@ -192,10 +203,14 @@ nel_status exit_heads_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n
     ex.out[e] = logits ? logits[e] : nullptr;
     ex.d[e] = d[e];
   }
-  char* ws = static_cast<char*>(workspace);
   float* best = reinterpret_cast<float*>(ws + L.best);
   TileInfo info;
-  hipError_t err = timed(NEL_K_HEADS_ARGMAX, s, [&] {
+  auto run = [&](int k, auto&& launch) -> hipError_t {
+    if (hooks) return timed(k, s, launch);
+    (void)hipGetLastError();
+    return launch();
+  };
+  hipError_t err = run(NEL_K_HEADS_ARGMAX, [&] {
     if (packed) return launch_heads_argmax_packed(n_exits, n_tokens, vocab, ex, best, &info, s);
     return dt == NEL_BF16
                ? launch_heads_argmax<bf16_t>(n_exits, n_tokens, vocab, ex, best, &info, s)
@@ -203,11 +218,52 @@ nel_status exit_heads_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n
   });
   if (err != hipSuccess) return from_hip(err);
   if (argmax) {
-    err = timed(NEL_K_ARGMAX_MERGE, s, [&] {
+    err = run(NEL_K_ARGMAX_MERGE, [&] {
       return launch_argmax_merge(n_exits, n_tokens, vocab, info.vtile, best, argmax, s);
     });
   }
   return from_hip(err);
+}
+
+nel_status exit_heads_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_tokens,
+                           int32_t vocab, const int32_t* d, const void* const* h,
+                           const void* const* w, float* const* logits, int32_t* argmax,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  HeadsWs L;
+  const nel_status st =
+      exit_heads_check(packed, dt, n_exits, n_tokens, vocab, d, h, w, logits, argmax, &L);
+  if (st != NEL_OK) return st;
+  if (misaligned(workspace)) return NEL_EALIGN;
+  if (!workspace || ws_bytes < L.total) return NEL_EWORKSPACE;
+  return exit_heads_run(packed, true, dt, n_exits, n_tokens, vocab, d, h, w, logits, argmax,
+                        static_cast<char*>(workspace), L, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------ no-allocation
+// Scratch of nel_exit_heads_packed_noalloc: the per-tile partial results of
+// the argmax GEMM, in a fixed array that every device holds from module load
+// to process end.  Host code never uses `scratch` itself (in host code the
+// name is a stand-in, not a device address): each device's address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocScratchBytes = NEL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+// This device's address of `scratch` (looked up on the device's first call).
+hipError_t noalloc_scratch(int device, void** ptr) {
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,
@@ -334,6 +390,35 @@ nel_status nel_exit_heads(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32
                           size_t ws_bytes, void* stream) {
   return exit_heads_impl(false, dt, n_exits, n_tokens, vocab, d, h, w, logits, argmax, workspace,
                          ws_bytes, stream);
+}
+
+nel_status nel_exit_heads_packed_noalloc(nel_dtype dt, int32_t n_exits, int64_t n_tokens,
+                                         int32_t vocab, const int32_t* d, const void* const* h,
+                                         const void* const* w_packed, float* const* logits,
+                                         int32_t* argmax, void* stream) {
+  HeadsWs L;
+  const nel_status st =
+      exit_heads_check(true, dt, n_exits, n_tokens, vocab, d, h, w_packed, logits, argmax, &L);
+  if (st != NEL_OK) return st;
+  if (L.total > kNoAllocScratchBytes) return NEL_ETOOLARGE;
+  if (n_tokens == 0 || (!logits && !argmax)) return NEL_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e);
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return NEL_EINVAL;
+  if (s) {   // the scratch address below is the current device's
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return from_hip(e);
+    if (sdev != dev) return NEL_EINVAL;
+  }
+  void* ptr = nullptr;
+  e = noalloc_scratch(dev, &ptr);
+  if (e != hipSuccess) return from_hip(e);
+  return exit_heads_run(true, false, dt, n_exits, n_tokens, vocab, d, h, w_packed, logits, argmax,
+                        static_cast<char*>(ptr), L, s);
 }
 
 nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,

@@ -20,7 +20,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = nel.load()
     syms = declared_symbols()
-    assert len(syms) == 23
+    assert len(syms) == 24
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -150,6 +150,26 @@ def test_packed_host_validation():
                                      FAKE, FAKE, need, None) == -2
     assert lib.nel_exit_heads_packed(1, 2, 4, 256, _arr(ctypes.c_int32, 64, 1 << 24), p2, p2,
                                      None, FAKE, FAKE, need, None) == -2   # 32-bit slice offsets
+
+
+def test_noalloc_host_validation():
+    """The allocation-free exit heads: the same host checks as
+    nel_exit_heads_packed, and a request beyond the fixed scratch is refused
+    before any device call (this runs without a GPU)."""
+    lib = nel.load()
+    d2 = _arr(ctypes.c_int32, 64, 192)
+    p2 = _arr(ctypes.c_void_p, FAKE, FAKE)
+    f = lib.nel_exit_heads_packed_noalloc
+    assert f(0, 2, 4, 256, d2, p2, p2, None, FAKE, None) == -3
+    assert f(1, 2, 4, 250, d2, p2, p2, None, FAKE, None) == -2
+    assert f(1, 2, 4, 256, _arr(ctypes.c_int32, 64, 100), p2, p2, None, FAKE, None) == -2
+    assert f(1, 0, 4, 256, d2, p2, p2, None, FAKE, None) == -1
+    assert f(1, 2, 4, 256, d2, p2, p2, None, MIS4, None) == -4
+    # partial results need 256 + 8 n_exits n_tokens ceil(V / 128) bytes of 16 MiB
+    assert f(1, 2, 4096, 32768, d2, p2, p2, None, FAKE, None) == nel.ETOOLARGE
+    assert f(1, 2, 4, 256, d2, p2, p2, None, None, None) == 0      # nothing asked: nothing launched
+    assert f(1, 2, 0, 256, d2, p2, p2, None, FAKE, None) == 0      # no tokens
+    assert "fixed scratch" in nel.status_string(nel.ETOOLARGE)
 
 
 def test_head_backward_host_validation():

@@ -245,10 +245,9 @@ nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, 
  * rewritten once into the tiled layout below and then used by the *_packed
  * entry points, which compute exactly what their row-major counterparts do.
  * Requires dt == NEL_BF16, vocab % 32 == 0, d % 64 == 0.  The layout, for row
- * block rb < vocab/32, column pair block kp < d/16, lane l < 64, j < 8:
- *     packed[((rb * (d/16) + kp) * 64 + l) * 8 + j]
- *         = w[32 rb + vperm(l % 32)][16 kp + 8 (l / 32) + j],
- *     vperm(q) = 16 ((q >> 2) & 1) + 4 (q >> 3) + (q & 3).
+ * block rb < vocab/16, column block kb < d/32, lane l < 64, j < 8:
+ *     packed[((rb * (d/32) + kb) * 64 + l) * 8 + j] = w[16 rb + l % 16][32 kb + 8 (l / 16) + j]
+ * (one A operand of the 16x16x32 bf16 matrix instruction per 1 KB block).
  *   w:        device bf16 [vocab, d] (input)
  *   w_packed: device bf16, vocab * d elements (output; must not overlap w)
  * Errors: NEL_EDTYPE unless bf16; NEL_ESHAPE if vocab or d breaks the rule

@@ -6,22 +6,29 @@
 // ("Matryoshka Language Model Suites", distillation paragraph) or into a
 // per-tile greedy argmax; no fp32 logit tensor is written for the loss.
 //
-// Why a second weight layout.  A wavefront that keeps its whole vocabulary
-// slice of W in registers needs no LDS for W at all, which removes most of the
-// LDS traffic that limits an LDS-staged GEMM on this chip; but the MFMA
-// operand layout puts 32 different W rows in consecutive lanes, and such
-// strided row loads run at a third of the rate of contiguous ones.  So W is
-// first rewritten (nel_pack_weights, one HBM-bound pass) into 1 KB blocks
-// that are exactly one MFMA A operand each:
-//     block (rb, kp), rb < V/32, kp < D/16, at element offset (rb * D/16 + kp) * 512;
-//     lane l's 8 elements at l * 8 are W[32 rb + vperm(l % 32)][16 kp + 8 (l / 32) + j],
+// Instruction: v_mfma_f32_16x16x32_bf16.  With W as the row operand and h as
+// the column operand, lane l of a 16 x 16 block holds vocabulary rows
+// 4 (l / 16) + i, i < 4, of token column l % 16 (checked on the device), so
+// a lane's accumulator is four consecutive vocabulary entries of one token.
+// On this chip the 16x16x32 shape sustains about 9 % more than 32x32x16 with
+// the same operand traffic (main loop measured alone at the widest exit).
+//
+// Why a second weight layout.  A wavefront that keeps its vocabulary slice of
+// W in registers needs no LDS for W at all; but the matrix-core operand puts
+// 16 different W rows in consecutive lanes, and such strided row loads run at
+// a third of the rate of contiguous ones.  So W is first rewritten
+// (nel_pack_weights, one HBM-bound pass) into 1 KB blocks that are exactly one
+// A operand each:
+//     block (rb, kb), rb < V/16, kb < D/32, at element offset (rb * D/32 + kb) * 512;
+//     lane l's 8 elements at l * 8 are W[16 rb + l % 16][32 kb + 8 (l / 16) + j],
 // so every operand load is one contiguous 1 KB read.
 //
 // Workgroup: 4 wavefronts, tile 128 tokens x 256 vocabulary entries, two
-// workgroups per CU; the main loop (packed_core.h) streams W (the packed A
-// operand) straight into registers and stages the token slice of h (the B
-// operand) through LDS.  Wavefront w owns vocabulary entries [64w, 64w + 64)
-// of the tile for all 128 tokens (4 x 2 accumulator blocks of 32 x 32).
+// workgroups per CU.  Each K step (64) streams the wavefront's 8 W blocks
+// straight into registers, one step ahead, and stages the 128-token slice of
+// h through LDS (double-buffered).  Wavefront w owns vocabulary entries
+// [64 w, 64 w + 64) of the tile for all 128 tokens: 8 token blocks x 4
+// vocabulary blocks of 16 x 16.
 //
 // Loss epilogue: per (token, tile) the row maximum m, sum exp(l - m) and the
 // label's logit, and one 16-bit copy of the tile in the exit's gradient
@@ -43,30 +50,116 @@ namespace nel {
 
 namespace {
 
-constexpr int kPkTok = kPkBRows;   // tokens per workgroup (the B rows)
-constexpr int kPkVoc = kPkARows;   // vocabulary entries per workgroup (the A rows)
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kPkTok = kPkBRows;   // tokens per workgroup (the h rows)
+constexpr int kPkVoc = kPkARows;   // vocabulary entries per workgroup
 constexpr int kPkGroup = 8;        // token tiles per tile group (see tile_coords)
+constexpr int kNTB = 8;            // token blocks of 16 per wavefront
+constexpr int kNVB = 4;            // vocabulary blocks of 16 per wavefront
 
 // ---------------------------------------------------------------- packing
-// One thread per 16-byte chunk of W, visited as (row block rb, 64-column
-// group kc, row in block, chunk in the 128-byte row piece) with the chunk
-// fastest: the reads are whole 128-byte row pieces, the writes of a
-// workgroup fill four whole 1 KB blocks.
+// One workgroup per (16-row block rb, four 32-column blocks kb0 .. kb0 + 3):
+// thread i reads row i / 16, 16-byte chunk i % 16 of the 256-byte row piece
+// (whole rows per 16 lanes) and writes it to lane 16 (chunk % 4) + row of
+// block kb0 + chunk / 4 (the four 1 KB blocks are filled together).
 __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ w,
                                                    bf16_t* __restrict__ p, int vocab, int d) {
-  const int64_t chunks = static_cast<int64_t>(vocab) * d / 8;
-  const int cpr = d / 64;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < chunks;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t grp = i >> 8;
-    const int x = static_cast<int>(i & 255), row = x >> 3, ch = x & 7;
-    const int64_t rb = grp / cpr;
-    const int kc = static_cast<int>(grp - rb * cpr);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(w + (rb * 32 + row) * d + kc * 64 + ch * 8);
-    const int kp = kc * 4 + (ch >> 1);
-    const int l = (ch & 1) * 32 + vperm_inv(row);
-    *reinterpret_cast<u32x4*>(p + ((rb * (d / 16) + kp) * 64 + l) * 8) = v;
+  const int nkb = d / 32;
+  const int units_per_rb = (nkb + 3) / 4;
+  const int64_t units = static_cast<int64_t>(vocab / 16) * units_per_rb;
+  const int x = threadIdx.x >> 4, c16 = threadIdx.x & 15;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t rb = u / units_per_rb;
+    const int kb = static_cast<int>(u - rb * units_per_rb) * 4 + (c16 >> 2);
+    if (kb >= nkb) continue;
+    const int g = c16 & 3;
+    const u32x4 v =
+        *reinterpret_cast<const u32x4*>(w + (rb * 16 + x) * d + kb * 32 + g * 8);
+    *reinterpret_cast<u32x4*>(p + ((rb * nkb + kb) * 64 + 16 * g + x) * 8) = v;
   }
+}
+
+// ---------------------------------------------------------------- main loop
+// acc[tb][vb] += W(rows of vocabulary block vb) . h(token block tb) over
+// K = 64 nsteps.  Wb[vb]: byte base of the wavefront's packed row block vb;
+// Hb: byte base of the tile's h row 0; hoff: byte offsets (from Hb) of this
+// thread's four 16-byte h chunks (per step the base advances 128 bytes).
+// Every wavefront of the workgroup calls this together (it has barriers).
+__device__ __forceinline__ void packed16_tile_gemm(f32x4 (&acc)[kNTB][kNVB],
+                                                   u32x4 (&hs)[2][8 * kPkBRows],
+                                                   const char* const (&Wb)[kNVB],
+                                                   const char* __restrict__ Hb,
+                                                   const uint32_t (&hoff)[4], int hslot,
+                                                   int nsteps) {
+#pragma unroll
+  for (int tb = 0; tb < kNTB; ++tb)
+#pragma unroll
+    for (int vb = 0; vb < kNVB; ++vb) acc[tb][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
+  // LDS slot of token x, chunk 4 kh + g (block tb: + 16 tb): the stage holds
+  // token t, chunk c at 128 c + (t ^ 2 c), so each 16-lane pass of a fragment
+  // read covers 16 distinct bank groups
+  int fsl[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const int c = 4 * kh + g;
+    fsl[kh] = 128 * c + (x ^ (2 * c));
+  }
+  const uint32_t aoff = static_cast<uint32_t>(lane) * 16u;
+  u32x4 R0[kNVB][2], R1[kNVB][2], hr[4];
+  auto load_a = [&](u32x4 (&dst)[kNVB][2], int gs) {
+#pragma unroll
+    for (int vb = 0; vb < kNVB; ++vb)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+        dst[vb][kh] = *reinterpret_cast<const u32x4*>(Wb[vb] + static_cast<int64_t>(2 * gs + kh) * 1024 + aoff);
+  };
+  auto load_b = [&](int gs) {
+    const char* a = Hb + static_cast<int64_t>(gs) * (kPkBK * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hr[j] = *reinterpret_cast<const u32x4*>(a + hoff[j]);
+  };
+  auto store_b = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hs[st][hslot + 32 * j] = hr[j];
+  };
+  auto mfma = [&](const u32x4 (&cur)[kNVB][2], int st) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      bf16x8 b[kNTB];
+#pragma unroll
+      for (int tb = 0; tb < kNTB; ++tb) b[tb] = __builtin_bit_cast(bf16x8, hs[st][fsl[kh] + 16 * tb]);
+#pragma unroll
+      for (int vb = 0; vb < kNVB; ++vb) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, cur[vb][kh]);
+#pragma unroll
+        for (int tb = 0; tb < kNTB; ++tb)
+          acc[tb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[tb], acc[tb][vb], 0, 0, 0);
+      }
+    }
+  };
+  // step gs: prefetch step gs + 1 (the last step re-reads itself), compute
+  // step gs from LDS stage st, publish the prefetched h slice in stage st ^ 1
+  auto step = [&](const u32x4 (&cur)[kNVB][2], u32x4 (&nxt)[kNVB][2], int gs, int st) {
+    const int gn = gs + 1 < nsteps ? gs + 1 : gs;
+    load_b(gn);
+    load_a(nxt, gn);
+    mfma(cur, st);
+    store_b(st ^ 1);
+    __syncthreads();
+  };
+  load_b(0);
+  store_b(0);
+  load_a(R0, 0);
+  __syncthreads();
+  int gs = 0;
+  for (; gs + 2 <= nsteps; gs += 2) {
+    step(R0, R1, gs, 0);
+    step(R1, R0, gs + 1, 1);
+  }
+  if (gs < nsteps) step(R0, R1, gs, 0);
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -78,12 +171,11 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
   // The exit table is the first kernel argument; indexing it through the
   // kernarg segment pointer keeps per-exit lookups scalar.
   const ExitSet& ex = *(const ExitSet*)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int NTB = kPkNTB, NVB = kPkNAB;
   __shared__ u32x4 hs[2][8 * kPkTok];
   __shared__ float xmax[4][kPkTok];
   __shared__ float xsum[4][kPkTok][2];
 
-  const int tid = threadIdx.x, lane = tid & 63, q = lane & 31, hl = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, x = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Loss modes: every exit in one workgroup (the teacher first).  Argmax: one
   // exit per workgroup, the widest exit's tiles first, so that at small token
@@ -98,20 +190,22 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
   int tt, vt;
   tile_coords(bid, n_tt, n_vt, kPkGroup, tt, vt);
   const int64_t t0 = static_cast<int64_t>(tt) * kPkTok;
-  const int vw = vt * kPkVoc + wave * (NVB * 32);   // this wavefront's first vocabulary entry
-  const int64_t tq = t0 + q;                        // token of this lane in token block 0
+  const int vw = vt * kPkVoc + wave * 64;   // this wavefront's first vocabulary entry
+  const int vlane = vw + 4 * g;             // first of this lane's 4 entries in block 0
+  const int64_t tx = t0 + x;                // token of this lane in token block 0
 
-  int ylab[NTB];
+  int ylab[kNTB];
 #pragma unroll
-  for (int tb = 0; tb < NTB; ++tb)
-    ylab[tb] = (MODE != kModeArgmax && tq + tb * 32 < n) ? labels[tq + tb * 32] : -1;
-  const int vlane = vw + 16 * hl;   // first of this lane's 16 consecutive entries in block 0
-  // W row block of the loads for block 0 and block 1, clamped: rows beyond V are never stored
-  const int rb0 = min(vw >> 5, vocab / 32 - 1), rb1 = min((vw >> 5) + 1, vocab / 32 - 1);
+  for (int tb = 0; tb < kNTB; ++tb)
+    ylab[tb] = (MODE != kModeArgmax && tx + 16 * tb < n) ? labels[tx + 16 * tb] : -1;
   const PackedLanes pl = packed_lanes(tid);
   uint32_t hoff[4];   // byte offsets of this thread's h chunks from row t0 (rows beyond n clamped)
+  // packed row blocks of the wavefront's 4 vocabulary blocks, clamped: rows beyond V are never stored
+  int rbk[kNVB];
+#pragma unroll
+  for (int vb = 0; vb < kNVB; ++vb) rbk[vb] = min((vw >> 4) + vb, vocab / 16 - 1);
 
-  f32x16 acc[NTB][NVB];
+  f32x4 acc[kNTB][kNVB];
   for (int ei = ei0; ei < ei1; ++ei) {
     const int e = (MODE != kModeArgmax) ? (ei == 0 ? n_exits - 1 : ei - 1) : ei;
     const bool teacher = MODE == kModeLossF16 && ei == 0;
@@ -124,105 +218,100 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
       const int64_t row = min(t0 + pl.brow + 32 * j, n - 1) - t0;
       hoff[j] = static_cast<uint32_t>((row * D + pl.bchunk * 8) * 2);
     }
-    packed_tile_gemm<NTB, NVB>(acc, hs, P + static_cast<int64_t>(rb0) * 64 * D,
-                               P + static_cast<int64_t>(rb1) * 64 * D, Hb, hoff, pl, D / kPkBK);
+    const char* Wb[kNVB];
+#pragma unroll
+    for (int vb = 0; vb < kNVB; ++vb) Wb[vb] = P + static_cast<int64_t>(rbk[vb]) * D * 32;
+    packed16_tile_gemm(acc, hs, Wb, Hb, hoff, pl.hslot, D / kPkBK);
 
-    // vocabulary entries beyond V (last tile only) vanish under exp and never win a max
+    // vocabulary entries beyond V (last tile only) vanish under exp and never
+    // win a max; V is a multiple of 32, so a 16-block is wholly in or beyond V
     if (vt * kPkVoc + kPkVoc > vocab) {
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb)
+      for (int vb = 0; vb < kNVB; ++vb)
+        if (vw + 16 * vb >= vocab)
 #pragma unroll
-        for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (vlane + 32 * vb + r >= vocab) acc[tb][vb][r] = kMasked;
+          for (int tb = 0; tb < kNTB; ++tb) acc[tb][vb] = f32x4{kMasked, kMasked, kMasked, kMasked};
     }
 
     const int64_t plane = static_cast<int64_t>(n_vt) * n;
     if constexpr (MODE != kModeArgmax) {
-      // (1) row maximum over the tile's 256 entries: registers, lane 32 apart, 4 wavefronts
+      // (1) row maximum over the tile's 256 entries: a lane's 16, the four
+      // lane groups of its token (lanes 16 apart), then the 4 wavefronts
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        float m0 = acc[tb][0][0], m1 = acc[tb][0][1];
+      for (int tb = 0; tb < kNTB; ++tb) {
+        float m = acc[tb][0][0];
 #pragma unroll
-        for (int vb = 0; vb < NVB; ++vb)
+        for (int vb = 0; vb < kNVB; ++vb)
 #pragma unroll
-          for (int r = (vb == 0 ? 2 : 0); r < 16; r += 2) {
-            m0 = fmaxf(m0, acc[tb][vb][r]);
-            m1 = fmaxf(m1, acc[tb][vb][r + 1]);
-          }
-        float m = fmaxf(m0, m1);
+          for (int i = (vb == 0 ? 1 : 0); i < 4; ++i) m = fmaxf(m, acc[tb][vb][i]);
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
         m = fmaxf(m, __shfl_xor(m, 32, 64));
-        if (hl == 0) xmax[wave][tb * 32 + q] = m;
+        if (g == 0) xmax[wave][16 * tb + x] = m;
       }
       __syncthreads();
-      float M[NTB];
+      float M[kNTB];
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        const int j = tb * 32 + q;
+      for (int tb = 0; tb < kNTB; ++tb) {
+        const int j = 16 * tb + x;
         M[tb] = fmaxf(fmaxf(xmax[0][j], xmax[1][j]), fmaxf(xmax[2][j], xmax[3][j]));
       }
       // (2) sums, teacher weights / shifted logits, label logit
       bf16_t* __restrict__ O = static_cast<bf16_t*>(ex.out[e]);
-      // The 16-bit copies leave through LDS, one 32-token block at a time: a
-      // lane holds 32 bytes of one token row, but the wavefront's 64 entries
-      // of a row are one aligned 128-byte line, so after a wave-local
-      // transpose eight lanes store a whole line (the MFMA lanes would write
-      // 32 rows x 2 pieces per store instead).  The wavefront uses its own
-      // 4 KB of the B stage, which no wavefront reads again before the barrier
-      // that ends this block.  Row r, 16-byte chunk c sits at slot
-      // 8 r + (c ^ ((r / 2) mod 8)): writes and reads cover all 64 banks.
+      // The 16-bit copies leave through LDS, 32 tokens at a time: a lane holds
+      // four 8-byte pieces of one token row, but the wavefront's 64 entries of
+      // a row are one aligned 128-byte line, so after a wave-local transpose
+      // eight lanes store a whole line.  The wavefront uses its own 4 KB of the
+      // h stage, which no wavefront reads again before the barrier that ends
+      // this exit's epilogue.  Row r, 16-byte chunk c sits at slot
+      // 8 r + (c ^ ((r / 2) mod 8)): the 8-byte writes of a half wavefront and
+      // the 16-byte reads of 16 lanes each cover all 64 banks.
       char* const stage = reinterpret_cast<char*>(&hs[0][0]) + wave * 4096;
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        const float ml = M[tb] * kLog2e;
-        const int64_t tok = tq + 32 * tb;
-        float s0 = 0.f, s1 = 0.f;
+      for (int tp = 0; tp < kNTB / 2; ++tp) {
+        float s[2];
 #pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
-          // V is a multiple of 32, so a lane's 16 entries are all inside or all beyond V
-          const int vbase = vlane + 32 * vb;
-          if (teacher) {
-            u32x4 pk[2];
+        for (int u = 0; u < 2; ++u) {
+          const int tb = 2 * tp + u;
+          const float ml = M[tb] * kLog2e;
+          const int row = 16 * u + x;
+          float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              const float x0 = __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][r], kLog2e, -ml));
-              const float x1 = __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][r + 1], kLog2e, -ml));
-              s0 += x0;
-              s1 += x1;
-              pk[r >> 3][(r >> 1) & 3] = pack_f16x2(x0, x1);
+          for (int vb = 0; vb < kNVB; ++vb) {
+            uint32_t pk0, pk1;
+            if (teacher) {
+              float wv[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) wv[i] = __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i], kLog2e, -ml));
+              s0 += wv[0] + wv[2];
+              s1 += wv[1] + wv[3];
+              pk0 = pack_f16x2(wv[0], wv[1]);
+              pk1 = pack_f16x2(wv[2], wv[3]);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; i += 2) {
+                s0 += __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i], kLog2e, -ml));
+                s1 += __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i + 1], kLog2e, -ml));
+              }
+              pk0 = pack_f16x2(acc[tb][vb][0] - M[tb], acc[tb][vb][1] - M[tb]);
+              pk1 = pack_f16x2(acc[tb][vb][2] - M[tb], acc[tb][vb][3] - M[tb]);
             }
+            // entries 16 vb + 4 g .. + 3 of the row: chunk 2 vb + g / 2, half g % 2
+            const int c = 2 * vb + (g >> 1);
+            *reinterpret_cast<u32x2*>(stage + (8 * row + (c ^ ((row >> 1) & 7))) * 16 + 8 * (g & 1)) =
+                u32x2{pk0, pk1};
+            const int dd = ylab[tb] - (vlane + 16 * vb);
+            if (static_cast<unsigned>(dd) < 4u && ylab[tb] < vocab) {
+              float val = acc[tb][vb][0];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-              *reinterpret_cast<u32x4*>(stage +
-                                        (8 * q + ((4 * vb + 2 * hl + h2) ^ ((q >> 1) & 7))) * 16) =
-                  pk[h2];
-          } else {
-            u32x4 pk[2];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              const float a0 = acc[tb][vb][r], a1 = acc[tb][vb][r + 1];
-              s0 += __builtin_amdgcn_exp2f(fmaf(a0, kLog2e, -ml));
-              s1 += __builtin_amdgcn_exp2f(fmaf(a1, kLog2e, -ml));
-              pk[r >> 3][(r >> 1) & 3] = pack_f16x2(a0 - M[tb], a1 - M[tb]);
+              for (int i = 1; i < 4; ++i) val = (i == dd) ? acc[tb][vb][i] : val;
+              lab[static_cast<int64_t>(e) * n + tx + 16 * tb] = val;
             }
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-              *reinterpret_cast<u32x4*>(stage +
-                                        (8 * q + ((4 * vb + 2 * hl + h2) ^ ((q >> 1) & 7))) * 16) =
-                  pk[h2];
           }
-          const int dd = ylab[tb] - vbase;
-          if (static_cast<unsigned>(dd) < 16u && ylab[tb] < vocab) {
-            float val = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) val = (r == dd) ? acc[tb][vb][r] : val;
-            lab[static_cast<int64_t>(e) * n + tok] = val;
-          }
+          s[u] = s0 + s1;
         }
         wave_lds_sync();
         {
-          // wave-uniform row base, 32-bit lane offsets (a block is 32 rows of 2 V bytes)
+          // wave-uniform row base, 32-bit lane offsets (32 rows of 2 V bytes)
           const int ch = lane & 7;
           const uint32_t loff = (static_cast<uint32_t>(lane >> 3) * static_cast<uint32_t>(vocab) +
                                  8u * static_cast<uint32_t>(ch)) * 2u;
@@ -232,75 +321,73 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
             const int row = 8 * j + (lane >> 3);
             const u32x4 v =
                 *reinterpret_cast<const u32x4*>(stage + (8 * row + (ch ^ ((row >> 1) & 7))) * 16);
-            char* rb = reinterpret_cast<char*>(O) + ((t0 + 32 * tb + 8 * j) * vocab + vw) * 2;
+            char* rb = reinterpret_cast<char*>(O) + ((t0 + 32 * tp + 8 * j) * vocab + vw) * 2;
             // whole lines, not read again before the gradient pass: nontemporal
-            if (col_ok && t0 + 32 * tb + row < n)
+            if (col_ok && t0 + 32 * tp + row < n)
               __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
           }
         }
         wave_lds_sync();
-        float s = s0 + s1;
-        s += __shfl_xor(s, 32, 64);
-        if (hl == 0) xsum[wave][tb * 32 + q][0] = s;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float t = s[u];
+          t += __shfl_xor(t, 16, 64);
+          t += __shfl_xor(t, 32, 64);
+          if (g == 0) xsum[wave][32 * tp + 16 * u + x][0] = t;
+        }
       }
       __syncthreads();
-      // (3) wavefront w writes the statistics of token block w
-      float Mw = M[0];
-#pragma unroll
-      for (int tb = 1; tb < NTB; ++tb) Mw = (tb == wave) ? M[tb] : Mw;
-      const int j = wave * 32 + q;
-      const int64_t tk = t0 + j;
-      if (hl == 0 && tk < n) {
-        float* st = stats + (static_cast<int64_t>(e) * 3 * n_vt + vt) * n + tk;
-        st[0] = Mw;
+      // (3) thread j < 128 writes the statistics of token j
+      if (tid < kPkTok && t0 + tid < n) {
+        const int j = tid;
+        float* st = stats + (static_cast<int64_t>(e) * 3 * n_vt + vt) * n + t0 + j;
+        st[0] = fmaxf(fmaxf(xmax[0][j], xmax[1][j]), fmaxf(xmax[2][j], xmax[3][j]));
         st[plane] = (xsum[0][j][0] + xsum[1][j][0]) + (xsum[2][j][0] + xsum[3][j][0]);
       }
     } else {
       // per token the tile's (max, lowest index); optional fp32 logits
       float* __restrict__ O = static_cast<float*>(ex.out[e]);
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
+      for (int tb = 0; tb < kNTB; ++tb) {
         float bv = -INFINITY;
         int bi = INT_MAX;
 #pragma unroll
-        for (int vb = 0; vb < NVB; ++vb)
+        for (int vb = 0; vb < kNVB; ++vb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (acc[tb][vb][r] > bv) {   // ascending vocabulary: strict > keeps the lowest index
-              bv = acc[tb][vb][r];
-              bi = vlane + 32 * vb + r;
+          for (int i = 0; i < 4; ++i)
+            if (acc[tb][vb][i] > bv) {   // ascending vocabulary: strict > keeps the lowest index
+              bv = acc[tb][vb][i];
+              bi = vlane + 16 * vb + i;
             }
-        const float ov = __shfl_xor(bv, 32, 64);
-        const int oi = __shfl_xor(bi, 32, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-        const int64_t tok = tq + 32 * tb;
-        if (O != nullptr && tok < n) {
 #pragma unroll
-          for (int vb = 0; vb < NVB; ++vb) {
-            const int vbase = vlane + 32 * vb;
-            if (vbase >= vocab) continue;
-            u32x4* dst = reinterpret_cast<u32x4*>(O + tok * vocab + vbase);
-#pragma unroll
-            for (int h4 = 0; h4 < 4; ++h4) {
-              u32x4 pk;
-#pragma unroll
-              for (int k = 0; k < 4; ++k) pk[k] = __float_as_uint(acc[tb][vb][4 * h4 + k]);
-              dst[h4] = pk;
-            }
+        for (int o = 16; o <= 32; o <<= 1) {
+          const float ov = __shfl_xor(bv, o, 64);
+          const int oi = __shfl_xor(bi, o, 64);
+          if (ov > bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
           }
         }
-        if (hl == 0) {
-          xsum[wave][tb * 32 + q][0] = bv;
-          xsum[wave][tb * 32 + q][1] = __int_as_float(bi);
+        const int64_t tok = tx + 16 * tb;
+        if (O != nullptr && tok < n) {
+#pragma unroll
+          for (int vb = 0; vb < kNVB; ++vb) {
+            const int vbase = vlane + 16 * vb;
+            if (vbase >= vocab) continue;
+            u32x4 pk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pk[i] = __float_as_uint(acc[tb][vb][i]);
+            *reinterpret_cast<u32x4*>(O + tok * vocab + vbase) = pk;
+          }
+        }
+        if (g == 0) {
+          xsum[wave][16 * tb + x][0] = bv;
+          xsum[wave][16 * tb + x][1] = __int_as_float(bi);
         }
       }
       __syncthreads();
-      const int j = wave * 32 + q;
-      const int64_t tk = t0 + j;
-      if (hl == 0 && tk < n) {
+      if (tid < kPkTok && t0 + tid < n) {
+        const int j = tid;
         float bv = xsum[0][j][0];
         int bi = __float_as_int(xsum[0][j][1]);
 #pragma unroll
@@ -309,12 +396,13 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
             bv = xsum[w][j][0];
             bi = __float_as_int(xsum[w][j][1]);
           }
-        float* b = stats + (static_cast<int64_t>(e) * 2 * n_vt + vt) * n + tk;
+        float* b = stats + (static_cast<int64_t>(e) * 2 * n_vt + vt) * n + t0 + j;
         b[0] = bv;
         b[plane] = __int_as_float(bi);
       }
     }
-    // xmax / xsum are next written after this exit's main loop, behind its barriers
+    // xmax / xsum are next written after this exit's main loop, behind its
+    // barriers, which also end every read of them above
   }
 }
 
@@ -341,9 +429,8 @@ bool packed_shape_ok(int vocab, int d) {
 }
 
 hipError_t launch_pack_weights(int vocab, int d, const void* w, void* packed, hipStream_t s) {
-  const int64_t chunks = static_cast<int64_t>(vocab) * d / 8;
-  const int64_t blocks = (chunks + 255) / 256;
-  const int grid = static_cast<int>(blocks < 65536 ? blocks : 65536);
+  const int64_t units = static_cast<int64_t>(vocab / 16) * ((d / 32 + 3) / 4);
+  const int grid = static_cast<int>(units < 65536 ? units : 65536);
   hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, s, static_cast<const bf16_t*>(w),
                      static_cast<bf16_t*>(packed), vocab, d);
   return hipGetLastError();

@@ -79,14 +79,15 @@ def head_error_bound(h: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 def head_error_bound_ordered(h: np.ndarray, w: np.ndarray) -> np.ndarray:
     """The same bound following the order the bf16 GEMMs accumulate in: every
-    matrix-core instruction adds the sum of 16 exact products (bf16 x bf16
-    fits fp32) to the fp32 accumulator, so each logit is a chain of
-    ceil(K / 16) accumulator roundings plus, inside each instruction, a sum of
-    16 terms in any order (at most 15 roundings of any one term).  The unit
-    roundoff is taken as 2^-23 (truncation as well as round-to-nearest), so
-        |error| <= (ceil(K / 16) + 15) 2^-23 sum_k |h_k w_k|  (first order)."""
+    matrix-core instruction adds the sum of 16 (32x32x16) or 32 (16x16x32)
+    exact products (bf16 x bf16 fits fp32) to the fp32 accumulator, so each
+    logit is a chain of at most ceil(K / 16) accumulator roundings plus, inside
+    each instruction, a sum of at most 32 terms in any order (at most 31
+    roundings of any one term).  The unit roundoff is taken as 2^-23
+    (truncation as well as round-to-nearest), so
+        |error| <= (ceil(K / 16) + 31) 2^-23 sum_k |h_k w_k|  (first order)."""
     K = h.shape[1]
-    n = -(-K // 16) + 15
+    n = -(-K // 16) + 31
     u = 2.0 ** -23
     gamma = n * u / (1.0 - n * u)
     return gamma * (np.abs(h) @ np.abs(w).T)

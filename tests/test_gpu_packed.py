@@ -16,19 +16,14 @@ from test_gpu_verify import check_argmax
 pytestmark = pytest.mark.gpu
 
 
-def vperm(q):
-    """A-row q of a 32-row operand block holds vocabulary entry vperm(q) (nel.h)."""
-    return ((q >> 2) & 1) * 16 + (q >> 3) * 4 + (q & 3)
-
-
 def packed_reference(w: np.ndarray) -> np.ndarray:
     """The tiled layout written out from its definition in nel.h:
-    P[((rb * D/16 + kp) * 64 + l) * 8 + j] = W[32 rb + vperm(l % 32), 16 kp + 8 (l / 32) + j]."""
+    P[((rb * D/32 + kb) * 64 + l) * 8 + j] = W[16 rb + l % 16, 32 kb + 8 (l / 16) + j]."""
     V, D = w.shape
-    rb, kp, l, j = np.meshgrid(np.arange(V // 32), np.arange(D // 16), np.arange(64), np.arange(8),
+    rb, kb, l, j = np.meshgrid(np.arange(V // 16), np.arange(D // 32), np.arange(64), np.arange(8),
                                indexing="ij")
-    rows = 32 * rb + vperm(l % 32)
-    cols = 16 * kp + 8 * (l // 32) + j
+    rows = 16 * rb + l % 16
+    cols = 32 * kb + 8 * (l // 16) + j
     return w[rows, cols].reshape(-1)
 
 

@@ -407,11 +407,15 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
 // w = exp(l_M - m), each smaller exit's its fp16 l - m (m the 256-entry tile
 // maximum).  One workgroup per token row (grid-stride) writes every exit's
 // gradient in place, as finalize_vec, and reduces per smaller exit
-// sum_v p_v l_m,v (l_m,v = (l - m) + m) in a fixed order (per-thread fp32 in
-// vocabulary order, then a fixed tree): dv[e][t] = LSE_e - that sum, the
-// cross-entropy to the teacher.
+// sum_v p_v l_m,v in a fixed order (per-thread fp32 in vocabulary order, then
+// a fixed tree): dv[e][t] = LSE_e - that sum, the cross-entropy to the teacher.
+// Per 16-byte chunk (8 entries, one tile): p = w exp(m_M - LSE_M),
+// q = exp2(s log2 e + (m_e - LSE_e) log2 e), g_e = lambda_e gs (q - a p) and
+// g_M = lambda_M gs p, with the label's entry corrected only in the chunk that
+// holds it; sum_v p l_e over the chunk is sum p s + m_e sum p.  A bad label
+// makes the scale NaN, which turns the whole row into NaN.
 template <int MS>   // the most smaller exits the loops are unrolled for
-__global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int vocab, int vtile,
+__global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int vocab, int vshift,
                                                          const int32_t* __restrict__ labels,
                                                          float alpha, float gs,
                                                          const float* __restrict__ stats,
@@ -426,69 +430,93 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
   for (int64_t t = blockIdx.x; t < n; t += gridDim.x) {
     const int y = labels[t];
     const bool bad = y < 0 || y >= vocab;
+    const float nanv = __builtin_nanf("");
     const float lseT = lse[static_cast<int64_t>(M - 1) * n + t];
-    float acc[MS];
+    const float gT = bad ? nanv : gs * lam.w[M - 1];
+    float ge[MS], lseE[MS], acc[MS];
 #pragma unroll
-    for (int e = 0; e < MS; ++e) acc[e] = 0.f;
-#pragma unroll 2
-    for (int64_t c = tid; c < cpr; c += 256) {
-      const int v0 = static_cast<int>(c * 8);
-      const int64_t tile = v0 / vtile;
-      const u32x4 tw = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
-      const float scT =
-          fexp(stats[static_cast<int64_t>(M - 1) * 3 * plane + tile * n + t] - lseT);
-      float p[8];
+    for (int e = 0; e < MS; ++e) {
+      acc[e] = 0.f;
+      ge[e] = 0.f;
+      lseE[e] = 0.f;
+      if (e < S) {
+        ge[e] = bad ? nanv : gs * lam.w[e];
+        lseE[e] = lse[static_cast<int64_t>(e) * n + t];
+      }
+    }
+    // four chunks per thread per round (chunks c0 + 256 k): every exit's
+    // loads of the round are issued before any of them is used, 12 16-byte
+    // loads in flight per thread for three exits
+    for (int64_t c0 = tid; c0 < cpr; c0 += 4 * 256) {
+      u32x4 tw[4], sr[MS][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // (bit_cast of a vector-element expression read element 0 on this
-        // compiler: the element goes through a scalar first)
-        const uint32_t word = tw[j];
-        const half2_t hw = __builtin_bit_cast(half2_t, word);
-        p[2 * j] = static_cast<float>(hw[0]) * scT;
-        p[2 * j + 1] = static_cast<float>(hw[1]) * scT;
+      for (int k = 0; k < 4; ++k) {
+        const int64_t c = c0 + 256 * k;
+        if (c < cpr) {
+          tw[k] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
+#pragma unroll
+          for (int e = 0; e < MS; ++e)
+            if (e < S)
+              sr[e][k] = __builtin_nontemporal_load(
+                  reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(dl.p[e]) + t * vocab) + c);
+        }
       }
 #pragma unroll
-      for (int e = 0; e < MS; ++e) {
-        if (e >= S) break;
-        const u32x4 sr = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(dl.p[e]) + t * vocab) + c);
-        const float mt = stats[static_cast<int64_t>(e) * 3 * plane + tile * n + t];
-        const float off = mt - lse[static_cast<int64_t>(e) * n + t];
-        const float ge = gs * lam.w[e];
+      for (int k = 0; k < 4; ++k) {
+        const int64_t c = c0 + 256 * k;
+        if (c >= cpr) break;
+        const int v0 = static_cast<int>(c * 8);
+        const int64_t tile = v0 >> vshift;   // the tile width is a power of 2
+        const float scT =
+            fexp(stats[static_cast<int64_t>(M - 1) * 3 * plane + tile * n + t] - lseT);
+        const int yi = y - v0;   // the label's entry in this chunk when 0 <= yi < 8
+        float p[8], pa[8];
+        float sp = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = Scratch<bf16_t>::get(tw[k], i) * scT;
+          pa[i] = alpha * p[i];
+          sp += p[i];
+        }
+#pragma unroll
+        for (int e = 0; e < MS; ++e) {
+          if (e >= S) break;
+          const float mt = stats[static_cast<int64_t>(e) * 3 * plane + tile * n + t];
+          const float c1 = (mt - lseE[e]) * kLog2e;
+          float g[8], ps = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float sv = Scratch<bf16_t>::get(sr[e][k], i);
+            ps = fmaf(p[i], sv, ps);
+            g[i] = ge[e] * (__builtin_amdgcn_exp2f(fmaf(sv, kLog2e, c1)) - pa[i]);
+          }
+          acc[e] += fmaf(mt, sp, ps);
+          if (static_cast<unsigned>(yi) < 8u) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (i == yi) g[i] -= ge[e] * (1.f - alpha);
+          }
+          u32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(g[2 * j], g[2 * j + 1]);
+          __builtin_nontemporal_store(
+              o, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[e]) + t * vocab) + c);
+        }
         float g[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t word = sr[j];
-          const half2_t hs = __builtin_bit_cast(half2_t, word);
+        for (int i = 0; i < 8; ++i) g[i] = gT * p[i];
+        if (static_cast<unsigned>(yi) < 8u) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int i = 2 * j + h;
-            const float sv = static_cast<float>(hs[h]);
-            acc[e] = fmaf(p[i], sv + mt, acc[e]);
-            float val = fexp(sv + off) - alpha * p[i];
-            if (v0 + i == y) val -= 1.f - alpha;
-            g[i] = bad ? __builtin_nanf("") : ge * val;
-          }
+          for (int i = 0; i < 8; ++i)
+            if (i == yi) g[i] -= gT;
         }
         u32x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(g[2 * j], g[2 * j + 1]);
         __builtin_nontemporal_store(
-            o, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[e]) + t * vocab) + c);
+            o, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
       }
-      const float gT = gs * lam.w[M - 1];
-      float g[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float val = p[i] - (v0 + i == y ? 1.f : 0.f);
-        g[i] = bad ? __builtin_nanf("") : gT * val;
-      }
-      u32x4 o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(g[2 * j], g[2 * j + 1]);
-      __builtin_nontemporal_store(
-          o, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
     }
 #pragma unroll
     for (int e = 0; e < MS; ++e) {
@@ -625,7 +653,9 @@ hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInf
                                 const float* stats, const float* lse, void* const* dlogits,
                                 float* dv, const ExitW& lam, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (!info.teacher_w16 || vocab % 8 != 0) return hipErrorInvalidValue;
+  if (!info.teacher_w16 || vocab % 8 != 0 || (info.vtile & (info.vtile - 1)) != 0)
+    return hipErrorInvalidValue;
+  const int vshift = __builtin_ctz(static_cast<unsigned>(info.vtile));
   DlPtrs dl{};
   for (int e = 0; e < n_exits; ++e) dl.p[e] = dlogits[e];
   // one workgroup per row up to 65536 rows (grid-stride beyond)
@@ -633,10 +663,10 @@ hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInf
   const int n_vt = (vocab + info.vtile - 1) / info.vtile;
   if (n_exits <= 3)
     hipLaunchKernelGGL((finalize_rows_f16<2>), dim3(grid), dim3(256), 0, s, n_exits, n, vocab,
-                       info.vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, dv, lam);
+                       vshift, labels, alpha, grad_scale, stats, lse, dl, n_vt, dv, lam);
   else
     hipLaunchKernelGGL((finalize_rows_f16<kMaxExits - 1>), dim3(grid), dim3(256), 0, s, n_exits, n,
-                       vocab, info.vtile, labels, alpha, grad_scale, stats, lse, dl, n_vt, dv, lam);
+                       vocab, vshift, labels, alpha, grad_scale, stats, lse, dl, n_vt, dv, lam);
   return hipGetLastError();
 }
 

@@ -86,7 +86,7 @@ def test_loss_full_size_sampled(nel, k, alpha):
 
 def test_junction_parity(nel):
     import torch
-    for k in (0, 2):
+    for k in (0, 1, 2, 3):
         s = synth.make_workload(k) if k == 0 else synth.make_workload(k, batch=1)
         ds = DevSuite(s)
         log(f"[junction] workload {k}: N={s.n_tokens} widths={s.widths}")
@@ -107,6 +107,34 @@ def test_junction_parity(nel):
                 else:
                     np.testing.assert_allclose(out[:, :d_in], ref[:, :d_in], rtol=1e-6, atol=1e-30)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("widths,dtype", [((64, 128), "bf16"), ((128, 256), "bf16"),
+                                          ((64, 96), "f32"), ((512, 768), "bf16")])
+def test_junction_narrow_rows_bad_ids_ragged(nel, widths, dtype):
+    """Rows short enough that several tokens share a wavefront (8, 16 or 32
+    lanes per token): bit-exact embedding half, <= 1 ulp rescaled half, bad ids
+    give NaN rows and the flag, and a token count that fills no wavefront."""
+    import torch
+    from gpu_util import bf16_ulp
+    s = synth.make_suite(widths, 300, 1, 53, dtype=dtype, seed=32)
+    ds = DevSuite(s)
+    ids = ds.ids.clone()
+    ids[7] = 300
+    ids[52] = -3
+    flags = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    out = to_np(nel.junction(ds.h[0], ids, ds.emb[1], flags=flags))
+    ok = np.ones(s.n_tokens, bool)
+    ok[[7, 52]] = False
+    ref = oracle.junction(s.h[0][ok], s.ids[ok], s.emb[1])
+    d_in = widths[0]
+    np.testing.assert_array_equal(out[ok][:, d_in:], s.emb[1][s.ids[ok]].astype(np.float64))
+    if dtype == "bf16":
+        assert np.all(np.abs(out[ok][:, :d_in] - ref[:, :d_in]) <= bf16_ulp(ref[:, :d_in]) + 1e-30)
+    else:
+        np.testing.assert_allclose(out[ok][:, :d_in], ref[:, :d_in], rtol=1e-6, atol=1e-30)
+    assert np.all(np.isnan(out[[7, 52]]))
+    assert nel.read_flags(flags) == nel.FLAG_BAD_ID
 
 
 def test_junction_generic_widths_and_bad_ids(nel):

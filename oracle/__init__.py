@@ -31,5 +31,5 @@ from .matryoshka import (  # noqa: F401
     junction, junction_backward, JUNCTION_RESCALE, JUNCTION_NO_RESCALE, JUNCTION_ZERO_FILL,
     divergence, divergence_grad, DIV_FORWARD, DIV_REVERSE_KL, DIV_JS, DIV_TV, heads, head_backward, logsumexp, softmax, matryoshka_loss, matryoshka_grad,
     argmax_lowest, accept_prefix, forward_tokens, nucleus, sample_inverse_cdf,
-    speculative_verify, working_precision,
+    speculative_verify, working_precision, loss_backward,
 )

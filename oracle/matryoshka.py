@@ -456,3 +456,31 @@ def forward_tokens(hs: Sequence[np.ndarray], ws: Sequence[np.ndarray], labels: n
     if want_grad:
         grads = [np.concatenate(g, axis=0) for g in grads]
     return res, grads
+
+
+def loss_backward(hs: Sequence[np.ndarray], ws: Sequence[np.ndarray], labels: np.ndarray,
+                  alpha: float, grad_scale: float = 1.0,
+                  exit_weights: Optional[Sequence[float]] = None, chunk: int = 1024):
+    """The loss and the backward of every exit head in one pass over the
+    tokens, the logit gradients never kept beyond a chunk of ``chunk`` tokens.
+
+    For each chunk: the heads (``heads``), the losses (``matryoshka_loss``),
+    G_m = ``matryoshka_grad`` (teacher under stop-gradient; "Matryoshka
+    Language Model Suites", distillation paragraph), then by the chain rule
+    through l_m = h_m W^m^T (``head_backward``) the chunk's rows of
+    dh_m = G_m W^m and its share of dW^m = sum over tokens of G_m[t]^T h_m[t].
+    Returns (loss dict as ``forward_tokens``, [dh_m [N, D_m]], [dW^m [V, D_m]]).
+    """
+    n = hs[0].shape[0]
+    res, _ = forward_tokens(hs, ws, labels, alpha, grad_scale, chunk=chunk, want_grad=False,
+                            exit_weights=exit_weights)
+    dhs = [np.zeros((n, h.shape[1]), dtype=_DTYPE) for h in hs]
+    dws = [np.zeros(np.shape(w), dtype=_DTYPE) for w in ws]
+    for s in range(0, n, chunk):
+        r = slice(s, min(n, s + chunk))
+        lg = heads([h[r] for h in hs], ws)
+        for m, g in enumerate(matryoshka_grad(lg, labels[r], alpha, grad_scale, exit_weights)):
+            dh, dw = head_backward(g, hs[m][r], ws[m])
+            dhs[m][r] = dh
+            dws[m] += dw
+    return res, dhs, dws

@@ -334,6 +334,66 @@ def test_head_backward_weight_gradient_columns_sum_to_zero():
         np.testing.assert_allclose(dw.sum(axis=0), 0, atol=1e-12)
 
 
+def test_loss_backward_matches_torch_autograd_with_weights_and_scale():
+    """The chunked loss + head backward equals torch autograd of
+    grad_scale * sum_t sum_m lambda_m L_m through the heads, the teacher's
+    softmax detached inside the smaller exits' distillation terms; chunks of
+    3 tokens over 7 split the tokens unevenly."""
+    r = rng(17)
+    D, V, N, a, gs = (3, 5, 8), 13, 7, 0.3, 0.37
+    lam = (0.5, 2.0, 1.25)
+    hs = [torch.tensor(r.standard_normal((N, d)), requires_grad=True) for d in D]
+    ws = [torch.tensor(r.standard_normal((V, d)) * 0.4, requires_grad=True) for d in D]
+    y = torch.tensor(r.integers(0, V, N))
+    ls = [h @ w.T for h, w in zip(hs, ws)]
+    logp = torch.log_softmax(ls[-1], dim=1).detach()
+    tot = lam[2] * F.cross_entropy(ls[-1], y, reduction="sum")
+    for m in range(2):
+        dist = F.kl_div(torch.log_softmax(ls[m], dim=1), logp, log_target=True,
+                        reduction="sum") + (-(logp.exp() * logp).sum())
+        tot = tot + lam[m] * ((1 - a) * F.cross_entropy(ls[m], y, reduction="sum") + a * dist)
+    (gs * tot).backward()
+    res, dhs, dws = oracle.loss_backward([h.detach().numpy() for h in hs],
+                                         [w.detach().numpy() for w in ws], y.numpy(), a,
+                                         grad_scale=gs, exit_weights=lam, chunk=3)
+    assert res["total"].sum() == pytest.approx(tot.item(), rel=1e-12)
+    for m in range(3):
+        np.testing.assert_allclose(dhs[m], hs[m].grad.numpy(), atol=1e-12)
+        np.testing.assert_allclose(dws[m], ws[m].grad.numpy(), atol=1e-12)
+
+
+def test_loss_backward_invariant_to_a_common_head_row():
+    """Adding one vector c to every row of W^m shifts each token's logits by
+    h_t . c, which leaves every softmax and so G unchanged; dW = G^T h is then
+    unchanged and dh = G (W + 1 c^T) = G W because each row of G sums to 0
+    (1 - (1 - a) - a for a smaller exit, 1 - 1 for the teacher)."""
+    r = rng(18)
+    D, V, N = (4, 6), 17, 9
+    hs = [r.standard_normal((N, d)) for d in D]
+    ws = [r.standard_normal((V, d)) * 0.5 for d in D]
+    y = r.integers(0, V, N)
+    _, dh0, dw0 = oracle.loss_backward(hs, ws, y, 0.3)
+    ws2 = [w + r.standard_normal((1, w.shape[1])) for w in ws]
+    _, dh1, dw1 = oracle.loss_backward(hs, ws2, y, 0.3)
+    for m in range(2):
+        np.testing.assert_allclose(dh1[m], dh0[m], atol=1e-12)
+        np.testing.assert_allclose(dw1[m], dw0[m], atol=1e-12)
+        assert np.abs(dh0[m]).max() > 1e-3
+
+
+def test_loss_backward_single_exit_is_plain_cross_entropy_backward():
+    """One exit (alpha irrelevant): dh and dW are those of the summed
+    library cross-entropy through a linear head."""
+    r = rng(19)
+    h = torch.tensor(r.standard_normal((6, 5)), requires_grad=True)
+    w = torch.tensor(r.standard_normal((11, 5)), requires_grad=True)
+    y = torch.tensor(r.integers(0, 11, 6))
+    F.cross_entropy(h @ w.T, y, reduction="sum").backward()
+    _, dhs, dws = oracle.loss_backward([h.detach().numpy()], [w.detach().numpy()], y.numpy(), 0.9)
+    np.testing.assert_allclose(dhs[0], h.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dws[0], w.grad.numpy(), atol=1e-12)
+
+
 # --------------------------------------------------------------------- heads
 def test_heads_against_exactly_rounded_dot_products():
     r = rng(13)

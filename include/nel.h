@@ -390,6 +390,49 @@ nel_status nel_heads_backward(nel_dtype dt, int32_t n_exits, int64_t n_tokens, i
 size_t nel_heads_backward_workspace(int32_t n_exits, int64_t n_tokens, int32_t vocab,
                                     const int32_t* d);
 
+/*
+ * The loss and the backward of every exit head in one call, with the logit
+ * gradients G_e never written to memory.  G_e is the gradient
+ * nel_matryoshka_loss_packed (NEL_DIV_FORWARD) writes into dlogits[e], i.e.
+ * grad_scale lambda_e d(sum_t total_t)/d l_e with the teacher under
+ * stop-gradient ("Matryoshka Language Model Suites", distillation paragraph;
+ * the backward through l = h W^T follows from the head of the copyedit of
+ * Sec. 2 "Modeling"):
+ *     dh[e] = G_e W_e      [n_tokens, d_e] bf16
+ *     dw[e] = G_e^T h_e    [vocab, d_e]    fp32
+ * The head GEMM leaves its 16-bit scratch in scratch[e]; the dh and dw GEMMs
+ * form each 64-entry slice of G_e from it and per-row constants in
+ * registers, with the arithmetic of the gradient pass, so dh and dw are
+ * bit-identical to nel_matryoshka_loss_packed (same inputs, dlogits =
+ * scratch) followed by nel_heads_backward on the stored gradients.
+ *   h, labels, alpha_d, grad_scale, exit_weights, token_loss, mean_loss:
+ *            as nel_matryoshka_loss (the divergence is NEL_DIV_FORWARD)
+ *   w:        host array of n_exits device bf16 [vocab, d_e] (row-major heads,
+ *            read by the dh GEMM's transposing pack)
+ *   w_packed: the same heads in the layout of nel_pack_weights
+ *   scratch:  host array of n_exits device buffers of n_tokens * vocab 16-bit
+ *            entries (no alias); their contents on return are scratch
+ *   dh, dw:   NULL (skip that output for every exit) or host arrays of n_exits
+ *            device pointers, none NULL (dh's may be when n_tokens is 0); not
+ *            both NULL
+ *   workspace: >= nel_loss_backward_workspace() bytes; its first int32 is the
+ *            device flag word (NEL_FLAG_BAD_LABEL: that token's losses, its
+ *            rows of dh and, through the sum over tokens, all of dw are NaN)
+ * Requires dt == NEL_BF16 (NEL_EDTYPE); vocab and every d_e multiples of 64,
+ * d_e below 2^22, the padded token count below 2^24 (NEL_ESHAPE).  Other
+ * errors as nel_matryoshka_loss_packed and nel_heads_backward; on any error
+ * nothing is launched.  n_tokens == 0 writes the means and sets dw to 0.
+ */
+nel_status nel_matryoshka_loss_backward_packed(
+    nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab, const int32_t* d,
+    const void* const* h, const void* const* w, const void* const* w_packed,
+    const int32_t* labels, float alpha_d, float grad_scale, const float* exit_weights,
+    float* token_loss, float* mean_loss, void* const* scratch, void* const* dh,
+    float* const* dw, void* workspace, size_t ws_bytes, void* stream);
+/* Bytes of workspace nel_matryoshka_loss_backward_packed needs (0 on bad arguments). */
+size_t nel_loss_backward_workspace(int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                                   const int32_t* d);
+
 /* Bytes of device workspace an op needs (0 on bad arguments). */
 size_t nel_workspace_size(int32_t op, int32_t n_exits, int64_t n_tokens, int32_t vocab);
 
@@ -413,7 +456,9 @@ const char* nel_last_hip_error(void);
  * 0 junction, 1 heads+loss statistics GEMM, 2 loss merge, 3 means,
  * 4 dlogits finalize, 5 heads+argmax GEMM, 6 argmax merge, 7 accept,
  * 8 weight packing, 9 head-backward operand packs, 10 dH GEMM, 11 dW GEMM,
- * 12 junction backward, 13 sampled speculative verification, 14 divergence pass.
+ * 12 junction backward, 13 sampled speculative verification, 14 divergence pass,
+ * 15 gradient row constants (fused loss backward; that call's gradient pass,
+ * which then writes no gradients, counts as 4).
  * The record is process-global.  A lock guards it, so launching and reading
  * from several threads is free of data races, but launches from every thread
  * and stream are summed together: for benchmarks, with one thread launching.
@@ -422,7 +467,7 @@ enum { NEL_K_JUNCTION = 0, NEL_K_HEADS_LOSS = 1, NEL_K_MERGE = 2, NEL_K_MEANS = 
        NEL_K_FINALIZE = 4, NEL_K_HEADS_ARGMAX = 5, NEL_K_ARGMAX_MERGE = 6,
        NEL_K_ACCEPT = 7, NEL_K_PACK = 8, NEL_K_BWD_PACK = 9, NEL_K_BWD_DH = 10,
        NEL_K_BWD_DW = 11, NEL_K_JUNCTION_BWD = 12, NEL_K_SPECULATIVE = 13,
-       NEL_K_DIVERGENCE = 14, NEL_K_COUNT = 15 };
+       NEL_K_DIVERGENCE = 14, NEL_K_GRAD_CONSTS = 15, NEL_K_COUNT = 16 };
 nel_status nel_timing_enable(int32_t on);
 /* Synchronises the device, then returns the summed milliseconds and the
  * number of timed launches of `kernel` since the last reset. */

@@ -15,6 +15,9 @@ its own per operation, device and stream.
     matryoshka_loss_packed / exit_heads_packed -> as above, on packed weights
     head_backward(dlogits, h, w)               -> (dL/dh bf16, dL/dW fp32) of one exit head
     heads_backward(dlogits, hs, ws)            -> ([dL/dh_m], [dL/dW_m]) of every exit, grouped
+    loss_backward_packed(hs, ws, ws_packed, labels, alpha_d, grad_scale)
+                                               -> (mean_loss, token_loss, [dL/dh_m], [dL/dW_m]),
+                                                  the logit gradients never stored
     junction_backward(h, ids, emb, dout)       -> (dL/dh, dL/demb fp32) of one junction
     speculative_verify(draft_logits, verify_logits, tokens, u_accept, u_next, draft_len)
                                                -> (beta, accepted, next_token)
@@ -32,6 +35,7 @@ __all__ = [
     "FLAG_BAD_LABEL", "Workspace", "pack_weights", "matryoshka_loss_packed", "exit_heads_packed", "head_backward",
     "head_backward_workspace_size", "heads_backward", "heads_backward_workspace_size", "loss_workspace",
     "junction_backward", "speculative_verify", "speculative_row_stats", "exit_heads_packed_noalloc",
+    "loss_backward_packed", "loss_backward_workspace_size",
     "JUNCTION_RESCALE", "JUNCTION_NO_RESCALE", "JUNCTION_ZERO_FILL", "DIV_FORWARD",
     "DIV_REVERSE_KL", "DIV_JS", "DIV_TV",
 ]
@@ -47,7 +51,7 @@ FLAG_BAD_ID, FLAG_BAD_LABEL = 1, 2
 MAX_EXITS = 8
 KERNELS = ["junction", "heads_loss", "merge", "means", "finalize", "heads_argmax",
            "argmax_merge", "accept", "pack", "bwd_pack", "bwd_dh", "bwd_dw", "junction_bwd", "speculative",
-           "divergence"]
+           "divergence", "grad_consts"]
 
 
 def lib_path() -> str:
@@ -108,6 +112,10 @@ def load():
         "nel_head_backward_workspace": [c_i64, c_int, c_int],
         "nel_heads_backward": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "nel_heads_backward_workspace": [c_int, c_i64, c_int, vp],
+        "nel_matryoshka_loss_backward_packed": [c_int, c_int, c_i64, c_int, vp, vp, vp, vp, vp,
+                                                ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
+                                                vp, vp, vp, sz, vp],
+        "nel_loss_backward_workspace": [c_int, c_i64, c_int, vp],
         "nel_junction_backward": [c_int, c_i64, c_int, c_int, c_int, vp, vp, vp, vp, c_int, c_int,
                                   vp, vp, vp, vp, sz, vp],
         "nel_junction_backward_workspace": [c_i64, c_int, c_int, c_int],
@@ -128,6 +136,7 @@ def load():
     lib.nel_workspace_size.restype = sz
     lib.nel_head_backward_workspace.restype = sz
     lib.nel_heads_backward_workspace.restype = sz
+    lib.nel_loss_backward_workspace.restype = sz
     lib.nel_junction_backward_workspace.restype = sz
     lib.nel_speculative_workspace.restype = sz
     lib.nel_status_string.restype = ctypes.c_char_p
@@ -536,6 +545,78 @@ def heads_backward(dlogits, hs, ws, want_dh: bool = True, want_dw: bool = True, 
                                      wsb.numel(), _stream(device)), "nel_heads_backward")
     return dhs, dws
 
+
+
+def loss_backward_workspace_size(n_tokens: int, vocab: int, widths) -> int:
+    ds = (ctypes.c_int32 * len(widths))(*widths)
+    return int(load().nel_loss_backward_workspace(len(widths), n_tokens, vocab, ds))
+
+
+def loss_backward_packed(hs: Sequence, ws: Sequence, ws_packed: Sequence, labels,
+                         alpha_d: float = 0.3, grad_scale: float = 1.0,
+                         want_dh: bool = True, want_dw: bool = True,
+                         exit_weights: Optional[Sequence[float]] = None,
+                         want_token_loss: bool = True, scratch: Optional[List] = None,
+                         dhs=None, dws=None, mean_loss=None, token_loss=None, workspace=None):
+    """The losses (as matryoshka_loss_packed) and every exit head's backward, the logit
+    gradients formed inside the dh and dW GEMMs and never stored.  ws: the heads row-major
+    (bf16 [V, d_m]); ws_packed: the same heads from pack_weights; scratch: n x V 16-bit
+    buffers, one per exit (allocated when None).  The workspace's first int32 is the
+    device flag word.  Returns (mean_loss, token_loss | None, [dh_m bf16] | None,
+    [dW_m fp32] | None), bit-identical to matryoshka_loss_packed followed by
+    heads_backward."""
+    torch = _torch()
+    M = len(hs)
+    if not (len(ws) == M == len(ws_packed)) or not 1 <= M <= MAX_EXITS:
+        raise ValueError("need 1..8 exits with one head (row-major and packed) each")
+    device = hs[0].device
+    n, V = hs[0].shape[0], ws[0].shape[0]
+    widths = [h.shape[1] for h in hs]
+    for m in range(M):
+        for t, name in ((hs[m], "h"), (ws[m], "w"), (ws_packed[m], "w_packed")):
+            if t.dtype != torch.bfloat16:
+                raise TypeError(f"{name}[{m}] must be bfloat16")
+            _dev(t, device, name)
+        if hs[m].shape[0] != n or ws[m].shape != (V, widths[m]) or ws_packed[m].shape != ws[m].shape:
+            raise ValueError("need h[m] [n, d_m], w[m] and w_packed[m] [V, d_m]")
+    if labels.dtype != torch.int32 or labels.shape != (n,):
+        raise ValueError("labels must be int32 [n]")
+    if scratch is None:
+        scratch = [torch.empty(n, V, dtype=torch.bfloat16, device=device) for _ in range(M)]
+    if len(scratch) != M or any(t.numel() != n * V or t.element_size() != 2 for t in scratch):
+        raise ValueError("scratch needs one n x V 16-bit buffer per exit")
+    dhs = (dhs if dhs is not None else [torch.empty(n, d, dtype=torch.bfloat16, device=device)
+                                        for d in widths]) if want_dh else None
+    dws = (dws if dws is not None else [torch.empty(V, d, dtype=torch.float32, device=device)
+                                        for d in widths]) if want_dw else None
+    for lst, name in ((dhs, "dhs"), (dws, "dws")):
+        if lst is not None and len(lst) != M:
+            raise ValueError(f"{name} needs one tensor per exit")
+    if mean_loss is None:
+        mean_loss = torch.empty(3 * M + 1, dtype=torch.float32, device=device)
+    if want_token_loss and token_loss is None:
+        token_loss = torch.empty(M, 3, n, dtype=torch.float32, device=device)
+    if not want_token_loss:
+        token_loss = None
+    lam = None
+    if exit_weights is not None:
+        if len(exit_weights) != M:
+            raise ValueError("exit_weights needs one weight per exit")
+        lam = (ctypes.c_float * M)(*[float(x) for x in exit_weights])
+    need = loss_backward_workspace_size(n, V, widths)
+    if need == 0:
+        raise ValueError("shape not supported (V and every d_m must be multiples of 64)")
+    wsb = workspace if workspace is not None else _workspace("loss_backward", device, need)
+    ds = (ctypes.c_int32 * M)(*widths)
+    _check(load().nel_matryoshka_loss_backward_packed(
+        BF16, M, n, V, ds, _ptrs(hs), _ptrs(ws), _ptrs(ws_packed),
+        _dev(labels, device, "labels"), float(alpha_d), float(grad_scale), lam,
+        _dev(token_loss, device, "token_loss"), _dev(mean_loss, device, "mean_loss"),
+        _ptrs([_dev(t, device, "scratch") for t in scratch]),
+        _ptrs([_dev(t, device, "dh") for t in dhs]) if dhs is not None else None,
+        _ptrs([_dev(t, device, "dw") for t in dws]) if dws is not None else None,
+        wsb.data_ptr(), wsb.numel(), _stream(device)), "nel_matryoshka_loss_backward_packed")
+    return mean_loss, token_loss, dhs, dws
 
 
 def junction_backward(h, ids, emb, dout, stop_grad: bool = False, want_dh: bool = True,

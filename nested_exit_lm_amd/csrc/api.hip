@@ -271,7 +271,7 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
                      const int32_t* labels, float alpha_d, float grad_scale,
                      const float* exit_weights, int32_t div, float* token_loss,
                      float* mean_loss, void* const* dlogits, void* workspace, size_t ws_bytes,
-                     void* stream) {
+                     void* stream, bool write_g = true, TileInfo* info_out = nullptr) {
   if (dt != NEL_F32 && dt != NEL_BF16) return NEL_EDTYPE;
   if (packed && dt != NEL_BF16) return NEL_EDTYPE;
   if (n_tokens < 0 || vocab < 1) return NEL_ESHAPE;
@@ -355,7 +355,7 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
   if (rows && n_tokens > 0) {
     err = timed(NEL_K_FINALIZE, s, [&] {
       return launch_finalize_rows(n_exits, n_tokens, vocab, info, labels, alpha_d, grad_scale,
-                                  stats, lse, dlogits, dv, lam, s);
+                                  stats, lse, dlogits, dv, lam, write_g, s);
     });
     if (err != hipSuccess) return from_hip(err);
   }
@@ -367,6 +367,7 @@ nel_status loss_impl(bool packed, nel_dtype dt, int32_t n_exits, int64_t n_token
     return launch_loss_means(n_exits, n_tokens, partials, mean_loss, s);
   });
   if (err != hipSuccess) return from_hip(err);
+  if (info_out) *info_out = info;
   if (dlogits && n_tokens > 0 && !rows) {
     err = timed(NEL_K_FINALIZE, s, [&] {
       return dt == NEL_BF16 ? launch_finalize<bf16_t>(n_exits, n_tokens, vocab, info, labels,
@@ -592,7 +593,7 @@ nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int3
     BwdGroup gw{};
     if (!bwd_group_add(gw, ht, d, dlogits, vocab, vocab, L.n_pad, dw, d, n_tokens))
       return NEL_ESHAPE;
-    err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float, true>(gw, s); });
+    err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float, true, false>(gw, s); });
     if (err != hipSuccess) return from_hip(err);
   }
   return NEL_OK;
@@ -665,10 +666,134 @@ nel_status nel_heads_backward(nel_dtype dt, int32_t n_exits, int64_t n_tokens, i
     }
   }
   if (dh) {
-    err = timed(NEL_K_BWD_DH, s, [&] { return launch_bwd_group<bf16_t, false>(gh, s); });
+    err = timed(NEL_K_BWD_DH, s, [&] { return launch_bwd_group<bf16_t, false, false>(gh, s); });
     if (err != hipSuccess) return from_hip(err);
   }
-  if (dw) err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float, true>(gw, s); });
+  if (dw) err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float, true, false>(gw, s); });
+  return from_hip(err);
+}
+
+// Workspace of nel_matryoshka_loss_backward_packed: the loss op's, then the
+// gradient row constants (16 bytes per exit, statistics tile and token,
+// sized for the narrowest tile), then nel_heads_backward's.
+struct LossBwdWs {
+  size_t loss, consts, bwd, total;
+};
+static LossBwdWs loss_bwd_ws_layout(int32_t n_exits, int64_t n, int32_t vocab, const int32_t* d) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  LossBwdWs L;
+  L.loss = 0;
+  L.consts = up(loss_ws_layout(n_exits, n, vocab).total);
+  L.bwd = L.consts + up(size_t{16} * n_exits * static_cast<size_t>(n_vocab_tiles(vocab)) *
+                        static_cast<size_t>(n));
+  L.total = L.bwd + heads_bwd_offset(n_exits, n, vocab, d);
+  return L;
+}
+
+size_t nel_loss_backward_workspace(int32_t n_exits, int64_t n_tokens, int32_t vocab,
+                                   const int32_t* d) {
+  if (nel_heads_backward_workspace(n_exits, n_tokens, vocab, d) == 0) return 0;
+  for (int32_t e = 0; e < n_exits; ++e)
+    if (!packed_shape_ok(vocab, d[e])) return 0;
+  if (!grid_fits(n_tokens, vocab)) return 0;
+  return loss_bwd_ws_layout(n_exits, n_tokens, vocab, d).total;
+}
+
+nel_status nel_matryoshka_loss_backward_packed(
+    nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab, const int32_t* d,
+    const void* const* h, const void* const* w, const void* const* w_packed,
+    const int32_t* labels, float alpha_d, float grad_scale, const float* exit_weights,
+    float* token_loss, float* mean_loss, void* const* scratch, void* const* dh,
+    float* const* dw, void* workspace, size_t ws_bytes, void* stream) {
+  // everything the backward needs is checked before the loss launches anything
+  if (dt != NEL_BF16) return NEL_EDTYPE;
+  if (n_exits < 1 || n_exits > NEL_MAX_EXITS || !d) return NEL_EINVAL;
+  for (int32_t e = 0; e < n_exits; ++e)
+    if (!head_bwd_shape_ok(n_tokens, vocab, d[e]) || !packed_shape_ok(vocab, d[e]))
+      return NEL_ESHAPE;
+  if (!dh && !dw) return NEL_EINVAL;
+  if (!scratch || (n_tokens > 0 && (!h || !w || !w_packed))) return NEL_EINVAL;
+  for (int32_t e = 0; e < n_exits; ++e) {
+    if (n_tokens > 0 && (!scratch[e] || !h[e] || !w[e] || !w_packed[e])) return NEL_EINVAL;
+    if ((dh && n_tokens > 0 && !dh[e]) || (dw && !dw[e])) return NEL_EINVAL;   // dh may be empty
+    if ((n_tokens > 0 && (misaligned(scratch[e]) || misaligned(h[e]) || misaligned(w[e]))) ||
+        (dh && misaligned(dh[e])) || (dw && misaligned(dw[e])))
+      return NEL_EALIGN;
+  }
+  if (misaligned(workspace)) return NEL_EALIGN;
+  if (!grid_fits(n_tokens, vocab)) return NEL_ESHAPE;
+  const LossBwdWs L = loss_bwd_ws_layout(n_exits, n_tokens, vocab, d);
+  if (!workspace || ws_bytes < L.total) return NEL_EWORKSPACE;
+  ExitW lam;
+  for (int e = 0; e < kMaxExits; ++e) lam.w[e] = 1.f;
+  if (exit_weights)
+    for (int e = 0; e < n_exits; ++e) lam.w[e] = exit_weights[e];   // checked by the loss
+  char* ws = static_cast<char*>(workspace);
+  TileInfo info;
+  nel_status st = loss_impl(true, dt, n_exits, n_tokens, vocab, d, h, w_packed, labels, alpha_d,
+                            grad_scale, exit_weights, NEL_DIV_FORWARD, token_loss, mean_loss,
+                            scratch, ws + L.loss, L.consts - L.loss, stream, /*write_g=*/false,
+                            &info);
+  if (st != NEL_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (n_tokens == 0) {   // no tokens: dH is empty, dW = 0
+    if (!dw) return NEL_OK;
+    for (int32_t e = 0; e < n_exits && err == hipSuccess; ++e)
+      err = timed(NEL_K_BWD_DW, s, [&] {
+        return launch_zero_f32(dw[e], static_cast<int64_t>(vocab) * d[e], s);
+      });
+    return from_hip(err);
+  }
+  if ((info.vtile & (info.vtile - 1)) != 0 || info.vtile < kPkBRows) return NEL_EINVAL;
+  const LossWs LL = loss_ws_layout(n_exits, n_tokens, vocab);
+  const float* stats = reinterpret_cast<const float*>(ws + L.loss + LL.stats);
+  const float* lse = reinterpret_cast<const float*>(ws + L.loss + LL.lse);
+  char* consts = ws + L.consts;
+  err = timed(NEL_K_GRAD_CONSTS, s, [&] {
+    return launch_grad_consts(n_exits, n_tokens, vocab, info, labels, stats, lse, consts, s);
+  });
+  if (err != hipSuccess) return from_hip(err);
+  const int64_t plane = ((vocab + info.vtile - 1) / info.vtile) * n_tokens;
+  BwdGroup gh{}, gw{};
+  for (BwdGroup* g : {&gh, &gw}) {
+    g->tw = static_cast<const uint16_t*>(scratch[n_exits - 1]);
+    g->n_tok = n_tokens;
+    g->vshift = __builtin_ctz(static_cast<unsigned>(info.vtile));
+    g->alpha = alpha_d;
+  }
+  for (int32_t e = 0; e < n_exits; ++e) {
+    const HeadBwdWs HL = head_bwd_ws_layout(n_tokens, vocab, d[e]);
+    char* base = ws + L.bwd + heads_bwd_offset(e, n_tokens, vocab, d);
+    auto fill = [&](BwdGroup& g) {
+      const int k = g.count - 1;
+      g.tab[k] = consts + size_t{16} * static_cast<size_t>(e) * plane;
+      g.ge[k] = grad_scale * lam.w[e];
+      g.teacher[k] = e == n_exits - 1;
+    };
+    if (dh) {
+      err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack_t(w[e], vocab, d[e], vocab, base + HL.wt, s); });
+      if (err != hipSuccess) return from_hip(err);
+      if (!bwd_group_add(gh, base + HL.wt, d[e], scratch[e], n_tokens, vocab, vocab, dh[e], d[e]))
+        return NEL_ESHAPE;
+      fill(gh);
+    }
+    if (dw) {
+      err = timed(NEL_K_BWD_PACK, s, [&] {
+        return launch_pack_t(h[e], n_tokens, d[e], HL.n_pad, base + HL.ht, s);
+      });
+      if (err != hipSuccess) return from_hip(err);
+      if (!bwd_group_add(gw, base + HL.ht, d[e], scratch[e], vocab, vocab, HL.n_pad, dw[e], d[e],
+                         n_tokens))
+        return NEL_ESHAPE;
+      fill(gw);
+    }
+  }
+  if (dh) {
+    err = timed(NEL_K_BWD_DH, s, [&] { return launch_bwd_group<bf16_t, false, true>(gh, s); });
+    if (err != hipSuccess) return from_hip(err);
+  }
+  if (dw) err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float, true, true>(gw, s); });
   return from_hip(err);
 }
 

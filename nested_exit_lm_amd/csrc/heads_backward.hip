@@ -13,9 +13,15 @@
 // so each lane's accumulators are 16 consecutive d of one output row and the
 // stores are row-major.  W^T and h^T are written tiled by one transposing
 // pass each (HBM-bound, into the workspace; K zero-padded to a multiple of 64).
+// The fused form reads no G: each thread forms its B chunks from the fp16
+// scratch of the packed loss GEMM and 16-byte row constants per (vocabulary
+// tile, token), with the arithmetic of the in-place gradient pass
+// (grad_chunk.h), so G only ever exists in registers and LDS and the
+// products equal those of the stored G bit for bit.
 #include <cstdint>
 
 #include "common.h"
+#include "grad_chunk.h"
 #include "internal.h"
 #include "packed_core.h"
 #include "tiles.h"
@@ -75,14 +81,111 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
     p[i] = 0.f;
 }
 
+// ---------------------------------------------------------------- fused B
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// {c1, sc} of a row constant record (the label is read once per row where
+// the row does not change).
+__device__ __forceinline__ u32x2 load_c1_sc(const GradRowConst* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// B = G of one exit, rows = tokens, K = vocabulary (dh = G W).  A K step
+// (64 entries) lies inside one statistics tile (at least 128 wide).
+struct BRowsGrad {
+  const char* S;              // exit's scratch at the tile's token row 0 (bytes)
+  const char* W;              // the teacher's weights, same place
+  const GradRowConst* tab;    // the exit's constants, [tile][n]
+  int64_t n;
+  int32_t row[4];             // tokens of the thread's four chunks
+  int32_t y[4];               // their labels
+  uint32_t boff[4];           // byte offsets of the chunks at K step 0
+  int vlane, vshift;          // first entry of the thread's chunk in a K step; log2 tile width
+  float ge, alpha;
+  bool teacher;
+  int gcur;
+  u32x4 rs[4], rw[4];
+  u32x2 k[4];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = tab[row[j]].y;
+  }
+  __device__ __forceinline__ void issue(int g) {
+    gcur = g;
+    const int64_t off = static_cast<int64_t>(g) * (kPkBK * 2);
+    const GradRowConst* t = tab + ((static_cast<int64_t>(g) * kPkBK) >> vshift) * n;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      rw[j] = *reinterpret_cast<const u32x4*>(W + off + boff[j]);
+      if (!teacher) rs[j] = *reinterpret_cast<const u32x4*>(S + off + boff[j]);
+      k[j] = load_c1_sc(t + row[j]);
+    }
+  }
+  __device__ __forceinline__ void finish(u32x4 (&hr)[4]) const {
+    const int v0 = gcur * kPkBK + vlane;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float c1 = __uint_as_float(k[j][0]), sc = __uint_as_float(k[j][1]);
+      hr[j] = teacher ? grad_chunk_teacher(rw[j], sc, ge, y[j] - v0)
+                      : grad_chunk_student(rs[j], rw[j], sc, c1, ge, alpha, y[j] - v0);
+    }
+  }
+};
+
+// B = G of one exit read K-major: K = tokens, the tile's 128 product rows =
+// 128 vocabulary entries inside one statistics tile (dW = G^T h).  Tokens
+// from n on read as 0.
+struct BKMajorGrad {
+  const char* S;              // exit's scratch at (token lrow, entry v0) (bytes)
+  const char* W;              // the teacher's weights, same place
+  const GradRowConst* tab;    // the exit's constants of the tile's statistics tile, [n]
+  int64_t n, step_bytes;
+  uint32_t rstride;           // bytes between the thread's K rows (16 rows)
+  int lrow, v0;               // the thread's first K row; its chunk's first vocabulary entry
+  bool col_ok;
+  float ge, alpha;
+  bool teacher;
+  unsigned valid;             // bit j: chunk j of the current step exists
+  u32x4 rs[4], rw[4];
+  u32x4 k[4];
+  __device__ __forceinline__ void issue(int gs) {
+    const int64_t base = gs * step_bytes;
+    const int64_t k0 = static_cast<int64_t>(gs) * kPkBK + lrow;
+    valid = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = k0 + 16 * j;
+      if (col_ok && t < n) {
+        valid |= 1u << j;
+        rw[j] = *reinterpret_cast<const u32x4*>(W + base + j * rstride);
+        if (!teacher) rs[j] = *reinterpret_cast<const u32x4*>(S + base + j * rstride);
+        k[j] = *reinterpret_cast<const u32x4*>(tab + t);
+      }
+    }
+  }
+  __device__ __forceinline__ void finish(u32x4 (&hr)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hr[j] = u32x4{0u, 0u, 0u, 0u};
+      if (valid & (1u << j)) {
+        const float c1 = __uint_as_float(k[j][0]), sc = __uint_as_float(k[j][1]);
+        const int yi = static_cast<int32_t>(k[j][2]) - v0;
+        hr[j] = teacher ? grad_chunk_teacher(rw[j], sc, ge, yi)
+                        : grad_chunk_student(rs[j], rw[j], sc, c1, ge, alpha, yi);
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------- GEMM
 // out[b][a] = sum_k A[a][k] B[b][k] for a < a_rows, b < b_rows; A tiled
 // (a_rows % 32 == 0, K % 64 == 0), B row-major with row stride ldb.  One
 // launch covers a group of such products (the exits of a suite): workgroup
 // ids are split by the prefix sums `first` of the products' tile counts, so
-// one product's workgroups fill another's last partial round.
-template <typename OutT, bool KMAJOR>
-__global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
+// one product's workgroups fill another's last partial round.  FUSED: B is
+// the exit's G formed from its scratch (g.B[e]) and the teacher's (g.tw).
+template <typename OutT, bool KMAJOR, bool FUSED>
+__global__ __launch_bounds__(kPkThreads, FUSED ? 1 : 2) void bwd_gemm_kernel(
     BwdGroup /*read through the kernarg pointer*/) {
   // Per-product fields are read through the kernarg segment pointer, which
   // keeps the lookups by a run-time product index scalar.
@@ -105,24 +208,67 @@ __global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
   const int rb0 = min(aw >> 5, a_rows / 32 - 1), rb1 = min((aw >> 5) + 1, a_rows / 32 - 1);
   const char* Ab = reinterpret_cast<const char*>(A);
   f32x16 acc[NTB][NAB];
+  const char* A0 = Ab + static_cast<int64_t>(rb0) * 64 * K;
+  const char* A1 = Ab + static_cast<int64_t>(rb1) * 64 * K;
+  const int nsteps = static_cast<int>(K / kPkBK);
   if constexpr (KMAJOR) {
     const int cols = static_cast<int>(min(b_rows - b0, static_cast<int64_t>(kPkBRows)));
-    packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, Ab + static_cast<int64_t>(rb0) * 64 * K,
-                                      Ab + static_cast<int64_t>(rb1) * 64 * K,
-                                      reinterpret_cast<const char*>(B + b0), ldb, g.k_valid[e],
-                                      cols, static_cast<int>(K / kPkBK));
+    const KMajorLanes kl = kmajor_lanes(tid);
+    if constexpr (FUSED) {
+      BKMajorGrad src;
+      const int64_t off = (static_cast<int64_t>(kl.lrow) * ldb + b0 + 8 * kl.lchunk) * 2;
+      src.S = reinterpret_cast<const char*>(B) + off;
+      src.W = reinterpret_cast<const char*>(g.tw) + off;
+      src.tab = static_cast<const GradRowConst*>(g.tab[e]) + (b0 >> g.vshift) * g.n_tok;
+      src.n = g.k_valid[e];
+      src.step_bytes = int64_t{kPkBK} * ldb * 2;
+      src.rstride = static_cast<uint32_t>(16 * ldb * 2);
+      src.lrow = kl.lrow;
+      src.v0 = static_cast<int>(b0) + 8 * kl.lchunk;
+      src.col_ok = 8 * kl.lchunk < cols;
+      src.ge = g.ge[e];
+      src.alpha = g.alpha;
+      src.teacher = g.teacher[e] != 0;
+      packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, A0, A1, src, nsteps);
+    } else {
+      BKMajorPlain src(reinterpret_cast<const char*>(B + b0), ldb, g.k_valid[e], cols, kl);
+      packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, A0, A1, src, nsteps);
+    }
   } else {
     const PackedLanes pl = packed_lanes(tid);
     uint32_t boff[4];
+    int64_t rows[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t row = min(b0 + pl.brow + 32 * j, b_rows - 1) - b0;
-      boff[j] = static_cast<uint32_t>((row * ldb + pl.bchunk * 8) * 2);
+      rows[j] = min(b0 + pl.brow + 32 * j, b_rows - 1);
+      boff[j] = static_cast<uint32_t>(((rows[j] - b0) * ldb + pl.bchunk * 8) * 2);
     }
-    const char* Bb = reinterpret_cast<const char*>(B) + b0 * ldb * 2;
-    packed_tile_gemm<NTB, NAB>(acc, hs, Ab + static_cast<int64_t>(rb0) * 64 * K,
-                               Ab + static_cast<int64_t>(rb1) * 64 * K, Bb, boff, pl,
-                               static_cast<int>(K / kPkBK));
+    const int64_t tile_off = b0 * ldb * 2;
+    if constexpr (FUSED) {
+      BRowsGrad src;
+      src.S = reinterpret_cast<const char*>(B) + tile_off;
+      src.W = reinterpret_cast<const char*>(g.tw) + tile_off;
+      src.tab = static_cast<const GradRowConst*>(g.tab[e]);
+      src.n = g.n_tok;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        src.row[j] = static_cast<int32_t>(rows[j]);
+        src.boff[j] = boff[j];
+      }
+      src.vlane = 8 * pl.bchunk;
+      src.vshift = g.vshift;
+      src.ge = g.ge[e];
+      src.alpha = g.alpha;
+      src.teacher = g.teacher[e] != 0;
+      src.init();
+      packed_tile_gemm<NTB, NAB>(acc, hs, A0, A1, src, pl, nsteps);
+    } else {
+      BRowsPlain src;
+      src.Bb = reinterpret_cast<const char*>(B) + tile_off;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) src.boff[j] = boff[j];
+      packed_tile_gemm<NTB, NAB>(acc, hs, A0, A1, src, pl, nsteps);
+    }
   }
   // Stores leave through a wave-local LDS transpose, one 32-row block at a
   // time: a lane holds 16 consecutive outputs of one row, but the
@@ -237,11 +383,11 @@ bool bwd_group_add(BwdGroup& g, const void* A, int a_rows, const void* B, int64_
   return true;
 }
 
-template <typename OutT, bool KMAJOR>
+template <typename OutT, bool KMAJOR, bool FUSED>
 hipError_t launch_bwd_group(const BwdGroup& g, hipStream_t s) {
   if (g.count == 0 || g.first[g.count] == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_gemm_kernel<OutT, KMAJOR>), dim3(static_cast<unsigned>(g.first[g.count])),
-                     dim3(kPkThreads), 0, s, g);
+  hipLaunchKernelGGL((bwd_gemm_kernel<OutT, KMAJOR, FUSED>),
+                     dim3(static_cast<unsigned>(g.first[g.count])), dim3(kPkThreads), 0, s, g);
   return hipGetLastError();
 }
 
@@ -250,15 +396,17 @@ hipError_t launch_bwd_gemm(const void* A, int a_rows, const void* B, int64_t b_r
                            int64_t K, OutT* out, int64_t ldo, hipStream_t s) {
   BwdGroup g{};
   if (!bwd_group_add(g, A, a_rows, B, b_rows, ldb, K, out, ldo)) return hipErrorInvalidValue;
-  return launch_bwd_group<OutT, false>(g, s);
+  return launch_bwd_group<OutT, false, false>(g, s);
 }
 
 template hipError_t launch_bwd_gemm<bf16_t>(const void*, int, const void*, int64_t, int64_t,
                                             int64_t, bf16_t*, int64_t, hipStream_t);
 template hipError_t launch_bwd_gemm<float>(const void*, int, const void*, int64_t, int64_t,
                                            int64_t, float*, int64_t, hipStream_t);
-template hipError_t launch_bwd_group<bf16_t, false>(const BwdGroup&, hipStream_t);
-template hipError_t launch_bwd_group<float, false>(const BwdGroup&, hipStream_t);
-template hipError_t launch_bwd_group<float, true>(const BwdGroup&, hipStream_t);
+template hipError_t launch_bwd_group<bf16_t, false, false>(const BwdGroup&, hipStream_t);
+template hipError_t launch_bwd_group<float, false, false>(const BwdGroup&, hipStream_t);
+template hipError_t launch_bwd_group<float, true, false>(const BwdGroup&, hipStream_t);
+template hipError_t launch_bwd_group<bf16_t, false, true>(const BwdGroup&, hipStream_t);
+template hipError_t launch_bwd_group<float, true, true>(const BwdGroup&, hipStream_t);
 
 }  // namespace nel

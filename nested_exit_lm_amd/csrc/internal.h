@@ -125,13 +125,25 @@ struct BwdGroup {
   int a_rows[kMaxExits], n_bt[kMaxExits], n_at[kMaxExits];
   int first[kMaxExits + 1];
   int count;
+  // Fused launches (B = G formed from the packed loss GEMM's fp16 scratch):
+  // B[e] is exit e's scratch, tw the teacher's, tab[e] exit e's row
+  // constants [vocabulary tile][n_tok] (launch_grad_consts), ge[e] its
+  // gradient scale grad_scale * lambda_e, teacher[e] != 0 for the teacher.
+  const uint16_t* tw;
+  const void* tab[kMaxExits];
+  float ge[kMaxExits];
+  int teacher[kMaxExits];
+  int64_t n_tok;
+  int vshift;   // log2 of the statistics tile width
+  float alpha;
 };
 bool bwd_group_add(BwdGroup& g, const void* A, int a_rows, const void* B, int64_t b_rows,
                    int64_t ldb, int64_t K, void* out, int64_t ldo, int64_t k_valid = -1);
 // KMAJOR: B(b, k) is element k * ldb + b of a row-major [K x ldb] matrix
 // (b_rows columns of it; K rows k_valid.. read as 0); else B is row-major
-// [b_rows x ldb] with K contiguous.
-template <typename OutT, bool KMAJOR>
+// [b_rows x ldb] with K contiguous.  FUSED: B is formed from the scratch
+// (the fused fields of the group).
+template <typename OutT, bool KMAJOR, bool FUSED>
 hipError_t launch_bwd_group(const BwdGroup& g, hipStream_t s);
 // Tiled A operand of S^T for S [k_rows, R] row-major, K zero-padded to k_pad.
 hipError_t launch_pack_t(const void* S, int64_t k_rows, int R, int64_t k_pad, void* P,
@@ -175,12 +187,18 @@ hipError_t launch_loss_merge(int n_exits, int64_t n, int vocab, int vtile, const
                              float alpha, const float* stats, const float* lab, float* lse,
                              float* tokloss, double* partials, int32_t* flags, const ExitW& lam,
                              bool skip_dist, hipStream_t s);
-// After the fp16 scratch: every exit's gradient in place, one token row per
-// workgroup, and dv[e][t] = Dist_e from the teacher-weighted logit sums.
+// After the fp16 scratch: every exit's gradient in place (unless !write_g,
+// which leaves the scratch as it is), one token row per workgroup, and
+// dv[e][t] = Dist_e from the teacher-weighted logit sums.
 hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInfo& info,
                                 const int32_t* labels, float alpha, float grad_scale,
                                 const float* stats, const float* lse, void* const* dlogits,
-                                float* dv, const ExitW& lam, hipStream_t s);
+                                float* dv, const ExitW& lam, bool write_g, hipStream_t s);
+// Row constants of the gradients formed from the fp16 scratch: 16 bytes per
+// (exit, vocabulary tile, token) at out + 16 ((e n_vt + tile) n + t).
+hipError_t launch_grad_consts(int n_exits, int64_t n, int vocab, const TileInfo& info,
+                              const int32_t* labels, const float* stats, const float* lse,
+                              void* out, hipStream_t s);
 // The losses and mean partials with Dist from dv (after launch_loss_merge with skip_dist).
 hipError_t launch_loss_finish(int n_exits, int64_t n, float alpha, const float* dv,
                               float* tokloss, double* partials, const ExitW& lam, hipStream_t s);

@@ -25,6 +25,7 @@
 #include <limits.h>
 
 #include "common.h"
+#include "grad_chunk.h"
 #include "internal.h"
 
 namespace nel {
@@ -413,8 +414,11 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
 // q = exp2(s log2 e + (m_e - LSE_e) log2 e), g_e = lambda_e gs (q - a p) and
 // g_M = lambda_M gs p, with the label's entry corrected only in the chunk that
 // holds it; sum_v p l_e over the chunk is sum p s + m_e sum p.  A bad label
-// makes the scale NaN, which turns the whole row into NaN.
-template <int MS>   // the most smaller exits the loops are unrolled for
+// makes the scale NaN, which turns the whole row into NaN.  The gradients
+// come from grad_chunk.h, shared with the backward GEMMs that form them
+// without storing them; WRITE_G = false keeps the buffers as they are and
+// computes dv only (for those GEMMs).
+template <int MS, bool WRITE_G>   // MS: the most smaller exits the loops are unrolled for
 __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int vocab, int vshift,
                                                          const int32_t* __restrict__ labels,
                                                          float alpha, float gs,
@@ -471,51 +475,32 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
         const float scT =
             fexp(stats[static_cast<int64_t>(M - 1) * 3 * plane + tile * n + t] - lseT);
         const int yi = y - v0;   // the label's entry in this chunk when 0 <= yi < 8
-        float p[8], pa[8];
+        float p[8];
         float sp = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           p[i] = Scratch<bf16_t>::get(tw[k], i) * scT;
-          pa[i] = alpha * p[i];
           sp += p[i];
         }
 #pragma unroll
         for (int e = 0; e < MS; ++e) {
           if (e >= S) break;
           const float mt = stats[static_cast<int64_t>(e) * 3 * plane + tile * n + t];
-          const float c1 = (mt - lseE[e]) * kLog2e;
-          float g[8], ps = 0.f;
+          float ps = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float sv = Scratch<bf16_t>::get(sr[e][k], i);
-            ps = fmaf(p[i], sv, ps);
-            g[i] = ge[e] * (__builtin_amdgcn_exp2f(fmaf(sv, kLog2e, c1)) - pa[i]);
-          }
+          for (int i = 0; i < 8; ++i) ps = fmaf(p[i], Scratch<bf16_t>::get(sr[e][k], i), ps);
           acc[e] += fmaf(mt, sp, ps);
-          if (static_cast<unsigned>(yi) < 8u) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              if (i == yi) g[i] -= ge[e] * (1.f - alpha);
+          if constexpr (WRITE_G) {
+            const float c1 = (mt - lseE[e]) * kLog2e;
+            __builtin_nontemporal_store(
+                grad_chunk_student(sr[e][k], tw[k], scT, c1, ge[e], alpha, yi),
+                reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[e]) + t * vocab) + c);
           }
-          u32x4 o;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(g[2 * j], g[2 * j + 1]);
+        }
+        if constexpr (WRITE_G)
           __builtin_nontemporal_store(
-              o, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[e]) + t * vocab) + c);
-        }
-        float g[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) g[i] = gT * p[i];
-        if (static_cast<unsigned>(yi) < 8u) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (i == yi) g[i] -= gT;
-        }
-        u32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(g[2 * j], g[2 * j + 1]);
-        __builtin_nontemporal_store(
-            o, reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
+              grad_chunk_teacher(tw[k], scT, gT, yi),
+              reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
       }
     }
 #pragma unroll
@@ -529,6 +514,42 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
       dv[static_cast<int64_t>(tid) * n + t] = lse[static_cast<int64_t>(tid) * n + t] -
                                               ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]));
     __syncthreads();   // red is reused by the next row
+  }
+}
+
+// Row constants of the gradients that the backward GEMMs form from the fp16
+// scratch (grad_chunk.h), per (vocabulary tile, token) over the plane:
+// exit e < M - 1 gets c1 = (m_e - LSE_e) log2 e, every exit the teacher's
+// sc = exp(m_M - LSE_M) and the label; both are NaN for a bad label, which
+// makes every gradient of that token NaN, as the in-place pass does.  The
+// expressions are those of finalize_rows_f16.
+__global__ __launch_bounds__(256) void grad_consts_kernel(int M, int64_t n, int vocab, int n_vt,
+                                                          const int32_t* __restrict__ labels,
+                                                          const float* __restrict__ stats,
+                                                          const float* __restrict__ lse,
+                                                          GradRowConst* __restrict__ out) {
+  const int64_t plane = static_cast<int64_t>(n_vt) * n;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < plane;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t tile = i / n, t = i - tile * n;
+    const int y = labels[t];
+    const bool bad = y < 0 || y >= vocab;
+    const float nanv = __builtin_nanf("");
+    const float lseT = lse[static_cast<int64_t>(M - 1) * n + t];
+    const float scT = bad ? nanv : fexp(stats[static_cast<int64_t>(M - 1) * 3 * plane + tile * n + t] - lseT);
+    for (int e = 0; e < M; ++e) {
+      float c1 = 0.f;
+      if (e < M - 1) {
+        const float mt = stats[static_cast<int64_t>(e) * 3 * plane + tile * n + t];
+        c1 = bad ? nanv : (mt - lse[static_cast<int64_t>(e) * n + t]) * kLog2e;
+      }
+      u32x4 v;
+      v[0] = __float_as_uint(c1);
+      v[1] = __float_as_uint(scT);
+      v[2] = static_cast<uint32_t>(y);
+      v[3] = 0u;
+      *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(e) * plane + i) = v;
+    }
   }
 }
 
@@ -651,7 +672,7 @@ hipError_t launch_loss_finish(int n_exits, int64_t n, float alpha, const float* 
 hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInfo& info,
                                 const int32_t* labels, float alpha, float grad_scale,
                                 const float* stats, const float* lse, void* const* dlogits,
-                                float* dv, const ExitW& lam, hipStream_t s) {
+                                float* dv, const ExitW& lam, bool write_g, hipStream_t s) {
   if (n == 0) return hipSuccess;
   if (!info.teacher_w16 || vocab % 8 != 0 || (info.vtile & (info.vtile - 1)) != 0)
     return hipErrorInvalidValue;
@@ -661,12 +682,29 @@ hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInf
   // one workgroup per row up to 65536 rows (grid-stride beyond)
   const unsigned grid = static_cast<unsigned>(n < 65536 ? n : 65536);
   const int n_vt = (vocab + info.vtile - 1) / info.vtile;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, vshift, labels, alpha,
+                       grad_scale, stats, lse, dl, n_vt, dv, lam);
+  };
   if (n_exits <= 3)
-    hipLaunchKernelGGL((finalize_rows_f16<2>), dim3(grid), dim3(256), 0, s, n_exits, n, vocab,
-                       vshift, labels, alpha, grad_scale, stats, lse, dl, n_vt, dv, lam);
+    write_g ? go(finalize_rows_f16<2, true>) : go(finalize_rows_f16<2, false>);
   else
-    hipLaunchKernelGGL((finalize_rows_f16<kMaxExits - 1>), dim3(grid), dim3(256), 0, s, n_exits, n,
-                       vocab, vshift, labels, alpha, grad_scale, stats, lse, dl, n_vt, dv, lam);
+    write_g ? go(finalize_rows_f16<kMaxExits - 1, true>)
+            : go(finalize_rows_f16<kMaxExits - 1, false>);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_consts(int n_exits, int64_t n, int vocab, const TileInfo& info,
+                              const int32_t* labels, const float* stats, const float* lse,
+                              void* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (!info.teacher_w16) return hipErrorInvalidValue;   // constants of the fp16 scratch only
+  const int n_vt = (vocab + info.vtile - 1) / info.vtile;
+  const int64_t plane = static_cast<int64_t>(n_vt) * n;
+  const int64_t blocks = (plane + 255) / 256;
+  hipLaunchKernelGGL(grad_consts_kernel, dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)),
+                     dim3(256), 0, s, n_exits, n, vocab, n_vt, labels, stats, lse,
+                     static_cast<GradRowConst*>(out));
   return hipGetLastError();
 }
 

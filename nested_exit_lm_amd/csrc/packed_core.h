@@ -53,22 +53,39 @@ __device__ __forceinline__ PackedLanes packed_lanes(int tid) {
   return p;
 }
 
+// B sources of the main loops.  Per K step a thread copies four 16-byte
+// chunks of B into LDS: issue(g) starts the loads of step g before the
+// step's matrix instructions, finish(hr) hands over the chunks after them.
+//
+// Row-major 16-bit B as stored.
+struct BRowsPlain {
+  const char* Bb;     // byte base of the tile's B row 0
+  uint32_t boff[4];   // byte offsets from Bb of the thread's chunks (+128 per K step)
+  u32x4 r[4];
+  __device__ __forceinline__ void issue(int g) {
+    const char* a = Bb + static_cast<int64_t>(g) * (kPkBK * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const u32x4*>(a + boff[j]);
+  }
+  __device__ __forceinline__ void finish(u32x4 (&hr)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hr[j] = r[j];
+  }
+};
+
 // acc = A(this wavefront's two row blocks) x B(the workgroup's 128 rows)^T
 // over K = 64 * nsteps.
 //   A0, A1: byte bases of the wavefront's two packed A row blocks
-//   Bb:     byte base of the tile's B row 0
-//   boff:   byte offsets from Bb of this thread's four B chunks (per K step
-//           the base advances by 128 bytes)
+//   src:    the B source (chunk i = tid + 256 j of a 128 x 64 slice is row
+//           i / 8, 16-byte chunk i % 8, as packed_lanes assigns them)
 //   hs:     the workgroup's two LDS stages
 // Every wavefront of the workgroup calls this together (it contains barriers).
-template <int NTB, int NAB>
+template <int NTB, int NAB, typename Src>
 __device__ __forceinline__ void packed_tile_gemm(f32x16 (&acc)[NTB][NAB],
                                                  u32x4 (&hs)[2][8 * kPkBRows],
                                                  const char* __restrict__ A0,
-                                                 const char* __restrict__ A1,
-                                                 const char* __restrict__ Bb,
-                                                 const uint32_t (&boff)[4], const PackedLanes& pl,
-                                                 int nsteps) {
+                                                 const char* __restrict__ A1, Src& src,
+                                                 const PackedLanes& pl, int nsteps) {
   static_assert(NAB == 2, "two A row blocks per wavefront");
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb)
@@ -88,12 +105,9 @@ __device__ __forceinline__ void packed_tile_gemm(f32x16 (&acc)[NTB][NAB],
       dst[1][s] = *reinterpret_cast<const u32x4*>(a1 + pl.aoff + s * 1024);
     }
   };
-  auto load_b = [&](int g) {
-    const char* a = Bb + static_cast<int64_t>(g) * (kPkBK * 2);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hr[j] = *reinterpret_cast<const u32x4*>(a + boff[j]);
-  };
+  auto load_b = [&](int g) { src.issue(g); };
   auto store_b = [&](int st) {
+    src.finish(hr);
 #pragma unroll
     for (int j = 0; j < 4; ++j) hs[st][pl.hslot + 32 * j] = hr[j];
   };
@@ -134,6 +148,47 @@ __device__ __forceinline__ void packed_tile_gemm(f32x16 (&acc)[NTB][NAB],
   if (g < nsteps) step(R0, R1, g, 0);
 }
 
+// The B source's thread copies, per K step gs, 16-byte chunk tid % 16 of
+// the slice's K rows tid / 16 + 16 j (KMajorLanes).
+struct KMajorLanes {
+  int lrow, lchunk;
+};
+__device__ __forceinline__ KMajorLanes kmajor_lanes(int tid) { return {tid >> 4, tid & 15}; }
+
+// K-major 16-bit B as stored.
+struct BKMajorPlain {
+  const char* Bb;     // byte address of element (k = 0, column b0) of the tile
+  int64_t step_bytes; // 64 K rows
+  int64_t k_valid;    // K rows that exist (the rest read as 0)
+  uint32_t boff[4];
+  int lrow;
+  bool col_ok;        // the thread's 8 columns exist
+  u32x4 r[4];
+  // ldb: row stride of the K-major matrix, in elements (< 2^24);
+  // cols_valid: columns of this tile that exist (a multiple of 8, <= 128)
+  __device__ __forceinline__ BKMajorPlain(const char* b, int64_t ldb, int64_t kv, int cols_valid,
+                                          KMajorLanes kl)
+      : Bb(b), step_bytes(int64_t{kPkBK} * ldb * 2), k_valid(kv), lrow(kl.lrow),
+        col_ok(8 * kl.lchunk < cols_valid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      boff[j] = static_cast<uint32_t>(((kl.lrow + 16 * j) * ldb + 8 * kl.lchunk) * 2);
+  }
+  __device__ __forceinline__ void issue(int gs) {
+    const char* base = Bb + gs * step_bytes;
+    const int64_t k0 = static_cast<int64_t>(gs) * kPkBK + lrow;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r[j] = u32x4{0u, 0u, 0u, 0u};
+      if (col_ok && k0 + 16 * j < k_valid) r[j] = *reinterpret_cast<const u32x4*>(base + boff[j]);
+    }
+  }
+  __device__ __forceinline__ void finish(u32x4 (&hr)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hr[j] = r[j];
+  }
+};
+
 // Variant whose B operand is stored K-major: B(b, k) is the element at
 // (k * ldb + b) of a row-major [K x ldb] matrix, e.g. the logit gradients
 // G [tokens x vocabulary] when the product runs over tokens (dW = G^T h).
@@ -148,17 +203,12 @@ __device__ __forceinline__ void packed_tile_gemm(f32x16 (&acc)[NTB][NAB],
 // 16 s + 8 h .. +7 of column q, so source lane S = 16 g + 4 j + a (g = S / 16)
 // addresses K row 16 s + 8 (g / 2) + j (+ 4 for the second load) at column
 // 32 tb + 16 (g mod 2) + 4 a.
-//   Bb:         byte address of element (k = 0, column b0) of the tile
-//   ldb:        row stride of the K-major matrix, in elements (< 2^24)
-//   k_valid:    K rows that exist (rows k_valid .. 64 nsteps - 1 read as 0)
-//   cols_valid: columns of this tile that exist (a multiple of 8, <= 128)
-template <int NTB, int NAB>
+//   src: the B source (threads as kmajor_lanes assigns them)
+template <int NTB, int NAB, typename Src>
 __device__ __forceinline__ void packed_tile_gemm_kmajor(f32x16 (&acc)[NTB][NAB],
                                                         u32x4 (&hs)[2][8 * kPkBRows],
                                                         const char* __restrict__ A0,
-                                                        const char* __restrict__ A1,
-                                                        const char* __restrict__ Bb, int64_t ldb,
-                                                        int64_t k_valid, int cols_valid,
+                                                        const char* __restrict__ A1, Src& src,
                                                         int nsteps) {
   static_assert(NAB == 2 && NTB * 32 == kPkBRows, "128 columns, two A row blocks per wavefront");
   typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -172,14 +222,8 @@ __device__ __forceinline__ void packed_tile_gemm_kmajor(f32x16 (&acc)[NTB][NAB],
       for (int r = 0; r < 16; ++r) acc[tb][ab][r] = 0.f;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  // loads: K row tid / 16 + 16 j of the slice, 16-byte chunk tid % 16
-  const int lrow = tid >> 4, lchunk = tid & 15;
-  const bool col_ok = 8 * lchunk < cols_valid;
-  uint32_t boff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    boff[j] = static_cast<uint32_t>(((lrow + 16 * j) * ldb + 8 * lchunk) * 2);
-  const int wslot = lrow * 16 + (lchunk ^ ((lrow & 3) << 2));   // + 256 j per row group
+  const KMajorLanes kl = kmajor_lanes(tid);
+  const int wslot = kl.lrow * 16 + (kl.lchunk ^ ((kl.lrow & 3) << 2));   // + 256 j per row group
   // fragment reads: byte offset in a stage of (s = 0, load 0) for block tb
   const int g = lane >> 4, ja = (lane >> 2) & 3, aa = lane & 3;
   uint32_t roff[NTB];
@@ -187,7 +231,6 @@ __device__ __forceinline__ void packed_tile_gemm_kmajor(f32x16 (&acc)[NTB][NAB],
   for (int tb = 0; tb < NTB; ++tb)
     roff[tb] = static_cast<uint32_t>((8 * (g >> 1) + ja) * 256 + 64 * (tb ^ ja) + 32 * (g & 1) + 8 * aa);
   const uint32_t aoff = static_cast<uint32_t>(lane) * 16u;
-  const int64_t step_bytes = int64_t{kPkBK} * ldb * 2;
 
   u32x4 R0[NAB][4], R1[NAB][4], hr[4];
   auto load_a = [&](u32x4 (&dst)[NAB][4], int gs) {
@@ -199,16 +242,9 @@ __device__ __forceinline__ void packed_tile_gemm_kmajor(f32x16 (&acc)[NTB][NAB],
       dst[1][s] = *reinterpret_cast<const u32x4*>(a1 + aoff + s * 1024);
     }
   };
-  auto load_b = [&](int gs) {
-    const char* base = Bb + gs * step_bytes;
-    const int64_t k0 = static_cast<int64_t>(gs) * kPkBK + lrow;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      hr[j] = u32x4{0u, 0u, 0u, 0u};
-      if (col_ok && k0 + 16 * j < k_valid) hr[j] = *reinterpret_cast<const u32x4*>(base + boff[j]);
-    }
-  };
+  auto load_b = [&](int g) { src.issue(g); };
   auto store_b = [&](int st) {
+    src.finish(hr);
 #pragma unroll
     for (int j = 0; j < 4; ++j) hs[st][wslot + 256 * j] = hr[j];
   };

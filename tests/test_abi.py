@@ -20,7 +20,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = nel.load()
     syms = declared_symbols()
-    assert len(syms) == 24
+    assert len(syms) == 26
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -227,6 +227,51 @@ def test_heads_backward_host_validation():
     assert call(ws=MIS) == -4
     assert call(ws=None) == -5
     assert call(wsb=need - 1) == -5
+
+
+def test_loss_backward_host_validation():
+    """Every call below fails a host check before the first launch (FAKE
+    pointers are never dereferenced)."""
+    lib = nel.load()
+    d2 = _arr(ctypes.c_int32, 64, 128)
+    need = nel.loss_backward_workspace_size(100, 256, [64, 128])
+    assert need > nel.heads_backward_workspace_size(100, 256, [64, 128])
+    assert nel.loss_backward_workspace_size(100, 256, [64, 96]) == 0
+    assert nel.loss_backward_workspace_size(100, 250, [64, 128]) == 0
+    assert lib.nel_loss_backward_workspace(9, 100, 256, d2) == 0
+    p2 = _arr(ctypes.c_void_p, FAKE, FAKE)
+
+    def call(dt=1, E=2, n=100, V=256, d=d2, h=p2, w=p2, wp=p2, labels=FAKE, alpha=0.3, gs=1.0,
+             lam=None, tok=FAKE, mean=FAKE, scr=p2, dh=p2, dw=p2, ws=FAKE, wsb=need):
+        return lib.nel_matryoshka_loss_backward_packed(dt, E, n, V, d, h, w, wp, labels, alpha,
+                                                       gs, lam, tok, mean, scr, dh, dw, ws, wsb,
+                                                       None)
+
+    assert call(dt=0) == -3                 # bf16 only
+    assert call(E=0) == -1
+    assert call(E=9) == -1
+    assert call(d=None) == -1
+    assert call(V=250) == -2                # vocabulary a multiple of 64
+    assert call(d=_arr(ctypes.c_int32, 64, 96)) == -2
+    assert call(n=-1) == -2
+    assert call(dh=None, dw=None) == -1     # nothing to compute
+    assert call(scr=None) == -1
+    assert call(wp=_arr(ctypes.c_void_p, FAKE, None)) == -1
+    assert call(dw=_arr(ctypes.c_void_p, None, FAKE)) == -1
+    assert call(scr=_arr(ctypes.c_void_p, FAKE, MIS)) == -4
+    assert call(dh=_arr(ctypes.c_void_p, MIS, FAKE)) == -4
+    assert call(ws=MIS) == -4
+    assert call(ws=None) == -5
+    assert call(wsb=need - 1) == -5
+    # checked by the loss, still before anything is launched
+    assert call(d=_arr(ctypes.c_int32, 128, 128),          # widths must increase strictly
+                wsb=nel.loss_backward_workspace_size(100, 256, [128, 128])) == -2
+    assert call(alpha=1.5) == -1
+    assert call(gs=float("inf")) == -1
+    assert call(lam=_arr(ctypes.c_float, 1.0, -1.0)) == -1
+    assert call(mean=None) == -1
+    assert call(labels=None) == -1
+    assert call(labels=MIS4) == -4
 
 
 def test_junction_backward_host_validation():

@@ -296,7 +296,8 @@ def main():
     if not args.no_verify:
         out["verify_102x7"] = bench_verify(nel, torch, synth, dev, args)
     if not args.no_backward:
-        out["backward"] = bench_backward(nel, torch, hs, ws, dl, args, ids=ids, embs=embs)
+        out["backward"] = bench_backward(nel, torch, hs, ws, dl, args, ids=ids, embs=embs,
+                                         pw=pw, labels=labels, alpha=s.alpha)
     if not args.no_variants:
         out["variants"] = bench_variants(nel, torch, hs, pw, labels, dl, wsb, mean, tok, s.alpha,
                                          args, ids=ids, embs=embs)
@@ -353,10 +354,13 @@ def summarize_counters(fetch_dir, write_dir):
     print(json.dumps(res))
 
 
-def bench_backward(nel, torch, hs, ws, dl, args, ids=None, embs=None):
+def bench_backward(nel, torch, hs, ws, dl, args, ids=None, embs=None, pw=None, labels=None,
+                   alpha=0.3):
     """Backward of the three exit heads on the step's own logit gradients:
     dh_m = G_m W^m (bf16) and dW^m = G_m^T h_m (fp32), with the W and h operand packs;
-    and the backward of both junctions on seeded synthetic upstream gradients."""
+    the backward of both junctions on seeded synthetic upstream gradients; and (with
+    the packed heads and labels) the loss plus head backward with stored gradients
+    against the fused call that never stores them."""
     N, V = dl[0].shape
     D = [h.shape[1] for h in hs]
     need = nel.heads_backward_workspace_size(N, V, D)
@@ -428,7 +432,68 @@ def bench_backward(nel, torch, hs, ws, dl, args, ids=None, embs=None):
                      + V * 4 * (D[m] - D[m - 1]) for m in (1, 2))
         res["junction_bwd_ms"] = tot / steps
         res["junction_bwd_gbs"] = jbytes / (tot / steps / 1e3) / 1e9
+    if pw is not None and labels is not None:
+        res["fused"] = bench_fused(nel, torch, hs, ws, pw, labels, dl, dhs, dws, wsb, alpha, steps)
     return res
+
+
+def bench_fused(nel, torch, hs, ws, pw, labels, dl, dhs, dws, bwd_ws, alpha, steps):
+    """Loss plus the backward of every head, two ways on the same inputs: stored
+    (the loss writes the logit gradients G, then the grouped dh and dW GEMMs read
+    them) and fused (one call; the dh and dW GEMMs form G from the loss pass's fp16
+    scratch, bit-identical results, G never written).  The dl buffers serve as the
+    stored gradients and as the fused call's scratch."""
+    N, V = dl[0].shape
+    D = [h.shape[1] for h in hs]
+    M = len(D)
+    dev = hs[0].device
+    lw = torch.zeros(nel.workspace_size(nel.OP_LOSS, M, N, V), dtype=torch.uint8, device=dev)
+    fw = torch.zeros(nel.loss_backward_workspace_size(N, V, D), dtype=torch.uint8, device=dev)
+    mean = torch.empty(3 * M + 1, dtype=torch.float32, device=dev)
+    tok = torch.empty(M, 3, N, dtype=torch.float32, device=dev)
+
+    def stored():
+        nel.matryoshka_loss_packed(hs, pw, labels, alpha_d=alpha, dlogits=dl, workspace=lw,
+                                   mean_loss=mean, token_loss=tok)
+        nel.heads_backward(dl, hs, ws, dhs=dhs, dws=dws, workspace=bwd_ws)
+
+    def fused():
+        nel.loss_backward_packed(hs, ws, pw, labels, alpha_d=alpha, scratch=dl, dhs=dhs,
+                                 dws=dws, mean_loss=mean, token_loss=tok, workspace=fw)
+
+    flops = 2.0 * N * V * sum(D)          # per GEMM kind (forward, dh, dW), all exits
+    out = {"work": "loss (fwd + gradients) and dh, dW of all three heads; the weight "
+                   "packs (W^T, h^T) included, the forward's weight pack not",
+           "steps": steps}
+    names = ("heads_loss", "merge", "finalize", "means", "grad_consts", "bwd_pack", "bwd_dh",
+             "bwd_dw")
+    for key, fn in (("stored", stored), ("fused", fused)):
+        fn()
+        torch.cuda.synchronize()
+        nel.timing_reset()
+        nel.timing_enable(True)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        nel.timing_enable(False)
+        k = {}
+        for nm in names:
+            tot, cnt = nel.timing_read(nm)
+            if cnt:
+                k[nm + "_ms"] = tot / steps
+        k["dh_tflops"] = flops / (k["bwd_dh_ms"] / 1e3) / 1e12
+        k["dw_tflops"] = flops / (k["bwd_dw_ms"] / 1e3) / 1e12
+        k["dh_mfma_frac"] = k["dh_tflops"] / BF16_PEAK_TFLOPS
+        k["dw_mfma_frac"] = k["dw_tflops"] / BF16_PEAK_TFLOPS
+        out[key] = {"ms_per_step": e0.elapsed_time(e1) / steps,
+                    "tokens_per_s": N / (e0.elapsed_time(e1) / steps / 1e3), "kernels": k}
+    out["fused_speedup"] = out["stored"]["ms_per_step"] / out["fused"]["ms_per_step"]
+    del lw, fw
+    return out
 
 
 def bench_reference(torch, dev):

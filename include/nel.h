@@ -226,7 +226,7 @@ size_t nel_speculative_workspace(int32_t batch, int32_t draft_len);
  *           first int32 is the device flag word.
  * No fp32 logit tensor is ever written to memory.  With NEL_DIV_FORWARD the
  * distillation term comes from fp32 logits; the other divergences are summed
- * from the stored shifted logits (bf16 for dt = NEL_BF16).
+ * from the stored shifted logits (fp16 for dt = NEL_BF16).
  * Errors: NEL_EINVAL if alpha_d is outside [0,1], n_exits outside [1,8], a
  * weight is negative or not finite, the divergence is unknown, or it needs
  * dlogits and they are NULL.
@@ -265,7 +265,7 @@ nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* 
  * NEL_DIV_FORWARD the teacher's holds its softmax weights exp(l_M - m) (m the
  * 256-entry tile maximum) and the smaller exits' hold l - m, all fp16; the
  * gradient pass forms the teacher-weighted logit sums of Dist from them.  The
- * other divergences store l - m in bf16 for every exit.  Every dlogits buffer
+ * other divergences store l - m in fp16 for every exit.  Every dlogits buffer
  * is scratch until the call's work on `stream` has completed.
  */
 nel_status nel_matryoshka_loss_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens,

@@ -108,13 +108,17 @@ __device__ __forceinline__ void packed16_tile_gemm(f32x4 (&acc)[kNTB][kNVB],
     fsl[kh] = 128 * c + (x ^ (2 * c));
   }
   const uint32_t aoff = static_cast<uint32_t>(lane) * 16u;
-  u32x4 R0[kNVB][2], R1[kNVB][2], hr[4];
-  auto load_a = [&](u32x4 (&dst)[kNVB][2], int gs) {
+  // One set of W fragments: R[vb][kh] is reloaded for the next step as soon
+  // as the current step's last matrix instruction that reads it has issued
+  // (kh = 0 after the first half of the step, kh = 1 after the second), and
+  // the next step's h slice is loaded at the start of the step, so every
+  // load has at least half a step of this wavefront's matrix instructions
+  // ahead of its first use without a second register set.
+  u32x4 R[kNVB][2], hr[4];
+  auto load_a = [&](int kh, int gs) {
 #pragma unroll
     for (int vb = 0; vb < kNVB; ++vb)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-        dst[vb][kh] = *reinterpret_cast<const u32x4*>(Wb[vb] + static_cast<int64_t>(2 * gs + kh) * 1024 + aoff);
+      R[vb][kh] = *reinterpret_cast<const u32x4*>(Wb[vb] + static_cast<int64_t>(2 * gs + kh) * 1024 + aoff);
   };
   auto load_b = [&](int gs) {
     const char* a = Hb + static_cast<int64_t>(gs) * (kPkBK * 2);
@@ -125,41 +129,45 @@ __device__ __forceinline__ void packed16_tile_gemm(f32x4 (&acc)[kNTB][kNVB],
 #pragma unroll
     for (int j = 0; j < 4; ++j) hs[st][hslot + 32 * j] = hr[j];
   };
-  auto mfma = [&](const u32x4 (&cur)[kNVB][2], int st) {
+  auto mfma = [&](int kh, int st) {
+    bf16x8 b[kNTB];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      bf16x8 b[kNTB];
+    for (int tb = 0; tb < kNTB; ++tb) b[tb] = __builtin_bit_cast(bf16x8, hs[st][fsl[kh] + 16 * tb]);
 #pragma unroll
-      for (int tb = 0; tb < kNTB; ++tb) b[tb] = __builtin_bit_cast(bf16x8, hs[st][fsl[kh] + 16 * tb]);
+    for (int vb = 0; vb < kNVB; ++vb) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, R[vb][kh]);
 #pragma unroll
-      for (int vb = 0; vb < kNVB; ++vb) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, cur[vb][kh]);
-#pragma unroll
-        for (int tb = 0; tb < kNTB; ++tb)
-          acc[tb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[tb], acc[tb][vb], 0, 0, 0);
-      }
+      for (int tb = 0; tb < kNTB; ++tb)
+        acc[tb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[tb], acc[tb][vb], 0, 0, 0);
     }
   };
-  // step gs: prefetch step gs + 1 (the last step re-reads itself), compute
-  // step gs from LDS stage st, publish the prefetched h slice in stage st ^ 1
-  auto step = [&](const u32x4 (&cur)[kNVB][2], u32x4 (&nxt)[kNVB][2], int gs, int st) {
+  // step gs: compute step gs from LDS stage st while loading step gs + 1
+  // (the last step re-reads itself), publish its h slice in stage st ^ 1
+  auto step = [&](int gs, int st) {
     const int gn = gs + 1 < nsteps ? gs + 1 : gs;
     load_b(gn);
-    load_a(nxt, gn);
-    mfma(cur, st);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(0, st);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(0, gn);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(1, st);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(1, gn);
     store_b(st ^ 1);
     __syncthreads();
   };
   load_b(0);
   store_b(0);
-  load_a(R0, 0);
+  load_a(0, 0);
+  load_a(1, 0);
   __syncthreads();
   int gs = 0;
   for (; gs + 2 <= nsteps; gs += 2) {
-    step(R0, R1, gs, 0);
-    step(R1, R0, gs + 1, 1);
+    step(gs, 0);
+    step(gs + 1, 1);
   }
-  if (gs < nsteps) step(R0, R1, gs, 0);
+  if (gs < nsteps) step(gs, 0);
 }
 
 // ---------------------------------------------------------------- GEMM

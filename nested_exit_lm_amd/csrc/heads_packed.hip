@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ w,
 // thread's four 16-byte h chunks (per step the base advances 128 bytes).
 // Every wavefront of the workgroup calls this together (it has barriers).
 __device__ __forceinline__ void packed16_tile_gemm(f32x4 (&acc)[kNTB][kNVB],
-                                                   u32x4 (&hs)[2][8 * kPkBRows],
+                                                   u32x4 (&hs)[2][16 * kPkBRows],
                                                    const char* const (&Wb)[kNVB],
                                                    const char* __restrict__ Hb,
                                                    const uint32_t (&hoff)[4], int hslot,
@@ -125,14 +125,15 @@ __device__ __forceinline__ void packed16_tile_gemm(f32x4 (&acc)[kNTB][kNVB],
 #pragma unroll
     for (int j = 0; j < 4; ++j) hr[j] = *reinterpret_cast<const u32x4*>(a + hoff[j]);
   };
-  auto store_b = [&](int st) {
+  auto store_b = [&](int st, int q) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hs[st][hslot + 32 * j] = hr[j];
+    for (int j = 0; j < 4; ++j) hs[st][1024 * q + hslot + 32 * j] = hr[j];
   };
-  auto mfma = [&](int kh, int st) {
+  auto mfma = [&](int kh, int st, int q) {
     bf16x8 b[kNTB];
 #pragma unroll
-    for (int tb = 0; tb < kNTB; ++tb) b[tb] = __builtin_bit_cast(bf16x8, hs[st][fsl[kh] + 16 * tb]);
+    for (int tb = 0; tb < kNTB; ++tb)
+      b[tb] = __builtin_bit_cast(bf16x8, hs[st][1024 * q + fsl[kh] + 16 * tb]);
 #pragma unroll
     for (int vb = 0; vb < kNVB; ++vb) {
       const bf16x8 a = __builtin_bit_cast(bf16x8, R[vb][kh]);
@@ -141,33 +142,41 @@ __device__ __forceinline__ void packed16_tile_gemm(f32x4 (&acc)[kNTB][kNVB],
         acc[tb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[tb], acc[tb][vb], 0, 0, 0);
     }
   };
-  // step gs: compute step gs from LDS stage st while loading step gs + 1
-  // (the last step re-reads itself), publish its h slice in stage st ^ 1
-  auto step = [&](int gs, int st) {
-    const int gn = gs + 1 < nsteps ? gs + 1 : gs;
-    load_b(gn);
+  // Steps go in pairs: stage st holds the h slices of steps 2p and 2p + 1
+  // (sub-stages q = 0, 1), so the workgroup meets at a barrier once per two
+  // steps.  Step g = 2p + q computes from sub-stage q while it loads the h
+  // slice of step g + 2 (into the other stage's sub-stage q) and the W
+  // fragments of step g + 1; loads past the last step re-read it.
+  const int last = nsteps - 1;
+  auto step = [&](int gi, int st, int q) {
+    load_b(min(gi + 2, last));
     __builtin_amdgcn_sched_barrier(0);
-    mfma(0, st);
+    mfma(0, st, q);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(0, gn);
+    load_a(0, min(gi + 1, last));
     __builtin_amdgcn_sched_barrier(0);
-    mfma(1, st);
+    mfma(1, st, q);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(1, gn);
-    store_b(st ^ 1);
-    __syncthreads();
+    load_a(1, min(gi + 1, last));
+    store_b(st ^ 1, q);
   };
   load_b(0);
-  store_b(0);
+  store_b(0, 0);
+  load_b(min(1, last));
+  store_b(0, 1);
   load_a(0, 0);
   load_a(1, 0);
   __syncthreads();
-  int gs = 0;
-  for (; gs + 2 <= nsteps; gs += 2) {
-    step(gs, 0);
-    step(gs + 1, 1);
+  int gs = 0, st = 0;
+  for (; gs + 2 <= nsteps; gs += 2, st ^= 1) {
+    step(gs, st, 0);
+    step(gs + 1, st, 1);
+    __syncthreads();
   }
-  if (gs < nsteps) step(gs, 0);
+  if (gs < nsteps) {   // an odd last step; the barrier frees LDS for the epilogue
+    step(gs, st, 0);
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
   // The exit table is the first kernel argument; indexing it through the
   // kernarg segment pointer keeps per-exit lookups scalar.
   const ExitSet& ex = *(const ExitSet*)__builtin_amdgcn_kernarg_segment_ptr();
-  __shared__ u32x4 hs[2][8 * kPkTok];
+  __shared__ u32x4 hs[2][16 * kPkTok];
   __shared__ float xmax[4][kPkTok];
   __shared__ float xsum[4][kPkTok][2];
 

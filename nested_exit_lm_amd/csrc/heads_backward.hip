@@ -136,6 +136,7 @@ struct BRowsGrad {
 // 128 vocabulary entries inside one statistics tile (dW = G^T h).  Tokens
 // from n on read as 0.
 struct BKMajorGrad {
+  static constexpr bool kPinLoads = true;
   const char* S;              // exit's scratch at (token lrow, entry v0) (bytes)
   const char* W;              // the teacher's weights, same place
   const GradRowConst* tab;    // the exit's constants of the tile's statistics tile, [n]
@@ -185,7 +186,7 @@ struct BKMajorGrad {
 // one product's workgroups fill another's last partial round.  FUSED: B is
 // the exit's G formed from its scratch (g.B[e]) and the teacher's (g.tw).
 template <typename OutT, bool KMAJOR, bool FUSED>
-__global__ __launch_bounds__(kPkThreads, FUSED ? 1 : 2) void bwd_gemm_kernel(
+__global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
     BwdGroup /*read through the kernarg pointer*/) {
   // Per-product fields are read through the kernarg segment pointer, which
   // keeps the lookups by a run-time product index scalar.

@@ -94,58 +94,64 @@ __device__ __forceinline__ void packed_tile_gemm(f32x16 (&acc)[NTB][NAB],
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tb][ab][r] = 0.f;
 
-  u32x4 R0[NAB][4], R1[NAB][4], hr[4];
-  // A operands of step g: blocks kp = 4g + s of the two row blocks
-  auto load_a = [&](u32x4 (&dst)[NAB][4], int g) {
+  // One set of A fragments R[ab][s]: the half s = 2h, 2h + 1 is reloaded for
+  // the next step right after the step's last matrix instruction that reads
+  // it, and the B source's loads for the next step start with the step, so
+  // every load has half a step of this wavefront's matrix instructions ahead
+  // of its first use (the scheduling barriers keep that order).
+  u32x4 R[NAB][4], hr[4];
+  // A operands of step g, K slices s = 2h, 2h + 1: blocks kp = 4g + s
+  auto load_a = [&](int h, int g) {
     const char* a0 = A0 + static_cast<int64_t>(g) * 4096;
     const char* a1 = A1 + static_cast<int64_t>(g) * 4096;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      dst[0][s] = *reinterpret_cast<const u32x4*>(a0 + pl.aoff + s * 1024);
-      dst[1][s] = *reinterpret_cast<const u32x4*>(a1 + pl.aoff + s * 1024);
+    for (int s = 2 * h; s < 2 * h + 2; ++s) {
+      R[0][s] = *reinterpret_cast<const u32x4*>(a0 + pl.aoff + s * 1024);
+      R[1][s] = *reinterpret_cast<const u32x4*>(a1 + pl.aoff + s * 1024);
     }
   };
-  auto load_b = [&](int g) { src.issue(g); };
   auto store_b = [&](int st) {
     src.finish(hr);
 #pragma unroll
     for (int j = 0; j < 4; ++j) hs[st][pl.hslot + 32 * j] = hr[j];
   };
-  auto mfma = [&](const u32x4 (&cur)[NAB][4], int st) {
+  auto mfma = [&](int h, int st) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 2 * h; s < 2 * h + 2; ++s) {
       bf16x8 b[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) b[tb] = __builtin_bit_cast(bf16x8, hs[st][pl.bslot[s] + 32 * tb]);
 #pragma unroll
       for (int ab = 0; ab < NAB; ++ab) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, cur[ab][s]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, R[ab][s]);
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
           acc[tb][ab] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[tb], acc[tb][ab], 0, 0, 0);
       }
     }
   };
-  // Step g: prefetch step g + 1 (the last step re-reads itself), compute
-  // step g from LDS stage st, publish the prefetched B slice in stage st ^ 1.
-  auto step = [&](const u32x4 (&cur)[NAB][4], u32x4 (&nxt)[NAB][4], int g, int st) {
+  // Step g: compute step g from LDS stage st while loading step g + 1 (the
+  // last step re-reads itself), publish the loaded B slice in stage st ^ 1.
+  auto step = [&](int g, int st) {
     const int gn = g + 1 < nsteps ? g + 1 : g;
-    load_b(gn);
-    load_a(nxt, gn);
-    mfma(cur, st);
+    src.issue(gn);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(0, st);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(0, gn);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(1, st);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(1, gn);
     store_b(st ^ 1);
     __syncthreads();
   };
-  load_b(0);
+  src.issue(0);
   store_b(0);
-  load_a(R0, 0);
+  load_a(0, 0);
+  load_a(1, 0);
   __syncthreads();
-  int g = 0;
-  for (; g + 2 <= nsteps; g += 2) {
-    step(R0, R1, g, 0);
-    step(R1, R0, g + 1, 1);
-  }
-  if (g < nsteps) step(R0, R1, g, 0);
+  for (int g = 0; g < nsteps; ++g) step(g, g & 1);
 }
 
 // The B source's thread copies, per K step gs, 16-byte chunk tid % 16 of
@@ -157,6 +163,7 @@ __device__ __forceinline__ KMajorLanes kmajor_lanes(int tid) { return {tid >> 4,
 
 // K-major 16-bit B as stored.
 struct BKMajorPlain {
+  static constexpr bool kPinLoads = false;
   const char* Bb;     // byte address of element (k = 0, column b0) of the tile
   int64_t step_bytes; // 64 K rows
   int64_t k_valid;    // K rows that exist (the rest read as 0)
@@ -232,26 +239,86 @@ __device__ __forceinline__ void packed_tile_gemm_kmajor(f32x16 (&acc)[NTB][NAB],
     roff[tb] = static_cast<uint32_t>((8 * (g >> 1) + ja) * 256 + 64 * (tb ^ ja) + 32 * (g & 1) + 8 * aa);
   const uint32_t aoff = static_cast<uint32_t>(lane) * 16u;
 
-  u32x4 R0[NAB][4], R1[NAB][4], hr[4];
-  auto load_a = [&](u32x4 (&dst)[NAB][4], int gs) {
+  if constexpr (!Src::kPinLoads) {
+    // compiler-scheduled, two A register sets (measured faster for plain
+    // K-major B than the pinned order below)
+    u32x4 R0[NAB][4], R1[NAB][4], hr2[4];
+    auto load_a2 = [&](u32x4 (&dst)[NAB][4], int gs) {
+      const char* a0 = A0 + static_cast<int64_t>(gs) * 4096;
+      const char* a1 = A1 + static_cast<int64_t>(gs) * 4096;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        dst[0][s] = *reinterpret_cast<const u32x4*>(a0 + aoff + s * 1024);
+        dst[1][s] = *reinterpret_cast<const u32x4*>(a1 + aoff + s * 1024);
+      }
+    };
+    auto store_b2 = [&](int st) {
+      src.finish(hr2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hs[st][wslot + 256 * j] = hr2[j];
+    };
+    auto mfma2 = [&](const u32x4 (&cur)[NAB][4], int st) {
+      const char* stage = reinterpret_cast<const char*>(&hs[st][0]);
+  #pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 b[NTB];
+  #pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+          const char* p = stage + roff[tb] + 16 * s * 256;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 256));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          b[tb] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+        }
+  #pragma unroll
+        for (int ab = 0; ab < NAB; ++ab) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, cur[ab][s]);
+  #pragma unroll
+          for (int tb = 0; tb < NTB; ++tb)
+            acc[tb][ab] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[tb], acc[tb][ab], 0, 0, 0);
+        }
+      }
+    };
+    auto step2 = [&](const u32x4 (&cur)[NAB][4], u32x4 (&nxt)[NAB][4], int gs, int st) {
+      const int gn = gs + 1 < nsteps ? gs + 1 : gs;
+      src.issue(gn);
+      load_a2(nxt, gn);
+      mfma2(cur, st);
+      store_b2(st ^ 1);
+      __syncthreads();
+    };
+    src.issue(0);
+    store_b2(0);
+    load_a2(R0, 0);
+    __syncthreads();
+    int gs = 0;
+    for (; gs + 2 <= nsteps; gs += 2) {
+      step2(R0, R1, gs, 0);
+      step2(R1, R0, gs + 1, 1);
+    }
+    if (gs < nsteps) step2(R0, R1, gs, 0);
+    return;
+  }
+  // A fragments and load order as in packed_tile_gemm
+  u32x4 R[NAB][4], hr[4];
+  auto load_a = [&](int h, int gs) {
     const char* a0 = A0 + static_cast<int64_t>(gs) * 4096;
     const char* a1 = A1 + static_cast<int64_t>(gs) * 4096;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      dst[0][s] = *reinterpret_cast<const u32x4*>(a0 + aoff + s * 1024);
-      dst[1][s] = *reinterpret_cast<const u32x4*>(a1 + aoff + s * 1024);
+    for (int s = 2 * h; s < 2 * h + 2; ++s) {
+      R[0][s] = *reinterpret_cast<const u32x4*>(a0 + aoff + s * 1024);
+      R[1][s] = *reinterpret_cast<const u32x4*>(a1 + aoff + s * 1024);
     }
   };
-  auto load_b = [&](int g) { src.issue(g); };
   auto store_b = [&](int st) {
     src.finish(hr);
 #pragma unroll
     for (int j = 0; j < 4; ++j) hs[st][wslot + 256 * j] = hr[j];
   };
-  auto mfma = [&](const u32x4 (&cur)[NAB][4], int st) {
+  auto mfma = [&](int h, int st) {
     const char* stage = reinterpret_cast<const char*>(&hs[st][0]);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 2 * h; s < 2 * h + 2; ++s) {
       bf16x8 b[NTB];
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
@@ -263,31 +330,33 @@ __device__ __forceinline__ void packed_tile_gemm_kmajor(f32x16 (&acc)[NTB][NAB],
       }
 #pragma unroll
       for (int ab = 0; ab < NAB; ++ab) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, cur[ab][s]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, R[ab][s]);
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
           acc[tb][ab] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[tb], acc[tb][ab], 0, 0, 0);
       }
     }
   };
-  auto step = [&](const u32x4 (&cur)[NAB][4], u32x4 (&nxt)[NAB][4], int gs, int st) {
+  auto step = [&](int gs, int st) {
     const int gn = gs + 1 < nsteps ? gs + 1 : gs;
-    load_b(gn);
-    load_a(nxt, gn);
-    mfma(cur, st);
+    src.issue(gn);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(0, st);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(0, gn);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(1, st);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(1, gn);
     store_b(st ^ 1);
     __syncthreads();
   };
-  load_b(0);
+  src.issue(0);
   store_b(0);
-  load_a(R0, 0);
+  load_a(0, 0);
+  load_a(1, 0);
   __syncthreads();
-  int gs = 0;
-  for (; gs + 2 <= nsteps; gs += 2) {
-    step(R0, R1, gs, 0);
-    step(R1, R0, gs + 1, 1);
-  }
-  if (gs < nsteps) step(R0, R1, gs, 0);
+  for (int gs = 0; gs < nsteps; ++gs) step(gs, gs & 1);
 }
 
 }  // namespace nel

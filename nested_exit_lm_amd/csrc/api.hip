@@ -578,12 +578,11 @@ nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int3
   void* ht = ws + L.ht;
   hipError_t err;
   if (dh) {
-    err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack_t(w, vocab, d, vocab, wt, s); });
+    err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack16_t(w, vocab, d, vocab, wt, s); });
     if (err != hipSuccess) return from_hip(err);
-    err = timed(NEL_K_BWD_DH, s, [&] {
-      return launch_bwd_gemm<bf16_t>(wt, d, dlogits, n_tokens, vocab, vocab,
-                                     static_cast<bf16_t*>(dh), d, s);
-    });
+    BwdGroup gh{};
+    if (!bwd_group_add(gh, wt, d, dlogits, n_tokens, vocab, vocab, dh, d)) return NEL_ESHAPE;
+    err = timed(NEL_K_BWD_DH, s, [&] { return launch_dh_group<false>(gh, s); });
     if (err != hipSuccess) return from_hip(err);
   }
   if (dw) {
@@ -593,7 +592,7 @@ nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int3
     BwdGroup gw{};
     if (!bwd_group_add(gw, ht, d, dlogits, vocab, vocab, L.n_pad, dw, d, n_tokens))
       return NEL_ESHAPE;
-    err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float, true, false>(gw, s); });
+    err = timed(NEL_K_BWD_DW, s, [&] { return launch_dw_group<false>(gw, s); });
     if (err != hipSuccess) return from_hip(err);
   }
   return NEL_OK;
@@ -650,7 +649,7 @@ nel_status nel_heads_backward(nel_dtype dt, int32_t n_exits, int64_t n_tokens, i
     const HeadBwdWs L = head_bwd_ws_layout(n_tokens, vocab, d[e]);
     char* base = ws + heads_bwd_offset(e, n_tokens, vocab, d);
     if (dh) {
-      err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack_t(w[e], vocab, d[e], vocab, base + L.wt, s); });
+      err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack16_t(w[e], vocab, d[e], vocab, base + L.wt, s); });
       if (err != hipSuccess) return from_hip(err);
       if (!bwd_group_add(gh, base + L.wt, d[e], dlogits[e], n_tokens, vocab, vocab, dh[e], d[e]))
         return NEL_ESHAPE;
@@ -666,10 +665,10 @@ nel_status nel_heads_backward(nel_dtype dt, int32_t n_exits, int64_t n_tokens, i
     }
   }
   if (dh) {
-    err = timed(NEL_K_BWD_DH, s, [&] { return launch_bwd_group<bf16_t, false, false>(gh, s); });
+    err = timed(NEL_K_BWD_DH, s, [&] { return launch_dh_group<false>(gh, s); });
     if (err != hipSuccess) return from_hip(err);
   }
-  if (dw) err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float, true, false>(gw, s); });
+  if (dw) err = timed(NEL_K_BWD_DW, s, [&] { return launch_dw_group<false>(gw, s); });
   return from_hip(err);
 }
 
@@ -751,7 +750,8 @@ nel_status nel_matryoshka_loss_backward_packed(
   const float* lse = reinterpret_cast<const float*>(ws + L.loss + LL.lse);
   char* consts = ws + L.consts;
   err = timed(NEL_K_GRAD_CONSTS, s, [&] {
-    return launch_grad_consts(n_exits, n_tokens, vocab, info, labels, stats, lse, consts, s);
+    return launch_grad_consts(n_exits, n_tokens, vocab, info, labels, alpha_d, grad_scale, lam,
+                              stats, lse, consts, s);
   });
   if (err != hipSuccess) return from_hip(err);
   const int64_t plane = ((vocab + info.vtile - 1) / info.vtile) * n_tokens;
@@ -760,7 +760,6 @@ nel_status nel_matryoshka_loss_backward_packed(
     g->tw = static_cast<const uint16_t*>(scratch[n_exits - 1]);
     g->n_tok = n_tokens;
     g->vshift = __builtin_ctz(static_cast<unsigned>(info.vtile));
-    g->alpha = alpha_d;
   }
   for (int32_t e = 0; e < n_exits; ++e) {
     const HeadBwdWs HL = head_bwd_ws_layout(n_tokens, vocab, d[e]);
@@ -768,11 +767,10 @@ nel_status nel_matryoshka_loss_backward_packed(
     auto fill = [&](BwdGroup& g) {
       const int k = g.count - 1;
       g.tab[k] = consts + size_t{16} * static_cast<size_t>(e) * plane;
-      g.ge[k] = grad_scale * lam.w[e];
-      g.teacher[k] = e == n_exits - 1;
+      g.neg[k] = grad_scale * lam.w[e] < 0.f ? 0x80008000u : 0u;
     };
     if (dh) {
-      err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack_t(w[e], vocab, d[e], vocab, base + HL.wt, s); });
+      err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack16_t(w[e], vocab, d[e], vocab, base + HL.wt, s); });
       if (err != hipSuccess) return from_hip(err);
       if (!bwd_group_add(gh, base + HL.wt, d[e], scratch[e], n_tokens, vocab, vocab, dh[e], d[e]))
         return NEL_ESHAPE;
@@ -790,10 +788,10 @@ nel_status nel_matryoshka_loss_backward_packed(
     }
   }
   if (dh) {
-    err = timed(NEL_K_BWD_DH, s, [&] { return launch_bwd_group<bf16_t, false, true>(gh, s); });
+    err = timed(NEL_K_BWD_DH, s, [&] { return launch_dh_group<true>(gh, s); });
     if (err != hipSuccess) return from_hip(err);
   }
-  if (dw) err = timed(NEL_K_BWD_DW, s, [&] { return launch_bwd_group<float, true, true>(gw, s); });
+  if (dw) err = timed(NEL_K_BWD_DW, s, [&] { return launch_dw_group<true>(gw, s); });
   return from_hip(err);
 }
 

@@ -23,8 +23,11 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   __bf16 r = static_cast<__bf16>(f);
   return __builtin_bit_cast(bf16_t, r);
 }
+// Two at once: one v_cvt_pk_bf16_f32, the same rounding as f32_to_bf16.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // fp16 <-> fp32 (round to nearest even).  The loss path keeps its 16-bit

@@ -3,16 +3,16 @@
 // in its own head W^m in R^{V x D}), the chain rule gives
 //     dH = G W      [N x D] = sum over the vocabulary
 //     dW = G^T h    [V x D] = sum over the tokens.
-// Both run on the MFMA main loops of packed_core.h, whose A operand is
-// MFMA-tiled:
-//     dH:  A = W^T tiled (rows d, K = vocabulary),  B = G row-major (rows tokens,
-//          K = vocabulary contiguous)
-//     dW:  A = h^T tiled (rows d, K = tokens),      B = G read K-major (rows
-//          vocabulary, K = tokens): staged in LDS as stored and transposed by
-//          the LDS fragment loads, so G is never copied
-// so each lane's accumulators are 16 consecutive d of one output row and the
-// stores are row-major.  W^T and h^T are written tiled by one transposing
-// pass each (HBM-bound, into the workspace; K zero-padded to a multiple of 64).
+//     dH:  16x16x32 main loop of packed16_core.h (the head GEMM's): A = W^T
+//          in the 16-row tiled layout (rows d, K = vocabulary), B = G
+//          row-major (rows tokens, K = vocabulary contiguous)
+//     dW:  32x32x16 K-major main loop of packed_core.h: A = h^T tiled (rows d,
+//          K = tokens), B = G read K-major (rows vocabulary, K = tokens):
+//          staged in LDS as stored and transposed by the LDS fragment loads,
+//          so G is never copied
+// Both outputs are row-major.  W^T and h^T are written tiled by one
+// transposing pass each (HBM-bound, into the workspace; K zero-padded to a
+// multiple of 64).
 // The fused form reads no G: each thread forms its B chunks from the fp16
 // scratch of the packed loss GEMM and 16-byte row constants per (vocabulary
 // tile, token), with the arithmetic of the in-place gradient pass
@@ -23,6 +23,7 @@
 #include "common.h"
 #include "grad_chunk.h"
 #include "internal.h"
+#include "packed16_core.h"
 #include "packed_core.h"
 #include "tiles.h"
 
@@ -75,6 +76,51 @@ __global__ __launch_bounds__(256) void pack_t_kernel(const bf16_t* __restrict__ 
   }
 }
 
+// 16-row tiled A operand of S^T (packed16_core.h) for S [k_rows, R]
+// row-major (R % 64 == 0): element (r, k) = S[k][r] for k < k_rows, 0 up to
+// k_pad, at P[((rb * (k_pad / 32) + kb) * 64 + l) * 8 + j] for r = 16 rb +
+// (l mod 16), k = 32 kb + 8 (l / 16) + j.  One workgroup per 64 x 64 tile:
+// rows k0..k0+63 of S are read whole into LDS, then every thread writes two
+// 16-byte lane slots of the tile's eight 1 KB blocks, reading its 8 elements
+// down an LDS column (16 lanes take 16 adjacent columns, the four lane groups
+// rows 8 apart: 32 distinct banks).
+__global__ __launch_bounds__(256) void pack16_t_kernel(const bf16_t* __restrict__ S,
+                                                       bf16_t* __restrict__ P, int64_t k_rows,
+                                                       int R, int64_t k_pad, int r_tiles) {
+  __shared__ bf16_t tile[64][64 + 2];
+  const int tid = threadIdx.x;
+  const int rt = static_cast<int>(blockIdx.x % r_tiles);
+  const int64_t kt = blockIdx.x / r_tiles;
+  const int r0 = rt * 64;
+  const int64_t k0 = kt * 64;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + 256 * j, row = i >> 3, ch = i & 7;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k0 + row < k_rows)
+      v = *reinterpret_cast<const u32x4*>(S + (k0 + row) * R + r0 + ch * 8);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[row][ch * 8]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dst[w] = v[w];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + 256 * j;          // 512 lane slots: block (rbl, kbl), lane l
+    const int l = i & 63, blk = i >> 6;   // blk 0..7
+    const int rbl = blk & 3, kbl = blk >> 2;
+    const int r = 16 * rbl + (l & 15);
+    const int kk = 32 * kbl + 8 * (l >> 4);
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      v[w] = static_cast<uint32_t>(tile[kk + 2 * w][r]) |
+             (static_cast<uint32_t>(tile[kk + 2 * w + 1][r]) << 16);
+    const int64_t rb = r0 / 16 + rbl, kb = k0 / 32 + kbl;
+    *reinterpret_cast<u32x4*>(P + ((rb * (k_pad / 32) + kb) * 64 + l) * 8) = v;
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t count) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < count;
        i += static_cast<int64_t>(gridDim.x) * 256)
@@ -84,51 +130,55 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
 // ---------------------------------------------------------------- fused B
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-// {c1, sc} of a row constant record (the label is read once per row where
-// the row does not change).
-__device__ __forceinline__ u32x2 load_c1_sc(const GradRowConst* p) {
+// {c, k} of a row constant record (the label's entry and term are read once
+// per row where the row does not change).
+__device__ __forceinline__ u32x2 load_c_k(const GradRowConst* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
 
-// B = G of one exit, rows = tokens, K = vocabulary (dh = G W).  A K step
-// (64 entries) lies inside one statistics tile (at least 128 wide).
+// B = G of one exit, rows = tokens, K = vocabulary (dh = G W), NCH chunks
+// per thread.  A K step (64 entries) lies inside one statistics tile (at
+// least 128 wide).
+template <int NCH>
 struct BRowsGrad {
+  static constexpr int kChunks = NCH;
   const char* S;              // exit's scratch at the tile's token row 0 (bytes)
   const char* W;              // the teacher's weights, same place
   const GradRowConst* tab;    // the exit's constants, [tile][n]
   int64_t n;
-  int32_t row[4];             // tokens of the thread's four chunks
-  int32_t y[4];               // their labels
-  uint32_t boff[4];           // byte offsets of the chunks at K step 0
+  int32_t row[NCH];           // tokens of the thread's chunks
+  int32_t y[NCH];             // their labels
+  float lab[NCH];             // and the label's terms
+  uint32_t boff[NCH];         // byte offsets of the chunks at K step 0
   int vlane, vshift;          // first entry of the thread's chunk in a K step; log2 tile width
-  float ge, alpha;
-  bool teacher;
+  uint32_t neg;               // grad_chunk's sign mask of the exit
   int gcur;
-  u32x4 rs[4], rw[4];
-  u32x2 k[4];
+  u32x4 rs[NCH], rw[NCH];
+  u32x2 k[NCH];
   __device__ __forceinline__ void init() {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) y[j] = tab[row[j]].y;
+    for (int j = 0; j < NCH; ++j) {
+      y[j] = tab[row[j]].y;
+      lab[j] = tab[row[j]].lab;
+    }
   }
   __device__ __forceinline__ void issue(int g) {
     gcur = g;
     const int64_t off = static_cast<int64_t>(g) * (kPkBK * 2);
     const GradRowConst* t = tab + ((static_cast<int64_t>(g) * kPkBK) >> vshift) * n;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NCH; ++j) {
       rw[j] = *reinterpret_cast<const u32x4*>(W + off + boff[j]);
-      if (!teacher) rs[j] = *reinterpret_cast<const u32x4*>(S + off + boff[j]);
-      k[j] = load_c1_sc(t + row[j]);
+      rs[j] = *reinterpret_cast<const u32x4*>(S + off + boff[j]);
+      k[j] = load_c_k(t + row[j]);
     }
   }
-  __device__ __forceinline__ void finish(u32x4 (&hr)[4]) const {
+  __device__ __forceinline__ void finish(u32x4 (&hr)[NCH]) const {
     const int v0 = gcur * kPkBK + vlane;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float c1 = __uint_as_float(k[j][0]), sc = __uint_as_float(k[j][1]);
-      hr[j] = teacher ? grad_chunk_teacher(rw[j], sc, ge, y[j] - v0)
-                      : grad_chunk_student(rs[j], rw[j], sc, c1, ge, alpha, y[j] - v0);
-    }
+    for (int j = 0; j < NCH; ++j)
+      hr[j] = grad_chunk(rs[j], rw[j], __uint_as_float(k[j][0]), __uint_as_float(k[j][1]), lab[j],
+                         label_offset(y[j], v0), neg);
   }
 };
 
@@ -144,8 +194,7 @@ struct BKMajorGrad {
   uint32_t rstride;           // bytes between the thread's K rows (16 rows)
   int lrow, v0;               // the thread's first K row; its chunk's first vocabulary entry
   bool col_ok;
-  float ge, alpha;
-  bool teacher;
+  uint32_t neg;               // grad_chunk's sign mask of the exit
   unsigned valid;             // bit j: chunk j of the current step exists
   u32x4 rs[4], rw[4];
   u32x4 k[4];
@@ -159,34 +208,139 @@ struct BKMajorGrad {
       if (col_ok && t < n) {
         valid |= 1u << j;
         rw[j] = *reinterpret_cast<const u32x4*>(W + base + j * rstride);
-        if (!teacher) rs[j] = *reinterpret_cast<const u32x4*>(S + base + j * rstride);
+        rs[j] = *reinterpret_cast<const u32x4*>(S + base + j * rstride);
         k[j] = *reinterpret_cast<const u32x4*>(tab + t);
+      } else {
+        rw[j] = rs[j] = u32x4{0u, 0u, 0u, 0u};
+        k[j] = u32x4{0u, 0u, 0u, ~0u};   // finite constants, no label
       }
     }
   }
   __device__ __forceinline__ void finish(u32x4 (&hr)[4]) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      hr[j] = u32x4{0u, 0u, 0u, 0u};
-      if (valid & (1u << j)) {
-        const float c1 = __uint_as_float(k[j][0]), sc = __uint_as_float(k[j][1]);
-        const int yi = static_cast<int32_t>(k[j][2]) - v0;
-        hr[j] = teacher ? grad_chunk_teacher(rw[j], sc, ge, yi)
-                        : grad_chunk_student(rs[j], rw[j], sc, c1, ge, alpha, yi);
-      }
+      // every lane forms the chunk (grad_chunk's wavefront vote); a missing
+      // one has finite inputs (issue zeroes them)
+      const u32x4 v = grad_chunk(rs[j], rw[j], __uint_as_float(k[j][0]), __uint_as_float(k[j][1]),
+                                 __uint_as_float(k[j][2]), label_offset(k[j][3], v0), neg);
+      hr[j] = (valid & (1u << j)) ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
 };
 
-// ---------------------------------------------------------------- GEMM
-// out[b][a] = sum_k A[a][k] B[b][k] for a < a_rows, b < b_rows; A tiled
-// (a_rows % 32 == 0, K % 64 == 0), B row-major with row stride ldb.  One
-// launch covers a group of such products (the exits of a suite): workgroup
-// ids are split by the prefix sums `first` of the products' tile counts, so
-// one product's workgroups fill another's last partial round.  FUSED: B is
-// the exit's G formed from its scratch (g.B[e]) and the teacher's (g.tw).
-template <typename OutT, bool KMAJOR, bool FUSED>
-__global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
+// ---------------------------------------------------------------- dh GEMM
+// dh[t][d] = sum_v G[t][v] W[v][d] for t < b_rows (tokens), d < a_rows, on
+// the head GEMM's main loop: A = W^T in the 16-row tiled layout (K = V),
+// B = the token rows of G (row stride ldb), or with FUSED the gradients formed
+// from the scratch.  Tile 128 tokens x 256 columns of d.  FUSED runs one
+// workgroup per CU: forming the gradients beside the accumulators takes more
+// than the 256 registers per lane of two (measured: spills inside the main
+// loop at two, and a slower eight-wavefront variant).  One launch covers a
+// group of exits: workgroup ids are split by the prefix sums `first` of the
+// exits' tile counts, so one exit's workgroups fill another's last partial
+// round.  The bf16 outputs leave through a wave-local LDS transpose: a lane
+// holds four consecutive d of one token per 16 x 16 block and the
+// wavefront's 64 d of a token are one 128-byte line, so after the transpose
+// eight lanes store each whole line (nontemporal).  Row r, 16-byte chunk c
+// of a wavefront's 32-token stage sits at slot 8 r + (c ^ ((r / 2) mod 8)).
+template <bool FUSED>
+__global__ __launch_bounds__(kPkThreads, FUSED ? 1 : 2) void dh16_kernel(
+    BwdGroup /*read through the kernarg pointer*/) {
+  constexpr int NCH = 8 * kPkBRows / kPkThreads;   // B chunks per thread
+  const BwdGroup& g = *(const BwdGroup*)__builtin_amdgcn_kernarg_segment_ptr();
+  __shared__ u32x4 hs[2][16 * kPkBRows];
+  int e = 0;
+  while (e + 1 < g.count && static_cast<int>(blockIdx.x) >= g.first[e + 1]) ++e;
+  const char* __restrict__ A = reinterpret_cast<const char*>(g.A[e]);
+  const bf16_t* __restrict__ B = g.B[e];
+  char* __restrict__ out = static_cast<char*>(g.out[e]);
+  const int a_rows = g.a_rows[e];
+  const int64_t b_rows = g.b_rows[e], ldb = g.ldb[e], K = g.K[e], ldo = g.ldo[e];
+  const int tid = threadIdx.x, lane = tid & 63, x = lane & 15, gq = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int bt, at;
+  tile_coords(static_cast<int>(blockIdx.x) - g.first[e], g.n_bt[e], g.n_at[e], kBwdGroup, bt, at);
+  const int64_t b0 = static_cast<int64_t>(bt) * kPkBRows;
+  const int aw = at * kPkARows + wave * 64;   // this wavefront's first column of d
+  const char* Ab[k16NAB];
+#pragma unroll
+  for (int ab = 0; ab < k16NAB; ++ab)
+    Ab[ab] = A + static_cast<int64_t>(min((aw >> 4) + ab, a_rows / 16 - 1)) * (K / 32) * 1024;
+  const PackedLanes pl = packed_lanes(tid);
+  uint32_t boff[NCH];
+  int64_t rows[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    rows[j] = min(b0 + pl.brow + 32 * j, b_rows - 1);
+    boff[j] = static_cast<uint32_t>(((rows[j] - b0) * ldb + pl.bchunk * 8) * 2);
+  }
+  const int64_t tile_off = b0 * ldb * 2;
+  const int nsteps = static_cast<int>(K / kPkBK);
+  f32x4 acc[k16NTB][k16NAB];
+  if constexpr (FUSED) {
+    BRowsGrad<NCH> src;
+    src.S = reinterpret_cast<const char*>(B) + tile_off;
+    src.W = reinterpret_cast<const char*>(g.tw) + tile_off;
+    src.tab = static_cast<const GradRowConst*>(g.tab[e]);
+    src.n = g.n_tok;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      src.row[j] = static_cast<int32_t>(rows[j]);
+      src.boff[j] = boff[j];
+    }
+    src.vlane = 8 * pl.bchunk;
+    src.vshift = g.vshift;
+    src.neg = g.neg[e];
+    src.init();
+    packed16_tile_gemm(acc, hs, Ab, src, pl.hslot, nsteps);
+  } else {
+    BRowsPlain<NCH> src;
+    src.Bb = reinterpret_cast<const char*>(B) + tile_off;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) src.boff[j] = boff[j];
+    packed16_tile_gemm(acc, hs, Ab, src, pl.hslot, nsteps);
+  }
+  char* const stage = reinterpret_cast<char*>(&hs[0][0]) + wave * 4096;
+  const bool col_ok = aw < a_rows;   // a_rows % 64 == 0: all 64 columns or none
+  const int ch = lane & 7;
+  // 32-bit lane offsets from a wave-uniform row base (ldo is below 2^22)
+  const uint32_t loff = (static_cast<uint32_t>(lane >> 3) * static_cast<uint32_t>(ldo) +
+                         static_cast<uint32_t>(aw + 8 * ch)) * 2u;
+#pragma unroll
+  for (int tp = 0; tp < k16NTB / 2; ++tp) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tb = 2 * tp + u, row = 16 * u + x;
+#pragma unroll
+      for (int ab = 0; ab < k16NAB; ++ab) {
+        // d = 16 ab + 4 gq .. + 3 of the row: chunk 2 ab + gq / 2, half gq % 2
+        const int c = 2 * ab + (gq >> 1);
+        *reinterpret_cast<uint2*>(stage + (8 * row + (c ^ ((row >> 1) & 7))) * 16 + 8 * (gq & 1)) =
+            make_uint2(pack_bf16x2(acc[tb][ab][0], acc[tb][ab][1]),
+                       pack_bf16x2(acc[tb][ab][2], acc[tb][ab][3]));
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 8 * j + (lane >> 3);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (8 * row + (ch ^ ((row >> 1) & 7))) * 16);
+      const int64_t r0 = b0 + 32 * tp + 8 * j;   // this store's first token
+      if (col_ok && r0 + (lane >> 3) < b_rows)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + r0 * ldo * 2 + loff));
+    }
+    wave_lds_sync();
+  }
+}
+
+// ---------------------------------------------------------------- dW GEMM
+// dW[v][d] = sum_t G[t][v] h[t][d]: out[b][a] = sum_k A[a][k] B(b, k) with
+// A = h^T tiled (a_rows = d, K = padded tokens) and B read K-major from G
+// (b = vocabulary entry, k = token; K rows from k_valid read as 0), fp32
+// output.  Grouped over the exits like dh16_kernel.  FUSED: B is the exit's G
+// formed from its scratch (g.B[e]) and the teacher's (g.tw).
+template <bool FUSED>
+__global__ __launch_bounds__(kPkThreads, 2) void dw_gemm_kernel(
     BwdGroup /*read through the kernarg pointer*/) {
   // Per-product fields are read through the kernarg segment pointer, which
   // keeps the lookups by a run-time product index scalar.
@@ -197,7 +351,7 @@ __global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
   while (e + 1 < g.count && static_cast<int>(blockIdx.x) >= g.first[e + 1]) ++e;
   const bf16_t* __restrict__ A = g.A[e];
   const bf16_t* __restrict__ B = g.B[e];
-  OutT* __restrict__ out = static_cast<OutT*>(g.out[e]);
+  float* __restrict__ out = static_cast<float*>(g.out[e]);
   const int a_rows = g.a_rows[e];
   const int64_t b_rows = g.b_rows[e], ldb = g.ldb[e], K = g.K[e], ldo = g.ldo[e];
   const int tid = threadIdx.x, lane = tid & 63, q = lane & 31, hl = lane >> 5;
@@ -212,119 +366,63 @@ __global__ __launch_bounds__(kPkThreads, 2) void bwd_gemm_kernel(
   const char* A0 = Ab + static_cast<int64_t>(rb0) * 64 * K;
   const char* A1 = Ab + static_cast<int64_t>(rb1) * 64 * K;
   const int nsteps = static_cast<int>(K / kPkBK);
-  if constexpr (KMAJOR) {
-    const int cols = static_cast<int>(min(b_rows - b0, static_cast<int64_t>(kPkBRows)));
-    const KMajorLanes kl = kmajor_lanes(tid);
-    if constexpr (FUSED) {
-      BKMajorGrad src;
-      const int64_t off = (static_cast<int64_t>(kl.lrow) * ldb + b0 + 8 * kl.lchunk) * 2;
-      src.S = reinterpret_cast<const char*>(B) + off;
-      src.W = reinterpret_cast<const char*>(g.tw) + off;
-      src.tab = static_cast<const GradRowConst*>(g.tab[e]) + (b0 >> g.vshift) * g.n_tok;
-      src.n = g.k_valid[e];
-      src.step_bytes = int64_t{kPkBK} * ldb * 2;
-      src.rstride = static_cast<uint32_t>(16 * ldb * 2);
-      src.lrow = kl.lrow;
-      src.v0 = static_cast<int>(b0) + 8 * kl.lchunk;
-      src.col_ok = 8 * kl.lchunk < cols;
-      src.ge = g.ge[e];
-      src.alpha = g.alpha;
-      src.teacher = g.teacher[e] != 0;
-      packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, A0, A1, src, nsteps);
-    } else {
-      BKMajorPlain src(reinterpret_cast<const char*>(B + b0), ldb, g.k_valid[e], cols, kl);
-      packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, A0, A1, src, nsteps);
-    }
+  const int cols = static_cast<int>(min(b_rows - b0, static_cast<int64_t>(kPkBRows)));
+  const KMajorLanes kl = kmajor_lanes(tid);
+  if constexpr (FUSED) {
+    BKMajorGrad src;
+    const int64_t off = (static_cast<int64_t>(kl.lrow) * ldb + b0 + 8 * kl.lchunk) * 2;
+    src.S = reinterpret_cast<const char*>(B) + off;
+    src.W = reinterpret_cast<const char*>(g.tw) + off;
+    src.tab = static_cast<const GradRowConst*>(g.tab[e]) + (b0 >> g.vshift) * g.n_tok;
+    src.n = g.k_valid[e];
+    src.step_bytes = int64_t{kPkBK} * ldb * 2;
+    src.rstride = static_cast<uint32_t>(16 * ldb * 2);
+    src.lrow = kl.lrow;
+    src.v0 = static_cast<int>(b0) + 8 * kl.lchunk;
+    src.col_ok = 8 * kl.lchunk < cols;
+    src.neg = g.neg[e];
+    packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, A0, A1, src, nsteps);
   } else {
-    const PackedLanes pl = packed_lanes(tid);
-    uint32_t boff[4];
-    int64_t rows[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      rows[j] = min(b0 + pl.brow + 32 * j, b_rows - 1);
-      boff[j] = static_cast<uint32_t>(((rows[j] - b0) * ldb + pl.bchunk * 8) * 2);
-    }
-    const int64_t tile_off = b0 * ldb * 2;
-    if constexpr (FUSED) {
-      BRowsGrad src;
-      src.S = reinterpret_cast<const char*>(B) + tile_off;
-      src.W = reinterpret_cast<const char*>(g.tw) + tile_off;
-      src.tab = static_cast<const GradRowConst*>(g.tab[e]);
-      src.n = g.n_tok;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        src.row[j] = static_cast<int32_t>(rows[j]);
-        src.boff[j] = boff[j];
-      }
-      src.vlane = 8 * pl.bchunk;
-      src.vshift = g.vshift;
-      src.ge = g.ge[e];
-      src.alpha = g.alpha;
-      src.teacher = g.teacher[e] != 0;
-      src.init();
-      packed_tile_gemm<NTB, NAB>(acc, hs, A0, A1, src, pl, nsteps);
-    } else {
-      BRowsPlain src;
-      src.Bb = reinterpret_cast<const char*>(B) + tile_off;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) src.boff[j] = boff[j];
-      packed_tile_gemm<NTB, NAB>(acc, hs, A0, A1, src, pl, nsteps);
-    }
+    BKMajorPlain src(reinterpret_cast<const char*>(B + b0), ldb, g.k_valid[e], cols, kl);
+    packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, A0, A1, src, nsteps);
   }
   // Stores leave through a wave-local LDS transpose, one 32-row block at a
   // time: a lane holds 16 consecutive outputs of one row, but the
-  // wavefront's 64 outputs of a row are whole 128-byte lines (bf16: one,
-  // fp32: two), so after the transpose each store instruction writes whole
-  // lines, nontemporal (nothing reads them back here).  The wavefront uses
-  // its own 8 KB of the B stage, free since the main loop's last barrier.
-  // Row r, 16-byte chunk c sits at slot CPR r + (c ^ swizzle(r)), CPR chunks
-  // per row; writes and reads then cover all 64 banks.  Addresses: a
-  // wave-uniform 64-bit row base and 32-bit lane offsets (the outputs' row
-  // length ldo is below 2^22).
-  constexpr int ES = sizeof(OutT);
-  constexpr int CPR = 64 * ES / 16;              // 16-byte chunks per row: 8 or 16
-  constexpr int RPS = 64 / CPR;                  // rows per wavefront store: 8 or 4
-  auto swz = [](int r) { return CPR == 8 ? (r >> 1) & 7 : r & 15; };
+  // wavefront's 64 fp32 outputs of a row are two whole 128-byte lines, so
+  // after the transpose each store instruction writes whole lines,
+  // nontemporal (nothing reads them back here).  The wavefront uses its own
+  // 8 KB of the B stage, free since the main loop's last barrier.  Row r,
+  // 16-byte chunk c sits at slot 16 r + (c ^ (r mod 16)); writes and reads
+  // then cover all 64 banks.  Addresses: a wave-uniform 64-bit row base and
+  // 32-bit lane offsets (the outputs' row length ldo is below 2^22).
   char* const stage = reinterpret_cast<char*>(&hs[0][0]) + wave * 8192;
   const bool col_ok = aw < a_rows;               // a_rows % 64 == 0: all 64 columns or none
-  const int ch = lane % CPR;
-  const uint32_t loff = (static_cast<uint32_t>(lane / CPR) * static_cast<uint32_t>(ldo) +
-                         static_cast<uint32_t>(aw + ch * (16 / ES))) * ES;
+  const int ch = lane & 15;
+  const uint32_t loff = (static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(ldo) +
+                         static_cast<uint32_t>(aw + ch * 4)) * 4;
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb) {
 #pragma unroll
     for (int ab = 0; ab < NAB; ++ab) {
-      if constexpr (ES == 2) {
+      // (+ 0.0f: storing the accumulators unchanged made the register
+      // allocator spill accumulator blocks inside the main loop)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          u32x4 pk;
+      for (int h4 = 0; h4 < 4; ++h4) {
+        u32x4 pk;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            pk[j] = pack_bf16x2(acc[tb][ab][8 * h2 + 2 * j], acc[tb][ab][8 * h2 + 2 * j + 1]);
-          const int c = 4 * ab + 2 * hl + h2;
-          *reinterpret_cast<u32x4*>(stage + (CPR * q + (c ^ swz(q))) * 16) = pk;
-        }
-      } else {
-        // (+ 0.0f: storing the accumulators unchanged made the register
-        // allocator spill accumulator blocks inside the main loop)
-#pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) {
-          u32x4 pk;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pk[j] = __float_as_uint(acc[tb][ab][4 * h4 + j] + 0.0f);
-          const int c = 8 * ab + 4 * hl + h4;
-          *reinterpret_cast<u32x4*>(stage + (CPR * q + (c ^ swz(q))) * 16) = pk;
-        }
+        for (int j = 0; j < 4; ++j) pk[j] = __float_as_uint(acc[tb][ab][4 * h4 + j] + 0.0f);
+        const int c = 8 * ab + 4 * hl + h4;
+        *reinterpret_cast<u32x4*>(stage + (16 * q + (c ^ (q & 15))) * 16) = pk;
       }
     }
     wave_lds_sync();
 #pragma unroll
-    for (int j = 0; j < 32 / RPS; ++j) {
-      const int row = RPS * j + lane / CPR;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (CPR * row + (ch ^ swz(row))) * 16);
-      const int64_t r0 = b0 + 32 * tb + RPS * j;   // this store's first row
-      char* rb = static_cast<char*>(static_cast<void*>(out)) + r0 * ldo * ES;
-      if (col_ok && r0 + lane / CPR < b_rows)
+    for (int j = 0; j < 8; ++j) {
+      const int row = 4 * j + (lane >> 4);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (16 * row + (ch ^ (row & 15))) * 16);
+      const int64_t r0 = b0 + 32 * tb + 4 * j;   // this store's first row
+      char* rb = reinterpret_cast<char*>(out) + r0 * ldo * 4;
+      if (col_ok && r0 + (lane >> 4) < b_rows)
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
     }
     wave_lds_sync();
@@ -348,6 +446,16 @@ hipError_t launch_pack_t(const void* S, int64_t k_rows, int R, int64_t k_pad, vo
   const int r_tiles = R / 64;
   const int64_t tiles = static_cast<int64_t>(r_tiles) * (k_pad / 64);
   hipLaunchKernelGGL(pack_t_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(S), static_cast<bf16_t*>(P), k_rows, R, k_pad,
+                     r_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack16_t(const void* S, int64_t k_rows, int R, int64_t k_pad, void* P,
+                           hipStream_t s) {
+  const int r_tiles = R / 64;
+  const int64_t tiles = static_cast<int64_t>(r_tiles) * (k_pad / 64);
+  hipLaunchKernelGGL(pack16_t_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s,
                      static_cast<const bf16_t*>(S), static_cast<bf16_t*>(P), k_rows, R, k_pad,
                      r_tiles);
   return hipGetLastError();
@@ -384,30 +492,25 @@ bool bwd_group_add(BwdGroup& g, const void* A, int a_rows, const void* B, int64_
   return true;
 }
 
-template <typename OutT, bool KMAJOR, bool FUSED>
-hipError_t launch_bwd_group(const BwdGroup& g, hipStream_t s) {
+template <bool FUSED>
+hipError_t launch_dh_group(const BwdGroup& g, hipStream_t s) {
   if (g.count == 0 || g.first[g.count] == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_gemm_kernel<OutT, KMAJOR, FUSED>),
-                     dim3(static_cast<unsigned>(g.first[g.count])), dim3(kPkThreads), 0, s, g);
+  hipLaunchKernelGGL((dh16_kernel<FUSED>), dim3(static_cast<unsigned>(g.first[g.count])),
+                     dim3(kPkThreads), 0, s, g);
   return hipGetLastError();
 }
 
-template <typename OutT>
-hipError_t launch_bwd_gemm(const void* A, int a_rows, const void* B, int64_t b_rows, int64_t ldb,
-                           int64_t K, OutT* out, int64_t ldo, hipStream_t s) {
-  BwdGroup g{};
-  if (!bwd_group_add(g, A, a_rows, B, b_rows, ldb, K, out, ldo)) return hipErrorInvalidValue;
-  return launch_bwd_group<OutT, false, false>(g, s);
+template <bool FUSED>
+hipError_t launch_dw_group(const BwdGroup& g, hipStream_t s) {
+  if (g.count == 0 || g.first[g.count] == 0) return hipSuccess;
+  hipLaunchKernelGGL((dw_gemm_kernel<FUSED>), dim3(static_cast<unsigned>(g.first[g.count])),
+                     dim3(kPkThreads), 0, s, g);
+  return hipGetLastError();
 }
 
-template hipError_t launch_bwd_gemm<bf16_t>(const void*, int, const void*, int64_t, int64_t,
-                                            int64_t, bf16_t*, int64_t, hipStream_t);
-template hipError_t launch_bwd_gemm<float>(const void*, int, const void*, int64_t, int64_t,
-                                           int64_t, float*, int64_t, hipStream_t);
-template hipError_t launch_bwd_group<bf16_t, false, false>(const BwdGroup&, hipStream_t);
-template hipError_t launch_bwd_group<float, false, false>(const BwdGroup&, hipStream_t);
-template hipError_t launch_bwd_group<float, true, false>(const BwdGroup&, hipStream_t);
-template hipError_t launch_bwd_group<bf16_t, false, true>(const BwdGroup&, hipStream_t);
-template hipError_t launch_bwd_group<float, true, true>(const BwdGroup&, hipStream_t);
+template hipError_t launch_dh_group<false>(const BwdGroup&, hipStream_t);
+template hipError_t launch_dh_group<true>(const BwdGroup&, hipStream_t);
+template hipError_t launch_dw_group<false>(const BwdGroup&, hipStream_t);
+template hipError_t launch_dw_group<true>(const BwdGroup&, hipStream_t);
 
 }  // namespace nel

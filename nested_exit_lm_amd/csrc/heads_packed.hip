@@ -24,11 +24,10 @@
 // so every operand load is one contiguous 1 KB read.
 //
 // Workgroup: 4 wavefronts, tile 128 tokens x 256 vocabulary entries, two
-// workgroups per CU.  Each K step (64) streams the wavefront's 8 W blocks
-// straight into registers, one step ahead, and stages the 128-token slice of
-// h through LDS (double-buffered).  Wavefront w owns vocabulary entries
-// [64 w, 64 w + 64) of the tile for all 128 tokens: 8 token blocks x 4
-// vocabulary blocks of 16 x 16.
+// workgroups per CU, on the main loop of packed16_core.h (W as the A operand
+// straight into registers, h as the B operand staged through LDS).
+// Wavefront w owns vocabulary entries [64 w, 64 w + 64) of the tile for all
+// 128 tokens: 8 token blocks x 4 vocabulary blocks of 16 x 16.
 //
 // Loss epilogue: per (token, tile) the row maximum m, sum exp(l - m) and the
 // label's logit, and one 16-bit copy of the tile in the exit's gradient
@@ -43,6 +42,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "packed16_core.h"
 #include "packed_core.h"
 #include "tiles.h"
 
@@ -50,14 +50,13 @@ namespace nel {
 
 namespace {
 
-typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kPkTok = kPkBRows;   // tokens per workgroup (the h rows)
 constexpr int kPkVoc = kPkARows;   // vocabulary entries per workgroup
 constexpr int kPkGroup = 8;        // token tiles per tile group (see tile_coords)
-constexpr int kNTB = 8;            // token blocks of 16 per wavefront
-constexpr int kNVB = 4;            // vocabulary blocks of 16 per wavefront
+constexpr int kNTB = k16NTB;       // token blocks of 16 per wavefront
+constexpr int kNVB = k16NAB;       // vocabulary blocks of 16 per wavefront
 
 // ---------------------------------------------------------------- packing
 // One workgroup per (16-row block rb, four 32-column blocks kb0 .. kb0 + 3):
@@ -78,104 +77,6 @@ __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ w,
     const u32x4 v =
         *reinterpret_cast<const u32x4*>(w + (rb * 16 + x) * d + kb * 32 + g * 8);
     *reinterpret_cast<u32x4*>(p + ((rb * nkb + kb) * 64 + 16 * g + x) * 8) = v;
-  }
-}
-
-// ---------------------------------------------------------------- main loop
-// acc[tb][vb] += W(rows of vocabulary block vb) . h(token block tb) over
-// K = 64 nsteps.  Wb[vb]: byte base of the wavefront's packed row block vb;
-// Hb: byte base of the tile's h row 0; hoff: byte offsets (from Hb) of this
-// thread's four 16-byte h chunks (per step the base advances 128 bytes).
-// Every wavefront of the workgroup calls this together (it has barriers).
-__device__ __forceinline__ void packed16_tile_gemm(f32x4 (&acc)[kNTB][kNVB],
-                                                   u32x4 (&hs)[2][16 * kPkBRows],
-                                                   const char* const (&Wb)[kNVB],
-                                                   const char* __restrict__ Hb,
-                                                   const uint32_t (&hoff)[4], int hslot,
-                                                   int nsteps) {
-#pragma unroll
-  for (int tb = 0; tb < kNTB; ++tb)
-#pragma unroll
-    for (int vb = 0; vb < kNVB; ++vb) acc[tb][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
-  // LDS slot of token x, chunk 4 kh + g (block tb: + 16 tb): the stage holds
-  // token t, chunk c at 128 c + (t ^ 2 c), so each 16-lane pass of a fragment
-  // read covers 16 distinct bank groups
-  int fsl[2];
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    const int c = 4 * kh + g;
-    fsl[kh] = 128 * c + (x ^ (2 * c));
-  }
-  const uint32_t aoff = static_cast<uint32_t>(lane) * 16u;
-  // One set of W fragments: R[vb][kh] is reloaded for the next step as soon
-  // as the current step's last matrix instruction that reads it has issued
-  // (kh = 0 after the first half of the step, kh = 1 after the second), and
-  // the next step's h slice is loaded at the start of the step, so every
-  // load has at least half a step of this wavefront's matrix instructions
-  // ahead of its first use without a second register set.
-  u32x4 R[kNVB][2], hr[4];
-  auto load_a = [&](int kh, int gs) {
-#pragma unroll
-    for (int vb = 0; vb < kNVB; ++vb)
-      R[vb][kh] = *reinterpret_cast<const u32x4*>(Wb[vb] + static_cast<int64_t>(2 * gs + kh) * 1024 + aoff);
-  };
-  auto load_b = [&](int gs) {
-    const char* a = Hb + static_cast<int64_t>(gs) * (kPkBK * 2);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hr[j] = *reinterpret_cast<const u32x4*>(a + hoff[j]);
-  };
-  auto store_b = [&](int st, int q) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hs[st][1024 * q + hslot + 32 * j] = hr[j];
-  };
-  auto mfma = [&](int kh, int st, int q) {
-    bf16x8 b[kNTB];
-#pragma unroll
-    for (int tb = 0; tb < kNTB; ++tb)
-      b[tb] = __builtin_bit_cast(bf16x8, hs[st][1024 * q + fsl[kh] + 16 * tb]);
-#pragma unroll
-    for (int vb = 0; vb < kNVB; ++vb) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, R[vb][kh]);
-#pragma unroll
-      for (int tb = 0; tb < kNTB; ++tb)
-        acc[tb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[tb], acc[tb][vb], 0, 0, 0);
-    }
-  };
-  // Steps go in pairs: stage st holds the h slices of steps 2p and 2p + 1
-  // (sub-stages q = 0, 1), so the workgroup meets at a barrier once per two
-  // steps.  Step g = 2p + q computes from sub-stage q while it loads the h
-  // slice of step g + 2 (into the other stage's sub-stage q) and the W
-  // fragments of step g + 1; loads past the last step re-read it.
-  const int last = nsteps - 1;
-  auto step = [&](int gi, int st, int q) {
-    load_b(min(gi + 2, last));
-    __builtin_amdgcn_sched_barrier(0);
-    mfma(0, st, q);
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(0, min(gi + 1, last));
-    __builtin_amdgcn_sched_barrier(0);
-    mfma(1, st, q);
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(1, min(gi + 1, last));
-    store_b(st ^ 1, q);
-  };
-  load_b(0);
-  store_b(0, 0);
-  load_b(min(1, last));
-  store_b(0, 1);
-  load_a(0, 0);
-  load_a(1, 0);
-  __syncthreads();
-  int gs = 0, st = 0;
-  for (; gs + 2 <= nsteps; gs += 2, st ^= 1) {
-    step(gs, st, 0);
-    step(gs + 1, st, 1);
-    __syncthreads();
-  }
-  if (gs < nsteps) {   // an odd last step; the barrier frees LDS for the epilogue
-    step(gs, st, 0);
-    __syncthreads();
   }
 }
 
@@ -238,7 +139,11 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_kernel_packed(
     const char* Wb[kNVB];
 #pragma unroll
     for (int vb = 0; vb < kNVB; ++vb) Wb[vb] = P + static_cast<int64_t>(rbk[vb]) * D * 32;
-    packed16_tile_gemm(acc, hs, Wb, Hb, hoff, pl.hslot, D / kPkBK);
+    BRowsPlain<4> hsrc;
+    hsrc.Bb = Hb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hsrc.boff[j] = hoff[j];
+    packed16_tile_gemm(acc, hs, Wb, hsrc, pl.hslot, D / kPkBK);
 
     // vocabulary entries beyond V (last tile only) vanish under exp and never
     // win a max; V is a multiple of 32, so a 16-block is wholly in or beyond V

@@ -127,33 +127,34 @@ struct BwdGroup {
   int count;
   // Fused launches (B = G formed from the packed loss GEMM's fp16 scratch):
   // B[e] is exit e's scratch, tw the teacher's, tab[e] exit e's row
-  // constants [vocabulary tile][n_tok] (launch_grad_consts), ge[e] its
-  // gradient scale grad_scale * lambda_e, teacher[e] != 0 for the teacher.
+  // constants [vocabulary tile][n_tok] (launch_grad_consts), which scale by
+  // |grad_scale * lambda_e|; neg[e] is 0x80008000 where that product is
+  // negative (grad_chunk flips the bf16 gradients, as the stored pass does).
   const uint16_t* tw;
   const void* tab[kMaxExits];
-  float ge[kMaxExits];
-  int teacher[kMaxExits];
+  uint32_t neg[kMaxExits];
   int64_t n_tok;
   int vshift;   // log2 of the statistics tile width
-  float alpha;
 };
 bool bwd_group_add(BwdGroup& g, const void* A, int a_rows, const void* B, int64_t b_rows,
                    int64_t ldb, int64_t K, void* out, int64_t ldo, int64_t k_valid = -1);
-// KMAJOR: B(b, k) is element k * ldb + b of a row-major [K x ldb] matrix
-// (b_rows columns of it; K rows k_valid.. read as 0); else B is row-major
-// [b_rows x ldb] with K contiguous.  FUSED: B is formed from the scratch
-// (the fused fields of the group).
-template <typename OutT, bool KMAJOR, bool FUSED>
-hipError_t launch_bwd_group(const BwdGroup& g, hipStream_t s);
-// Tiled A operand of S^T for S [k_rows, R] row-major, K zero-padded to k_pad.
+// dh: out[b][a] = sum_k A[a][k] B[b][k], A tiled for the 16x16x32 loop
+// (launch_pack16_t), B row-major [b_rows x ldb] with K contiguous; bf16 out.
+// dW: the same with A tiled for the 32x32x16 loop (launch_pack_t) and B(b, k)
+// the element k * ldb + b of a row-major [K x ldb] matrix (b_rows columns of
+// it; K rows k_valid.. read as 0); fp32 out.  FUSED: B is formed from the
+// scratch (the fused fields of the group).
+template <bool FUSED>
+hipError_t launch_dh_group(const BwdGroup& g, hipStream_t s);
+template <bool FUSED>
+hipError_t launch_dw_group(const BwdGroup& g, hipStream_t s);
+// Tiled A operand of S^T for S [k_rows, R] row-major, K zero-padded to k_pad:
+// for the 32x32x16 loop (pack_t) or the 16x16x32 loop (pack16_t).
 hipError_t launch_pack_t(const void* S, int64_t k_rows, int R, int64_t k_pad, void* P,
                          hipStream_t s);
+hipError_t launch_pack16_t(const void* S, int64_t k_rows, int R, int64_t k_pad, void* P,
+                           hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t s);
-// out[b][a] = sum_k A[a][k] B[b][k]; A tiled (a_rows x K), B row-major (b_rows x ldb).
-template <typename OutT>
-hipError_t launch_bwd_gemm(const void* A, int a_rows, const void* B, int64_t b_rows, int64_t ldb,
-                           int64_t K, OutT* out, int64_t ldo, hipStream_t s);
-
 template <typename T>
 hipError_t launch_junction(int64_t n, int d_in, int d_out, int vocab, const void* h,
                            const int32_t* ids, const void* emb, void* out, int32_t* flags,
@@ -195,10 +196,12 @@ hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInf
                                 const float* stats, const float* lse, void* const* dlogits,
                                 float* dv, const ExitW& lam, bool write_g, hipStream_t s);
 // Row constants of the gradients formed from the fp16 scratch: 16 bytes per
-// (exit, vocabulary tile, token) at out + 16 ((e n_vt + tile) n + t).
+// (exit, vocabulary tile, token) at out + 16 ((e n_vt + tile) n + t): c1 (-inf
+// for the teacher), the teacher's scale, the label (grad_chunk.h).
 hipError_t launch_grad_consts(int n_exits, int64_t n, int vocab, const TileInfo& info,
-                              const int32_t* labels, const float* stats, const float* lse,
-                              void* out, hipStream_t s);
+                              const int32_t* labels, float alpha, float grad_scale,
+                              const ExitW& lam, const float* stats, const float* lse, void* out,
+                              hipStream_t s);
 // The losses and mean partials with Dist from dv (after launch_loss_merge with skip_dist).
 hipError_t launch_loss_finish(int n_exits, int64_t n, float alpha, const float* dv,
                               float* tokloss, double* partials, const ExitW& lam, hipStream_t s);

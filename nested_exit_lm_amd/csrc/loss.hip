@@ -415,9 +415,10 @@ __global__ __launch_bounds__(256) void finalize_vec(int M, int64_t n, int vocab,
 // g_M = lambda_M gs p, with the label's entry corrected only in the chunk that
 // holds it; sum_v p l_e over the chunk is sum p s + m_e sum p.  A bad label
 // makes the scale NaN, which turns the whole row into NaN.  The gradients
-// come from grad_chunk.h, shared with the backward GEMMs that form them
-// without storing them; WRITE_G = false keeps the buffers as they are and
-// computes dv only (for those GEMMs).
+// come from grad_chunk.h (grad_exit_row per row, grad_tile_c / grad_tile_k
+// per tile), shared with the backward GEMMs that form them without storing
+// them; WRITE_G = false keeps the buffers as they are and computes dv only
+// (for those GEMMs).
 template <int MS, bool WRITE_G>   // MS: the most smaller exits the loops are unrolled for
 __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int vocab, int vshift,
                                                          const int32_t* __restrict__ labels,
@@ -436,15 +437,21 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
     const bool bad = y < 0 || y >= vocab;
     const float nanv = __builtin_nanf("");
     const float lseT = lse[static_cast<int64_t>(M - 1) * n + t];
-    const float gT = bad ? nanv : gs * lam.w[M - 1];
-    float ge[MS], lseE[MS], acc[MS];
+    const float geT = gs * lam.w[M - 1];
+    const GradExitRow rT = grad_exit_row(true, bad ? nanv : fabsf(geT), alpha);
+    const uint32_t negT = geT < 0.f ? 0x80008000u : 0u;
+    GradExitRow rE[MS];
+    uint32_t negE[MS];
+    float lseE[MS], acc[MS];
 #pragma unroll
     for (int e = 0; e < MS; ++e) {
       acc[e] = 0.f;
-      ge[e] = 0.f;
       lseE[e] = 0.f;
+      negE[e] = 0u;
       if (e < S) {
-        ge[e] = bad ? nanv : gs * lam.w[e];
+        const float ge = gs * lam.w[e];
+        rE[e] = grad_exit_row(false, bad ? nanv : fabsf(ge), alpha);
+        negE[e] = ge < 0.f ? 0x80008000u : 0u;
         lseE[e] = lse[static_cast<int64_t>(e) * n + t];
       }
     }
@@ -474,7 +481,7 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
         const int64_t tile = v0 >> vshift;   // the tile width is a power of 2
         const float scT =
             fexp(stats[static_cast<int64_t>(M - 1) * 3 * plane + tile * n + t] - lseT);
-        const int yi = y - v0;   // the label's entry in this chunk when 0 <= yi < 8
+        const int yi = label_offset(y, v0);   // the label's entry in this chunk when 0 <= yi < 8
         float p[8];
         float sp = 0.f;
 #pragma unroll
@@ -490,16 +497,15 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
 #pragma unroll
           for (int i = 0; i < 8; ++i) ps = fmaf(p[i], Scratch<bf16_t>::get(sr[e][k], i), ps);
           acc[e] += fmaf(mt, sp, ps);
-          if constexpr (WRITE_G) {
-            const float c1 = (mt - lseE[e]) * kLog2e;
+          if constexpr (WRITE_G)
             __builtin_nontemporal_store(
-                grad_chunk_student(sr[e][k], tw[k], scT, c1, ge[e], alpha, yi),
+                grad_chunk(sr[e][k], tw[k], grad_tile_c(false, rE[e], mt, lseE[e]),
+                           grad_tile_k(rE[e], scT), rE[e].lab, yi, negE[e]),
                 reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[e]) + t * vocab) + c);
-          }
         }
         if constexpr (WRITE_G)
           __builtin_nontemporal_store(
-              grad_chunk_teacher(tw[k], scT, gT, yi),
+              grad_chunk_teacher(tw[k], grad_tile_k(rT, scT), rT.lab, yi, negT),
               reinterpret_cast<u32x4*>(static_cast<bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
       }
     }
@@ -518,13 +524,13 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
 }
 
 // Row constants of the gradients that the backward GEMMs form from the fp16
-// scratch (grad_chunk.h), per (vocabulary tile, token) over the plane:
-// exit e < M - 1 gets c1 = (m_e - LSE_e) log2 e, every exit the teacher's
-// sc = exp(m_M - LSE_M) and the label; both are NaN for a bad label, which
-// makes every gradient of that token NaN, as the in-place pass does.  The
-// expressions are those of finalize_rows_f16.
+// scratch (grad_chunk.h), per (exit, vocabulary tile, token) over the plane,
+// from the same expressions as finalize_rows_f16: |gs lambda_e| NaN for a bad
+// label, which makes every gradient of that token NaN, as the in-place pass
+// does.  The signs of gs lambda_e are left to the GEMMs.
 __global__ __launch_bounds__(256) void grad_consts_kernel(int M, int64_t n, int vocab, int n_vt,
                                                           const int32_t* __restrict__ labels,
+                                                          float alpha, float gs, ExitW lam,
                                                           const float* __restrict__ stats,
                                                           const float* __restrict__ lse,
                                                           GradRowConst* __restrict__ out) {
@@ -536,18 +542,19 @@ __global__ __launch_bounds__(256) void grad_consts_kernel(int M, int64_t n, int 
     const bool bad = y < 0 || y >= vocab;
     const float nanv = __builtin_nanf("");
     const float lseT = lse[static_cast<int64_t>(M - 1) * n + t];
-    const float scT = bad ? nanv : fexp(stats[static_cast<int64_t>(M - 1) * 3 * plane + tile * n + t] - lseT);
+    const float scT = fexp(stats[static_cast<int64_t>(M - 1) * 3 * plane + tile * n + t] - lseT);
     for (int e = 0; e < M; ++e) {
-      float c1 = 0.f;
-      if (e < M - 1) {
-        const float mt = stats[static_cast<int64_t>(e) * 3 * plane + tile * n + t];
-        c1 = bad ? nanv : (mt - lse[static_cast<int64_t>(e) * n + t]) * kLog2e;
-      }
+      const bool teacher = e == M - 1;
+      const GradExitRow r = grad_exit_row(teacher, bad ? nanv : fabsf(gs * lam.w[e]), alpha);
+      float c = -INFINITY;
+      if (!teacher)
+        c = grad_tile_c(false, r, stats[static_cast<int64_t>(e) * 3 * plane + tile * n + t],
+                        lse[static_cast<int64_t>(e) * n + t]);
       u32x4 v;
-      v[0] = __float_as_uint(c1);
-      v[1] = __float_as_uint(scT);
-      v[2] = static_cast<uint32_t>(y);
-      v[3] = 0u;
+      v[0] = __float_as_uint(c);
+      v[1] = __float_as_uint(grad_tile_k(r, scT));
+      v[2] = __float_as_uint(r.lab);
+      v[3] = static_cast<uint32_t>(y);
       *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(e) * plane + i) = v;
     }
   }
@@ -695,16 +702,17 @@ hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInf
 }
 
 hipError_t launch_grad_consts(int n_exits, int64_t n, int vocab, const TileInfo& info,
-                              const int32_t* labels, const float* stats, const float* lse,
-                              void* out, hipStream_t s) {
+                              const int32_t* labels, float alpha, float grad_scale,
+                              const ExitW& lam, const float* stats, const float* lse, void* out,
+                              hipStream_t s) {
   if (n == 0) return hipSuccess;
   if (!info.teacher_w16) return hipErrorInvalidValue;   // constants of the fp16 scratch only
   const int n_vt = (vocab + info.vtile - 1) / info.vtile;
   const int64_t plane = static_cast<int64_t>(n_vt) * n;
   const int64_t blocks = (plane + 255) / 256;
   hipLaunchKernelGGL(grad_consts_kernel, dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)),
-                     dim3(256), 0, s, n_exits, n, vocab, n_vt, labels, stats, lse,
-                     static_cast<GradRowConst*>(out));
+                     dim3(256), 0, s, n_exits, n, vocab, n_vt, labels, alpha, grad_scale, lam,
+                     stats, lse, static_cast<GradRowConst*>(out));
   return hipGetLastError();
 }
 

@@ -1,18 +1,18 @@
-// Main loop of the bf16 GEMMs whose A operand is in the MFMA-tiled layout
-// (device side; shared by the head GEMM and the head-backward GEMMs).
+// Shared pieces of the bf16 GEMMs whose A operand is in an MFMA-tiled layout
+// (device side): the tile geometry, the thread-to-chunk maps and plain B
+// sources, and the 32x32x16 main loop with a K-major B operand (the head
+// backward's dW GEMM).  The 16x16x32 main loop of the head GEMM and the dh
+// GEMM is in packed16_core.h.
 //
-// A workgroup of 4 wavefronts computes a 128 x 256 tile of C = B A^T:
+// The K-major loop: a workgroup of 4 wavefronts computes a 128 x 256 tile of
+// C = B A^T:
 //  * A: 256 rows (64 per wavefront, two 32-row blocks), packed so that every
 //    MFMA A operand is one contiguous 1 KB block: row block rb, K block kp
 //    (16 columns) at byte (rb * K / 16 + kp) * 1024, lane l's 16 bytes at
 //    l * 16 holding row 32 rb + vperm(l % 32), columns 16 kp + 8 (l / 32) ...+7.
 //    Each wavefront loads its blocks straight into registers, one K step
 //    (64 columns, 4 blocks per row block) ahead of the MFMAs.
-//  * B: 128 rows, row-major with K contiguous.  The workgroup loads each
-//    128 x 64 slice once and publishes it in LDS (double-buffered) for all
-//    four wavefronts.  LDS holds the slice chunk-major: row t, 16-byte chunk c
-//    in slot 128 c + (t ^ 2c), so the reads of 16 consecutive rows and the
-//    writes of 2 rows x 8 chunks both cover all 64 banks once per 16-lane pass.
+//  * B: 128 columns of a K-major matrix (below).
 //  * C: accumulator acc[tb][ab] is the 32 x 32 block (B rows 32 tb.., A rows
 //    32 ab..) of the wavefront; lane (q, h) holds B row 32 tb + q and the 16
 //    consecutive A rows 32 ab + 16 h + r, r = acc register.
@@ -28,28 +28,20 @@ constexpr int kPkBK = 64;         // K per step
 constexpr int kPkNTB = 4;         // B blocks of 32 rows per wavefront
 constexpr int kPkNAB = 2;         // A blocks of 32 rows per wavefront
 
-// Per-thread constants of the main loop.
+// Row-major B: which 16-byte chunks of each 128 x 64 slice a thread copies,
+// and where they go in the LDS stage (row t, chunk c in slot 128 c + (t ^ 2c)).
 struct PackedLanes {
   int hslot;          // LDS slot of this thread's first B chunk (next: + 32 j)
-  int bslot[4];       // LDS slot of the B fragment of K slice s, block 0 (block tb: + 32 tb)
   int brow, bchunk;   // B row and 16-byte chunk this thread loads (rows brow + 32 j)
-  uint32_t aoff;      // byte offset of this lane's 16 bytes in an A block
 };
 
 __device__ __forceinline__ PackedLanes packed_lanes(int tid) {
   PackedLanes p;
-  const int lane = tid & 63, q = lane & 31, hl = lane >> 5;
   p.bchunk = tid & 7;
   p.brow = tid >> 3;
   // chunk i = tid + 256 j of the 128 x 64 slice is row i / 8 = tid / 8 + 32 j,
   // chunk i % 8; slot 128 c + (t ^ 2c) = hslot + 32 j (2c < 32 leaves bit 5 alone)
   p.hslot = p.bchunk * kPkBRows + (p.brow ^ (2 * p.bchunk));
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int c = 2 * s + hl;
-    p.bslot[s] = c * kPkBRows + (q ^ (2 * c));
-  }
-  p.aoff = static_cast<uint32_t>(lane) * 16u;
   return p;
 }
 
@@ -57,102 +49,23 @@ __device__ __forceinline__ PackedLanes packed_lanes(int tid) {
 // chunks of B into LDS: issue(g) starts the loads of step g before the
 // step's matrix instructions, finish(hr) hands over the chunks after them.
 //
-// Row-major 16-bit B as stored.
+// Row-major 16-bit B as stored; NCH chunks per thread.
+template <int NCH = 4>
 struct BRowsPlain {
-  const char* Bb;     // byte base of the tile's B row 0
-  uint32_t boff[4];   // byte offsets from Bb of the thread's chunks (+128 per K step)
-  u32x4 r[4];
+  static constexpr int kChunks = NCH;
+  const char* Bb;       // byte base of the tile's B row 0
+  uint32_t boff[NCH];   // byte offsets from Bb of the thread's chunks (+128 per K step)
+  u32x4 r[NCH];
   __device__ __forceinline__ void issue(int g) {
     const char* a = Bb + static_cast<int64_t>(g) * (kPkBK * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const u32x4*>(a + boff[j]);
+    for (int j = 0; j < NCH; ++j) r[j] = *reinterpret_cast<const u32x4*>(a + boff[j]);
   }
-  __device__ __forceinline__ void finish(u32x4 (&hr)[4]) const {
+  __device__ __forceinline__ void finish(u32x4 (&hr)[NCH]) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hr[j] = r[j];
+    for (int j = 0; j < NCH; ++j) hr[j] = r[j];
   }
 };
-
-// acc = A(this wavefront's two row blocks) x B(the workgroup's 128 rows)^T
-// over K = 64 * nsteps.
-//   A0, A1: byte bases of the wavefront's two packed A row blocks
-//   src:    the B source (chunk i = tid + 256 j of a 128 x 64 slice is row
-//           i / 8, 16-byte chunk i % 8, as packed_lanes assigns them)
-//   hs:     the workgroup's two LDS stages
-// Every wavefront of the workgroup calls this together (it contains barriers).
-template <int NTB, int NAB, typename Src>
-__device__ __forceinline__ void packed_tile_gemm(f32x16 (&acc)[NTB][NAB],
-                                                 u32x4 (&hs)[2][8 * kPkBRows],
-                                                 const char* __restrict__ A0,
-                                                 const char* __restrict__ A1, Src& src,
-                                                 const PackedLanes& pl, int nsteps) {
-  static_assert(NAB == 2, "two A row blocks per wavefront");
-#pragma unroll
-  for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-    for (int ab = 0; ab < NAB; ++ab)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[tb][ab][r] = 0.f;
-
-  // One set of A fragments R[ab][s]: the half s = 2h, 2h + 1 is reloaded for
-  // the next step right after the step's last matrix instruction that reads
-  // it, and the B source's loads for the next step start with the step, so
-  // every load has half a step of this wavefront's matrix instructions ahead
-  // of its first use (the scheduling barriers keep that order).
-  u32x4 R[NAB][4], hr[4];
-  // A operands of step g, K slices s = 2h, 2h + 1: blocks kp = 4g + s
-  auto load_a = [&](int h, int g) {
-    const char* a0 = A0 + static_cast<int64_t>(g) * 4096;
-    const char* a1 = A1 + static_cast<int64_t>(g) * 4096;
-#pragma unroll
-    for (int s = 2 * h; s < 2 * h + 2; ++s) {
-      R[0][s] = *reinterpret_cast<const u32x4*>(a0 + pl.aoff + s * 1024);
-      R[1][s] = *reinterpret_cast<const u32x4*>(a1 + pl.aoff + s * 1024);
-    }
-  };
-  auto store_b = [&](int st) {
-    src.finish(hr);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hs[st][pl.hslot + 32 * j] = hr[j];
-  };
-  auto mfma = [&](int h, int st) {
-#pragma unroll
-    for (int s = 2 * h; s < 2 * h + 2; ++s) {
-      bf16x8 b[NTB];
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) b[tb] = __builtin_bit_cast(bf16x8, hs[st][pl.bslot[s] + 32 * tb]);
-#pragma unroll
-      for (int ab = 0; ab < NAB; ++ab) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, R[ab][s]);
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
-          acc[tb][ab] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[tb], acc[tb][ab], 0, 0, 0);
-      }
-    }
-  };
-  // Step g: compute step g from LDS stage st while loading step g + 1 (the
-  // last step re-reads itself), publish the loaded B slice in stage st ^ 1.
-  auto step = [&](int g, int st) {
-    const int gn = g + 1 < nsteps ? g + 1 : g;
-    src.issue(gn);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma(0, st);
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(0, gn);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma(1, st);
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(1, gn);
-    store_b(st ^ 1);
-    __syncthreads();
-  };
-  src.issue(0);
-  store_b(0);
-  load_a(0, 0);
-  load_a(1, 0);
-  __syncthreads();
-  for (int g = 0; g < nsteps; ++g) step(g, g & 1);
-}
 
 // The B source's thread copies, per K step gs, 16-byte chunk tid % 16 of
 // the slice's K rows tid / 16 + 16 j (KMajorLanes).
@@ -299,7 +212,11 @@ __device__ __forceinline__ void packed_tile_gemm_kmajor(f32x16 (&acc)[NTB][NAB],
     if (gs < nsteps) step2(R0, R1, gs, 0);
     return;
   }
-  // A fragments and load order as in packed_tile_gemm
+  // One set of A fragments R[ab][s]: the half s = 2h, 2h + 1 is reloaded for
+  // the next step right after the step's last matrix instruction that reads
+  // it, and the B source's loads for the next step start with the step, so
+  // every load has half a step of this wavefront's matrix instructions ahead
+  // of its first use (the scheduling barriers keep that order).
   u32x4 R[NAB][4], hr[4];
   auto load_a = [&](int h, int gs) {
     const char* a0 = A0 + static_cast<int64_t>(gs) * 4096;

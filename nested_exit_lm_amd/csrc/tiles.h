@@ -6,7 +6,7 @@ namespace nel {
 
 constexpr float kMasked = -1.0e30f;   // logit of a vocabulary entry beyond V
 // Loss epilogues: kModeLoss (row-major GEMM) forms the teacher-weighted sums
-// in the epilogue; the packed GEMM's kModeLossPlain stores l - m in bf16 for
+// in the epilogue; the packed GEMM's kModeLossPlain stores l - m in fp16 for
 // every exit and kModeLossF16 the teacher's weights and the smaller exits'
 // l - m in fp16 (sums formed by the gradient pass).
 enum { kModeLoss = 0, kModeArgmax = 1, kModeLossPlain = 2, kModeLossF16 = 3 };

@@ -59,6 +59,8 @@ CASES = [
     ("one-exit", (128,), 256, 1, 65, 0.3, 1.0, None, 73),
     ("vocab-64", (64, 128), 64, 1, 65, 1.0, 1.0, None, 74),
     ("alpha-0", (64, 128, 256), 768, 2, 64, 0.0, 1.0, (1.0, 0.0, 1.5), 75),
+    # a negative upstream gradient: every exit's sign flips, one weight is 0
+    ("negative-scale", (64, 128, 192), 512, 2, 70, 0.3, -0.75, (1.0, 0.0, 2.0), 76),
 ]
 
 

@@ -40,6 +40,8 @@
 // every exit.  No epilogue reads another exit's tile back.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "packed16_core.h"
@@ -118,7 +120,6 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
   f32x4 acc[NB][NB];
   for (int ei = 0; ei < n_exits; ++ei) {
     const int e = ei == 0 ? n_exits - 1 : ei - 1;
-    const bool teacher = MODE == kModeLossF16 && ei == 0;
     const int D = ex.d[e];
     W128Operands op;
     int hslot;
@@ -129,16 +130,23 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
     w128_tile_gemm(acc, stage, op, hslot, D / 64);
 
     // Opaque copies of values that are the same for every exit keep the
-    // compiler from hoisting the epilogue's per-lane predicates and label
-    // loads out of the exit loop, where they would be live (and spilled)
-    // across the main loop.
+    // compiler from hoisting the epilogue's per-lane offsets and predicates
+    // out of the exit loop, where they would be live (and spilled) across
+    // the main loop.
     int vwe = vw;
     int64_t t0e = t0;
-    const int32_t* lbl = labels;
     int lane = tid & 63;
-    asm volatile("" : "+s"(vwe), "+s"(t0e), "+s"(lbl), "+v"(lane));
+    asm volatile("" : "+s"(vwe), "+s"(t0e), "+v"(lane));
     const int x = lane & 15, g = lane >> 4;
-    const int64_t tx = t0e + x;   // token of this lane in token block 0
+    // the labels of this lane's 8 tokens, loaded ahead of their use (rows
+    // beyond n read row n - 1 and are dropped)
+    int ylab[NB];
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+      const int64_t tok = t0e + x + 16 * tb;
+      const int yy = labels[tok < n ? tok : n - 1];
+      ylab[tb] = tok < n ? yy : -1;
+    }
     // vocabulary entries beyond V vanish under exp; V is a multiple of 32, so
     // a 16-block is wholly in or beyond V
     if (vwe + 128 > vocab) {
@@ -151,99 +159,111 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
     float* __restrict__ st = stats + (static_cast<int64_t>(e) * 3 * n_st + (vwe >> 7)) * n;
     bf16_t* __restrict__ O = static_cast<bf16_t*>(ex.out[e]);
     char* const ob = reinterpret_cast<char*>(&outbuf[wave][0]);
+    // one instance per kind of exit, so that no branch sits inside the loops
+    auto epilogue = [&](auto teacher_tag) {
+      constexpr bool teacher = decltype(teacher_tag)::value;
 #pragma unroll
-    for (int tp = 0; tp < NB / 2; ++tp) {
+      for (int tp = 0; tp < NB / 2; ++tp) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tb = 2 * tp + u;
-        // row maximum over the wavefront's 128 entries: a lane's 32, then
-        // the four lane groups of its token (lanes 16 apart)
-        float m = acc[tb][0][0];
+        for (int u = 0; u < 2; ++u) {
+          const int tb = 2 * tp + u;
+          // row maximum over the wavefront's 128 entries: a lane's 32, then
+          // the four lane groups of its token (lanes 16 apart)
+          float m = acc[tb][0][0];
 #pragma unroll
-        for (int vb = 0; vb < NB; ++vb)
+          for (int vb = 0; vb < NB; ++vb)
 #pragma unroll
-          for (int i = (vb == 0 ? 1 : 0); i < 4; ++i) m = fmaxf(m, acc[tb][vb][i]);
-        m = fmaxf(m, __shfl_xor(m, 16, 64));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        const float ml = m * kLog2e;
-        const int row = 16 * u + x;
-        float s0 = 0.f, s1 = 0.f;
+            for (int i = (vb == 0 ? 1 : 0); i < 4; ++i) m = fmaxf(m, acc[tb][vb][i]);
+          m = fmaxf(m, __shfl_xor(m, 16, 64));
+          m = fmaxf(m, __shfl_xor(m, 32, 64));
+          const float ml = m * kLog2e;
+          const int row = 16 * u + x;
+          float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int vb = 0; vb < NB; ++vb) {
-          uint32_t pk0, pk1;
-          if (teacher) {
-            float wv[4];
+          for (int vb = 0; vb < NB; ++vb) {
+            uint32_t pk0, pk1;
+            if constexpr (teacher) {
+              float wv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wv[i] = __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i], kLog2e, -ml));
-            s0 += wv[0] + wv[2];
-            s1 += wv[1] + wv[3];
-            pk0 = pack_f16x2(wv[0], wv[1]);
-            pk1 = pack_f16x2(wv[2], wv[3]);
-          } else {
+              for (int i = 0; i < 4; ++i) wv[i] = __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i], kLog2e, -ml));
+              s0 += wv[0] + wv[2];
+              s1 += wv[1] + wv[3];
+              pk0 = pack_f16x2(wv[0], wv[1]);
+              pk1 = pack_f16x2(wv[2], wv[3]);
+            } else {
 #pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-              s0 += __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i], kLog2e, -ml));
-              s1 += __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i + 1], kLog2e, -ml));
+              for (int i = 0; i < 4; i += 2) {
+                s0 += __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i], kLog2e, -ml));
+                s1 += __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i + 1], kLog2e, -ml));
+              }
+              pk0 = pack_f16x2(acc[tb][vb][0] - m, acc[tb][vb][1] - m);
+              pk1 = pack_f16x2(acc[tb][vb][2] - m, acc[tb][vb][3] - m);
             }
-            pk0 = pack_f16x2(acc[tb][vb][0] - m, acc[tb][vb][1] - m);
-            pk1 = pack_f16x2(acc[tb][vb][2] - m, acc[tb][vb][3] - m);
+            // The 16-bit copies leave through LDS: a lane holds 8-byte pieces
+            // of one token row, but the wavefront's 128 entries of a row are
+            // 256 contiguous bytes.  Row r, 16-byte chunk c sits at slot
+            // 16 r + (c ^ (r mod 16)), so the 8-byte writes of a half
+            // wavefront and the 16-byte reads of 16 lanes each cover all 64
+            // banks.  Entries 16 vb + 4 g .. + 3: chunk 2 vb + g / 2, half g % 2.
+            const int c = 2 * vb + (g >> 1);
+            *reinterpret_cast<u32x2*>(ob + (16 * row + (c ^ x)) * 16 + 8 * (g & 1)) = u32x2{pk0, pk1};
           }
-          // The 16-bit copies leave through LDS: a lane holds 8-byte pieces of
-          // one token row, but the wavefront's 128 entries of a row are 256
-          // contiguous bytes.  Row r, 16-byte chunk c sits at slot
-          // 16 r + (c ^ (r mod 16)), so the 8-byte writes of a half wavefront
-          // and the 16-byte reads of 16 lanes each cover all 64 banks.
-          // Entries 16 vb + 4 g .. + 3: chunk 2 vb + g / 2, half g % 2.
-          const int c = 2 * vb + (g >> 1);
-          *reinterpret_cast<u32x2*>(ob + (16 * row + (c ^ x)) * 16 + 8 * (g & 1)) = u32x2{pk0, pk1};
-        }
-        float s = s0 + s1;
-        s += __shfl_xor(s, 16, 64);
-        s += __shfl_xor(s, 32, 64);
-        // the label's logit, from the one lane that holds it: entry
-        // 16 vb + 4 g + i of this wavefront
-        const int64_t tok = tx + 16 * tb;
-        const int y = tok < n ? lbl[tok] : -1;
-        const int rel = y - (vwe + 4 * g);
-        const int vsel = rel >> 4, isel = rel & 3;
-        float yv[4];
+          float s = s0 + s1;
+          s += __shfl_xor(s, 16, 64);
+          s += __shfl_xor(s, 32, 64);
+          // The label's logit, from the one lane that holds it: entry
+          // 16 vb + 4 g + i of this wavefront.  The 16 tokens of a block
+          // rarely have a label among the wavefront's 128 entries, so the
+          // selection runs only in a wavefront where one does.
+          const int64_t tok = t0e + x + 16 * tb;
+          const int y = ylab[tb];
+          const int rel = y - (vwe + 4 * g);
+          const bool hit = rel >= 0 && rel < 128 && (rel & 12) == 0 && y < vocab;
+          if (__any(hit)) {
+            const int vsel = rel >> 4, isel = rel & 3;
+            float yv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          yv[i] = acc[tb][0][i];
+            for (int i = 0; i < 4; ++i) {
+              yv[i] = acc[tb][0][i];
 #pragma unroll
-          for (int vb = 1; vb < NB; ++vb) yv[i] = vsel == vb ? acc[tb][vb][i] : yv[i];
-        }
-        float lv = yv[0];
+              for (int vb = 1; vb < NB; ++vb) yv[i] = vsel == vb ? acc[tb][vb][i] : yv[i];
+            }
+            float lv = yv[0];
 #pragma unroll
-        for (int i = 1; i < 4; ++i) lv = isel == i ? yv[i] : lv;
-        if (rel >= 0 && rel < 128 && (rel & 12) == 0 && y < vocab)
-          lab[static_cast<int64_t>(e) * n + tok] = lv;
-        // (a wavefront wholly beyond V, in the last tile only, writes nothing)
-        if (g == 0 && tok < n && vwe < vocab) {
-          st[tok] = m;
-          st[plane + tok] = s;
+            for (int i = 1; i < 4; ++i) lv = isel == i ? yv[i] : lv;
+            if (hit) lab[static_cast<int64_t>(e) * n + tok] = lv;
+          }
+          // (a wavefront wholly beyond V, in the last tile only, writes nothing)
+          if (g == 0 && tok < n && vwe < vocab) {
+            st[tok] = m;
+            st[plane + tok] = s;
+          }
         }
+        wave_lds_sync();
+        {
+          // chunk lane % 16 of rows lane / 16 + 4 j: wave-uniform row base,
+          // 32-bit lane offsets; whole row segments, not read again before
+          // the gradient pass: nontemporal
+          const int ch = lane & 15;
+          const bool col_ok = vwe + 8 * ch < vocab;
+          const uint32_t loff = (static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(vocab) +
+                                 8u * static_cast<uint32_t>(ch)) * 2u;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int row = 4 * j + (lane >> 4);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ob + (16 * row + (ch ^ (row & 15))) * 16);
+            char* rb = reinterpret_cast<char*>(O) + ((t0e + 32 * tp + 4 * j) * vocab + vwe) * 2;
+            if (col_ok && t0e + 32 * tp + row < n)
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
+          }
+        }
+        wave_lds_sync();
       }
-      wave_lds_sync();
-      {
-        // chunk lane % 16 of rows lane / 16 + 4 j: wave-uniform row base,
-        // 32-bit lane offsets; whole row segments, not read again before the
-        // gradient pass: nontemporal
-        const int ch = lane & 15;
-        const bool col_ok = vwe + 8 * ch < vocab;
-        const uint32_t loff = (static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(vocab) +
-                               8u * static_cast<uint32_t>(ch)) * 2u;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = 4 * j + (lane >> 4);
-          const u32x4 v = *reinterpret_cast<const u32x4*>(ob + (16 * row + (ch ^ (row & 15))) * 16);
-          char* rb = reinterpret_cast<char*>(O) + ((t0e + 32 * tp + 4 * j) * vocab + vwe) * 2;
-          if (col_ok && t0e + 32 * tp + row < n)
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
-        }
-      }
-      wave_lds_sync();
-    }
+    };
+    if (MODE == kModeLossF16 && ei == 0)
+      epilogue(std::true_type{});
+    else
+      epilogue(std::false_type{});
   }
 }
 

@@ -37,7 +37,8 @@ def log(msg):
 
 
 # Sources that make up the head GEMM whose HBM traffic the counter runs measured.
-GEMM_SOURCES = ("heads_packed.hip", "packed_core.h", "common.h", "tiles.h", "internal.h")
+GEMM_SOURCES = ("heads_packed.hip", "wave128_core.h", "packed16_core.h", "packed_core.h", "common.h",
+                "tiles.h", "internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -340,8 +341,8 @@ def summarize_counters(fetch_dir, write_dir):
     _, cw = pick(write, "AUnaryFunctor")
     f_scale = gib_kib / (sorted(cf)[len(cf) // 2])
     w_scale = gib_kib / (sorted(cw)[len(cw) // 2])
-    name, hf = pick(fetch, "heads_kernel_packed")
-    _, hw = pick(write, "heads_kernel_packed")
+    name, hf = pick(fetch, "heads_loss_kernel<3>")
+    _, hw = pick(write, "heads_loss_kernel<3>")
     fb = sum(hf) / len(hf) * 1024 * f_scale
     wb = sum(hw) / len(hw) * 1024 * w_scale
     res = {"source_hash": kernel_source_hash(), "kernel": name,

@@ -33,7 +33,7 @@
 // sum exp(l - m) and the label's logit (one statistics tile per wavefront),
 // and one 16-bit copy of those 128 logits in the exit's gradient buffer, in
 // fp16 (relative rounding 2^-11).  kModeLossF16 (the cross-entropy to the
-// teacher): the teacher (last exit, run first) stores its weights
+// teacher): the teacher (the last exit) stores its weights
 // w = exp(l_M - m), the smaller exits l - m; the row-wise gradient pass forms
 // the teacher-weighted sums sum_v p_v l_m,v from them.  kModeLossPlain (the
 // other divergences, whose pass reads every exit's l - m) stores l - m for
@@ -174,8 +174,7 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
           for (int vb = 0; vb < NB; ++vb)
 #pragma unroll
             for (int i = (vb == 0 ? 1 : 0); i < 4; ++i) m = fmaxf(m, acc[tb][vb][i]);
-          m = fmaxf(m, __shfl_xor(m, 16, 64));
-          m = fmaxf(m, __shfl_xor(m, 32, 64));
+          m = max_xor32(max_xor16(m));
           const float ml = m * kLog2e;
           const int row = 16 * u + x;
           float s0 = 0.f, s1 = 0.f;
@@ -208,9 +207,7 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
             const int c = 2 * vb + (g >> 1);
             *reinterpret_cast<u32x2*>(ob + (16 * row + (c ^ x)) * 16 + 8 * (g & 1)) = u32x2{pk0, pk1};
           }
-          float s = s0 + s1;
-          s += __shfl_xor(s, 16, 64);
-          s += __shfl_xor(s, 32, 64);
+          const float s = sum_xor32(sum_xor16(s0 + s1));
           // The label's logit, from the one lane that holds it: entry
           // 16 vb + 4 g + i of this wavefront.  The 16 tokens of a block
           // rarely have a label among the wavefront's 128 entries, so the

@@ -264,6 +264,193 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
   }
 }
 
+// ------------------------------------------------- loss GEMM, narrow exits
+// Two workgroups per CU, 128 tokens x 256 vocabulary entries each, on the main
+// loop of packed16_core.h (128 x 64 per wavefront, 128 accumulators): the
+// statistics tiles are the workgroup's 256 entries.  Its main loop is slower
+// than the one-wavefront-per-SIMD kernel's, but each workgroup's epilogue
+// runs beside the other workgroup's matrix instructions, which pays off when
+// the exits are narrow and the epilogue (the same per logit at any width) is
+// a large share of the work.
+template <int MODE>
+__global__ __launch_bounds__(kPkThreads, 2) void heads_loss_kernel_2wg(
+    ExitSet /*read through the kernarg pointer*/, int n_exits, int64_t n, int vocab,
+    const int32_t* __restrict__ labels, float* __restrict__ stats, float* __restrict__ lab,
+    int n_tt, int n_vt) {
+  // The exit table is the first kernel argument; indexing it through the
+  // kernarg segment pointer keeps per-exit lookups scalar.
+  const ExitSet& ex = *(const ExitSet*)__builtin_amdgcn_kernarg_segment_ptr();
+  __shared__ u32x4 hs[2][16 * kPkTok];
+  __shared__ float xmax[4][kPkTok];
+  __shared__ float xsum[4][kPkTok][2];
+
+  const int tid = threadIdx.x, lane = tid & 63, x = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tt, vt;
+  tile_coords(blockIdx.x, n_tt, n_vt, kPkGroup, tt, vt);
+  const int64_t t0 = static_cast<int64_t>(tt) * kPkTok;
+  const int vw = vt * kPkVoc + wave * 64;   // this wavefront's first vocabulary entry
+  const int vlane = vw + 4 * g;             // first of this lane's 4 entries in block 0
+  const int64_t tx = t0 + x;                // token of this lane in token block 0
+
+  int ylab[kNTB];
+#pragma unroll
+  for (int tb = 0; tb < kNTB; ++tb)
+    ylab[tb] = tx + 16 * tb < n ? labels[tx + 16 * tb] : -1;
+  const PackedLanes pl = packed_lanes(tid);
+  uint32_t hoff[4];   // byte offsets of this thread's h chunks from row t0 (rows beyond n clamped)
+  // packed row blocks of the wavefront's 4 vocabulary blocks, clamped: rows beyond V are never stored
+  int rbk[kNVB];
+#pragma unroll
+  for (int vb = 0; vb < kNVB; ++vb) rbk[vb] = min((vw >> 4) + vb, vocab / 16 - 1);
+
+  f32x4 acc[kNTB][kNVB];
+  for (int ei = 0; ei < n_exits; ++ei) {
+    const int e = ei == 0 ? n_exits - 1 : ei - 1;
+    const bool teacher = MODE == kModeLossF16 && ei == 0;
+    const int D = ex.d[e];
+    // wave-uniform bases; per-lane 32-bit byte offsets
+    const char* __restrict__ Hb = static_cast<const char*>(ex.h[e]) + t0 * D * 2;
+    const char* __restrict__ P = static_cast<const char*>(ex.w[e]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t row = min(t0 + pl.brow + 32 * j, n - 1) - t0;
+      hoff[j] = static_cast<uint32_t>((row * D + pl.bchunk * 8) * 2);
+    }
+    const char* Wb[kNVB];
+#pragma unroll
+    for (int vb = 0; vb < kNVB; ++vb) Wb[vb] = P + static_cast<int64_t>(rbk[vb]) * D * 32;
+    BRowsPlain<4> hsrc;
+    hsrc.Bb = Hb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hsrc.boff[j] = hoff[j];
+    packed16_tile_gemm(acc, hs, Wb, hsrc, pl.hslot, D / kPkBK);
+
+    // vocabulary entries beyond V (last tile only) vanish under exp and never
+    // win a max; V is a multiple of 32, so a 16-block is wholly in or beyond V
+    if (vt * kPkVoc + kPkVoc > vocab) {
+#pragma unroll
+      for (int vb = 0; vb < kNVB; ++vb)
+        if (vw + 16 * vb >= vocab)
+#pragma unroll
+          for (int tb = 0; tb < kNTB; ++tb) acc[tb][vb] = f32x4{kMasked, kMasked, kMasked, kMasked};
+    }
+
+    const int64_t plane = static_cast<int64_t>(n_vt) * n;
+    // (1) row maximum over the tile's 256 entries: a lane's 16, the four
+    // lane groups of its token (lanes 16 apart), then the 4 wavefronts
+#pragma unroll
+    for (int tb = 0; tb < kNTB; ++tb) {
+      float m = acc[tb][0][0];
+#pragma unroll
+      for (int vb = 0; vb < kNVB; ++vb)
+#pragma unroll
+        for (int i = (vb == 0 ? 1 : 0); i < 4; ++i) m = fmaxf(m, acc[tb][vb][i]);
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (g == 0) xmax[wave][16 * tb + x] = m;
+    }
+    __syncthreads();
+    float M[kNTB];
+#pragma unroll
+    for (int tb = 0; tb < kNTB; ++tb) {
+      const int j = 16 * tb + x;
+      M[tb] = fmaxf(fmaxf(xmax[0][j], xmax[1][j]), fmaxf(xmax[2][j], xmax[3][j]));
+    }
+    // (2) sums, teacher weights / shifted logits, label logit
+    bf16_t* __restrict__ O = static_cast<bf16_t*>(ex.out[e]);
+    // The 16-bit copies leave through LDS, 32 tokens at a time: a lane holds
+    // four 8-byte pieces of one token row, but the wavefront's 64 entries of
+    // a row are one aligned 128-byte line, so after a wave-local transpose
+    // eight lanes store a whole line.  The wavefront uses its own 4 KB of the
+    // h stage, which no wavefront reads again before the barrier that ends
+    // this exit's epilogue.  Row r, 16-byte chunk c sits at slot
+    // 8 r + (c ^ ((r / 2) mod 8)): the 8-byte writes of a half wavefront and
+    // the 16-byte reads of 16 lanes each cover all 64 banks.
+    char* const stage = reinterpret_cast<char*>(&hs[0][0]) + wave * 4096;
+#pragma unroll
+    for (int tp = 0; tp < kNTB / 2; ++tp) {
+      float s[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tb = 2 * tp + u;
+        const float ml = M[tb] * kLog2e;
+        const int row = 16 * u + x;
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int vb = 0; vb < kNVB; ++vb) {
+          uint32_t pk0, pk1;
+          if (teacher) {
+            float wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[i] = __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i], kLog2e, -ml));
+            s0 += wv[0] + wv[2];
+            s1 += wv[1] + wv[3];
+            pk0 = pack_f16x2(wv[0], wv[1]);
+            pk1 = pack_f16x2(wv[2], wv[3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+              s0 += __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i], kLog2e, -ml));
+              s1 += __builtin_amdgcn_exp2f(fmaf(acc[tb][vb][i + 1], kLog2e, -ml));
+            }
+            pk0 = pack_f16x2(acc[tb][vb][0] - M[tb], acc[tb][vb][1] - M[tb]);
+            pk1 = pack_f16x2(acc[tb][vb][2] - M[tb], acc[tb][vb][3] - M[tb]);
+          }
+          // entries 16 vb + 4 g .. + 3 of the row: chunk 2 vb + g / 2, half g % 2
+          const int c = 2 * vb + (g >> 1);
+          *reinterpret_cast<u32x2*>(stage + (8 * row + (c ^ ((row >> 1) & 7))) * 16 + 8 * (g & 1)) =
+              u32x2{pk0, pk1};
+          const int dd = ylab[tb] - (vlane + 16 * vb);
+          if (static_cast<unsigned>(dd) < 4u && ylab[tb] < vocab) {
+            float val = acc[tb][vb][0];
+#pragma unroll
+            for (int i = 1; i < 4; ++i) val = (i == dd) ? acc[tb][vb][i] : val;
+            lab[static_cast<int64_t>(e) * n + tx + 16 * tb] = val;
+          }
+        }
+        s[u] = s0 + s1;
+      }
+      wave_lds_sync();
+      {
+        // wave-uniform row base, 32-bit lane offsets (32 rows of 2 V bytes)
+        const int ch = lane & 7;
+        const uint32_t loff = (static_cast<uint32_t>(lane >> 3) * static_cast<uint32_t>(vocab) +
+                               8u * static_cast<uint32_t>(ch)) * 2u;
+        const bool col_ok = vw + 8 * ch < vocab;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 8 * j + (lane >> 3);
+          const u32x4 v =
+              *reinterpret_cast<const u32x4*>(stage + (8 * row + (ch ^ ((row >> 1) & 7))) * 16);
+          char* rb = reinterpret_cast<char*>(O) + ((t0 + 32 * tp + 8 * j) * vocab + vw) * 2;
+          // whole lines, not read again before the gradient pass: nontemporal
+          if (col_ok && t0 + 32 * tp + row < n)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float t = s[u];
+        t += __shfl_xor(t, 16, 64);
+        t += __shfl_xor(t, 32, 64);
+        if (g == 0) xsum[wave][32 * tp + 16 * u + x][0] = t;
+      }
+    }
+    __syncthreads();
+    // (3) thread j < 128 writes the statistics of token j
+    if (tid < kPkTok && t0 + tid < n) {
+      const int j = tid;
+      float* st = stats + (static_cast<int64_t>(e) * 3 * n_vt + vt) * n + t0 + j;
+      st[0] = fmaxf(fmaxf(xmax[0][j], xmax[1][j]), fmaxf(xmax[2][j], xmax[3][j]));
+      st[plane] = (xsum[0][j][0] + xsum[1][j][0]) + (xsum[2][j][0] + xsum[3][j][0]);
+    }
+    // xmax / xsum are next written after this exit's main loop, behind its
+    // barriers, which also end every read of them above
+  }
+}
+
 // ---------------------------------------------------------------- argmax GEMM
 // Greedy verify: per (token, tile) the maximum logit and its lowest index, on
 // the main loop of packed16_core.h (128 tokens x 256 entries per workgroup,
@@ -372,11 +559,27 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_argmax_kernel(
   }
 }
 
+// Exits whose mean width is below this use the two-workgroups-per-CU kernel
+// (measured at widths 512 / 768 / 1024: 955 against 878 TF/s; at
+// 1024 / 2304 / 4352: 1173 against 1239 TF/s for the other kernel).
+constexpr int kWideMeanD = 1536;
+
 template <int MODE>
 hipError_t launch_loss(int n_exits, int64_t n, int vocab, const ExitSet& ex, const int32_t* labels,
                        float* stats, float* lab, TileInfo* info, hipStream_t s) {
-  info->vtile = kW128StatTile;
   info->teacher_w16 = MODE == kModeLossF16;
+  int64_t dsum = 0;
+  for (int e = 0; e < n_exits; ++e) dsum += ex.d[e];
+  if (dsum < static_cast<int64_t>(kWideMeanD) * n_exits) {
+    info->vtile = kPkVoc;
+    if (n == 0) return hipSuccess;
+    const int n_tt = static_cast<int>((n + kPkTok - 1) / kPkTok);
+    const int n_vt = (vocab + kPkVoc - 1) / kPkVoc;
+    hipLaunchKernelGGL((heads_loss_kernel_2wg<MODE>), dim3(n_tt * n_vt), dim3(kPkThreads), 0, s,
+                       ex, n_exits, n, vocab, labels, stats, lab, n_tt, n_vt);
+    return hipGetLastError();
+  }
+  info->vtile = kW128StatTile;
   if (n == 0) return hipSuccess;
   const int n_tt = static_cast<int>((n + kW128Tok - 1) / kW128Tok);
   const int n_vt = (vocab + kW128Voc - 1) / kW128Voc;

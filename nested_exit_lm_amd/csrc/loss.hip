@@ -456,31 +456,42 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
       }
     }
     // four chunks per thread per round (chunks c0 + 256 k): every exit's
-    // loads of the round are issued before any of them is used, 12 16-byte
-    // loads in flight per thread for three exits
+    // loads of the round, and the tile statistics they need, are issued
+    // before any of them is used (12 16-byte loads in flight per thread for
+    // three exits).  No load sits under a condition: chunks past the row end
+    // re-read its last chunk and exit slots beyond the smaller exits re-read
+    // the teacher's row, and neither is used, so the compiler keeps every
+    // load of the round in flight at once.
+    const bf16_t* rowT = static_cast<const bf16_t*>(dl.p[M - 1]) + t * vocab;
+    const float* stTp = stats + static_cast<int64_t>(M - 1) * 3 * plane + t;
+    const bf16_t* rowE[MS];
+    const float* stEp[MS];
+#pragma unroll
+    for (int e = 0; e < MS; ++e) {
+      rowE[e] = static_cast<const bf16_t*>(dl.p[e < S ? e : M - 1]) + t * vocab;
+      stEp[e] = stats + static_cast<int64_t>(e < S ? e : M - 1) * 3 * plane + t;
+    }
     for (int64_t c0 = tid; c0 < cpr; c0 += 4 * 256) {
       u32x4 tw[4], sr[MS][4];
+      float mT[4], mE[MS][4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int64_t c = c0 + 256 * k;
-        if (c < cpr) {
-          tw[k] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(dl.p[M - 1]) + t * vocab) + c);
+        const int64_t cl = min(c0 + 256 * k, cpr - 1);
+        const int64_t tile = (cl * 8) >> vshift;   // the tile width is a power of 2
+        tw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowT) + cl);
 #pragma unroll
-          for (int e = 0; e < MS; ++e)
-            if (e < S)
-              sr[e][k] = __builtin_nontemporal_load(
-                  reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(dl.p[e]) + t * vocab) + c);
-        }
+        for (int e = 0; e < MS; ++e)
+          sr[e][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowE[e]) + cl);
+        mT[k] = stTp[tile * n];
+#pragma unroll
+        for (int e = 0; e < MS; ++e) mE[e][k] = stEp[e][tile * n];
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int64_t c = c0 + 256 * k;
         if (c >= cpr) break;
         const int v0 = static_cast<int>(c * 8);
-        const int64_t tile = v0 >> vshift;   // the tile width is a power of 2
-        const float scT =
-            fexp(stats[static_cast<int64_t>(M - 1) * 3 * plane + tile * n + t] - lseT);
+        const float scT = fexp(mT[k] - lseT);
         const int yi = label_offset(y, v0);   // the label's entry in this chunk when 0 <= yi < 8
         float p[8];
         float sp = 0.f;
@@ -492,7 +503,7 @@ __global__ __launch_bounds__(256) void finalize_rows_f16(int M, int64_t n, int v
 #pragma unroll
         for (int e = 0; e < MS; ++e) {
           if (e >= S) break;
-          const float mt = stats[static_cast<int64_t>(e) * 3 * plane + tile * n + t];
+          const float mt = mE[e][k];
           float ps = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) ps = fmaf(p[i], Scratch<bf16_t>::get(sr[e][k], i), ps);
@@ -693,8 +704,14 @@ hipError_t launch_finalize_rows(int n_exits, int64_t n, int vocab, const TileInf
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, n_exits, n, vocab, vshift, labels, alpha,
                        grad_scale, stats, lse, dl, n_vt, dv, lam);
   };
-  if (n_exits <= 3)
+  // unrolled for exactly the smaller exits there are (up to three), so that no
+  // load of an unused exit slot is issued
+  if (n_exits <= 2)
+    write_g ? go(finalize_rows_f16<1, true>) : go(finalize_rows_f16<1, false>);
+  else if (n_exits == 3)
     write_g ? go(finalize_rows_f16<2, true>) : go(finalize_rows_f16<2, false>);
+  else if (n_exits == 4)
+    write_g ? go(finalize_rows_f16<3, true>) : go(finalize_rows_f16<3, false>);
   else
     write_g ? go(finalize_rows_f16<kMaxExits - 1, true>)
             : go(finalize_rows_f16<kMaxExits - 1, false>);

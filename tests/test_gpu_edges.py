@@ -93,15 +93,23 @@ def _loss_either(nel, ds, packed, hs=None, ws=None, alpha=0.3):
     return to_np(tok), dl
 
 
-@pytest.mark.parametrize("packed", [False, True], ids=["row-major", "packed"])
-def test_student_equal_to_teacher_gives_teacher_entropy(nel, packed):
+# The packed path runs one of two GEMMs by the mean exit width (below 1536:
+# two workgroups per CU; from 1536, as at the benchmark widths: one wavefront
+# per SIMD); "packed-wide" takes the second.
+PATHS = [("row-major", False, (128, 256)), ("packed", True, (128, 256)),
+         ("packed-wide", True, (1536, 1664))]
+
+
+@pytest.mark.parametrize("name,packed,widths", PATHS, ids=[p[0] for p in PATHS])
+def test_student_equal_to_teacher_gives_teacher_entropy(nel, name, packed, widths):
     """l_1 = l_2 exactly: W^2 = [W^1, 0] and h_2 = [h_1, noise].  On the packed
     path Dist is formed from the fp16 teacher weights and fp16 l - m."""
     V = 3008 if packed else 3000
-    s = synth.make_suite((128, 256), V, 2, 96, seed=54)
-    s.w[1][:, :128] = s.w[0]
-    s.w[1][:, 128:] = 0
-    s.h[1][:, :128] = s.h[0]
+    d1 = widths[0]
+    s = synth.make_suite(widths, V, 2, 96, seed=54)
+    s.w[1][:, :d1] = s.w[0]
+    s.w[1][:, d1:] = 0
+    s.h[1][:, :d1] = s.h[0]
     ds = DevSuite(s)
     tok, _ = _loss_either(nel, ds, packed)
     l = oracle.heads([s.h[1]], [s.w[1]])[0]
@@ -110,11 +118,14 @@ def test_student_equal_to_teacher_gives_teacher_entropy(nel, packed):
     np.testing.assert_allclose(tok[0, 0], tok[1, 0], rtol=1e-5)   # same CE
 
 
-@pytest.mark.parametrize("packed", [False, True], ids=["row-major", "packed"])
-def test_single_exit_and_alpha_zero_reduce_to_cross_entropy(nel, packed):
+M1_PATHS = [("row-major", False, (64, 96, 160), 1100), ("packed", True, (64, 128, 192), 1120),
+            ("packed-wide", True, (1536, 1600, 1664), 1120)]
+
+
+@pytest.mark.parametrize("name,packed,widths,V", M1_PATHS, ids=[p[0] for p in M1_PATHS])
+def test_single_exit_and_alpha_zero_reduce_to_cross_entropy(nel, name, packed, widths, V):
     import torch.nn.functional as F
     import torch
-    widths, V = ((64, 128, 192), 1120) if packed else ((64, 96, 160), 1100)
     s = synth.make_suite(widths, V, 1, 130, seed=55)
     ds = DevSuite(s)
     for m in range(3):

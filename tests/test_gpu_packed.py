@@ -48,6 +48,15 @@ PACKED_SMALL = [
     ("4exit-tiny-vocab", (64, 128, 192, 256), 96, 1, 129, 53),
     ("1exit", (64,), 256, 1, 1, 54),
     ("3exit-odd-steps", (64, 192, 320), 800, 1, 257, 55),
+    # mean width >= 1536: the one-wavefront-per-SIMD kernel (512-entry tiles,
+    # statistics per 128 entries).  Partial last tile with wavefronts wholly
+    # beyond V, V below one wavefront's 128 entries, odd step counts, exits of
+    # fewer K steps than the main loop's unrolling (1 and 5)
+    ("3exit-wide-ragged", (1536, 1600, 1664), 1056, 1, 300, 58),
+    ("2exit-wide-tiny-vocab", (1536, 1600), 96, 1, 129, 59),
+    ("1exit-wide", (1600,), 544, 2, 70, 60),
+    ("2exit-wide-short-exits", (64, 3008), 512, 1, 140, 61),
+    ("2exit-wide-five-steps", (320, 2752), 640, 1, 131, 62),
 ]
 
 

@@ -451,6 +451,95 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_loss_kernel_2wg(
   }
 }
 
+// ------------------------------------------- argmax GEMM, one wavefront per SIMD
+// Greedy verify on the main loop of wave128_core.h: one exit per workgroup
+// (the widest exit's tiles first), 128 tokens x 512 entries; per token and
+// wavefront the maximum logit of its 128 entries and the lowest index that
+// holds it (one tile of the argmax merge per wavefront); optional fp32 logits.
+__global__ __launch_bounds__(kW128Threads, 1) void heads_argmax_kernel_w128(
+    ExitSet /*read through the kernarg pointer*/, int n_exits, int64_t n, int vocab,
+    float* __restrict__ best, int n_tt, int n_vt_wg, int n_st) {
+  const ExitSet& ex = *(const ExitSet*)__builtin_amdgcn_kernarg_segment_ptr();
+  __shared__ u32x4 stage[kW128Stages * kW128Slots];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k = blockIdx.x / (n_tt * n_vt_wg);
+  const int e = n_exits - 1 - k;
+  int tt, vt;
+  tile_coords(blockIdx.x - k * (n_tt * n_vt_wg), n_tt, n_vt_wg, kPkGroup, tt, vt);
+  const int64_t t0 = static_cast<int64_t>(tt) * kW128Tok;
+  const int vw = vt * kW128Voc + wave * 128;   // this wavefront's first vocabulary entry
+  const int D = ex.d[e];
+  W128Operands op;
+  int hslot;
+  w128_lanes(tid, D, op, hslot);
+  op.h = make_rsrc(static_cast<const char*>(ex.h[e]) + t0 * D * 2, (n - t0) * D * 2);
+  op.w = make_rsrc(static_cast<const char*>(ex.w[e]) + static_cast<int64_t>(vw >> 4) * D * 32,
+                   static_cast<int64_t>(vocab / 16 - (vw >> 4)) * D * 32);
+  constexpr int NB = 8;
+  f32x4 acc[NB][NB];
+  w128_tile_gemm(acc, stage, op, hslot, D / 64);
+  // opaque copies: the epilogue's lane values are computed here, not kept
+  // live (and spilled) across the main loop
+  int vwe = vw;
+  int64_t t0e = t0;
+  int lane = tid & 63;
+  asm volatile("" : "+s"(vwe), "+s"(t0e), "+v"(lane));
+  const int x = lane & 15, g = lane >> 4;
+  // entries beyond V never win a max; V is a multiple of 32, so a 16-block is
+  // wholly in or beyond V
+  if (vwe + 128 > vocab) {
+#pragma unroll
+    for (int vb = 0; vb < NB; ++vb)
+      if (vw + 16 * vb >= vocab)
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) acc[tb][vb] = f32x4{kMasked, kMasked, kMasked, kMasked};
+  }
+  const int vlane = vwe + 4 * g;   // first of this lane's 4 entries in block 0
+  const int64_t plane = static_cast<int64_t>(n_st) * n;
+  float* __restrict__ O = static_cast<float*>(ex.out[e]);
+#pragma unroll
+  for (int tb = 0; tb < NB; ++tb) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int vb = 0; vb < NB; ++vb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (acc[tb][vb][i] > bv) {   // ascending vocabulary: strict > keeps the lowest index
+          bv = acc[tb][vb][i];
+          bi = vlane + 16 * vb + i;
+        }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    const int64_t tok = t0e + x + 16 * tb;
+    if (O != nullptr && tok < n) {
+#pragma unroll
+      for (int vb = 0; vb < NB; ++vb) {
+        const int vbase = vlane + 16 * vb;
+        if (vbase >= vocab) continue;
+        u32x4 pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = __float_as_uint(acc[tb][vb][i]);
+        *reinterpret_cast<u32x4*>(O + tok * vocab + vbase) = pk;
+      }
+    }
+    // (a wavefront wholly beyond V, in the last tile only, writes nothing)
+    if (g == 0 && tok < n && vwe < vocab) {
+      float* b = best + (static_cast<int64_t>(e) * 2 * n_st + (vwe >> 7)) * n + tok;
+      b[0] = bv;
+      b[plane] = __int_as_float(bi);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- argmax GEMM
 // Greedy verify: per (token, tile) the maximum logit and its lowest index, on
 // the main loop of packed16_core.h (128 tokens x 256 entries per workgroup,
@@ -559,6 +648,8 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_argmax_kernel(
   }
 }
 
+constexpr int64_t kCUs = 256;   // compute units of the MI355X
+
 // Exits whose mean width is below this use the two-workgroups-per-CU kernel
 // (measured at widths 512 / 768 / 1024: 955 against 878 TF/s; at
 // 1024 / 2304 / 4352: 1173 against 1239 TF/s for the other kernel).
@@ -613,8 +704,23 @@ hipError_t launch_heads_loss_packed(int n_exits, int64_t n, int vocab, const Exi
 
 hipError_t launch_heads_argmax_packed(int n_exits, int64_t n, int vocab, const ExitSet& ex,
                                       float* best, TileInfo* info, hipStream_t s) {
-  info->vtile = kPkVoc;
   info->teacher_w16 = false;
+  // The one-wavefront-per-SIMD kernel when its grid gives every CU at least
+  // two workgroups (its tiles are twice as wide); below that, at small token
+  // counts, the two-workgroups-per-CU kernel keeps more CUs busy.
+  {
+    const int64_t n_tt = (n + kW128Tok - 1) / kW128Tok;
+    const int n_vt = (vocab + kW128Voc - 1) / kW128Voc;
+    if (n_tt * n_vt * n_exits >= 2 * kCUs) {
+      info->vtile = kW128StatTile;
+      const int n_st = (vocab + kW128StatTile - 1) / kW128StatTile;
+      hipLaunchKernelGGL(heads_argmax_kernel_w128, dim3(static_cast<unsigned>(n_tt * n_vt * n_exits)),
+                         dim3(kW128Threads), 0, s, ex, n_exits, n, vocab, best,
+                         static_cast<int>(n_tt), n_vt, n_st);
+      return hipGetLastError();
+    }
+  }
+  info->vtile = kPkVoc;
   if (n == 0) return hipSuccess;
   const int n_tt = static_cast<int>((n + kPkTok - 1) / kPkTok);
   const int n_vt = (vocab + kPkVoc - 1) / kPkVoc;

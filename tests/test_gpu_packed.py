@@ -118,8 +118,13 @@ def test_packed_loss_full_size_sampled(nel, k, alpha):
         assert float(dl[m].float().sum(dim=1).abs().max()) < 5e-2
 
 
-def test_packed_heads_logits_partial_tile(nel):
-    s = synth.make_suite((64, 128), 544, 1, 131, seed=59)
+@pytest.mark.parametrize("V,S", [(544, 131), (1056, 11264)], ids=["few-tokens", "many-tokens"])
+def test_packed_heads_logits_partial_tile(nel, V, S):
+    """Logits and argmax against the oracle with a partial last vocabulary
+    tile.  Few tokens run the two-workgroups-per-CU argmax GEMM; 11,264 tokens
+    give the one-wavefront-per-SIMD one at least two workgroups per CU (its
+    512-entry tiles: the last has wavefronts wholly beyond V)."""
+    s = synth.make_suite((64, 128), V, 1, S, seed=59)
     ds = DevSuite(s)
     pw = [nel.pack_weights(w) for w in ds.w]
     logits, am = nel.exit_heads_packed(ds.h, pw, want_logits=True, want_argmax=True)

@@ -402,9 +402,10 @@ size_t nel_heads_backward_workspace(int32_t n_exits, int64_t n_tokens, int32_t v
  *     dw[e] = G_e^T h_e    [vocab, d_e]    fp32
  * The head GEMM leaves its 16-bit scratch in scratch[e]; the dh and dw GEMMs
  * form each 64-entry slice of G_e from it and per-row constants in
- * registers, with the arithmetic of the gradient pass, so dh and dw are
- * bit-identical to nel_matryoshka_loss_packed (same inputs, dlogits =
- * scratch) followed by nel_heads_backward on the stored gradients.
+ * registers, with the arithmetic of the gradient pass, so G_e is bit for
+ * bit the one nel_matryoshka_loss_packed stores (same inputs, dlogits =
+ * scratch): dh is then bit-identical to nel_heads_backward on the stored
+ * gradients, and dw sums the same products in another fp32 order.
  *   h, labels, alpha_d, grad_scale, exit_weights, token_loss, mean_loss:
  *            as nel_matryoshka_loss (the divergence is NEL_DIV_FORWARD)
  *   w:        host array of n_exits device bf16 [vocab, d_e] (row-major heads,

@@ -563,8 +563,8 @@ def loss_backward_packed(hs: Sequence, ws: Sequence, ws_packed: Sequence, labels
     (bf16 [V, d_m]); ws_packed: the same heads from pack_weights; scratch: n x V 16-bit
     buffers, one per exit (allocated when None).  The workspace's first int32 is the
     device flag word.  Returns (mean_loss, token_loss | None, [dh_m bf16] | None,
-    [dW_m fp32] | None), bit-identical to matryoshka_loss_packed followed by
-    heads_backward."""
+    [dW_m fp32] | None): dh bit-identical to matryoshka_loss_packed followed by
+    heads_backward, dW the same products summed in another fp32 order."""
     torch = _torch()
     M = len(hs)
     if not (len(ws) == M == len(ws_packed)) or not 1 <= M <= MAX_EXITS:

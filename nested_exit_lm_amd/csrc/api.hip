@@ -586,7 +586,7 @@ nel_status nel_head_backward(nel_dtype dt, int64_t n_tokens, int32_t vocab, int3
     if (err != hipSuccess) return from_hip(err);
   }
   if (dw) {
-    err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack_t(h, n_tokens, d, L.n_pad, ht, s); });
+    err = timed(NEL_K_BWD_PACK, s, [&] { return launch_pack16_t(h, n_tokens, d, L.n_pad, ht, s); });
     if (err != hipSuccess) return from_hip(err);
     // G itself is the K-major B operand: no transposed copy
     BwdGroup gw{};
@@ -656,7 +656,7 @@ nel_status nel_heads_backward(nel_dtype dt, int32_t n_exits, int64_t n_tokens, i
     }
     if (dw) {
       err = timed(NEL_K_BWD_PACK, s, [&] {
-        return launch_pack_t(h[e], n_tokens, d[e], L.n_pad, base + L.ht, s);
+        return launch_pack16_t(h[e], n_tokens, d[e], L.n_pad, base + L.ht, s);
       });
       if (err != hipSuccess) return from_hip(err);
       if (!bwd_group_add(gw, base + L.ht, d[e], dlogits[e], vocab, vocab, L.n_pad, dw[e], d[e],

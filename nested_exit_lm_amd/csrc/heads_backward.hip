@@ -186,7 +186,6 @@ struct BRowsGrad {
 // 128 vocabulary entries inside one statistics tile (dW = G^T h).  Tokens
 // from n on read as 0.
 struct BKMajorGrad {
-  static constexpr bool kPinLoads = true;
   const char* S;              // exit's scratch at (token lrow, entry v0) (bytes)
   const char* W;              // the teacher's weights, same place
   const GradRowConst* tab;    // the exit's constants of the tile's statistics tile, [n]
@@ -335,12 +334,14 @@ __global__ __launch_bounds__(kPkThreads, FUSED ? 1 : 2) void dh16_kernel(
 
 // ---------------------------------------------------------------- dW GEMM
 // dW[v][d] = sum_t G[t][v] h[t][d]: out[b][a] = sum_k A[a][k] B(b, k) with
-// A = h^T tiled (a_rows = d, K = padded tokens) and B read K-major from G
-// (b = vocabulary entry, k = token; K rows from k_valid read as 0), fp32
-// output.  Grouped over the exits like dh16_kernel.  FUSED: B is the exit's G
-// formed from its scratch (g.B[e]) and the teacher's (g.tw).
-template <bool FUSED>
-__global__ __launch_bounds__(kPkThreads, 2) void dw_gemm_kernel(
+// A = h^T tiled for the 32x32x16 loop (a_rows = d, K = padded tokens,
+// launch_pack_t) and B the exit's G, read K-major (b = vocabulary entry,
+// k = token; K rows from k_valid read as 0) and formed from its scratch
+// (g.B[e]) and the teacher's (g.tw); fp32 output.  Grouped over the exits
+// like dh16_kernel.  The gradients it forms are those the loss pass stores,
+// so its dW differs from the stored-gradient one only by the fp32 summation
+// order of the same products.
+__global__ __launch_bounds__(kPkThreads, 2) void dw_fused_kernel(
     BwdGroup /*read through the kernarg pointer*/) {
   // Per-product fields are read through the kernarg segment pointer, which
   // keeps the lookups by a run-time product index scalar.
@@ -368,24 +369,19 @@ __global__ __launch_bounds__(kPkThreads, 2) void dw_gemm_kernel(
   const int nsteps = static_cast<int>(K / kPkBK);
   const int cols = static_cast<int>(min(b_rows - b0, static_cast<int64_t>(kPkBRows)));
   const KMajorLanes kl = kmajor_lanes(tid);
-  if constexpr (FUSED) {
-    BKMajorGrad src;
-    const int64_t off = (static_cast<int64_t>(kl.lrow) * ldb + b0 + 8 * kl.lchunk) * 2;
-    src.S = reinterpret_cast<const char*>(B) + off;
-    src.W = reinterpret_cast<const char*>(g.tw) + off;
-    src.tab = static_cast<const GradRowConst*>(g.tab[e]) + (b0 >> g.vshift) * g.n_tok;
-    src.n = g.k_valid[e];
-    src.step_bytes = int64_t{kPkBK} * ldb * 2;
-    src.rstride = static_cast<uint32_t>(16 * ldb * 2);
-    src.lrow = kl.lrow;
-    src.v0 = static_cast<int>(b0) + 8 * kl.lchunk;
-    src.col_ok = 8 * kl.lchunk < cols;
-    src.neg = g.neg[e];
-    packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, A0, A1, src, nsteps);
-  } else {
-    BKMajorPlain src(reinterpret_cast<const char*>(B + b0), ldb, g.k_valid[e], cols, kl);
-    packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, A0, A1, src, nsteps);
-  }
+  BKMajorGrad src;
+  const int64_t off = (static_cast<int64_t>(kl.lrow) * ldb + b0 + 8 * kl.lchunk) * 2;
+  src.S = reinterpret_cast<const char*>(B) + off;
+  src.W = reinterpret_cast<const char*>(g.tw) + off;
+  src.tab = static_cast<const GradRowConst*>(g.tab[e]) + (b0 >> g.vshift) * g.n_tok;
+  src.n = g.k_valid[e];
+  src.step_bytes = int64_t{kPkBK} * ldb * 2;
+  src.rstride = static_cast<uint32_t>(16 * ldb * 2);
+  src.lrow = kl.lrow;
+  src.v0 = static_cast<int>(b0) + 8 * kl.lchunk;
+  src.col_ok = 8 * kl.lchunk < cols;
+  src.neg = g.neg[e];
+  packed_tile_gemm_kmajor<NTB, NAB>(acc, hs, A0, A1, src, nsteps);
   // Stores leave through a wave-local LDS transpose, one 32-row block at a
   // time: a lane holds 16 consecutive outputs of one row, but the
   // wavefront's 64 fp32 outputs of a row are two whole 128-byte lines, so
@@ -424,6 +420,83 @@ __global__ __launch_bounds__(kPkThreads, 2) void dw_gemm_kernel(
       char* rb = reinterpret_cast<char*>(out) + r0 * ldo * 4;
       if (col_ok && r0 + (lane >> 4) < b_rows)
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
+    }
+    wave_lds_sync();
+  }
+}
+
+// ---------------------------------------------------------------- dW GEMM
+// The stored-gradient dW on the 16x16x32 K-major main loop (packed16_core.h):
+// the product of dw_fused_kernel with B the stored G and A = h^T in the
+// 16-row tiled layout (launch_pack16_t).  A wavefront owns 128 vocabulary rows x 64 columns of d.
+// (The fused dW stays on dw_fused_kernel: forming the gradients beside
+// this loop's operands needs more than the 256 registers of two workgroups
+// per CU, and at one workgroup per CU it measured slower than the 32x32x16
+// loop at two.)
+// The fp32 outputs leave through a wave-local LDS transpose of one 16-row
+// block at a time: a lane holds four consecutive d of one row per 16 x 16
+// block, the wavefront's 64 d of a row are 256 contiguous bytes, and after
+// the transpose 16 lanes store each row's 256 bytes (nontemporal).  Row r,
+// 16-byte chunk c of the wavefront's 4 KB sits at slot 16 r + (c ^ r).
+__global__ __launch_bounds__(kPkThreads, 2) void dw16_kernel(
+    BwdGroup /*read through the kernarg pointer*/) {
+  const BwdGroup& g = *(const BwdGroup*)__builtin_amdgcn_kernarg_segment_ptr();
+  __shared__ u32x4 hs[2][16 * kPkBRows];
+  int e = 0;
+  while (e + 1 < g.count && static_cast<int>(blockIdx.x) >= g.first[e + 1]) ++e;
+  const char* __restrict__ A = reinterpret_cast<const char*>(g.A[e]);
+  const bf16_t* __restrict__ B = g.B[e];
+  char* __restrict__ out = static_cast<char*>(g.out[e]);
+  const int a_rows = g.a_rows[e];
+  const int64_t b_rows = g.b_rows[e], ldb = g.ldb[e], K = g.K[e], ldo = g.ldo[e];
+  const int tid = threadIdx.x, lane = tid & 63, x = lane & 15, gq = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int bt, at;
+  tile_coords(static_cast<int>(blockIdx.x) - g.first[e], g.n_bt[e], g.n_at[e], kBwdGroup, bt, at);
+  const int64_t b0 = static_cast<int64_t>(bt) * kPkBRows;
+  const int aw = at * kPkARows + wave * 64;   // this wavefront's first column of d
+  const int cols = static_cast<int>(min(b_rows - b0, static_cast<int64_t>(kPkBRows)));
+  const KMajorLanes kl = kmajor_lanes(tid);
+  // the wavefront's 4 packed A row blocks (a wavefront beyond a_rows reads
+  // the last 4 and stores nothing)
+  const int rb0 = min(aw >> 4, a_rows / 16 - k16NAB);
+  const uint32_t ablock = static_cast<uint32_t>((K / 32) * 1024);
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(A) + static_cast<int64_t>(rb0) * ablock, 0,
+      static_cast<int>(k16NAB * ablock), 0x00020000);
+  const int nsteps = static_cast<int>(K / kPkBK);
+  f32x4 acc[k16NTB][k16NAB];
+  BKMajorBuf src;
+  src.Bb = reinterpret_cast<const char*>(B + b0);
+  src.ldb = ldb;
+  src.k_valid = g.k_valid[e];
+  src.voff = 8 * kl.lchunk < cols ? static_cast<uint32_t>((kl.lrow * ldb + 8 * kl.lchunk) * 2)
+                                   : 0x80000000u;   // beyond the step's byte range: reads as zero
+  packed16_tile_gemm_kmajor(acc, hs, ar, ablock, src, nsteps);
+  char* const stage = reinterpret_cast<char*>(&hs[0][0]) + wave * 4096;
+  const bool col_ok = aw < a_rows;   // a_rows % 64 == 0: all 64 columns or none
+  const int ch = lane & 15;
+  // 32-bit lane offsets from a wave-uniform row base (ldo is below 2^22)
+  const uint32_t loff = (static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(ldo) +
+                         static_cast<uint32_t>(aw + 4 * ch)) * 4u;
+#pragma unroll
+  for (int tb = 0; tb < k16NTB; ++tb) {
+#pragma unroll
+    for (int ab = 0; ab < k16NAB; ++ab) {
+      // d = 16 ab + 4 gq .. + 3 of row x: chunk 4 ab + gq
+      u32x4 pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = __float_as_uint(acc[tb][ab][i] + 0.0f);
+      *reinterpret_cast<u32x4*>(stage + (16 * x + ((4 * ab + gq) ^ x)) * 16) = pk;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * j + (lane >> 4);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (16 * row + (ch ^ row)) * 16);
+      const int64_t r0 = b0 + 16 * tb + 4 * j;   // this store's first row
+      if (col_ok && r0 + (lane >> 4) < b_rows)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + r0 * ldo * 4 + loff));
     }
     wave_lds_sync();
   }
@@ -503,8 +576,12 @@ hipError_t launch_dh_group(const BwdGroup& g, hipStream_t s) {
 template <bool FUSED>
 hipError_t launch_dw_group(const BwdGroup& g, hipStream_t s) {
   if (g.count == 0 || g.first[g.count] == 0) return hipSuccess;
-  hipLaunchKernelGGL((dw_gemm_kernel<FUSED>), dim3(static_cast<unsigned>(g.first[g.count])),
-                     dim3(kPkThreads), 0, s, g);
+  if constexpr (FUSED)
+    hipLaunchKernelGGL(dw_fused_kernel, dim3(static_cast<unsigned>(g.first[g.count])),
+                       dim3(kPkThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL(dw16_kernel, dim3(static_cast<unsigned>(g.first[g.count])),
+                       dim3(kPkThreads), 0, s, g);
   return hipGetLastError();
 }
 

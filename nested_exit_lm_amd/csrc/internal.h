@@ -140,10 +140,9 @@ bool bwd_group_add(BwdGroup& g, const void* A, int a_rows, const void* B, int64_
                    int64_t ldb, int64_t K, void* out, int64_t ldo, int64_t k_valid = -1);
 // dh: out[b][a] = sum_k A[a][k] B[b][k], A tiled for the 16x16x32 loop
 // (launch_pack16_t), B row-major [b_rows x ldb] with K contiguous; bf16 out.
-// dW: the same with A tiled for the 32x32x16 loop (launch_pack_t) and B(b, k)
-// the element k * ldb + b of a row-major [K x ldb] matrix (b_rows columns of
-// it; K rows k_valid.. read as 0); fp32 out.  FUSED: B is formed from the
-// scratch (the fused fields of the group).
+// dW: the same with B(b, k) the element k * ldb + b of a row-major [K x ldb]
+// matrix (b_rows columns of it; K rows k_valid.. read as 0); fp32 out.
+// FUSED: B is formed from the scratch (the fused fields of the group).
 template <bool FUSED>
 hipError_t launch_dh_group(const BwdGroup& g, hipStream_t s);
 template <bool FUSED>

@@ -1,8 +1,8 @@
 // Shared pieces of the bf16 GEMMs whose A operand is in an MFMA-tiled layout
 // (device side): the tile geometry, the thread-to-chunk maps and plain B
-// sources, and the 32x32x16 main loop with a K-major B operand (the head
-// backward's dW GEMM).  The 16x16x32 main loop of the head GEMM and the dh
-// GEMM is in packed16_core.h.
+// sources, and the 32x32x16 main loop with a K-major B operand (the fused
+// head backward's dW GEMM).  The 16x16x32 main loops of the head GEMM, the dh
+// GEMM and the stored-gradient dW GEMM are in packed16_core.h.
 //
 // The K-major loop: a workgroup of 4 wavefronts computes a 128 x 256 tile of
 // C = B A^T:
@@ -74,41 +74,6 @@ struct KMajorLanes {
 };
 __device__ __forceinline__ KMajorLanes kmajor_lanes(int tid) { return {tid >> 4, tid & 15}; }
 
-// K-major 16-bit B as stored.
-struct BKMajorPlain {
-  static constexpr bool kPinLoads = false;
-  const char* Bb;     // byte address of element (k = 0, column b0) of the tile
-  int64_t step_bytes; // 64 K rows
-  int64_t k_valid;    // K rows that exist (the rest read as 0)
-  uint32_t boff[4];
-  int lrow;
-  bool col_ok;        // the thread's 8 columns exist
-  u32x4 r[4];
-  // ldb: row stride of the K-major matrix, in elements (< 2^24);
-  // cols_valid: columns of this tile that exist (a multiple of 8, <= 128)
-  __device__ __forceinline__ BKMajorPlain(const char* b, int64_t ldb, int64_t kv, int cols_valid,
-                                          KMajorLanes kl)
-      : Bb(b), step_bytes(int64_t{kPkBK} * ldb * 2), k_valid(kv), lrow(kl.lrow),
-        col_ok(8 * kl.lchunk < cols_valid) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      boff[j] = static_cast<uint32_t>(((kl.lrow + 16 * j) * ldb + 8 * kl.lchunk) * 2);
-  }
-  __device__ __forceinline__ void issue(int gs) {
-    const char* base = Bb + gs * step_bytes;
-    const int64_t k0 = static_cast<int64_t>(gs) * kPkBK + lrow;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      r[j] = u32x4{0u, 0u, 0u, 0u};
-      if (col_ok && k0 + 16 * j < k_valid) r[j] = *reinterpret_cast<const u32x4*>(base + boff[j]);
-    }
-  }
-  __device__ __forceinline__ void finish(u32x4 (&hr)[4]) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hr[j] = r[j];
-  }
-};
-
 // Variant whose B operand is stored K-major: B(b, k) is the element at
 // (k * ldb + b) of a row-major [K x ldb] matrix, e.g. the logit gradients
 // G [tokens x vocabulary] when the product runs over tokens (dW = G^T h).
@@ -152,66 +117,6 @@ __device__ __forceinline__ void packed_tile_gemm_kmajor(f32x16 (&acc)[NTB][NAB],
     roff[tb] = static_cast<uint32_t>((8 * (g >> 1) + ja) * 256 + 64 * (tb ^ ja) + 32 * (g & 1) + 8 * aa);
   const uint32_t aoff = static_cast<uint32_t>(lane) * 16u;
 
-  if constexpr (!Src::kPinLoads) {
-    // compiler-scheduled, two A register sets (measured faster for plain
-    // K-major B than the pinned order below)
-    u32x4 R0[NAB][4], R1[NAB][4], hr2[4];
-    auto load_a2 = [&](u32x4 (&dst)[NAB][4], int gs) {
-      const char* a0 = A0 + static_cast<int64_t>(gs) * 4096;
-      const char* a1 = A1 + static_cast<int64_t>(gs) * 4096;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        dst[0][s] = *reinterpret_cast<const u32x4*>(a0 + aoff + s * 1024);
-        dst[1][s] = *reinterpret_cast<const u32x4*>(a1 + aoff + s * 1024);
-      }
-    };
-    auto store_b2 = [&](int st) {
-      src.finish(hr2);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hs[st][wslot + 256 * j] = hr2[j];
-    };
-    auto mfma2 = [&](const u32x4 (&cur)[NAB][4], int st) {
-      const char* stage = reinterpret_cast<const char*>(&hs[st][0]);
-  #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 b[NTB];
-  #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-          const char* p = stage + roff[tb] + 16 * s * 256;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 256));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          b[tb] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
-        }
-  #pragma unroll
-        for (int ab = 0; ab < NAB; ++ab) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, cur[ab][s]);
-  #pragma unroll
-          for (int tb = 0; tb < NTB; ++tb)
-            acc[tb][ab] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[tb], acc[tb][ab], 0, 0, 0);
-        }
-      }
-    };
-    auto step2 = [&](const u32x4 (&cur)[NAB][4], u32x4 (&nxt)[NAB][4], int gs, int st) {
-      const int gn = gs + 1 < nsteps ? gs + 1 : gs;
-      src.issue(gn);
-      load_a2(nxt, gn);
-      mfma2(cur, st);
-      store_b2(st ^ 1);
-      __syncthreads();
-    };
-    src.issue(0);
-    store_b2(0);
-    load_a2(R0, 0);
-    __syncthreads();
-    int gs = 0;
-    for (; gs + 2 <= nsteps; gs += 2) {
-      step2(R0, R1, gs, 0);
-      step2(R1, R0, gs + 1, 1);
-    }
-    if (gs < nsteps) step2(R0, R1, gs, 0);
-    return;
-  }
   // One set of A fragments R[ab][s]: the half s = 2h, 2h + 1 is reloaded for
   // the next step right after the step's last matrix instruction that reads
   // it, and the B source's loads for the next step start with the step, so

@@ -1,8 +1,10 @@
 """The loss and every exit head's backward with the logit gradients G formed
 inside the dh and dW GEMMs (nel_matryoshka_loss_backward_packed), checked
-(a) bit for bit against the stored-gradient path (nel_matryoshka_loss_packed
-then nel_heads_backward), and (b) against the oracle's composition
-oracle.loss_backward.
+(a) against the stored-gradient path (nel_matryoshka_loss_packed then
+nel_heads_backward): dh bit for bit (one GEMM loop, the same gradients), dW
+within the reordering bound 2 gamma_n |G~|^T |h| (the same bf16 products
+summed in fp32 by two different loops), and (b) against the oracle's
+composition oracle.loss_backward.
 
 Bars for (b), per element, by the triangle inequality through the GPU's own
 stored gradients G~ (which the loss tests hold to the oracle's G within the
@@ -38,18 +40,30 @@ def run_both(nel, ds, alpha, gs, lam, want_dh=True, want_dw=True):
     return (mean_f, tok_f, dh_f, dw_f), (mean_u, tok_u, dl, dh_u, dw_u)
 
 
-def assert_bit_identical(nel, fused, unfused):
+def assert_matches_stored(nel, ds, fused, unfused):
+    """dh bit for bit; dW within 2 gamma_n |G~|^T |h| of the stored-gradient
+    dW (the bound's product runs in fp32 on the GPU: its own rounding is far
+    below the factor 2 it carries)."""
     import torch
     _, _, dh_f, dw_f = fused
-    _, _, _, dh_u, dw_u = unfused
-    for lst_f, lst_u, what in ((dh_f, dh_u, "dh"), (dw_f, dw_u, "dW")):
-        if lst_f is None:
-            assert lst_u is None
-            continue
-        for m, (a, b) in enumerate(zip(lst_f, lst_u)):
-            iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
-            same = torch.equal(a.view(iv), b.view(iv))
-            assert same, f"{what} exit {m}: fused differs from the stored-gradient path"
+    _, _, dl, dh_u, dw_u = unfused
+    if dh_f is None:
+        assert dh_u is None
+    else:
+        for m, (a, b) in enumerate(zip(dh_f, dh_u)):
+            same = torch.equal(a.view(torch.int16), b.view(torch.int16))
+            assert same, f"dh exit {m}: fused differs from the stored-gradient path"
+    if dw_f is None:
+        assert dw_u is None
+        return
+    for m, (a, b) in enumerate(zip(dw_f, dw_u)):
+        n = dl[m].shape[0]
+        bound = 2.0 * gamma(n) * (dl[m].float().abs().t().contiguous() @ ds.h[m].float().abs())
+        err = (a - b).abs()
+        assert bool(torch.all(err <= bound + 1e-30)), (
+            f"dW exit {m}: fused differs from the stored-gradient dW by "
+            f"{float((err / (bound + 1e-30)).max()):.3g} x the reordering bound")
+        assert bool(torch.isfinite(a).all()) == bool(torch.isfinite(b).all())
 
 
 CASES = [
@@ -70,7 +84,7 @@ def test_fused_backward_small(nel, name, widths, V, B, S, alpha, gs, lam, seed):
     log(f"[fused-bwd] {name}: n={s.n_tokens} V={V} widths={widths} alpha={alpha} gs={gs} lam={lam}")
     ds = DevSuite(s)
     fused, unfused = run_both(nel, ds, alpha, gs, lam)
-    assert_bit_identical(nel, fused, unfused)
+    assert_matches_stored(nel, ds, fused, unfused)
     mean_f, tok_f, dh_f, dw_f = fused
     dl = unfused[2]
     ref, dh_ref, dw_ref = oracle.loss_backward(s.h, s.w, s.labels, alpha, grad_scale=gs,
@@ -85,7 +99,7 @@ def test_fused_backward_small(nel, name, widths, V, B, S, alpha, gs, lam, seed):
     g_ref = oracle.matryoshka_grad(oracle.heads(s.h, s.w), s.labels, alpha, gs, lam)
     n = s.n_tokens
     for m in range(s.n_exits):
-        gt = to_np(dl[m])   # the stored gradients the fused GEMMs reproduce bit for bit
+        gt = to_np(dl[m])   # the stored gradients, which the fused GEMMs form bit for bit
         assert_grad_close(gt, g_ref[m], GRAD_TOL["bf16"] * max(1.0, abs(gs)), f"G exit {m}")
         dG = np.abs(gt - g_ref[m])
         w, h = s.w[m].astype(np.float64), s.h[m].astype(np.float64)
@@ -110,7 +124,7 @@ def test_fused_backward_single_outputs(nel):
     for want_dh, want_dw in ((True, False), (False, True)):
         fused, unfused = run_both(nel, ds, 0.3, 1.0, None, want_dh=want_dh, want_dw=want_dw)
         assert (fused[2] is None) != want_dh and (fused[3] is None) != want_dw
-        assert_bit_identical(nel, fused, unfused)
+        assert_matches_stored(nel, ds, fused, unfused)
 
 
 def test_fused_backward_bad_label_is_nan_and_flagged(nel):
@@ -148,15 +162,15 @@ def test_fused_backward_no_tokens(nel):
 
 
 def test_fused_backward_benchmark_shape(nel):
-    """500M-1.5B-3B-3exit (16,384 tokens, V = 32,768): dh and dW bit-identical
-    to the stored-gradient path on every entry, and 24 sampled tokens' dh rows
-    against the oracle by the bar above."""
+    """500M-1.5B-3B-3exit (16,384 tokens, V = 32,768): dh bit-identical to
+    the stored-gradient path and dW within its reordering bound, on every
+    entry, and 24 sampled tokens' dh rows against the oracle by the bar above."""
     import torch
     s = synth.make_workload(2)
     log(f"[fused-bwd] workload 2: n={s.n_tokens} V={s.vocab} widths={s.widths}")
     ds = DevSuite(s)
     fused, unfused = run_both(nel, ds, 0.3, 1.0, None)
-    assert_bit_identical(nel, fused, unfused)
+    assert_matches_stored(nel, ds, fused, unfused)
     rows = np.unique(np.concatenate([[0, 1, s.n_tokens - 1],
                                      np.random.default_rng(78).choice(s.n_tokens, 21, replace=False)]))
     lg = oracle.heads([h[rows] for h in s.h], s.w)

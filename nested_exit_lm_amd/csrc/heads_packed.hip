@@ -138,14 +138,20 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
     int lane = tid & 63;
     asm volatile("" : "+s"(vwe), "+s"(t0e), "+v"(lane));
     const int x = lane & 15, g = lane >> 4;
-    // the labels of this lane's 8 tokens, loaded ahead of their use (rows
-    // beyond n read row n - 1 and are dropped)
+    // Per-token values go through buffer resources that start at the tile's
+    // first token and end at token n (accesses beyond it: loads read 0,
+    // stores are dropped), with 32-bit lane offsets; a lane offset at or
+    // above 2^31 drops a store.  The labels of this lane's 8 tokens are
+    // loaded ahead of their use.
+    const int64_t n_left = n - t0e;
+    const int tok_left = static_cast<int>(min(n_left, static_cast<int64_t>(kW128Tok)));
+    const uint32_t toff = static_cast<uint32_t>(x) * 4u;   // token x of block 0, bytes
+    const buf_rsrc lab_in = make_rsrc(labels + t0e, n_left * 4);
     int ylab[NB];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
-      const int64_t tok = t0e + x + 16 * tb;
-      const int yy = labels[tok < n ? tok : n - 1];
-      ylab[tb] = tok < n ? yy : -1;
+      const int yy = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lab_in, toff, 64 * tb, 0));
+      ylab[tb] = x + 16 * tb < tok_left ? yy : -1;
     }
     // vocabulary entries beyond V vanish under exp; V is a multiple of 32, so
     // a 16-block is wholly in or beyond V
@@ -156,7 +162,12 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
 #pragma unroll
           for (int tb = 0; tb < NB; ++tb) acc[tb][vb] = f32x4{kMasked, kMasked, kMasked, kMasked};
     }
-    float* __restrict__ st = stats + (static_cast<int64_t>(e) * 3 * n_st + (vwe >> 7)) * n;
+    // this wavefront's statistics tile: the maxima, then (a plane further) the sums
+    float* const st = stats + (static_cast<int64_t>(e) * 3 * n_st + (vwe >> 7)) * n + t0e;
+    const buf_rsrc st_m = make_rsrc(st, n_left * 4), st_s = make_rsrc(st + plane, n_left * 4);
+    const buf_rsrc lab_out = make_rsrc(lab + static_cast<int64_t>(e) * n + t0e, n_left * 4);
+    // (a wavefront wholly beyond V, in the last tile only, writes no statistics)
+    const uint32_t st_off = g == 0 && vwe < vocab ? toff : 0x80000000u;
     bf16_t* __restrict__ O = static_cast<bf16_t*>(ex.out[e]);
     char* const ob = reinterpret_cast<char*>(&outbuf[wave][0]);
     // one instance per kind of exit, so that no branch sits inside the loops
@@ -208,11 +219,43 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
             *reinterpret_cast<u32x2*>(ob + (16 * row + (c ^ x)) * 16 + 8 * (g & 1)) = u32x2{pk0, pk1};
           }
           const float s = sum_xor32(sum_xor16(s0 + s1));
-          // The label's logit, from the one lane that holds it: entry
-          // 16 vb + 4 g + i of this wavefront.  The 16 tokens of a block
-          // rarely have a label among the wavefront's 128 entries, so the
-          // selection runs only in a wavefront where one does.
-          const int64_t tok = t0e + x + 16 * tb;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), st_m, st_off, 64 * tb, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), st_s, st_off, 64 * tb, 0);
+        }
+        wave_lds_sync();
+        {
+          // chunk lane % 16 of rows lane / 16 + 4 j, whole row segments, not
+          // read again before the gradient pass: nontemporal buffer stores
+          // from a resource that ends at token n (rows beyond it are
+          // dropped) and a lane offset beyond any range for entries beyond
+          // V, so no store sits under a condition and no 64-bit address is
+          // formed per lane
+          const int ch = lane & 15;
+          const int64_t r0 = t0e + 32 * tp;
+          const buf_rsrc orr = make_rsrc(reinterpret_cast<const char*>(O) + (r0 * vocab + vwe) * 2,
+                                         (n - r0) * vocab * 2 - static_cast<int64_t>(vwe) * 2);
+          const uint32_t loff = vwe + 8 * ch < vocab
+                                    ? (static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(vocab) +
+                                       8u * static_cast<uint32_t>(ch)) * 2u
+                                    : 0x80000000u;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int row = 4 * j + (lane >> 4);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ob + (16 * row + (ch ^ (row & 15))) * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(v, orr, loff, j * 8 * vocab, kBufNontemporal);
+          }
+        }
+        wave_lds_sync();
+      }
+        // The label's logit, from the one lane that holds it: entry
+        // 16 vb + 4 g + i of this wavefront.  The 16 tokens of a block rarely
+        // have a label among the wavefront's 128 entries, so the selection
+        // runs only in a wavefront where one does.  It follows the pair's
+        // statistics (a branch between the two token blocks would keep the
+        // compiler from interleaving their arithmetic), and the pair's
+        // accumulators are dead after it.
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
           const int y = ylab[tb];
           const int rel = y - (vwe + 4 * g);
           const bool hit = rel >= 0 && rel < 128 && (rel & 12) == 0 && y < vocab;
@@ -228,34 +271,10 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
             float lv = yv[0];
 #pragma unroll
             for (int i = 1; i < 4; ++i) lv = isel == i ? yv[i] : lv;
-            if (hit) lab[static_cast<int64_t>(e) * n + tok] = lv;
-          }
-          // (a wavefront wholly beyond V, in the last tile only, writes nothing)
-          if (g == 0 && tok < n && vwe < vocab) {
-            st[tok] = m;
-            st[plane + tok] = s;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv), lab_out, hit ? toff : 0x80000000u,
+                                                  64 * tb, 0);
           }
         }
-        wave_lds_sync();
-        {
-          // chunk lane % 16 of rows lane / 16 + 4 j: wave-uniform row base,
-          // 32-bit lane offsets; whole row segments, not read again before
-          // the gradient pass: nontemporal
-          const int ch = lane & 15;
-          const bool col_ok = vwe + 8 * ch < vocab;
-          const uint32_t loff = (static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(vocab) +
-                                 8u * static_cast<uint32_t>(ch)) * 2u;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int row = 4 * j + (lane >> 4);
-            const u32x4 v = *reinterpret_cast<const u32x4*>(ob + (16 * row + (ch ^ (row & 15))) * 16);
-            char* rb = reinterpret_cast<char*>(O) + ((t0e + 32 * tp + 4 * j) * vocab + vwe) * 2;
-            if (col_ok && t0e + 32 * tp + row < n)
-              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
-          }
-        }
-        wave_lds_sync();
-      }
     };
     if (MODE == kModeLossF16 && ei == 0)
       epilogue(std::true_type{});
@@ -401,32 +420,29 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_loss_kernel_2wg(
           const int c = 2 * vb + (g >> 1);
           *reinterpret_cast<u32x2*>(stage + (8 * row + (c ^ ((row >> 1) & 7))) * 16 + 8 * (g & 1)) =
               u32x2{pk0, pk1};
-          const int dd = ylab[tb] - (vlane + 16 * vb);
-          if (static_cast<unsigned>(dd) < 4u && ylab[tb] < vocab) {
-            float val = acc[tb][vb][0];
-#pragma unroll
-            for (int i = 1; i < 4; ++i) val = (i == dd) ? acc[tb][vb][i] : val;
-            lab[static_cast<int64_t>(e) * n + tx + 16 * tb] = val;
-          }
         }
         s[u] = s0 + s1;
       }
       wave_lds_sync();
       {
-        // wave-uniform row base, 32-bit lane offsets (32 rows of 2 V bytes)
+        // whole lines, not read again before the gradient pass: nontemporal
+        // buffer stores from a resource that ends at token n (rows beyond it
+        // are dropped) and a lane offset beyond any range for entries beyond
+        // V, so no store sits under a condition (32 rows of 2 V bytes)
         const int ch = lane & 7;
-        const uint32_t loff = (static_cast<uint32_t>(lane >> 3) * static_cast<uint32_t>(vocab) +
-                               8u * static_cast<uint32_t>(ch)) * 2u;
-        const bool col_ok = vw + 8 * ch < vocab;
+        const int64_t r0 = t0 + 32 * tp;
+        const buf_rsrc orr = make_rsrc(reinterpret_cast<const char*>(O) + (r0 * vocab + vw) * 2,
+                                       (n - r0) * vocab * 2 - static_cast<int64_t>(vw) * 2);
+        const uint32_t loff = vw + 8 * ch < vocab
+                                  ? (static_cast<uint32_t>(lane >> 3) * static_cast<uint32_t>(vocab) +
+                                     8u * static_cast<uint32_t>(ch)) * 2u
+                                  : 0x80000000u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 8 * j + (lane >> 3);
           const u32x4 v =
               *reinterpret_cast<const u32x4*>(stage + (8 * row + (ch ^ ((row >> 1) & 7))) * 16);
-          char* rb = reinterpret_cast<char*>(O) + ((t0 + 32 * tp + 8 * j) * vocab + vw) * 2;
-          // whole lines, not read again before the gradient pass: nontemporal
-          if (col_ok && t0 + 32 * tp + row < n)
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(rb + loff));
+          __builtin_amdgcn_raw_buffer_store_b128(v, orr, loff, j * 16 * vocab, kBufNontemporal);
         }
       }
       wave_lds_sync();
@@ -436,6 +452,27 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_loss_kernel_2wg(
         t += __shfl_xor(t, 16, 64);
         t += __shfl_xor(t, 32, 64);
         if (g == 0) xsum[wave][32 * tp + 16 * u + x][0] = t;
+      }
+    }
+    // the label's logit, from the one lane that holds it (entry
+    // 16 vb + 4 g + i of the wavefront), in a wavefront where one does
+#pragma unroll
+    for (int tb = 0; tb < kNTB; ++tb) {
+      const int rel = ylab[tb] - vlane;
+      const bool hit = rel >= 0 && rel < 64 && (rel & 12) == 0 && ylab[tb] < vocab;
+      if (__any(hit)) {
+        const int vsel = rel >> 4, isel = rel & 3;
+        float yv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          yv[i] = acc[tb][0][i];
+#pragma unroll
+          for (int vb = 1; vb < kNVB; ++vb) yv[i] = vsel == vb ? acc[tb][vb][i] : yv[i];
+        }
+        float lv = yv[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) lv = isel == i ? yv[i] : lv;
+        if (hit) lab[static_cast<int64_t>(e) * n + tx + 16 * tb] = lv;
       }
     }
     __syncthreads();

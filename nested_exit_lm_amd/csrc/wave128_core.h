@@ -51,6 +51,9 @@ constexpr int kW128Stages = 3;
 
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 
+// Cache-policy operand of a nontemporal buffer access (the "nt" bit).
+constexpr int kBufNontemporal = 2;
+
 // Raw buffer resource over `bytes` bytes from `base` (clamped to 32 bits).
 __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, int64_t bytes) {
   const int64_t b = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);

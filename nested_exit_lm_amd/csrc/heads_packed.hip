@@ -687,10 +687,12 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_argmax_kernel(
 
 constexpr int64_t kCUs = 256;   // compute units of the MI355X
 
-// Exits whose mean width is below this use the two-workgroups-per-CU kernel
-// (measured at widths 512 / 768 / 1024: 955 against 878 TF/s; at
-// 1024 / 2304 / 4352: 1173 against 1239 TF/s for the other kernel).
-constexpr int kWideMeanD = 1536;
+// Exits whose mean width is below this use the two-workgroups-per-CU kernel.
+// Measured, one-wavefront-per-SIMD kernel against it (TF/s, V = 32,768):
+// widths 512 / 768 / 1024 at 16,384 tokens 936 / 926; 512 / 1024 / 1536 /
+// 2048 at 32,768 tokens 1123 / 1095; 1024 / 1536 / 2048 1149 / 1113;
+// 1024 / 2304 / 4352 1254 / 1202.  Narrower exits are not measured.
+constexpr int kWideMeanD = 512;
 
 template <int MODE>
 hipError_t launch_loss(int n_exits, int64_t n, int vocab, const ExitSet& ex, const int32_t* labels,

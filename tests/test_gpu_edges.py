@@ -93,8 +93,8 @@ def _loss_either(nel, ds, packed, hs=None, ws=None, alpha=0.3):
     return to_np(tok), dl
 
 
-# The packed path runs one of two GEMMs by the mean exit width (below 1536:
-# two workgroups per CU; from 1536, as at the benchmark widths: one wavefront
+# The packed path runs one of two GEMMs by the mean exit width (below 512:
+# two workgroups per CU; from 512, as at every benchmark width: one wavefront
 # per SIMD); "packed-wide" takes the second.
 PATHS = [("row-major", False, (128, 256)), ("packed", True, (128, 256)),
          ("packed-wide", True, (1536, 1664))]

@@ -48,7 +48,7 @@ PACKED_SMALL = [
     ("4exit-tiny-vocab", (64, 128, 192, 256), 96, 1, 129, 53),
     ("1exit", (64,), 256, 1, 1, 54),
     ("3exit-odd-steps", (64, 192, 320), 800, 1, 257, 55),
-    # mean width >= 1536: the one-wavefront-per-SIMD kernel (512-entry tiles,
+    # mean width >= 512: the one-wavefront-per-SIMD kernel (512-entry tiles,
     # statistics per 128 entries).  Partial last tile with wavefronts wholly
     # beyond V, V below one wavefront's 128 entries, odd step counts, exits of
     # fewer K steps than the main loop's unrolling (1 and 5)

@@ -244,7 +244,8 @@ nel_status nel_matryoshka_loss(nel_dtype dt, int32_t n_exits, int64_t n_tokens, 
  * core operand is one contiguous 1 KB read, so a bf16 head W [vocab, d] may be
  * rewritten once into the tiled layout below and then used by the *_packed
  * entry points, which compute exactly what their row-major counterparts do.
- * Requires dt == NEL_BF16, vocab % 32 == 0, d % 64 == 0.  The layout, for row
+ * Requires dt == NEL_BF16, vocab % 32 == 0 and below 2^24, d % 64 == 0 and
+ * below 2^24 (NEL_ESHAPE).  The layout, for row
  * block rb < vocab/16, column block kb < d/32, lane l < 64, j < 8:
  *     packed[((rb * (d/32) + kb) * 64 + l) * 8 + j] = w[16 rb + l % 16][32 kb + 8 (l / 16) + j]
  * (one A operand of the 16x16x32 bf16 matrix instruction per 1 KB block).
@@ -259,7 +260,7 @@ nel_status nel_pack_weights(nel_dtype dt, int32_t vocab, int32_t d, const void* 
 /*
  * nel_matryoshka_loss with every w[e] in the tiled layout of
  * nel_pack_weights.  Same arguments, outputs and errors, plus: dt must be
- * NEL_BF16 (NEL_EDTYPE), vocab % 32 == 0 and every d[e] % 64 == 0 and
+ * NEL_BF16 (NEL_EDTYPE), vocab % 32 == 0 and every d[e] % 64 == 0, both
  * below 2^24 (NEL_ESHAPE), and dlogits must be given (NEL_EINVAL): between the head GEMM
  * and the final gradient pass the dlogits buffers hold 16-bit scratch.  With
  * NEL_DIV_FORWARD the teacher's holds its softmax weights exp(l_M - m) (m the
@@ -278,7 +279,7 @@ nel_status nel_matryoshka_loss_packed(nel_dtype dt, int32_t n_exits, int64_t n_t
 
 /*
  * nel_exit_heads with every w[e] in the tiled layout of nel_pack_weights
- * (dt NEL_BF16, vocab % 32 == 0, every d[e] % 64 == 0 and below 2^24; same
+ * (dt NEL_BF16, vocab % 32 == 0, every d[e] % 64 == 0, both below 2^24; same
  * outputs and errors).
  */
 nel_status nel_exit_heads_packed(nel_dtype dt, int32_t n_exits, int64_t n_tokens, int32_t vocab,

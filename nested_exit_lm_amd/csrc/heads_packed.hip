@@ -138,15 +138,15 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
     int lane = tid & 63;
     asm volatile("" : "+s"(vwe), "+s"(t0e), "+v"(lane));
     const int x = lane & 15, g = lane >> 4;
-    // Per-token values go through buffer resources that start at the tile's
-    // first token and end at token n (accesses beyond it: loads read 0,
-    // stores are dropped), with 32-bit lane offsets; a lane offset at or
-    // above 2^31 drops a store.  The labels of this lane's 8 tokens are
-    // loaded ahead of their use.
+    // Per-token values go through buffer resources that cover the tile's
+    // tokens below n (accesses beyond: loads read 0, stores are dropped),
+    // with 32-bit lane offsets; a lane offset at or above 2^31 drops a store
+    // (every resource here spans less than 2^31 bytes).  The labels of this
+    // lane's 8 tokens are loaded ahead of their use.
     const int64_t n_left = n - t0e;
     const int tok_left = static_cast<int>(min(n_left, static_cast<int64_t>(kW128Tok)));
     const uint32_t toff = static_cast<uint32_t>(x) * 4u;   // token x of block 0, bytes
-    const buf_rsrc lab_in = make_rsrc(labels + t0e, n_left * 4);
+    const buf_rsrc lab_in = make_rsrc(labels + t0e, tok_left * 4);
     int ylab[NB];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
@@ -164,8 +164,8 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
     }
     // this wavefront's statistics tile: the maxima, then (a plane further) the sums
     float* const st = stats + (static_cast<int64_t>(e) * 3 * n_st + (vwe >> 7)) * n + t0e;
-    const buf_rsrc st_m = make_rsrc(st, n_left * 4), st_s = make_rsrc(st + plane, n_left * 4);
-    const buf_rsrc lab_out = make_rsrc(lab + static_cast<int64_t>(e) * n + t0e, n_left * 4);
+    const buf_rsrc st_m = make_rsrc(st, tok_left * 4), st_s = make_rsrc(st + plane, tok_left * 4);
+    const buf_rsrc lab_out = make_rsrc(lab + static_cast<int64_t>(e) * n + t0e, tok_left * 4);
     // (a wavefront wholly beyond V, in the last tile only, writes no statistics)
     const uint32_t st_off = g == 0 && vwe < vocab ? toff : 0x80000000u;
     bf16_t* __restrict__ O = static_cast<bf16_t*>(ex.out[e]);
@@ -226,14 +226,15 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
         {
           // chunk lane % 16 of rows lane / 16 + 4 j, whole row segments, not
           // read again before the gradient pass: nontemporal buffer stores
-          // from a resource that ends at token n (rows beyond it are
-          // dropped) and a lane offset beyond any range for entries beyond
-          // V, so no store sits under a condition and no 64-bit address is
-          // formed per lane
+          // from a resource over the pair's 32 rows that ends at token n
+          // (rows beyond it are dropped; below 2^31 bytes since V < 2^24)
+          // and a lane offset of 2^31 for entries beyond V, so no store sits
+          // under a condition and no 64-bit address is formed per lane
           const int ch = lane & 15;
           const int64_t r0 = t0e + 32 * tp;
+          const int64_t rows = min(max(n - r0, int64_t{0}), int64_t{32});
           const buf_rsrc orr = make_rsrc(reinterpret_cast<const char*>(O) + (r0 * vocab + vwe) * 2,
-                                         (n - r0) * vocab * 2 - static_cast<int64_t>(vwe) * 2);
+                                         rows * vocab * 2 - static_cast<int64_t>(vwe) * 2);
           const uint32_t loff = vwe + 8 * ch < vocab
                                     ? (static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(vocab) +
                                        8u * static_cast<uint32_t>(ch)) * 2u
@@ -426,13 +427,15 @@ __global__ __launch_bounds__(kPkThreads, 2) void heads_loss_kernel_2wg(
       wave_lds_sync();
       {
         // whole lines, not read again before the gradient pass: nontemporal
-        // buffer stores from a resource that ends at token n (rows beyond it
-        // are dropped) and a lane offset beyond any range for entries beyond
-        // V, so no store sits under a condition (32 rows of 2 V bytes)
+        // buffer stores from a resource over the pair's 32 rows that ends at
+        // token n (rows beyond it are dropped; below 2^31 bytes since
+        // V < 2^24) and a lane offset of 2^31 for entries beyond V, so no
+        // store sits under a condition
         const int ch = lane & 7;
         const int64_t r0 = t0 + 32 * tp;
+        const int64_t rows = min(max(n - r0, int64_t{0}), int64_t{32});
         const buf_rsrc orr = make_rsrc(reinterpret_cast<const char*>(O) + (r0 * vocab + vw) * 2,
-                                       (n - r0) * vocab * 2 - static_cast<int64_t>(vw) * 2);
+                                       rows * vocab * 2 - static_cast<int64_t>(vw) * 2);
         const uint32_t loff = vw + 8 * ch < vocab
                                   ? (static_cast<uint32_t>(lane >> 3) * static_cast<uint32_t>(vocab) +
                                      8u * static_cast<uint32_t>(ch)) * 2u
@@ -723,7 +726,8 @@ hipError_t launch_loss(int n_exits, int64_t n, int vocab, const ExitSet& ex, con
 
 // d below 2^24 keeps the 32-bit byte offsets of a 128-token slice of h in range.
 bool packed_shape_ok(int vocab, int d) {
-  return vocab >= 32 && vocab % 32 == 0 && d >= 64 && d % 64 == 0 && d < (1 << 24);
+  return vocab >= 32 && vocab % 32 == 0 && vocab < (1 << 24) && d >= 64 && d % 64 == 0 &&
+         d < (1 << 24);
 }
 
 hipError_t launch_pack_weights(int vocab, int d, const void* w, void* packed, hipStream_t s) {

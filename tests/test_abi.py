@@ -137,6 +137,7 @@ def test_packed_host_validation():
 
     assert loss(dt=0) == -3                                    # fp32 has no packed form
     assert loss(V=100) == -2
+    assert loss(V=1 << 24) == -2                               # 32-bit scratch-store ranges
     assert loss(d=_arr(ctypes.c_int32, 64, 128, 200)) == -2    # a width not a multiple of 64
     assert loss(d=_arr(ctypes.c_int32, 64, 64, 192)) == -2
     assert loss(dl=None) == -1                                 # gradients are required
@@ -146,6 +147,8 @@ def test_packed_host_validation():
     need = nel.workspace_size(nel.OP_HEADS, 2, 4, 256)
     assert lib.nel_exit_heads_packed(0, 2, 4, 256, d2, p2, p2, None, FAKE, FAKE, need, None) == -3
     assert lib.nel_exit_heads_packed(1, 2, 4, 250, d2, p2, p2, None, FAKE, FAKE, need, None) == -2
+    assert lib.nel_exit_heads_packed(1, 2, 4, 1 << 24, d2, p2, p2, None, FAKE, FAKE, need,
+                                     None) == -2
     assert lib.nel_exit_heads_packed(1, 2, 4, 256, _arr(ctypes.c_int32, 64, 100), p2, p2, None,
                                      FAKE, FAKE, need, None) == -2
     assert lib.nel_exit_heads_packed(1, 2, 4, 256, _arr(ctypes.c_int32, 64, 1 << 24), p2, p2,

@@ -168,3 +168,42 @@ def test_packed_benchmark_shape_every_token(nel):
     assert_loss_close(mean, want, 1e-3, "means")
     log(f"[packed] benchmark shape, every token: worst |dlogits err| {worst_g:.2e}, "
         f"worst mean scaled err {np.max(np.abs(mean - want) / np.maximum(1.0, np.abs(want))):.2e}")
+
+
+@pytest.mark.parametrize("widths", [(64, 960), (64, 128)], ids=["one-wave-per-simd", "two-wg-per-cu"])
+def test_packed_loss_large_scratch_partial_vocab(nel, widths):
+    """V = 32,800 (not a multiple of 128: the last vocabulary tile's first
+    wavefront holds 32 valid entries, the rest are dropped stores) and 34,816
+    tokens, so that the scratch beyond a tile's first row spans more than
+    2^31 bytes: a dropped store's lane offset (2^31) would land inside the
+    buffer about 32,737 rows later if a store resource spanned to token n.
+    The rows that such stores would hit are checked against the oracle (a
+    student entry overwritten with -inf makes its Dist infinite), plus a few
+    others; every sampled gradient row is finite and within the bar."""
+    import torch
+    V = 32800
+    s = synth.make_suite(widths, V, 17, 2048, seed=91)
+    n = s.n_tokens
+    assert n * V * 2 > 2 ** 31 + 2 * 32768   # from row 0, column 32,768: past 2^31 bytes
+    log(f"[packed] large scratch: n={n} V={V} widths={widths}")
+    ds = DevSuite(s)
+    pw = [nel.pack_weights(w) for w in ds.w]
+    mean, tok, dl = run_loss(nel, ds, 0.3, packed=pw)
+    r = np.random.default_rng(92)
+    danger = np.arange(32736, n)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, n - 1],
+                                     r.choice(danger, size=120, replace=False),
+                                     r.choice(32736, size=20, replace=False)]))
+    ref, grads = oracle.forward_tokens(s.h, s.w, s.labels, 0.3, 1.0, rows=rows)
+    assert np.all(np.isfinite(tok[:, :, rows]))
+    assert_loss_close(tok[:, 0, rows], ref["ce"], 1e-3, "CE")
+    assert_loss_close(tok[:, 1, rows], ref["dist"], 1e-3, "Dist")
+    assert_loss_close(tok[:, 2, rows], ref["loss"], 1e-3, "L")
+    idx = torch.from_numpy(rows).cuda()
+    for m in range(s.n_exits):
+        got = to_np(dl[m].index_select(0, idx))
+        assert np.all(np.isfinite(got))
+        assert_grad_close(got, grads[m], 2e-2, f"dlogits exit {m}")
+    assert np.all(np.isfinite(mean))
+    del dl, ds, pw
+    torch.cuda.empty_cache()

@@ -75,8 +75,9 @@ __device__ __forceinline__ void w128_lanes(int tid, int d, W128Operands& op, int
   const int bchunk = tid & 7, brow = tid >> 3;
   hslot = bchunk * kW128Tok + (brow ^ (2 * bchunk));
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    op.hoff[j] = static_cast<uint32_t>(((brow + 32 * j) * d + bchunk * 8) * 2);
+  for (int j = 0; j < 4; ++j)   // unsigned: 128 rows of d < 2^24 entries stay below 2^32 bytes
+    op.hoff[j] = static_cast<uint32_t>(brow + 32 * j) * static_cast<uint32_t>(d) * 2u +
+                 static_cast<uint32_t>(bchunk) * 16u;
   const uint32_t lane = tid & 63;
 #pragma unroll
   for (int ab = 0; ab < 8; ++ab) op.woff[ab] = static_cast<uint32_t>(ab) * d * 32u + lane * 16u;

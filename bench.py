@@ -50,10 +50,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(p=None):
     """HBM bytes per launch of the head GEMM from rocprofv3 counter runs, if they
-    were taken on the current kernel sources (else None)."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+    were taken on the current kernel sources (else None).  p: the record
+    (default profiles/traffic.json)."""
+    p = p or os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -323,10 +324,11 @@ def _read_counter_csv(d):
     return out
 
 
-def summarize_counters(fetch_dir, write_dir):
+def summarize_counters(fetch_dir, write_dir, out=None):
     """HBM traffic per launch of the head GEMM: rocprofv3 FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch), each scaled so that the calibration kernel (1 GiB read,
-    1 GiB written) reads exactly its size."""
+    1 GiB written) reads exactly its size.  Written to `out` (default
+    profiles/traffic.json) and returned."""
     fetch, write = _read_counter_csv(fetch_dir), _read_counter_csv(write_dir)
 
     def pick(dct, key):
@@ -349,10 +351,12 @@ def summarize_counters(fetch_dir, write_dir):
            "fetch_scale": f_scale, "write_scale": w_scale,
            "heads_loss_fetch_bytes": fb, "heads_loss_write_bytes": wb,
            "heads_loss_bytes_per_launch": fb + wb}
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    out = out or os.path.join(ROOT, "profiles", "traffic.json")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    with open(out, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res))
+    return res
 
 
 def bench_backward(nel, torch, hs, ws, dl, args, ids=None, embs=None, pw=None, labels=None,

@@ -136,13 +136,16 @@ def test_packed_heads_logits_partial_tile(nel, V, S):
         check_argmax(am[m], s.h[m], s.w[m], to_np(logits[m]))
 
 
-def test_packed_benchmark_shape_every_token(nel):
-    """The benchmark's workload (500M/1.5B/3B widths, 16,384 tokens, V = 32,768,
-    alpha 0.3) in the benchmark's launch configuration, every token against the
-    oracle: CE, Dist and L per token and exit, every logit gradient, and the
-    ten reported means (rel 1e-3 of the oracle's float64 means)."""
+@pytest.mark.parametrize("k", [2, 1, 3], ids=["500M-1.5B-3B-3exit", "200M-proxy-3exit", "4exit"])
+def test_packed_every_token(nel, k):
+    """Each bf16 training workload (k = 2 is the benchmark's: 500M/1.5B/3B
+    widths, 16,384 tokens, V = 32,768, alpha 0.3) in the benchmark's launch
+    configuration, every token against the oracle: CE, Dist and L per token
+    and exit, every logit gradient, and the reported means (rel 1e-3 of the
+    oracle's float64 means)."""
     import torch
-    s = synth.make_workload(2)
+    s = synth.make_workload(k)
+    log(f"[packed] workload {k} ({s.name}) every token: N={s.n_tokens} widths={s.widths}")
     ds = DevSuite(s)
     pw = [nel.pack_weights(w) for w in ds.w]
     mean, tok, dl = run_loss(nel, ds, s.alpha, packed=pw)
@@ -166,7 +169,7 @@ def test_packed_benchmark_shape_every_token(nel):
     ce, dist, loss = (np.concatenate(x, axis=1) for x in (ce, dist, loss))
     want = np.concatenate([ce.mean(1), dist.mean(1), loss.mean(1), [loss.sum(0).mean()]])
     assert_loss_close(mean, want, 1e-3, "means")
-    log(f"[packed] benchmark shape, every token: worst |dlogits err| {worst_g:.2e}, "
+    log(f"[packed] workload {k}, every token: worst |dlogits err| {worst_g:.2e}, "
         f"worst mean scaled err {np.max(np.abs(mean - want) / np.maximum(1.0, np.abs(want))):.2e}")
 
 

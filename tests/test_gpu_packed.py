@@ -57,6 +57,11 @@ PACKED_SMALL = [
     ("1exit-wide", (1600,), 544, 2, 70, 60),
     ("2exit-wide-short-exits", (64, 3008), 512, 1, 140, 61),
     ("2exit-wide-five-steps", (320, 2752), 640, 1, 131, 62),
+    # V = 32 (two of a wavefront's eight 16-entry blocks exist), a single
+    # token, and a mean width of exactly 512 (the rule's threshold)
+    ("2exit-wide-vocab-32", (512, 576), 32, 1, 70, 63),
+    ("2exit-wide-one-token", (1536, 1600), 1056, 1, 1, 64),
+    ("2exit-mean-512", (448, 576), 800, 2, 67, 65),
 ]
 
 

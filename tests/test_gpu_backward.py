@@ -54,6 +54,8 @@ CASES = [
     ("partial-A-tile", (320,), 512, 1, 129, 62),
     ("tiny-vocab", (64, 128), 64, 1, 65, 63),
     ("one-token", (128,), 256, 1, 1, 64),
+    # V % 128 == 64: dW's last 128-entry B tile half outside the vocabulary
+    ("partial-B-tile", (192, 256), 576, 2, 77, 65),
 ]
 
 

@@ -23,11 +23,13 @@
 //     lane l's 8 elements at l * 8 are W[16 rb + l % 16][32 kb + 8 (l / 16) + j],
 // so every operand load is one contiguous 1 KB read.
 //
-// Loss GEMM: workgroups of 4 wavefronts, tile 128 tokens x 512 vocabulary
-// entries, one workgroup per CU, on the main loop of wave128_core.h (W as the
-// A operand straight into registers, h as the B operand staged through LDS,
-// 128 x 128 per wavefront).  Greedy-verify GEMM: tile 128 tokens x 256
-// entries, two workgroups per CU, on the main loop of packed16_core.h.
+// Loss and greedy-verify GEMMs: workgroups of 4 wavefronts, tile 128 tokens x
+// 512 vocabulary entries, one workgroup per CU, on the main loop of
+// wave128_core.h (W as the A operand straight into registers, h as the B
+// operand staged through LDS, 128 x 128 per wavefront).  Exits of mean width
+// below 512 (loss) and grids of fewer than two workgroups per CU (verify) run
+// a 128 x 256 tile at two workgroups per CU on the main loop of
+// packed16_core.h instead.
 //
 // Loss epilogue, per wavefront and token: the maximum m of its 128 logits,
 // sum exp(l - m) and the label's logit (one statistics tile per wavefront),

@@ -124,12 +124,11 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_loss_kernel(
     const int e = ei == 0 ? n_exits - 1 : ei - 1;
     const int D = ex.d[e];
     W128Operands op;
-    int hslot;
-    w128_lanes(tid, D, op, hslot);
+    w128_lanes(tid, D, op);
     op.h = make_rsrc(static_cast<const char*>(ex.h[e]) + t0 * D * 2, (n - t0) * D * 2);
     op.w = make_rsrc(static_cast<const char*>(ex.w[e]) + static_cast<int64_t>(vw >> 4) * D * 32,
                      static_cast<int64_t>(vocab / 16 - (vw >> 4)) * D * 32);
-    w128_tile_gemm(acc, stage, op, hslot, D / 64);
+    w128_tile_gemm(acc, stage, op, D / 64);
 
     // Opaque copies of values that are the same for every exit keep the
     // compiler from hoisting the epilogue's per-lane offsets and predicates
@@ -513,14 +512,13 @@ __global__ __launch_bounds__(kW128Threads, 1) void heads_argmax_kernel_w128(
   const int vw = vt * kW128Voc + wave * 128;   // this wavefront's first vocabulary entry
   const int D = ex.d[e];
   W128Operands op;
-  int hslot;
-  w128_lanes(tid, D, op, hslot);
+  w128_lanes(tid, D, op);
   op.h = make_rsrc(static_cast<const char*>(ex.h[e]) + t0 * D * 2, (n - t0) * D * 2);
   op.w = make_rsrc(static_cast<const char*>(ex.w[e]) + static_cast<int64_t>(vw >> 4) * D * 32,
                    static_cast<int64_t>(vocab / 16 - (vw >> 4)) * D * 32);
   constexpr int NB = 8;
   f32x4 acc[NB][NB];
-  w128_tile_gemm(acc, stage, op, hslot, D / 64);
+  w128_tile_gemm(acc, stage, op, D / 64);
   // opaque copies: the epilogue's lane values are computed here, not kept
   // live (and spilled) across the main loop
   int vwe = vw;

@@ -13,26 +13,29 @@
 //    (ab, kh) of a K step is reloaded with the next step's block right after
 //    the 8 matrix instructions that read it, so every load has a whole step
 //    of matrix work ahead of its use.
-//  * B (h_m, row-major): each K step's 128 x 64 slice is staged in a ring of
-//    three 16 KB LDS stages, chunk-major (row t, 16-byte chunk c in slot
-//    128 c + (t ^ 2 c): 16 consecutive rows of a fragment read, and 2 rows x
-//    8 chunks of a write, each cover all 64 banks).  A thread's 4 chunks of a
-//    slice are loaded two register sets deep: the loads for step g + 3 go out
-//    in the second half of step g and are stored into the ring in the middle
-//    of step g + 1.  The fragments are double buffered: the next half step's
-//    8 are read from LDS while this half step's instructions run.
+//  * B (h_m, row-major): each K step's 128 x 64 slice goes straight from
+//    memory into a ring of four 16 KB LDS stages (buffer loads that write
+//    LDS, no registers), two steps ahead of its first use.  Stage layout:
+//    row t, 16-byte chunk c at slot 8 t + (c ^ ((t / 2) mod 8)).  A load
+//    instruction fills 64 consecutive slots (8 rows, every chunk of each, so
+//    8 lanes read one row's 128 bytes), and the 16 rows of a fragment read
+//    fall in 16 different bank groups.  The fragments are double buffered:
+//    the next half step's 8 are read from LDS while this half step's
+//    instructions run.
 //  * Loads are buffer loads: the wave-uniform K offset is a scalar operand and
 //    the lane offsets are computed once, so no vector instruction computes an
 //    address in the loop; a load outside the resource's byte range returns
 //    zero, which covers token rows beyond n and vocabulary rows beyond V.
-//  * One barrier per K step.  Stage (g + 2) mod 3 is written in step g after
-//    the barrier of step g - 1 (every read of step g - 1 is done) and is first
-//    read in step g + 1's second half, after the barrier of step g.  That
-//    barrier waits only for the LDS writes, which were issued half a step
-//    earlier, not for the 8 fragment reads issued after them.
-//  * Between the groups of 8 matrix instructions the scheduling barriers pin
-//    the loads: per group at most one W block, one fragment read and one h
-//    chunk, spread evenly over the step.
+//  * One barrier per K step.  Step g's slice is loaded at the start of step
+//    g - 3 (the prologue loads steps 0 to 2) into stage g mod 4, last read in
+//    step g - 4's first half, so every wavefront is past those reads (the
+//    barrier of step g - 4).  It is first read in step g - 1's second half;
+//    the barrier of step g - 2 waits for it (a fixed count of later loads may
+//    still be outstanding: every step issues the same loads, past the last
+//    step they re-read it).
+//  * Scheduling barriers pin the order: a step's 4 stage loads at its start,
+//    then after every group of 8 matrix instructions one W block and one
+//    fragment read.
 //
 // Layout of the accumulators: acc[tb][ab] is the 16 x 16 block of token rows
 // 16 tb .. and A rows 16 ab .. of the wavefront; lane l holds token row
@@ -47,7 +50,7 @@ constexpr int kW128Threads = 256;   // 4 wavefronts
 constexpr int kW128Tok = 128;       // token rows (B) per workgroup
 constexpr int kW128Voc = 512;       // A rows per workgroup (128 per wavefront)
 constexpr int kW128Slots = 8 * kW128Tok;   // 16-byte LDS slots per stage
-constexpr int kW128Stages = 3;
+constexpr int kW128Stages = 4;
 
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 
@@ -65,20 +68,21 @@ __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, int64_t bytes) {
 struct W128Operands {
   buf_rsrc h;          // the tile's token rows of h_m (row t0 at byte 0), rows beyond n excluded
   buf_rsrc w;          // the wavefront's first packed row block of W^m, blocks beyond V excluded
-  uint32_t hoff[4];    // the thread's h chunks in K step 0: rows brow + 32 j, chunk bchunk
+  uint32_t hoff[4];    // the lane's h chunk of stage load j in K step 0
   uint32_t woff[8];    // the lane's 16 bytes of row block ab in K block 0
 };
 
-// Thread -> h chunk map: chunk i = tid + 256 j of a 128 x 64 slice is row
-// i / 8 = tid / 8 + 32 j, chunk i % 8, at slot 128 c + (t ^ 2c) = hslot + 32 j.
-__device__ __forceinline__ void w128_lanes(int tid, int d, W128Operands& op, int& hslot) {
-  const int bchunk = tid & 7, brow = tid >> 3;
-  hslot = bchunk * kW128Tok + (brow ^ (2 * bchunk));
+// Stage load j of wavefront w fills slots 64 (4 w + j) + lane: row
+// t = 32 w + 8 j + lane / 8 at position lane mod 8, i.e. chunk
+// (lane mod 8) ^ ((t / 2) mod 8).
+__device__ __forceinline__ void w128_lanes(int tid, int d, W128Operands& op) {
+  const int lane = tid & 63, w = tid >> 6;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)   // unsigned: 128 rows of d < 2^24 entries stay below 2^32 bytes
-    op.hoff[j] = static_cast<uint32_t>(brow + 32 * j) * static_cast<uint32_t>(d) * 2u +
-                 static_cast<uint32_t>(bchunk) * 16u;
-  const uint32_t lane = tid & 63;
+  for (int j = 0; j < 4; ++j) {   // unsigned: 128 rows of d < 2^24 entries stay below 2^32 bytes
+    const int t = 32 * w + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((t >> 1) & 7);
+    op.hoff[j] = static_cast<uint32_t>(t) * static_cast<uint32_t>(d) * 2u + static_cast<uint32_t>(c) * 16u;
+  }
 #pragma unroll
   for (int ab = 0; ab < 8; ++ab) op.woff[ab] = static_cast<uint32_t>(ab) * d * 32u + lane * 16u;
 }
@@ -88,51 +92,65 @@ __device__ __forceinline__ void w128_lanes(int tid, int d, W128Operands& op, int
 // of the workgroup calls this together; it ends with a full barrier, after
 // which the stages are free.
 __device__ __forceinline__ void w128_tile_gemm(f32x4 (&acc)[8][8], u32x4* stage,
-                                               const W128Operands& op, int hslot, int nsteps) {
+                                               const W128Operands& op, int nsteps) {
   constexpr int NB = 8;
 #pragma unroll
   for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
     for (int ab = 0; ab < NB; ++ab) acc[tb][ab] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
-  int fsl[2];   // slot of fragment row x, chunk 4 kh + g (token block tb: + 16 tb)
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  int fsl[2];   // slot of fragment row x, chunk 4 kh + g (token block tb: + 128 tb)
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    const int c = 4 * kh + g;
-    fsl[kh] = kW128Tok * c + (x ^ (2 * c));
-  }
-  u32x4 R[NB][2], hr[2][4];
+  for (int kh = 0; kh < 2; ++kh) fsl[kh] = 8 * x + ((4 * kh + g) ^ ((x >> 1) & 7));
+  u32x4 R[NB][2];
   bf16x8 b[2][NB];
   auto ld_w = [&](int ab, int kh, int gs) {
     R[ab][kh] = __builtin_amdgcn_raw_buffer_load_b128(op.w, op.woff[ab] + kh * 1024, gs * 2048, 0);
   };
-  auto ld_h = [&](int set, int j, int gs) {
-    hr[set][j] = __builtin_amdgcn_raw_buffer_load_b128(op.h, op.hoff[j], gs * 128, 0);
-  };
-  auto st_h = [&](int set, int st) {
+  // Step gs's slice into stage st: 4 loads per wavefront, 1 KB of slots each
+  // (lane l's 16 bytes go to the LDS address in m0 plus 16 l).  Written as
+  // assembly so that the compiler, which cannot tell the stages apart, adds
+  // no wait for these loads before every fragment read; the barrier of each
+  // step waits for them instead.  The loads have no register destination,
+  // and the compiler's own waits for the W registers stay correct (loads
+  // complete in order; loads it does not know of only make them wait
+  // longer).  m0 is saved and restored around the load, with the one wait
+  // state a write of m0 needs before a load that reads it.
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                            (__attribute__((address_space(3))) u32x4*)(stage))) +
+                        1024u * static_cast<uint32_t>(4 * wave);
+  auto ld_stage = [&](int st, int gs) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) stage[st * kW128Slots + hslot + 32 * j] = hr[set][j];
+    for (int j = 0; j < 4; ++j) {
+      uint32_t saved;
+      asm volatile(
+          "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+          "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(lds0 + static_cast<uint32_t>(st * kW128Slots * 16 + 1024 * j)), "v"(op.hoff[j]),
+            "s"(op.h), "s"(gs * 128)
+          : "memory");
+    }
   };
   const int last = nsteps - 1;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ld_h(0, j, 0);
-  st_h(0, 0);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ld_h(1, j, min(1, last));
-  st_h(1, 1);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ld_h(0, j, min(2, last));
+  ld_stage(0, 0);
+  ld_stage(1, min(1, last));
+  ld_stage(2, min(2, last));
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
     for (int ab = 0; ab < NB; ++ab) ld_w(ab, kh, 0);
-  __syncthreads();
+  // steps 0 and 1 have landed once at most step 2's 4 and the 16 W loads are outstanding
+  asm volatile("s_waitcnt vmcnt(20)\n\ts_barrier" ::: "memory");
 #pragma unroll
-  for (int tb = 0; tb < NB; ++tb) b[0][tb] = __builtin_bit_cast(bf16x8, stage[fsl[0] + 16 * tb]);
-  // Step gi reads stage st and h register set hs holds step gi + 2's slice.
-  auto step = [&](int gi, int st, int hs) {
+  for (int tb = 0; tb < NB; ++tb) b[0][tb] = __builtin_bit_cast(bf16x8, stage[fsl[0] + 128 * tb]);
+  // Step gi reads stage st = gi mod 4.
+  auto step = [&](int gi, int st) {
     const int gw = min(gi + 1, last), gh = min(gi + 3, last);
-    const int nst = st == 2 ? 0 : st + 1;
+    const int nst = (st + 1) & 3;
+    ld_stage((st + 3) & 3, gh);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
@@ -143,26 +161,22 @@ __device__ __forceinline__ void w128_tile_gemm(f32x4 (&acc)[8][8], u32x4* stage,
               __builtin_bit_cast(bf16x8, R[ab][kh]), b[kh][tb], acc[tb][ab], 0, 0, 0);
         ld_w(ab, kh, gw);
         // next half step's fragment ab (fragments are indexed by token block)
-        const int idx = kh == 0 ? st * kW128Slots + fsl[1] + 16 * ab
-                                : nst * kW128Slots + fsl[0] + 16 * ab;
-        b[kh ^ 1][ab] = __builtin_bit_cast(bf16x8, stage[idx]);
-        if (kh == 1 && ab < 4) ld_h(hs ^ 1, ab, gh);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (kh == 0) {
-        st_h(hs, st == 0 ? 2 : st - 1);   // (st + 2) mod 3
+        const u32x4 v = kh == 0 ? stage[st * kW128Slots + fsl[1] + 128 * ab]
+                            : stage[nst * kW128Slots + fsl[0] + 128 * ab];
+        b[kh ^ 1][ab] = __builtin_bit_cast(bf16x8, v);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the LDS writes above are done once at most the 8 fragment reads issued
-    // after them are outstanding (LDS operations complete in order)
-    asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
+    // step gi + 2's slice (loaded at the start of step gi - 1, or in the
+    // prologue) has landed once at most the 16 W loads before this step, this
+    // step's stage load and its 16 W loads are outstanding
+    asm volatile("s_waitcnt vmcnt(36)\n\ts_barrier" ::: "memory");
   };
-  // unrolled by 6 so that the stage (mod 3) and h set (mod 2) are constants
-  for (int gs = 0; gs < nsteps; gs += 6) {
+  // unrolled by 4 so that the stage is a constant
+  for (int gs = 0; gs < nsteps; gs += 4) {
 #pragma unroll
-    for (int u = 0; u < 6; ++u)
-      if (gs + u < nsteps) step(gs + u, u % 3, u & 1);
+    for (int u = 0; u < 4; ++u)
+      if (gs + u < nsteps) step(gs + u, u);
   }
   __syncthreads();
 }

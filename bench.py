@@ -259,9 +259,12 @@ def main():
     kern["finalize"]["hbm_frac"] = kern["finalize"]["gbs"] / HBM_PEAK_GBS
     kern["pack"]["gbs"] = pbytes / (kern["pack"]["avg_ms"] / 1e3) / 1e9
     kern["pack"]["hbm_frac"] = kern["pack"]["gbs"] / HBM_PEAK_GBS
-    # merge: read (m, sigma) per (exit, 256-entry tile, token), the label logits and
-    # labels; write LSE and (CE, Dist, L) per (exit, token)
-    n_vt = (V + 255) // 256
+    # merge: read (m, sigma) per (exit, statistics tile, token), the label logits and
+    # labels; write LSE and (CE, Dist, L) per (exit, token).  The statistics tiles
+    # are 128 entries wide from the one-wavefront-per-SIMD loss GEMM (mean exit
+    # width of at least 512) and 256 from the two-workgroups-per-CU one.
+    tile = 128 if sum(D) >= 512 * len(D) else 256
+    n_vt = (V + tile - 1) // tile
     mbytes = 4 * N * (2 * len(D) * n_vt + len(D) + 1 + len(D) + 3 * len(D))
     kern["merge"]["gbs"] = mbytes / (kern["merge"]["avg_ms"] / 1e3) / 1e9
     kern["merge"]["hbm_frac"] = kern["merge"]["gbs"] / HBM_PEAK_GBS

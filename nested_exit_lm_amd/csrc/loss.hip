@@ -46,6 +46,7 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 }
 
 constexpr int kMergeGroups = 16;
+constexpr int kMergeBatch = 8;    // tiles whose loads a merge thread issues together
 
 template <int N>
 __device__ __forceinline__ float group_tree(const float (*sh)[64][2], int tl) {
@@ -80,10 +81,22 @@ __global__ __launch_bounds__(1024) void loss_merge_kernel(int M, int64_t n, int 
   for (int ei = 0; ei < M; ++ei) {
     const int e = ei == 0 ? M - 1 : ei - 1;
     const float* st = stats + static_cast<int64_t>(e) * 3 * plane + t;
+    // a thread's tiles vt = g + kMergeGroups i in ascending order, their
+    // loads issued kMergeBatch at a time (past the last tile: re-reads, unused)
     float m = -INFINITY, s = 0.f;
     if (valid)
-      for (int vt = g; vt < n_vt; vt += kMergeGroups)
-        lse_merge(m, s, st[static_cast<int64_t>(vt) * n], st[plane + static_cast<int64_t>(vt) * n]);
+      for (int vt0 = g; vt0 < n_vt; vt0 += kMergeBatch * kMergeGroups) {
+        float mm[kMergeBatch], ss[kMergeBatch];
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+          const int64_t o = static_cast<int64_t>(min(vt0 + k * kMergeGroups, n_vt - 1)) * n;
+          mm[k] = st[o];
+          ss[k] = st[plane + o];
+        }
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k)
+          if (vt0 + k * kMergeGroups < n_vt) lse_merge(m, s, mm[k], ss[k]);
+      }
     sh[g][tl][0] = m;
     sh[g][tl][1] = s;
     __syncthreads();
@@ -97,9 +110,18 @@ __global__ __launch_bounds__(1024) void loss_merge_kernel(int M, int64_t n, int 
     if (ei > 0 && !skip_dist) {   // (otherwise div_finish_kernel supplies Dist)
       float a = 0.f;
       if (valid)
-        for (int vt = g; vt < n_vt; vt += kMergeGroups)
-          a = fmaf(fexp(stT[static_cast<int64_t>(vt) * n] - lseT),
-                   st[2 * plane + static_cast<int64_t>(vt) * n], a);
+        for (int vt0 = g; vt0 < n_vt; vt0 += kMergeBatch * kMergeGroups) {
+          float mt[kMergeBatch], ws[kMergeBatch];
+#pragma unroll
+          for (int k = 0; k < kMergeBatch; ++k) {
+            const int64_t o = static_cast<int64_t>(min(vt0 + k * kMergeGroups, n_vt - 1)) * n;
+            mt[k] = stT[o];
+            ws[k] = st[2 * plane + o];
+          }
+#pragma unroll
+          for (int k = 0; k < kMergeBatch; ++k)
+            if (vt0 + k * kMergeGroups < n_vt) a = fmaf(fexp(mt[k] - lseT), ws[k], a);
+        }
       sh[g][tl][0] = a;
       __syncthreads();
       const float T = group_tree<kMergeGroups>(sh, tl);
